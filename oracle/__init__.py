@@ -1,0 +1,209 @@
+"""CPU oracle for the DeepSeek-V4.1 Indexer hot path -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls anything here, and this
+package imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain C, OpenMP over rows, built with
+``-O2 -ffp-contract=off``); this module builds it with gcc when needed and
+marshals numpy arrays through ctypes.  ``topk_bruteforce`` and
+``select_blocks_bruteforce`` below are independent pure-numpy restatements
+used to pin the C code on tiny inputs.
+
+Pages cited (by page and section):
+  [IDX]  "DeepSeek V4.1" -- class Indexer (atlas.klimoza.dev, .../indexer/index-keys)
+  [CMP]  "Module compress" -- Rust CPU reference API (docs.atlascybernetics.ai)
+  [VLLM] "launcher/.../patches/attention.py" -- vLLM DeepseekV4 patch (git.kilork.org)
+
+Parity status per function (what pins it; see tests/test_oracle_*.py):
+  fp4_quant_rows   pinned: exhaustive e8m0 exponent vs exact rationals, e2m1
+                   tie table, nearest-point property, idempotence.
+  head_dots        pinned: equals float64 matmul of the dequantised rows.
+  score            pinned: H=1 reduces to relu(d); a hand-worked order case;
+                   fsum error bound; masks by brute force.
+  topk             pinned: numpy lexsort brute force; width/order/-1 invariants;
+                   the short-context closed form [VLLM, _fill_short_context_topk_indices].
+  select_blocks    pinned: numpy brute force; ctb >= nb keeps every reachable block.
+  yarn_cos_sin     pinned for factor 1 (plain RoPE); the YaRN constants
+                   themselves are parity unpinned (the pages name them only).
+  publish          pinned: pre-quantisation key vs a float64 restatement within
+                   bf16 rounding; RoPE identity at position 0; norm preservation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-D_GNU_SOURCE", _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, f32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
+        L.orc_fp4_quant_rows.argtypes = [P, i64, P, P]
+        L.orc_fp4_quant_rows.restype = None
+        L.orc_head_dots.argtypes = [P, P, i64, i32, i32, i32, i32, P]
+        L.orc_head_dots.restype = i64
+        L.orc_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, i32, i32, P, i64]
+        L.orc_score.restype = i64
+        L.orc_topk.argtypes = [P, i64, i32, i32, P, i32, ctypes.c_int32, P, i64]
+        L.orc_topk.restype = None
+        L.orc_select_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64]
+        L.orc_select_blocks.restype = None
+        L.orc_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
+        L.orc_yarn_cos_sin.restype = None
+        L.orc_publish.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, P, i64, P]
+        L.orc_publish.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# ----------------------------------------------------------------- quantiser
+def fp4_quant_rows(x_bf16: np.ndarray):
+    """[IDX, forward: fp4_act_quant]; [CMP, fp4_quant_e8m0_inplace].
+
+    x_bf16: uint16 [..., 128] bf16 bit patterns.  Returns (rows uint8
+    [..., 68], roundtrip uint16 [..., 128])."""
+    x = _c(x_bf16, np.uint16)
+    assert x.shape[-1] == 128
+    n = x.size // 128
+    rows = np.empty(x.shape[:-1] + (68,), np.uint8)
+    rt = np.empty_like(x)
+    lib().orc_fp4_quant_rows(_p(x), n, _p(rows), _p(rt))
+    return rows, rt
+
+
+# ---------------------------------------------------------------- scoring
+def head_dots(q, kc, B, S, H, T):
+    """Exact per-head dots d[r][h][t] (fp32).  q uint16 [R][H][128], kc uint8
+    [B][Tcap][68].  Returns (d, inexact_count)."""
+    q = _c(q, np.uint16)
+    kc = _c(kc, np.uint8)
+    kstride = kc.shape[1]
+    d = np.empty((B * S, H, T), np.float32)
+    inexact = lib().orc_head_dots(_p(q), _p(kc), kstride, B, S, H, T, _p(d))
+    return d, inexact
+
+
+def score(q, w, kc, B, S, H, T, cl, cand=None, cbs=0):
+    """[IDX, forward: index_score with relu, weights, head sum, masks].
+
+    Returns (scores float32 [R][T] with every t < T defined, inexact_count)."""
+    q = _c(q, np.uint16)
+    w = _c(w, np.uint16)
+    kc = _c(kc, np.uint8)
+    cl = _c(cl, np.int32)
+    R = B * S
+    assert q.shape[:2] == (R, H) and w.shape == (R, H) and cl.shape == (R,)
+    kstride = kc.shape[1]
+    n_cand = 0
+    if cand is not None:
+        cand = _c(cand, np.int32)
+        n_cand = cand.shape[1]
+    out = np.empty((R, T), np.float32)
+    inexact = lib().orc_score(_p(q), _p(w), _p(kc), kstride, B, S, H, T, _p(cl), _p(cand),
+                              n_cand, cbs, _p(out), T)
+    return out, inexact
+
+
+# ------------------------------------------------------------------- top-k
+def topk(scores, cl, k, offset=0, T=None):
+    """[IDX, forward: top-k, position re-sort, -1 and offset]."""
+    scores = _c(scores, np.float32)
+    cl = _c(cl, np.int32)
+    R = scores.shape[0]
+    T = scores.shape[1] if T is None else T
+    kout = min(k, T)
+    out = np.empty((R, kout), np.int32)
+    lib().orc_topk(_p(scores), scores.shape[1], R, T, _p(cl), k, offset, _p(out), kout)
+    return out
+
+
+def select_blocks(scores, cl, ctb, cbs, T=None):
+    """[IDX, forward: select_candidate_blocks] (body not on the pages; block
+    max reading)."""
+    scores = _c(scores, np.float32)
+    cl = _c(cl, np.int32)
+    R = scores.shape[0]
+    T = scores.shape[1] if T is None else T
+    nb = (T + cbs - 1) // cbs
+    kk = min(ctb, nb)
+    ids = np.empty((R, kk), np.int32)
+    lib().orc_select_blocks(_p(scores), scores.shape[1], R, T, _p(cl), ctb, cbs, _p(ids), kk)
+    return ids
+
+
+# ---------------------------------------------------------------- publish
+def yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):
+    out = np.empty((P, rd // 2, 2), np.float32)
+    lib().orc_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow, _p(out))
+    return out
+
+
+def publish(latent, wk, gamma, cos_sin, start_pos, ratio, eps, kc, rd=64):
+    """[IDX, forward: index-key publish].  latent uint16 [B][G][Din], wk
+    uint16 [128][Din], gamma float32 [128], cos_sin float32 [P][rd/2][2],
+    kc uint8 [B][Tcap][68] updated in place.  Returns the pre-quantisation
+    keys uint16 [B][G][128]."""
+    latent = _c(latent, np.uint16)
+    wk = _c(wk, np.uint16)
+    gamma = _c(gamma, np.float32)
+    cos_sin = _c(cos_sin, np.float32)
+    assert kc.flags.c_contiguous and kc.dtype == np.uint8
+    B, G, Din = latent.shape
+    pre = np.empty((B, G, 128), np.uint16)
+    lib().orc_publish(_p(latent), _p(wk), _p(gamma), _p(cos_sin), cos_sin.shape[0], B, G, Din, rd,
+                      eps, start_pos, ratio, _p(kc), kc.shape[1], _p(pre))
+    return pre
+
+
+# ------------------------------------------------- tiny numpy brute force
+def topk_bruteforce(scores_row: np.ndarray, cl: int, k: int, offset: int = 0) -> np.ndarray:
+    """Independent restatement for tiny rows: a full lexsort by (-score, t)."""
+    T = scores_row.shape[0]
+    t = np.arange(T)
+    s = np.where(t < cl, scores_row.astype(np.float64), -np.inf)
+    s = np.where(s == 0.0, 0.0, s)  # -0 ties with +0
+    order = np.lexsort((t, -s))[: min(k, T)]
+    order = np.sort(order)
+    return np.where(order < cl, order + offset, -1).astype(np.int32)
+
+
+def select_blocks_bruteforce(scores_row, cl, ctb, cbs):
+    T = scores_row.shape[0]
+    c = min(cl, T)
+    nb = (T + cbs - 1) // cbs
+    s = np.where(np.arange(T) < c, scores_row.astype(np.float64), -np.inf)
+    bm = np.array([s[j * cbs: min((j + 1) * cbs, T)].max() for j in range(nb)])
+    return topk_bruteforce(bm, (c + cbs - 1) // cbs, ctb, 0)
