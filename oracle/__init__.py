@@ -125,7 +125,7 @@ def score(q, w, kc, B, S, H, T, cl, cand=None, cbs=0):
     kc = _c(kc, np.uint8)
     cl = _c(cl, np.int32)
     R = B * S
-    assert q.shape[:2] == (R, H) and w.shape == (R, H) and cl.shape == (R,)
+    assert q.shape[:2] == (R, H) and w.shape == (R, H) and cl.shape == (R,) and H <= 1024
     kstride = kc.shape[1]
     n_cand = 0
     if cand is not None:

@@ -271,17 +271,16 @@ int64_t orc_score(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64
                   float *scores, int64_t ld)
 {
     int64_t R = (int64_t)B * S, inexact_total = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(+ : inexact_total)
+    decoded_row *dq = (decoded_row *)malloc(sizeof(decoded_row) * (size_t)H);
     for (int64_t r = 0; r < R; ++r) {
         int64_t b = r / S;
-        decoded_row *dq = (decoded_row *)malloc(sizeof(decoded_row) * (size_t)H);
-        float *dh = (float *)malloc(sizeof(float) * (size_t)H);
         for (int h = 0; h < H; ++h) {
             uint8_t qrow[ROW_BYTES];
             quant_row(q + (r * H + h) * HEAD_DIM, qrow, NULL);
             decode_row(qrow, &dq[h]);
         }
         int64_t inexact = 0;
+#pragma omp parallel for schedule(static) reduction(+ : inexact)
         for (int t = 0; t < T; ++t) {
             float *out = &scores[r * ld + t];
             if (t >= cl[r]) {
@@ -294,6 +293,7 @@ int64_t orc_score(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64
             }
             decoded_row dk;
             decode_row(kc + (b * kstride + t) * ROW_BYTES, &dk);
+            float dh[1024];
             for (int h = 0; h < H; ++h)
                 dh[h] = exact_dot(&dq[h], &dk, &inexact);
             float acc = 0.0f;
@@ -302,9 +302,8 @@ int64_t orc_score(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64
             *out = acc + 0.0f;
         }
         inexact_total += inexact;
-        free(dq);
-        free(dh);
     }
+    free(dq);
     return inexact_total;
 }
 
