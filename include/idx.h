@@ -1,0 +1,197 @@
+/*
+ * idx.h -- C ABI of the MI355X (gfx950) DeepSeek-V4.1 Indexer hot path.
+ *
+ * The operations follow the Indexer as stated on three web pages, cited by
+ * page and section:
+ *   [IDX]  "DeepSeek V4.1" -- class Indexer, forward (atlas.klimoza.dev,
+ *          models/deepseek-v4.1 .../attention/indexer/index-keys)
+ *   [CMP]  "Module compress" -- API docs of a CPU reference
+ *          (docs.atlascybernetics.ai, spark_model/layers/deepseek_v41_ref/compress)
+ *   [VLLM] "launcher/docker-images/dsv41-flash/patches/attention.py" -- vLLM
+ *          DeepseekV4 attention patch (git.kilork.org)
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates device memory and keeps no state between calls.
+ *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *   - stream is a hipStream_t (NULL = the default stream); every launch is
+ *     asynchronous on it and calls on one stream run in call order.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation failure nothing is launched and IDX_EINVAL /
+ *     IDX_EUNSUPPORTED is returned.  IDX_EHIP reports a launch error.
+ *     Values inside device arrays (compress_lens, candidate ids) are read on
+ *     the device and clamped as documented; they cannot be validated on the
+ *     host without a synchronisation.
+ *   - Inputs must be finite; block maxima of at most 2^120 keep every
+ *     dequantised value finite.  NaN or Inf inputs give unspecified results.
+ *
+ * fp4 key row (68 bytes, [VLLM, _indexer_k_cache_head_dim] fixes the size):
+ *   bytes 0..63  the 128 e2m1 codes, two per byte, element 2i in the low
+ *                nibble of byte i (bit 3 of a code = sign);
+ *   bytes 64..67 the e8m0 exponents e_j + 127 of blocks j = 0..3 (32 values
+ *                each).  Element i dequantises to code_value * 2^e_(i/32).
+ * A key cache is [B][Tcap][68] bytes: sequence b's rows are contiguous and
+ * start at byte b * k_batch_stride_rows * 68.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IDX_OK = 0,
+    IDX_EINVAL = 1,       /* bad pointer, size or shape */
+    IDX_EUNSUPPORTED = 2, /* valid but not implemented (e.g. index_head_dim != 128) */
+    IDX_EHIP = 3          /* a HIP launch failed */
+} idx_status;
+
+/* Human-readable name of a status code (static string). */
+const char *idx_status_string(idx_status s);
+
+/* Library version string (static). */
+const char *idx_version(void);
+
+/*
+ * idx_fp4_quant -- block-32 e2m1 / e8m0 quantise-dequantise of 128-wide rows
+ * ([IDX, forward: fp4_act_quant on q and k]; [CMP, fp4_quant_e8m0_inplace,
+ * to_e2m1_rne]).  Per block of 32 values: amax raised to at least 6*2^-126,
+ * scale 2^e with e the smallest integer such that 6*2^e >= amax, each value
+ * rounded to the nearest e2m1 point of x/2^e with ties to the even code and
+ * its sign kept.
+ *   x          device, [n_rows][128] bf16
+ *   rows68     device, [n_rows][68] output key rows (layout above)
+ *   roundtrip  device, [n_rows][128] bf16 output (dequantised values), or NULL
+ * n_rows >= 0 (0 launches nothing).
+ */
+idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uint16_t *roundtrip,
+                         void *stream);
+
+/*
+ * idx_score -- rectified, weighted head sum of fp4 q against the fp4 keys
+ * ([IDX, forward: the einsum of q and index_k, relu, times weights, sum over
+ * heads, compress_lens mask, level-two candidate mask]).
+ *   scores[r][t] = sum_{h=0..H-1} relu(qhat[r][h] . khat[b][t]) * w[r][h]
+ * with r = b*S + s, qhat the fp4 round trip of q (done in the kernel),
+ * khat the dequantised key row t of sequence b.  The head sum is fp32, heads
+ * ascending, one fused multiply-add per head starting from +0; the dot
+ * products are exact for the documented input range.
+ *   q              device, [B*S][H][D] bf16, RoPE already applied
+ *   w              device, [B*S][H] bf16, weights_proj output already
+ *                  multiplied by D^-0.5 * H^-0.5
+ *   k_cache        device, key rows, sequence stride k_batch_stride_rows >= T
+ *   compress_lens  device, [B*S] int32: row r scores positions t < cl[r]
+ *                  (values clamped to [0, T])
+ *   cand_blocks    device, [B*S][n_cand] int32 block ids (level two), or
+ *                  NULL.  When given, every t < T is first set to -inf and
+ *                  only positions t < cl[r] inside the listed blocks of
+ *                  cand_block_size positions are scored; ids < 0 or
+ *                  >= ceil(T/cand_block_size) are skipped.
+ *   scores         device, [B*S][ld] fp32, ld >= T.  Entries t >= cl[r] are
+ *                  left unspecified without cand_blocks (callers mask by cl).
+ * Requires D == 128 and H in {32, 64}.  T == 0 launches nothing.
+ */
+idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
+                     int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                     const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
+                     int cand_block_size, float *scores, int64_t ld, void *stream);
+
+/*
+ * Bytes of device workspace idx_topk needs for R rows of width T.
+ */
+size_t idx_topk_workspace_size(int R, int T, int index_topk);
+
+/*
+ * idx_topk -- per-row top-k in position order ([IDX, forward: topk of
+ * min(index_topk, end_pos//ratio), sort by position, -1 where not below
+ * compress_lens, plus offset]).  Row r ranks positions t in [0, T) by
+ * (masked score descending, t ascending), where positions t >= cl[r] count
+ * as -inf and -0 equals +0; it keeps the first k_out = min(index_topk, T),
+ * and writes them by ascending t as t + offset when t < cl[r], else -1.
+ * When index_topk >= T the result is the closed form of
+ * [VLLM, _fill_short_context_topk_indices] plus the offset.
+ *   scores         device, [R][ld] fp32
+ *   compress_lens  device, [R] int32 (clamped to [0, T])
+ *   out            device, [R][ld_out] int32, ld_out >= k_out; only the first
+ *                  k_out entries of each row are written
+ *   ws, ws_bytes   device workspace of at least idx_topk_workspace_size bytes
+ *                  (may be NULL when that size is 0)
+ * NaN scores give unspecified results.
+ */
+idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t *compress_lens,
+                    int index_topk, int32_t offset, int32_t *out, int64_t ld_out, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * Bytes of device workspace idx_select_candidate_blocks needs.
+ */
+size_t idx_select_workspace_size(int R, int T, int candidate_topk_blocks, int cand_block_size);
+
+/*
+ * idx_select_candidate_blocks -- level one of the two-level selection
+ * ([IDX, forward: select_candidate_blocks]; [CMP, select_candidate_blocks],
+ * whose body the pages do not give).  Reading implemented here: block j
+ * covers positions [j*cbs, (j+1)*cbs) clipped to T, its score is the maximum
+ * of its scores at positions t < cl[r] (-inf when it has none); the blocks
+ * are ranked like idx_topk with k = candidate_topk_blocks, compress_lens
+ * ceil(cl[r]/cbs) and offset 0.
+ *   scores     device, [R][ld] fp32 (level-one scores)
+ *   block_ids  device, [R][ld_ids] int32, ld_ids >= min(ctb, ceil(T/cbs));
+ *              ascending block ids, -1 for a kept block without reachable
+ *              positions.  The keep mask of the pages is the union of the
+ *              listed blocks.
+ */
+idx_status idx_select_candidate_blocks(const float *scores, int64_t ld, int R, int T,
+                                       const int32_t *compress_lens, int candidate_topk_blocks,
+                                       int cand_block_size, int32_t *block_ids, int64_t ld_ids,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * idx_publish_keys -- index-key publish of a key-owning layer ([IDX,
+ * forward: k = k_norm(wk(latent)), RoPE on the last rope_head_dim dims,
+ * fp4_act_quant, write into k_cache]; [VLLM, DeepseekV4Indexer._produce_k]).
+ * For sequence b and group g:
+ *   y  = wk . latent[b][g]     fp32, one fma per input feature in order,
+ *                              rounded to bf16 (the bf16 Linear output)
+ *   z  = bf16((y * inv) * gamma), inv = 1/sqrt(sum_o y_o^2 / D + eps)
+ *        (sum in order with fma; sqrt and division correctly rounded)
+ *   RoPE on dims [D-rd, D) as interleaved pairs (x0, x1) with (c, s) =
+ *        cos_sin[pos][i]: (x0*c - x1*s, x0*s + x1*c), products and sums
+ *        rounded in fp32, result bf16
+ *   quantise as idx_fp4_quant and write the 68-byte row.
+ * Slots: start_pos == 0 (prefill) puts group g at position g*ratio, row g;
+ * start_pos > 0 (decode, G must be 1) puts the completed group at position
+ * start_pos + 1 - ratio, row start_pos / ratio.
+ *   latent     device, [B][G][Din] bf16
+ *   wk         device, [D][Din] bf16
+ *   gamma      device, [D] fp32 (k_norm weight)
+ *   cos_sin    device, [P][rd/2][2] fp32; every position used must be < P
+ *   k_cache    device, written rows must be < Tcap
+ * Requires D == 128, rd even with 0 <= rd <= D, Din >= 1, ratio >= 1.
+ */
+idx_status idx_publish_keys(const uint16_t *latent, const uint16_t *wk, const float *gamma,
+                            const float *cos_sin, int P, int B, int G, int Din, int D, int rd,
+                            float eps, int start_pos, int ratio, uint8_t *k_cache,
+                            int64_t k_batch_stride_rows, int Tcap, void *stream);
+
+/*
+ * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys
+ * ([CMP, yarn_freqs_cis]; the YaRN method of Peng et al.).  Base inverse
+ * frequency theta^(-2i/rd); with orig_len > 0 and factor != 1 the
+ * frequencies are blended towards base/factor by a linear ramp between the
+ * correction dimensions of beta_fast and beta_slow rotations.  Angles,
+ * cosines and sines in double, stored fp32.
+ *   out  host, [P][rd/2][2] fp32 (cos, sin)
+ */
+idx_status idx_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len,
+                            double beta_fast, double beta_slow, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

@@ -1,0 +1,222 @@
+"""Python binding of the gfx950 DeepSeek-V4.1 Indexer library (libidx.so).
+
+Thin argument marshalling only: every function below checks shapes and
+dtypes of torch tensors, passes their device pointers and the current HIP
+stream to the C ABI declared in include/idx.h, and raises on a non-zero
+status.  All computation happens in the library's HIP kernels.  There is no
+fallback: if libidx.so is missing or fails to load, every call raises.
+
+bf16 tensors may be passed as torch.bfloat16 or as torch.uint16/int16 bit
+patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["idx_fp4_quant", "idx_score", "idx_topk", "idx_topk_workspace_size",
+           "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
+           "idx_yarn_cos_sin", "library_path", "load_library", "IdxError", "ROW_BYTES"]
+
+ROW_BYTES = 68
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libidx.so")
+_lib = None
+
+
+class IdxError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libidx.so (built by sparse_attention_top_fp4_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise IdxError(f"HIP library not built: {_LIB_PATH} is missing "
+                       "(run python -m sparse_attention_top_fp4_amd.build)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+    L.idx_status_string.argtypes = [i32]
+    L.idx_status_string.restype = ctypes.c_char_p
+    L.idx_version.restype = ctypes.c_char_p
+    L.idx_fp4_quant.argtypes = [P, i64, P, P, P]
+    L.idx_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32, P, i64, P]
+    L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
+    L.idx_topk_workspace_size.restype = sz
+    L.idx_topk.argtypes = [P, i64, i32, i32, P, i32, ctypes.c_int32, P, i64, P, sz, P]
+    L.idx_select_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.idx_select_workspace_size.restype = sz
+    L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
+    L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
+                                   i32, P]
+    L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
+    for name in ("idx_fp4_quant", "idx_score", "idx_topk", "idx_select_candidate_blocks",
+                 "idx_publish_keys", "idx_yarn_cos_sin"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().idx_status_string(status).decode()
+        raise IdxError(f"{what}: {msg}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def idx_fp4_quant(x, rows68, roundtrip=None, stream=None):
+    """x [n, 128] bf16 -> rows68 [n, 68] uint8 (+ roundtrip [n, 128] bf16)."""
+    torch = _torch()
+    _dev(x, "x", _bf16_types())
+    _dev(rows68, "rows68", (torch.uint8,))
+    n = x.numel() // 128
+    if x.shape[-1] != 128 or rows68.numel() != n * ROW_BYTES:
+        raise ValueError("x must be [..., 128] and rows68 [..., 68] with the same rows")
+    if roundtrip is not None:
+        _dev(roundtrip, "roundtrip", _bf16_types())
+        if roundtrip.numel() != x.numel():
+            raise ValueError("roundtrip must match x")
+    _check(load_library().idx_fp4_quant(_ptr(x), n, _ptr(rows68), _ptr(roundtrip),
+                                        _stream(stream)), "idx_fp4_quant")
+
+
+def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
+              cand_block_size=0, stream=None):
+    """q [B*S, H, 128] bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8,
+    compress_lens [B*S] int32, scores [B*S, ld] float32 (ld >= T),
+    cand_blocks [B*S, n_cand] int32 or None."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES or scores.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 68] and scores [B*S, ld]")
+    n_cand = 0
+    if cand_blocks is not None:
+        _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+        if cand_blocks.shape[0] != R:
+            raise ValueError("cand_blocks must have B*S rows")
+        n_cand = cand_blocks.shape[1]
+    _check(load_library().idx_score(_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D,
+                                    T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
+                                    cand_block_size, _ptr(scores), scores.shape[1],
+                                    _stream(stream)), "idx_score")
+
+
+def idx_topk_workspace_size(R, T, index_topk) -> int:
+    return int(load_library().idx_topk_workspace_size(R, T, index_topk))
+
+
+def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, stream=None):
+    """scores [R, ld] float32, compress_lens [R] int32, out [R, ld_out] int32
+    (ld_out >= min(index_topk, T)).  workspace: uint8 device tensor of at
+    least idx_topk_workspace_size bytes, allocated here when None."""
+    torch = _torch()
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    R = scores.shape[0]
+    need = idx_topk_workspace_size(R, T, index_topk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().idx_topk(_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
+                                   index_topk, offset, _ptr(out), out.shape[1], _ptr(workspace),
+                                   wsb, _stream(stream)), "idx_topk")
+
+
+def idx_select_workspace_size(R, T, ctb, cbs) -> int:
+    return int(load_library().idx_select_workspace_size(R, T, ctb, cbs))
+
+
+def idx_select_candidate_blocks(scores, T, compress_lens, candidate_topk_blocks,
+                                cand_block_size, block_ids, workspace=None, stream=None):
+    torch = _torch()
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(block_ids, "block_ids", (torch.int32,), 2)
+    R = scores.shape[0]
+    need = idx_select_workspace_size(R, T, candidate_topk_blocks, cand_block_size)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().idx_select_candidate_blocks(
+        _ptr(scores), scores.shape[1], R, T, _ptr(compress_lens), candidate_topk_blocks,
+        cand_block_size, _ptr(block_ids), block_ids.shape[1], _ptr(workspace), wsb,
+        _stream(stream)), "idx_select_candidate_blocks")
+
+
+def idx_publish_keys(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache, rd=64,
+                     stream=None):
+    """latent [B, G, Din] bf16, wk [128, Din] bf16, gamma [128] float32,
+    cos_sin [P, rd/2, 2] float32, k_cache [B', Tcap, 68] uint8 (B' >= B)."""
+    torch = _torch()
+    _dev(latent, "latent", _bf16_types(), 3)
+    _dev(wk, "wk", _bf16_types(), 2)
+    _dev(gamma, "gamma", (torch.float32,), 1)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    B, G, Din = latent.shape
+    D = wk.shape[0]
+    if wk.shape[1] != Din or gamma.shape[0] != D or k_cache.shape[0] < B:
+        raise ValueError("shape mismatch in idx_publish_keys")
+    _check(load_library().idx_publish_keys(_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin),
+                                           cos_sin.shape[0], B, G, Din, D, rd, eps, start_pos,
+                                           ratio, _ptr(k_cache), k_cache.shape[1],
+                                           k_cache.shape[1], _stream(stream)), "idx_publish_keys")
+
+
+def idx_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):
+    """Host table [P, rd/2, 2] float32 (numpy) for idx_publish_keys."""
+    import numpy as np
+    out = np.empty((P, rd // 2, 2), np.float32)
+    _check(load_library().idx_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow,
+                                           out.ctypes.data_as(ctypes.c_void_p)),
+           "idx_yarn_cos_sin")
+    return out

@@ -1,0 +1,130 @@
+// idx_common.hpp -- device helpers shared by the gfx950 kernels of the
+// DeepSeek-V4.1 Indexer hot path: bf16 conversion, the block-32 e2m1/e8m0
+// quantiser, order-preserving score keys, and wave/block scans.
+//
+// Pages cited by page and section: [IDX] "DeepSeek V4.1" (class Indexer),
+// [CMP] "Module compress" (CPU reference API), [VLLM] the vLLM
+// "attention.py" patch (DeepseekV4Indexer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/idx.h"
+
+namespace idx {
+
+constexpr int kHeadDim = 128;   // index_head_dim
+constexpr int kRowBytes = 68;   // [VLLM, _indexer_k_cache_head_dim]: 64 code bytes + 4 scale bytes
+constexpr int kBlock = 32;      // values per e8m0 scale
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;  // order key of -inf
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round a finite fp32 to bf16, nearest-even.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------- quantiser
+// [CMP, fp4_quant_e8m0_inplace]: the scale is the power-of-two ceiling of
+// amax/6 with amax raised to at least 6*2^-126.  Writing the (normal) amax as
+// m*2^E with m in [1,2): 6*2^e >= m*2^E  <=>  e >= E-2 + log2(m/1.5), so the
+// ceiling is e = E-2 when m <= 1.5 and E-1 otherwise.  Exact, no division.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const float a = fmaxf(amax, 0x1.8p-124f);  // 6 * 2^-126
+  const uint32_t u = __float_as_uint(a);
+  const int E = (int)(u >> 23) - 127;
+  return E - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+}
+
+// [CMP, to_e2m1_rne]: magnitude code of y = |x|/2^e on the grid
+// {0,.5,1,1.5,2,3,4,6} (codes 0..7), ties to the even code.  The midpoints
+// 0.25 1.25 2.5 5 go down to an even code and 0.75 1.75 3.5 go up to one.
+__device__ __forceinline__ uint32_t e2m1_magnitude_code(float y) {
+  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+         (uint32_t)(y > 5.0f);
+}
+
+// Quantise 32 bf16 values packed two per word (element 2i in the low half of
+// word i).  Returns e; codes[j] holds elements 8j..8j+7, element 8j+m in
+// nibble m, so the four words are bytes 16*block.. of the 68-byte row.
+__device__ __forceinline__ int quant_block32(const uint32_t (&xp)[16], uint32_t (&codes)[4]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = fmaxf(amax, fabsf(bf16f(xp[i] & 0xffffu)));
+    amax = fmaxf(amax, fabsf(bf16f(xp[i] >> 16)));
+  }
+  const int e = e8m0_exponent(amax);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 126]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t h = (m & 1) ? (xp[4 * j + m / 2] >> 16) : (xp[4 * j + m / 2] & 0xffffu);
+      const float y = fabsf(bf16f(h)) * inv;  // exact: h has 8 significant bits
+      const uint32_t c = e2m1_magnitude_code(y) | ((h >> 12) & 8u);
+      word |= c << (4 * m);
+    }
+    codes[j] = word;
+  }
+  return e;
+}
+
+// Dequantised bf16 of a code at exponent e (exact: at most 2 significant
+// bits; 0.5 * 2^-126 is a subnormal that fp32 and bf16 both hold).
+__device__ __forceinline__ uint32_t e2m1_dequant_bf16(uint32_t code, int e) {
+  const uint32_t m = code & 7u;
+  // twice the grid value: 0 1 2 3 4 6 8 12
+  const uint32_t tw = m < 4u ? m : (m == 4u ? 4u : (m == 5u ? 6u : (m == 6u ? 8u : 12u)));
+  const float half_scale = __uint_as_float((uint32_t)(127 + e) << 23) * 0.5f;  // 2^(e-1)
+  const float v = (float)tw * half_scale;
+  return f32_to_bf16((code & 8u) ? -v : v);
+}
+
+// ---------------------------------------------------------- score keys
+// Order-preserving key of a score: larger score -> larger key; -0 maps to +0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------ wave/block scans
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// number of lanes below this one with the predicate set
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+}  // namespace idx
+
+// ------------------------------------------------------- host helpers
+namespace idx_host {
+inline idx_status launch_status() {
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
+}
+}  // namespace idx_host

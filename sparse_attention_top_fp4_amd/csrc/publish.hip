@@ -1,0 +1,163 @@
+// publish.hip -- index-key publish of a key-owning Indexer layer
+// ([IDX, forward: k = k_norm(wk(latent)), RoPE on the last rope_head_dim
+// dims at the group's position, fp4 round trip, store at start_pos // ratio];
+// [VLLM, DeepseekV4Indexer._produce_k / indexer_k_norm_rope_store]).
+//
+// One workgroup of 128 threads per (sequence, group); thread o owns output
+// feature o.  Every floating-point step has a fixed order and explicit
+// rounding (the library is built with -ffp-contract=off):
+//   y_o  = bf16(sum_i fma(wk[o][i], latent[i]))      i ascending, from +0
+//   ss   = sum_o fma(y_o, y_o)                        o ascending, from +0
+//   inv  = 1 / sqrt(ss / 128 + eps)                   correctly rounded
+//   z_o  = bf16((y_o * inv) * gamma_o)
+//   RoPE on interleaved pairs of the last rd dims: (x0*c - x1*s, x0*s + x1*c)
+//   then the block-32 e2m1/e8m0 quantiser and the 68-byte row store.
+// Tiny and latency-bound (one row per sequence in decode); it must run
+// before the score of the same step reads the cache, which the caller gets
+// by issuing both on one stream.
+#include "idx_common.hpp"
+
+#include <math.h>
+
+namespace idx {
+
+__global__ __launch_bounds__(128) void publish_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
+    const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
+    int start_pos, int ratio, int G, uint8_t* __restrict__ kc, int64_t kstride) {
+  extern __shared__ uint16_t lat_s[];  // Din bf16
+  __shared__ float y_s[kHeadDim];
+  __shared__ uint32_t z_s[kHeadDim];
+  __shared__ float inv_s;
+  const int bg = blockIdx.x;
+  const int b = bg / G, g = bg % G;
+  const int pos = start_pos == 0 ? g * ratio : start_pos + 1 - ratio;
+  const int row = start_pos == 0 ? g : start_pos / ratio + g;
+  const int o = threadIdx.x;
+
+  for (int i = o; i < Din; i += kHeadDim) lat_s[i] = latent[(int64_t)bg * Din + i];
+  __syncthreads();
+
+  const uint16_t* wrow = wk + (int64_t)o * Din;
+  float acc = 0.0f;
+  for (int i = 0; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
+  y_s[o] = bf16f(f32_to_bf16(acc));
+  __syncthreads();
+
+  if (o == 0) {
+    float ss = 0.0f;
+    for (int i = 0; i < kHeadDim; ++i) ss = __builtin_fmaf(y_s[i], y_s[i], ss);
+    const float mean = ss / (float)kHeadDim;
+    inv_s = 1.0f / sqrtf(mean + eps);
+  }
+  __syncthreads();
+  float v = y_s[o] * inv_s;
+  v = v * gamma[o];
+  z_s[o] = f32_to_bf16(v);
+  __syncthreads();
+
+  const int base = kHeadDim - rd;
+  uint32_t r0 = 0, r1 = 0;
+  const bool lead = o >= base && ((o - base) & 1) == 0;
+  if (lead) {
+    const int i = (o - base) >> 1;
+    const float x0 = bf16f(z_s[o]), x1 = bf16f(z_s[o + 1]);
+    const float c = cos_sin[((int64_t)pos * (rd / 2) + i) * 2];
+    const float s = cos_sin[((int64_t)pos * (rd / 2) + i) * 2 + 1];
+    const float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
+    r0 = f32_to_bf16(a - bb);
+    r1 = f32_to_bf16(cc + dd);
+  }
+  __syncthreads();
+  if (lead) {
+    z_s[o] = r0;
+    z_s[o + 1] = r1;
+  }
+  __syncthreads();
+
+  if (o < 4) {
+    uint32_t xp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = z_s[32 * o + 2 * i] | (z_s[32 * o + 2 * i + 1] << 16);
+    uint32_t codes[4];
+    const int e = quant_block32(xp, codes);
+    uint8_t* dst = kc + ((int64_t)b * kstride + row) * kRowBytes;
+    uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
+    dst[64 + o] = (uint8_t)(e + 127);
+  }
+}
+
+}  // namespace idx
+
+extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* wk,
+                                       const float* gamma, const float* cos_sin, int P, int B,
+                                       int G, int Din, int D, int rd, float eps, int start_pos,
+                                       int ratio, uint8_t* k_cache, int64_t k_batch_stride_rows,
+                                       int Tcap, void* stream) {
+  if (B < 0 || G < 0 || Din <= 0 || D <= 0 || ratio <= 0 || start_pos < 0 || P < 0 || Tcap < 0)
+    return IDX_EINVAL;
+  if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
+  if (rd < 0 || rd > D || (rd & 1)) return IDX_EINVAL;
+  if (!(eps >= 0.0f)) return IDX_EINVAL;
+  if ((int64_t)B * G == 0) return IDX_OK;
+  if (!latent || !wk || !gamma || !k_cache || (rd > 0 && !cos_sin)) return IDX_EINVAL;
+  if (k_batch_stride_rows < Tcap) return IDX_EINVAL;
+  int64_t max_pos, max_row;
+  if (start_pos == 0) {
+    max_pos = (int64_t)(G - 1) * ratio;
+    max_row = G - 1;
+  } else {
+    if (G != 1) return IDX_EINVAL;
+    max_pos = (int64_t)start_pos + 1 - ratio;
+    if (max_pos < 0) return IDX_EINVAL;
+    max_row = start_pos / ratio;
+  }
+  if (rd > 0 && max_pos >= P) return IDX_EINVAL;
+  if (max_row >= Tcap) return IDX_EINVAL;
+  if ((int64_t)B * G > 0x7fffffffLL) return IDX_EINVAL;
+  if ((size_t)Din * 2 > 60 * 1024) return IDX_EUNSUPPORTED;
+  hipLaunchKernelGGL(idx::publish_kernel, dim3((unsigned)(B * G)), dim3(idx::kHeadDim),
+                     (size_t)Din * 2, (hipStream_t)stream, latent, wk, gamma, cos_sin, Din, rd, eps,
+                     start_pos, ratio, G, k_cache, k_batch_stride_rows);
+  return idx_host::launch_status();
+}
+
+// Host-side YaRN RoPE table (the YaRN method of Peng et al.): base inverse
+// frequencies theta^(-2i/rd); with orig_len > 0 and factor != 1 the
+// frequency of dimension pair i is blended towards base/factor by a linear
+// ramp that is 0 below the correction dimension of beta_fast rotations and
+// 1 above that of beta_slow rotations over the original context length.
+extern "C" idx_status idx_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len,
+                                       double beta_fast, double beta_slow, float* out) {
+  if (P < 0 || rd <= 0 || (rd & 1) || !(theta > 1.0) || !(factor > 0.0) || orig_len < 0)
+    return IDX_EINVAL;
+  if (P == 0) return IDX_OK;
+  if (!out) return IDX_EINVAL;
+  const int half = rd / 2;
+  double freq[1024];
+  if (half > 1024) return IDX_EUNSUPPORTED;
+  for (int i = 0; i < half; ++i) freq[i] = pow(theta, -(2.0 * i) / rd);
+  if (orig_len > 0 && factor != 1.0) {
+    auto corr_dim = [&](double rotations) {
+      return rd * log((double)orig_len / (rotations * 2.0 * M_PI)) / (2.0 * log(theta));
+    };
+    double lo = floor(corr_dim(beta_fast)), hi = ceil(corr_dim(beta_slow));
+    lo = lo < 0.0 ? 0.0 : lo;
+    hi = hi > half - 1 ? half - 1 : hi;
+    if (hi == lo) hi += 0.001;
+    for (int i = 0; i < half; ++i) {
+      double t = (i - lo) / (hi - lo);
+      t = t < 0.0 ? 0.0 : (t > 1.0 ? 1.0 : t);
+      freq[i] = freq[i] / factor * t + freq[i] * (1.0 - t);
+    }
+  }
+  for (int64_t p = 0; p < P; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)p * freq[i];
+      out[(p * half + i) * 2] = (float)cos(a);
+      out[(p * half + i) * 2 + 1] = (float)sin(a);
+    }
+  return IDX_OK;
+}

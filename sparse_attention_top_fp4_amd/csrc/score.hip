@@ -1,0 +1,299 @@
+// score.hip -- the Indexer score on gfx950 scaled-fp4 MFMA
+// ([IDX, forward: the einsum of fp4 q with index_k, relu, times weights, sum
+// over heads, compress_lens mask, level-two candidate mask]).
+//
+// Work split: one workgroup (4 waves) per (query row r, chunk of key
+// positions).  The workgroup quantises the row's H x 128 bf16 query into LDS
+// (one thread per 32-value block), then each wave walks 64-key tiles:
+//
+//   - the contraction is v_mfma_scale_f32_32x32x64_f8f6f4 with both operands
+//     e2m1 and e8m0 block scales: M = 32 heads, N = 32 keys, K = 64 dims (two
+//     32-value scale blocks, one per half-wave).  A 64-key tile is
+//     2 key tiles x H/32 head tiles x 2 K-steps of MFMA; the key bytes feed
+//     the B operand straight from the 68-byte rows (lane n+32g loads the 16
+//     code bytes of block g of key n, and the block's scale byte).
+//   - query heads are assigned to M rows so that, in the 32x32 accumulator,
+//     lanes 0..31 hold heads [0, H/2) and lanes 32..63 heads [H/2, H) of
+//     their key; one v_permlane32_swap per accumulator register pair then
+//     gives each lane all H heads of one key (lane l: key t0+l).
+//   - each lane runs the head sum in the fixed order: heads ascending, one
+//     fma(max(d, 0), w, acc) per head from +0, then stores one fp32 score.
+//
+// The dot products are exact (integer-valued block sums times powers of two
+// fit fp32 for the documented input range), so the only rounding is the
+// fixed-order head sum, which the oracle performs identically.
+#include "idx_common.hpp"
+
+namespace idx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+struct __attribute__((aligned(4))) u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Head carried by M-row m of head tile ht (32 heads per tile).  The 32x32
+// f32 accumulator gives lane l, register i the row (i/4)*8 + (l/32)*4 + i%4,
+// so rows with bit 2 clear sit in lanes 0..31 and rows with bit 2 set in
+// lanes 32..63; this map makes register i of tile ht hold head 32*ht + i in
+// the low half-wave and 32*ht + 16 + i in the high half-wave.
+__device__ __forceinline__ int head_of_row(int ht, int m) {
+  return ht * 32 + ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+}
+
+constexpr int kMaxCand = 2048;  // candidate blocks per row held in LDS
+
+struct KeyTile {
+  u32x4 c[2][2];   // [key tile][K-step]: 16 code bytes of block 2*step + lane/32
+  uint32_t sc[2];  // [key tile]: the row's four scale bytes
+};
+
+// Virtual position v -> key position, for plain and candidate mode.
+struct PosMap {
+  const int32_t* cand;  // row's candidate block ids (in LDS), or nullptr
+  int cbs;
+  int nblk;   // ceil(T / cbs)
+  int limit;  // positions must be < limit (= clamped compress_lens)
+  int vlim;   // virtual positions must be < vlim
+  __device__ __forceinline__ int pos(int v) const {  // -1 when not scored
+    if (!cand) return v < vlim ? v : -1;  // vlim <= limit
+    if (v >= vlim) return -1;
+    const int j = v / cbs;
+    const int id = cand[j];
+    if (id < 0 || id >= nblk) return -1;
+    const int p = id * cbs + (v - j * cbs);
+    return p < limit ? p : -1;
+  }
+};
+
+// Loads are issued for every lane without branches, so the compiler can keep
+// the next tile's loads in flight while the current tile computes.  A lane
+// without a key reads row 0 of the sequence instead; its MFMA column is then
+// a product of valid codes that is simply not stored (columns of the
+// accumulator depend only on their own key).
+__device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq, const PosMap& pm,
+                                             int v0, int lane) {
+  KeyTile kt;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int p = pm.pos(v0 + 32 * t + (lane & 31));
+    const uint8_t* row = kseq + (int64_t)(p < 0 ? 0 : p) * kRowBytes;
+    kt.c[t][0] = ld16(row + 16 * half);
+    kt.c[t][1] = ld16(row + 32 + 16 * half);
+    kt.sc[t] = *reinterpret_cast<const uint32_t*>(row + 64);
+  }
+  return kt;
+}
+
+// relu on the bit pattern: non-negative floats are non-negative int32s and
+// every negative float (and -0) is a negative int32, so max(bits, 0) is
+// max(x, +0) in one integer instruction (no NaN canonicalisation).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// One 64-key tile: 2 key tiles x HT head tiles x 2 K-steps of MFMA, the
+// half-wave swap, and the fixed-order head sum; lane l scores key v0 + l.
+template <int HT>
+__device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
+                                           const int (&sA)[HT][2], const float (&wf)[32 * HT],
+                                           const PosMap& pm, float* __restrict__ srow, int v0,
+                                           int lane) {
+  float sc = 0.0f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    v16f acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4 c = kt.c[t][s];
+        const v8i B = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const int sB = (int)((kt.sc[t] >> (8 * (2 * s + (lane >> 5)))) & 0xffu);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][s], B, acc[t], 4, 4, 0,
+                                                                 sA[ht][s], 0, sB);
+      }
+    }
+    // low half-wave keeps key tile 0, high half-wave key tile 1:
+    // acc[0] <- heads 32ht + [0,16), acc[1] <- heads 32ht + [16,32) of key v0 + lane
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][i]),
+                                                       __float_as_uint(acc[1][i]), false, false);
+      acc[0][i] = __uint_as_float(sw[0]);
+      acc[1][i] = __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc = __builtin_fmaf(relu_bits(acc[0][i]), wf[32 * ht + i], sc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      sc = __builtin_fmaf(relu_bits(acc[1][i]), wf[32 * ht + 16 + i], sc);
+  }
+  const int p = pm.pos(v0 + lane);
+  if (p >= 0) srow[p] = sc;
+}
+
+template <int HT>
+__global__ __launch_bounds__(256) void score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
+    const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
+    float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+  constexpr int H = 32 * HT;
+  __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
+  __shared__ int32_t cand_s[kMaxCand];
+  const int r = blockIdx.x;
+  const int b = r / S;
+  int limit = cl[r];
+  limit = limit < 0 ? 0 : (limit > T ? T : limit);
+
+  PosMap pm;
+  pm.cand = cand ? cand_s : nullptr;
+  pm.cbs = cbs;
+  pm.nblk = cand ? (T + cbs - 1) / cbs : 0;
+  pm.limit = limit;
+  const int vtotal = cand ? n_cand * cbs : limit;
+  const int vbeg = blockIdx.y * keys_per_wg;
+  const int vend = min(vbeg + keys_per_wg, vtotal);
+  if (vbeg >= vend) return;
+  pm.vlim = vend;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (cand) {
+    for (int i = tid; i < n_cand; i += 256) cand_s[i] = cand[(int64_t)r * n_cand + i];
+    __syncthreads();
+  }
+
+  // --- quantise the query row: thread (h, g) handles block g of head h
+  if (tid < 4 * H) {
+    const int h = tid >> 2, g = tid & 3;
+    const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kHeadDim + 32 * g);
+    uint32_t xp[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      xp[4 * i] = v.x;
+      xp[4 * i + 1] = v.y;
+      xp[4 * i + 2] = v.z;
+      xp[4 * i + 3] = v.w;
+    }
+    uint32_t codes[4];
+    const int e = quant_block32(xp, codes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
+    reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
+  }
+
+  // weights of the row (uniform across the workgroup)
+  float wf[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) wf[h] = bf16f(w[(int64_t)r * H + h]);
+
+  const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
+  const int ntiles = (vend - vbeg + 63) >> 6;
+  int j = wave;
+  KeyTile cur = load_tile(kseq, pm, vbeg + 64 * j, lane);
+
+  __syncthreads();
+
+  // A operands: head tile ht, K-step s -> head head_of_row(ht, lane%32), block 2s + lane/32
+  v8i A[HT][2];
+  int sA[HT][2];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = head_of_row(ht, lane & 31);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = 2 * s + (lane >> 5);
+      const uint32_t* p = qs + h * 17 + 4 * g;
+      A[ht][s] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
+      sA[ht][s] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+    }
+  }
+
+  float* srow = scores + (int64_t)r * ld;
+  // two register sets: compute one tile while the next one loads
+  KeyTile nxt;
+  while (true) {
+    nxt = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
+    score_tile<HT>(cur, A, sA, wf, pm, srow, vbeg + 64 * j, lane);
+    j += 4;
+    if (j >= ntiles) break;
+    cur = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
+    score_tile<HT>(nxt, A, sA, wf, pm, srow, vbeg + 64 * j, lane);
+    j += 4;
+    if (j >= ntiles) break;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* __restrict__ scores, int64_t ld,
+                                                           int T) {
+  const int r = blockIdx.x;
+  for (int t = threadIdx.x; t < T; t += 256) scores[(int64_t)r * ld + t] = -__builtin_inff();
+}
+
+}  // namespace idx
+
+namespace {
+int g_keys_per_wg_override = -1;
+
+int pick_keys_per_wg(int R, int vtotal) {
+  if (g_keys_per_wg_override < 0) {
+    const char* e = getenv("IDX_SCORE_KEYS_PER_WG");
+    g_keys_per_wg_override = e ? atoi(e) : 0;
+  }
+  if (g_keys_per_wg_override > 0) return (g_keys_per_wg_override + 255) / 256 * 256;
+  // aim for several workgroups per CU without splitting rows too finely
+  int kpw = 2048;
+  if (R >= 2048) kpw = vtotal;  // many rows (prefill): one chunk per row
+  if (kpw < 256) kpw = 256;
+  return (kpw + 255) / 256 * 256;
+}
+}  // namespace
+
+extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                                const int32_t* compress_lens, const int32_t* cand_blocks,
+                                int n_cand, int cand_block_size, float* scores, int64_t ld,
+                                void* stream) {
+  if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
+  if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
+  if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
+  if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
+  if (!q || !w || !k_cache || !compress_lens || !scores) return IDX_EINVAL;
+  if (ld < T || k_batch_stride_rows < T) return IDX_EINVAL;
+  if (cand_blocks && (n_cand <= 0 || cand_block_size <= 0)) return IDX_EINVAL;
+  if (cand_blocks && n_cand > idx::kMaxCand) return IDX_EUNSUPPORTED;
+  const int64_t R = (int64_t)B * S;
+  if (R > 0x7fffffffLL) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  int64_t vtotal = T;
+  if (cand_blocks) {
+    vtotal = (int64_t)n_cand * cand_block_size;
+    if (vtotal > 0x7fffffffLL) return IDX_EINVAL;
+  }
+  const int kpw = pick_keys_per_wg((int)(R < 0x7fffffff ? R : 0x7fffffff), (int)vtotal);
+  const int64_t nchunks = (vtotal + kpw - 1) / kpw;
+  if (nchunks > 65535) return IDX_EINVAL;
+  if (cand_blocks) {
+    hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)R), dim3(256), 0, st, scores, ld,
+                       T);
+  }
+  dim3 grid((unsigned)R, (unsigned)nchunks);
+  if (H == 64)
+    hipLaunchKernelGGL(idx::score_kernel<2>, grid, dim3(256), 0, st, q, w, k_cache,
+                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
+                       cand_block_size, scores, ld, kpw);
+  else
+    hipLaunchKernelGGL(idx::score_kernel<1>, grid, dim3(256), 0, st, q, w, k_cache,
+                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
+                       cand_block_size, scores, ld, kpw);
+  return idx_host::launch_status();
+}

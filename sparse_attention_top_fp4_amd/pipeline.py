@@ -1,0 +1,124 @@
+"""One step of the Indexer hot path on device buffers, composed from the C
+ABI calls (argument marshalling and buffer bookkeeping only).
+
+A step follows the Indexer's forward ("DeepSeek V4.1" page, class Indexer):
+  [key publish]  -> score -> [candidate block select -> level-one top-k ->
+  level-two score inside the candidate blocks] -> top-k
+For the two-level workload the level-one layer (the candidate source) keeps
+its own top-k as the Indexer does, and the level-two layer scores with its
+own weights inside the selected blocks.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (idx_fp4_quant, idx_publish_keys, idx_score, idx_select_candidate_blocks,
+               idx_select_workspace_size, idx_topk, idx_topk_workspace_size, idx_yarn_cos_sin)
+from .inputs import YARN
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(a: np.ndarray):
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def quantize_cache(k_bf16_dev):
+    """bf16 keys [B, T, 128] on device -> 68-byte rows [B, T, 68]."""
+    torch = _torch()
+    rows = torch.empty(tuple(k_bf16_dev.shape[:-1]) + (68,), dtype=torch.uint8,
+                       device=k_bf16_dev.device)
+    idx_fp4_quant(k_bf16_dev, rows)
+    return rows
+
+
+class IndexerStep:
+    """Device state of one workload: inputs, the fp4 key cache(s), outputs and
+    workspaces.  ``n_caches`` > 1 keeps several copies of the key cache and
+    cycles through them step by step (benchmarks use it so that consecutive
+    steps do not read keys left in the 256 MB last-level cache)."""
+
+    def __init__(self, wl, inp: dict, n_caches: int = 1):
+        torch = _torch()
+        self.wl = wl
+        R, T = wl.R, wl.T
+        self.q = to_device(inp["q"])
+        self.w = to_device(inp["w"])
+        self.cl = to_device(inp["cl"])
+        k = to_device(inp["k"])
+        self.caches = [quantize_cache(k)]
+        del k
+        for _ in range(1, n_caches):
+            self.caches.append(self.caches[0].clone())
+        self.cur = 0
+        self.scores = torch.empty((R, T), dtype=torch.float32, device="cuda")
+        self.kout = min(wl.topk, T)
+        self.out = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
+        self.topk_ws = self._ws(idx_topk_workspace_size(R, T, wl.topk))
+        self.two_level = bool(wl.ctb)
+        if self.two_level:
+            self.w2 = to_device(inp["w2"])
+            nb = (T + wl.cbs - 1) // wl.cbs
+            self.ids = torch.empty((R, min(wl.ctb, nb)), dtype=torch.int32, device="cuda")
+            self.sel_ws = self._ws(idx_select_workspace_size(R, T, wl.ctb, wl.cbs))
+            self.scores2 = torch.empty((R, T), dtype=torch.float32, device="cuda")
+            self.out_l1 = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
+        self.publish = bool(wl.publish)
+        if self.publish:
+            self.latent = to_device(inp["latent"])
+            self.wk = to_device(inp["wk"])
+            self.gamma = to_device(inp["gamma"])
+            groups = 1 if wl.start_pos > 0 else wl.S // wl.ratio
+            pos_max = (wl.start_pos + 1 - wl.ratio if wl.start_pos > 0
+                       else (groups - 1) * wl.ratio)
+            P = pos_max + 1
+            self.cos_sin = to_device(idx_yarn_cos_sin(P, wl.rd, YARN["theta"], YARN["factor"],
+                                                      YARN["orig_len"], YARN["beta_fast"],
+                                                      YARN["beta_slow"]))
+
+    @staticmethod
+    def _ws(nbytes):
+        torch = _torch()
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device="cuda")
+
+    @property
+    def k_cache(self):
+        return self.caches[self.cur]
+
+    def step(self, stream=None):
+        """Issue one step on the current stream (asynchronous)."""
+        wl = self.wl
+        kc = self.caches[self.cur]
+        if self.publish:
+            idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
+                             wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+        idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores, stream=stream)
+        if self.two_level:
+            idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
+                                        workspace=self.sel_ws, stream=stream)
+            idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
+                     workspace=self.topk_ws, stream=stream)
+            idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
+                      cand_blocks=self.ids, cand_block_size=wl.cbs, stream=stream)
+            idx_topk(self.scores2, wl.T, self.cl, wl.topk, wl.offset, self.out,
+                     workspace=self.topk_ws, stream=stream)
+        else:
+            idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
+                     workspace=self.topk_ws, stream=stream)
+        self.cur = (self.cur + 1) % len(self.caches)
+
+    def keys_scored(self):
+        """Algorithmic (query, key) pairs scored per step."""
+        wl = self.wl
+        cl = np.minimum(wl.compress_lens().astype(np.int64), wl.T)
+        n = int(cl.sum())
+        if self.two_level:
+            n += wl.R * min(wl.ctb * wl.cbs, wl.T)
+        return n

@@ -1,0 +1,118 @@
+"""The C ABI library on the host: it loads, exports every entry point that
+include/idx.h declares, rejects invalid arguments before launching anything,
+and its host-side RoPE table agrees with the oracle's.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_top_fp4_amd as idx
+from sparse_attention_top_fp4_amd.inputs import YARN
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED = 0, 1, 2
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "idx.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(idx.library_path()):
+        from sparse_attention_top_fp4_amd import build
+        build.build()
+    return idx.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = _declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.idx_status_string(code).startswith(b"IDX_")
+
+
+def test_score_rejects_bad_arguments_without_launching(lib):
+    P = ctypes.c_void_p
+    dummy = P(0x1000)  # never dereferenced: validation fails first
+    # D != 128 and unsupported head counts
+    assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 64, 8, dummy, None, 0, 0, dummy, 8,
+                         None) == IDX_EUNSUPPORTED
+    assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 48, 128, 8, dummy, None, 0, 0, dummy, 8,
+                         None) == IDX_EUNSUPPORTED
+    # null pointers, short row stride, short cache stride, bad candidates
+    assert lib.idx_score(None, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
+                         None) == IDX_EINVAL
+    assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 7,
+                         None) == IDX_EINVAL
+    assert lib.idx_score(dummy, dummy, dummy, 7, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
+                         None) == IDX_EINVAL
+    assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, dummy, 0, 128, dummy, 8,
+                         None) == IDX_EINVAL
+    assert lib.idx_score(dummy, dummy, dummy, 8, -1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
+                         None) == IDX_EINVAL
+    # empty work is a no-op, even with null pointers
+    assert lib.idx_score(None, None, None, 0, 0, 1, 64, 128, 8, None, None, 0, 0, None, 8,
+                         None) == IDX_OK
+
+
+def test_topk_and_select_reject_bad_arguments(lib):
+    P = ctypes.c_void_p
+    d = P(0x1000)
+    assert lib.idx_topk(d, 8, 1, 8, d, 0, 0, d, 8, None, 0, None) == IDX_EINVAL  # topk 0
+    assert lib.idx_topk(d, 7, 1, 8, d, 4, 0, d, 8, None, 0, None) == IDX_EINVAL  # ld < T
+    assert lib.idx_topk(d, 8, 1, 8, d, 4, 0, d, 3, None, 0, None) == IDX_EINVAL  # ld_out < k
+    assert lib.idx_topk(None, 8, 0, 8, None, 4, 0, None, 8, None, 0, None) == IDX_OK  # R = 0
+    need = lib.idx_topk_workspace_size(4, 100000, 2048)
+    assert need > 0
+    assert lib.idx_topk(d, 100000, 4, 100000, d, 2048, 0, d, 2048, None, 0, None) == IDX_EINVAL
+    assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 0, 4, d, 2, None, 0, None) == IDX_EINVAL
+    assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 2, 4, d, 1, d, 1 << 20,
+                                           None) == IDX_EINVAL  # ld_ids < min(ctb, nb)
+    assert lib.idx_topk_workspace_size(4, 512, 2048) == 0  # every position kept
+
+
+def test_publish_rejects_bad_arguments(lib):
+    d = ctypes.c_void_p(0x1000)
+    args = dict(P=100, B=1, G=1, Din=512, D=128, rd=64, eps=1e-6, sp=39, ratio=4, stride=64,
+                Tcap=64)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.idx_publish_keys(d, d, d, d, a["P"], a["B"], a["G"], a["Din"], a["D"], a["rd"],
+                                    a["eps"], a["sp"], a["ratio"], d, a["stride"], a["Tcap"], None)
+
+    assert call(D=64) == IDX_EUNSUPPORTED
+    assert call(rd=63) == IDX_EINVAL
+    assert call(G=2) == IDX_EINVAL  # decode publishes one group
+    assert call(P=36) == IDX_EINVAL  # position 36 not in the table
+    assert call(sp=4 * 64 + 3) == IDX_EINVAL  # row 64 beyond Tcap
+    assert call(sp=2) == IDX_EINVAL  # start_pos + 1 - ratio < 0
+    assert call(stride=10) == IDX_EINVAL
+    assert call(B=0) == IDX_OK
+
+
+def test_quant_rejects_bad_arguments(lib):
+    assert lib.idx_fp4_quant(None, -1, None, None, None) == IDX_EINVAL
+    assert lib.idx_fp4_quant(None, 0, None, None, None) == IDX_OK
+    assert lib.idx_fp4_quant(None, 3, None, None, None) == IDX_EINVAL
+
+
+def test_host_rope_table_matches_oracle(lib):
+    for factor, orig in ((YARN["factor"], YARN["orig_len"]), (1.0, 0)):
+        a = idx.idx_yarn_cos_sin(5000, 64, YARN["theta"], factor, orig, YARN["beta_fast"],
+                                 YARN["beta_slow"])
+        b = oracle.yarn_cos_sin(5000, 64, YARN["theta"], factor, orig, YARN["beta_fast"],
+                                YARN["beta_slow"])
+        diff = np.abs(a.astype(np.float64) - b.astype(np.float64))
+        assert diff.max() <= 2.0 ** -24

@@ -1,0 +1,222 @@
+"""GPU parity of every entry point against the CPU oracle, on fuzz-sized
+inputs that span several tiles and ragged tails, plus the edge cases
+(empty rows, compress_lens 0, rows shorter than index_topk, candidate ids
+out of range).  Indices and key rows must be bit-exact; scores must be
+bit-identical (the dot products are exact and both sides run the same
+fixed-order fp32 head sum).  Tolerance for scores written in the test:
+exact, with 1e-2 relative as the reported fallback bound."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_top_fp4_amd.inputs import (YARN, bf16_bits, head_weights, normal_bf16,
+                                                 small_case)
+
+from gpu_util import bits, dev, fp4_cache, host, say, sync, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def idx():
+    import sparse_attention_top_fp4_amd as m
+    m.load_library()
+    return m
+
+
+# ---------------------------------------------------------------- quantiser
+def test_quant_all_bf16_patterns(idx):
+    t = torch()
+    allb = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = allb[(allb & 0x7F80) != 0x7F80]
+    rng = np.random.default_rng(1)
+    shuffled = rng.permutation(finite)
+    blocks = []
+    # every finite value as the maximum of its own block, and in random blocks
+    b0 = np.zeros((len(finite), 32), np.uint16)
+    b0[:, 0] = finite
+    b0[:, 1:] = rng.permutation(finite)[: len(finite)][:, None] & np.uint16(0x807F)  # small values
+    blocks.append(b0)
+    n = len(shuffled) // 32 * 32
+    blocks.append(shuffled[:n].reshape(-1, 32))
+    x = np.concatenate(blocks)
+    x = x[: len(x) // 4 * 4].reshape(-1, 128)
+    say("quant rows", x.shape)
+    rows_ref, rt_ref = oracle.fp4_quant_rows(x)
+    xd = dev(x)
+    rows = t.empty((x.shape[0], 68), dtype=t.uint8, device="cuda")
+    rt = t.empty_like(xd)
+    idx.idx_fp4_quant(xd, rows, rt)
+    sync()
+    assert np.array_equal(host(rows), rows_ref)
+    assert np.array_equal(host(rt, np.uint16), rt_ref)
+
+
+# ------------------------------------------------------------------- score
+SCORE_CASES = [
+    # (seed, B, S, H, T, tcap, start_pos)   start_pos None: decode at end_pos = 4T
+    (1, 1, 1, 64, 512, 512, None),
+    (2, 3, 1, 64, 1000, 1100, None),
+    (3, 2, 5, 32, 300, 300, 1100),
+    (4, 1, 70, 64, 17, 17, 0),
+    (5, 2, 1, 64, 1, 4, None),
+    (6, 4, 1, 32, 4100, 4100, None),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES)
+def test_score_matches_oracle(idx, case):
+    t = torch()
+    seed, B, S, H, T, tcap, sp = case
+    say("score", case)
+    c = small_case(seed, B, S, H, T, start_pos=sp, tcap=tcap)
+    if sp is not None and S == 1:
+        c["cl"][:] = min(T, (sp + 1) // 4)
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref, inexact = oracle.score(c["q"], c["w"], kc_ref, B, S, H, T, c["cl"])
+    assert inexact == 0
+    kc = fp4_cache(c["k"])
+    sync()
+    assert np.array_equal(host(kc), kc_ref)
+    ld = T + 3
+    out = t.full((B * S, ld), float("nan"), dtype=t.float32, device="cuda")
+    idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, S, T, dev(c["cl"]), out)
+    sync()
+    got = host(out)
+    for r in range(B * S):
+        n = min(int(c["cl"][r]), T)
+        assert np.array_equal(bits(got[r, :n]), bits(ref[r, :n])), (r, n)
+        assert np.all(np.isnan(got[r, T:]))  # nothing written past T
+
+
+@pytest.mark.parametrize("cbs,cand_rows", [
+    (128, [[0, 3, 5, 7], [1, 2, -1, 6]]),
+    (48, [[0, 1, 20, 21], [4, 99, 5, 13]]),  # 99 is out of range: skipped
+])
+def test_score_candidates_match_oracle(idx, cbs, cand_rows):
+    t = torch()
+    B, H, T = 2, 64, 1000
+    say("score candidates", cbs, cand_rows)
+    c = small_case(21, B, 1, H, T)
+    c["cl"][:] = [T, 700]
+    cand = np.array(cand_rows, np.int32)
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref_cand = np.where((cand >= 0) & (cand < (T + cbs - 1) // cbs), cand, -1)
+    ref, _ = oracle.score(c["q"], c["w"], kc_ref, B, 1, H, T, c["cl"], cand=ref_cand, cbs=cbs)
+    kc = fp4_cache(c["k"])
+    out = t.zeros((B, T), dtype=t.float32, device="cuda")
+    idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, 1, T, dev(c["cl"]), out,
+                  cand_blocks=dev(cand), cand_block_size=cbs)
+    sync()
+    assert np.array_equal(bits(host(out)), bits(ref))
+
+
+# ------------------------------------------------------------------- top-k
+def _score_rows(rng, R, T, nvals):
+    vals = np.concatenate([rng.standard_normal(nvals).astype(np.float32), [0.0, -0.0, -np.inf]])
+    return vals[rng.integers(0, len(vals), size=(R, T))].astype(np.float32)
+
+
+TOPK_CASES = [
+    # (seed, R, T, k, nvals)
+    (1, 5, 1, 4, 3),
+    (2, 9, 63, 8, 5),
+    (3, 7, 700, 256, 1000),
+    (4, 3, 1024, 1000, 40),
+    (5, 6, 5000, 2048, 100000),
+    (6, 4, 8192, 2048, 7),
+    (7, 3, 20000, 2048, 100000),
+    (8, 2, 32768, 2048, 300),
+    (9, 2, 40000, 2048, 100000),
+    (10, 2, 100000, 2048, 50),
+    (11, 3, 600, 2048, 20),  # every position kept
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES)
+@pytest.mark.parametrize("path", ["auto", "chunked"])
+def test_topk_matches_oracle(idx, case, path, monkeypatch):
+    t = torch()
+    seed, R, T, k, nvals = case
+    if path == "chunked":
+        if T <= 1024:
+            pytest.skip("rows this short always use one workgroup")
+        monkeypatch.setenv("IDX_TOPK_PATH", "chunked")
+    say("topk", case, path)
+    rng = np.random.default_rng(seed)
+    s = _score_rows(rng, R, T, nvals)
+    cl = rng.integers(0, T + 2, size=R).astype(np.int32)
+    cl[0] = T
+    if R > 2:
+        cl[1] = 0
+    off = int(rng.integers(0, 100000))
+    ref = oracle.topk(s, cl, k, off)
+    kout = min(k, T)
+    out = t.full((R, kout + 5), -7, dtype=t.int32, device="cuda")
+    idx.idx_topk(dev(s), T, dev(cl), k, off, out)
+    sync()
+    got = host(out)
+    assert np.array_equal(got[:, :kout], ref)
+    assert np.all(got[:, kout:] == -7)
+
+
+def test_topk_real_score_distribution(idx):
+    """Scores from the score kernel itself (few exact ties, both signs)."""
+    t = torch()
+    B, H, T = 3, 64, 9000
+    say("topk on real scores")
+    c = small_case(31, B, 1, H, T)
+    kc = fp4_cache(c["k"])
+    sc = t.empty((B, T), dtype=t.float32, device="cuda")
+    idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, 1, T, dev(c["cl"]), sc)
+    out = t.empty((B, 2048), dtype=t.int32, device="cuda")
+    idx.idx_topk(sc, T, dev(c["cl"]), 2048, 5, out)
+    sync()
+    assert np.array_equal(host(out), oracle.topk(host(sc), c["cl"], 2048, 5))
+
+
+# ------------------------------------------------------ candidate blocks
+@pytest.mark.parametrize("T,cbs,ctb", [(65536, 128, 64), (1000, 100, 3), (700, 128, 64),
+                                       (5000, 7, 600)])
+def test_select_blocks_matches_oracle(idx, T, cbs, ctb):
+    t = torch()
+    say("select", T, cbs, ctb)
+    rng = np.random.default_rng(T + cbs)
+    R = 4
+    s = rng.standard_normal((R, T)).astype(np.float32)
+    s[:, ::3] = np.round(s[:, ::3])  # ties between block maxima
+    cl = np.array([T, T // 2, 1, 0], np.int32)
+    ref = oracle.select_blocks(s, cl, ctb, cbs)
+    out = t.full((R, ref.shape[1]), -7, dtype=t.int32, device="cuda")
+    idx.idx_select_candidate_blocks(dev(s), T, dev(cl), ctb, cbs, out)
+    sync()
+    assert np.array_equal(host(out), ref)
+
+
+# ------------------------------------------------------------------ publish
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_publish_matches_oracle(idx, mode):
+    t = torch()
+    say("publish", mode)
+    rng = np.random.default_rng(41)
+    B, din, tcap = 4, 512, 300
+    G = 1 if mode == "decode" else 37
+    start_pos = 4 * 250 - 1 if mode == "decode" else 0
+    latent = normal_bf16(rng, (B, G, din))
+    wk = normal_bf16(rng, (128, din), std=0.02)
+    gamma = (1.0 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    P = 1200
+    cs = oracle.yarn_cos_sin(P, 64, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                             YARN["beta_fast"], YARN["beta_slow"])
+    kc0 = rng.integers(0, 256, size=(B, tcap, 68), dtype=np.uint8)
+    kc_ref = kc0.copy()
+    oracle.publish(latent, wk, gamma, cs, start_pos, 4, 1e-6, kc_ref)
+    cs_lib = idx.idx_yarn_cos_sin(P, 64, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                                  YARN["beta_fast"], YARN["beta_slow"])
+    assert np.array_equal(cs_lib, cs)
+    kc = dev(kc0)
+    idx.idx_publish_keys(dev(latent), dev(wk), dev(gamma), dev(cs_lib), start_pos, 4, 1e-6, kc)
+    sync()
+    assert np.array_equal(host(kc), kc_ref)
