@@ -92,14 +92,20 @@ class IndexerStep:
     def k_cache(self):
         return self.caches[self.cur]
 
-    def step(self, stream=None):
-        """Issue one step on the current stream (asynchronous)."""
+    def step(self, stream=None, score_events=None):
+        """Issue one step on the current stream (asynchronous).  score_events:
+        optional (start, end) torch.cuda.Event pair recorded on the stream
+        around the (level-one) score launch."""
         wl = self.wl
         kc = self.caches[self.cur]
         if self.publish:
             idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+        if score_events is not None:
+            score_events[0].record(stream)
         idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores, stream=stream)
+        if score_events is not None:
+            score_events[1].record(stream)
         if self.two_level:
             idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
                                         workspace=self.sel_ws, stream=stream)
