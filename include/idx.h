@@ -93,12 +93,19 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  *                  >= ceil(T/cand_block_size) are skipped.
  *   scores         device, [B*S][ld] fp32, ld >= T.  Entries t >= cl[r] are
  *                  left unspecified without cand_blocks (callers mask by cl).
+ *   key_hist       device, [B*S][2048] uint32, or NULL.  When given it is
+ *                  cleared and then counts, per row, the scores this call
+ *                  wrote by the top 11 bits of their order key (the key maps
+ *                  -0 to +0, then flips negative floats and sets the sign of
+ *                  positive ones).  idx_topk takes it to skip its first pass;
+ *                  positions it does not count are -inf there.
  * Requires D == 128 and H in {32, 64}.  T == 0 launches nothing.
  */
 idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
                      int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                      const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
-                     int cand_block_size, float *scores, int64_t ld, void *stream);
+                     int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
+                     void *stream);
 
 /*
  * Bytes of device workspace idx_topk needs for R rows of width T.
@@ -116,6 +123,9 @@ size_t idx_topk_workspace_size(int R, int T, int index_topk);
  * [VLLM, _fill_short_context_topk_indices] plus the offset.
  *   scores         device, [R][ld] fp32
  *   compress_lens  device, [R] int32 (clamped to [0, T])
+ *   key_hist       device, [R][2048] from idx_score on these scores and
+ *                  compress_lens, or NULL (then the first digit is counted
+ *                  here)
  *   out            device, [R][ld_out] int32, ld_out >= k_out; only the first
  *                  k_out entries of each row are written
  *   ws, ws_bytes   device workspace of at least idx_topk_workspace_size bytes
@@ -123,8 +133,8 @@ size_t idx_topk_workspace_size(int R, int T, int index_topk);
  * NaN scores give unspecified results.
  */
 idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t *compress_lens,
-                    int index_topk, int32_t offset, int32_t *out, int64_t ld_out, void *ws,
-                    size_t ws_bytes, void *stream);
+                    const uint32_t *key_hist, int index_topk, int32_t offset, int32_t *out,
+                    int64_t ld_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Bytes of device workspace idx_select_candidate_blocks needs.

@@ -47,10 +47,10 @@ def load_library():
     L.idx_status_string.restype = ctypes.c_char_p
     L.idx_version.restype = ctypes.c_char_p
     L.idx_fp4_quant.argtypes = [P, i64, P, P, P]
-    L.idx_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32, P, i64, P]
+    L.idx_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32, P, i64, P, P]
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
-    L.idx_topk.argtypes = [P, i64, i32, i32, P, i32, ctypes.c_int32, P, i64, P, sz, P]
+    L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, sz, P]
     L.idx_select_workspace_size.argtypes = [i32, i32, i32, i32]
     L.idx_select_workspace_size.restype = sz
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
@@ -122,10 +122,11 @@ def idx_fp4_quant(x, rows68, roundtrip=None, stream=None):
 
 
 def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
-              cand_block_size=0, stream=None):
+              cand_block_size=0, key_hist=None, stream=None):
     """q [B*S, H, 128] bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8,
     compress_lens [B*S] int32, scores [B*S, ld] float32 (ld >= T),
-    cand_blocks [B*S, n_cand] int32 or None."""
+    cand_blocks [B*S, n_cand] int32 or None, key_hist [B*S, 2048] int32
+    (uint32 counts) or None."""
     torch = _torch()
     _dev(q, "q", _bf16_types(), 3)
     _dev(w, "w", _bf16_types(), 2)
@@ -143,20 +144,26 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
         if cand_blocks.shape[0] != R:
             raise ValueError("cand_blocks must have B*S rows")
         n_cand = cand_blocks.shape[1]
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
     _check(load_library().idx_score(_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
-                                    _stream(stream)), "idx_score")
+                                    _ptr(key_hist), _stream(stream)), "idx_score")
 
 
 def idx_topk_workspace_size(R, T, index_topk) -> int:
     return int(load_library().idx_topk_workspace_size(R, T, index_topk))
 
 
-def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, stream=None):
+def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, key_hist=None,
+             stream=None):
     """scores [R, ld] float32, compress_lens [R] int32, out [R, ld_out] int32
     (ld_out >= min(index_topk, T)).  workspace: uint8 device tensor of at
-    least idx_topk_workspace_size bytes, allocated here when None."""
+    least idx_topk_workspace_size bytes, allocated here when None.
+    key_hist: the [R, 2048] histogram idx_score produced for these scores."""
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)
@@ -166,9 +173,13 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [R, 2048]")
     _check(load_library().idx_topk(_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
-                                   index_topk, offset, _ptr(out), out.shape[1], _ptr(workspace),
-                                   wsb, _stream(stream)), "idx_topk")
+                                   _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
+                                   _ptr(workspace), wsb, _stream(stream)), "idx_topk")
 
 
 def idx_select_workspace_size(R, T, ctb, cbs) -> int:

@@ -40,37 +40,36 @@ __device__ __forceinline__ int e8m0_exponent(float amax) {
   return E - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
 }
 
-// [CMP, to_e2m1_rne]: magnitude code of y = |x|/2^e on the grid
-// {0,.5,1,1.5,2,3,4,6} (codes 0..7), ties to the even code.  The midpoints
-// 0.25 1.25 2.5 5 go down to an even code and 0.75 1.75 3.5 go up to one.
-__device__ __forceinline__ uint32_t e2m1_magnitude_code(float y) {
-  return (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
-         (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
-         (uint32_t)(y > 5.0f);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // Quantise 32 bf16 values packed two per word (element 2i in the low half of
 // word i).  Returns e; codes[j] holds elements 8j..8j+7, element 8j+m in
 // nibble m, so the four words are bytes 16*block.. of the 68-byte row.
+//   amax: the largest |x| as the largest sign-cleared bf16 pattern (the
+//         patterns of non-negative finite values order like their values),
+//         with packed 16-bit max;
+//   codes: [CMP, to_e2m1_rne] -- nearest point of the e2m1 grid
+//         {0,.5,1,1.5,2,3,4,6} to |x|/2^e, ties to the even code (the
+//         midpoints .25 1.25 2.5 5 go down, .75 1.75 3.5 go up), sign kept.
+//         gfx950's scaled bf16->fp4 conversion of x with scale 2^e rounds to
+//         nearest-even and keeps the sign, which is this rule; the GPU tests
+//         check it against the oracle on every finite bf16 at several scales.
 __device__ __forceinline__ int quant_block32(const uint32_t (&xp)[16], uint32_t (&codes)[4]) {
-  float amax = 0.0f;
+  u16x2_t m = __builtin_bit_cast(u16x2_t, xp[0] & 0x7fff7fffu);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    amax = fmaxf(amax, fabsf(bf16f(xp[i] & 0xffffu)));
-    amax = fmaxf(amax, fabsf(bf16f(xp[i] >> 16)));
-  }
-  const int e = e8m0_exponent(amax);
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 126]
+  for (int i = 1; i < 16; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, xp[i] & 0x7fff7fffu));
+  const uint32_t amax_bits = m[0] > m[1] ? m[0] : m[1];
+  const int e = e8m0_exponent(bf16f(amax_bits));
+  const float scale = __uint_as_float((uint32_t)(127 + e) << 23);  // 2^e, e in [-126, 126]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t word = 0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t h = (m & 1) ? (xp[4 * j + m / 2] >> 16) : (xp[4 * j + m / 2] & 0xffffu);
-      const float y = fabsf(bf16f(h)) * inv;  // exact: h has 8 significant bits
-      const uint32_t c = e2m1_magnitude_code(y) | ((h >> 12) & 8u);
-      word |= c << (4 * m);
-    }
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, xp[4 * j + 0]), scale, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, xp[4 * j + 1]), scale, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, xp[4 * j + 2]), scale, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2_t, xp[4 * j + 3]), scale, 3);
     codes[j] = word;
   }
   return e;
@@ -97,14 +96,18 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // ------------------------------------------------------ wave/block scans
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-// inclusive prefix sum over the 64 lanes
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS traffic):
+// Hillis-Steele steps inside each row of 16 lanes (row_shr 1, 2, 4, 8), then
+// row_bcast15 carries each row's total into the next row (rows 1 and 3) and
+// row_bcast31 carries the first half-wave's total into rows 2 and 3.  Lanes
+// whose source is outside the row read 0.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (l >= d) v += o;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 

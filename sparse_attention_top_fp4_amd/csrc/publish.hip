@@ -25,7 +25,7 @@ __global__ __launch_bounds__(128) void publish_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
     const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
     int start_pos, int ratio, int G, uint8_t* __restrict__ kc, int64_t kstride) {
-  extern __shared__ uint16_t lat_s[];  // Din bf16
+  extern __shared__ __attribute__((aligned(16))) uint16_t lat_s[];  // Din bf16
   __shared__ float y_s[kHeadDim];
   __shared__ uint32_t z_s[kHeadDim];
   __shared__ float inv_s;
@@ -35,18 +35,47 @@ __global__ __launch_bounds__(128) void publish_kernel(
   const int row = start_pos == 0 ? g : start_pos / ratio + g;
   const int o = threadIdx.x;
 
+#pragma unroll 4
   for (int i = o; i < Din; i += kHeadDim) lat_s[i] = latent[(int64_t)bg * Din + i];
   __syncthreads();
 
+  // y_o: the row of wk in chunks of 256 values; each chunk's wk loads and
+  // latent reads are issued together before its fixed-order fma chain
   const uint16_t* wrow = wk + (int64_t)o * Din;
   float acc = 0.0f;
-  for (int i = 0; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
+  int i = 0;
+  if ((Din & 7) == 0 && (reinterpret_cast<uintptr_t>(wk) & 15) == 0) {
+    const uint4* w4 = reinterpret_cast<const uint4*>(wrow);
+    const uint4* l4 = reinterpret_cast<const uint4*>(lat_s);
+    for (; i + 256 <= Din; i += 256) {
+      uint4 wv[32], lv[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) wv[j] = w4[i / 8 + j];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) lv[j] = l4[i / 8 + j];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t u[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+        const uint32_t l[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc = __builtin_fmaf(bf16f(u[m] & 0xffffu), bf16f(l[m] & 0xffffu), acc);
+          acc = __builtin_fmaf(bf16f(u[m] >> 16), bf16f(l[m] >> 16), acc);
+        }
+      }
+    }
+  }
+  for (; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
   y_s[o] = bf16f(f32_to_bf16(acc));
   __syncthreads();
 
   if (o == 0) {
+    float yv[kHeadDim];
+#pragma unroll
+    for (int j = 0; j < kHeadDim; ++j) yv[j] = y_s[j];
     float ss = 0.0f;
-    for (int i = 0; i < kHeadDim; ++i) ss = __builtin_fmaf(y_s[i], y_s[i], ss);
+#pragma unroll
+    for (int j = 0; j < kHeadDim; ++j) ss = __builtin_fmaf(yv[j], yv[j], ss);
     const float mean = ss / (float)kHeadDim;
     inv_s = 1.0f / sqrtf(mean + eps);
   }

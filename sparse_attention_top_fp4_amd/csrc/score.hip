@@ -104,7 +104,7 @@ template <int HT>
 __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
                                            const int (&sA)[HT][2], const float (&wf)[32 * HT],
                                            const PosMap& pm, float* __restrict__ srow, int v0,
-                                           int lane) {
+                                           int lane, uint32_t* hist_s) {
   float sc = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -137,7 +137,10 @@ __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT]
       sc = __builtin_fmaf(relu_bits(acc[1][i]), wf[32 * ht + 16 + i], sc);
   }
   const int p = pm.pos(v0 + lane);
-  if (p >= 0) srow[p] = sc;
+  if (p >= 0) {
+    srow[p] = sc;
+    if (hist_s) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
+  }
 }
 
 template <int HT>
@@ -145,9 +148,10 @@ __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
-    float* __restrict__ scores, int64_t ld, int keys_per_wg) {
+    float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg) {
   constexpr int H = 32 * HT;
   __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
+  __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
   __shared__ int32_t cand_s[kMaxCand];
   const int r = blockIdx.x;
   const int b = r / S;
@@ -170,6 +174,10 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int i = tid; i < n_cand; i += 256) cand_s[i] = cand[(int64_t)r * n_cand + i];
     __syncthreads();
   }
+
+  uint32_t* hist_s = key_hist ? hist_lds : nullptr;
+  if (key_hist)
+    for (int i = tid; i < 2048; i += 256) hist_lds[i] = 0;
 
   // --- quantise the query row: thread (h, g) handles block g of head h
   if (tid < 4 * H) {
@@ -198,8 +206,11 @@ __global__ __launch_bounds__(256) void score_kernel(
 
   const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
   const int ntiles = (vend - vbeg + 63) >> 6;
+  // three register sets: while one tile computes, the next two are in flight
   int j = wave;
-  KeyTile cur = load_tile(kseq, pm, vbeg + 64 * j, lane);
+  KeyTile ta = load_tile(kseq, pm, vbeg + 64 * j, lane);
+  KeyTile tb = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
+  KeyTile tc;
 
   __syncthreads();
 
@@ -219,24 +230,40 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
 
   float* srow = scores + (int64_t)r * ld;
-  // two register sets: compute one tile while the next one loads
-  KeyTile nxt;
   while (true) {
-    nxt = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
-    score_tile<HT>(cur, A, sA, wf, pm, srow, vbeg + 64 * j, lane);
+    tc = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
+    score_tile<HT>(ta, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
     j += 4;
     if (j >= ntiles) break;
-    cur = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
-    score_tile<HT>(nxt, A, sA, wf, pm, srow, vbeg + 64 * j, lane);
+    ta = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
+    score_tile<HT>(tb, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
+    j += 4;
+    if (j >= ntiles) break;
+    tb = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
+    score_tile<HT>(tc, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
     j += 4;
     if (j >= ntiles) break;
   }
+  if (key_hist) {
+    __syncthreads();
+    uint32_t* grow = key_hist + (int64_t)r * 2048;
+    for (int i = tid; i < 2048; i += 256)
+      if (hist_lds[i]) atomicAdd(&grow[i], hist_lds[i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_hist_kernel(uint32_t* __restrict__ h, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    h[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* __restrict__ scores, int64_t ld,
                                                            int T) {
-  const int r = blockIdx.x;
-  for (int t = threadIdx.x; t < T; t += 256) scores[(int64_t)r * ld + t] = -__builtin_inff();
+  const int r = blockIdx.y;
+  const int t0 = blockIdx.x * 2048 + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (t0 + 256 * i < T) scores[(int64_t)r * ld + t0 + 256 * i] = -__builtin_inff();
 }
 
 }  // namespace idx
@@ -244,17 +271,20 @@ __global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* __restrict__ s
 namespace {
 int g_keys_per_wg_override = -1;
 
-int pick_keys_per_wg(int R, int vtotal) {
+int pick_keys_per_wg(int64_t R, int vtotal) {
   if (g_keys_per_wg_override < 0) {
     const char* e = getenv("IDX_SCORE_KEYS_PER_WG");
     g_keys_per_wg_override = e ? atoi(e) : 0;
   }
   if (g_keys_per_wg_override > 0) return (g_keys_per_wg_override + 255) / 256 * 256;
-  // aim for several workgroups per CU without splitting rows too finely
-  int kpw = 2048;
-  if (R >= 2048) kpw = vtotal;  // many rows (prefill): one chunk per row
+  // about two resident workgroups per CU over the whole launch (256 CUs), at
+  // least 1024 keys per workgroup so the query quantisation stays amortised
+  const int64_t total = R * (int64_t)vtotal;
+  int64_t kpw = (total + 511) / 512;
+  if (kpw < 1024) kpw = 1024;
+  if (kpw > vtotal) kpw = vtotal;
   if (kpw < 256) kpw = 256;
-  return (kpw + 255) / 256 * 256;
+  return (int)((kpw + 255) / 256 * 256);
 }
 }  // namespace
 
@@ -262,7 +292,7 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                                 int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                                 const int32_t* compress_lens, const int32_t* cand_blocks,
                                 int n_cand, int cand_block_size, float* scores, int64_t ld,
-                                void* stream) {
+                                uint32_t* key_hist, void* stream) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -279,21 +309,27 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
     vtotal = (int64_t)n_cand * cand_block_size;
     if (vtotal > 0x7fffffffLL) return IDX_EINVAL;
   }
-  const int kpw = pick_keys_per_wg((int)(R < 0x7fffffff ? R : 0x7fffffff), (int)vtotal);
+  const int kpw = pick_keys_per_wg(R, (int)vtotal);
   const int64_t nchunks = (vtotal + kpw - 1) / kpw;
   if (nchunks > 65535) return IDX_EINVAL;
   if (cand_blocks) {
-    hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)R), dim3(256), 0, st, scores, ld,
-                       T);
+    if (R > 65535) return IDX_EUNSUPPORTED;
+    hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048), (unsigned)R),
+                       dim3(256), 0, st, scores, ld, T);
+  }
+  if (key_hist) {
+    const int64_t n = R * 2048;
+    const int64_t g = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+    hipLaunchKernelGGL(idx::zero_hist_kernel, dim3((unsigned)g), dim3(256), 0, st, key_hist, n);
   }
   dim3 grid((unsigned)R, (unsigned)nchunks);
   if (H == 64)
     hipLaunchKernelGGL(idx::score_kernel<2>, grid, dim3(256), 0, st, q, w, k_cache,
                        k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                       cand_block_size, scores, ld, kpw);
+                       cand_block_size, scores, ld, key_hist, kpw);
   else
     hipLaunchKernelGGL(idx::score_kernel<1>, grid, dim3(256), 0, st, q, w, k_cache,
                        k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                       cand_block_size, scores, ld, kpw);
+                       cand_block_size, scores, ld, key_hist, kpw);
   return idx_host::launch_status();
 }

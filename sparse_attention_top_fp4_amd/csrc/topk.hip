@@ -6,23 +6,30 @@
 // go to the lower position; positions t >= compress_lens count as -inf.
 //
 // Method: radix select on order-preserving 32-bit keys in three digit passes
-// (bits 31..21, 20..10, 9..0) with LDS histograms, then a compaction in
-// position order.  Each wave owns a contiguous run of positions and visits
-// it in order (element e of lane l is position base + 64e + l), so a wave
-// ballot plus mbcnt gives every selected element its output slot and the
-// result comes out already sorted by position; the threshold ties are taken
-// from the lowest positions by ranking equal keys the same way.
+// (bits 31..21, 20..10, 9..0), then a compaction in position order.
 //
-//  - single-workgroup path: one workgroup per row, the row held in
-//    registers (up to 64*EPT*NW positions);
-//  - multi-workgroup path for long rows: chunks of 4096 positions, the
-//    three histograms and per-chunk counts in a device workspace, one launch
-//    per pass (each workgroup re-derives the earlier thresholds from the
-//    global histograms, so no launch depends on a single-workgroup step).
+// The first digit's histogram usually comes from the score kernel, which
+// counts the top 11 key bits of every score it writes (positions it did not
+// score are -inf in the top-k's view, so their count is T minus the
+// histogram's total).  Given that histogram:
 //
+//  - single-workgroup path (rows up to 32768): the row is loaded once into
+//    registers; elements in the threshold bin are compacted into an LDS list
+//    and the two remaining digits are resolved on that short list; the
+//    selection is then written as two position-ordered bit masks in LDS (keys
+//    above the threshold; keys equal to it), and one thread per 32-position
+//    word turns them into output slots with two block scans, taking equal
+//    keys from the lowest positions.  Comparisons after the threshold search
+//    are done on the float scores (the threshold key maps back to a float;
+//    -0 equals +0 there as in the key order).
+//  - chunked path (longer rows): chunks of 4096 positions over many
+//    workgroups; the remaining digit histograms and per-chunk counts live in
+//    a device workspace, one launch per step, and each workgroup re-derives
+//    the earlier thresholds from the global histograms.
+//
+// Without a score histogram the first digit is histogrammed here as well.
 // Elements equal to -inf (masked positions) are counted with a wave ballot
-// instead of an LDS atomic per element, so heavily masked rows do not
-// serialise on one histogram bin.
+// instead of an LDS atomic per element.
 #include "idx_common.hpp"
 
 #include <stdlib.h>
@@ -31,11 +38,18 @@ namespace idx {
 
 constexpr int kHist1 = 0, kHist2 = 2048, kHist3 = 4096, kCnt = 5120;  // workspace row layout (words)
 constexpr int kChunkNW = 4, kChunkEPT = 16, kChunk = kChunkNW * 64 * kChunkEPT;  // 4096
+constexpr uint32_t kInfBin = kKeyNegInf >> 21;  // first-digit bin of -inf
+constexpr int kCandCap = 4096;                  // LDS candidate list of the single-WG path
 
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
 __device__ __forceinline__ int pass_match_shift(int p) { return p == 0 ? 32 : (p == 1 ? 21 : 10); }
 __device__ __forceinline__ int pass_hist_offset(int p) { return p == 0 ? kHist1 : (p == 1 ? kHist2 : kHist3); }
+
+// Float whose key is k (inverse of score_key for non-NaN keys).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
 
 template <int NT>
 __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wtot) {
@@ -52,31 +66,45 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wt
   return x + add;
 }
 
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
+  constexpr int NW = NT / 64;
+  const uint32_t x = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += wtot[i];
+  __syncthreads();
+  return s;
+}
+
 // Threshold bin of a histogram (LDS or global): the bin b with
-// count(bins > b) < krem <= count(bins >= b).  Returns b and the number of
+// count(bins > b) < krem <= count(bins >= b), where bin `xbin` counts
+// `xcnt` more elements than the array says.  Returns b and the number of
 // elements still to take inside bin b.  Every thread of the block calls it.
 template <int NT>
 __device__ __forceinline__ void select_bin(const uint32_t* hist, int nbins, uint32_t krem,
-                                           uint32_t* sh, uint32_t* wtot, uint32_t& bin,
-                                           uint32_t& krem_out) {
+                                           uint32_t xbin, uint32_t xcnt, uint32_t* sh,
+                                           uint32_t* wtot, uint32_t& bin, uint32_t& krem_out) {
   const int tid = threadIdx.x;
   const int bpt = (nbins + NT - 1) / NT;
   const int hi = nbins - tid * bpt;  // my bins are [lo, hi), scanned from the top
   const int lo = hi - bpt < 0 ? 0 : hi - bpt;
   uint32_t mine = 0;
-  for (int b = hi - 1; b >= lo; --b) mine += hist[b];
+  for (int b = hi - 1; b >= lo; --b) mine += hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
   const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
   const uint32_t excl = incl - mine;
   if (excl < krem && krem <= incl) {
     uint32_t cum = excl;
     for (int b = hi - 1; b >= lo; --b) {
-      const uint32_t c = hist[b];
-      if (cum + c >= krem) {
+      const uint32_t cnt = hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
+      if (cum + cnt >= krem) {
         sh[0] = (uint32_t)b;
         sh[1] = krem - cum;
         break;
       }
-      cum += c;
+      cum += cnt;
     }
   }
   __syncthreads();
@@ -85,13 +113,77 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int nbins, uint
   __syncthreads();
 }
 
-// Adds this block's elements to the LDS histogram of digit `pass`, among
-// elements whose higher digits equal `prefix`.  Element e of a lane is
-// present when 64e + lane < nvalid.  -inf elements are counted into
-// *ninf_sh by ballot.
+// First-digit threshold from a score histogram (already in LDS): positions
+// the histogram does not count (T minus its total) are -inf.
+template <int NT>
+__device__ __forceinline__ void select_first_bin(const uint32_t* h1, int T, uint32_t kout,
+                                                 uint32_t* sh, uint32_t* wtot, uint32_t& bin,
+                                                 uint32_t& krem) {
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < 2048 / NT; ++j) mine += h1[threadIdx.x + j * NT];
+  const uint32_t total = block_sum<NT>(mine, wtot);
+  select_bin<NT>(h1, 2048, kout, kInfBin, (uint32_t)T - total, sh, wtot, bin, krem);
+}
+
+// Copy n (a multiple of NT) words from global memory into LDS, all loads in
+// flight together.
+template <int NT, int N>
+__device__ __forceinline__ void copy_to_lds(uint32_t* dst, const uint32_t* __restrict__ src) {
+  uint32_t tmp[N / NT];
+#pragma unroll
+  for (int j = 0; j < N / NT; ++j) tmp[j] = src[threadIdx.x + j * NT];
+#pragma unroll
+  for (int j = 0; j < N / NT; ++j) dst[threadIdx.x + j * NT] = tmp[j];
+}
+
+__device__ __forceinline__ uint32_t extend_prefix(uint32_t prefix, int pass, uint32_t bin) {
+  return pass == 0 ? bin : ((prefix << (pass == 1 ? 11 : 10)) | bin);
+}
+
+// ------------------------------------------------ register-resident keys
+// Keys of a run of positions; a position past T gets key 0 (the key of a
+// negative NaN, which no supported score produces), so "present" needs no
+// mask of its own.  Every lane loads (past-the-end lanes re-read position
+// T-1), so all loads are in flight together.
 template <int EPT>
-__device__ __forceinline__ void hist_pass(const uint32_t (&key)[EPT], int nvalid, int pass,
-                                          uint32_t prefix, uint32_t* hist, uint32_t* ninf_sh) {
+__device__ __forceinline__ void load_vals(const float* __restrict__ srow, int base, int T,
+                                          float (&v)[EPT]) {
+  const int lane = threadIdx.x & 63;
+  const unsigned last = (unsigned)(T - 1);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const unsigned t = (unsigned)(base + e * 64 + lane);
+    v[e] = srow[t < last ? t : last];
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void vals_to_keys(const float (&v)[EPT], int base, int T, int c,
+                                             uint32_t (&key)[EPT]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int t = base + e * 64 + lane;
+    key[e] = t < T ? (t < c ? score_key(v[e]) : kKeyNegInf) : 0u;
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void load_keys(const float* __restrict__ srow, int base, int T, int c,
+                                          uint32_t (&key)[EPT]) {
+  float v[EPT];
+  load_vals<EPT>(srow, base, T, v);
+  vals_to_keys<EPT>(v, base, T, c, key);
+}
+
+// Adds the block's keys to the LDS histogram of digit `pass`, among keys
+// whose higher digits equal `prefix` (key 0 marks an absent element; it only
+// lands in bin 0 of the first digit, which no supported key reaches).  -inf
+// keys are counted into *ninf_sh by ballot.
+template <int EPT>
+__device__ __forceinline__ void hist_pass(const uint32_t (&key)[EPT], int pass, uint32_t prefix,
+                                          uint32_t* hist, uint32_t* ninf_sh) {
   const int lane = threadIdx.x & 63;
   const int shift = pass_shift(pass), ms = pass_match_shift(pass);
   const uint32_t mask = (uint32_t)pass_bins(pass) - 1u;
@@ -99,60 +191,43 @@ __device__ __forceinline__ void hist_pass(const uint32_t (&key)[EPT], int nvalid
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const uint32_t k = key[e];
-    const bool present = e * 64 + lane < nvalid;
-    const bool match = present && (ms == 32 || (k >> ms) == prefix);
-    const bool isinf = match && k == kKeyNegInf;
+    const bool match = ms == 32 ? k != 0u : (k >> ms) == prefix;
+    const bool isinf = k == kKeyNegInf;
     if (match && !isinf) atomicAdd(&hist[(k >> shift) & mask], 1u);
-    ninf += (uint32_t)__popcll(__ballot(isinf));
+    ninf += (uint32_t)__popcll(__ballot(match && isinf));
   }
   if (lane == 0 && ninf) atomicAdd(ninf_sh, ninf);
 }
 
-template <int EPT>
-__device__ __forceinline__ void load_keys(const float* __restrict__ srow, int base, int T, int c,
-                                          uint32_t (&key)[EPT]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int t = base + e * 64 + lane;
-    key[e] = t < T ? (t < c ? score_key(srow[t]) : kKeyNegInf) : 0u;
-  }
-}
-
 // Histogram one digit of the block's keys into LDS (ready after return).
 template <int NT, int EPT>
-__device__ __forceinline__ void block_hist(const uint32_t (&key)[EPT], int nvalid, int pass,
-                                           uint32_t prefix, uint32_t* hist, uint32_t* ninf_sh) {
+__device__ __forceinline__ void block_hist(const uint32_t (&key)[EPT], int pass, uint32_t prefix,
+                                           uint32_t* hist, uint32_t* ninf_sh) {
   const int nb = pass_bins(pass);
   for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0;
   if (threadIdx.x == 0) *ninf_sh = 0;
   __syncthreads();
-  hist_pass<EPT>(key, nvalid, pass, prefix, hist, ninf_sh);
+  hist_pass<EPT>(key, pass, prefix, hist, ninf_sh);
   __syncthreads();
   if (threadIdx.x == 0 && *ninf_sh) hist[(kKeyNegInf >> pass_shift(pass)) & (uint32_t)(nb - 1)] += *ninf_sh;
   __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t extend_prefix(uint32_t prefix, int pass, uint32_t bin) {
-  return pass == 0 ? bin : ((prefix << (pass == 1 ? 11 : 10)) | bin);
 }
 
 // Writes the selected elements of the block (keys > ustar, and keys ==
 // ustar while their global equal-rank is below need) in position order.
 // out_base / eq_base: selected and equal elements before this block.
 template <int NW, int EPT>
-__device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int nvalid, int base,
+__device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int base,
                                            uint32_t ustar, uint32_t need, uint32_t out_base,
                                            uint32_t eq_base, int c, int32_t offset,
                                            int32_t* __restrict__ orow, uint32_t kout,
                                            uint32_t (*wcnt)[NW]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t gt = 0, eq = 0;
+  uint32_t gt = 0, eq = 0;  // absent elements (key 0) are below any threshold key
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const bool present = e * 64 + lane < nvalid;
-    gt += (uint32_t)__popcll(__ballot(present && key[e] > ustar));
-    eq += (uint32_t)__popcll(__ballot(present && key[e] == ustar));
+    gt += (uint32_t)__popcll(__ballot(key[e] > ustar));
+    eq += (uint32_t)__popcll(__ballot(key[e] == ustar));
   }
   if (lane == 0) {
     wcnt[0][w] = gt;
@@ -168,9 +243,8 @@ __device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int nvali
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const bool present = e * 64 + lane < nvalid;
-    const bool g = present && key[e] > ustar;
-    const bool q = present && key[e] == ustar;
+    const bool g = key[e] > ustar;
+    const bool q = key[e] == ustar;
     const uint64_t qm = __ballot(q);
     const uint32_t qrank = eqb + lanes_below(qm);
     const bool sel = g || (q && qrank < need);
@@ -186,37 +260,186 @@ __device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int nvali
 }
 
 // ------------------------------------------------ single-workgroup path
+// One workgroup per row of at most NW*64*EPT positions; in the compaction,
+// thread i owns the 32-position mask words [i*WPT, (i+1)*WPT).
 template <int NW, int EPT>
-__global__ __launch_bounds__(NW * 64) void topk_row_kernel(const float* __restrict__ scores,
-                                                           int64_t ld, int T,
-                                                           const int32_t* __restrict__ cl_arr,
-                                                           int kout, int32_t offset,
-                                                           int32_t* __restrict__ out,
-                                                           int64_t ld_out) {
-  constexpr int NT = NW * 64, SEG = 64 * EPT;
+__global__ __launch_bounds__(NW * 64) void topk_row_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    const uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
+    int64_t ld_out) {
+  constexpr int NT = NW * 64, SEG = 64 * EPT, NWORDS = NT * EPT / 32;
+  constexpr int WPT = NWORDS / NT;
+  static_assert(WPT * NT == NWORDS && WPT >= 1, "whole mask words per thread");
   __shared__ uint32_t hist[2048];
+  __shared__ uint32_t cand_key[kCandCap];
+  __shared__ uint32_t cand_pos[kCandCap];
+  __shared__ uint32_t gt_mask[NWORDS];
+  __shared__ uint32_t eq_mask[NWORDS];
   __shared__ uint32_t wtot[NW];
   __shared__ uint32_t sh[4];
-  __shared__ uint32_t wcnt[2][NW];
-  const int r = blockIdx.x, w = threadIdx.x >> 6;
+  const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
   const int base = w * SEG;
-  const int nvalid = T - base;
-  uint32_t key[EPT];
-  load_keys<EPT>(scores + (int64_t)r * ld, base, T, c, key);
+  const float* srow = scores + (int64_t)r * ld;
 
-  uint32_t prefix = 0, krem = (uint32_t)kout;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    block_hist<NT, EPT>(key, nvalid, pass, prefix, hist, &sh[2]);
-    uint32_t bin, k2;
-    select_bin<NT>(hist, pass_bins(pass), krem, sh, wtot, bin, k2);
-    prefix = extend_prefix(prefix, pass, bin);
-    krem = k2;
+  // row values: masked positions -inf, positions past T NaN (never selected)
+  float v[EPT];
+  {
+    const unsigned last = (unsigned)(T - 1);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const unsigned t = (unsigned)(base + e * 64 + lane);
+      v[e] = srow[t < last ? t : last];
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int t = base + e * 64 + lane;
+      v[e] = t < T ? (t < c ? v[e] : -__builtin_inff()) : __builtin_nanf("");
+    }
   }
-  block_emit<NW, EPT>(key, nvalid, base, prefix, krem, 0u, 0u, c, offset,
-                      out + (int64_t)r * ld_out, (uint32_t)kout, wcnt);
+
+  // ---- first digit
+  uint32_t b1, krem;
+  bool only_inf = false;
+  if (key_hist) {
+    copy_to_lds<NT, 2048>(hist, key_hist + (int64_t)r * 2048);
+    __syncthreads();
+    select_first_bin<NT>(hist, T, (uint32_t)kout, sh, wtot, b1, krem);
+    // the threshold bin holds only -inf when the scores put nothing in it
+    only_inf = b1 == kInfBin && hist[kInfBin] == 0u;
+    __syncthreads();
+  } else {
+    uint32_t key[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) key[e] = v[e] != v[e] ? 0u : score_key(v[e]);
+    block_hist<NT, EPT>(key, 0, 0u, hist, &sh[2]);
+    select_bin<NT>(hist, 2048, (uint32_t)kout, 0xffffffffu, 0u, sh, wtot, b1, krem);
+  }
+
+  // ---- remaining digits
+  uint32_t ustar;
+  if (only_inf) {
+    ustar = kKeyNegInf;  // the threshold bin holds only -inf: its elements are all equal
+  } else {
+    // compact the threshold bin's elements into LDS
+    const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
+    const bool top = b1 >= 2044u;  // the bin reaches +inf: no upper edge
+    const float hi = top ? 0.0f : key_to_float((b1 + 1u) << 21);
+    // each wave counts its bin elements, one scan over the waves gives every
+    // wave its slot range, then each wave writes its elements in order
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) mine += (uint32_t)__popcll(__ballot(v[e] >= lo && (top || v[e] < hi)));
+    if (lane == 0) wtot[w] = mine;
+    __syncthreads();
+    uint32_t slot = 0, ncand = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t x = wtot[i];
+      slot += i < w ? x : 0u;
+      ncand += x;
+    }
+    __syncthreads();
+    if (ncand <= (uint32_t)kCandCap) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const bool isc = v[e] >= lo && (top || v[e] < hi);
+        const uint64_t m = __ballot(isc);
+        if (isc) {
+          const uint32_t k = slot + lanes_below(m);
+          cand_key[k] = score_key(v[e]);
+          cand_pos[k] = (uint32_t)(base + e * 64 + lane);
+        }
+        slot += (uint32_t)__popcll(m);
+      }
+    }
+    __syncthreads();
+    uint32_t prefix = b1;
+    if (ncand <= (uint32_t)kCandCap) {
+      for (int pass = 1; pass < 3; ++pass) {
+        const int nb = pass_bins(pass), shift = pass_shift(pass), ms = pass_match_shift(pass);
+        for (int i = tid; i < nb; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < ncand; i += NT) {
+          const uint32_t k = cand_key[i];
+          if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t bin, k2;
+        select_bin<NT>(hist, nb, krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
+        prefix = extend_prefix(prefix, pass, bin);
+        krem = k2;
+      }
+    } else {
+      // too many elements in the bin for the LDS list: resolve over registers
+      uint32_t key[EPT];
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) key[e] = v[e] != v[e] ? 0u : score_key(v[e]);
+      for (int pass = 1; pass < 3; ++pass) {
+        block_hist<NT, EPT>(key, pass, prefix, hist, &sh[2]);
+        uint32_t bin, k2;
+        select_bin<NT>(hist, pass_bins(pass), krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
+        prefix = extend_prefix(prefix, pass, bin);
+        krem = k2;
+      }
+    }
+    ustar = prefix;
+  }
+  const uint32_t need = krem;  // elements equal to the threshold still to take
+  const float thr = key_to_float(ustar);
+
+  // ---- position-ordered bit masks of the selection
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint64_t gm = __ballot(v[e] > thr);
+    const uint64_t qm = __ballot(v[e] == thr);
+    if (lane == 0) {
+      const int word = (base + e * 64) >> 5;
+      gt_mask[word] = (uint32_t)gm;
+      gt_mask[word + 1] = (uint32_t)(gm >> 32);
+      eq_mask[word] = (uint32_t)qm;
+      eq_mask[word + 1] = (uint32_t)(qm >> 32);
+    }
+  }
+  __syncthreads();
+
+  // ---- compaction: one scan of packed (above, equal) counts gives every
+  // thread the selected elements before it: all above-threshold ones plus
+  // min(equal ones before it, need)
+  uint32_t gw[WPT], qw[WPT];
+  uint32_t ng = 0, nq = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    gw[j] = gt_mask[tid * WPT + j];
+    qw[j] = eq_mask[tid * WPT + j];
+    ng += (uint32_t)__popc(gw[j]);
+    nq += (uint32_t)__popc(qw[j]);
+  }
+  const uint32_t packed = (ng << 16) | nq;  // block totals are at most 32768
+  const uint32_t excl = block_inclusive_sum<NT>(packed, wtot) - packed;
+  uint32_t qbefore = excl & 0xffffu;
+  uint32_t slot = (excl >> 16) + (qbefore < need ? qbefore : need);
+  int32_t* orow = out + (int64_t)r * ld_out;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const uint32_t qn = (uint32_t)__popc(qw[j]);
+    uint32_t take = need > qbefore ? (need - qbefore < qn ? need - qbefore : qn) : 0u;
+    qbefore += qn;
+    uint32_t bits = gw[j], rest = qw[j];
+    while (take--) {  // the lowest `take` equal positions of this word
+      const uint32_t low = rest & (0u - rest);
+      bits |= low;
+      rest ^= low;
+    }
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int t = (tid * WPT + j) * 32 + b;
+      if (slot < (uint32_t)kout) orow[slot] = t < c ? t + offset : -1;
+      ++slot;
+    }
+  }
 }
 
 // ------------------------------------------------- multi-workgroup path
@@ -225,16 +448,27 @@ __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ 
     p[i] = 0u;
 }
 
-// Re-derive the thresholds of passes [0, npass) from the global histograms.
+// Re-derive the thresholds of passes [0, npass) from the global histograms
+// (the first one from the score histogram when given), each copied into the
+// LDS buffer lh (2048 words) first.
 template <int NT>
-__device__ __forceinline__ void resolve_passes(const uint32_t* __restrict__ wrow, int npass,
-                                               int kout, uint32_t* sh, uint32_t* wtot,
-                                               uint32_t& prefix, uint32_t& krem) {
+__device__ __forceinline__ void resolve_passes(const uint32_t* __restrict__ wrow,
+                                               const uint32_t* __restrict__ h1, int T, int npass,
+                                               int kout, uint32_t* lh, uint32_t* sh,
+                                               uint32_t* wtot, uint32_t& prefix, uint32_t& krem) {
   prefix = 0;
   krem = (uint32_t)kout;
   for (int p = 0; p < npass; ++p) {
     uint32_t bin, k2;
-    select_bin<NT>(wrow + pass_hist_offset(p), pass_bins(p), krem, sh, wtot, bin, k2);
+    if (p == 2)
+      copy_to_lds<NT, 1024>(lh, wrow + pass_hist_offset(p));
+    else
+      copy_to_lds<NT, 2048>(lh, (p == 0 && h1) ? h1 : wrow + pass_hist_offset(p));
+    __syncthreads();
+    if (p == 0 && h1)
+      select_first_bin<NT>(lh, T, krem, sh, wtot, bin, k2);
+    else
+      select_bin<NT>(lh, pass_bins(p), krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
     prefix = extend_prefix(prefix, p, bin);
     krem = k2;
   }
@@ -243,21 +477,25 @@ __device__ __forceinline__ void resolve_passes(const uint32_t* __restrict__ wrow
 template <int PASS>
 __global__ __launch_bounds__(kChunkNW * 64) void topk_chunk_hist_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
-    int kout, uint32_t* __restrict__ ws, int64_t ws_row_words) {
+    const uint32_t* __restrict__ key_hist, int kout, uint32_t* __restrict__ ws,
+    int64_t ws_row_words) {
   constexpr int NT = kChunkNW * 64, SEG = 64 * kChunkEPT;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wtot[kChunkNW];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.y, w = threadIdx.x >> 6;
   uint32_t* wrow = ws + (int64_t)r * ws_row_words;
+  const uint32_t* h1 = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
-  uint32_t prefix, krem;
-  resolve_passes<NT>(wrow, PASS, kout, sh, wtot, prefix, krem);
   const int base = blockIdx.x * kChunk + w * SEG;
+  float v[kChunkEPT];
+  load_vals<kChunkEPT>(scores + (int64_t)r * ld, base, T, v);  // in flight during the resolve
+  uint32_t prefix, krem;
+  resolve_passes<NT>(wrow, h1, T, PASS, kout, hist, sh, wtot, prefix, krem);
   uint32_t key[kChunkEPT];
-  load_keys<kChunkEPT>(scores + (int64_t)r * ld, base, T, c, key);
-  block_hist<NT, kChunkEPT>(key, T - base, PASS, prefix, hist, &sh[2]);
+  vals_to_keys<kChunkEPT>(v, base, T, c, key);
+  block_hist<NT, kChunkEPT>(key, PASS, prefix, hist, &sh[2]);
   const int nb = pass_bins(PASS);
   for (int i = threadIdx.x; i < nb; i += NT)
     if (hist[i]) atomicAdd(&wrow[pass_hist_offset(PASS) + i], hist[i]);
@@ -266,28 +504,32 @@ __global__ __launch_bounds__(kChunkNW * 64) void topk_chunk_hist_kernel(
 // Per chunk: count of keys above the threshold and equal to it.
 __global__ __launch_bounds__(kChunkNW * 64) void topk_chunk_count_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
-    int kout, uint32_t* __restrict__ ws, int64_t ws_row_words) {
+    const uint32_t* __restrict__ key_hist, int kout, uint32_t* __restrict__ ws,
+    int64_t ws_row_words) {
   constexpr int NT = kChunkNW * 64, SEG = 64 * kChunkEPT;
+  __shared__ uint32_t lh[2048];
   __shared__ uint32_t wtot[kChunkNW];
   __shared__ uint32_t sh[4];
   __shared__ uint32_t tot[2];
   const int r = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t* wrow = ws + (int64_t)r * ws_row_words;
+  const uint32_t* h1 = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
-  uint32_t ustar, need;
-  resolve_passes<NT>(wrow, 3, kout, sh, wtot, ustar, need);
   const int base = blockIdx.x * kChunk + w * SEG;
+  float v[kChunkEPT];
+  load_vals<kChunkEPT>(scores + (int64_t)r * ld, base, T, v);
+  uint32_t ustar, need;
+  resolve_passes<NT>(wrow, h1, T, 3, kout, lh, sh, wtot, ustar, need);
   uint32_t key[kChunkEPT];
-  load_keys<kChunkEPT>(scores + (int64_t)r * ld, base, T, c, key);
+  vals_to_keys<kChunkEPT>(v, base, T, c, key);
   if (threadIdx.x < 2) tot[threadIdx.x] = 0;
   __syncthreads();
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < kChunkEPT; ++e) {
-    const bool present = e * 64 + lane < T - base;
-    gt += (uint32_t)__popcll(__ballot(present && key[e] > ustar));
-    eq += (uint32_t)__popcll(__ballot(present && key[e] == ustar));
+    gt += (uint32_t)__popcll(__ballot(key[e] > ustar));
+    eq += (uint32_t)__popcll(__ballot(key[e] == ustar));
   }
   if (lane == 0) {
     atomicAdd(&tot[0], gt);
@@ -302,36 +544,53 @@ __global__ __launch_bounds__(kChunkNW * 64) void topk_chunk_count_kernel(
 
 __global__ __launch_bounds__(kChunkNW * 64) void topk_chunk_emit_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
-    int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out,
-    const uint32_t* __restrict__ ws, int64_t ws_row_words) {
+    const uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
+    int64_t ld_out, const uint32_t* __restrict__ ws, int64_t ws_row_words) {
   constexpr int NT = kChunkNW * 64, SEG = 64 * kChunkEPT;
+  __shared__ uint32_t lh[2048];
   __shared__ uint32_t wtot[kChunkNW];
   __shared__ uint32_t sh[4];
   __shared__ uint32_t wcnt[2][kChunkNW];
   __shared__ uint32_t bases[2];
   const int r = blockIdx.y, w = threadIdx.x >> 6;
   const uint32_t* wrow = ws + (int64_t)r * ws_row_words;
+  const uint32_t* h1 = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
-  uint32_t ustar, need;
-  resolve_passes<NT>(wrow, 3, kout, sh, wtot, ustar, need);
-  if (threadIdx.x == 0) {
-    uint32_t ob = 0, eqb = 0;
-    for (int i = 0; i < (int)blockIdx.x; ++i) {
-      const uint32_t gi = wrow[kCnt + 2 * i], ei = wrow[kCnt + 2 * i + 1];
-      const uint32_t take = need > eqb ? (ei < need - eqb ? ei : need - eqb) : 0u;
-      ob += gi + take;
-      eqb += ei;
-    }
-    bases[0] = ob;
-    bases[1] = eqb;
-  }
   const int base = blockIdx.x * kChunk + w * SEG;
+  float v[kChunkEPT];
+  load_vals<kChunkEPT>(scores + (int64_t)r * ld, base, T, v);
+  uint32_t ustar, need;
+  resolve_passes<NT>(wrow, h1, T, 3, kout, lh, sh, wtot, ustar, need);
+  // selected and equal elements in the chunks before this one: a scan of the
+  // equal counts gives each chunk its share of the `need` equal elements
+  const int nprev = (int)blockIdx.x, cpt = (nprev + NT - 1) / NT;
+  uint32_t esum = 0;
+  for (int j = 0; j < cpt; ++j) {
+    const int ch = threadIdx.x * cpt + j;
+    if (ch < nprev) esum += wrow[kCnt + 2 * ch + 1];
+  }
+  uint32_t eb = block_inclusive_sum<NT>(esum, wtot) - esum;
+  uint32_t gsum = 0;
+  for (int j = 0; j < cpt; ++j) {
+    const int ch = threadIdx.x * cpt + j;
+    if (ch < nprev) {
+      const uint32_t gi = wrow[kCnt + 2 * ch], ei = wrow[kCnt + 2 * ch + 1];
+      gsum += gi + (need > eb ? (ei < need - eb ? ei : need - eb) : 0u);
+      eb += ei;
+    }
+  }
+  const uint32_t out_before = block_sum<NT>(gsum, wtot);
+  const uint32_t eq_before = block_sum<NT>(esum, wtot);
+  if (threadIdx.x == 0) {
+    bases[0] = out_before;
+    bases[1] = eq_before;
+  }
   uint32_t key[kChunkEPT];
-  load_keys<kChunkEPT>(scores + (int64_t)r * ld, base, T, c, key);
+  vals_to_keys<kChunkEPT>(v, base, T, c, key);
   __syncthreads();
-  block_emit<kChunkNW, kChunkEPT>(key, T - base, base, ustar, need, bases[0], bases[1], c,
-                                  offset, out + (int64_t)r * ld_out, (uint32_t)kout, wcnt);
+  block_emit<kChunkNW, kChunkEPT>(key, base, ustar, need, bases[0], bases[1], c, offset,
+                                  out + (int64_t)r * ld_out, (uint32_t)kout, wcnt);
 }
 
 // ----------------------------------------------------------- short rows
@@ -373,13 +632,11 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* __restrict_
 // ------------------------------------------------------------ host side
 namespace {
 
-enum TopkPath { kAuto = 0, kSingle = 1, kChunked = 2 };
-
 // IDX_TOPK_PATH=chunked forces the multi-workgroup path for rows longer
 // than 1024 (read on every call; used by tests and tuning).
-TopkPath topk_path_override() {
+bool chunked_forced() {
   const char* e = getenv("IDX_TOPK_PATH");
-  return (e && e[0] == 'c') ? kChunked : kAuto;
+  return e && e[0] == 'c';
 }
 
 int64_t n_chunks(int T) { return ((int64_t)T + idx::kChunk - 1) / idx::kChunk; }
@@ -388,17 +645,11 @@ int64_t ws_row_words(int T) { return idx::kCnt + 2 * n_chunks(T); }
 
 size_t chunked_ws_bytes(int R, int T) { return (size_t)R * (size_t)ws_row_words(T) * 4u; }
 
-bool needs_chunked(int R, int T) {
-  const TopkPath o = topk_path_override();
-  if (T > 32768) return true;
-  if (o == kChunked && T > 1024) return true;
-  (void)R;
-  return false;
-}
+bool use_chunked(int T) { return T > 32768 || (chunked_forced() && T > 1024); }
 
-idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int32_t* cl, int k,
-                       int32_t offset, int32_t* out, int64_t ld_out, void* ws, size_t ws_bytes,
-                       hipStream_t st) {
+idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int32_t* cl,
+                       const uint32_t* key_hist, int k, int32_t offset, int32_t* out,
+                       int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t st) {
   if (R == 0 || T == 0) return IDX_OK;
   const int kout = k < T ? k : T;
   if (k >= T) {
@@ -406,16 +657,13 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
                        out, ld_out);
     return idx_host::launch_status();
   }
-  if (!needs_chunked(R, T)) {
-    if (T <= 1024)
-      hipLaunchKernelGGL((idx::topk_row_kernel<4, 4>), dim3((unsigned)R), dim3(256), 0, st, scores,
-                         ld, T, cl, kout, offset, out, ld_out);
-    else if (T <= 8192)
+  if (!use_chunked(T)) {
+    if (T <= 8192)
       hipLaunchKernelGGL((idx::topk_row_kernel<4, 32>), dim3((unsigned)R), dim3(256), 0, st,
-                         scores, ld, T, cl, kout, offset, out, ld_out);
+                         scores, ld, T, cl, key_hist, kout, offset, out, ld_out);
     else
       hipLaunchKernelGGL((idx::topk_row_kernel<16, 32>), dim3((unsigned)R), dim3(1024), 0, st,
-                         scores, ld, T, cl, kout, offset, out, ld_out);
+                         scores, ld, T, cl, key_hist, kout, offset, out, ld_out);
     return idx_host::launch_status();
   }
   if (R > 65535) return IDX_EUNSUPPORTED;
@@ -428,16 +676,17 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
   hipLaunchKernelGGL(idx::zero_words_kernel, dim3((unsigned)zg), dim3(256), 0, st, w, zero_n);
   const dim3 grid((unsigned)n_chunks(T), (unsigned)R);
   const dim3 blk(idx::kChunkNW * 64);
-  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<0>, grid, blk, 0, st, scores, ld, T, cl, kout, w,
-                     rw);
-  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<1>, grid, blk, 0, st, scores, ld, T, cl, kout, w,
-                     rw);
-  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<2>, grid, blk, 0, st, scores, ld, T, cl, kout, w,
-                     rw);
-  hipLaunchKernelGGL(idx::topk_chunk_count_kernel, grid, blk, 0, st, scores, ld, T, cl, kout, w,
-                     rw);
-  hipLaunchKernelGGL(idx::topk_chunk_emit_kernel, grid, blk, 0, st, scores, ld, T, cl, kout,
-                     offset, out, ld_out, (const uint32_t*)w, rw);
+  if (!key_hist)
+    hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<0>, grid, blk, 0, st, scores, ld, T, cl,
+                       key_hist, kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<1>, grid, blk, 0, st, scores, ld, T, cl,
+                     key_hist, kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<2>, grid, blk, 0, st, scores, ld, T, cl,
+                     key_hist, kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_count_kernel, grid, blk, 0, st, scores, ld, T, cl, key_hist,
+                     kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_emit_kernel, grid, blk, 0, st, scores, ld, T, cl, key_hist,
+                     kout, offset, out, ld_out, (const uint32_t*)w, rw);
   return idx_host::launch_status();
 }
 
@@ -455,16 +704,16 @@ extern "C" size_t idx_topk_workspace_size(int R, int T, int index_topk) {
 }
 
 extern "C" idx_status idx_topk(const float* scores, int64_t ld, int R, int T,
-                               const int32_t* compress_lens, int index_topk, int32_t offset,
-                               int32_t* out, int64_t ld_out, void* ws, size_t ws_bytes,
-                               void* stream) {
+                               const int32_t* compress_lens, const uint32_t* key_hist,
+                               int index_topk, int32_t offset, int32_t* out, int64_t ld_out,
+                               void* ws, size_t ws_bytes, void* stream) {
   if (R < 0 || T < 0 || index_topk <= 0) return IDX_EINVAL;
   if (R == 0 || T == 0) return IDX_OK;
   if (!scores || !compress_lens || !out) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
   if (ld < T || ld_out < kout) return IDX_EINVAL;
-  return topk_launch(scores, ld, R, T, compress_lens, index_topk, offset, out, ld_out, ws, ws_bytes,
-                     (hipStream_t)stream);
+  return topk_launch(scores, ld, R, T, compress_lens, key_hist, index_topk, offset, out, ld_out,
+                     ws, ws_bytes, (hipStream_t)stream);
 }
 
 extern "C" size_t idx_select_workspace_size(int R, int T, int ctb, int cbs) {
@@ -497,6 +746,6 @@ extern "C" idx_status idx_select_candidate_blocks(const float* scores, int64_t l
                      0, st, scores, ld, T, compress_lens, cand_block_size, nb, bmax, clb);
   const idx_status s = idx_host::launch_status();
   if (s != IDX_OK) return s;
-  return topk_launch(bmax, nb, R, nb, clb, candidate_topk_blocks, 0, block_ids, ld_ids, tws,
-                     tws_bytes, st);
+  return topk_launch(bmax, nb, R, nb, clb, nullptr, candidate_topk_blocks, 0, block_ids, ld_ids,
+                     tws, tws_bytes, st);
 }

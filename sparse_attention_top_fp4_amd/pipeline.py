@@ -62,6 +62,8 @@ class IndexerStep:
         self.kout = min(wl.topk, T)
         self.out = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
         self.topk_ws = self._ws(idx_topk_workspace_size(R, T, wl.topk))
+        # first-digit histogram of the scores, filled by the score kernel
+        self.key_hist = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
         self.two_level = bool(wl.ctb)
         if self.two_level:
             self.w2 = to_device(inp["w2"])
@@ -103,21 +105,23 @@ class IndexerStep:
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
         if score_events is not None:
             score_events[0].record(stream)
-        idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores, stream=stream)
+        idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                  key_hist=self.key_hist, stream=stream)
         if score_events is not None:
             score_events[1].record(stream)
         if self.two_level:
             idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
                                         workspace=self.sel_ws, stream=stream)
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
-                     workspace=self.topk_ws, stream=stream)
+                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
             idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                      cand_blocks=self.ids, cand_block_size=wl.cbs, stream=stream)
+                      cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
+                      stream=stream)
             idx_topk(self.scores2, wl.T, self.cl, wl.topk, wl.offset, self.out,
-                     workspace=self.topk_ws, stream=stream)
+                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
         else:
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
-                     workspace=self.topk_ws, stream=stream)
+                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
         self.cur = (self.cur + 1) % len(self.caches)
 
     def keys_scored(self):

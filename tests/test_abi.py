@@ -47,38 +47,38 @@ def test_score_rejects_bad_arguments_without_launching(lib):
     dummy = P(0x1000)  # never dereferenced: validation fails first
     # D != 128 and unsupported head counts
     assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 64, 8, dummy, None, 0, 0, dummy, 8,
-                         None) == IDX_EUNSUPPORTED
+                         None, None) == IDX_EUNSUPPORTED
     assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 48, 128, 8, dummy, None, 0, 0, dummy, 8,
-                         None) == IDX_EUNSUPPORTED
+                         None, None) == IDX_EUNSUPPORTED
     # null pointers, short row stride, short cache stride, bad candidates
     assert lib.idx_score(None, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
-                         None) == IDX_EINVAL
+                         None, None) == IDX_EINVAL
     assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 7,
-                         None) == IDX_EINVAL
+                         None, None) == IDX_EINVAL
     assert lib.idx_score(dummy, dummy, dummy, 7, 1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
-                         None) == IDX_EINVAL
+                         None, None) == IDX_EINVAL
     assert lib.idx_score(dummy, dummy, dummy, 8, 1, 1, 64, 128, 8, dummy, dummy, 0, 128, dummy, 8,
-                         None) == IDX_EINVAL
+                         None, None) == IDX_EINVAL
     assert lib.idx_score(dummy, dummy, dummy, 8, -1, 1, 64, 128, 8, dummy, None, 0, 0, dummy, 8,
-                         None) == IDX_EINVAL
+                         None, None) == IDX_EINVAL
     # empty work is a no-op, even with null pointers
     assert lib.idx_score(None, None, None, 0, 0, 1, 64, 128, 8, None, None, 0, 0, None, 8,
-                         None) == IDX_OK
+                         None, None) == IDX_OK
 
 
 def test_topk_and_select_reject_bad_arguments(lib):
     P = ctypes.c_void_p
     d = P(0x1000)
-    assert lib.idx_topk(d, 8, 1, 8, d, 0, 0, d, 8, None, 0, None) == IDX_EINVAL  # topk 0
-    assert lib.idx_topk(d, 7, 1, 8, d, 4, 0, d, 8, None, 0, None) == IDX_EINVAL  # ld < T
-    assert lib.idx_topk(d, 8, 1, 8, d, 4, 0, d, 3, None, 0, None) == IDX_EINVAL  # ld_out < k
-    assert lib.idx_topk(None, 8, 0, 8, None, 4, 0, None, 8, None, 0, None) == IDX_OK  # R = 0
+    assert lib.idx_topk(d, 8, 1, 8, d, None, 0, 0, d, 8, None, 0, None) == IDX_EINVAL  # topk 0
+    assert lib.idx_topk(d, 7, 1, 8, d, None, 4, 0, d, 8, None, 0, None) == IDX_EINVAL  # ld < T
+    assert lib.idx_topk(d, 8, 1, 8, d, None, 4, 0, d, 3, None, 0, None) == IDX_EINVAL  # ld_out < k
+    assert lib.idx_topk(None, 8, 0, 8, None, None, 4, 0, None, 8, None, 0, None) == IDX_OK  # R = 0
     need = lib.idx_topk_workspace_size(4, 100000, 2048)
     assert need > 0
-    assert lib.idx_topk(d, 100000, 4, 100000, d, 2048, 0, d, 2048, None, 0, None) == IDX_EINVAL
+    assert lib.idx_topk(d, 100000, 4, 100000, d, None, 2048, 0, d, 2048, None, 0, None) == IDX_EINVAL
     assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 0, 4, d, 2, None, 0, None) == IDX_EINVAL
     assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 2, 4, d, 1, d, 1 << 20,
-                                           None) == IDX_EINVAL  # ld_ids < min(ctb, nb)
+                                           None, None) == IDX_EINVAL  # ld_ids < min(ctb, nb)
     assert lib.idx_topk_workspace_size(4, 512, 2048) == 0  # every position kept
 
 

@@ -54,6 +54,32 @@ def test_quant_all_bf16_patterns(idx):
     assert np.array_equal(host(rt, np.uint16), rt_ref)
 
 
+def test_quant_every_bf16_at_several_scales(idx):
+    """Blocks of scale 2^e holding every finite bf16 x with |x| <= 6*2^e: the
+    device codes and round trip equal the oracle's (nearest grid point, ties
+    to the even code, sign kept)."""
+    t = torch()
+    allb = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    allb = allb[(allb & 0x7F80) != 0x7F80]
+    from sparse_attention_top_fp4_amd.inputs import bf16_to_f32
+    for e in (-126, -20, -1, 0, 9, 125):
+        amax = np.float32(6.0 * 2.0 ** e)
+        sel = allb[np.abs(bf16_to_f32(allb).astype(np.float64)) <= float(amax)]
+        sel = np.concatenate([sel, np.zeros((-len(sel)) % 31, np.uint16)]).reshape(-1, 31)
+        amaxb = bf16_bits(np.array([amax]))[0]
+        x = np.concatenate([sel, np.full((sel.shape[0], 1), amaxb, np.uint16)], axis=1)
+        x = np.concatenate([x, np.tile(x[:1], ((-x.shape[0]) % 4, 1))]).reshape(-1, 128)
+        say("quant scale", e, x.shape)
+        rows_ref, rt_ref = oracle.fp4_quant_rows(x)
+        xd = dev(x)
+        rows = t.empty((x.shape[0], 68), dtype=t.uint8, device="cuda")
+        rt = t.empty_like(xd)
+        idx.idx_fp4_quant(xd, rows, rt)
+        sync()
+        assert np.array_equal(host(rows), rows_ref), e
+        assert np.array_equal(host(rt, np.uint16), rt_ref), e
+
+
 # ------------------------------------------------------------------- score
 SCORE_CASES = [
     # (seed, B, S, H, T, tcap, start_pos)   start_pos None: decode at end_pos = 4T
@@ -220,3 +246,56 @@ def test_publish_matches_oracle(idx, mode):
     idx.idx_publish_keys(dev(latent), dev(wk), dev(gamma), dev(cs_lib), start_pos, 4, 1e-6, kc)
     sync()
     assert np.array_equal(host(kc), kc_ref)
+
+
+# ------------------------------------------- score histogram -> top-k path
+def _host_hist(scores_rows, counted):
+    """Top-11-bit key digit counts of the counted positions of each row."""
+    out = np.zeros((scores_rows.shape[0], 2048), np.int64)
+    for r in range(scores_rows.shape[0]):
+        v = scores_rows[r][counted[r]].astype(np.float32)
+        v = np.where(v == 0.0, np.float32(0.0), v)
+        u = v.view(np.uint32)
+        key = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+        out[r] = np.bincount(key >> 21, minlength=2048)
+    return out
+
+
+HIST_CASES = [
+    # (seed, B, S, T, start_pos, cand_blocks, cbs, k, path)
+    (51, 3, 1, 9000, None, None, 0, 2048, "auto"),       # one workgroup of 1024 per row
+    (52, 2, 1, 5000, None, None, 0, 2048, "auto"),       # one workgroup of 256 per row
+    (53, 1, 40, 700, 0, None, 0, 64, "auto"),            # prefill rows, many with cl < k
+    (54, 2, 1, 40000, None, None, 0, 2048, "auto"),      # chunked rows
+    (55, 2, 1, 9000, None, None, 0, 2048, "chunked"),
+    (56, 2, 1, 20000, None, [[0, 5, 7, 100], [3, 4, 90, 150]], 128, 2048, "auto"),  # few finite
+    (57, 2, 1, 20000, None, [list(range(0, 156, 2)), list(range(1, 156, 2))], 128, 2048, "auto"),
+]
+
+
+@pytest.mark.parametrize("case", HIST_CASES)
+def test_topk_with_score_histogram(idx, case, monkeypatch):
+    t = torch()
+    seed, B, S, T, sp, cand_rows, cbs, k, path = case
+    if path == "chunked":
+        monkeypatch.setenv("IDX_TOPK_PATH", "chunked")
+    say("topk with score histogram", case[:5], cbs, k, path)
+    c = small_case(seed, B, S, 64, T, start_pos=sp)
+    R = B * S
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    cand = None if cand_rows is None else np.array(cand_rows, np.int32)
+    ref, _ = oracle.score(c["q"], c["w"], kc_ref, B, S, 64, T, c["cl"], cand=cand, cbs=cbs)
+    kc = fp4_cache(c["k"])
+    sc = t.empty((R, T), dtype=t.float32, device="cuda")
+    hist = t.full((R, 2048), 7, dtype=t.int32, device="cuda")
+    idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, S, T, dev(c["cl"]), sc,
+                  cand_blocks=None if cand is None else dev(cand), cand_block_size=cbs,
+                  key_hist=hist)
+    kout = min(k, T)
+    out = t.full((R, kout), -7, dtype=t.int32, device="cuda")
+    idx.idx_topk(sc, T, dev(c["cl"]), k, 3, out, key_hist=hist)
+    sync()
+    tt = np.arange(T)[None, :]
+    counted = np.isfinite(ref) & (tt < c["cl"][:, None])
+    assert np.array_equal(host(hist).astype(np.int64), _host_hist(ref, counted))
+    assert np.array_equal(host(out), oracle.topk(ref, c["cl"], k, 3))
