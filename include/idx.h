@@ -93,12 +93,13 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  *                  >= ceil(T/cand_block_size) are skipped.
  *   scores         device, [B*S][ld] fp32, ld >= T.  Entries t >= cl[r] are
  *                  left unspecified without cand_blocks (callers mask by cl).
- *   key_hist       device, [B*S][2048] uint32, or NULL.  When given it is
- *                  cleared and then counts, per row, the scores this call
+ *   key_hist       device, [B*S][2048] uint32, or NULL.  When given, the
+ *                  call adds to it, per row, the count of the scores it
  *                  wrote by the top 11 bits of their order key (the key maps
  *                  -0 to +0, then flips negative floats and sets the sign of
- *                  positive ones).  idx_topk takes it to skip its first pass;
- *                  positions it does not count are -inf there.
+ *                  positive ones).  Clear it with idx_clear_key_hist first.
+ *                  idx_topk takes it to skip its first pass; positions it
+ *                  does not count are -inf there.
  * Requires D == 128 and H in {32, 64}.  T == 0 launches nothing.
  */
 idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
@@ -106,6 +107,12 @@ idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cach
                      const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
                      int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
                      void *stream);
+
+/*
+ * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on
+ * the stream, before idx_score accumulates into it.
+ */
+idx_status idx_clear_key_hist(uint32_t *key_hist, int R, void *stream);
 
 /*
  * Bytes of device workspace idx_topk needs for R rows of width T.

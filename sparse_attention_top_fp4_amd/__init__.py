@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["idx_fp4_quant", "idx_score", "idx_topk", "idx_topk_workspace_size",
+__all__ = ["idx_fp4_quant", "idx_score", "idx_clear_key_hist", "idx_topk",
+           "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
            "idx_yarn_cos_sin", "library_path", "load_library", "IdxError", "ROW_BYTES"]
 
@@ -48,6 +49,7 @@ def load_library():
     L.idx_version.restype = ctypes.c_char_p
     L.idx_fp4_quant.argtypes = [P, i64, P, P, P]
     L.idx_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32, P, i64, P, P]
+    L.idx_clear_key_hist.argtypes = [P, i32, P]
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
     L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, sz, P]
@@ -57,7 +59,8 @@ def load_library():
     L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
                                    i32, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
-    for name in ("idx_fp4_quant", "idx_score", "idx_topk", "idx_select_candidate_blocks",
+    for name in ("idx_fp4_quant", "idx_score", "idx_clear_key_hist", "idx_topk",
+                 "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin"):
         getattr(L, name).restype = i32
     _lib = L
@@ -126,7 +129,7 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
     """q [B*S, H, 128] bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8,
     compress_lens [B*S] int32, scores [B*S, ld] float32 (ld >= T),
     cand_blocks [B*S, n_cand] int32 or None, key_hist [B*S, 2048] int32
-    (uint32 counts) or None."""
+    (uint32 counts, added to; clear with idx_clear_key_hist) or None."""
     torch = _torch()
     _dev(q, "q", _bf16_types(), 3)
     _dev(w, "w", _bf16_types(), 2)
@@ -152,6 +155,16 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
                                     _ptr(key_hist), _stream(stream)), "idx_score")
+
+
+def idx_clear_key_hist(key_hist, stream=None):
+    """Zero a [R, 2048] int32 score histogram before idx_score adds to it."""
+    torch = _torch()
+    _dev(key_hist, "key_hist", (torch.int32,), 2)
+    if key_hist.shape[1] != 2048:
+        raise ValueError("key_hist must be [R, 2048]")
+    _check(load_library().idx_clear_key_hist(_ptr(key_hist), key_hist.shape[0], _stream(stream)),
+           "idx_clear_key_hist")
 
 
 def idx_topk_workspace_size(R, T, index_topk) -> int:

@@ -288,6 +288,17 @@ int pick_keys_per_wg(int64_t R, int vtotal) {
 }
 }  // namespace
 
+extern "C" idx_status idx_clear_key_hist(uint32_t* key_hist, int R, void* stream) {
+  if (R < 0) return IDX_EINVAL;
+  if (R == 0) return IDX_OK;
+  if (!key_hist) return IDX_EINVAL;
+  const int64_t n = (int64_t)R * 2048;
+  const int64_t g = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+  hipLaunchKernelGGL(idx::zero_hist_kernel, dim3((unsigned)g), dim3(256), 0, (hipStream_t)stream,
+                     key_hist, n);
+  return idx_host::launch_status();
+}
+
 extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
                                 int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                                 const int32_t* compress_lens, const int32_t* cand_blocks,
@@ -316,11 +327,6 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
     if (R > 65535) return IDX_EUNSUPPORTED;
     hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048), (unsigned)R),
                        dim3(256), 0, st, scores, ld, T);
-  }
-  if (key_hist) {
-    const int64_t n = R * 2048;
-    const int64_t g = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
-    hipLaunchKernelGGL(idx::zero_hist_kernel, dim3((unsigned)g), dim3(256), 0, st, key_hist, n);
   }
   dim3 grid((unsigned)R, (unsigned)nchunks);
   if (H == 64)

@@ -442,6 +442,225 @@ __global__ __launch_bounds__(NW * 64) void topk_row_kernel(
   }
 }
 
+// ---------------------------------------- split path (score histogram given)
+// Rows of 8193..262144 positions.  Kernel A: one workgroup of 512 threads per
+// 8192-position part of a row writes the part's "above the threshold bin"
+// bit mask and the (key, position) list of the elements inside the bin, one
+// list per wave.  Kernel B: one workgroup of 1024 threads per row resolves
+// the remaining digits on the collected list in LDS, marks the selected
+// list elements into the masks and compacts the row in position order.
+constexpr int kPartNW = 8, kPartEPT = 16, kPart = kPartNW * 64 * kPartEPT;  // 8192
+constexpr int kSplitMaxT = 262144;
+constexpr int kSplitCandCap = 8192;  // list elements resolved in LDS
+
+struct SplitLayout {  // per-row workspace, in 32-bit words
+  int64_t nwords;     // T/32 rounded up: above-mask words
+  int64_t nparts;
+  int64_t cand_off, cnt_off, state_off, row_words;
+  __host__ __device__ SplitLayout(int T) {
+    nwords = ((int64_t)T + 31) / 32;
+    nparts = ((int64_t)T + kPart - 1) / kPart;
+    cand_off = nwords;                                   // [nparts][8 waves][1024][2]
+    cnt_off = cand_off + nparts * kPartNW * 1024 * 2;    // [nparts][8 waves]
+    state_off = cnt_off + nparts * kPartNW;              // b1, krem
+    row_words = state_off + 2;
+  }
+};
+
+__global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    const uint32_t* __restrict__ key_hist, int kout, uint32_t* __restrict__ ws) {
+  constexpr int NT = kPartNW * 64, SEG = 64 * kPartEPT;
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wtot[kPartNW];
+  __shared__ uint32_t sh[4];
+  const int r = blockIdx.y, part = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const SplitLayout L(T);
+  uint32_t* wrow = ws + (int64_t)r * L.row_words;
+  int c = cl_arr[r];
+  c = c < 0 ? 0 : (c > T ? T : c);
+  const int base = part * kPart + w * SEG;
+  float v[kPartEPT];
+  load_vals<kPartEPT>(scores + (int64_t)r * ld, base, T, v);
+  copy_to_lds<NT, 2048>(hist, key_hist + (int64_t)r * 2048);
+  __syncthreads();
+  uint32_t b1, krem;
+  select_first_bin<NT>(hist, T, (uint32_t)kout, sh, wtot, b1, krem);
+  if (part == 0 && threadIdx.x == 0) {
+    wrow[L.state_off] = b1;
+    wrow[L.state_off + 1] = krem;
+  }
+  const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
+  const bool top = b1 >= 2044u;
+  const float hi = top ? __builtin_inff() : key_to_float((b1 + 1u) << 21);
+  uint32_t* cand = wrow + L.cand_off + ((int64_t)part * kPartNW + w) * 1024 * 2;
+  uint32_t run = 0;
+#pragma unroll
+  for (int e = 0; e < kPartEPT; ++e) {
+    const int t = base + e * 64 + lane;
+    const float x = t < T ? (t < c ? v[e] : -__builtin_inff()) : __builtin_nanf("");
+    const bool above = !top && x >= hi;
+    const bool isc = x >= lo && (top || x < hi);
+    const uint64_t am = __ballot(above);
+    const uint64_t cm = __ballot(isc);
+    if (lane == 0 && base + e * 64 < T) {
+      const int64_t word = (base + e * 64) >> 5;
+      wrow[word] = (uint32_t)am;
+      if (word + 1 < L.nwords) wrow[word + 1] = (uint32_t)(am >> 32);
+    }
+    if (isc) {
+      const uint32_t k = run + lanes_below(cm);
+      cand[2 * k] = score_key(x);
+      cand[2 * k + 1] = (uint32_t)t;
+    }
+    run += (uint32_t)__popcll(cm);
+  }
+  if (lane == 0) wrow[L.cnt_off + (int64_t)part * kPartNW + w] = run;
+}
+
+__global__ __launch_bounds__(1024) void topk_split_b_kernel(
+    int T, const int32_t* __restrict__ cl_arr, const uint32_t* __restrict__ key_hist, int kout,
+    int32_t offset, int32_t* __restrict__ out, int64_t ld_out, const uint32_t* __restrict__ ws) {
+  constexpr int NT = 1024, NW = 16;
+  extern __shared__ uint32_t dyn[];  // sel[nwords] eq[nwords] ckey[cap] cpos[cap]
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t regions[kSplitMaxT / kPart * kPartNW + 1];  // prefix of list counts
+  __shared__ uint32_t wtot[NW];
+  __shared__ uint32_t sh[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const SplitLayout L(T);
+  const uint32_t* wrow = ws + (int64_t)r * L.row_words;
+  int c = cl_arr[r];
+  c = c < 0 ? 0 : (c > T ? T : c);
+  const int nw = (int)L.nwords;
+  uint32_t* sel = dyn;
+  uint32_t* eqm = dyn + nw;
+  uint32_t* ckey = dyn + 2 * nw;
+  uint32_t* cpos = ckey + kSplitCandCap;
+  const int nreg = (int)L.nparts * kPartNW;
+
+  for (int i = tid; i < nw; i += NT) {
+    sel[i] = 0u;
+    eqm[i] = 0u;
+  }
+  // list counts -> region prefix (thread 0 scans at most 256 entries in LDS)
+  for (int i = tid; i < nreg; i += NT) regions[i + 1] = wrow[L.cnt_off + i];
+  const uint32_t b1 = wrow[L.state_off];
+  uint32_t krem = wrow[L.state_off + 1];
+  __syncthreads();
+  if (tid == 0) {
+    regions[0] = 0;
+    for (int i = 1; i <= nreg; ++i) regions[i] += regions[i - 1];
+  }
+  __syncthreads();
+  const uint32_t ncand = regions[nreg];
+  const bool only_inf = b1 == kInfBin && key_hist[(int64_t)r * 2048 + kInfBin] == 0u;
+
+  uint32_t ustar = kKeyNegInf;
+  if (!only_inf) {
+    const bool in_lds = ncand <= (uint32_t)kSplitCandCap;
+    // list element i lives in region j with regions[j] <= i < regions[j+1]
+    auto fetch = [&](uint32_t i, uint32_t& k, uint32_t& p) {
+      int lo = 0, hi = nreg;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (regions[mid] <= i) lo = mid; else hi = mid;
+      }
+      const uint32_t* cl = wrow + L.cand_off + (int64_t)lo * 1024 * 2;
+      const uint32_t j = i - regions[lo];
+      k = cl[2 * j];
+      p = cl[2 * j + 1];
+    };
+    if (in_lds) {
+      for (uint32_t i = tid; i < ncand; i += NT) {
+        uint32_t k, p;
+        fetch(i, k, p);
+        ckey[i] = k;
+        cpos[i] = p;
+      }
+      __syncthreads();
+    }
+    uint32_t prefix = b1;
+    for (int pass = 1; pass < 3; ++pass) {
+      const int nb = pass_bins(pass), shift = pass_shift(pass), ms = pass_match_shift(pass);
+      for (int i = tid; i < nb; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < ncand; i += NT) {
+        uint32_t k, p;
+        if (in_lds) k = ckey[i]; else fetch(i, k, p);
+        if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      uint32_t bin, k2;
+      select_bin<NT>(hist, nb, krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
+      prefix = extend_prefix(prefix, pass, bin);
+      krem = k2;
+    }
+    ustar = prefix;
+    // mark the list elements above the threshold and equal to it
+    for (uint32_t i = tid; i < ncand; i += NT) {
+      uint32_t k, p;
+      if (in_lds) {
+        k = ckey[i];
+        p = cpos[i];
+      } else {
+        fetch(i, k, p);
+      }
+      if (k > ustar) atomicOr(&sel[p >> 5], 1u << (p & 31));
+      else if (k == ustar) atomicOr(&eqm[p >> 5], 1u << (p & 31));
+    }
+  }
+  const uint32_t need = krem;
+  __syncthreads();
+
+  // compaction: thread i owns words [i*WPT, (i+1)*WPT)
+  const int wpt = (nw + NT - 1) / NT;
+  uint32_t ng = 0, nq = 0;
+  for (int j = 0; j < wpt; ++j) {
+    const int word = tid * wpt + j;
+    if (word < nw) {
+      uint32_t a = wrow[word] | sel[word];
+      uint32_t q = eqm[word];
+      if (only_inf) {  // the equal elements are the -inf ones: present and not above
+        const int rem = T - word * 32;
+        const uint32_t present = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
+        q = present & ~wrow[word];
+        a = wrow[word];
+      }
+      sel[word] = a;
+      eqm[word] = q;
+      ng += (uint32_t)__popc(a);
+      nq += (uint32_t)__popc(q);
+    }
+  }
+  const uint32_t packed_g = ng, packed_q = nq;
+  const uint32_t gx = block_inclusive_sum<NT>(packed_g, wtot) - packed_g;
+  uint32_t qbefore = block_inclusive_sum<NT>(packed_q, wtot) - packed_q;
+  uint32_t slot = gx + (qbefore < need ? qbefore : need);
+  int32_t* orow = out + (int64_t)r * ld_out;
+  for (int j = 0; j < wpt; ++j) {
+    const int word = tid * wpt + j;
+    if (word >= nw) break;
+    const uint32_t qw = eqm[word];
+    const uint32_t qn = (uint32_t)__popc(qw);
+    uint32_t take = need > qbefore ? (need - qbefore < qn ? need - qbefore : qn) : 0u;
+    qbefore += qn;
+    uint32_t bits = sel[word], rest = qw;
+    while (take--) {
+      const uint32_t low = rest & (0u - rest);
+      bits |= low;
+      rest ^= low;
+    }
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int t = word * 32 + b;
+      if (slot < (uint32_t)kout) orow[slot] = t < c ? t + offset : -1;
+      ++slot;
+    }
+  }
+}
+
 // ------------------------------------------------- multi-workgroup path
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -647,6 +866,18 @@ size_t chunked_ws_bytes(int R, int T) { return (size_t)R * (size_t)ws_row_words(
 
 bool use_chunked(int T) { return T > 32768 || (chunked_forced() && T > 1024); }
 
+bool use_split(int T, const uint32_t* key_hist) {
+  return key_hist && T > 8192 && T <= idx::kSplitMaxT && !chunked_forced();
+}
+
+size_t split_ws_bytes(int R, int T) {
+  return (size_t)R * (size_t)idx::SplitLayout(T).row_words * 4u;
+}
+
+size_t split_b_lds(int T) {
+  return ((size_t)2 * idx::SplitLayout(T).nwords + 2 * idx::kSplitCandCap) * 4u;
+}
+
 idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int32_t* cl,
                        const uint32_t* key_hist, int k, int32_t offset, int32_t* out,
                        int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -655,6 +886,24 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
   if (k >= T) {
     hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T, cl, offset,
                        out, ld_out);
+    return idx_host::launch_status();
+  }
+  if (use_split(T, key_hist)) {
+    if (R > 65535) return IDX_EUNSUPPORTED;
+    if (!ws || ws_bytes < split_ws_bytes(R, T)) return IDX_EINVAL;
+    const idx::SplitLayout L(T);
+    static bool lds_attr = false;  // kernel B may use more than 64 KB of dynamic LDS
+    if (!lds_attr) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&idx::topk_split_b_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)split_b_lds(idx::kSplitMaxT));
+      lds_attr = true;
+    }
+    hipLaunchKernelGGL(idx::topk_split_a_kernel, dim3((unsigned)L.nparts, (unsigned)R),
+                       dim3(idx::kPartNW * 64), 0, st, scores, ld, T, cl, key_hist, kout,
+                       (uint32_t*)ws);
+    hipLaunchKernelGGL(idx::topk_split_b_kernel, dim3((unsigned)R), dim3(1024), split_b_lds(T), st,
+                       T, cl, key_hist, kout, offset, out, ld_out, (const uint32_t*)ws);
     return idx_host::launch_status();
   }
   if (!use_chunked(T)) {
@@ -692,7 +941,9 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
 
 size_t topk_ws_bytes(int R, int T, int k) {
   if (R <= 0 || T <= 0 || k >= T || T <= 1024) return 0;
-  return chunked_ws_bytes(R, T);
+  size_t n = chunked_ws_bytes(R, T);
+  if (T > 8192 && T <= idx::kSplitMaxT) n = n > split_ws_bytes(R, T) ? n : split_ws_bytes(R, T);
+  return n;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -12,8 +12,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (idx_fp4_quant, idx_publish_keys, idx_score, idx_select_candidate_blocks,
-               idx_select_workspace_size, idx_topk, idx_topk_workspace_size, idx_yarn_cos_sin)
+from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score,
+               idx_select_candidate_blocks, idx_select_workspace_size, idx_topk,
+               idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
 
 
@@ -103,6 +104,7 @@ class IndexerStep:
         if self.publish:
             idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+        idx_clear_key_hist(self.key_hist, stream=stream)
         if score_events is not None:
             score_events[0].record(stream)
         idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
@@ -114,6 +116,7 @@ class IndexerStep:
                                         workspace=self.sel_ws, stream=stream)
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
+            idx_clear_key_hist(self.key_hist, stream=stream)
             idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
                       cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
                       stream=stream)

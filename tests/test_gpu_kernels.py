@@ -270,6 +270,8 @@ HIST_CASES = [
     (55, 2, 1, 9000, None, None, 0, 2048, "chunked"),
     (56, 2, 1, 20000, None, [[0, 5, 7, 100], [3, 4, 90, 150]], 128, 2048, "auto"),  # few finite
     (57, 2, 1, 20000, None, [list(range(0, 156, 2)), list(range(1, 156, 2))], 128, 2048, "auto"),
+    (58, 2, 1, 20000, None, None, 0, 2048, "zero-weights"),  # every score equal: all ties
+    (59, 1, 1, 262144, None, None, 0, 2048, "auto"),         # longest split row
 ]
 
 
@@ -281,6 +283,8 @@ def test_topk_with_score_histogram(idx, case, monkeypatch):
         monkeypatch.setenv("IDX_TOPK_PATH", "chunked")
     say("topk with score histogram", case[:5], cbs, k, path)
     c = small_case(seed, B, S, 64, T, start_pos=sp)
+    if path == "zero-weights":
+        c["w"][:] = 0
     R = B * S
     kc_ref, _ = oracle.fp4_quant_rows(c["k"])
     cand = None if cand_rows is None else np.array(cand_rows, np.int32)
@@ -288,6 +292,7 @@ def test_topk_with_score_histogram(idx, case, monkeypatch):
     kc = fp4_cache(c["k"])
     sc = t.empty((R, T), dtype=t.float32, device="cuda")
     hist = t.full((R, 2048), 7, dtype=t.int32, device="cuda")
+    idx.idx_clear_key_hist(hist)
     idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, S, T, dev(c["cl"]), sc,
                   cand_blocks=None if cand is None else dev(cand), cand_block_size=cbs,
                   key_hist=hist)
