@@ -164,9 +164,12 @@ def main():
     t1 = time.perf_counter()
 
     if args.copy_calibration:
-        a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda")
+        # known-size reference kernels for the counter calibration: a 256 MiB
+        # device copy and an elementwise negation that reads and writes 256 MiB
+        a = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
         b.copy_(a)
+        torch.neg(a, out=b)
         torch.cuda.synchronize()
 
     step_s = (t1 - t0) / args.steps
