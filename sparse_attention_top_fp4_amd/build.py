@@ -2,7 +2,9 @@
 
 All HIP sources under csrc/ are compiled for gfx950 only, with
 -ffp-contract=off (every fused multiply-add in the kernels is explicit) and
-packed-fp32 instructions disabled.
+packed-fp32 instructions disabled, and with matrix-core results kept in
+ordinary VGPRs (the kernels read every MFMA result with VALU instructions,
+so accumulation registers would only add a copy per value).
 """
 import glob
 import os
@@ -16,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",
-         "-Wno-unused-function"]
+         "-Wno-unused-function", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def sources():

@@ -47,21 +47,27 @@ __device__ __forceinline__ int head_of_row(int ht, int m) {
 }
 
 constexpr int kMaxCand = 2048;  // candidate blocks per row held in LDS
+#ifndef IDX_SCORE_TILE_SETS
+#define IDX_SCORE_TILE_SETS 3
+#endif
+constexpr int kTileSets = IDX_SCORE_TILE_SETS;  // key tiles per wave held in registers
 
 struct KeyTile {
   u32x4 c[2][2];   // [key tile][K-step]: 16 code bytes of block 2*step + lane/32
   uint32_t sc[2];  // [key tile]: the row's four scale bytes
 };
 
-// Virtual position v -> key position, for plain and candidate mode.
+// Virtual position v -> key position.  Plain mode scores positions
+// [0, limit) directly; candidate mode (level two) walks the listed blocks.
+template <bool CAND>
 struct PosMap {
-  const int32_t* cand;  // row's candidate block ids (in LDS), or nullptr
+  const int32_t* cand;  // row's candidate block ids (in LDS), candidate mode
   int cbs;
   int nblk;   // ceil(T / cbs)
   int limit;  // positions must be < limit (= clamped compress_lens)
   int vlim;   // virtual positions must be < vlim
   __device__ __forceinline__ int pos(int v) const {  // -1 when not scored
-    if (!cand) return v < vlim ? v : -1;  // vlim <= limit
+    if (!CAND) return v < vlim ? v : -1;  // vlim <= limit
     if (v >= vlim) return -1;
     const int j = v / cbs;
     const int id = cand[j];
@@ -76,8 +82,9 @@ struct PosMap {
 // without a key reads row 0 of the sequence instead; its MFMA column is then
 // a product of valid codes that is simply not stored (columns of the
 // accumulator depend only on their own key).
-__device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq, const PosMap& pm,
-                                             int v0, int lane) {
+template <bool CAND>
+__device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
+                                             const PosMap<CAND>& pm, int v0, int lane) {
   KeyTile kt;
   const int half = lane >> 5;
 #pragma unroll
@@ -100,11 +107,11 @@ __device__ __forceinline__ float relu_bits(float x) {
 
 // One 64-key tile: 2 key tiles x HT head tiles x 2 K-steps of MFMA, the
 // half-wave swap, and the fixed-order head sum; lane l scores key v0 + l.
-template <int HT>
+template <int HT, bool CAND>
 __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
                                            const int (&sA)[HT][2], const float (&wf)[32 * HT],
-                                           const PosMap& pm, float* __restrict__ srow, int v0,
-                                           int lane, uint32_t* hist_s) {
+                                           const PosMap<CAND>& pm, float* __restrict__ sbuf, int v0,
+                                           int vbeg, int lane, uint32_t* hist_s) {
   float sc = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -136,14 +143,11 @@ __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT]
     for (int i = 0; i < 16; ++i)
       sc = __builtin_fmaf(relu_bits(acc[1][i]), wf[32 * ht + 16 + i], sc);
   }
-  const int p = pm.pos(v0 + lane);
-  if (p >= 0) {
-    srow[p] = sc;
-    if (hist_s) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
-  }
+  sbuf[v0 - vbeg + lane] = sc;  // staged in LDS, written out when the chunk is done
+  if (hist_s && pm.pos(v0 + lane) >= 0) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
 }
 
-template <int HT>
+template <int HT, bool CAND>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
@@ -152,28 +156,40 @@ __global__ __launch_bounds__(256) void score_kernel(
   constexpr int H = 32 * HT;
   __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
   __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
-  __shared__ int32_t cand_s[kMaxCand];
+  __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
+  extern __shared__ float sbuf[];  // keys_per_wg scores of this workgroup's chunk
   const int r = blockIdx.x;
   const int b = r / S;
   int limit = cl[r];
   limit = limit < 0 ? 0 : (limit > T ? T : limit);
 
-  PosMap pm;
-  pm.cand = cand ? cand_s : nullptr;
+  PosMap<CAND> pm;
+  pm.cand = cand_s;
   pm.cbs = cbs;
-  pm.nblk = cand ? (T + cbs - 1) / cbs : 0;
+  pm.nblk = CAND ? (T + cbs - 1) / cbs : 0;
   pm.limit = limit;
-  const int vtotal = cand ? n_cand * cbs : limit;
+  const int vtotal = CAND ? n_cand * cbs : limit;
   const int vbeg = blockIdx.y * keys_per_wg;
   const int vend = min(vbeg + keys_per_wg, vtotal);
   if (vbeg >= vend) return;
   pm.vlim = vend;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (cand) {
+  if (CAND) {
     for (int i = tid; i < n_cand; i += 256) cand_s[i] = cand[(int64_t)r * n_cand + i];
     __syncthreads();
   }
+
+  // the first key tiles are requested before the query work, so their
+  // latency overlaps the query load and quantisation.  kTileSets register
+  // sets: while one tile computes, the next kTileSets - 1 tiles of this wave
+  // are in flight
+  const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
+  const int ntiles = (vend - vbeg + 63) >> 6;
+  int j = wave;
+  KeyTile buf[kTileSets];
+#pragma unroll
+  for (int i = 0; i < kTileSets - 1; ++i) buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane);
 
   uint32_t* hist_s = key_hist ? hist_lds : nullptr;
   if (key_hist)
@@ -202,15 +218,8 @@ __global__ __launch_bounds__(256) void score_kernel(
   // weights of the row (uniform across the workgroup)
   float wf[H];
 #pragma unroll
-  for (int h = 0; h < H; ++h) wf[h] = bf16f(w[(int64_t)r * H + h]);
-
-  const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
-  const int ntiles = (vend - vbeg + 63) >> 6;
-  // three register sets: while one tile computes, the next two are in flight
-  int j = wave;
-  KeyTile ta = load_tile(kseq, pm, vbeg + 64 * j, lane);
-  KeyTile tb = load_tile(kseq, pm, vbeg + 64 * (j + 4), lane);
-  KeyTile tc;
+  for (int h = 0; h < H; ++h)  // uniform: kept in scalar registers, read by the fmas directly
+    wf[h] = __uint_as_float(__builtin_amdgcn_readfirstlane((uint32_t)w[(int64_t)r * H + h] << 16));
 
   __syncthreads();
 
@@ -230,22 +239,35 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
 
   float* srow = scores + (int64_t)r * ld;
+  // the loop body is unrolled over the sets so every set index is a
+  // compile-time constant (the sets stay in distinct registers)
   while (true) {
-    tc = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
-    score_tile<HT>(ta, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
-    j += 4;
-    if (j >= ntiles) break;
-    ta = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
-    score_tile<HT>(tb, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
-    j += 4;
-    if (j >= ntiles) break;
-    tb = load_tile(kseq, pm, vbeg + 64 * (j + 8), lane);
-    score_tile<HT>(tc, A, sA, wf, pm, srow, vbeg + 64 * j, lane, hist_s);
-    j += 4;
-    if (j >= ntiles) break;
+#pragma unroll
+    for (int u = 0; u < kTileSets; ++u) {
+      buf[(u + kTileSets - 1) % kTileSets] =
+          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane);
+      score_tile<HT, CAND>(buf[u], A, sA, wf, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
+      j += 4;
+      if (j >= ntiles) goto done;
+    }
+  }
+done:
+  // the chunk's scores leave in one coalesced pass: interleaving small score
+  // stores with the key stream costs far more HBM time than one burst
+  __syncthreads();
+  const int n = vend - vbeg;
+  if (!CAND && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
+    float4* dst = reinterpret_cast<float4*>(srow + vbeg);
+    const float4* src = reinterpret_cast<const float4*>(sbuf);
+    for (int i = tid; i < (n >> 2); i += 256) dst[i] = src[i];
+    for (int i = (n & ~3) + tid; i < n; i += 256) srow[vbeg + i] = sbuf[i];
+  } else {
+    for (int i = tid; i < n; i += 256) {
+      const int p = pm.pos(vbeg + i);
+      if (p >= 0) srow[p] = sbuf[i];
+    }
   }
   if (key_hist) {
-    __syncthreads();
     uint32_t* grow = key_hist + (int64_t)r * 2048;
     for (int i = tid; i < 2048; i += 256)
       if (hist_lds[i]) atomicAdd(&grow[i], hist_lds[i]);
@@ -269,6 +291,7 @@ __global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* __restrict__ s
 }  // namespace idx
 
 namespace {
+constexpr int kMaxKeysPerWg = 8192;  // bounds the LDS score buffer (32 KB)
 int g_keys_per_wg_override = -1;
 
 int pick_keys_per_wg(int64_t R, int vtotal) {
@@ -276,13 +299,17 @@ int pick_keys_per_wg(int64_t R, int vtotal) {
     const char* e = getenv("IDX_SCORE_KEYS_PER_WG");
     g_keys_per_wg_override = e ? atoi(e) : 0;
   }
-  if (g_keys_per_wg_override > 0) return (g_keys_per_wg_override + 255) / 256 * 256;
+  if (g_keys_per_wg_override > 0) {
+    const int o = (g_keys_per_wg_override + 255) / 256 * 256;
+    return o < kMaxKeysPerWg ? o : kMaxKeysPerWg;
+  }
   // about two resident workgroups per CU over the whole launch (256 CUs), at
   // least 1024 keys per workgroup so the query quantisation stays amortised
   const int64_t total = R * (int64_t)vtotal;
   int64_t kpw = (total + 511) / 512;
   if (kpw < 1024) kpw = 1024;
   if (kpw > vtotal) kpw = vtotal;
+  if (kpw > kMaxKeysPerWg) kpw = kMaxKeysPerWg;
   if (kpw < 256) kpw = 256;
   return (int)((kpw + 255) / 256 * 256);
 }
@@ -329,13 +356,10 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                        dim3(256), 0, st, scores, ld, T);
   }
   dim3 grid((unsigned)R, (unsigned)nchunks);
-  if (H == 64)
-    hipLaunchKernelGGL(idx::score_kernel<2>, grid, dim3(256), 0, st, q, w, k_cache,
-                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                       cand_block_size, scores, ld, key_hist, kpw);
-  else
-    hipLaunchKernelGGL(idx::score_kernel<1>, grid, dim3(256), 0, st, q, w, k_cache,
-                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                       cand_block_size, scores, ld, key_hist, kpw);
+  auto kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true> : idx::score_kernel<2, false>)
+                      : (cand_blocks ? idx::score_kernel<1, true> : idx::score_kernel<1, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)kpw * sizeof(float), st, q, w, k_cache, k_batch_stride_rows, S, T,
+                     compress_lens, cand_blocks, n_cand, cand_block_size, scores, ld, key_hist,
+                     kpw);
   return idx_host::launch_status();
 }
