@@ -97,9 +97,11 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  *                  call adds to it, per row, the count of the scores it
  *                  wrote by the top 11 bits of their order key (the key maps
  *                  -0 to +0, then flips negative floats and sets the sign of
- *                  positive ones).  Clear it with idx_clear_key_hist first.
- *                  idx_topk takes it to skip its first pass; positions it
- *                  does not count are -inf there.
+ *                  positive ones).  It must hold zeros before the call:
+ *                  idx_clear_key_hist clears it once, and every idx_topk
+ *                  that consumes it leaves it zeroed again.  idx_topk takes
+ *                  it to skip its first pass; positions it does not count
+ *                  are -inf there.
  * Requires D == 128 and H in {32, 64}.  T == 0 launches nothing.
  */
 idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
@@ -110,7 +112,8 @@ idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cach
 
 /*
  * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on
- * the stream, before idx_score accumulates into it.
+ * the stream, before the first idx_score accumulates into it (idx_topk
+ * resets it after each use).
  */
 idx_status idx_clear_key_hist(uint32_t *key_hist, int R, void *stream);
 
@@ -132,7 +135,8 @@ size_t idx_topk_workspace_size(int R, int T, int index_topk);
  *   compress_lens  device, [R] int32 (clamped to [0, T])
  *   key_hist       device, [R][2048] from idx_score on these scores and
  *                  compress_lens, or NULL (then the first digit is counted
- *                  here)
+ *                  here).  The call reads it and resets it to zero (in
+ *                  stream order), ready for the next idx_score.
  *   out            device, [R][ld_out] int32, ld_out >= k_out; only the first
  *                  k_out entries of each row are written
  *   ws, ws_bytes   device workspace of at least idx_topk_workspace_size bytes
@@ -140,7 +144,7 @@ size_t idx_topk_workspace_size(int R, int T, int index_topk);
  * NaN scores give unspecified results.
  */
 idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t *compress_lens,
-                    const uint32_t *key_hist, int index_topk, int32_t offset, int32_t *out,
+                    uint32_t *key_hist, int index_topk, int32_t offset, int32_t *out,
                     int64_t ld_out, void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -176,7 +176,8 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
     """scores [R, ld] float32, compress_lens [R] int32, out [R, ld_out] int32
     (ld_out >= min(index_topk, T)).  workspace: uint8 device tensor of at
     least idx_topk_workspace_size bytes, allocated here when None.
-    key_hist: the [R, 2048] histogram idx_score produced for these scores."""
+    key_hist: the [R, 2048] histogram idx_score produced for these scores;
+    the call resets it to zero."""
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)

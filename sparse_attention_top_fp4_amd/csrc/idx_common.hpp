@@ -111,10 +111,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
+// Sum over the wave (every lane active), by DPP scan: no LDS round trips.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_sum(v), 63);
 }
 
 // number of lanes below this one with the predicate set

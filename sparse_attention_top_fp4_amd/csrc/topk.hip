@@ -34,12 +34,13 @@
 
 #include <stdlib.h>
 
+#include <atomic>
+
 namespace idx {
 
 constexpr int kHist1 = 0, kHist2 = 2048, kHist3 = 4096, kCnt = 5120;  // workspace row layout (words)
 constexpr int kChunkNW = 4, kChunkEPT = 16, kChunk = kChunkNW * 64 * kChunkEPT;  // 4096
 constexpr uint32_t kInfBin = kKeyNegInf >> 21;  // first-digit bin of -inf
-constexpr int kCandCap = 4096;                  // LDS candidate list of the single-WG path
 
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
@@ -259,186 +260,293 @@ __device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int base,
   }
 }
 
-// ------------------------------------------------ single-workgroup path
-// One workgroup per row of at most NW*64*EPT positions; in the compaction,
-// thread i owns the 32-position mask words [i*WPT, (i+1)*WPT).
-template <int NW, int EPT>
-__global__ __launch_bounds__(NW * 64) void topk_row_kernel(
-    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
-    const uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
-    int64_t ld_out) {
-  constexpr int NT = NW * 64, SEG = 64 * EPT, NWORDS = NT * EPT / 32;
-  constexpr int WPT = NWORDS / NT;
-  static_assert(WPT * NT == NWORDS && WPT >= 1, "whole mask words per thread");
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t cand_key[kCandCap];
-  __shared__ uint32_t cand_pos[kCandCap];
-  __shared__ uint32_t gt_mask[NWORDS];
-  __shared__ uint32_t eq_mask[NWORDS];
-  __shared__ uint32_t wtot[NW];
-  __shared__ uint32_t sh[4];
-  const int r = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
-  int c = cl_arr[r];
-  c = c < 0 ? 0 : (c > T ? T : c);
-  const int base = w * SEG;
-  const float* srow = scores + (int64_t)r * ld;
+// ------------------------------------------------ single-workgroup rows
+// One workgroup of NT threads per row of at most NT*EPT positions.  Wave w
+// owns the positions [w*64*EPT, (w+1)*64*EPT); in step i its lane l holds the
+// four consecutive positions w*64*EPT + i*256 + 4l + [0, 4), so every load is
+// a contiguous 1 KB per wave.  The keys stay in registers.  Each radix pass
+// histograms in LDS the next digit of the keys whose higher digits equal the
+// threshold prefix found so far, and the search stops as soon as every
+// element of the prefix bin is taken.  The output is written in position
+// order with wave scans.  key_hist (optional) is the score kernel's
+// first-digit histogram of the row: it is read once and reset to zero for
+// the next score call.  Only positions below compress_lens are loaded; a row
+// with compress_lens <= k keeps all of them and needs no scores at all.
 
-  // row values: masked positions -inf, positions past T NaN (never selected)
-  float v[EPT];
-  {
-    const unsigned last = (unsigned)(T - 1);
+// Threshold bin of an LDS histogram of NB bins, bins read into registers at
+// once (thread i owns the bins [NB - (i+1)*BPT, NB - i*BPT), the top bins
+// first): the bin b with count(bins > b) < krem <= count(bins >= b), where
+// bin `xbin` counts `xcnt` more.  Also returns the count of bin b.
+template <int NT, int NB>
+__device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
+                                             uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
+                                             uint32_t& bin, uint32_t& krem_out,
+                                             uint32_t& bin_count) {
+  constexpr int BPT = NB / NT;
+  static_assert(BPT * NT == NB && BPT >= 1, "whole bins per thread");
+  const int hi = NB - (int)threadIdx.x * BPT;  // my bins are [hi - BPT, hi)
+  uint32_t cnt[BPT];
+  uint32_t mine = 0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const unsigned t = (unsigned)(base + e * 64 + lane);
-      v[e] = srow[t < last ? t : last];
-    }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int t = base + e * 64 + lane;
-      v[e] = t < T ? (t < c ? v[e] : -__builtin_inff()) : __builtin_nanf("");
-    }
+  for (int j = 0; j < BPT; ++j) {
+    const int b = hi - 1 - j;
+    cnt[j] = hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
+    mine += cnt[j];
   }
-
-  // ---- first digit
-  uint32_t b1, krem;
-  bool only_inf = false;
-  if (key_hist) {
-    copy_to_lds<NT, 2048>(hist, key_hist + (int64_t)r * 2048);
-    __syncthreads();
-    select_first_bin<NT>(hist, T, (uint32_t)kout, sh, wtot, b1, krem);
-    // the threshold bin holds only -inf when the scores put nothing in it
-    only_inf = b1 == kInfBin && hist[kInfBin] == 0u;
-    __syncthreads();
-  } else {
-    uint32_t key[EPT];
+  const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
+  uint32_t cum = incl - mine;
+  if (cum < krem && krem <= incl) {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) key[e] = v[e] != v[e] ? 0u : score_key(v[e]);
-    block_hist<NT, EPT>(key, 0, 0u, hist, &sh[2]);
-    select_bin<NT>(hist, 2048, (uint32_t)kout, 0xffffffffu, 0u, sh, wtot, b1, krem);
-  }
-
-  // ---- remaining digits
-  uint32_t ustar;
-  if (only_inf) {
-    ustar = kKeyNegInf;  // the threshold bin holds only -inf: its elements are all equal
-  } else {
-    // compact the threshold bin's elements into LDS
-    const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
-    const bool top = b1 >= 2044u;  // the bin reaches +inf: no upper edge
-    const float hi = top ? 0.0f : key_to_float((b1 + 1u) << 21);
-    // each wave counts its bin elements, one scan over the waves gives every
-    // wave its slot range, then each wave writes its elements in order
-    uint32_t mine = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) mine += (uint32_t)__popcll(__ballot(v[e] >= lo && (top || v[e] < hi)));
-    if (lane == 0) wtot[w] = mine;
-    __syncthreads();
-    uint32_t slot = 0, ncand = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint32_t x = wtot[i];
-      slot += i < w ? x : 0u;
-      ncand += x;
-    }
-    __syncthreads();
-    if (ncand <= (uint32_t)kCandCap) {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const bool isc = v[e] >= lo && (top || v[e] < hi);
-        const uint64_t m = __ballot(isc);
-        if (isc) {
-          const uint32_t k = slot + lanes_below(m);
-          cand_key[k] = score_key(v[e]);
-          cand_pos[k] = (uint32_t)(base + e * 64 + lane);
-        }
-        slot += (uint32_t)__popcll(m);
+    for (int j = 0; j < BPT; ++j) {
+      if (cum < krem && cum + cnt[j] >= krem) {
+        sh[0] = (uint32_t)(hi - 1 - j);
+        sh[1] = krem - cum;
+        sh[2] = cnt[j];
       }
-    }
-    __syncthreads();
-    uint32_t prefix = b1;
-    if (ncand <= (uint32_t)kCandCap) {
-      for (int pass = 1; pass < 3; ++pass) {
-        const int nb = pass_bins(pass), shift = pass_shift(pass), ms = pass_match_shift(pass);
-        for (int i = tid; i < nb; i += NT) hist[i] = 0;
-        __syncthreads();
-        for (uint32_t i = tid; i < ncand; i += NT) {
-          const uint32_t k = cand_key[i];
-          if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        uint32_t bin, k2;
-        select_bin<NT>(hist, nb, krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
-        prefix = extend_prefix(prefix, pass, bin);
-        krem = k2;
-      }
-    } else {
-      // too many elements in the bin for the LDS list: resolve over registers
-      uint32_t key[EPT];
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) key[e] = v[e] != v[e] ? 0u : score_key(v[e]);
-      for (int pass = 1; pass < 3; ++pass) {
-        block_hist<NT, EPT>(key, pass, prefix, hist, &sh[2]);
-        uint32_t bin, k2;
-        select_bin<NT>(hist, pass_bins(pass), krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
-        prefix = extend_prefix(prefix, pass, bin);
-        krem = k2;
-      }
-    }
-    ustar = prefix;
-  }
-  const uint32_t need = krem;  // elements equal to the threshold still to take
-  const float thr = key_to_float(ustar);
-
-  // ---- position-ordered bit masks of the selection
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const uint64_t gm = __ballot(v[e] > thr);
-    const uint64_t qm = __ballot(v[e] == thr);
-    if (lane == 0) {
-      const int word = (base + e * 64) >> 5;
-      gt_mask[word] = (uint32_t)gm;
-      gt_mask[word + 1] = (uint32_t)(gm >> 32);
-      eq_mask[word] = (uint32_t)qm;
-      eq_mask[word + 1] = (uint32_t)(qm >> 32);
+      cum += cnt[j];
     }
   }
   __syncthreads();
+  bin = sh[0];
+  krem_out = sh[1];
+  bin_count = sh[2];
+  __syncthreads();
+}
 
-  // ---- compaction: one scan of packed (above, equal) counts gives every
-  // thread the selected elements before it: all above-threshold ones plus
-  // min(equal ones before it, need)
-  uint32_t gw[WPT], qw[WPT];
-  uint32_t ng = 0, nq = 0;
-#pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    gw[j] = gt_mask[tid * WPT + j];
-    qw[j] = eq_mask[tid * WPT + j];
-    ng += (uint32_t)__popc(gw[j]);
-    nq += (uint32_t)__popc(qw[j]);
-  }
-  const uint32_t packed = (ng << 16) | nq;  // block totals are at most 32768
-  const uint32_t excl = block_inclusive_sum<NT>(packed, wtot) - packed;
-  uint32_t qbefore = excl & 0xffffu;
-  uint32_t slot = (excl >> 16) + (qbefore < need ? qbefore : need);
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_rows_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
+    int64_t ld_out) {
+  static_assert(EPT % 4 == 0 && 2048 % NT == 0 && 1024 % NT == 0, "shape");
+  constexpr int NW = NT / 64, SEG = 64 * EPT, NV = EPT / 4;
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wtot[2 * NW];
+  __shared__ uint32_t sh[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int c = cl_arr[r];
+  c = c < 0 ? 0 : (c > T ? T : c);
   int32_t* orow = out + (int64_t)r * ld_out;
+  uint32_t* hrow = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
+
+  if (c <= kout) {
+    // every position below c ranks above every masked one: the row keeps
+    // [0, c) and then the lowest masked positions
+    for (int i = tid; i < kout; i += NT) orow[i] = i < c ? i + offset : -1;
+    if (hrow)
+      for (int i = tid; i < 2048; i += NT) hrow[i] = 0u;
+    return;
+  }
+
+  // the score histogram is requested first so its latency overlaps the row
+  constexpr int HPT = 2048 / NT;
+  uint32_t hpre[HPT];
+  if (hrow)
 #pragma unroll
-  for (int j = 0; j < WPT; ++j) {
-    const uint32_t qn = (uint32_t)__popc(qw[j]);
-    uint32_t take = need > qbefore ? (need - qbefore < qn ? need - qbefore : qn) : 0u;
-    qbefore += qn;
-    uint32_t bits = gw[j], rest = qw[j];
-    while (take--) {  // the lowest `take` equal positions of this word
-      const uint32_t low = rest & (0u - rest);
-      bits |= low;
-      rest ^= low;
+    for (int j = 0; j < HPT; ++j) hpre[j] = hrow[tid + j * NT];
+
+  // ---- keys: position >= T -> 0 (absent, below every key), masked -> -inf
+  const float* srow = scores + (int64_t)r * ld;
+  const int wbase = w * SEG + 4 * lane;  // position of (step 0, j 0)
+  uint32_t key[EPT];
+  {
+    float v[EPT];
+    const int cv = c & ~3;  // positions [0, cv) come in whole aligned float4 runs
+    if ((((uintptr_t)srow) & 15) == 0) {
+      if (cv >= 4) {
+        const int last = cv - 4;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int t = wbase + 256 * i;
+          const float4 f = *reinterpret_cast<const float4*>(srow + (t < last ? t : last));
+          v[4 * i] = f.x;
+          v[4 * i + 1] = f.y;
+          v[4 * i + 2] = f.z;
+          v[4 * i + 3] = f.w;
+        }
+      }
+      if (cv < c) {  // the ragged end below c (at most 3 positions, one lane)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int t = wbase + 256 * i;
+          if (t == cv) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (t + j < c) v[4 * i + j] = srow[t + j];
+          }
+        }
+      }
+    } else {
+      const unsigned lastu = (unsigned)(c - 1);  // c >= 1 here
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned t = (unsigned)(wbase + 256 * i + j);
+          v[4 * i + j] = srow[t < lastu ? t : lastu];
+        }
     }
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int t = (tid * WPT + j) * 32 + b;
-      if (slot < (uint32_t)kout) orow[slot] = t < c ? t + offset : -1;
-      ++slot;
+    // validity by integer arithmetic (sign bit of t - c), kept out of the
+    // compiler's reach: compare masks hoisted above the loads would hold two
+    // scalar registers per element until the loads return
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = wbase + 256 * i + j;
+        uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
+        asm volatile("" : "+v"(below_c), "+v"(below_t));
+        const uint32_t m = kKeyNegInf & (0u - below_t);
+        const uint32_t k = score_key(v[4 * i + j]);
+        key[4 * i + j] = m ^ ((k ^ m) & (0u - below_c));
+      }
+  }
+
+  // ---- first digit (bits 31..21)
+  uint32_t b1, krem, bcnt;
+  if (hrow) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      hist[tid + j * NT] = hpre[j];
+      mine += hpre[j];
     }
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) hrow[tid + j * NT] = 0u;  // ready for the next score call
+    const uint32_t total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
+    // positions the histogram does not count are -inf
+    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - total, sh, wtot, b1, krem,
+                           bcnt);
+  } else {
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+    if (tid == 0) sh[3] = 0u;
+    __syncthreads();
+    uint32_t ninf = 0;  // -inf keys are counted per thread, not by atomics
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = key[e];
+      if (k != 0u && k != kKeyNegInf) atomicAdd(&hist[k >> 21], 1u);
+      ninf += k == kKeyNegInf ? 1u : 0u;
+    }
+    ninf = wave_sum(ninf);
+    if (lane == 0 && ninf) atomicAdd(&sh[3], ninf);
+    __syncthreads();
+    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, sh[3], sh, wtot, b1, krem, bcnt);
+  }
+
+  // ---- remaining digits, among the keys of the threshold prefix
+  uint32_t prefix = b1;
+  int shift = 21;  // the prefix holds the key bits [shift, 32)
+  // the -inf bin holds only -inf keys (all equal); otherwise stop as soon as
+  // every element of the prefix bin is taken
+  bool done = b1 == kInfBin || bcnt == krem;
+#pragma unroll
+  for (int pass = 1; pass < 3; ++pass) {
+    if (done) break;
+    constexpr int kNb2 = 2048, kNb3 = 1024;
+    const int nshift = pass == 1 ? 10 : 0;
+    const uint32_t nbm = pass == 1 ? (uint32_t)kNb2 - 1u : (uint32_t)kNb3 - 1u;
+    for (int i = tid; i <= (int)nbm; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = key[e];
+      if ((k >> shift) == prefix) atomicAdd(&hist[(k >> nshift) & nbm], 1u);
+    }
+    __syncthreads();
+    uint32_t bin, k2;
+    if (pass == 1)
+      select_bin_r<NT, kNb2>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
+    else
+      select_bin_r<NT, kNb3>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
+    prefix = (prefix << (shift - nshift)) | bin;
+    shift = nshift;
+    krem = k2;
+    done = bcnt == k2;
+  }
+  const uint32_t need = krem;  // elements with the prefix still to take, lowest positions first
+
+  // ---- position-ordered output: wave totals, then one pass of wave scans.
+  // Bit j of g4[i] / q4[i]: element j of step i is above / equal to the
+  // prefix (kept as vector bit masks, not per-element compare results)
+  uint32_t g4[NV], q4[NV];
+  {
+    uint32_t ng = 0, nq = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      uint32_t g = 0, q = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t d = key[4 * i + j] >> shift;
+        g |= (d > prefix ? 1u : 0u) << j;
+        q |= (d == prefix ? 1u : 0u) << j;
+      }
+      asm volatile("" : "+v"(g), "+v"(q));
+      g4[i] = g;
+      q4[i] = q;
+      ng += (uint32_t)__popc(g);
+      nq += (uint32_t)__popc(q);
+    }
+    ng = wave_sum(ng);
+    nq = wave_sum(nq);
+    if (lane == 0) {
+      wtot[w] = ng;
+      wtot[NW + w] = nq;
+    }
+  }
+  __syncthreads();
+  uint32_t ob = 0, eqb = 0, qall = 0;  // selected / equal elements before this wave; all equal
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t gi = wtot[i], qi = wtot[NW + i];
+    if (i < w) {
+      const uint32_t take = need > eqb ? (qi < need - eqb ? qi : need - eqb) : 0u;
+      ob += gi + take;
+      eqb += qi;
+    }
+    qall += qi;
+  }
+  // when every equal element is taken their ranks are not needed
+  const bool all_eq = need >= qall;
+  // the output row is assembled in LDS (the histogram's space is free now)
+  // and written out in one coalesced pass when it fits
+  const bool stage = kout <= 2048;
+  int32_t* dst = stage ? reinterpret_cast<int32_t*>(hist) : orow;
+  int wb = wbase;
+  asm volatile("" : "+v"(wb));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    uint32_t s4 = g4[i];
+    if (all_eq) {
+      s4 |= q4[i];
+    } else if (__ballot(q4[i] != 0u)) {  // equal elements here: rank them in position order
+      const uint32_t nq = (uint32_t)__popc(q4[i]);
+      const uint32_t qincl = wave_inclusive_sum(nq);
+      uint32_t qr = eqb + qincl - nq;  // equal elements before my first one
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((q4[i] >> j) & 1u) {
+          if (qr < need) s4 |= 1u << j;
+          ++qr;
+        }
+      eqb += (uint32_t)__builtin_amdgcn_readlane((int)qincl, 63);
+    }
+    const uint32_t ns = (uint32_t)__popc(s4);
+    const uint32_t sincl = wave_inclusive_sum(ns);
+    uint32_t slot = ob + sincl - ns;
+    const int t0 = wb + 256 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((s4 >> j) & 1u) {
+        const int t = t0 + j;
+        if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
+        ++slot;
+      }
+    ob += (uint32_t)__builtin_amdgcn_readlane((int)sincl, 63);
+  }
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kout; i += NT) orow[i] = dst[i];
   }
 }
 
@@ -519,7 +627,7 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
 }
 
 __global__ __launch_bounds__(1024) void topk_split_b_kernel(
-    int T, const int32_t* __restrict__ cl_arr, const uint32_t* __restrict__ key_hist, int kout,
+    int T, const int32_t* __restrict__ cl_arr, uint32_t* __restrict__ key_hist, int kout,
     int32_t offset, int32_t* __restrict__ out, int64_t ld_out, const uint32_t* __restrict__ ws) {
   constexpr int NT = 1024, NW = 16;
   extern __shared__ uint32_t dyn[];  // sel[nwords] eq[nwords] ckey[cap] cpos[cap]
@@ -659,6 +767,9 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
       ++slot;
     }
   }
+  // every thread read the histogram before the scans above: reset it for the
+  // next score call
+  for (int i = tid; i < 2048; i += NT) key_hist[(int64_t)r * 2048 + i] = 0u;
 }
 
 // ------------------------------------------------- multi-workgroup path
@@ -864,7 +975,6 @@ int64_t ws_row_words(int T) { return idx::kCnt + 2 * n_chunks(T); }
 
 size_t chunked_ws_bytes(int R, int T) { return (size_t)R * (size_t)ws_row_words(T) * 4u; }
 
-bool use_chunked(int T) { return T > 32768 || (chunked_forced() && T > 1024); }
 
 bool use_split(int T, const uint32_t* key_hist) {
   return key_hist && T > 8192 && T <= idx::kSplitMaxT && !chunked_forced();
@@ -878,41 +988,69 @@ size_t split_b_lds(int T) {
   return ((size_t)2 * idx::SplitLayout(T).nwords + 2 * idx::kSplitCandCap) * 4u;
 }
 
+// Kernel B may use more than 64 KB of dynamic LDS; the limit is a per-device
+// function attribute, raised once on each device the library runs on.
+bool set_split_lds_limit() {
+  static std::atomic<uint64_t> done_mask{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done_mask.load(std::memory_order_acquire) & bit)) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&idx::topk_split_b_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)split_b_lds(idx::kSplitMaxT)) != hipSuccess)
+    return false;
+  if (bit) done_mask.fetch_or(bit, std::memory_order_acq_rel);
+  return true;
+}
+
+// Rows up to this width run in one workgroup (keys in registers).
+constexpr int kRowsMaxT = 32768;
+
+void zero_hist(uint32_t* key_hist, int R, hipStream_t st) {
+  const int64_t n = (int64_t)R * 2048;
+  const int64_t g = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(idx::zero_words_kernel, dim3((unsigned)g), dim3(256), 0, st, key_hist, n);
+}
+
 idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int32_t* cl,
-                       const uint32_t* key_hist, int k, int32_t offset, int32_t* out,
+                       uint32_t* key_hist, int k, int32_t offset, int32_t* out,
                        int64_t ld_out, void* ws, size_t ws_bytes, hipStream_t st) {
   if (R == 0 || T == 0) return IDX_OK;
   const int kout = k < T ? k : T;
   if (k >= T) {
     hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T, cl, offset,
                        out, ld_out);
+    if (key_hist) zero_hist(key_hist, R, st);
+    return idx_host::launch_status();
+  }
+  // rows up to 8192 (and longer rows without a score histogram, up to
+  // 32768) in one workgroup; longer rows with a histogram over several
+  // workgroups per row (split); the rest in chunks
+  const bool forced = chunked_forced() && T > 1024;
+  if (!forced && (T <= 8192 || (T <= kRowsMaxT && !use_split(T, key_hist)))) {
+    const dim3 g((unsigned)R);
+    if (T <= 2048)
+      hipLaunchKernelGGL((idx::topk_rows_kernel<256, 8>), g, dim3(256), 0, st, scores, ld, T, cl,
+                         key_hist, kout, offset, out, ld_out);
+    else if (T <= 8192)
+      hipLaunchKernelGGL((idx::topk_rows_kernel<256, 32>), g, dim3(256), 0, st, scores, ld, T, cl,
+                         key_hist, kout, offset, out, ld_out);
+    else
+      hipLaunchKernelGGL((idx::topk_rows_kernel<1024, 32>), g, dim3(1024), 0, st, scores, ld, T,
+                         cl, key_hist, kout, offset, out, ld_out);
     return idx_host::launch_status();
   }
   if (use_split(T, key_hist)) {
     if (R > 65535) return IDX_EUNSUPPORTED;
     if (!ws || ws_bytes < split_ws_bytes(R, T)) return IDX_EINVAL;
     const idx::SplitLayout L(T);
-    static bool lds_attr = false;  // kernel B may use more than 64 KB of dynamic LDS
-    if (!lds_attr) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&idx::topk_split_b_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)split_b_lds(idx::kSplitMaxT));
-      lds_attr = true;
-    }
+    if (!set_split_lds_limit()) return IDX_EHIP;
     hipLaunchKernelGGL(idx::topk_split_a_kernel, dim3((unsigned)L.nparts, (unsigned)R),
                        dim3(idx::kPartNW * 64), 0, st, scores, ld, T, cl, key_hist, kout,
                        (uint32_t*)ws);
     hipLaunchKernelGGL(idx::topk_split_b_kernel, dim3((unsigned)R), dim3(1024), split_b_lds(T), st,
                        T, cl, key_hist, kout, offset, out, ld_out, (const uint32_t*)ws);
-    return idx_host::launch_status();
-  }
-  if (!use_chunked(T)) {
-    if (T <= 8192)
-      hipLaunchKernelGGL((idx::topk_row_kernel<4, 32>), dim3((unsigned)R), dim3(256), 0, st,
-                         scores, ld, T, cl, key_hist, kout, offset, out, ld_out);
-    else
-      hipLaunchKernelGGL((idx::topk_row_kernel<16, 32>), dim3((unsigned)R), dim3(1024), 0, st,
-                         scores, ld, T, cl, key_hist, kout, offset, out, ld_out);
     return idx_host::launch_status();
   }
   if (R > 65535) return IDX_EUNSUPPORTED;
@@ -936,6 +1074,7 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
                      kout, w, rw);
   hipLaunchKernelGGL(idx::topk_chunk_emit_kernel, grid, blk, 0, st, scores, ld, T, cl, key_hist,
                      kout, offset, out, ld_out, (const uint32_t*)w, rw);
+  if (key_hist) zero_hist(key_hist, R, st);
   return idx_host::launch_status();
 }
 
@@ -955,7 +1094,7 @@ extern "C" size_t idx_topk_workspace_size(int R, int T, int index_topk) {
 }
 
 extern "C" idx_status idx_topk(const float* scores, int64_t ld, int R, int T,
-                               const int32_t* compress_lens, const uint32_t* key_hist,
+                               const int32_t* compress_lens, uint32_t* key_hist,
                                int index_topk, int32_t offset, int32_t* out, int64_t ld_out,
                                void* ws, size_t ws_bytes, void* stream) {
   if (R < 0 || T < 0 || index_topk <= 0) return IDX_EINVAL;

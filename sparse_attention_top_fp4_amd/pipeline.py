@@ -63,8 +63,10 @@ class IndexerStep:
         self.kout = min(wl.topk, T)
         self.out = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
         self.topk_ws = self._ws(idx_topk_workspace_size(R, T, wl.topk))
-        # first-digit histogram of the scores, filled by the score kernel
+        # first-digit histogram of the scores, filled by the score kernel and
+        # reset by the top-k that consumes it; cleared once here
         self.key_hist = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
+        idx_clear_key_hist(self.key_hist)
         self.two_level = bool(wl.ctb)
         if self.two_level:
             self.w2 = to_device(inp["w2"])
@@ -104,7 +106,6 @@ class IndexerStep:
         if self.publish:
             idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
-        idx_clear_key_hist(self.key_hist, stream=stream)
         if score_events is not None:
             score_events[0].record(stream)
         idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
@@ -116,7 +117,6 @@ class IndexerStep:
                                         workspace=self.sel_ws, stream=stream)
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
-            idx_clear_key_hist(self.key_hist, stream=stream)
             idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
                       cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
                       stream=stream)

@@ -266,12 +266,17 @@ HIST_CASES = [
     (51, 3, 1, 9000, None, None, 0, 2048, "auto"),       # one workgroup of 1024 per row
     (52, 2, 1, 5000, None, None, 0, 2048, "auto"),       # one workgroup of 256 per row
     (53, 1, 40, 700, 0, None, 0, 64, "auto"),            # prefill rows, many with cl < k
-    (54, 2, 1, 40000, None, None, 0, 2048, "auto"),      # chunked rows
+    (54, 2, 1, 40000, None, None, 0, 2048, "auto"),      # split rows (two kernels)
     (55, 2, 1, 9000, None, None, 0, 2048, "chunked"),
     (56, 2, 1, 20000, None, [[0, 5, 7, 100], [3, 4, 90, 150]], 128, 2048, "auto"),  # few finite
     (57, 2, 1, 20000, None, [list(range(0, 156, 2)), list(range(1, 156, 2))], 128, 2048, "auto"),
     (58, 2, 1, 20000, None, None, 0, 2048, "zero-weights"),  # every score equal: all ties
     (59, 1, 1, 262144, None, None, 0, 2048, "auto"),         # longest split row
+    (60, 2, 1, 32768, None, None, 0, 2048, "auto"),          # widest one-workgroup row
+    (61, 3, 1, 2049, None, None, 0, 100, "auto"),            # just past the smallest instance
+    (62, 2, 1, 8193, None, None, 0, 2048, "auto"),           # just past the 256-thread instance
+    (63, 1, 1, 32771, None, None, 0, 2048, "auto"),          # ragged split row
+    (64, 1, 24, 4096, 0, None, 0, 2048, "auto"),             # prefill rows, cl 0..6
 ]
 
 
@@ -296,11 +301,14 @@ def test_topk_with_score_histogram(idx, case, monkeypatch):
     idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, S, T, dev(c["cl"]), sc,
                   cand_blocks=None if cand is None else dev(cand), cand_block_size=cbs,
                   key_hist=hist)
+    scored_hist = hist.clone()
     kout = min(k, T)
     out = t.full((R, kout), -7, dtype=t.int32, device="cuda")
     idx.idx_topk(sc, T, dev(c["cl"]), k, 3, out, key_hist=hist)
     sync()
     tt = np.arange(T)[None, :]
     counted = np.isfinite(ref) & (tt < c["cl"][:, None])
-    assert np.array_equal(host(hist).astype(np.int64), _host_hist(ref, counted))
+    assert np.array_equal(host(scored_hist).astype(np.int64), _host_hist(ref, counted))
     assert np.array_equal(host(out), oracle.topk(ref, c["cl"], k, 3))
+    # the top-k leaves the histogram cleared for the next score call
+    assert not host(hist).any()
