@@ -111,6 +111,24 @@ idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cach
                      void *stream);
 
 /*
+ * idx_score_topk -- idx_score followed by idx_topk in one launch, for rows of
+ * at most 8192 positions (prefill rows, short contexts): one workgroup
+ * scores a whole row into on-chip memory and ranks it there, so the scores
+ * never travel through device memory unless asked for.  Arguments and
+ * results as idx_score (no candidates, no histogram) and idx_topk (no
+ * workspace): out gets, per row, min(index_topk, T) positions in position
+ * order, t + offset where t < compress_lens[r], else -1.
+ *   scores  device, [B*S][ld] fp32, or NULL: when given, also receives the
+ *           scores exactly as idx_score writes them
+ * Requires D == 128, H in {32, 64} and T <= 8192 (IDX_EUNSUPPORTED
+ * otherwise).
+ */
+idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
+                          int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                          const int32_t *compress_lens, int index_topk, int32_t offset,
+                          int32_t *out, int64_t ld_out, float *scores, int64_t ld, void *stream);
+
+/*
  * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on
  * the stream, before the first idx_score accumulates into it (idx_topk
  * resets it after each use).

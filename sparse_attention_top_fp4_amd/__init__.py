@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["idx_fp4_quant", "idx_score", "idx_clear_key_hist", "idx_topk",
+__all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
            "idx_yarn_cos_sin", "library_path", "load_library", "IdxError", "ROW_BYTES"]
@@ -49,6 +49,8 @@ def load_library():
     L.idx_version.restype = ctypes.c_char_p
     L.idx_fp4_quant.argtypes = [P, i64, P, P, P]
     L.idx_score.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32, P, i64, P, P]
+    L.idx_score_topk.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, i32, ctypes.c_int32,
+                                 P, i64, P, i64, P]
     L.idx_clear_key_hist.argtypes = [P, i32, P]
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
@@ -59,7 +61,7 @@ def load_library():
     L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
                                    i32, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
-    for name in ("idx_fp4_quant", "idx_score", "idx_clear_key_hist", "idx_topk",
+    for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
                  "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin"):
         getattr(L, name).restype = i32
@@ -155,6 +157,35 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
                                     _ptr(key_hist), _stream(stream)), "idx_score")
+
+
+def idx_score_topk(q, w, k_cache, B, S, T, compress_lens, index_topk, offset, out, scores=None,
+                   stream=None):
+    """idx_score then idx_topk in one launch, for T <= 8192: q [B*S, H, 128]
+    bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8, compress_lens [B*S]
+    int32, out [B*S, ld_out] int32 (ld_out >= min(index_topk, T)); scores
+    [B*S, ld] float32 also receives the scores when given."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES or out.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 68] and out [B*S, ld_out]")
+    ld = 0
+    if scores is not None:
+        _dev(scores, "scores", (torch.float32,), 2)
+        if scores.shape[0] != R:
+            raise ValueError("scores must be [B*S, ld]")
+        ld = scores.shape[1]
+    _check(load_library().idx_score_topk(_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S,
+                                         H, D, T, _ptr(compress_lens), index_topk, offset,
+                                         _ptr(out), out.shape[1], _ptr(scores), ld,
+                                         _stream(stream)), "idx_score_topk")
 
 
 def idx_clear_key_hist(key_hist, stream=None):

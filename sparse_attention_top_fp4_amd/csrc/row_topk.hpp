@@ -1,0 +1,288 @@
+// row_topk.hpp -- one workgroup ranks one row whose order keys sit in
+// registers: the threshold search of the Indexer's top-k and the
+// position-ordered output ([IDX, forward]: keep min(index_topk, T) positions
+// by score, re-sort them by position, t + offset where t < compress_lens and
+// -1 otherwise; ties go to the lower position).
+//
+// Layout: wave w owns the positions [w*64*EPT, (w+1)*64*EPT); in step i its
+// lane l holds the four consecutive positions w*64*EPT + i*256 + 4l + [0, 4),
+// key[4i + j] for position +j.  Loads of that layout are contiguous per wave.
+//
+// Search: radix select on the order keys in digits of 11, 11 and 10 bits.
+// Each pass histograms in LDS the next digit of the keys whose higher digits
+// equal the threshold prefix found so far (the first digit may come from the
+// score kernel instead), and the search stops as soon as every element of
+// the prefix bin is taken.  Output: per step, a wave scan of the selected
+// counts gives every selected position its slot in position order.
+#pragma once
+
+#include "idx_common.hpp"
+
+namespace idx {
+
+constexpr uint32_t kInfBin = kKeyNegInf >> 21;  // first-digit bin of -inf
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wtot) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t x = wave_inclusive_sum(v);
+  if (lane == 63) wtot[w] = x;
+  __syncthreads();
+  uint32_t add = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < w) add += wtot[i];
+  __syncthreads();
+  return x + add;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
+  constexpr int NW = NT / 64;
+  const uint32_t x = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += wtot[i];
+  __syncthreads();
+  return s;
+}
+
+// Threshold bin of an LDS histogram of NB bins, bins read into registers at
+// once (thread i owns the bins [NB - (i+1)*BPT, NB - i*BPT), the top bins
+// first): the bin b with count(bins > b) < krem <= count(bins >= b), where
+// bin `xbin` counts `xcnt` more.  Also returns the count of bin b.
+template <int NT, int NB>
+__device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
+                                             uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
+                                             uint32_t& bin, uint32_t& krem_out,
+                                             uint32_t& bin_count) {
+  constexpr int BPT = NB / NT;
+  static_assert(BPT * NT == NB && BPT >= 1, "whole bins per thread");
+  const int hi = NB - (int)threadIdx.x * BPT;  // my bins are [hi - BPT, hi)
+  uint32_t cnt[BPT];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = hi - 1 - j;
+    cnt[j] = hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
+    mine += cnt[j];
+  }
+  const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
+  uint32_t cum = incl - mine;
+  if (cum < krem && krem <= incl) {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (cum < krem && cum + cnt[j] >= krem) {
+        sh[0] = (uint32_t)(hi - 1 - j);
+        sh[1] = krem - cum;
+        sh[2] = cnt[j];
+      }
+      cum += cnt[j];
+    }
+  }
+  __syncthreads();
+  bin = sh[0];
+  krem_out = sh[1];
+  bin_count = sh[2];
+  __syncthreads();
+}
+
+// Position of (step 0, element 0) for this thread.
+template <int EPT>
+__device__ __forceinline__ int row_base() {
+  return (int)(threadIdx.x >> 6) * 64 * EPT + 4 * (int)(threadIdx.x & 63);
+}
+
+// A row with compress_lens c <= kout: every position below c ranks above
+// every masked one, so the row keeps [0, c) and then the lowest masked
+// positions, whatever the scores.
+template <int NT>
+__device__ __forceinline__ void row_keep_prefix(int c, int kout, int32_t offset,
+                                                int32_t* __restrict__ orow) {
+  for (int i = threadIdx.x; i < kout; i += NT) orow[i] = i < c ? i + offset : -1;
+}
+
+// Order keys of the loaded values: position >= T -> 0 (absent, below every
+// key), position >= c -> the key of -inf.  Validity is integer arithmetic
+// (sign bit of t - c) kept out of the compiler's reach: compare masks hoisted
+// above the loads would hold two scalar registers per element.
+template <int EPT>
+__device__ __forceinline__ void row_keys(const float (&v)[EPT], int wbase, int c, int T,
+                                         uint32_t (&key)[EPT]) {
+#pragma unroll
+  for (int i = 0; i < EPT / 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = wbase + 256 * i + j;
+      uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
+      asm volatile("" : "+v"(below_c), "+v"(below_t));
+      const uint32_t m = kKeyNegInf & (0u - below_t);
+      const uint32_t k = score_key(v[4 * i + j]);
+      key[4 * i + j] = m ^ ((k ^ m) & (0u - below_c));
+    }
+}
+
+// Threshold search.  hist: LDS, 2048 words.  counted == 0xffffffff: the
+// first digit is counted here (hist is scratch); otherwise hist already
+// holds the first-digit counts of the row's finite positions, `counted` of
+// them, and the other T - counted positions are -inf.  Result: the keys
+// whose bits [shift, 32) exceed `prefix` are taken, and of those equal to
+// it the `need` lowest positions.
+template <int NT, int EPT>
+__device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t* hist,
+                                           uint32_t counted, int T, int kout, uint32_t* sh,
+                                           uint32_t* wtot, uint32_t& prefix, int& shift,
+                                           uint32_t& need) {
+  static_assert(EPT % 4 == 0 && 2048 % NT == 0 && 1024 % NT == 0, "shape");
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t b1, krem, bcnt;
+  if (counted != 0xffffffffu) {
+    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - counted, sh, wtot, b1,
+                           krem, bcnt);
+  } else {
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+    if (tid == 0) sh[3] = 0u;
+    __syncthreads();
+    uint32_t ninf = 0;  // -inf keys are counted per thread, not by atomics
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = key[e];
+      if (k != 0u && k != kKeyNegInf) atomicAdd(&hist[k >> 21], 1u);
+      ninf += k == kKeyNegInf ? 1u : 0u;
+    }
+    ninf = wave_sum(ninf);
+    if (lane == 0 && ninf) atomicAdd(&sh[3], ninf);
+    __syncthreads();
+    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, sh[3], sh, wtot, b1, krem, bcnt);
+  }
+
+  // remaining digits, among the keys of the threshold prefix
+  prefix = b1;
+  shift = 21;  // the prefix holds the key bits [shift, 32)
+  // the -inf bin holds only -inf keys (all equal); otherwise stop as soon as
+  // every element of the prefix bin is taken
+  bool done = b1 == kInfBin || bcnt == krem;
+#pragma unroll
+  for (int pass = 1; pass < 3; ++pass) {
+    if (done) break;
+    constexpr int kNb2 = 2048, kNb3 = 1024;
+    const int nshift = pass == 1 ? 10 : 0;
+    const uint32_t nbm = pass == 1 ? (uint32_t)kNb2 - 1u : (uint32_t)kNb3 - 1u;
+    for (int i = tid; i <= (int)nbm; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t k = key[e];
+      if ((k >> shift) == prefix) atomicAdd(&hist[(k >> nshift) & nbm], 1u);
+    }
+    __syncthreads();
+    uint32_t bin, k2;
+    if (pass == 1)
+      select_bin_r<NT, kNb2>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
+    else
+      select_bin_r<NT, kNb3>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
+    prefix = (prefix << (shift - nshift)) | bin;
+    shift = nshift;
+    krem = k2;
+    done = bcnt == k2;
+  }
+  need = krem;
+}
+
+// Position-ordered output of the selection: wave totals, then one pass of
+// wave scans.  stage: LDS of at least kout words to assemble the row in (it
+// is then written out in one coalesced pass; its contents may be the search
+// histogram, which is no longer needed), or null to write directly.
+template <int NT, int EPT>
+__device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t prefix, int shift,
+                                         uint32_t need, int c, int kout, int32_t offset,
+                                         int wbase, int32_t* stage, uint32_t* wtot,
+                                         int32_t* __restrict__ orow) {
+  constexpr int NW = NT / 64, NV = EPT / 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // bit j of g4[i] / q4[i]: element j of step i is above / equal to the
+  // prefix (kept as vector bit masks, not per-element compare results)
+  uint32_t g4[NV], q4[NV];
+  {
+    uint32_t ng = 0, nq = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      uint32_t g = 0, q = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t d = key[4 * i + j] >> shift;
+        g |= (d > prefix ? 1u : 0u) << j;
+        q |= (d == prefix ? 1u : 0u) << j;
+      }
+      asm volatile("" : "+v"(g), "+v"(q));
+      g4[i] = g;
+      q4[i] = q;
+      ng += (uint32_t)__popc(g);
+      nq += (uint32_t)__popc(q);
+    }
+    ng = wave_sum(ng);
+    nq = wave_sum(nq);
+    if (lane == 0) {
+      wtot[w] = ng;
+      wtot[NW + w] = nq;
+    }
+  }
+  __syncthreads();
+  uint32_t ob = 0, eqb = 0, qall = 0;  // selected / equal elements before this wave; all equal
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t gi = wtot[i], qi = wtot[NW + i];
+    if (i < w) {
+      const uint32_t take = need > eqb ? (qi < need - eqb ? qi : need - eqb) : 0u;
+      ob += gi + take;
+      eqb += qi;
+    }
+    qall += qi;
+  }
+  // when every equal element is taken their ranks are not needed
+  const bool all_eq = need >= qall;
+  int32_t* dst = stage ? stage : orow;
+  // a fresh copy of the position base: the comparisons with c below are
+  // recomputed here rather than kept alive from the load phase
+  int wb = wbase;
+  asm volatile("" : "+v"(wb));
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    uint32_t s4 = g4[i];
+    if (all_eq) {
+      s4 |= q4[i];
+    } else if (__ballot(q4[i] != 0u)) {  // equal elements here: rank them in position order
+      const uint32_t nq = (uint32_t)__popc(q4[i]);
+      const uint32_t qincl = wave_inclusive_sum(nq);
+      uint32_t qr = eqb + qincl - nq;  // equal elements before my first one
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((q4[i] >> j) & 1u) {
+          if (qr < need) s4 |= 1u << j;
+          ++qr;
+        }
+      eqb += (uint32_t)__builtin_amdgcn_readlane((int)qincl, 63);
+    }
+    const uint32_t ns = (uint32_t)__popc(s4);
+    const uint32_t sincl = wave_inclusive_sum(ns);
+    uint32_t slot = ob + sincl - ns;
+    const int t0 = wb + 256 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((s4 >> j) & 1u) {
+        const int t = t0 + j;
+        if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
+        ++slot;
+      }
+    ob += (uint32_t)__builtin_amdgcn_readlane((int)sincl, 63);
+  }
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kout; i += NT) orow[i] = stage[i];
+  }
+}
+
+}  // namespace idx

@@ -23,6 +23,7 @@
 // fit fp32 for the documented input range), so the only rounding is the
 // fixed-order head sum, which the oracle performs identically.
 #include "idx_common.hpp"
+#include "row_topk.hpp"
 
 namespace idx {
 
@@ -106,12 +107,12 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 // One 64-key tile: 2 key tiles x HT head tiles x 2 K-steps of MFMA, the
-// half-wave swap, and the fixed-order head sum; lane l scores key v0 + l.
-template <int HT, bool CAND>
-__device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
-                                           const int (&sA)[HT][2], const float (&wf)[32 * HT],
-                                           const PosMap<CAND>& pm, float* __restrict__ sbuf, int v0,
-                                           int vbeg, int lane, uint32_t* hist_s) {
+// half-wave swap, and the fixed-order head sum; returns the score of key
+// v0 + lane for lane `lane`.
+template <int HT>
+__device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)[HT][2],
+                                               const int (&sA)[HT][2],
+                                               const float (&wf)[32 * HT], int lane) {
   float sc = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -143,21 +144,43 @@ __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT]
     for (int i = 0; i < 16; ++i)
       sc = __builtin_fmaf(relu_bits(acc[1][i]), wf[32 * ht + 16 + i], sc);
   }
+  return sc;
+}
+
+// Score tile of the one-row kernel: staged in LDS, histogram in LDS.
+template <int HT, bool CAND>
+__device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
+                                           const int (&sA)[HT][2], const float (&wf)[32 * HT],
+                                           const PosMap<CAND>& pm, float* __restrict__ sbuf, int v0,
+                                           int vbeg, int lane, uint32_t* hist_s) {
+  const float sc = head_sum_tile<HT>(kt, A, sA, wf, lane);
   sbuf[v0 - vbeg + lane] = sc;  // staged in LDS, written out when the chunk is done
   if (hist_s && pm.pos(v0 + lane) >= 0) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
 }
 
-template <int HT, bool CAND>
+// Fused top-k of a row scored by one workgroup (rows up to kFusedMaxT).
+struct FusedTopk {
+  int kout;          // min(index_topk, T)
+  int32_t offset;
+  int32_t* out;      // [R][ld_out]
+  int64_t ld_out;
+};
+constexpr int kFusedEPT = 32;                     // keys per thread in the fused ranking
+constexpr int kFusedMaxT = 256 * kFusedEPT;       // 8192
+
+template <int HT, bool CAND, bool TOPK>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
-    float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg) {
+    float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
+    FusedTopk tk) {
   constexpr int H = 32 * HT;
   __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
   __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
   __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
-  extern __shared__ float sbuf[];  // keys_per_wg scores of this workgroup's chunk
+  __shared__ uint32_t wtot[8], sh[4];
+  extern __shared__ __attribute__((aligned(16))) float sbuf[];  // this chunk's scores
   const int r = blockIdx.x;
   const int b = r / S;
   int limit = cl[r];
@@ -171,7 +194,11 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int vtotal = CAND ? n_cand * cbs : limit;
   const int vbeg = blockIdx.y * keys_per_wg;
   const int vend = min(vbeg + keys_per_wg, vtotal);
-  if (vbeg >= vend) return;
+  if (vbeg >= vend) {
+    if (TOPK)  // nothing to score: the row keeps its lowest positions, all masked
+      row_keep_prefix<256>(limit, tk.kout, tk.offset, tk.out + (int64_t)r * tk.ld_out);
+    return;
+  }
   pm.vlim = vend;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -191,8 +218,8 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
   for (int i = 0; i < kTileSets - 1; ++i) buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane);
 
-  uint32_t* hist_s = key_hist ? hist_lds : nullptr;
-  if (key_hist)
+  uint32_t* hist_s = (key_hist || TOPK) ? hist_lds : nullptr;
+  if (hist_s)
     for (int i = tid; i < 2048; i += 256) hist_lds[i] = 0;
 
   // --- quantise the query row: thread (h, g) handles block g of head h
@@ -238,7 +265,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
   }
 
-  float* srow = scores + (int64_t)r * ld;
+  float* srow = scores ? scores + (int64_t)r * ld : nullptr;
   // the loop body is unrolled over the sets so every set index is a
   // compile-time constant (the sets stay in distinct registers)
   while (true) {
@@ -256,7 +283,9 @@ done:
   // stores with the key stream costs far more HBM time than one burst
   __syncthreads();
   const int n = vend - vbeg;
-  if (!CAND && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
+  if (TOPK && !srow) {
+    // scores not wanted: only the ranking below
+  } else if (!CAND && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
     float4* dst = reinterpret_cast<float4*>(srow + vbeg);
     const float4* src = reinterpret_cast<const float4*>(sbuf);
     for (int i = tid; i < (n >> 2); i += 256) dst[i] = src[i];
@@ -267,10 +296,44 @@ done:
       if (p >= 0) srow[p] = sbuf[i];
     }
   }
-  if (key_hist) {
+  if (key_hist && !TOPK) {
     uint32_t* grow = key_hist + (int64_t)r * 2048;
     for (int i = tid; i < 2048; i += 256)
       if (hist_lds[i]) atomicAdd(&grow[i], hist_lds[i]);
+  }
+  if (TOPK) {
+    // the whole row [0, T) is this workgroup's chunk: rank it from LDS
+    int32_t* orow = tk.out + (int64_t)r * tk.ld_out;
+    if (limit <= tk.kout) {
+      row_keep_prefix<256>(limit, tk.kout, tk.offset, orow);
+      return;
+    }
+    const int wbase = row_base<kFusedEPT>();
+    const int last = keys_per_wg - 4;  // keys_per_wg: a multiple of 256, at least T
+    uint32_t key[kFusedEPT];
+    {
+      float v[kFusedEPT];
+#pragma unroll
+      for (int i = 0; i < kFusedEPT / 4; ++i) {
+        const int t = wbase + 256 * i;
+        const float4 f = *reinterpret_cast<const float4*>(sbuf + (t < last ? t : last));
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+      }
+      row_keys<kFusedEPT>(v, wbase, limit, T, key);
+    }
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mine += hist_lds[tid + 256 * j];
+    const uint32_t counted = block_sum<256>(mine, wtot);
+    uint32_t prefix, need;
+    int shift;
+    row_select<256, kFusedEPT>(key, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need);
+    row_emit<256, kFusedEPT>(key, prefix, shift, need, limit, tk.kout, tk.offset, wbase,
+                             tk.kout <= 2048 ? reinterpret_cast<int32_t*>(hist_lds) : nullptr,
+                             wtot, orow);
   }
 }
 
@@ -356,10 +419,37 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                        dim3(256), 0, st, scores, ld, T);
   }
   dim3 grid((unsigned)R, (unsigned)nchunks);
-  auto kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true> : idx::score_kernel<2, false>)
-                      : (cand_blocks ? idx::score_kernel<1, true> : idx::score_kernel<1, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)kpw * sizeof(float), st, q, w, k_cache, k_batch_stride_rows, S, T,
-                     compress_lens, cand_blocks, n_cand, cand_block_size, scores, ld, key_hist,
-                     kpw);
+  auto kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true, false>
+                                     : idx::score_kernel<2, false, false>)
+                      : (cand_blocks ? idx::score_kernel<1, true, false>
+                                     : idx::score_kernel<1, false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)kpw * sizeof(float), st, q, w, k_cache,
+                     k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
+                     cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0});
+  return idx_host::launch_status();
+}
+
+extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                     int64_t k_batch_stride_rows, int B, int S, int H, int D,
+                                     int T, const int32_t* compress_lens, int index_topk,
+                                     int32_t offset, int32_t* out, int64_t ld_out, float* scores,
+                                     int64_t ld, void* stream) {
+  if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0 || index_topk <= 0) return IDX_EINVAL;
+  if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
+  if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
+  if (T > idx::kFusedMaxT) return IDX_EUNSUPPORTED;
+  if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
+  if (!q || !w || !k_cache || !compress_lens || !out) return IDX_EINVAL;
+  const int kout = index_topk < T ? index_topk : T;
+  if (k_batch_stride_rows < T || ld_out < kout || (scores && ld < T)) return IDX_EINVAL;
+  const int64_t R = (int64_t)B * S;
+  if (R > 0x7fffffffLL) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  // one workgroup scores and ranks each whole row
+  const int kpw = (T + 255) / 256 * 256;
+  auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)R, 1u), dim3(256), (size_t)kpw * sizeof(float), st, q,
+                     w, k_cache, k_batch_stride_rows, S, T, compress_lens, nullptr, 0, 0, scores,
+                     ld, nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out});
   return idx_host::launch_status();
 }

@@ -31,6 +31,7 @@
 // Elements equal to -inf (masked positions) are counted with a wave ballot
 // instead of an LDS atomic per element.
 #include "idx_common.hpp"
+#include "row_topk.hpp"
 
 #include <stdlib.h>
 
@@ -40,7 +41,6 @@ namespace idx {
 
 constexpr int kHist1 = 0, kHist2 = 2048, kHist3 = 4096, kCnt = 5120;  // workspace row layout (words)
 constexpr int kChunkNW = 4, kChunkEPT = 16, kChunk = kChunkNW * 64 * kChunkEPT;  // 4096
-constexpr uint32_t kInfBin = kKeyNegInf >> 21;  // first-digit bin of -inf
 
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
@@ -50,34 +50,6 @@ __device__ __forceinline__ int pass_hist_offset(int p) { return p == 0 ? kHist1 
 // Float whose key is k (inverse of score_key for non-NaN keys).
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wtot) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint32_t x = wave_inclusive_sum(v);
-  if (lane == 63) wtot[w] = x;
-  __syncthreads();
-  uint32_t add = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-    if (i < w) add += wtot[i];
-  __syncthreads();
-  return x + add;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
-  constexpr int NW = NT / 64;
-  const uint32_t x = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = x;
-  __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) s += wtot[i];
-  __syncthreads();
-  return s;
 }
 
 // Threshold bin of a histogram (LDS or global): the bin b with
@@ -261,78 +233,29 @@ __device__ __forceinline__ void block_emit(const uint32_t (&key)[EPT], int base,
 }
 
 // ------------------------------------------------ single-workgroup rows
-// One workgroup of NT threads per row of at most NT*EPT positions.  Wave w
-// owns the positions [w*64*EPT, (w+1)*64*EPT); in step i its lane l holds the
-// four consecutive positions w*64*EPT + i*256 + 4l + [0, 4), so every load is
-// a contiguous 1 KB per wave.  The keys stay in registers.  Each radix pass
-// histograms in LDS the next digit of the keys whose higher digits equal the
-// threshold prefix found so far, and the search stops as soon as every
-// element of the prefix bin is taken.  The output is written in position
-// order with wave scans.  key_hist (optional) is the score kernel's
-// first-digit histogram of the row: it is read once and reset to zero for
-// the next score call.  Only positions below compress_lens are loaded; a row
-// with compress_lens <= k keeps all of them and needs no scores at all.
-
-// Threshold bin of an LDS histogram of NB bins, bins read into registers at
-// once (thread i owns the bins [NB - (i+1)*BPT, NB - i*BPT), the top bins
-// first): the bin b with count(bins > b) < krem <= count(bins >= b), where
-// bin `xbin` counts `xcnt` more.  Also returns the count of bin b.
-template <int NT, int NB>
-__device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
-                                             uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
-                                             uint32_t& bin, uint32_t& krem_out,
-                                             uint32_t& bin_count) {
-  constexpr int BPT = NB / NT;
-  static_assert(BPT * NT == NB && BPT >= 1, "whole bins per thread");
-  const int hi = NB - (int)threadIdx.x * BPT;  // my bins are [hi - BPT, hi)
-  uint32_t cnt[BPT];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const int b = hi - 1 - j;
-    cnt[j] = hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
-    mine += cnt[j];
-  }
-  const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
-  uint32_t cum = incl - mine;
-  if (cum < krem && krem <= incl) {
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      if (cum < krem && cum + cnt[j] >= krem) {
-        sh[0] = (uint32_t)(hi - 1 - j);
-        sh[1] = krem - cum;
-        sh[2] = cnt[j];
-      }
-      cum += cnt[j];
-    }
-  }
-  __syncthreads();
-  bin = sh[0];
-  krem_out = sh[1];
-  bin_count = sh[2];
-  __syncthreads();
-}
-
+// One workgroup of NT threads per row of at most NT*EPT positions; the keys
+// stay in registers (layout and method in row_topk.hpp).  key_hist
+// (optional) is the score kernel's first-digit histogram of the row: it is
+// read once and reset to zero for the next score call.  Only positions below
+// compress_lens are loaded; a row with compress_lens <= k keeps all of them
+// and needs no scores at all.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
     int64_t ld_out) {
-  static_assert(EPT % 4 == 0 && 2048 % NT == 0 && 1024 % NT == 0, "shape");
-  constexpr int NW = NT / 64, SEG = 64 * EPT, NV = EPT / 4;
+  constexpr int NV = EPT / 4;
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wtot[2 * NW];
+  __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = blockIdx.x, tid = threadIdx.x;
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
   int32_t* orow = out + (int64_t)r * ld_out;
   uint32_t* hrow = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
 
   if (c <= kout) {
-    // every position below c ranks above every masked one: the row keeps
-    // [0, c) and then the lowest masked positions
-    for (int i = tid; i < kout; i += NT) orow[i] = i < c ? i + offset : -1;
+    row_keep_prefix<NT>(c, kout, offset, orow);
     if (hrow)
       for (int i = tid; i < 2048; i += NT) hrow[i] = 0u;
     return;
@@ -345,9 +268,8 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
 #pragma unroll
     for (int j = 0; j < HPT; ++j) hpre[j] = hrow[tid + j * NT];
 
-  // ---- keys: position >= T -> 0 (absent, below every key), masked -> -inf
   const float* srow = scores + (int64_t)r * ld;
-  const int wbase = w * SEG + 4 * lane;  // position of (step 0, j 0)
+  const int wbase = row_base<EPT>();
   uint32_t key[EPT];
   {
     float v[EPT];
@@ -386,24 +308,10 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
           v[4 * i + j] = srow[t < lastu ? t : lastu];
         }
     }
-    // validity by integer arithmetic (sign bit of t - c), kept out of the
-    // compiler's reach: compare masks hoisted above the loads would hold two
-    // scalar registers per element until the loads return
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = wbase + 256 * i + j;
-        uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
-        asm volatile("" : "+v"(below_c), "+v"(below_t));
-        const uint32_t m = kKeyNegInf & (0u - below_t);
-        const uint32_t k = score_key(v[4 * i + j]);
-        key[4 * i + j] = m ^ ((k ^ m) & (0u - below_c));
-      }
+    row_keys<EPT>(v, wbase, c, T, key);
   }
 
-  // ---- first digit (bits 31..21)
-  uint32_t b1, krem, bcnt;
+  uint32_t counted = 0xffffffffu;  // no histogram: count the first digit here
   if (hrow) {
     uint32_t mine = 0;
 #pragma unroll
@@ -413,141 +321,13 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
     }
 #pragma unroll
     for (int j = 0; j < HPT; ++j) hrow[tid + j * NT] = 0u;  // ready for the next score call
-    const uint32_t total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
-    // positions the histogram does not count are -inf
-    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - total, sh, wtot, b1, krem,
-                           bcnt);
-  } else {
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
-    if (tid == 0) sh[3] = 0u;
-    __syncthreads();
-    uint32_t ninf = 0;  // -inf keys are counted per thread, not by atomics
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = key[e];
-      if (k != 0u && k != kKeyNegInf) atomicAdd(&hist[k >> 21], 1u);
-      ninf += k == kKeyNegInf ? 1u : 0u;
-    }
-    ninf = wave_sum(ninf);
-    if (lane == 0 && ninf) atomicAdd(&sh[3], ninf);
-    __syncthreads();
-    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, sh[3], sh, wtot, b1, krem, bcnt);
+    counted = block_sum<NT>(mine, wtot);  // its barriers also publish hist
   }
-
-  // ---- remaining digits, among the keys of the threshold prefix
-  uint32_t prefix = b1;
-  int shift = 21;  // the prefix holds the key bits [shift, 32)
-  // the -inf bin holds only -inf keys (all equal); otherwise stop as soon as
-  // every element of the prefix bin is taken
-  bool done = b1 == kInfBin || bcnt == krem;
-#pragma unroll
-  for (int pass = 1; pass < 3; ++pass) {
-    if (done) break;
-    constexpr int kNb2 = 2048, kNb3 = 1024;
-    const int nshift = pass == 1 ? 10 : 0;
-    const uint32_t nbm = pass == 1 ? (uint32_t)kNb2 - 1u : (uint32_t)kNb3 - 1u;
-    for (int i = tid; i <= (int)nbm; i += NT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = key[e];
-      if ((k >> shift) == prefix) atomicAdd(&hist[(k >> nshift) & nbm], 1u);
-    }
-    __syncthreads();
-    uint32_t bin, k2;
-    if (pass == 1)
-      select_bin_r<NT, kNb2>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
-    else
-      select_bin_r<NT, kNb3>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
-    prefix = (prefix << (shift - nshift)) | bin;
-    shift = nshift;
-    krem = k2;
-    done = bcnt == k2;
-  }
-  const uint32_t need = krem;  // elements with the prefix still to take, lowest positions first
-
-  // ---- position-ordered output: wave totals, then one pass of wave scans.
-  // Bit j of g4[i] / q4[i]: element j of step i is above / equal to the
-  // prefix (kept as vector bit masks, not per-element compare results)
-  uint32_t g4[NV], q4[NV];
-  {
-    uint32_t ng = 0, nq = 0;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      uint32_t g = 0, q = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t d = key[4 * i + j] >> shift;
-        g |= (d > prefix ? 1u : 0u) << j;
-        q |= (d == prefix ? 1u : 0u) << j;
-      }
-      asm volatile("" : "+v"(g), "+v"(q));
-      g4[i] = g;
-      q4[i] = q;
-      ng += (uint32_t)__popc(g);
-      nq += (uint32_t)__popc(q);
-    }
-    ng = wave_sum(ng);
-    nq = wave_sum(nq);
-    if (lane == 0) {
-      wtot[w] = ng;
-      wtot[NW + w] = nq;
-    }
-  }
-  __syncthreads();
-  uint32_t ob = 0, eqb = 0, qall = 0;  // selected / equal elements before this wave; all equal
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t gi = wtot[i], qi = wtot[NW + i];
-    if (i < w) {
-      const uint32_t take = need > eqb ? (qi < need - eqb ? qi : need - eqb) : 0u;
-      ob += gi + take;
-      eqb += qi;
-    }
-    qall += qi;
-  }
-  // when every equal element is taken their ranks are not needed
-  const bool all_eq = need >= qall;
-  // the output row is assembled in LDS (the histogram's space is free now)
-  // and written out in one coalesced pass when it fits
-  const bool stage = kout <= 2048;
-  int32_t* dst = stage ? reinterpret_cast<int32_t*>(hist) : orow;
-  int wb = wbase;
-  asm volatile("" : "+v"(wb));
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    uint32_t s4 = g4[i];
-    if (all_eq) {
-      s4 |= q4[i];
-    } else if (__ballot(q4[i] != 0u)) {  // equal elements here: rank them in position order
-      const uint32_t nq = (uint32_t)__popc(q4[i]);
-      const uint32_t qincl = wave_inclusive_sum(nq);
-      uint32_t qr = eqb + qincl - nq;  // equal elements before my first one
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((q4[i] >> j) & 1u) {
-          if (qr < need) s4 |= 1u << j;
-          ++qr;
-        }
-      eqb += (uint32_t)__builtin_amdgcn_readlane((int)qincl, 63);
-    }
-    const uint32_t ns = (uint32_t)__popc(s4);
-    const uint32_t sincl = wave_inclusive_sum(ns);
-    uint32_t slot = ob + sincl - ns;
-    const int t0 = wb + 256 * i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((s4 >> j) & 1u) {
-        const int t = t0 + j;
-        if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
-        ++slot;
-      }
-    ob += (uint32_t)__builtin_amdgcn_readlane((int)sincl, 63);
-  }
-  if (stage) {
-    __syncthreads();
-    for (int i = tid; i < kout; i += NT) orow[i] = dst[i];
-  }
+  uint32_t prefix, need;
+  int shift;
+  row_select<NT, EPT>(key, hist, counted, T, kout, sh, wtot, prefix, shift, need);
+  row_emit<NT, EPT>(key, prefix, shift, need, c, kout, offset, wbase,
+                    kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow);
 }
 
 // ---------------------------------------- split path (score histogram given)

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score,
+from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score, idx_score_topk,
                idx_select_candidate_blocks, idx_select_workspace_size, idx_topk,
                idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
@@ -46,7 +46,10 @@ class IndexerStep:
     cycles through them step by step (benchmarks use it so that consecutive
     steps do not read keys left in the 256 MB last-level cache)."""
 
-    def __init__(self, wl, inp: dict, n_caches: int = 1):
+    # rows up to this width are scored and ranked in one launch
+    FUSED_MAX_T = 8192
+
+    def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True):
         torch = _torch()
         self.wl = wl
         R, T = wl.R, wl.T
@@ -59,14 +62,21 @@ class IndexerStep:
         for _ in range(1, n_caches):
             self.caches.append(self.caches[0].clone())
         self.cur = 0
-        self.scores = torch.empty((R, T), dtype=torch.float32, device="cuda")
+        # single-level rows up to FUSED_MAX_T take the fused score + top-k
+        # launch; its scores are written only when kept
+        self.fused = not wl.ctb and T <= self.FUSED_MAX_T
+        self.scores = None
+        if keep_scores or not self.fused:
+            self.scores = torch.empty((R, T), dtype=torch.float32, device="cuda")
         self.kout = min(wl.topk, T)
         self.out = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
         self.topk_ws = self._ws(idx_topk_workspace_size(R, T, wl.topk))
         # first-digit histogram of the scores, filled by the score kernel and
         # reset by the top-k that consumes it; cleared once here
-        self.key_hist = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
-        idx_clear_key_hist(self.key_hist)
+        self.key_hist = None
+        if not self.fused:
+            self.key_hist = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
+            idx_clear_key_hist(self.key_hist)
         self.two_level = bool(wl.ctb)
         if self.two_level:
             self.w2 = to_device(inp["w2"])
@@ -108,6 +118,13 @@ class IndexerStep:
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
         if score_events is not None:
             score_events[0].record(stream)
+        if self.fused:
+            idx_score_topk(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
+                           self.out, scores=self.scores, stream=stream)
+            if score_events is not None:
+                score_events[1].record(stream)
+            self.cur = (self.cur + 1) % len(self.caches)
+            return
         idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                   key_hist=self.key_hist, stream=stream)
         if score_events is not None:

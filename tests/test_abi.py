@@ -116,3 +116,20 @@ def test_host_rope_table_matches_oracle(lib):
                                 YARN["beta_slow"])
         diff = np.abs(a.astype(np.float64) - b.astype(np.float64))
         assert diff.max() <= 2.0 ** -24
+
+
+def test_fused_score_topk_rejects_bad_arguments(lib):
+    d = ctypes.c_void_p(0x1000)
+    # rows wider than one workgroup ranks
+    assert lib.idx_score_topk(d, d, d, 9000, 1, 1, 64, 128, 8193, d, 2048, 0, d, 2048, None, 0,
+                              None) == IDX_EUNSUPPORTED
+    assert lib.idx_score_topk(d, d, d, 64, 1, 1, 64, 128, 64, d, 0, 0, d, 64, None, 0,
+                              None) == IDX_EINVAL  # index_topk 0
+    assert lib.idx_score_topk(d, d, d, 64, 1, 1, 64, 128, 64, d, 32, 0, d, 31, None, 0,
+                              None) == IDX_EINVAL  # ld_out < k_out
+    assert lib.idx_score_topk(d, d, d, 64, 1, 1, 64, 128, 64, d, 32, 0, d, 32, d, 63,
+                              None) == IDX_EINVAL  # scores ld < T
+    assert lib.idx_score_topk(d, d, d, 64, 1, 1, 48, 128, 64, d, 32, 0, d, 32, None, 0,
+                              None) == IDX_EUNSUPPORTED  # 48 heads
+    assert lib.idx_score_topk(None, None, None, 0, 0, 1, 64, 128, 64, None, 32, 0, None, 32,
+                              None, 0, None) == IDX_OK  # no rows

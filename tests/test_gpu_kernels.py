@@ -89,6 +89,11 @@ SCORE_CASES = [
     (4, 1, 70, 64, 17, 17, 0),
     (5, 2, 1, 64, 1, 4, None),
     (6, 4, 1, 32, 4100, 4100, None),
+    # many query rows per sequence: rows share staged key chunks
+    (7, 2, 40, 64, 700, 700, 0),
+    (8, 1, 300, 64, 600, 600, 1500),      # rows cross a key-chunk boundary
+    (9, 1, 19, 32, 1100, 1200, 3000),     # ragged last group of rows
+    (10, 3, 9, 64, 2600, 2700, 8000),
 ]
 
 
@@ -312,3 +317,43 @@ def test_topk_with_score_histogram(idx, case, monkeypatch):
     assert np.array_equal(host(out), oracle.topk(ref, c["cl"], k, 3))
     # the top-k leaves the histogram cleared for the next score call
     assert not host(hist).any()
+
+
+FUSED_CASES = [
+    # (seed, B, S, H, T, start_pos, k, with_scores)
+    (71, 1, 64, 64, 2000, 0, 300, True),        # prefill rows: cl 0..16, every row cl <= k
+    (72, 1, 48, 64, 4096, 12000, 1000, True),   # chunked prefill: cl 3000..3012
+    (73, 3, 1, 64, 8192, None, 2048, False),    # decode at the widest fused row
+    (74, 2, 1, 32, 777, None, 100, True),       # ragged width, 32 heads
+    (75, 1, 20, 64, 1500, 5800, 2048, True),    # index_topk >= T
+    (76, 2, 9, 64, 5000, 15990, 7, False),      # tiny k
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+def test_fused_score_topk_matches_oracle(idx, case):
+    t = torch()
+    seed, B, S, H, T, sp, k, with_scores = case
+    say("fused score+topk", case)
+    c = small_case(seed, B, S, H, T, start_pos=sp)
+    if sp is not None and S == 1:
+        c["cl"][:] = min(T, (sp + 1) // 4)
+    R = B * S
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref, inexact = oracle.score(c["q"], c["w"], kc_ref, B, S, H, T, c["cl"])
+    assert inexact == 0
+    kc = fp4_cache(c["k"])
+    kout = min(k, T)
+    out = t.full((R, kout + 2), -7, dtype=t.int32, device="cuda")
+    sc = t.full((R, T + 1), float("nan"), dtype=t.float32, device="cuda") if with_scores else None
+    idx.idx_score_topk(dev(c["q"]), dev(c["w"]), kc, B, S, T, dev(c["cl"]), k, 5, out, scores=sc)
+    sync()
+    got = host(out)
+    assert np.array_equal(got[:, :kout], oracle.topk(ref, c["cl"], k, 5))
+    assert np.all(got[:, kout:] == -7)  # nothing written past k_out
+    if with_scores:
+        g = host(sc)
+        for r in range(R):
+            n = min(int(c["cl"][r]), T)
+            assert np.array_equal(bits(g[r, :n]), bits(ref[r, :n])), r
+        assert np.all(np.isnan(g[:, T:]))

@@ -20,6 +20,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(cid):
+    """One step with the scores kept; where the step is a single fused
+    launch, also the step the benchmark times (scores not written), whose
+    indices must be the same."""
     from sparse_attention_top_fp4_amd.pipeline import IndexerStep
     wl = workload(cid)
     say("workload", cid, wl.name, "generating")
@@ -27,6 +30,12 @@ def _run(cid):
     say("workload", cid, "step")
     st = IndexerStep(wl, inp)
     st.step()
+    if st.fused:
+        lean = IndexerStep(wl, inp, keep_scores=False)
+        lean.step()
+        sync()
+        assert lean.scores is None
+        assert np.array_equal(host(lean.out), host(st.out))
     sync()
     return wl, inp, st
 
