@@ -37,6 +37,30 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wt
   return x + add;
 }
 
+// Two independent inclusive scans over the block in one exchange (wtot: 2*NT/64 words).
+template <int NT>
+__device__ __forceinline__ void block_inclusive_sum2(uint32_t& a, uint32_t& b, uint32_t* wtot) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  a = wave_inclusive_sum(a);
+  b = wave_inclusive_sum(b);
+  if (lane == 63) {
+    wtot[w] = a;
+    wtot[NW + w] = b;
+  }
+  __syncthreads();
+  uint32_t ad = 0, bd = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < w) {
+      ad += wtot[i];
+      bd += wtot[NW + i];
+    }
+  __syncthreads();
+  a += ad;
+  b += bd;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
   constexpr int NW = NT / 64;

@@ -341,6 +341,10 @@ constexpr int kPartNW = 8, kPartEPT = 16, kPart = kPartNW * 64 * kPartEPT;  // 8
 constexpr int kSplitMaxT = 262144;
 constexpr int kSplitCandCap = 8192;  // list elements resolved in LDS
 
+// LDS index of mask word w (one pad word per 32) and the padded length.
+__host__ __device__ __forceinline__ int split_pad(int w) { return w + (w >> 5); }
+__host__ __device__ __forceinline__ int split_padded_words(int nw) { return nw + (nw >> 5) + 1; }
+
 struct SplitLayout {  // per-row workspace, in 32-bit words
   int64_t nwords;     // T/32 rounded up: above-mask words
   int64_t nparts;
@@ -410,10 +414,14 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
     int T, const int32_t* __restrict__ cl_arr, uint32_t* __restrict__ key_hist, int kout,
     int32_t offset, int32_t* __restrict__ out, int64_t ld_out, const uint32_t* __restrict__ ws) {
   constexpr int NT = 1024, NW = 16;
-  extern __shared__ uint32_t dyn[];  // sel[nwords] eq[nwords] ckey[cap] cpos[cap]
+  // sel[padded nwords] eq[padded nwords] ckey[cap] cpos[cap]; mask word w
+  // lives at w + w/32, so threads owning consecutive runs of words hit
+  // distinct banks
+  extern __shared__ uint32_t dyn[];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t regions[kSplitMaxT / kPart * kPartNW + 1];  // prefix of list counts
   __shared__ uint32_t wtot[NW];
+  __shared__ uint32_t wtot2[2 * NW];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   const SplitLayout L(T);
@@ -422,24 +430,35 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
   c = c < 0 ? 0 : (c > T ? T : c);
   const int nw = (int)L.nwords;
   uint32_t* sel = dyn;
-  uint32_t* eqm = dyn + nw;
-  uint32_t* ckey = dyn + 2 * nw;
+  const int nwp = split_padded_words(nw);
+  uint32_t* eqm = dyn + nwp;
+  uint32_t* ckey = dyn + 2 * nwp;
   uint32_t* cpos = ckey + kSplitCandCap;
   const int nreg = (int)L.nparts * kPartNW;
 
-  for (int i = tid; i < nw; i += NT) {
+  for (int i = tid; i < nwp; i += NT) {
     sel[i] = 0u;
     eqm[i] = 0u;
   }
-  // list counts -> region prefix (thread 0 scans at most 256 entries in LDS)
-  for (int i = tid; i < nreg; i += NT) regions[i + 1] = wrow[L.cnt_off + i];
+  // this thread's words of the above-threshold masks (kernel A's output),
+  // requested first: their latency overlaps the threshold search below.
+  // Unconditional (clamped) loads, all in flight together.
+  constexpr int kMaxWpt = (kSplitMaxT / 32 + NT - 1) / NT;
+  const int wpt = (nw + NT - 1) / NT;
+  uint32_t aw[kMaxWpt];
+#pragma unroll
+  for (int j = 0; j < kMaxWpt; ++j) {
+    const int word = tid * wpt + j;
+    aw[j] = wrow[word < nw ? word : nw - 1];
+  }
+  // list counts -> region prefix, one block scan (at most 256 regions)
+  static_assert(kSplitMaxT / kPart * kPartNW <= NT, "one region per thread");
+  const uint32_t rc = tid < nreg ? wrow[L.cnt_off + tid] : 0u;
   const uint32_t b1 = wrow[L.state_off];
   uint32_t krem = wrow[L.state_off + 1];
-  __syncthreads();
-  if (tid == 0) {
-    regions[0] = 0;
-    for (int i = 1; i <= nreg; ++i) regions[i] += regions[i - 1];
-  }
+  const uint32_t rincl = block_inclusive_sum<NT>(rc, wtot);
+  if (tid < nreg) regions[tid + 1] = rincl;
+  if (tid == 0) regions[0] = 0;
   __syncthreads();
   const uint32_t ncand = regions[nreg];
   const bool only_inf = b1 == kInfBin && key_hist[(int64_t)r * 2048 + kInfBin] == 0u;
@@ -460,11 +479,29 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
       p = cl[2 * j + 1];
     };
     if (in_lds) {
-      for (uint32_t i = tid; i < ncand; i += NT) {
-        uint32_t k, p;
-        fetch(i, k, p);
-        ckey[i] = k;
-        cpos[i] = p;
+      // threads split evenly over the regions; each thread copies every
+      // tpr-th element of its region, eight loads in flight at a time
+      const int tpr = NT / nreg;  // at least 4
+      const int j = tid / tpr, li = tid - j * tpr;
+      if (j < nreg) {
+        const uint32_t base = regions[j], cnt = regions[j + 1] - base;
+        const uint2* src = reinterpret_cast<const uint2*>(wrow + L.cand_off + (int64_t)j * 1024 * 2);
+        for (uint32_t e0 = li; e0 < cnt; e0 += 8u * tpr) {
+          uint2 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t e = e0 + u * tpr;
+            v[u] = src[e < cnt ? e : 0u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t e = e0 + u * tpr;
+            if (e < cnt) {
+              ckey[base + e] = v[u].x;
+              cpos[base + e] = v[u].y;
+            }
+          }
+        }
       }
       __syncthreads();
     }
@@ -479,8 +516,11 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
         if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
-      uint32_t bin, k2;
-      select_bin<NT>(hist, nb, krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
+      uint32_t bin, k2, bc;
+      if (pass == 1)
+        select_bin_r<NT, 2048>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
+      else
+        select_bin_r<NT, 1024>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
       prefix = extend_prefix(prefix, pass, bin);
       krem = k2;
     }
@@ -494,46 +534,50 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
       } else {
         fetch(i, k, p);
       }
-      if (k > ustar) atomicOr(&sel[p >> 5], 1u << (p & 31));
-      else if (k == ustar) atomicOr(&eqm[p >> 5], 1u << (p & 31));
+      if (k > ustar) atomicOr(&sel[split_pad(p >> 5)], 1u << (p & 31));
+      else if (k == ustar) atomicOr(&eqm[split_pad(p >> 5)], 1u << (p & 31));
     }
   }
   const uint32_t need = krem;
   __syncthreads();
 
-  // compaction: thread i owns words [i*WPT, (i+1)*WPT)
-  const int wpt = (nw + NT - 1) / NT;
+  // compaction: thread i owns words [i*wpt, (i+1)*wpt), wpt <= kMaxWpt; the
+  // mask words are loaded together, the output row is assembled in LDS (the
+  // histogram is free now) and written out in one coalesced pass
   uint32_t ng = 0, nq = 0;
-  for (int j = 0; j < wpt; ++j) {
+#pragma unroll
+  for (int j = 0; j < kMaxWpt; ++j) {
     const int word = tid * wpt + j;
-    if (word < nw) {
-      uint32_t a = wrow[word] | sel[word];
-      uint32_t q = eqm[word];
+    if (j < wpt && word < nw) {
+      uint32_t a = aw[j] | sel[split_pad(word)];
+      uint32_t q = eqm[split_pad(word)];
       if (only_inf) {  // the equal elements are the -inf ones: present and not above
         const int rem = T - word * 32;
         const uint32_t present = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
-        q = present & ~wrow[word];
-        a = wrow[word];
+        q = present & ~aw[j];
+        a = aw[j];
       }
-      sel[word] = a;
-      eqm[word] = q;
+      sel[split_pad(word)] = a;
+      eqm[split_pad(word)] = q;
       ng += (uint32_t)__popc(a);
       nq += (uint32_t)__popc(q);
     }
   }
-  const uint32_t packed_g = ng, packed_q = nq;
-  const uint32_t gx = block_inclusive_sum<NT>(packed_g, wtot) - packed_g;
-  uint32_t qbefore = block_inclusive_sum<NT>(packed_q, wtot) - packed_q;
-  uint32_t slot = gx + (qbefore < need ? qbefore : need);
+  uint32_t gi = ng, qi = nq;
+  block_inclusive_sum2<NT>(gi, qi, wtot2);
+  uint32_t qbefore = qi - nq;
+  uint32_t slot = (gi - ng) + (qbefore < need ? qbefore : need);
   int32_t* orow = out + (int64_t)r * ld_out;
+  const bool stage = kout <= 2048;
+  int32_t* dst = stage ? reinterpret_cast<int32_t*>(hist) : orow;
   for (int j = 0; j < wpt; ++j) {
     const int word = tid * wpt + j;
     if (word >= nw) break;
-    const uint32_t qw = eqm[word];
+    const uint32_t qw = eqm[split_pad(word)];
     const uint32_t qn = (uint32_t)__popc(qw);
     uint32_t take = need > qbefore ? (need - qbefore < qn ? need - qbefore : qn) : 0u;
     qbefore += qn;
-    uint32_t bits = sel[word], rest = qw;
+    uint32_t bits = sel[split_pad(word)], rest = qw;
     while (take--) {
       const uint32_t low = rest & (0u - rest);
       bits |= low;
@@ -543,9 +587,13 @@ __global__ __launch_bounds__(1024) void topk_split_b_kernel(
       const int b = __ffs(bits) - 1;
       bits &= bits - 1u;
       const int t = word * 32 + b;
-      if (slot < (uint32_t)kout) orow[slot] = t < c ? t + offset : -1;
+      if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
       ++slot;
     }
+  }
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kout; i += NT) orow[i] = dst[i];
   }
   // every thread read the histogram before the scans above: reset it for the
   // next score call
@@ -765,7 +813,8 @@ size_t split_ws_bytes(int R, int T) {
 }
 
 size_t split_b_lds(int T) {
-  return ((size_t)2 * idx::SplitLayout(T).nwords + 2 * idx::kSplitCandCap) * 4u;
+  return ((size_t)2 * idx::split_padded_words((int)idx::SplitLayout(T).nwords) +
+          2 * idx::kSplitCandCap) * 4u;
 }
 
 // Kernel B may use more than 64 KB of dynamic LDS; the limit is a per-device
