@@ -166,6 +166,26 @@ idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t
                     int64_t ld_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * idx_topk_candidates -- idx_topk for a level-two row, whose finite scores
+ * all lie in its candidate blocks (as idx_score with the same cand_blocks
+ * writes them; [IDX, forward: the level-two mask, then the final topk]).
+ * The result equals idx_topk's on the full row: when at least k_out
+ * candidate positions lie below compress_lens the row is ranked among them
+ * only; otherwise every finite position is kept plus the lowest other
+ * positions, as the full ranking does.
+ *   cand_blocks  device, [R][n_cand] int32 block ids in ascending order
+ *                (idx_select_candidate_blocks' output); ids < 0 or
+ *                >= ceil(T/cand_block_size) are skipped
+ *   scores, compress_lens, index_topk, offset, out, ld_out: as idx_topk
+ * Requires T <= 65536, n_cand <= 2048 and n_cand * cand_block_size <= 8192
+ * (IDX_EUNSUPPORTED otherwise).
+ */
+idx_status idx_topk_candidates(const float *scores, int64_t ld, int R, int T,
+                               const int32_t *compress_lens, const int32_t *cand_blocks,
+                               int n_cand, int cand_block_size, int index_topk, int32_t offset,
+                               int32_t *out, int64_t ld_out, void *stream);
+
+/*
  * Bytes of device workspace idx_select_candidate_blocks needs.
  */
 size_t idx_select_workspace_size(int R, int T, int candidate_topk_blocks, int cand_block_size);

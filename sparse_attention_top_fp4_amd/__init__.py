@@ -15,6 +15,7 @@ import ctypes
 import os
 
 __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
+           "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
            "idx_yarn_cos_sin", "library_path", "load_library", "IdxError", "ROW_BYTES"]
@@ -55,6 +56,8 @@ def load_library():
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
     L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, sz, P]
+    L.idx_topk_candidates.argtypes = [P, i64, i32, i32, P, P, i32, i32, i32, ctypes.c_int32, P,
+                                      i64, P]
     L.idx_select_workspace_size.argtypes = [i32, i32, i32, i32]
     L.idx_select_workspace_size.restype = sz
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
@@ -62,6 +65,7 @@ def load_library():
                                    i32, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
     for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
+                 "idx_topk_candidates",
                  "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin"):
         getattr(L, name).restype = i32
@@ -225,6 +229,26 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
     _check(load_library().idx_topk(_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
                                    _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
                                    _ptr(workspace), wsb, _stream(stream)), "idx_topk")
+
+
+def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, index_topk,
+                        offset, out, stream=None):
+    """Top-k of level-two rows whose finite scores lie in the ascending
+    candidate blocks cand_blocks [R, n_cand] int32 (the output of
+    idx_select_candidate_blocks); scores [R, ld] float32, out [R, ld_out]."""
+    torch = _torch()
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+    _dev(out, "out", (torch.int32,), 2)
+    R = scores.shape[0]
+    if compress_lens.shape[0] != R or cand_blocks.shape[0] != R or out.shape[0] != R:
+        raise ValueError("scores, compress_lens, cand_blocks and out need the same rows")
+    _check(load_library().idx_topk_candidates(_ptr(scores), scores.shape[1], R, T,
+                                              _ptr(compress_lens), _ptr(cand_blocks),
+                                              cand_blocks.shape[1], cand_block_size, index_topk,
+                                              offset, _ptr(out), out.shape[1], _stream(stream)),
+           "idx_topk_candidates")
 
 
 def idx_select_workspace_size(R, T, ctb, cbs) -> int:

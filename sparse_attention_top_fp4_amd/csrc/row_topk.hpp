@@ -216,15 +216,22 @@ __device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t*
   need = krem;
 }
 
+// Identity map from a row's slot to its position.
+struct SamePos {
+  __device__ __forceinline__ int operator()(int v) const { return v; }
+};
+
 // Position-ordered output of the selection: wave totals, then one pass of
 // wave scans.  stage: LDS of at least kout words to assemble the row in (it
 // is then written out in one coalesced pass; its contents may be the search
-// histogram, which is no longer needed), or null to write directly.
-template <int NT, int EPT>
+// histogram, which is no longer needed), or null to write directly.  pos:
+// maps a slot of the ranked row to its position (increasing), which is
+// written as pos + offset below c and as -1 otherwise.
+template <int NT, int EPT, class Pos = SamePos>
 __device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t prefix, int shift,
                                          uint32_t need, int c, int kout, int32_t offset,
                                          int wbase, int32_t* stage, uint32_t* wtot,
-                                         int32_t* __restrict__ orow) {
+                                         int32_t* __restrict__ orow, Pos pos = Pos()) {
   constexpr int NW = NT / 64, NV = EPT / 4;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   // bit j of g4[i] / q4[i]: element j of step i is above / equal to the
@@ -297,7 +304,7 @@ __device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t pr
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if ((s4 >> j) & 1u) {
-        const int t = t0 + j;
+        const int t = pos(t0 + j);
         if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
         ++slot;
       }

@@ -330,6 +330,164 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
                     kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow);
 }
 
+// ------------------------------------------------ level-two rows
+// A level-two row is finite only inside its candidate blocks (idx_score with
+// cand_blocks writes -inf everywhere else).  With at least k_out finite
+// candidates, the top k_out of the whole row are among them, so the row is
+// ranked as the virtual row of its candidate positions: slot v is position
+// ids[v / cbs] * cbs + v % cbs, increasing with v because the ids ascend.
+// With fewer (the literal rule keeps -inf positions then, lowest first), the
+// kept set is every finite position plus the lowest k_out - F others, which
+// all lie below k_out; that case is resolved on an LDS bit map of the row.
+constexpr int kCandMaxT = 65536;    // row width the fallback bit map covers
+constexpr int kCandMaxIds = 2048;   // candidate ids per row held in LDS
+
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_cand_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    const int32_t* __restrict__ cand, int n_cand, int cbs, int kout, int32_t offset,
+    int32_t* __restrict__ out, int64_t ld_out) {
+  constexpr int NV = EPT / 4, WPT = (kCandMaxT / 32) / NT;
+  __shared__ uint32_t hist[2048];
+  __shared__ int32_t ids[kCandMaxIds];
+  __shared__ uint32_t wtot[2 * (NT / 64)];
+  __shared__ uint32_t sh[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  int c = cl_arr[r];
+  c = c < 0 ? 0 : (c > T ? T : c);
+  const int nb = (T + cbs - 1) / cbs;
+  for (int i = tid; i < n_cand; i += NT) {
+    const int id = cand[(int64_t)r * n_cand + i];
+    ids[i] = (id < 0 || id >= nb) ? -1 : id;
+  }
+  __syncthreads();
+  const int V = n_cand * cbs;
+  const float* srow = scores + (int64_t)r * ld;
+  // position of slot v, or -1 (no such block, or past T)
+  auto slot_pos = [&](int v) {
+    if (v >= V) return -1;
+    const int blk = v / cbs, id = ids[blk];
+    if (id < 0) return -1;
+    const int p = id * cbs + (v - blk * cbs);
+    return p < T ? p : -1;
+  };
+  const int wbase = row_base<EPT>();
+  uint32_t key[EPT];
+  uint32_t nfin = 0;
+  {
+    // validity as integer arithmetic on the sign bits, kept out of the
+    // compiler's reach (no per-element compare masks live across the loads)
+    float v[EPT];
+    uint32_t okp[EPT], fin[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int p = slot_pos(wbase + 256 * (e >> 2) + (e & 3));
+      uint32_t ok = (uint32_t)(~p) >> 31;                // p >= 0
+      uint32_t below_c = ((uint32_t)(p - c) >> 31) & ok;  // 0 <= p < c
+      asm volatile("" : "+v"(ok), "+v"(below_c));
+      okp[e] = ok;
+      fin[e] = below_c;
+      v[e] = srow[p & ~(p >> 31)];
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t m = kKeyNegInf & (0u - okp[e]);
+      const uint32_t k = score_key(v[e]);
+      key[e] = m ^ ((k ^ m) & (0u - fin[e]));
+      nfin += fin[e];
+    }
+  }
+  const uint32_t F = block_sum<NT>(nfin, wtot);
+  int32_t* orow = out + (int64_t)r * ld_out;
+  if (F >= (uint32_t)kout) {
+    uint32_t prefix, need;
+    int shift;
+    row_select<NT, EPT>(key, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need);
+    struct CandPos {
+      const int32_t* ids;
+      int cbs;
+      __device__ __forceinline__ int operator()(int v) const {
+        const int blk = v / cbs;
+        return ids[blk] * cbs + (v - blk * cbs);
+      }
+    };
+    row_emit<NT, EPT>(key, prefix, shift, need, c, kout, offset, wbase,
+                      kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow,
+                      CandPos{ids, cbs});
+    return;
+  }
+
+  // ---- fewer finite scores than k_out: bit map of the finite positions
+  uint32_t* fin = hist;  // kCandMaxT bits
+  for (int i = tid; i < kCandMaxT / 32; i += NT) fin[i] = 0u;
+  __syncthreads();
+  int wb = wbase;
+  asm volatile("" : "+v"(wb));
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t k = key[e];
+    if (k != 0u && k != kKeyNegInf) {
+      const int p = slot_pos(wb + 256 * (e >> 2) + (e & 3));
+      atomicOr(&fin[p >> 5], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+  // thread i owns words [i*WPT, (i+1)*WPT): the kept positions are the
+  // finite ones plus the non-finite ones whose rank among non-finite
+  // positions is below k_out - F
+  const int nw = (T + 31) / 32;
+  uint32_t selw[WPT];
+  uint32_t nf = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    selw[j] = w < nw ? fin[w] : 0u;
+    nf += (uint32_t)__popc(selw[j]);
+  }
+  const uint32_t fbefore = block_inclusive_sum<NT>(nf, wtot) - nf;  // finite before my words
+  const uint32_t extra = (uint32_t)kout - F;
+  uint32_t fb = fbefore, ns = 0;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    if (w < nw) {
+      const int rem = T - 32 * w;
+      const uint32_t valid = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
+      uint32_t rest = valid & ~selw[j];
+      const uint32_t rbefore = (uint32_t)(32 * w) - fb;  // non-finite positions before word w
+      uint32_t take = extra > rbefore ? extra - rbefore : 0u;
+      uint32_t kept = selw[j];
+      while (take-- && rest) {  // the lowest non-finite positions of this word
+        const uint32_t low = rest & (0u - rest);
+        kept |= low;
+        rest ^= low;
+      }
+      fb += (uint32_t)__popc(selw[j]);
+      selw[j] = kept;
+      ns += (uint32_t)__popc(kept);
+    }
+  }
+  __syncthreads();  // fin is rewritten as the output stage below
+  uint32_t slot = block_inclusive_sum<NT>(ns, wtot) - ns;
+  int32_t* dst = kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : orow;
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    uint32_t bits = selw[j];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int t = (tid * WPT + j) * 32 + b;
+      if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
+      ++slot;
+    }
+  }
+  if (dst != orow) {
+    __syncthreads();
+    for (int i = tid; i < kout; i += NT) orow[i] = dst[i];
+  }
+  (void)lane;
+}
+
 // ---------------------------------------- split path (score histogram given)
 // Rows of 8193..262144 positions.  Kernel A: one workgroup of 512 threads per
 // 8192-position part of a row writes the part's "above the threshold bin"
@@ -967,4 +1125,34 @@ extern "C" idx_status idx_select_candidate_blocks(const float* scores, int64_t l
   if (s != IDX_OK) return s;
   return topk_launch(bmax, nb, R, nb, clb, nullptr, candidate_topk_blocks, 0, block_ids, ld_ids,
                      tws, tws_bytes, st);
+}
+
+extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R, int T,
+                                          const int32_t* compress_lens, const int32_t* cand_blocks,
+                                          int n_cand, int cand_block_size, int index_topk,
+                                          int32_t offset, int32_t* out, int64_t ld_out,
+                                          void* stream) {
+  if (R < 0 || T < 0 || index_topk <= 0 || n_cand <= 0 || cand_block_size <= 0) return IDX_EINVAL;
+  if (R == 0 || T == 0) return IDX_OK;
+  if (!scores || !compress_lens || !cand_blocks || !out) return IDX_EINVAL;
+  const int kout = index_topk < T ? index_topk : T;
+  if (ld < T || ld_out < kout) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (index_topk >= T) {
+    hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T,
+                       compress_lens, offset, out, ld_out);
+    return idx_host::launch_status();
+  }
+  const int64_t V = (int64_t)n_cand * cand_block_size;
+  if (T > idx::kCandMaxT || n_cand > idx::kCandMaxIds || V > 8192) return IDX_EUNSUPPORTED;
+  // few rows, each a latency chain: many threads per row, few keys each
+  if (V <= 2048)
+    hipLaunchKernelGGL((idx::topk_cand_kernel<256, 8>), dim3((unsigned)R), dim3(256), 0, st,
+                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size, kout,
+                       offset, out, ld_out);
+  else
+    hipLaunchKernelGGL((idx::topk_cand_kernel<1024, 8>), dim3((unsigned)R), dim3(1024), 0, st,
+                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size, kout,
+                       offset, out, ld_out);
+  return idx_host::launch_status();
 }

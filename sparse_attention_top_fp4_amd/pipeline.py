@@ -14,6 +14,7 @@ import numpy as np
 
 from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score, idx_score_topk,
                idx_select_candidate_blocks, idx_select_workspace_size, idx_topk,
+               idx_topk_candidates,
                idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
 
@@ -135,10 +136,10 @@ class IndexerStep:
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
             idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                      cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
-                      stream=stream)
-            idx_topk(self.scores2, wl.T, self.cl, wl.topk, wl.offset, self.out,
-                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
+                      cand_blocks=self.ids, cand_block_size=wl.cbs, stream=stream)
+            # level two: only the candidate positions hold finite scores
+            idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs, wl.topk,
+                                wl.offset, self.out, stream=stream)
         else:
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)

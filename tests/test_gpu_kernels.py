@@ -357,3 +357,42 @@ def test_fused_score_topk_matches_oracle(idx, case):
             n = min(int(c["cl"][r]), T)
             assert np.array_equal(bits(g[r, :n]), bits(ref[r, :n])), r
         assert np.all(np.isnan(g[:, T:]))
+
+
+CAND_TOPK_CASES = [
+    # (seed, R, T, cbs, n_ids, cl, k, nvals)   level-two rows: finite only in the listed blocks
+    (81, 4, 65536, 128, 64, 65536, 2048, 100000),   # the two-level workload's shape
+    (82, 3, 65536, 128, 64, 20000, 2048, 50),       # blocks past cl: many ties
+    (83, 2, 65536, 128, 4, 65536, 2048, 1000),      # 512 finite < k: literal rule keeps -inf
+    (84, 3, 1000, 100, 7, 640, 300, 30),            # ragged blocks, fewer finite than k
+    (85, 2, 4096, 64, 32, 4096, 16, 5),             # small k, heavy ties
+    (86, 2, 300, 32, 8, 300, 500, 10),              # k >= T: closed form
+]
+
+
+@pytest.mark.parametrize("case", CAND_TOPK_CASES)
+def test_topk_candidates_matches_full_row_topk(idx, case):
+    t = torch()
+    seed, R, T, cbs, n_ids, clv, k, nvals = case
+    say("topk candidates", case)
+    rng = np.random.default_rng(seed)
+    nb = (T + cbs - 1) // cbs
+    ids = np.full((R, n_ids), -1, np.int32)
+    sc = np.full((R, T), -np.inf, np.float32)
+    vals = rng.standard_normal(nvals).astype(np.float32)
+    cl = np.full(R, clv, np.int32)
+    for r in range(R):
+        n_valid = n_ids - (r % 2)  # odd rows end with a -1 id
+        chosen = np.sort(rng.choice(nb, size=n_valid, replace=False)).astype(np.int32)
+        ids[r, :n_valid] = chosen
+        for b in chosen:
+            lo, hi = b * cbs, min(T, (b + 1) * cbs, clv)
+            if hi > lo:
+                sc[r, lo:hi] = vals[rng.integers(0, nvals, size=hi - lo)]
+    kout = min(k, T)
+    out = t.full((R, kout + 1), -7, dtype=t.int32, device="cuda")
+    idx.idx_topk_candidates(dev(sc), T, dev(cl), dev(ids), cbs, k, 3, out)
+    sync()
+    got = host(out)
+    assert np.array_equal(got[:, :kout], oracle.topk(sc, cl, k, 3))
+    assert np.all(got[:, kout:] == -7)
