@@ -510,10 +510,10 @@ struct SplitLayout {  // per-row workspace, in 32-bit words
   __host__ __device__ SplitLayout(int T) {
     nwords = ((int64_t)T + 31) / 32;
     nparts = ((int64_t)T + kPart - 1) / kPart;
-    cand_off = nwords;                                   // [nparts][8 waves][1024][2]
+    cand_off = (nwords + 1) & ~(int64_t)1;               // [nparts][8 waves][1024] (key, pos)
     cnt_off = cand_off + nparts * kPartNW * 1024 * 2;    // [nparts][8 waves]
     state_off = cnt_off + nparts * kPartNW;              // b1, krem
-    row_words = state_off + 2;
+    row_words = (state_off + 2 + 1) & ~(int64_t)1;       // rows and lists stay 8-byte aligned
   }
 };
 
@@ -532,10 +532,23 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
   const int base = part * kPart + w * SEG;
   float v[kPartEPT];
   load_vals<kPartEPT>(scores + (int64_t)r * ld, base, T, v);
-  copy_to_lds<NT, 2048>(hist, key_hist + (int64_t)r * 2048);
-  __syncthreads();
   uint32_t b1, krem;
-  select_first_bin<NT>(hist, T, (uint32_t)kout, sh, wtot, b1, krem);
+  {
+    constexpr int HPT = 2048 / NT;
+    uint32_t hv[HPT], mine = 0;
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) hv[j] = key_hist[(int64_t)r * 2048 + threadIdx.x + j * NT];
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) {
+      hist[threadIdx.x + j * NT] = hv[j];
+      mine += hv[j];
+    }
+    const uint32_t total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
+    uint32_t bc;
+    // positions the histogram does not count are -inf
+    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - total, sh, wtot, b1, krem,
+                           bc);
+  }
   if (part == 0 && threadIdx.x == 0) {
     wrow[L.state_off] = b1;
     wrow[L.state_off + 1] = krem;
@@ -543,8 +556,10 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
   const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
   const bool top = b1 >= 2044u;
   const float hi = top ? __builtin_inff() : key_to_float((b1 + 1u) << 21);
-  uint32_t* cand = wrow + L.cand_off + ((int64_t)part * kPartNW + w) * 1024 * 2;
+  uint2* cand = reinterpret_cast<uint2*>(wrow + L.cand_off +
+                                         ((int64_t)part * kPartNW + w) * 1024 * 2);
   uint32_t run = 0;
+  uint32_t myword = 0;  // lane 2e / 2e+1 collects the low / high half of step e's mask
 #pragma unroll
   for (int e = 0; e < kPartEPT; ++e) {
     const int t = base + e * 64 + lane;
@@ -553,25 +568,25 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
     const bool isc = x >= lo && (top || x < hi);
     const uint64_t am = __ballot(above);
     const uint64_t cm = __ballot(isc);
-    if (lane == 0 && base + e * 64 < T) {
-      const int64_t word = (base + e * 64) >> 5;
-      wrow[word] = (uint32_t)am;
-      if (word + 1 < L.nwords) wrow[word + 1] = (uint32_t)(am >> 32);
-    }
-    if (isc) {
-      const uint32_t k = run + lanes_below(cm);
-      cand[2 * k] = score_key(x);
-      cand[2 * k + 1] = (uint32_t)t;
-    }
+    myword = lane == 2 * e ? (uint32_t)am : (lane == 2 * e + 1 ? (uint32_t)(am >> 32) : myword);
+    if (isc) cand[run + lanes_below(cm)] = make_uint2(score_key(x), (uint32_t)t);
     run += (uint32_t)__popcll(cm);
   }
+  // the wave's 32 mask words in one store
+  const int64_t word = (base >> 5) + lane;
+  if (lane < 2 * kPartEPT && word < L.nwords) wrow[word] = myword;
   if (lane == 0) wrow[L.cnt_off + (int64_t)part * kPartNW + w] = run;
 }
 
-__global__ __launch_bounds__(1024) void topk_split_b_kernel(
+#ifndef IDX_SPLIT_B_THREADS
+#define IDX_SPLIT_B_THREADS 1024
+#endif
+constexpr int kSplitBThreads = IDX_SPLIT_B_THREADS;
+
+__global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
     int T, const int32_t* __restrict__ cl_arr, uint32_t* __restrict__ key_hist, int kout,
     int32_t offset, int32_t* __restrict__ out, int64_t ld_out, const uint32_t* __restrict__ ws) {
-  constexpr int NT = 1024, NW = 16;
+  constexpr int NT = kSplitBThreads, NW = NT / 64;
   // sel[padded nwords] eq[padded nwords] ckey[cap] cpos[cap]; mask word w
   // lives at w + w/32, so threads owning consecutive runs of words hit
   // distinct banks
@@ -1036,7 +1051,8 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
     hipLaunchKernelGGL(idx::topk_split_a_kernel, dim3((unsigned)L.nparts, (unsigned)R),
                        dim3(idx::kPartNW * 64), 0, st, scores, ld, T, cl, key_hist, kout,
                        (uint32_t*)ws);
-    hipLaunchKernelGGL(idx::topk_split_b_kernel, dim3((unsigned)R), dim3(1024), split_b_lds(T), st,
+    hipLaunchKernelGGL(idx::topk_split_b_kernel, dim3((unsigned)R), dim3(idx::kSplitBThreads),
+                       split_b_lds(T), st,
                        T, cl, key_hist, kout, offset, out, ld_out, (const uint32_t*)ws);
     return idx_host::launch_status();
   }
