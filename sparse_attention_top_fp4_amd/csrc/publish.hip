@@ -21,6 +21,65 @@
 
 namespace idx {
 
+// Steps after the linear layer, for the 128 threads o = 0..127 of a
+// workgroup (threads beyond them only take the barriers): k_norm, RoPE at
+// `pos`, quantise, store the row at dst.  y_s: the bf16 outputs as floats.
+__device__ __forceinline__ void publish_finish(const float* y_s, uint32_t* z_s, float* inv_s,
+                                               const float* __restrict__ gamma,
+                                               const float* __restrict__ cos_sin, int rd,
+                                               float eps, int pos, uint8_t* __restrict__ dst) {
+  const int o = threadIdx.x;
+
+  if (o == 0) {
+    float yv[kHeadDim];
+#pragma unroll
+    for (int j = 0; j < kHeadDim; ++j) yv[j] = y_s[j];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kHeadDim; ++j) ss = __builtin_fmaf(yv[j], yv[j], ss);
+    const float mean = ss / (float)kHeadDim;
+    *inv_s = 1.0f / sqrtf(mean + eps);
+  }
+  __syncthreads();
+  if (o < kHeadDim) {
+    float v = y_s[o] * *inv_s;
+    v = v * gamma[o];
+    z_s[o] = f32_to_bf16(v);
+  }
+  __syncthreads();
+
+  const int base = kHeadDim - rd;
+  uint32_t r0 = 0, r1 = 0;
+  const bool lead = o < kHeadDim && o >= base && ((o - base) & 1) == 0;
+  if (lead) {
+    const int i = (o - base) >> 1;
+    const float x0 = bf16f(z_s[o]), x1 = bf16f(z_s[o + 1]);
+    const float c = cos_sin[((int64_t)pos * (rd / 2) + i) * 2];
+    const float s = cos_sin[((int64_t)pos * (rd / 2) + i) * 2 + 1];
+    const float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
+    r0 = f32_to_bf16(a - bb);
+    r1 = f32_to_bf16(cc + dd);
+  }
+  __syncthreads();
+  if (lead) {
+    z_s[o] = r0;
+    z_s[o + 1] = r1;
+  }
+  __syncthreads();
+
+  if (o < 4) {
+    uint32_t xp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = z_s[32 * o + 2 * i] | (z_s[32 * o + 2 * i + 1] << 16);
+    uint32_t codes[4];
+    const int e = quant_block32(xp, codes);
+    uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
+    dst[64 + o] = (uint8_t)(e + 127);
+  }
+}
+
 __global__ __launch_bounds__(128) void publish_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
     const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
@@ -68,54 +127,7 @@ __global__ __launch_bounds__(128) void publish_kernel(
   for (; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
   y_s[o] = bf16f(f32_to_bf16(acc));
   __syncthreads();
-
-  if (o == 0) {
-    float yv[kHeadDim];
-#pragma unroll
-    for (int j = 0; j < kHeadDim; ++j) yv[j] = y_s[j];
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kHeadDim; ++j) ss = __builtin_fmaf(yv[j], yv[j], ss);
-    const float mean = ss / (float)kHeadDim;
-    inv_s = 1.0f / sqrtf(mean + eps);
-  }
-  __syncthreads();
-  float v = y_s[o] * inv_s;
-  v = v * gamma[o];
-  z_s[o] = f32_to_bf16(v);
-  __syncthreads();
-
-  const int base = kHeadDim - rd;
-  uint32_t r0 = 0, r1 = 0;
-  const bool lead = o >= base && ((o - base) & 1) == 0;
-  if (lead) {
-    const int i = (o - base) >> 1;
-    const float x0 = bf16f(z_s[o]), x1 = bf16f(z_s[o + 1]);
-    const float c = cos_sin[((int64_t)pos * (rd / 2) + i) * 2];
-    const float s = cos_sin[((int64_t)pos * (rd / 2) + i) * 2 + 1];
-    const float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
-    r0 = f32_to_bf16(a - bb);
-    r1 = f32_to_bf16(cc + dd);
-  }
-  __syncthreads();
-  if (lead) {
-    z_s[o] = r0;
-    z_s[o + 1] = r1;
-  }
-  __syncthreads();
-
-  if (o < 4) {
-    uint32_t xp[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xp[i] = z_s[32 * o + 2 * i] | (z_s[32 * o + 2 * i + 1] << 16);
-    uint32_t codes[4];
-    const int e = quant_block32(xp, codes);
-    uint8_t* dst = kc + ((int64_t)b * kstride + row) * kRowBytes;
-    uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
-    dst[64 + o] = (uint8_t)(e + 127);
-  }
+  publish_finish(y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, kc + ((int64_t)b * kstride + row) * kRowBytes);
 }
 
 }  // namespace idx

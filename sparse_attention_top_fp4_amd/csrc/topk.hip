@@ -717,10 +717,13 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   // compaction: thread i owns words [i*wpt, (i+1)*wpt), wpt <= kMaxWpt; the
   // mask words are loaded together, the output row is assembled in LDS (the
   // histogram is free now) and written out in one coalesced pass
+  // above / equal words of this thread stay in registers for the output
+  uint32_t qv[kMaxWpt];
   uint32_t ng = 0, nq = 0;
 #pragma unroll
   for (int j = 0; j < kMaxWpt; ++j) {
     const int word = tid * wpt + j;
+    qv[j] = 0u;
     if (j < wpt && word < nw) {
       uint32_t a = aw[j] | sel[split_pad(word)];
       uint32_t q = eqm[split_pad(word)];
@@ -730,10 +733,12 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
         q = present & ~aw[j];
         a = aw[j];
       }
-      sel[split_pad(word)] = a;
-      eqm[split_pad(word)] = q;
+      aw[j] = a;
+      qv[j] = q;
       ng += (uint32_t)__popc(a);
       nq += (uint32_t)__popc(q);
+    } else {
+      aw[j] = 0u;
     }
   }
   uint32_t gi = ng, qi = nq;
@@ -743,14 +748,13 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   int32_t* orow = out + (int64_t)r * ld_out;
   const bool stage = kout <= 2048;
   int32_t* dst = stage ? reinterpret_cast<int32_t*>(hist) : orow;
-  for (int j = 0; j < wpt; ++j) {
-    const int word = tid * wpt + j;
-    if (word >= nw) break;
-    const uint32_t qw = eqm[split_pad(word)];
+#pragma unroll
+  for (int j = 0; j < kMaxWpt; ++j) {
+    const uint32_t qw = qv[j];
     const uint32_t qn = (uint32_t)__popc(qw);
     uint32_t take = need > qbefore ? (need - qbefore < qn ? need - qbefore : qn) : 0u;
     qbefore += qn;
-    uint32_t bits = sel[split_pad(word)], rest = qw;
+    uint32_t bits = aw[j], rest = qw;
     while (take--) {
       const uint32_t low = rest & (0u - rest);
       bits |= low;
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1u;
-      const int t = word * 32 + b;
+      const int t = (tid * wpt + j) * 32 + b;
       if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
       ++slot;
     }
