@@ -88,9 +88,12 @@ __device__ __forceinline__ uint32_t e2m1_dequant_bf16(uint32_t code, int e) {
 
 // ---------------------------------------------------------- score keys
 // Order-preserving key of a score: larger score -> larger key; -0 maps to +0.
+// Integer form: negative floats have every bit flipped, the others only the
+// sign bit (the arithmetic shift spreads the sign over the word).
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  uint32_t u = __float_as_uint(s);
+  u = u == 0x80000000u ? 0u : u;
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // ------------------------------------------------------ wave/block scans
@@ -120,6 +123,18 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// v_writelane_b32: the result is `old` with lane `lane` set to the uniform
+// `val`.  This compiler has no builtin for it, so the LLVM intrinsic is
+// declared by name.
+extern "C" __device__ int idx_writelane_i32(int val, int lane, int old) __asm(
+    "llvm.amdgcn.writelane.i32");
+
+// acc + lanes_below(mask), in the two mbcnt instructions
+__device__ __forceinline__ uint32_t lanes_below_acc(uint64_t mask, uint32_t acc) {
+  return (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, acc));
 }
 
 }  // namespace idx

@@ -22,17 +22,50 @@ namespace idx {
 
 constexpr uint32_t kInfBin = kKeyNegInf >> 21;  // first-digit bin of -inf
 
+// An int32 in LDS, addressed as such (32-bit LDS addresses, ds_* access)
+// rather than through a generic pointer.
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+// Exclusive sum of the wave totals of the waves below this one, read back
+// from LDS after the barrier: a short loop for a few waves, otherwise one
+// word per lane and a wave sum.
+template <int NT>
+__device__ __forceinline__ uint32_t waves_below(const uint32_t* wtot, int w) {
+  constexpr int NW = NT / 64;
+  uint32_t add = 0;
+  if constexpr (NW <= 4) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (i < w) add += wtot[i];
+  } else {
+    const int lane = threadIdx.x & 63;
+    const uint32_t t = lane < NW ? wtot[lane] : 0u;
+    add = wave_sum(lane < w ? t : 0u);
+  }
+  return add;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t waves_total(const uint32_t* wtot) {
+  constexpr int NW = NT / 64;
+  uint32_t s = 0;
+  if constexpr (NW <= 4) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) s += wtot[i];
+  } else {
+    const int lane = threadIdx.x & 63;
+    s = wave_sum(lane < NW ? wtot[lane] : 0u);
+  }
+  return s;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wtot) {
-  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_sum(v);
   if (lane == 63) wtot[w] = x;
   __syncthreads();
-  uint32_t add = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-    if (i < w) add += wtot[i];
+  const uint32_t add = waves_below<NT>(wtot, w);
   __syncthreads();
   return x + add;
 }
@@ -49,13 +82,7 @@ __device__ __forceinline__ void block_inclusive_sum2(uint32_t& a, uint32_t& b, u
     wtot[NW + w] = b;
   }
   __syncthreads();
-  uint32_t ad = 0, bd = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i)
-    if (i < w) {
-      ad += wtot[i];
-      bd += wtot[NW + i];
-    }
+  const uint32_t ad = waves_below<NT>(wtot, w), bd = waves_below<NT>(wtot + NW, w);
   __syncthreads();
   a += ad;
   b += bd;
@@ -63,13 +90,10 @@ __device__ __forceinline__ void block_inclusive_sum2(uint32_t& a, uint32_t& b, u
 
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
-  constexpr int NW = NT / 64;
   const uint32_t x = wave_sum(v);
   if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = x;
   __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) s += wtot[i];
+  const uint32_t s = waves_total<NT>(wtot);
   __syncthreads();
   return s;
 }
@@ -130,12 +154,19 @@ __device__ __forceinline__ void row_keep_prefix(int c, int kout, int32_t offset,
 }
 
 // Order keys of the loaded values: position >= T -> 0 (absent, below every
-// key), position >= c -> the key of -inf.  Validity is integer arithmetic
-// (sign bit of t - c) kept out of the compiler's reach: compare masks hoisted
-// above the loads would hold two scalar registers per element.
+// key), position >= c -> the key of -inf.  A wave whose positions all lie
+// below c (c <= T) takes the plain keys.  Otherwise validity is integer
+// arithmetic (sign bit of t - c) kept out of the compiler's reach: compare
+// masks hoisted above the loads would hold two scalar registers per element.
 template <int EPT>
 __device__ __forceinline__ void row_keys(const float (&v)[EPT], int wbase, int c, int T,
                                          uint32_t (&key)[EPT]) {
+  const int wend = (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) + 1) * 64 * EPT;
+  if (wend <= c) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) key[e] = score_key(v[e]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < EPT / 4; ++i)
 #pragma unroll
@@ -154,12 +185,12 @@ __device__ __forceinline__ void row_keys(const float (&v)[EPT], int wbase, int c
 // holds the first-digit counts of the row's finite positions, `counted` of
 // them, and the other T - counted positions are -inf.  Result: the keys
 // whose bits [shift, 32) exceed `prefix` are taken, and of those equal to
-// it the `need` lowest positions.
+// it (bin_count keys) the `need` lowest positions.
 template <int NT, int EPT>
 __device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t* hist,
                                            uint32_t counted, int T, int kout, uint32_t* sh,
                                            uint32_t* wtot, uint32_t& prefix, int& shift,
-                                           uint32_t& need) {
+                                           uint32_t& need, uint32_t& bin_count) {
   static_assert(EPT % 4 == 0 && 2048 % NT == 0 && 1024 % NT == 0, "shape");
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t b1, krem, bcnt;
@@ -214,6 +245,7 @@ __device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t*
     done = bcnt == k2;
   }
   need = krem;
+  bin_count = bcnt;
 }
 
 // Identity map from a row's slot to its position.
@@ -221,98 +253,112 @@ struct SamePos {
   __device__ __forceinline__ int operator()(int v) const { return v; }
 };
 
-// Position-ordered output of the selection: wave totals, then one pass of
-// wave scans.  stage: LDS of at least kout words to assemble the row in (it
-// is then written out in one coalesced pass; its contents may be the search
+// Bits 0..7 of b moved to bits 0, 4, ..., 28.
+__device__ __forceinline__ uint32_t spread4(uint32_t b) {
+  b = (b | (b << 12)) & 0x000F000Fu;
+  b = (b | (b << 6)) & 0x03030303u;
+  return (b | (b << 3)) & 0x11111111u;
+}
+
+// Position-ordered output of the selection.  Keys above the prefix range
+// [lo, lo + span] are taken, and of the keys inside it the `need` at the
+// lowest positions (all of them when that is every tied key).
+//
+// Each wave ballots the taken keys (and, when only some tied keys are taken,
+// the tied ones): mask (i, j) of wave w has bit l for position
+// w*64*EPT + 256i + 4l + j.  The masks go to LDS (mbuf: NT*EPT/16 words).
+// Then thread g owns the 32 positions [32g, 32g + 32): it gathers byte
+// (g % 8) of its step's four masks into one position-ordered word, the block
+// scans the word counts, and the thread writes its positions in order.
+// stage: LDS of at least kout words to assemble the row in (it is then
+// written out in one coalesced pass; its contents may be the search
 // histogram, which is no longer needed), or null to write directly.  pos:
 // maps a slot of the ranked row to its position (increasing), which is
 // written as pos + offset below c and as -1 otherwise.
 template <int NT, int EPT, class Pos = SamePos>
 __device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t prefix, int shift,
-                                         uint32_t need, int c, int kout, int32_t offset,
-                                         int wbase, int32_t* stage, uint32_t* wtot,
+                                         uint32_t need, uint32_t bin_count, int c, int kout,
+                                         int32_t offset, int wbase, uint32_t* mbuf,
+                                         int32_t* stage, uint32_t* wtot,
                                          int32_t* __restrict__ orow, Pos pos = Pos()) {
-  constexpr int NW = NT / 64, NV = EPT / 4;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // bit j of g4[i] / q4[i]: element j of step i is above / equal to the
-  // prefix (kept as vector bit masks, not per-element compare results)
-  uint32_t g4[NV], q4[NV];
+  constexpr int NV = EPT / 4, NMW = NT * EPT / 64;  // masks per block
+  static_assert(EPT % 4 == 0 && EPT <= 32, "shape");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lo = prefix << shift;
+  const uint32_t span = (1u << shift) - 1u;
+  const uint32_t hi = lo + span;
+  const bool all_eq = need >= bin_count;  // every tied key is taken
+  // taken: key > cut (every tied key too when all are taken)
+  const uint32_t cut = all_eq ? lo - 1u : hi;
   {
-    uint32_t ng = 0, nq = 0;
+    uint32_t glo = 0, ghi = 0, qlo = 0, qhi = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      uint32_t g = 0, q = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t d = key[4 * i + j] >> shift;
-        g |= (d > prefix ? 1u : 0u) << j;
-        q |= (d == prefix ? 1u : 0u) << j;
-      }
-      asm volatile("" : "+v"(g), "+v"(q));
-      g4[i] = g;
-      q4[i] = q;
-      ng += (uint32_t)__popc(g);
-      nq += (uint32_t)__popc(q);
+    for (int e = 0; e < EPT; ++e) {
+      const uint64_t m = __ballot(key[e] > cut);
+      glo = (uint32_t)idx_writelane_i32((int)(uint32_t)m, e, (int)glo);
+      ghi = (uint32_t)idx_writelane_i32((int)(uint32_t)(m >> 32), e, (int)ghi);
     }
-    ng = wave_sum(ng);
-    nq = wave_sum(nq);
-    if (lane == 0) {
-      wtot[w] = ng;
-      wtot[NW + w] = nq;
+    if (!all_eq) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const uint64_t m = __ballot(key[e] - lo <= span);
+        qlo = (uint32_t)idx_writelane_i32((int)(uint32_t)m, e, (int)qlo);
+        qhi = (uint32_t)idx_writelane_i32((int)(uint32_t)(m >> 32), e, (int)qhi);
+      }
+    }
+    if (lane < EPT) {
+      reinterpret_cast<uint2*>(mbuf)[w * EPT + lane] = make_uint2(glo, ghi);
+      reinterpret_cast<uint2*>(mbuf)[NMW + w * EPT + lane] = make_uint2(qlo, qhi);
     }
   }
   __syncthreads();
-  uint32_t ob = 0, eqb = 0, qall = 0;  // selected / equal elements before this wave; all equal
+  // thread g: step (g / 8) of the block (wave-major), lanes 8(g % 8) .. + 8
+  constexpr int NG = NT * EPT / 32;
+  const bool has = NG >= NT || tid < NG;
+  uint32_t gw = 0, qw = 0;
+  const int gstep = tid >> 3, gbyte = tid & 7;
+  if (has) {
+    const uint8_t* mb = reinterpret_cast<const uint8_t*>(mbuf);
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t gi = wtot[i], qi = wtot[NW + i];
-    if (i < w) {
-      const uint32_t take = need > eqb ? (qi < need - eqb ? qi : need - eqb) : 0u;
-      ob += gi + take;
-      eqb += qi;
+    for (int j = 0; j < 4; ++j) {
+      gw |= spread4(mb[(gstep * 4 + j) * 8 + gbyte]) << j;
+      if (!all_eq) qw |= spread4(mb[(NMW + gstep * 4 + j) * 8 + gbyte]) << j;
     }
-    qall += qi;
   }
-  // when every equal element is taken their ranks are not needed
-  const bool all_eq = need >= qall;
-  int32_t* dst = stage ? stage : orow;
-  // a fresh copy of the position base: the comparisons with c below are
-  // recomputed here rather than kept alive from the load phase
-  int wb = wbase;
-  asm volatile("" : "+v"(wb));
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    uint32_t s4 = g4[i];
-    if (all_eq) {
-      s4 |= q4[i];
-    } else if (__ballot(q4[i] != 0u)) {  // equal elements here: rank them in position order
-      const uint32_t nq = (uint32_t)__popc(q4[i]);
-      const uint32_t qincl = wave_inclusive_sum(nq);
-      uint32_t qr = eqb + qincl - nq;  // equal elements before my first one
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((q4[i] >> j) & 1u) {
-          if (qr < need) s4 |= 1u << j;
-          ++qr;
-        }
-      eqb += (uint32_t)__builtin_amdgcn_readlane((int)qincl, 63);
+  uint32_t gc = (uint32_t)__popc(gw), qc = (uint32_t)__popc(qw);
+  block_inclusive_sum2<NT>(gc, qc, wtot);
+  // gc, qc: inclusive; before this word
+  const uint32_t gb = gc - (uint32_t)__popc(gw), qb = qc - (uint32_t)__popc(qw);
+  uint32_t sel = gw;
+  if (!all_eq && qw) {  // the first `need` tied keys of the row, by position
+    uint32_t take = need > qb ? need - qb : 0u, rest = qw;
+    while (take && rest) {
+      const uint32_t low = rest & (0u - rest);
+      sel |= low;
+      rest ^= low;
+      --take;
     }
-    const uint32_t ns = (uint32_t)__popc(s4);
-    const uint32_t sincl = wave_inclusive_sum(ns);
-    uint32_t slot = ob + sincl - ns;
-    const int t0 = wb + 256 * i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if ((s4 >> j) & 1u) {
-        const int t = pos(t0 + j);
-        if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
-        ++slot;
-      }
-    ob += (uint32_t)__builtin_amdgcn_readlane((int)sincl, 63);
   }
+  uint32_t slot = gb + (need < qb ? need : qb);
+  // position of bit b: the step's base + 4 * (8 * gbyte + l) + j = base + 32 gbyte + b
+  const int v0 = (gstep / NV) * 64 * EPT + (gstep % NV) * 256 + 32 * gbyte;
+  auto out = [&](auto* dst) {
+    while (sel) {
+      const int b = __ffs(sel) - 1;
+      sel &= sel - 1u;
+      const int t = pos(v0 + b);
+      if (slot < (uint32_t)kout) dst[slot] = t < c ? t + offset : -1;
+      ++slot;
+    }
+  };
   if (stage) {
+    lds_i32* st = (lds_i32*)stage;
+    out(st);
     __syncthreads();
-    for (int i = tid; i < kout; i += NT) orow[i] = stage[i];
+    for (int i = tid; i < kout; i += NT) orow[i] = st[i];
+  } else {
+    out(orow);
   }
 }
 

@@ -167,6 +167,7 @@ struct FusedTopk {
 };
 constexpr int kFusedEPT = 32;                     // keys per thread in the fused ranking
 constexpr int kFusedMaxT = 256 * kFusedEPT;       // 8192
+constexpr int kFusedMaskBytes = kFusedMaxT / 4;   // selection masks of the ranking
 
 template <int HT, bool CAND, bool TOPK>
 __global__ __launch_bounds__(256) void score_kernel(
@@ -328,10 +329,14 @@ done:
 #pragma unroll
     for (int j = 0; j < 8; ++j) mine += hist_lds[tid + 256 * j];
     const uint32_t counted = block_sum<256>(mine, wtot);
-    uint32_t prefix, need;
+    uint32_t prefix, need, bcnt;
     int shift;
-    row_select<256, kFusedEPT>(key, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need);
-    row_emit<256, kFusedEPT>(key, prefix, shift, need, limit, tk.kout, tk.offset, wbase,
+    row_select<256, kFusedEPT>(key, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need,
+                               bcnt);
+    // the score buffer is free once the keys are in registers: it holds the
+    // selection masks (the launch sizes it for them)
+    row_emit<256, kFusedEPT>(key, prefix, shift, need, bcnt, limit, tk.kout, tk.offset, wbase,
+                             reinterpret_cast<uint32_t*>(sbuf),
                              tk.kout <= 2048 ? reinterpret_cast<int32_t*>(hist_lds) : nullptr,
                              wtot, orow);
   }
@@ -447,8 +452,11 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   hipStream_t st = (hipStream_t)stream;
   // one workgroup scores and ranks each whole row
   const int kpw = (T + 255) / 256 * 256;
+  const size_t lds = (size_t)kpw * sizeof(float) > (size_t)idx::kFusedMaskBytes
+                         ? (size_t)kpw * sizeof(float)
+                         : (size_t)idx::kFusedMaskBytes;
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)R, 1u), dim3(256), (size_t)kpw * sizeof(float), st, q,
+  hipLaunchKernelGGL(kern, dim3((unsigned)R, 1u), dim3(256), lds, st, q,
                      w, k_cache, k_batch_stride_rows, S, T, compress_lens, nullptr, 0, 0, scores,
                      ld, nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out});
   return idx_host::launch_status();

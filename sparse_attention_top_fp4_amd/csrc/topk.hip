@@ -246,6 +246,7 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
     int64_t ld_out) {
   constexpr int NV = EPT / 4;
   __shared__ uint32_t hist[2048];
+  __shared__ uint32_t mbuf[NT * EPT / 16];
   __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -323,10 +324,10 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
     for (int j = 0; j < HPT; ++j) hrow[tid + j * NT] = 0u;  // ready for the next score call
     counted = block_sum<NT>(mine, wtot);  // its barriers also publish hist
   }
-  uint32_t prefix, need;
+  uint32_t prefix, need, bcnt;
   int shift;
-  row_select<NT, EPT>(key, hist, counted, T, kout, sh, wtot, prefix, shift, need);
-  row_emit<NT, EPT>(key, prefix, shift, need, c, kout, offset, wbase,
+  row_select<NT, EPT>(key, hist, counted, T, kout, sh, wtot, prefix, shift, need, bcnt);
+  row_emit<NT, EPT>(key, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
                     kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow);
 }
 
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   constexpr int NV = EPT / 4, WPT = (kCandMaxT / 32) / NT;
   __shared__ uint32_t hist[2048];
   __shared__ int32_t ids[kCandMaxIds];
+  __shared__ uint32_t mbuf[NT * EPT / 16];
   __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -400,9 +402,9 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   const uint32_t F = block_sum<NT>(nfin, wtot);
   int32_t* orow = out + (int64_t)r * ld_out;
   if (F >= (uint32_t)kout) {
-    uint32_t prefix, need;
+    uint32_t prefix, need, bcnt;
     int shift;
-    row_select<NT, EPT>(key, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need);
+    row_select<NT, EPT>(key, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
     struct CandPos {
       const int32_t* ids;
       int cbs;
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
         return ids[blk] * cbs + (v - blk * cbs);
       }
     };
-    row_emit<NT, EPT>(key, prefix, shift, need, c, kout, offset, wbase,
+    row_emit<NT, EPT>(key, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
                       kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow,
                       CandPos{ids, cbs});
     return;
@@ -974,6 +976,9 @@ bool chunked_forced() {
   return e && e[0] == 'c';
 }
 
+// Rows up to this width run in one workgroup (keys in registers).
+constexpr int kRowsMaxT = 32768;
+
 int64_t n_chunks(int T) { return ((int64_t)T + idx::kChunk - 1) / idx::kChunk; }
 
 int64_t ws_row_words(int T) { return idx::kCnt + 2 * n_chunks(T); }
@@ -981,8 +986,9 @@ int64_t ws_row_words(int T) { return idx::kCnt + 2 * n_chunks(T); }
 size_t chunked_ws_bytes(int R, int T) { return (size_t)R * (size_t)ws_row_words(T) * 4u; }
 
 
+// Longer rows with a score histogram: several workgroups per row.
 bool use_split(int T, const uint32_t* key_hist) {
-  return key_hist && T > 8192 && T <= idx::kSplitMaxT && !chunked_forced();
+  return key_hist && T > kRowsMaxT && T <= idx::kSplitMaxT && !chunked_forced();
 }
 
 size_t split_ws_bytes(int R, int T) {
@@ -1010,9 +1016,6 @@ bool set_split_lds_limit() {
   return true;
 }
 
-// Rows up to this width run in one workgroup (keys in registers).
-constexpr int kRowsMaxT = 32768;
-
 void zero_hist(uint32_t* key_hist, int R, hipStream_t st) {
   const int64_t n = (int64_t)R * 2048;
   const int64_t g = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
@@ -1030,11 +1033,10 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
     if (key_hist) zero_hist(key_hist, R, st);
     return idx_host::launch_status();
   }
-  // rows up to 8192 (and longer rows without a score histogram, up to
-  // 32768) in one workgroup; longer rows with a histogram over several
-  // workgroups per row (split); the rest in chunks
+  // rows up to 32768 in one workgroup; longer rows with a histogram over
+  // several workgroups per row (split); the rest in chunks
   const bool forced = chunked_forced() && T > 1024;
-  if (!forced && (T <= 8192 || (T <= kRowsMaxT && !use_split(T, key_hist)))) {
+  if (!forced && T <= kRowsMaxT) {
     const dim3 g((unsigned)R);
     if (T <= 2048)
       hipLaunchKernelGGL((idx::topk_rows_kernel<256, 8>), g, dim3(256), 0, st, scores, ld, T, cl,
@@ -1088,7 +1090,7 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
 size_t topk_ws_bytes(int R, int T, int k) {
   if (R <= 0 || T <= 0 || k >= T || T <= 1024) return 0;
   size_t n = chunked_ws_bytes(R, T);
-  if (T > 8192 && T <= idx::kSplitMaxT) n = n > split_ws_bytes(R, T) ? n : split_ws_bytes(R, T);
+  if (T > kRowsMaxT && T <= idx::kSplitMaxT) n = n > split_ws_bytes(R, T) ? n : split_ws_bytes(R, T);
   return n;
 }
 
