@@ -98,26 +98,20 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
   return s;
 }
 
-// Threshold bin of an LDS histogram of NB bins, bins read into registers at
-// once (thread i owns the bins [NB - (i+1)*BPT, NB - i*BPT), the top bins
-// first): the bin b with count(bins > b) < krem <= count(bins >= b), where
-// bin `xbin` counts `xcnt` more.  Also returns the count of bin b.
+// Threshold bin of NB bin counts held in registers, thread i owning the
+// bins [NB - (i+1)*BPT, NB - i*BPT), the top bins first (cnt[j]: bin
+// NB - 1 - i*BPT - j): the bin b with count(bins > b) < krem <=
+// count(bins >= b).  Also returns the count of bin b.
 template <int NT, int NB>
-__device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
-                                             uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
-                                             uint32_t& bin, uint32_t& krem_out,
-                                             uint32_t& bin_count) {
+__device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], uint32_t krem,
+                                                uint32_t* sh, uint32_t* wtot, uint32_t& bin,
+                                                uint32_t& krem_out, uint32_t& bin_count) {
   constexpr int BPT = NB / NT;
   static_assert(BPT * NT == NB && BPT >= 1, "whole bins per thread");
   const int hi = NB - (int)threadIdx.x * BPT;  // my bins are [hi - BPT, hi)
-  uint32_t cnt[BPT];
   uint32_t mine = 0;
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const int b = hi - 1 - j;
-    cnt[j] = hist[b] + ((uint32_t)b == xbin ? xcnt : 0u);
-    mine += cnt[j];
-  }
+  for (int j = 0; j < BPT; ++j) mine += cnt[j];
   const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
   uint32_t cum = incl - mine;
   if (cum < krem && krem <= incl) {
@@ -138,10 +132,31 @@ __device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem
   __syncthreads();
 }
 
-// Position of (step 0, element 0) for this thread.
+// The same from an LDS histogram, where bin `xbin` counts `xcnt` more and
+// bin b is stored at hist[b ^ flip].
+template <int NT, int NB>
+__device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
+                                             uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
+                                             uint32_t& bin, uint32_t& krem_out,
+                                             uint32_t& bin_count, uint32_t flip = 0u) {
+  constexpr int BPT = NB / NT;
+  const int hi = NB - (int)threadIdx.x * BPT;
+  uint32_t cnt[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = hi - 1 - j;
+    cnt[j] = hist[(uint32_t)b ^ flip] + ((uint32_t)b == xbin ? xcnt : 0u);
+  }
+  select_bin_regs<NT, NB>(cnt, krem, sh, wtot, bin, krem_out, bin_count);
+}
+
+// Row layout: element e of lane l of wave w is position w*64*EPT + 64e + l,
+// so each element's loads are 64 consecutive words and each element's
+// ballot is a position-ordered 64-bit word of the row's bit map.  Returns
+// the position of element 0.
 template <int EPT>
 __device__ __forceinline__ int row_base() {
-  return (int)(threadIdx.x >> 6) * 64 * EPT + 4 * (int)(threadIdx.x & 63);
+  return (int)(threadIdx.x >> 6) * 64 * EPT + (int)(threadIdx.x & 63);
 }
 
 // A row with compress_lens c <= kout: every position below c ranks above
@@ -153,41 +168,132 @@ __device__ __forceinline__ void row_keep_prefix(int c, int kout, int32_t offset,
   for (int i = threadIdx.x; i < kout; i += NT) orow[i] = i < c ? i + offset : -1;
 }
 
-// Order keys of the loaded values: position >= T -> 0 (absent, below every
-// key), position >= c -> the key of -inf.  A wave whose positions all lie
-// below c (c <= T) takes the plain keys.  Otherwise validity is integer
-// arithmetic (sign bit of t - c) kept out of the compiler's reach: compare
-// masks hoisted above the loads would hold two scalar registers per element.
-template <int EPT>
-__device__ __forceinline__ void row_keys(const float (&v)[EPT], int wbase, int c, int T,
-                                         uint32_t (&key)[EPT]) {
-  const int wend = (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) + 1) * 64 * EPT;
-  if (wend <= c) {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) key[e] = score_key(v[e]);
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < EPT / 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = wbase + 256 * i + j;
-      uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
-      asm volatile("" : "+v"(below_c), "+v"(below_t));
-      const uint32_t m = kKeyNegInf & (0u - below_t);
-      const uint32_t k = score_key(v[4 * i + j]);
-      key[4 * i + j] = m ^ ((k ^ m) & (0u - below_c));
+// ------------------------------------------------ keys as float ranges
+// The search runs on order keys (score_key), but the scores stay floats in
+// registers: a range of keys is the range of floats with those keys, so one
+// float compare tests "key > cut" and two test "key in [lo, hi]", and the
+// next digit of a key is read from the float's bits (within one first-digit
+// bin every float has the same sign; -0 falls in the bin of +0 and has the
+// same digits as +0).  Absent positions hold NaN, which no compare admits.
+constexpr uint32_t kKeyPosInf = 0xFF800000u;  // order key of +inf
+
+// Float whose key is k, for keys of non-NaN floats.
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Least float whose key is >= k (k <= kKeyPosInf): -inf below the key of
+// -inf; +0 for the key 0x7fffffff, which no float has (-0 takes +0's key).
+__device__ __forceinline__ float key_floor_float(uint32_t k) {
+  if (k <= kKeyNegInf) return -__builtin_inff();
+  return key_to_float(k == 0x7fffffffu ? 0x80000000u : k);
+}
+
+// Greatest float whose key is <= k (k >= kKeyNegInf).
+__device__ __forceinline__ float key_ceil_float(uint32_t k) {
+  if (k >= kKeyPosInf) return __builtin_inff();
+  return key_to_float(k == 0x7fffffffu ? 0x7ffffffeu : k);
+}
+
+// Floats whose keys lie in [lo, hi]: x >= f_lo && x <= f_hi.
+struct KeyRange {
+  float f_lo, f_hi;
+  __device__ __forceinline__ KeyRange(uint32_t lo, uint32_t hi) {
+    if (hi < kKeyNegInf || lo > kKeyPosInf) {  // only NaN keys: empty
+      f_lo = __builtin_inff();
+      f_hi = -__builtin_inff();
+    } else {
+      f_lo = key_floor_float(lo);
+      f_hi = key_ceil_float(hi);
     }
+  }
+  __device__ __forceinline__ bool has(float x) const { return x >= f_lo && x <= f_hi; }
+};
+
+// x >= key_above(cut)  <=>  key(x) > cut, for non-NaN x (NaN: never).
+__device__ __forceinline__ float key_above(uint32_t cut) {
+  if (cut >= kKeyPosInf) return __builtin_nanf("");
+  return key_floor_float(cut + 1u);
+}
+
+// Scores of the positions: position >= T -> NaN (absent), position >= c ->
+// -inf.  A wave whose positions all lie below c (c <= T) keeps them as they
+// are.  Otherwise validity is integer arithmetic (sign bit of t - c) kept
+// out of the compiler's reach: compare masks hoisted above the loads would
+// hold two scalar registers per element.
+template <int EPT>
+__device__ __forceinline__ void row_vals(float (&v)[EPT], int wbase, int c, int T) {
+  const int wend = (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) + 1) * 64 * EPT;
+  if (wend <= c) return;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int t = wbase + 64 * e;
+    uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
+    asm volatile("" : "+v"(below_c), "+v"(below_t));
+    // masked: -inf below T, NaN (0x7fc00000) past it
+    const uint32_t m = 0xff800000u ^ (0x80400000u & (below_t - 1u));
+    const uint32_t u = __float_as_uint(v[e]);
+    v[e] = __uint_as_float(m ^ ((u ^ m) & (0u - below_c)));
+  }
+}
+
+// The remaining digits of the threshold search, among the scores whose
+// first digit is b1 (krem of them still to take, bcnt in that bin):
+// histograms in LDS of the next digit of the scores matching the prefix so
+// far, stopping as soon as every element of the prefix bin is taken.  The
+// -inf bin holds only -inf scores (all equal), so it needs no further digit.
+// hist: 2048 words of LDS, already zero when hist_zeroed.  Result: the keys
+// whose bits [shift, 32) exceed `prefix` are taken, and of those equal to
+// it (bin_count keys) the `need` lowest positions.
+template <int NT, int EPT>
+__device__ __forceinline__ void row_refine(const float (&v)[EPT], uint32_t* hist,
+                                           bool hist_zeroed, uint32_t* sh, uint32_t* wtot,
+                                           uint32_t b1, uint32_t krem, uint32_t bcnt,
+                                           uint32_t& prefix, int& shift, uint32_t& need,
+                                           uint32_t& bin_count) {
+  const int tid = threadIdx.x;
+  prefix = b1;
+  shift = 21;  // the prefix holds the key bits [shift, 32)
+  // the digits of a negative score are the complement of its bits
+  const uint32_t neg = (b1 & 0x400u) ? 0u : 0xffffffffu;
+  bool done = b1 == kInfBin || bcnt == krem;
+#pragma unroll
+  for (int pass = 1; pass < 3; ++pass) {
+    if (done) break;
+    constexpr int kNb2 = 2048, kNb3 = 1024;
+    const int nshift = pass == 1 ? 10 : 0;
+    const uint32_t nbm = pass == 1 ? (uint32_t)kNb2 - 1u : (uint32_t)kNb3 - 1u;
+    if (pass > 1 || !hist_zeroed) {
+      for (int i = tid; i <= (int)nbm; i += NT) hist[i] = 0u;
+      __syncthreads();
+    }
+    // counted by the digit of the bits (the key digit of a negative score is
+    // its complement, applied when the bins are read)
+    const KeyRange in(prefix << shift, (prefix << shift) | ((1u << shift) - 1u));
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      if (in.has(v[e])) atomicAdd(&hist[(__float_as_uint(v[e]) >> nshift) & nbm], 1u);
+    __syncthreads();
+    uint32_t bin, k2;
+    if (pass == 1)
+      select_bin_r<NT, kNb2>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt, neg & nbm);
+    else
+      select_bin_r<NT, kNb3>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt, neg & nbm);
+    prefix = (prefix << (shift - nshift)) | bin;
+    shift = nshift;
+    krem = k2;
+    done = bcnt == k2;
+  }
+  need = krem;
+  bin_count = bcnt;
 }
 
 // Threshold search.  hist: LDS, 2048 words.  counted == 0xffffffff: the
 // first digit is counted here (hist is scratch); otherwise hist already
 // holds the first-digit counts of the row's finite positions, `counted` of
-// them, and the other T - counted positions are -inf.  Result: the keys
-// whose bits [shift, 32) exceed `prefix` are taken, and of those equal to
-// it (bin_count keys) the `need` lowest positions.
+// them, and the other T - counted positions are -inf.  Result as row_refine.
 template <int NT, int EPT>
-__device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t* hist,
+__device__ __forceinline__ void row_select(const float (&v)[EPT], uint32_t* hist,
                                            uint32_t counted, int T, int kout, uint32_t* sh,
                                            uint32_t* wtot, uint32_t& prefix, int& shift,
                                            uint32_t& need, uint32_t& bin_count) {
@@ -201,51 +307,19 @@ __device__ __forceinline__ void row_select(const uint32_t (&key)[EPT], uint32_t*
     for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
     if (tid == 0) sh[3] = 0u;
     __syncthreads();
-    uint32_t ninf = 0;  // -inf keys are counted per thread, not by atomics
+    uint32_t ninf = 0;  // -inf scores are counted per thread, not by atomics
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = key[e];
-      if (k != 0u && k != kKeyNegInf) atomicAdd(&hist[k >> 21], 1u);
-      ninf += k == kKeyNegInf ? 1u : 0u;
+      const float x = v[e];
+      if (x > -__builtin_inff()) atomicAdd(&hist[score_key(x) >> 21], 1u);  // not NaN, not -inf
+      ninf += x == -__builtin_inff() ? 1u : 0u;
     }
     ninf = wave_sum(ninf);
     if (lane == 0 && ninf) atomicAdd(&sh[3], ninf);
     __syncthreads();
     select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, sh[3], sh, wtot, b1, krem, bcnt);
   }
-
-  // remaining digits, among the keys of the threshold prefix
-  prefix = b1;
-  shift = 21;  // the prefix holds the key bits [shift, 32)
-  // the -inf bin holds only -inf keys (all equal); otherwise stop as soon as
-  // every element of the prefix bin is taken
-  bool done = b1 == kInfBin || bcnt == krem;
-#pragma unroll
-  for (int pass = 1; pass < 3; ++pass) {
-    if (done) break;
-    constexpr int kNb2 = 2048, kNb3 = 1024;
-    const int nshift = pass == 1 ? 10 : 0;
-    const uint32_t nbm = pass == 1 ? (uint32_t)kNb2 - 1u : (uint32_t)kNb3 - 1u;
-    for (int i = tid; i <= (int)nbm; i += NT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t k = key[e];
-      if ((k >> shift) == prefix) atomicAdd(&hist[(k >> nshift) & nbm], 1u);
-    }
-    __syncthreads();
-    uint32_t bin, k2;
-    if (pass == 1)
-      select_bin_r<NT, kNb2>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
-    else
-      select_bin_r<NT, kNb3>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt);
-    prefix = (prefix << (shift - nshift)) | bin;
-    shift = nshift;
-    krem = k2;
-    done = bcnt == k2;
-  }
-  need = krem;
-  bin_count = bcnt;
+  row_refine<NT, EPT>(v, hist, false, sh, wtot, b1, krem, bcnt, prefix, shift, need, bin_count);
 }
 
 // Identity map from a row's slot to its position.
@@ -253,56 +327,48 @@ struct SamePos {
   __device__ __forceinline__ int operator()(int v) const { return v; }
 };
 
-// Bits 0..7 of b moved to bits 0, 4, ..., 28.
-__device__ __forceinline__ uint32_t spread4(uint32_t b) {
-  b = (b | (b << 12)) & 0x000F000Fu;
-  b = (b | (b << 6)) & 0x03030303u;
-  return (b | (b << 3)) & 0x11111111u;
-}
-
 // Position-ordered output of the selection.  Keys above the prefix range
 // [lo, lo + span] are taken, and of the keys inside it the `need` at the
 // lowest positions (all of them when that is every tied key).
 //
-// Each wave ballots the taken keys (and, when only some tied keys are taken,
-// the tied ones): mask (i, j) of wave w has bit l for position
-// w*64*EPT + 256i + 4l + j.  The masks go to LDS (mbuf: NT*EPT/16 words).
-// Then thread g owns the 32 positions [32g, 32g + 32): it gathers byte
-// (g % 8) of its step's four masks into one position-ordered word, the block
-// scans the word counts, and the thread writes its positions in order.
+// Each wave ballots the taken scores (and, when only some tied scores are
+// taken, the tied ones): the ballot of element e is the bit map of the
+// positions w*64*EPT + 64e + [0, 64).  The maps go to LDS (mbuf: NT*EPT/16
+// words); then thread g takes the word of positions [32g, 32g + 32), the
+// block scans the word counts, and the thread writes its positions in order.
 // stage: LDS of at least kout words to assemble the row in (it is then
 // written out in one coalesced pass; its contents may be the search
 // histogram, which is no longer needed), or null to write directly.  pos:
 // maps a slot of the ranked row to its position (increasing), which is
 // written as pos + offset below c and as -1 otherwise.
 template <int NT, int EPT, class Pos = SamePos>
-__device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t prefix, int shift,
+__device__ __forceinline__ void row_emit(const float (&v)[EPT], uint32_t prefix, int shift,
                                          uint32_t need, uint32_t bin_count, int c, int kout,
                                          int32_t offset, int wbase, uint32_t* mbuf,
                                          int32_t* stage, uint32_t* wtot,
                                          int32_t* __restrict__ orow, Pos pos = Pos()) {
-  constexpr int NV = EPT / 4, NMW = NT * EPT / 64;  // masks per block
-  static_assert(EPT % 4 == 0 && EPT <= 32, "shape");
+  constexpr int NMW = NT * EPT / 64;  // 64-bit masks per block
+  static_assert(EPT <= 32, "shape");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lo = prefix << shift;
-  const uint32_t span = (1u << shift) - 1u;
-  const uint32_t hi = lo + span;
-  const bool all_eq = need >= bin_count;  // every tied key is taken
+  const uint32_t hi = lo | ((1u << shift) - 1u);
+  const bool all_eq = need >= bin_count;  // every tied score is taken
   // taken: key > cut (every tied key too when all are taken)
-  const uint32_t cut = all_eq ? lo - 1u : hi;
+  const float above = key_above(all_eq ? lo - 1u : hi);
   {
     uint32_t glo = 0, ghi = 0, qlo = 0, qhi = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const uint64_t m = __ballot(key[e] > cut);
+      const uint64_t m = __ballot(v[e] >= above);
       glo = (uint32_t)idx_writelane_i32((int)(uint32_t)m, e, (int)glo);
       ghi = (uint32_t)idx_writelane_i32((int)(uint32_t)(m >> 32), e, (int)ghi);
     }
     if (!all_eq) {
+      const KeyRange tied(lo, hi);
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        const uint64_t m = __ballot(key[e] - lo <= span);
+        const uint64_t m = __ballot(tied.has(v[e]));
         qlo = (uint32_t)idx_writelane_i32((int)(uint32_t)m, e, (int)qlo);
         qhi = (uint32_t)idx_writelane_i32((int)(uint32_t)(m >> 32), e, (int)qhi);
       }
@@ -313,18 +379,12 @@ __device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t pr
     }
   }
   __syncthreads();
-  // thread g: step (g / 8) of the block (wave-major), lanes 8(g % 8) .. + 8
+  // thread g: the 32 positions [32g, 32g + 32)
   constexpr int NG = NT * EPT / 32;
-  const bool has = NG >= NT || tid < NG;
   uint32_t gw = 0, qw = 0;
-  const int gstep = tid >> 3, gbyte = tid & 7;
-  if (has) {
-    const uint8_t* mb = reinterpret_cast<const uint8_t*>(mbuf);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      gw |= spread4(mb[(gstep * 4 + j) * 8 + gbyte]) << j;
-      if (!all_eq) qw |= spread4(mb[(NMW + gstep * 4 + j) * 8 + gbyte]) << j;
-    }
+  if (NG >= NT || tid < NG) {
+    gw = mbuf[tid];
+    if (!all_eq) qw = mbuf[2 * NMW + tid];
   }
   uint32_t gc = (uint32_t)__popc(gw), qc = (uint32_t)__popc(qw);
   block_inclusive_sum2<NT>(gc, qc, wtot);
@@ -341,8 +401,7 @@ __device__ __forceinline__ void row_emit(const uint32_t (&key)[EPT], uint32_t pr
     }
   }
   uint32_t slot = gb + (need < qb ? need : qb);
-  // position of bit b: the step's base + 4 * (8 * gbyte + l) + j = base + 32 gbyte + b
-  const int v0 = (gstep / NV) * 64 * EPT + (gstep % NV) * 256 + 32 * gbyte;
+  const int v0 = 32 * tid;  // position of bit 0
   auto out = [&](auto* dst) {
     while (sel) {
       const int b = __ffs(sel) - 1;

@@ -167,7 +167,6 @@ struct FusedTopk {
 };
 constexpr int kFusedEPT = 32;                     // keys per thread in the fused ranking
 constexpr int kFusedMaxT = 256 * kFusedEPT;       // 8192
-constexpr int kFusedMaskBytes = kFusedMaxT / 4;   // selection masks of the ranking
 
 template <int HT, bool CAND, bool TOPK>
 __global__ __launch_bounds__(256) void score_kernel(
@@ -309,33 +308,24 @@ done:
       row_keep_prefix<256>(limit, tk.kout, tk.offset, orow);
       return;
     }
+    // sbuf spans kFusedMaxT floats here; positions >= limit are masked by
+    // row_vals whatever they read
     const int wbase = row_base<kFusedEPT>();
-    const int last = keys_per_wg - 4;  // keys_per_wg: a multiple of 256, at least T
-    uint32_t key[kFusedEPT];
-    {
-      float v[kFusedEPT];
+    float v[kFusedEPT];
 #pragma unroll
-      for (int i = 0; i < kFusedEPT / 4; ++i) {
-        const int t = wbase + 256 * i;
-        const float4 f = *reinterpret_cast<const float4*>(sbuf + (t < last ? t : last));
-        v[4 * i] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
-      }
-      row_keys<kFusedEPT>(v, wbase, limit, T, key);
-    }
+    for (int e = 0; e < kFusedEPT; ++e) v[e] = sbuf[wbase + 64 * e];
+    row_vals<kFusedEPT>(v, wbase, limit, T);
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) mine += hist_lds[tid + 256 * j];
     const uint32_t counted = block_sum<256>(mine, wtot);
     uint32_t prefix, need, bcnt;
     int shift;
-    row_select<256, kFusedEPT>(key, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need,
+    row_select<256, kFusedEPT>(v, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need,
                                bcnt);
-    // the score buffer is free once the keys are in registers: it holds the
+    // the score buffer is free once the scores are in registers: it holds the
     // selection masks (the launch sizes it for them)
-    row_emit<256, kFusedEPT>(key, prefix, shift, need, bcnt, limit, tk.kout, tk.offset, wbase,
+    row_emit<256, kFusedEPT>(v, prefix, shift, need, bcnt, limit, tk.kout, tk.offset, wbase,
                              reinterpret_cast<uint32_t*>(sbuf),
                              tk.kout <= 2048 ? reinterpret_cast<int32_t*>(hist_lds) : nullptr,
                              wtot, orow);
@@ -451,10 +441,10 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   if (R > 0x7fffffffLL) return IDX_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   // one workgroup scores and ranks each whole row
+  // the score buffer spans the whole ranked layout (it then holds the
+  // selection masks)
   const int kpw = (T + 255) / 256 * 256;
-  const size_t lds = (size_t)kpw * sizeof(float) > (size_t)idx::kFusedMaskBytes
-                         ? (size_t)kpw * sizeof(float)
-                         : (size_t)idx::kFusedMaskBytes;
+  const size_t lds = (size_t)idx::kFusedMaxT * sizeof(float);
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
   hipLaunchKernelGGL(kern, dim3((unsigned)R, 1u), dim3(256), lds, st, q,
                      w, k_cache, k_batch_stride_rows, S, T, compress_lens, nullptr, 0, 0, scores,

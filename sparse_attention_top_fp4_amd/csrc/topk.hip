@@ -47,10 +47,6 @@ __device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
 __device__ __forceinline__ int pass_match_shift(int p) { return p == 0 ? 32 : (p == 1 ? 21 : 10); }
 __device__ __forceinline__ int pass_hist_offset(int p) { return p == 0 ? kHist1 : (p == 1 ? kHist2 : kHist3); }
 
-// Float whose key is k (inverse of score_key for non-NaN keys).
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
 
 // Threshold bin of a histogram (LDS or global): the bin b with
 // count(bins > b) < krem <= count(bins >= b), where bin `xbin` counts
@@ -262,72 +258,58 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
     return;
   }
 
-  // the score histogram is requested first so its latency overlaps the row
+  // the score histogram is requested first: this thread's bins
+  // [hhi - HPT, hhi), top bin first, straight into the threshold search
   constexpr int HPT = 2048 / NT;
-  uint32_t hpre[HPT];
+  const int hhi = 2048 - tid * HPT;
+  uint32_t hreg[HPT];
   if (hrow)
 #pragma unroll
-    for (int j = 0; j < HPT; ++j) hpre[j] = hrow[tid + j * NT];
+    for (int j = 0; j < HPT; ++j) hreg[j] = hrow[hhi - 1 - j];
 
   const float* srow = scores + (int64_t)r * ld;
   const int wbase = row_base<EPT>();
-  uint32_t key[EPT];
-  {
-    float v[EPT];
-    const int cv = c & ~3;  // positions [0, cv) come in whole aligned float4 runs
-    if ((((uintptr_t)srow) & 15) == 0) {
-      if (cv >= 4) {
-        const int last = cv - 4;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int t = wbase + 256 * i;
-          const float4 f = *reinterpret_cast<const float4*>(srow + (t < last ? t : last));
-          v[4 * i] = f.x;
-          v[4 * i + 1] = f.y;
-          v[4 * i + 2] = f.z;
-          v[4 * i + 3] = f.w;
-        }
-      }
-      if (cv < c) {  // the ragged end below c (at most 3 positions, one lane)
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          const int t = wbase + 256 * i;
-          if (t == cv) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (t + j < c) v[4 * i + j] = srow[t + j];
-          }
-        }
-      }
-    } else {
-      const unsigned lastu = (unsigned)(c - 1);  // c >= 1 here
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned t = (unsigned)(wbase + 256 * i + j);
-          v[4 * i + j] = srow[t < lastu ? t : lastu];
-        }
-    }
-    row_keys<EPT>(v, wbase, c, T, key);
-  }
-
-  uint32_t counted = 0xffffffffu;  // no histogram: count the first digit here
-  if (hrow) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-      hist[tid + j * NT] = hpre[j];
-      mine += hpre[j];
-    }
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) hrow[tid + j * NT] = 0u;  // ready for the next score call
-    counted = block_sum<NT>(mine, wtot);  // its barriers also publish hist
-  }
-  uint32_t prefix, need, bcnt;
+  float v[EPT];
+  uint32_t prefix, need, bin_count;
   int shift;
-  row_select<NT, EPT>(key, hist, counted, T, kout, sh, wtot, prefix, shift, need, bcnt);
-  row_emit<NT, EPT>(key, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
+  {
+    // every load in bounds and none conditional: a wave reaching past T
+    // reads position T - 1 there (positions >= c are masked by row_vals
+    // whatever they read)
+    const int wend = (__builtin_amdgcn_readfirstlane(tid >> 6) + 1) * 64 * EPT;
+    if (wend <= T) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) v[e] = srow[wbase + 64 * e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int t = wbase + 64 * e;
+        v[e] = srow[t < T ? t : T - 1];
+      }
+    }
+    uint32_t b1 = 0, krem = 0, bcnt = 0;
+    if (hrow) {
+      // first digit from the score histogram while the scores are in flight
+#pragma unroll
+      for (int j = 0; j < HPT; ++j) hrow[hhi - 1 - j] = 0u;  // ready for the next score call
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0u;     // the next digit's histogram
+      // the -inf bin counts the T - (histogram total) unscored positions; T
+      // bounds that, which selects the same bin and remainder (only the
+      // returned count of the -inf bin grows)
+#pragma unroll
+      for (int j = 0; j < HPT; ++j)
+        if (hhi - 1 - j == (int)kInfBin) hreg[j] += (uint32_t)T;
+      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bcnt);
+    }
+    row_vals<EPT>(v, wbase, c, T);
+    if (hrow) {
+      row_refine<NT, EPT>(v, hist, true, sh, wtot, b1, krem, bcnt, prefix, shift, need, bin_count);
+    } else {
+      row_select<NT, EPT>(v, hist, 0xffffffffu, T, kout, sh, wtot, prefix, shift, need,
+                          bin_count);
+    }
+  }
+  row_emit<NT, EPT>(v, prefix, shift, need, bin_count, c, kout, offset, wbase, mbuf,
                     kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow);
 }
 
@@ -374,16 +356,15 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     return p < T ? p : -1;
   };
   const int wbase = row_base<EPT>();
-  uint32_t key[EPT];
+  float v[EPT];
   uint32_t nfin = 0;
   {
     // validity as integer arithmetic on the sign bits, kept out of the
     // compiler's reach (no per-element compare masks live across the loads)
-    float v[EPT];
     uint32_t okp[EPT], fin[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const int p = slot_pos(wbase + 256 * (e >> 2) + (e & 3));
+      const int p = slot_pos(wbase + 64 * e);
       uint32_t ok = (uint32_t)(~p) >> 31;                // p >= 0
       uint32_t below_c = ((uint32_t)(p - c) >> 31) & ok;  // 0 <= p < c
       asm volatile("" : "+v"(ok), "+v"(below_c));
@@ -391,11 +372,12 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
       fin[e] = below_c;
       v[e] = srow[p & ~(p >> 31)];
     }
+    // no such slot: NaN (absent); at or past c: -inf
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const uint32_t m = kKeyNegInf & (0u - okp[e]);
-      const uint32_t k = score_key(v[e]);
-      key[e] = m ^ ((k ^ m) & (0u - fin[e]));
+      const uint32_t m = 0xff800000u ^ (0x80400000u & (okp[e] - 1u));
+      const uint32_t u = __float_as_uint(v[e]);
+      v[e] = __uint_as_float(m ^ ((u ^ m) & (0u - fin[e])));
       nfin += fin[e];
     }
   }
@@ -404,7 +386,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   if (F >= (uint32_t)kout) {
     uint32_t prefix, need, bcnt;
     int shift;
-    row_select<NT, EPT>(key, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
+    row_select<NT, EPT>(v, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
     struct CandPos {
       const int32_t* ids;
       int cbs;
@@ -413,7 +395,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
         return ids[blk] * cbs + (v - blk * cbs);
       }
     };
-    row_emit<NT, EPT>(key, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
+    row_emit<NT, EPT>(v, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
                       kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow,
                       CandPos{ids, cbs});
     return;
@@ -427,9 +409,8 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   asm volatile("" : "+v"(wb));
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    const uint32_t k = key[e];
-    if (k != 0u && k != kKeyNegInf) {
-      const int p = slot_pos(wb + 256 * (e >> 2) + (e & 3));
+    if (v[e] > -__builtin_inff()) {  // neither absent (NaN) nor -inf
+      const int p = slot_pos(wb + 64 * e);
       atomicOr(&fin[p >> 5], 1u << (p & 31));
     }
   }
