@@ -592,26 +592,29 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   uint32_t* cpos = ckey + kSplitCandCap;
   const int nreg = (int)L.nparts * kPartNW;
 
-  for (int i = tid; i < nwp; i += NT) {
-    sel[i] = 0u;
-    eqm[i] = 0u;
-  }
-  // this thread's words of the above-threshold masks (kernel A's output),
-  // requested first: their latency overlaps the threshold search below.
-  // Unconditional (clamped) loads, all in flight together.
-  constexpr int kMaxWpt = (kSplitMaxT / 32 + NT - 1) / NT;
-  const int wpt = (nw + NT - 1) / NT;
-  uint32_t aw[kMaxWpt];
-#pragma unroll
-  for (int j = 0; j < kMaxWpt; ++j) {
-    const int word = tid * wpt + j;
-    aw[j] = wrow[word < nw ? word : nw - 1];
-  }
-  // list counts -> region prefix, one block scan (at most 256 regions)
+  // list counts (at most 256 regions) and the search state first
   static_assert(kSplitMaxT / kPart * kPartNW <= NT, "one region per thread");
   const uint32_t rc = tid < nreg ? wrow[L.cnt_off + tid] : 0u;
   const uint32_t b1 = wrow[L.state_off];
   uint32_t krem = wrow[L.state_off + 1];
+  // this thread's words of the above-threshold masks (kernel A's output) are
+  // requested once the list is in LDS: their latency then overlaps the
+  // threshold search, and no earlier wait on the list loads drains them
+  constexpr int kMaxWpt = (kSplitMaxT / 32 + NT - 1) / NT;
+  const int wpt = (nw + NT - 1) / NT;
+  uint32_t aw[kMaxWpt];
+  auto load_words = [&]() {
+#pragma unroll
+    for (int j = 0; j < kMaxWpt; ++j) {
+      const int word = tid * wpt + j;
+      aw[j] = wrow[word < nw ? word : nw - 1];
+    }
+  };
+  for (int i = tid; i < nwp; i += NT) {
+    sel[i] = 0u;
+    eqm[i] = 0u;
+  }
+  // list counts -> region prefix, one block scan
   const uint32_t rincl = block_inclusive_sum<NT>(rc, wtot);
   if (tid < nreg) regions[tid + 1] = rincl;
   if (tid == 0) regions[0] = 0;
@@ -620,6 +623,7 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   const bool only_inf = b1 == kInfBin && key_hist[(int64_t)r * 2048 + kInfBin] == 0u;
 
   uint32_t ustar = kKeyNegInf;
+  if (only_inf) load_words();
   if (!only_inf) {
     const bool in_lds = ncand <= (uint32_t)kSplitCandCap;
     // list element i lives in region j with regions[j] <= i < regions[j+1]
@@ -661,16 +665,28 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
       }
       __syncthreads();
     }
+    load_words();
+    // every pass over the list runs one of two loops, so the LDS loop never
+    // waits on the global loads in flight
+    auto each = [&](auto&& body) {
+      if (in_lds) {
+        for (uint32_t i = tid; i < ncand; i += NT) body(ckey[i], cpos[i]);
+      } else {
+        for (uint32_t i = tid; i < ncand; i += NT) {
+          uint32_t k, p;
+          fetch(i, k, p);
+          body(k, p);
+        }
+      }
+    };
     uint32_t prefix = b1;
     for (int pass = 1; pass < 3; ++pass) {
       const int nb = pass_bins(pass), shift = pass_shift(pass), ms = pass_match_shift(pass);
       for (int i = tid; i < nb; i += NT) hist[i] = 0;
       __syncthreads();
-      for (uint32_t i = tid; i < ncand; i += NT) {
-        uint32_t k, p;
-        if (in_lds) k = ckey[i]; else fetch(i, k, p);
+      each([&](uint32_t k, uint32_t) {
         if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
+      });
       __syncthreads();
       uint32_t bin, k2, bc;
       if (pass == 1)
@@ -682,17 +698,10 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
     }
     ustar = prefix;
     // mark the list elements above the threshold and equal to it
-    for (uint32_t i = tid; i < ncand; i += NT) {
-      uint32_t k, p;
-      if (in_lds) {
-        k = ckey[i];
-        p = cpos[i];
-      } else {
-        fetch(i, k, p);
-      }
+    each([&](uint32_t k, uint32_t p) {
       if (k > ustar) atomicOr(&sel[split_pad(p >> 5)], 1u << (p & 31));
       else if (k == ustar) atomicOr(&eqm[split_pad(p >> 5)], 1u << (p & 31));
-    }
+    });
   }
   const uint32_t need = krem;
   __syncthreads();
