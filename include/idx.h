@@ -57,6 +57,21 @@ const char *idx_status_string(idx_status s);
 const char *idx_version(void);
 
 /*
+ * Launch timing of the score kernel (measurement support, not a page
+ * operation).  idx_timing_arm(slot) makes the next score launch of this
+ * process (idx_score or idx_score_topk, any stream) record the start and end
+ * of that kernel's execution into HIP event pair `slot` (0 <= slot < 256),
+ * through hipExtLaunchKernel, so no marker packet is added to the stream;
+ * the pair is created on first use on the current device and kept until
+ * the process ends.  idx_timing_read(slot, ms) waits for the pair's end
+ * event and writes the kernel's duration in milliseconds.  Not thread-safe:
+ * one thread arms and launches.  IDX_EINVAL for a slot out of range or never
+ * armed, IDX_EHIP when an event call fails.
+ */
+idx_status idx_timing_arm(int slot);
+idx_status idx_timing_read(int slot, float *ms);
+
+/*
  * idx_fp4_quant -- block-32 e2m1 / e8m0 quantise-dequantise of 128-wide rows
  * ([IDX, forward: fp4_act_quant on q and k]; [CMP, fp4_quant_e8m0_inplace,
  * to_e2m1_rne]).  Per block of 32 values: amax raised to at least 6*2^-126,

@@ -18,7 +18,8 @@ __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist",
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
-           "idx_yarn_cos_sin", "library_path", "load_library", "IdxError", "ROW_BYTES"]
+           "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
+           "load_library", "IdxError", "ROW_BYTES"]
 
 ROW_BYTES = 68
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,10 +65,12 @@ def load_library():
     L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
                                    i32, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
+    L.idx_timing_arm.argtypes = [i32]
+    L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
     for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
                  "idx_topk_candidates",
                  "idx_select_candidate_blocks",
-                 "idx_publish_keys", "idx_yarn_cos_sin"):
+                 "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -300,3 +303,15 @@ def idx_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):
                                            out.ctypes.data_as(ctypes.c_void_p)),
            "idx_yarn_cos_sin")
     return out
+
+
+def idx_timing_arm(slot: int):
+    """Time the next score launch (idx_score / idx_score_topk) into event pair `slot`."""
+    _check(load_library().idx_timing_arm(int(slot)), "idx_timing_arm")
+
+
+def idx_timing_read(slot: int) -> float:
+    """Duration in ms of the score kernel timed into `slot` (waits for it)."""
+    ms = ctypes.c_float()
+    _check(load_library().idx_timing_read(int(slot), ctypes.byref(ms)), "idx_timing_read")
+    return float(ms.value)

@@ -25,6 +25,8 @@
 #include "idx_common.hpp"
 #include "row_topk.hpp"
 
+#include <hip/hip_ext.h>
+
 namespace idx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -349,6 +351,25 @@ __global__ __launch_bounds__(256) void fill_neg_inf_kernel(float* __restrict__ s
 }  // namespace idx
 
 namespace {
+// ------------------------------------------------------- launch timing
+constexpr int kTimingSlots = 256;
+hipEvent_t g_timing_ev[kTimingSlots][2] = {};
+int g_timing_armed = -1;  // slot of the next score launch, or -1
+
+// Launches the score kernel, through hipExtLaunchKernel with the armed
+// event pair when timing is armed.
+template <typename... Args, typename F>
+idx_status launch_score(F kern, dim3 grid, size_t lds, hipStream_t st, Args... args) {
+  const int slot = g_timing_armed;
+  g_timing_armed = -1;
+  if (slot >= 0)
+    hipExtLaunchKernelGGL(kern, grid, dim3(256), (uint32_t)lds, st, g_timing_ev[slot][0],
+                          g_timing_ev[slot][1], 0u, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, args...);
+  return idx_host::launch_status();
+}
+
 constexpr int kMaxKeysPerWg = 8192;  // bounds the LDS score buffer (32 KB)
 int g_keys_per_wg_override = -1;
 
@@ -418,10 +439,9 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                                      : idx::score_kernel<2, false, false>)
                       : (cand_blocks ? idx::score_kernel<1, true, false>
                                      : idx::score_kernel<1, false, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(256), (size_t)kpw * sizeof(float), st, q, w, k_cache,
-                     k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                     cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0});
-  return idx_host::launch_status();
+  return launch_score(kern, grid, (size_t)kpw * sizeof(float), st, q, w, k_cache,
+                      k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
+                      cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0});
 }
 
 extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
@@ -446,8 +466,24 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   const int kpw = (T + 255) / 256 * 256;
   const size_t lds = (size_t)idx::kFusedMaxT * sizeof(float);
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)R, 1u), dim3(256), lds, st, q,
-                     w, k_cache, k_batch_stride_rows, S, T, compress_lens, nullptr, 0, 0, scores,
-                     ld, nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out});
-  return idx_host::launch_status();
+  return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, w, k_cache, k_batch_stride_rows, S,
+                      T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
+                      (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out});
+}
+
+extern "C" idx_status idx_timing_arm(int slot) {
+  if (slot < 0 || slot >= kTimingSlots) return IDX_EINVAL;
+  for (int i = 0; i < 2; ++i)
+    if (!g_timing_ev[slot][i] && hipEventCreate(&g_timing_ev[slot][i]) != hipSuccess)
+      return IDX_EHIP;
+  g_timing_armed = slot;
+  return IDX_OK;
+}
+
+extern "C" idx_status idx_timing_read(int slot, float* ms) {
+  if (slot < 0 || slot >= kTimingSlots || !ms || !g_timing_ev[slot][1]) return IDX_EINVAL;
+  if (hipEventSynchronize(g_timing_ev[slot][1]) != hipSuccess) return IDX_EHIP;
+  return hipEventElapsedTime(ms, g_timing_ev[slot][0], g_timing_ev[slot][1]) == hipSuccess
+             ? IDX_OK
+             : IDX_EHIP;
 }

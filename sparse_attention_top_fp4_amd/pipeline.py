@@ -15,7 +15,7 @@ import numpy as np
 from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score, idx_score_topk,
                idx_select_candidate_blocks, idx_select_workspace_size, idx_topk,
                idx_topk_candidates,
-               idx_topk_workspace_size, idx_yarn_cos_sin)
+               idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
 
 
@@ -108,28 +108,24 @@ class IndexerStep:
     def k_cache(self):
         return self.caches[self.cur]
 
-    def step(self, stream=None, score_events=None):
-        """Issue one step on the current stream (asynchronous).  score_events:
-        optional (start, end) torch.cuda.Event pair recorded on the stream
-        around the (level-one) score launch."""
+    def step(self, stream=None, time_slot=None):
+        """Issue one step on the current stream (asynchronous).  time_slot:
+        when given, the (level-one) score launch records its kernel's start
+        and end into that library event pair (idx_timing_read reads it)."""
         wl = self.wl
         kc = self.caches[self.cur]
         if self.publish:
             idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                              wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
-        if score_events is not None:
-            score_events[0].record(stream)
+        if time_slot is not None:
+            idx_timing_arm(time_slot)
         if self.fused:
             idx_score_topk(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
                            self.out, scores=self.scores, stream=stream)
-            if score_events is not None:
-                score_events[1].record(stream)
             self.cur = (self.cur + 1) % len(self.caches)
             return
         idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                   key_hist=self.key_hist, stream=stream)
-        if score_events is not None:
-            score_events[1].record(stream)
         if self.two_level:
             idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
                                         workspace=self.sel_ws, stream=stream)
