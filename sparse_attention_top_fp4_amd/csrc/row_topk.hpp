@@ -348,7 +348,7 @@ __device__ __forceinline__ void row_emit(const float (&v)[EPT], uint32_t prefix,
                                          int32_t* stage, uint32_t* wtot,
                                          int32_t* __restrict__ orow, Pos pos = Pos()) {
   constexpr int NMW = NT * EPT / 64;  // 64-bit masks per block
-  static_assert(EPT <= 32, "shape");
+  static_assert(EPT <= 32 && NT * EPT < 65536, "shape (counts packed in 16 bits)");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lo = prefix << shift;
@@ -386,10 +386,11 @@ __device__ __forceinline__ void row_emit(const float (&v)[EPT], uint32_t prefix,
     gw = mbuf[tid];
     if (!all_eq) qw = mbuf[2 * NMW + tid];
   }
-  uint32_t gc = (uint32_t)__popc(gw), qc = (uint32_t)__popc(qw);
-  block_inclusive_sum2<NT>(gc, qc, wtot);
-  // gc, qc: inclusive; before this word
-  const uint32_t gb = gc - (uint32_t)__popc(gw), qb = qc - (uint32_t)__popc(qw);
+  // both counts in one scan: taken in the low 16 bits, tied in the high
+  // (a block holds fewer than 65536 positions)
+  const uint32_t gq = (uint32_t)__popc(gw) | ((uint32_t)__popc(qw) << 16);
+  const uint32_t before = block_inclusive_sum<NT>(gq, wtot) - gq;
+  const uint32_t gb = before & 0xffffu, qb = before >> 16;
   uint32_t sel = gw;
   if (!all_eq && qw) {  // the first `need` tied keys of the row, by position
     uint32_t take = need > qb ? need - qb : 0u, rest = qw;

@@ -246,20 +246,13 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
   __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.x, tid = threadIdx.x;
-  int c = cl_arr[r];
-  c = c < 0 ? 0 : (c > T ? T : c);
   int32_t* orow = out + (int64_t)r * ld_out;
   uint32_t* hrow = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
 
-  if (c <= kout) {
-    row_keep_prefix<NT>(c, kout, offset, orow);
-    if (hrow)
-      for (int i = tid; i < 2048; i += NT) hrow[i] = 0u;
-    return;
-  }
-
-  // the score histogram is requested first: this thread's bins
-  // [hhi - HPT, hhi), top bin first, straight into the threshold search
+  // the histogram and the row are requested before compress_lens is known
+  // (every load is in bounds whatever it is), so the three latencies overlap.
+  // The score histogram first: this thread's bins [hhi - HPT, hhi), top bin
+  // first, straight into the threshold search
   constexpr int HPT = 2048 / NT;
   const int hhi = 2048 - tid * HPT;
   uint32_t hreg[HPT];
@@ -271,7 +264,7 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
   const int wbase = row_base<EPT>();
   float v[EPT];
   uint32_t prefix, need, bin_count;
-  int shift;
+  int shift, c;
   {
     // every load in bounds and none conditional: a wave reaching past T
     // reads position T - 1 there (positions >= c are masked by row_vals
@@ -286,6 +279,14 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
         const int t = wbase + 64 * e;
         v[e] = srow[t < T ? t : T - 1];
       }
+    }
+    c = cl_arr[r];
+    c = c < 0 ? 0 : (c > T ? T : c);
+    if (c <= kout) {
+      row_keep_prefix<NT>(c, kout, offset, orow);
+      if (hrow)
+        for (int i = tid; i < 2048; i += NT) hrow[i] = 0u;
+      return;
     }
     uint32_t b1 = 0, krem = 0, bcnt = 0;
     if (hrow) {
