@@ -282,6 +282,9 @@ HIST_CASES = [
     (62, 2, 1, 8193, None, None, 0, 2048, "auto"),           # just past the 256-thread instance
     (63, 1, 1, 32771, None, None, 0, 2048, "auto"),          # ragged split row
     (64, 1, 24, 4096, 0, None, 0, 2048, "auto"),             # prefill rows, cl 0..6
+    (65, 2, 1, 32768, None, None, 0, 2048, "negative-weights"),  # every score <= 0
+    (66, 1, 1, 40000, None, None, 0, 2048, "negative-weights"),  # the same, split rows
+    (67, 3, 1, 5000, None, None, 0, 2048, "negative-weights"),   # 256-thread rows
 ]
 
 
@@ -295,6 +298,8 @@ def test_topk_with_score_histogram(idx, case, monkeypatch):
     c = small_case(seed, B, S, 64, T, start_pos=sp)
     if path == "zero-weights":
         c["w"][:] = 0
+    if path == "negative-weights":  # bf16 sign bit set: every head weight negative
+        c["w"][:] |= np.uint16(0x8000)
     R = B * S
     kc_ref, _ = oracle.fp4_quant_rows(c["k"])
     cand = None if cand_rows is None else np.array(cand_rows, np.int32)
@@ -357,6 +362,58 @@ def test_fused_score_topk_matches_oracle(idx, case):
             n = min(int(c["cl"][r]), T)
             assert np.array_equal(bits(g[r, :n]), bits(ref[r, :n])), r
         assert np.all(np.isnan(g[:, T:]))
+
+
+@pytest.mark.parametrize("seed,B,T,k", [(77, 3, 8192, 2048), (78, 2, 3000, 700)])
+def test_fused_score_topk_negative_scores(idx, seed, B, T, k):
+    """Every head weight negative: every score <= 0, so the threshold lies in
+    a negative bin (digits read from complemented bits) or at zero."""
+    t = torch()
+    say("fused score+topk, negative weights", seed, B, T, k)
+    c = small_case(seed, B, 1, 64, T)
+    c["w"][:] |= np.uint16(0x8000)
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref, _ = oracle.score(c["q"], c["w"], kc_ref, B, 1, 64, T, c["cl"])
+    assert np.all(ref[np.isfinite(ref)] <= 0)
+    kc = fp4_cache(c["k"])
+    out = t.full((B, min(k, T)), -7, dtype=t.int32, device="cuda")
+    idx.idx_score_topk(dev(c["q"]), dev(c["w"]), kc, B, 1, T, dev(c["cl"]), k, 9, out)
+    sync()
+    assert np.array_equal(host(out), oracle.topk(ref, c["cl"], k, 9))
+
+
+SYNTH_HIST_CASES = [
+    # (seed, R, T, k, shift): normal scores shifted by `shift`, plus 0, -0 and -inf
+    (91, 3, 5000, 2048, -2.5),     # 256-thread rows, negative threshold
+    (92, 2, 32768, 2048, -2.5),    # 1024-thread rows
+    (93, 2, 32768, 2048, 0.0),     # threshold near zero: +0 / -0 ties
+    (94, 2, 70000, 2048, -2.5),    # split rows
+    (95, 1, 262144, 2048, -1.0),   # longest split row
+]
+
+
+@pytest.mark.parametrize("case", SYNTH_HIST_CASES)
+def test_topk_with_host_histogram(idx, case):
+    """Synthetic scores of both signs with the first-digit histogram built on
+    the host: the histogram paths on negative thresholds and signed zeros."""
+    t = torch()
+    seed, R, T, k, shift = case
+    say("topk with host histogram", case)
+    rng = np.random.default_rng(seed)
+    vals = np.concatenate([(rng.standard_normal(4000) + shift).astype(np.float32),
+                           [0.0, -0.0, -np.inf]]).astype(np.float32)
+    s = vals[rng.integers(0, len(vals), size=(R, T))].astype(np.float32)
+    cl = rng.integers(k + 1, T + 1, size=R).astype(np.int32)
+    cl[0] = T
+    tt = np.arange(T)[None, :]
+    counted = np.isfinite(s) & (tt < cl[:, None])
+    hist = t.tensor(_host_hist(s, counted).astype(np.int32), device="cuda")
+    kout = min(k, T)
+    out = t.full((R, kout), -7, dtype=t.int32, device="cuda")
+    idx.idx_topk(dev(s), T, dev(cl), k, 11, out, key_hist=hist)
+    sync()
+    assert np.array_equal(host(out), oracle.topk(s, cl, k, 11))
+    assert not host(hist).any()
 
 
 CAND_TOPK_CASES = [
