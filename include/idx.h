@@ -191,14 +191,19 @@ idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t
  *   cand_blocks  device, [R][n_cand] int32 block ids in ascending order
  *                (idx_select_candidate_blocks' output); ids < 0 or
  *                >= ceil(T/cand_block_size) are skipped
+ *   key_hist     device, [R][2048] from idx_score with these cand_blocks on
+ *                these scores and compress_lens, or NULL (then the first
+ *                digit is counted here).  Read and reset to zero, as by
+ *                idx_topk.
  *   scores, compress_lens, index_topk, offset, out, ld_out: as idx_topk
  * Requires T <= 65536, n_cand <= 2048 and n_cand * cand_block_size <= 8192
  * (IDX_EUNSUPPORTED otherwise).
  */
 idx_status idx_topk_candidates(const float *scores, int64_t ld, int R, int T,
                                const int32_t *compress_lens, const int32_t *cand_blocks,
-                               int n_cand, int cand_block_size, int index_topk, int32_t offset,
-                               int32_t *out, int64_t ld_out, void *stream);
+                               int n_cand, int cand_block_size, uint32_t *key_hist,
+                               int index_topk, int32_t offset, int32_t *out, int64_t ld_out,
+                               void *stream);
 
 /*
  * Bytes of device workspace idx_select_candidate_blocks needs.

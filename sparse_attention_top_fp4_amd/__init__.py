@@ -57,8 +57,8 @@ def load_library():
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
     L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, sz, P]
-    L.idx_topk_candidates.argtypes = [P, i64, i32, i32, P, P, i32, i32, i32, ctypes.c_int32, P,
-                                      i64, P]
+    L.idx_topk_candidates.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, i32, ctypes.c_int32,
+                                      P, i64, P]
     L.idx_select_workspace_size.argtypes = [i32, i32, i32, i32]
     L.idx_select_workspace_size.restype = sz
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
@@ -235,10 +235,12 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
 
 
 def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, index_topk,
-                        offset, out, stream=None):
+                        offset, out, key_hist=None, stream=None):
     """Top-k of level-two rows whose finite scores lie in the ascending
     candidate blocks cand_blocks [R, n_cand] int32 (the output of
-    idx_select_candidate_blocks); scores [R, ld] float32, out [R, ld_out]."""
+    idx_select_candidate_blocks); scores [R, ld] float32, out [R, ld_out].
+    key_hist: the [R, 2048] histogram idx_score produced for these scores
+    with these candidate blocks; the call resets it to zero."""
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)
@@ -247,10 +249,15 @@ def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, 
     R = scores.shape[0]
     if compress_lens.shape[0] != R or cand_blocks.shape[0] != R or out.shape[0] != R:
         raise ValueError("scores, compress_lens, cand_blocks and out need the same rows")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if key_hist.shape != (R, 2048):
+            raise ValueError("key_hist must be [R, 2048]")
     _check(load_library().idx_topk_candidates(_ptr(scores), scores.shape[1], R, T,
                                               _ptr(compress_lens), _ptr(cand_blocks),
-                                              cand_blocks.shape[1], cand_block_size, index_topk,
-                                              offset, _ptr(out), out.shape[1], _stream(stream)),
+                                              cand_blocks.shape[1], cand_block_size,
+                                              _ptr(key_hist), index_topk, offset, _ptr(out),
+                                              out.shape[1], _stream(stream)),
            "idx_topk_candidates")
 
 

@@ -329,8 +329,8 @@ constexpr int kCandMaxIds = 2048;   // candidate ids per row held in LDS
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_cand_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
-    const int32_t* __restrict__ cand, int n_cand, int cbs, int kout, int32_t offset,
-    int32_t* __restrict__ out, int64_t ld_out) {
+    const int32_t* __restrict__ cand, int n_cand, int cbs, uint32_t* __restrict__ key_hist,
+    int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out) {
   constexpr int NV = EPT / 4, WPT = (kCandMaxT / 32) / NT;
   __shared__ uint32_t hist[2048];
   __shared__ int32_t ids[kCandMaxIds];
@@ -338,6 +338,15 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  uint32_t* hrow = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
+  // the score histogram (level two: counts of the candidate positions below
+  // compress_lens) is requested first, this thread's bins [hhi - HPT, hhi)
+  constexpr int HPT = 2048 / NT;
+  const int hhi = 2048 - tid * HPT;
+  uint32_t hreg[HPT];
+  if (hrow)
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) hreg[j] = hrow[hhi - 1 - j];
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
   const int nb = (T + cbs - 1) / cbs;
@@ -345,13 +354,19 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     const int id = cand[(int64_t)r * n_cand + i];
     ids[i] = (id < 0 || id >= nb) ? -1 : id;
   }
+  for (int i = tid; i < 2048; i += NT) hist[i] = 0u;  // the next digit's histogram
   __syncthreads();
   const int V = n_cand * cbs;
   const float* srow = scores + (int64_t)r * ld;
+  // slot v lies in candidate block v / cbs (a shift for the usual
+  // power-of-two block size: the division is dozens of instructions)
+  const bool pow2 = (cbs & (cbs - 1)) == 0;
+  const int cshift = __builtin_ctz((unsigned)cbs);
+  auto block_of = [&](int v) { return pow2 ? v >> cshift : v / cbs; };
   // position of slot v, or -1 (no such block, or past T)
   auto slot_pos = [&](int v) {
     if (v >= V) return -1;
-    const int blk = v / cbs, id = ids[blk];
+    const int blk = block_of(v), id = ids[blk];
     if (id < 0) return -1;
     const int p = id * cbs + (v - blk * cbs);
     return p < T ? p : -1;
@@ -383,22 +398,37 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     }
   }
   const uint32_t F = block_sum<NT>(nfin, wtot);
+  if (hrow)
+#pragma unroll
+    for (int j = 0; j < HPT; ++j) hrow[hhi - 1 - j] = 0u;  // ready for the next score call
   int32_t* orow = out + (int64_t)r * ld_out;
   if (F >= (uint32_t)kout) {
     uint32_t prefix, need, bcnt;
     int shift;
-    row_select<NT, EPT>(v, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
+    if (hrow) {
+      // the -inf slots number at most V (only the returned count of the
+      // -inf bin grows, as in the rows kernel)
+      uint32_t b1, krem, bc1;
+#pragma unroll
+      for (int j = 0; j < HPT; ++j)
+        if (hhi - 1 - j == (int)kInfBin) hreg[j] += (uint32_t)V;
+      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bc1);
+      row_refine<NT, EPT>(v, hist, true, sh, wtot, b1, krem, bc1, prefix, shift, need, bcnt);
+    } else {
+      row_select<NT, EPT>(v, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
+    }
     struct CandPos {
       const int32_t* ids;
-      int cbs;
+      int cbs, cshift;
+      bool pow2;
       __device__ __forceinline__ int operator()(int v) const {
-        const int blk = v / cbs;
+        const int blk = pow2 ? v >> cshift : v / cbs;
         return ids[blk] * cbs + (v - blk * cbs);
       }
     };
     row_emit<NT, EPT>(v, prefix, shift, need, bcnt, c, kout, offset, wbase, mbuf,
                       kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr, wtot, orow,
-                      CandPos{ids, cbs});
+                      CandPos{ids, cbs, cshift, pow2});
     return;
   }
 
@@ -1142,9 +1172,9 @@ extern "C" idx_status idx_select_candidate_blocks(const float* scores, int64_t l
 
 extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R, int T,
                                           const int32_t* compress_lens, const int32_t* cand_blocks,
-                                          int n_cand, int cand_block_size, int index_topk,
-                                          int32_t offset, int32_t* out, int64_t ld_out,
-                                          void* stream) {
+                                          int n_cand, int cand_block_size, uint32_t* key_hist,
+                                          int index_topk, int32_t offset, int32_t* out,
+                                          int64_t ld_out, void* stream) {
   if (R < 0 || T < 0 || index_topk <= 0 || n_cand <= 0 || cand_block_size <= 0) return IDX_EINVAL;
   if (R == 0 || T == 0) return IDX_OK;
   if (!scores || !compress_lens || !cand_blocks || !out) return IDX_EINVAL;
@@ -1154,6 +1184,7 @@ extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R
   if (index_topk >= T) {
     hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T,
                        compress_lens, offset, out, ld_out);
+    if (key_hist) zero_hist(key_hist, R, st);
     return idx_host::launch_status();
   }
   const int64_t V = (int64_t)n_cand * cand_block_size;
@@ -1161,11 +1192,11 @@ extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R
   // few rows, each a latency chain: many threads per row, few keys each
   if (V <= 2048)
     hipLaunchKernelGGL((idx::topk_cand_kernel<256, 8>), dim3((unsigned)R), dim3(256), 0, st,
-                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size, kout,
-                       offset, out, ld_out);
+                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size,
+                       key_hist, kout, offset, out, ld_out);
   else
     hipLaunchKernelGGL((idx::topk_cand_kernel<1024, 8>), dim3((unsigned)R), dim3(1024), 0, st,
-                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size, kout,
-                       offset, out, ld_out);
+                       scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size,
+                       key_hist, kout, offset, out, ld_out);
   return idx_host::launch_status();
 }

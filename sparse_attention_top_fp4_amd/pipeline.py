@@ -131,11 +131,13 @@ class IndexerStep:
                                         workspace=self.sel_ws, stream=stream)
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
+            # level two: only the candidate positions hold finite scores; the
+            # histogram, reset by the level-one top-k, now counts them
             idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                      cand_blocks=self.ids, cand_block_size=wl.cbs, stream=stream)
-            # level two: only the candidate positions hold finite scores
+                      cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
+                      stream=stream)
             idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs, wl.topk,
-                                wl.offset, self.out, stream=stream)
+                                wl.offset, self.out, key_hist=self.key_hist, stream=stream)
         else:
             idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)

@@ -137,11 +137,13 @@ def test_fused_score_topk_rejects_bad_arguments(lib):
 
 def test_candidate_topk_rejects_bad_arguments(lib):
     d = ctypes.c_void_p(0x1000)
-    assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, 2048, 0, d, 2048,
+    assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, None, 2048, 0, d, 2048,
                                    None) == IDX_EUNSUPPORTED  # row wider than the bit map
-    assert lib.idx_topk_candidates(d, 65536, 1, 65536, d, d, 65, 128, 2048, 0, d, 2048,
+    assert lib.idx_topk_candidates(d, 65536, 1, 65536, d, d, 65, 128, None, 2048, 0, d, 2048,
                                    None) == IDX_EUNSUPPORTED  # more than 8192 candidate slots
-    assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 0, 4, 4, 0, d, 4, None) == IDX_EINVAL
-    assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 2, 4, 4, 0, d, 3, None) == IDX_EINVAL
-    assert lib.idx_topk_candidates(None, 8, 0, 8, None, None, 2, 4, 4, 0, None, 4,
+    assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 0, 4, None, 4, 0, d, 4,
+                                   None) == IDX_EINVAL
+    assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 2, 4, None, 4, 0, d, 3,
+                                   None) == IDX_EINVAL
+    assert lib.idx_topk_candidates(None, 8, 0, 8, None, None, 2, 4, None, 4, 0, None, 4,
                                    None) == IDX_OK

@@ -427,11 +427,12 @@ CAND_TOPK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("with_hist", [False, True])
 @pytest.mark.parametrize("case", CAND_TOPK_CASES)
-def test_topk_candidates_matches_full_row_topk(idx, case):
+def test_topk_candidates_matches_full_row_topk(idx, case, with_hist):
     t = torch()
     seed, R, T, cbs, n_ids, clv, k, nvals = case
-    say("topk candidates", case)
+    say("topk candidates", case, "histogram" if with_hist else "")
     rng = np.random.default_rng(seed)
     nb = (T + cbs - 1) // cbs
     ids = np.full((R, n_ids), -1, np.int32)
@@ -448,8 +449,14 @@ def test_topk_candidates_matches_full_row_topk(idx, case):
                 sc[r, lo:hi] = vals[rng.integers(0, nvals, size=hi - lo)]
     kout = min(k, T)
     out = t.full((R, kout + 1), -7, dtype=t.int32, device="cuda")
-    idx.idx_topk_candidates(dev(sc), T, dev(cl), dev(ids), cbs, k, 3, out)
+    hist = None
+    if with_hist:  # as idx_score with these blocks counts them: finite and below cl
+        counted = np.isfinite(sc) & (np.arange(T)[None, :] < cl[:, None])
+        hist = t.tensor(_host_hist(sc, counted).astype(np.int32), device="cuda")
+    idx.idx_topk_candidates(dev(sc), T, dev(cl), dev(ids), cbs, k, 3, out, key_hist=hist)
     sync()
     got = host(out)
     assert np.array_equal(got[:, :kout], oracle.topk(sc, cl, k, 3))
     assert np.all(got[:, kout:] == -7)
+    if with_hist:
+        assert not host(hist).any()
