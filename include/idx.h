@@ -92,8 +92,10 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  * heads, compress_lens mask, level-two candidate mask]).
  *   scores[r][t] = sum_{h=0..H-1} relu(qhat[r][h] . khat[b][t]) * w[r][h]
  * with r = b*S + s, qhat the fp4 round trip of q (done in the kernel),
- * khat the dequantised key row t of sequence b.  The head sum is fp32, heads
- * ascending, one fused multiply-add per head starting from +0; the dot
+ * khat the dequantised key row t of sequence b.  The head sum is fp32 in
+ * one fixed association: heads [0, H/2) and [H/2, H) are each summed
+ * ascending, one fused multiply-add per head starting from +0, and the
+ * score is the low sum plus the high sum (one rounded add); the dot
  * products are exact for the documented input range.
  *   q              device, [B*S][H][D] bf16, RoPE already applied
  *   w              device, [B*S][H] bf16, weights_proj output already

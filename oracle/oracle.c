@@ -258,8 +258,9 @@ static int in_candidates(const int32_t *cand, int n_cand, int cbs, int t)
 
 /* [IDX, forward]: index_score[r][t] = sum_h relu(q_h . k_t) * w_h, with
  *   - q quantised here (fp4_act_quant of q), k given as 68-byte rows;
- *   - the head sum in fp32, heads ascending, one fmaf per head, from +0
- *     (the fixed order both sides share);
+ *   - the head sum in fp32 in one fixed order both sides share: heads
+ *     [0, hs) and [hs, H), hs = ceil(H/2), each summed ascending by one
+ *     fmaf per head from +0, then lo + hi (one rounded add);
  *   - the causal mask t >= cl[r] -> -inf ([IDX, forward: compress_lens]);
  *   - with cand != NULL (level two): t < cl[r] outside the blocks listed in
  *     cand[r][0..n_cand) -> -inf ([IDX, forward: masked_fill of ~candidates]).
@@ -296,10 +297,14 @@ int64_t orc_score(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64
             float dh[1024];
             for (int h = 0; h < H; ++h)
                 dh[h] = exact_dot(&dq[h], &dk, &inexact);
-            float acc = 0.0f;
-            for (int h = 0; h < H; ++h)
-                acc = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(w[r * H + h]), acc);
-            *out = acc + 0.0f;
+            /* two chains, each heads ascending from +0, then one add */
+            const int hsplit = (H + 1) / 2;
+            float lo = 0.0f, hi = 0.0f;
+            for (int h = 0; h < hsplit; ++h)
+                lo = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(w[r * H + h]), lo);
+            for (int h = hsplit; h < H; ++h)
+                hi = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(w[r * H + h]), hi);
+            *out = (lo + hi) + 0.0f;
         }
         inexact_total += inexact;
     }

@@ -14,10 +14,12 @@
 //     code bytes of block g of key n, and the block's scale byte).
 //   - query heads are assigned to M rows so that, in the 32x32 accumulator,
 //     lanes 0..31 hold heads [0, H/2) and lanes 32..63 heads [H/2, H) of
-//     their key; one v_permlane32_swap per accumulator register pair then
-//     gives each lane all H heads of one key (lane l: key t0+l).
-//   - each lane runs the head sum in the fixed order: heads ascending, one
-//     fma(max(d, 0), w, acc) per head from +0, then stores one fp32 score.
+//     their key.
+//   - the head sum has one fixed association: each half-wave sums its own
+//     half of the heads ascending, one fma(max(d, 0), w, acc) per head from
+//     +0, so lane n and lane n+32 each run one chain per key tile on the
+//     registers the MFMA left them; one v_permlane32_swap of the two tiles'
+//     chains and one add then give lane l the score of key t0+l.
 //
 // The dot products are exact (integer-valued block sums times powers of two
 // fit fp32 for the documented input range), so the only rounding is the
@@ -40,13 +42,16 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Head carried by M-row m of head tile ht (32 heads per tile).  The 32x32
-// f32 accumulator gives lane l, register i the row (i/4)*8 + (l/32)*4 + i%4,
-// so rows with bit 2 clear sit in lanes 0..31 and rows with bit 2 set in
-// lanes 32..63; this map makes register i of tile ht hold head 32*ht + i in
-// the low half-wave and 32*ht + 16 + i in the high half-wave.
+// Head carried by M-row m of head tile ht (32 heads per tile, HT tiles).
+// The 32x32 f32 accumulator gives lane l, register i the row
+// (i/4)*8 + (l/32)*4 + i%4, so rows with bit 2 clear sit in lanes 0..31 and
+// rows with bit 2 set in lanes 32..63; this map makes register i of tile ht
+// hold head 16*ht + i in the low half-wave and H/2 + 16*ht + i in the high
+// half-wave, so each half-wave walks its half of the heads ascending by
+// (ht, i).
+template <int HT>
 __device__ __forceinline__ int head_of_row(int ht, int m) {
-  return ht * 32 + ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3);
+  return ((m >> 2) & 1) * 16 * HT + ht * 16 + (m >> 3) * 4 + (m & 3);
 }
 
 constexpr int kMaxCand = 2048;  // candidate blocks per row held in LDS
@@ -108,54 +113,49 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
-// One 64-key tile: 2 key tiles x HT head tiles x 2 K-steps of MFMA, the
-// half-wave swap, and the fixed-order head sum; returns the score of key
-// v0 + lane for lane `lane`.
+// One 64-key tile: 2 key tiles x HT head tiles x 2 K-steps of MFMA and the
+// fixed-order head sum; returns the score of key v0 + lane for lane `lane`.
+// wv[16*ht + i] is the weight of the head register i of tile ht holds in
+// this lane's half-wave.  Lane n and lane n+32 sum the low and the high half
+// of the heads of key n of each key tile (two chains, heads ascending, from
+// +0); the swap hands the low half-wave the chains of key tile 0 and the
+// high half-wave those of key tile 1, and score = low chain + high chain.
 template <int HT>
 __device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)[HT][2],
                                                const int (&sA)[HT][2],
-                                               const float (&wf)[32 * HT], int lane) {
-  float sc = 0.0f;
+                                               const float (&wv)[16 * HT], int lane) {
+  float ch[2] = {0.0f, 0.0f};  // this half-wave's chain for key tile 0 and 1
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    v16f acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      acc[t] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      v16f acc = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const u32x4 c = kt.c[t][s];
         const v8i B = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
         const int sB = (int)((kt.sc[t] >> (8 * (2 * s + (lane >> 5)))) & 0xffu);
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][s], B, acc[t], 4, 4, 0,
-                                                                 sA[ht][s], 0, sB);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][s], B, acc, 4, 4, 0,
+                                                              sA[ht][s], 0, sB);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ch[t] = __builtin_fmaf(relu_bits(acc[i]), wv[16 * ht + i], ch[t]);
     }
-    // low half-wave keeps key tile 0, high half-wave key tile 1:
-    // acc[0] <- heads 32ht + [0,16), acc[1] <- heads 32ht + [16,32) of key v0 + lane
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][i]),
-                                                       __float_as_uint(acc[1][i]), false, false);
-      acc[0][i] = __uint_as_float(sw[0]);
-      acc[1][i] = __uint_as_float(sw[1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc = __builtin_fmaf(relu_bits(acc[0][i]), wf[32 * ht + i], sc);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      sc = __builtin_fmaf(relu_bits(acc[1][i]), wf[32 * ht + 16 + i], sc);
   }
-  return sc;
+  // low half-wave: (low chain, high chain) of key tile 0; high half-wave:
+  // the same of key tile 1
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ch[0]), __float_as_uint(ch[1]),
+                                                   false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Score tile of the one-row kernel: staged in LDS, histogram in LDS.
 template <int HT, bool CAND>
 __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
-                                           const int (&sA)[HT][2], const float (&wf)[32 * HT],
+                                           const int (&sA)[HT][2], const float (&wv)[16 * HT],
                                            const PosMap<CAND>& pm, float* __restrict__ sbuf, int v0,
                                            int vbeg, int lane, uint32_t* hist_s) {
-  const float sc = head_sum_tile<HT>(kt, A, sA, wf, lane);
+  const float sc = head_sum_tile<HT>(kt, A, sA, wv, lane);
   sbuf[v0 - vbeg + lane] = sc;  // staged in LDS, written out when the chunk is done
   if (hist_s && pm.pos(v0 + lane) >= 0) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
 }
@@ -244,11 +244,13 @@ __global__ __launch_bounds__(256) void score_kernel(
     reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
   }
 
-  // weights of the row (uniform across the workgroup)
-  float wf[H];
+  // weights of the heads this lane's half-wave sums: wv[j] = w[r][H/2*half + j]
+  float wv[16 * HT];
+  {
+    const uint16_t* wrow = w + (int64_t)r * H + (lane >> 5) * (H / 2);
 #pragma unroll
-  for (int h = 0; h < H; ++h)  // uniform: kept in scalar registers, read by the fmas directly
-    wf[h] = __uint_as_float(__builtin_amdgcn_readfirstlane((uint32_t)w[(int64_t)r * H + h] << 16));
+    for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(wrow[j]);
+  }
 
   __syncthreads();
 
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   int sA[HT][2];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    const int h = head_of_row(ht, lane & 31);
+    const int h = head_of_row<HT>(ht, lane & 31);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = 2 * s + (lane >> 5);
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int u = 0; u < kTileSets; ++u) {
       buf[(u + kTileSets - 1) % kTileSets] =
           load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane);
-      score_tile<HT, CAND>(buf[u], A, sA, wf, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
+      score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
       if (j >= ntiles) goto done;
     }
