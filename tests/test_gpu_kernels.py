@@ -227,12 +227,17 @@ def test_select_blocks_matches_oracle(idx, T, cbs, ctb):
 
 
 # ------------------------------------------------------------------ publish
-@pytest.mark.parametrize("mode", ["decode", "prefill"])
-def test_publish_matches_oracle(idx, mode):
+@pytest.mark.parametrize("mode,din", [("decode", 512), ("prefill", 512), ("decode", 203),
+                                      ("decode", 1000), ("prefill", 4096), ("decode", 24)])
+def test_publish_matches_oracle(idx, mode, din):
+    """wk rows of Din features: whole 64-wide chunks (512), a ragged last
+    chunk with 16-byte rows (1000), rows that are not 16-byte multiples
+    (203: element loads), more chunks than are kept in flight (4096), less
+    than one chunk (24)."""
     t = torch()
-    say("publish", mode)
+    say("publish", mode, din)
     rng = np.random.default_rng(41)
-    B, din, tcap = 4, 512, 300
+    B, tcap = 4, 300
     G = 1 if mode == "decode" else 37
     start_pos = 4 * 250 - 1 if mode == "decode" else 0
     latent = normal_bf16(rng, (B, G, din))
