@@ -384,10 +384,12 @@ int pick_keys_per_wg(int64_t R, int vtotal) {
     const int o = (g_keys_per_wg_override + 255) / 256 * 256;
     return o < kMaxKeysPerWg ? o : kMaxKeysPerWg;
   }
-  // about two resident workgroups per CU over the whole launch (256 CUs), at
-  // least 1024 keys per workgroup so the query quantisation stays amortised
+  // about one workgroup per CU over the whole launch (256 CUs): measured on
+  // the decode shapes, one workgroup of four waves per CU streams as fast as
+  // two or more, and each workgroup pays the query load and quantisation
+  // once; at least 1024 keys per workgroup so that cost stays amortised
   const int64_t total = R * (int64_t)vtotal;
-  int64_t kpw = (total + 511) / 512;
+  int64_t kpw = (total + 255) / 256;
   if (kpw < 1024) kpw = 1024;
   if (kpw > vtotal) kpw = vtotal;
   if (kpw > kMaxKeysPerWg) kpw = kMaxKeysPerWg;
