@@ -87,14 +87,38 @@ struct PosMap {
 
 // Loads are issued for every lane without branches, so the compiler can keep
 // the next tile's loads in flight while the current tile computes.  A lane
-// without a key reads row 0 of the sequence instead; its MFMA column is then
-// a product of valid codes that is simply not stored (columns of the
+// without a key reads zeros (plain mode) or row 0 of the sequence (candidate
+// mode); its MFMA column is then simply not stored (columns of the
 // accumulator depend only on their own key).
+//
+// Plain mode: v0 is uniform across the wave, so the tile's base address and
+// the number of bytes left before vlim go into a buffer resource held in
+// scalar registers; every lane's offset is then the same for every tile, and
+// the hardware range check returns zeros for keys at or past vlim (without
+// reading them).  No per-tile vector address arithmetic.
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
+
 template <bool CAND>
 __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
                                              const PosMap<CAND>& pm, int v0, int lane) {
   KeyTile kt;
   const int half = lane >> 5;
+  if constexpr (!CAND) {
+    const int left = pm.vlim - v0;
+    const int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytes : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kseq + (int64_t)v0 * kRowBytes), (short)0, nrec, kBufWord3);
+    const int vs = (lane & 31) * kRowBytes, vc = vs + 16 * half;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, vc + 32 * kRowBytes * t, 0, 0);
+      const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, vc + 32 * kRowBytes * t + 32, 0, 0);
+      kt.c[t][0] = u32x4{c0[0], c0[1], c0[2], c0[3]};
+      kt.c[t][1] = u32x4{c1[0], c1[1], c1[2], c1[3]};
+      kt.sc[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 32 * kRowBytes * t + 64, 0, 0);
+    }
+    return kt;
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int p = pm.pos(v0 + 32 * t + (lane & 31));
@@ -183,7 +207,9 @@ __global__ __launch_bounds__(256) void score_kernel(
   __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
   __shared__ uint32_t wtot[8], sh[4];
   extern __shared__ __attribute__((aligned(16))) float sbuf[];  // this chunk's scores
-  const int r = blockIdx.x;
+  // rows in reverse dispatch order: causal rows grow with their index, so the
+  // longest start first and the short ones fill the end of the launch
+  const int r = gridDim.x - 1 - blockIdx.x;
   const int b = r / S;
   int limit = cl[r];
   limit = limit < 0 ? 0 : (limit > T ? T : limit);
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   // are in flight
   const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
   const int ntiles = (vend - vbeg + 63) >> 6;
-  int j = wave;
+  int j = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile bases stay scalar
   KeyTile buf[kTileSets];
 #pragma unroll
   for (int i = 0; i < kTileSets - 1; ++i) buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane);
