@@ -154,14 +154,16 @@ __device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       v16f acc = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 c = kt.c[t][s];
-        const v8i B = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        const int sB = (int)((kt.sc[t] >> (8 * (2 * s + (lane >> 5)))) & 0xffu);
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][s], B, acc, 4, 4, 0,
-                                                              sA[ht][s], 0, sB);
-      }
+      // the high half-wave's blocks are the odd ones: shift its scale bytes
+      // down by one, then the MFMA's scale byte select (op_sel) picks byte 2s
+      const int scs = (int)(kt.sc[t] >> (8 * (lane >> 5)));
+      const u32x4 c0 = kt.c[t][0], c1 = kt.c[t][1];
+      const v8i B0 = v8i{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, 0, 0, 0, 0};
+      const v8i B1 = v8i{(int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w, 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][0], B0, acc, 4, 4, 0, sA[ht][0],
+                                                            0, scs);
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][1], B1, acc, 4, 4, 0, sA[ht][1],
+                                                            2, scs);
 #pragma unroll
       for (int i = 0; i < 16; ++i) ch[t] = __builtin_fmaf(relu_bits(acc[i]), wv[16 * ht + i], ch[t]);
     }
@@ -181,7 +183,15 @@ __device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT]
                                            int vbeg, int lane, uint32_t* hist_s) {
   const float sc = head_sum_tile<HT>(kt, A, sA, wv, lane);
   sbuf[v0 - vbeg + lane] = sc;  // staged in LDS, written out when the chunk is done
-  if (hist_s && pm.pos(v0 + lane) >= 0) atomicAdd(&hist_s[score_key(sc) >> 21], 1u);
+  if (hist_s) {
+    // the head sum never yields -0 (two chains from +0, then their sum), so
+    // the first key digit needs no -0 canonicalisation
+    const uint32_t u = __float_as_uint(sc);
+    const uint32_t bin = (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) >> 21;
+    // plain mode counts every lane: a lane past the chunk read a zero key and
+    // scored exactly +0, and the caller removes those counts once
+    if (!CAND || pm.pos(v0 + lane) >= 0) atomicAdd(&hist_s[bin], 1u);
+  }
 }
 
 // Fused top-k of a row scored by one workgroup (rows up to kFusedMaxT).
@@ -313,6 +323,14 @@ done:
   // stores with the key stream costs far more HBM time than one burst
   __syncthreads();
   const int n = vend - vbeg;
+  // every wave scores at least one tile (a wave past the last tile scores a
+  // tile of zero keys before the loop test), so max(ntiles, 4) tiles ran
+  const int lanes_scored = (ntiles > 4 ? ntiles : 4) * 64;
+  if (!CAND && hist_s && lanes_scored > n) {  // uniform
+    // the lanes past the chunk end each counted one +0 score
+    if (tid == 0) hist_lds[score_key(0.0f) >> 21] -= (uint32_t)(lanes_scored - n);
+    __syncthreads();
+  }
   if (TOPK && !srow) {
     // scores not wanted: only the ranking below
   } else if (!CAND && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
