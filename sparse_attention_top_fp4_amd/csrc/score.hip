@@ -204,6 +204,37 @@ struct FusedTopk {
 constexpr int kFusedEPT = 32;                     // keys per thread in the fused ranking
 constexpr int kFusedMaxT = 256 * kFusedEPT;       // 8192
 
+// Ranks a row scored into LDS by one workgroup (limit > kout), with the
+// row layout of row_topk.hpp over 256 * EPT >= limit positions.  Positions
+// in [limit, 256 * EPT) rank as -inf and past T as absent; none of them can
+// be taken, since the row has more than kout finite scores.  hist_lds holds
+// the first-digit counts of the `limit` scores.
+template <int EPT>
+__device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint32_t* sh,
+                                           uint32_t* wtot, int limit, int T, const FusedTopk& tk,
+                                           int32_t* orow) {
+  const int tid = threadIdx.x;
+  const int span = T < 256 * EPT ? T : 256 * EPT;
+  const int wbase = row_base<EPT>();
+  float v[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) v[e] = sbuf[wbase + 64 * e];
+  row_vals<EPT>(v, wbase, limit, span);  // whatever sbuf held past limit
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mine += hist_lds[tid + 256 * j];
+  const uint32_t counted = block_sum<256>(mine, wtot);
+  uint32_t prefix, need, bcnt;
+  int shift;
+  row_select<256, EPT>(v, hist_lds, counted, span, tk.kout, sh, wtot, prefix, shift, need, bcnt);
+  // the score buffer is free once the scores are in registers: it holds the
+  // selection masks (the launch sizes it for them)
+  row_emit<256, EPT>(v, prefix, shift, need, bcnt, limit, tk.kout, tk.offset, wbase,
+                     reinterpret_cast<uint32_t*>(sbuf),
+                     tk.kout <= 2048 ? reinterpret_cast<int32_t*>(hist_lds) : nullptr, wtot,
+                     orow);
+}
+
 template <int HT, bool CAND, bool TOPK>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
@@ -356,27 +387,14 @@ done:
       row_keep_prefix<256>(limit, tk.kout, tk.offset, orow);
       return;
     }
-    // sbuf spans kFusedMaxT floats here; positions >= limit are masked by
-    // row_vals whatever they read
-    const int wbase = row_base<kFusedEPT>();
-    float v[kFusedEPT];
-#pragma unroll
-    for (int e = 0; e < kFusedEPT; ++e) v[e] = sbuf[wbase + 64 * e];
-    row_vals<kFusedEPT>(v, wbase, limit, T);
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mine += hist_lds[tid + 256 * j];
-    const uint32_t counted = block_sum<256>(mine, wtot);
-    uint32_t prefix, need, bcnt;
-    int shift;
-    row_select<256, kFusedEPT>(v, hist_lds, counted, T, tk.kout, sh, wtot, prefix, shift, need,
-                               bcnt);
-    // the score buffer is free once the scores are in registers: it holds the
-    // selection masks (the launch sizes it for them)
-    row_emit<256, kFusedEPT>(v, prefix, shift, need, bcnt, limit, tk.kout, tk.offset, wbase,
-                             reinterpret_cast<uint32_t*>(sbuf),
-                             tk.kout <= 2048 ? reinterpret_cast<int32_t*>(hist_lds) : nullptr,
-                             wtot, orow);
+    // the ranked layout only needs to cover [0, limit): 256 * EPT positions
+    // with EPT sized to the row (the ranking's work is proportional to EPT)
+    if (limit <= 256 * 16)
+      fused_rank<16>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
+    else if (limit <= 256 * 24)
+      fused_rank<24>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
+    else
+      fused_rank<kFusedEPT>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
   }
 }
 
