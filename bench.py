@@ -56,20 +56,29 @@ def parse():
     return ap.parse_args()
 
 
-def score_kernel_bytes(wl) -> int:
+def scored_compress_lens(wl, st):
+    """compress_lens of the rows the score launch scores: every row, except
+    that the fused launch without scores kept writes rows whose compress_lens
+    is at most k_out in closed form, without scoring them."""
+    import numpy as np
+    cl = np.minimum(wl.compress_lens().astype(np.int64), wl.T)
+    if st.fused and st.scores is None:
+        cl = np.where(cl > min(wl.topk, wl.T), cl, 0)
+    return cl
+
+
+def score_kernel_bytes(wl, st) -> int:
     """Algorithmic HBM bytes of one score launch: per scored (row, key) pair
     the 68-byte key row and the 4-byte fp32 score; per row the bf16 query
     (H x 128 x 2) and the bf16 weights (H x 2)."""
-    import numpy as np
-    cl = np.minimum(wl.compress_lens().astype(np.int64), wl.T)
+    cl = scored_compress_lens(wl, st)
     pairs = int(cl.sum())
-    return pairs * (68 + 4) + wl.R * (wl.H * 128 * 2 + wl.H * 2)
+    rows = int((cl > 0).sum())
+    return pairs * (68 + 4) + rows * (wl.H * 128 * 2 + wl.H * 2)
 
 
-def score_kernel_flops(wl) -> int:
-    import numpy as np
-    cl = np.minimum(wl.compress_lens().astype(np.int64), wl.T)
-    return int(cl.sum()) * wl.H * 128 * 2
+def score_kernel_flops(wl, st) -> int:
+    return int(scored_compress_lens(wl, st).sum()) * wl.H * 128 * 2
 
 
 def score_kernel_name(st) -> str:
@@ -191,8 +200,8 @@ def main():
 
     step_s = (t1 - t0) / args.steps
     score_ms = float(np.mean([idx.idx_timing_read(n) for n in slot.values()]))
-    kb = score_kernel_bytes(wl)
-    kf = score_kernel_flops(wl)
+    kb = score_kernel_bytes(wl, st)
+    kf = score_kernel_flops(wl, st)
     prefill = wl.S > 1
     if prefill:  # many queries share each key: the contraction bounds the kernel
         roof = {"bound": "mfma", "achieved": kf / (score_ms * 1e-3) / 1e12,

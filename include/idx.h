@@ -59,7 +59,7 @@ const char *idx_version(void);
 /*
  * Launch timing of the score kernel (measurement support, not a page
  * operation).  idx_timing_arm(slot) makes the next score launch of this
- * process (idx_score or idx_score_topk, any stream) record the start and end
+ * process (idx_score, idx_score_topk or their paged forms, any stream) record the start and end
  * of that kernel's execution into HIP event pair `slot` (0 <= slot < 256),
  * through hipExtLaunchKernel, so no marker packet is added to the stream;
  * the pair is created on first use on the current device and kept until
@@ -131,7 +131,10 @@ idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cach
  * idx_score_topk -- idx_score followed by idx_topk in one launch, for rows of
  * at most 8192 positions (prefill rows, short contexts): one workgroup
  * scores a whole row into on-chip memory and ranks it there, so the scores
- * never travel through device memory unless asked for.  Arguments and
+ * never travel through device memory unless asked for.  Without scores, a
+ * row with compress_lens[r] <= index_topk is written in closed form and not
+ * scored at all ([VLLM, _fill_short_context_topk_indices]: its result does
+ * not depend on the scores).  Arguments and
  * results as idx_score (no candidates, no histogram) and idx_topk (no
  * workspace): out gets, per row, min(index_topk, T) positions in position
  * order, t + offset where t < compress_lens[r], else -1.
@@ -144,6 +147,40 @@ idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k
                           int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                           const int32_t *compress_lens, int index_topk, int32_t offset,
                           int32_t *out, int64_t ld_out, float *scores, int64_t ld, void *stream);
+
+/*
+ * Paged key cache ([VLLM, DeepseekV4IndexerCache.get_kv_cache_spec]: pages of
+ * 64 compressed positions, 64 * compress_ratio tokens, reached through a
+ * per-sequence block table).  Row t of sequence b lives in slot t % 64 of
+ * physical page block_table[b][t / 64]; slot s of page p is the 68-byte row
+ * at k_pages + p * page_stride + 68 * s.
+ *   k_pages      device, the page pool
+ *   page_stride  bytes between pages, >= 64 * 68
+ *   n_pages      pages in the pool; an id outside [0, n_pages) is never
+ *                dereferenced: its keys score as zero rows (idx_score_paged)
+ *                or its row is not written (idx_publish_keys_paged)
+ *   block_table  device, [B][bt_stride] int32 physical page ids, read for
+ *                the pages that hold positions t < min(compress_lens[r], T)
+ *                (score) or the published rows (publish)
+ *   bt_stride    >= ceil(T / 64) (score) or ceil(Tcap / 64) (publish)
+ * Everything else, and every result, is as for the contiguous call of the
+ * same name; the results are bit-identical to it on the same rows.
+ */
+
+/* idx_score without candidate blocks, on a paged key cache. */
+idx_status idx_score_paged(const uint16_t *q, const uint16_t *w, const uint8_t *k_pages,
+                           int64_t page_stride, int n_pages, const int32_t *block_table,
+                           int64_t bt_stride, int B, int S, int H, int D, int T,
+                           const int32_t *compress_lens, float *scores, int64_t ld,
+                           uint32_t *key_hist, void *stream);
+
+/* idx_score_topk on a paged key cache. */
+idx_status idx_score_topk_paged(const uint16_t *q, const uint16_t *w, const uint8_t *k_pages,
+                                int64_t page_stride, int n_pages, const int32_t *block_table,
+                                int64_t bt_stride, int B, int S, int H, int D, int T,
+                                const int32_t *compress_lens, int index_topk, int32_t offset,
+                                int32_t *out, int64_t ld_out, float *scores, int64_t ld,
+                                void *stream);
 
 /*
  * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on
@@ -258,6 +295,13 @@ idx_status idx_publish_keys(const uint16_t *latent, const uint16_t *wk, const fl
                             const float *cos_sin, int P, int B, int G, int Din, int D, int rd,
                             float eps, int start_pos, int ratio, uint8_t *k_cache,
                             int64_t k_batch_stride_rows, int Tcap, void *stream);
+
+/* idx_publish_keys into a paged key cache (rows < Tcap, as above). */
+idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, const float *gamma,
+                                  const float *cos_sin, int P, int B, int G, int Din, int D,
+                                  int rd, float eps, int start_pos, int ratio, uint8_t *k_pages,
+                                  int64_t page_stride, int n_pages, const int32_t *block_table,
+                                  int64_t bt_stride, int Tcap, void *stream);
 
 /*
  * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys

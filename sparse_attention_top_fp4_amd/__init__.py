@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
+__all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_score_paged",
+           "idx_score_topk_paged", "idx_publish_keys_paged", "idx_clear_key_hist", "idx_topk",
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
@@ -22,6 +23,7 @@ __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist",
            "load_library", "IdxError", "ROW_BYTES"]
 
 ROW_BYTES = 68
+PAGE_ROWS = 64  # compressed positions per page of a paged key cache
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libidx.so")
 _lib = None
@@ -64,13 +66,20 @@ def load_library():
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
     L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
                                    i32, P]
+    L.idx_score_paged.argtypes = [P, P, P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, P, i64,
+                                  P, P]
+    L.idx_score_topk_paged.argtypes = [P, P, P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, i32,
+                                       ctypes.c_int32, P, i64, P, i64, P]
+    L.idx_publish_keys_paged.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                         P, i64, i32, P, i64, i32, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
     L.idx_timing_arm.argtypes = [i32]
     L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
     for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
                  "idx_topk_candidates",
                  "idx_select_candidate_blocks",
-                 "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read"):
+                 "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read",
+                 "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -193,6 +202,91 @@ def idx_score_topk(q, w, k_cache, B, S, T, compress_lens, index_topk, offset, ou
                                          H, D, T, _ptr(compress_lens), index_topk, offset,
                                          _ptr(out), out.shape[1], _ptr(scores), ld,
                                          _stream(stream)), "idx_score_topk")
+
+
+def _pages(k_pages, block_table, B):
+    """k_pages [n_pages, page_bytes] or [n_pages, 64, 68] uint8 (page_bytes >=
+    64 * 68), block_table [>= B, bt_stride] int32 -> (page_stride, n_pages,
+    bt_stride)."""
+    torch = _torch()
+    _dev(k_pages, "k_pages", (torch.uint8,))
+    _dev(block_table, "block_table", (torch.int32,), 2)
+    if k_pages.dim() not in (2, 3) or block_table.shape[0] < B:
+        raise ValueError("k_pages must be [n_pages, page_bytes] or [n_pages, 64, 68] and "
+                         "block_table [>=B, bt_stride]")
+    return k_pages.stride(0), k_pages.shape[0], block_table.shape[1]
+
+
+def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, key_hist=None,
+                    stream=None):
+    """idx_score (no candidates) on a paged key cache: row t of sequence b in
+    slot t % 64 of page block_table[b, t // 64] of k_pages."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if scores.shape[0] != R:
+        raise ValueError("scores must be [B*S, ld]")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    ps, npg, bts = _pages(k_pages, block_table, B)
+    _check(load_library().idx_score_paged(_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
+                                          _ptr(block_table), bts, B, S, H, D, T,
+                                          _ptr(compress_lens), _ptr(scores), scores.shape[1],
+                                          _ptr(key_hist), _stream(stream)), "idx_score_paged")
+
+
+def idx_score_topk_paged(q, w, k_pages, block_table, B, S, T, compress_lens, index_topk, offset,
+                         out, scores=None, stream=None):
+    """idx_score_topk on a paged key cache (pages as for idx_score_paged)."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if out.shape[0] != R:
+        raise ValueError("out must be [B*S, ld_out]")
+    ld = 0
+    if scores is not None:
+        _dev(scores, "scores", (torch.float32,), 2)
+        if scores.shape[0] != R:
+            raise ValueError("scores must be [B*S, ld]")
+        ld = scores.shape[1]
+    ps, npg, bts = _pages(k_pages, block_table, B)
+    _check(load_library().idx_score_topk_paged(_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
+                                               _ptr(block_table), bts, B, S, H, D, T,
+                                               _ptr(compress_lens), index_topk, offset,
+                                               _ptr(out), out.shape[1], _ptr(scores), ld,
+                                               _stream(stream)), "idx_score_topk_paged")
+
+
+def idx_publish_keys_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_pages,
+                           block_table, Tcap, rd=64, stream=None):
+    """idx_publish_keys into a paged key cache of Tcap rows per sequence."""
+    torch = _torch()
+    _dev(latent, "latent", _bf16_types(), 3)
+    _dev(wk, "wk", _bf16_types(), 2)
+    _dev(gamma, "gamma", (torch.float32,), 1)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    B, G, Din = latent.shape
+    D = wk.shape[0]
+    if wk.shape[1] != Din or gamma.shape[0] != D:
+        raise ValueError("shape mismatch in idx_publish_keys_paged")
+    ps, npg, bts = _pages(k_pages, block_table, B)
+    _check(load_library().idx_publish_keys_paged(_ptr(latent), _ptr(wk), _ptr(gamma),
+                                                 _ptr(cos_sin), cos_sin.shape[0], B, G, Din, D,
+                                                 rd, eps, start_pos, ratio, _ptr(k_pages), ps,
+                                                 npg, _ptr(block_table), bts, Tcap,
+                                                 _stream(stream)), "idx_publish_keys_paged")
 
 
 def idx_clear_key_hist(key_hist, stream=None):

@@ -67,7 +67,7 @@ __device__ __forceinline__ void publish_finish(const float* y_s, uint32_t* z_s, 
   }
   __syncthreads();
 
-  if (o < 4) {
+  if (o < 4 && dst) {
     uint32_t xp[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) xp[i] = z_s[32 * o + 2 * i] | (z_s[32 * o + 2 * i + 1] << 16);
@@ -80,10 +80,13 @@ __device__ __forceinline__ void publish_finish(const float* y_s, uint32_t* z_s, 
   }
 }
 
+constexpr int kPubPageRows = 64;  // compressed positions per page of a paged cache
+
 __global__ __launch_bounds__(128) void publish_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
     const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
-    int start_pos, int ratio, int G, uint8_t* __restrict__ kc, int64_t kstride) {
+    int start_pos, int ratio, int G, uint8_t* __restrict__ kc, int64_t kstride,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lat_s[];  // Din bf16
   __shared__ float y_s[kHeadDim];
   __shared__ uint32_t z_s[kHeadDim];
@@ -127,16 +130,29 @@ __global__ __launch_bounds__(128) void publish_kernel(
   for (; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
   y_s[o] = bf16f(f32_to_bf16(acc));
   __syncthreads();
-  publish_finish(y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, kc + ((int64_t)b * kstride + row) * kRowBytes);
+  // contiguous rows, or slot row % 64 of the sequence's page row / 64 (a
+  // page id outside [0, n_pages) is not written)
+  uint8_t* dst = nullptr;
+  if (!bt) {
+    dst = kc + ((int64_t)b * kstride + row) * kRowBytes;
+  } else {
+    const int page = bt[(int64_t)b * bt_stride + row / kPubPageRows];
+    if (page >= 0 && page < n_pages)
+      dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * kRowBytes;
+  }
+  publish_finish(y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst);
 }
 
 }  // namespace idx
 
-extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* wk,
-                                       const float* gamma, const float* cos_sin, int P, int B,
-                                       int G, int Din, int D, int rd, float eps, int start_pos,
-                                       int ratio, uint8_t* k_cache, int64_t k_batch_stride_rows,
-                                       int Tcap, void* stream) {
+namespace {
+// Shared by the contiguous and the paged entry points (bt null: contiguous
+// rows of stride k_batch_stride_rows).
+idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float* gamma,
+                        const float* cos_sin, int P, int B, int G, int Din, int D, int rd,
+                        float eps, int start_pos, int ratio, uint8_t* k_cache,
+                        int64_t k_batch_stride_rows, int Tcap, const int32_t* bt,
+                        int64_t bt_stride, int64_t page_stride, int n_pages, void* stream) {
   if (B < 0 || G < 0 || Din <= 0 || D <= 0 || ratio <= 0 || start_pos < 0 || P < 0 || Tcap < 0)
     return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
@@ -144,7 +160,7 @@ extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* w
   if (!(eps >= 0.0f)) return IDX_EINVAL;
   if ((int64_t)B * G == 0) return IDX_OK;
   if (!latent || !wk || !gamma || !k_cache || (rd > 0 && !cos_sin)) return IDX_EINVAL;
-  if (k_batch_stride_rows < Tcap) return IDX_EINVAL;
+  if (!bt && k_batch_stride_rows < Tcap) return IDX_EINVAL;
   int64_t max_pos, max_row;
   if (start_pos == 0) {
     max_pos = (int64_t)(G - 1) * ratio;
@@ -161,8 +177,36 @@ extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* w
   if ((size_t)Din * 2 > 60 * 1024) return IDX_EUNSUPPORTED;
   hipLaunchKernelGGL(idx::publish_kernel, dim3((unsigned)(B * G)), dim3(idx::kHeadDim),
                      (size_t)Din * 2, (hipStream_t)stream, latent, wk, gamma, cos_sin, Din, rd, eps,
-                     start_pos, ratio, G, k_cache, k_batch_stride_rows);
+                     start_pos, ratio, G, k_cache, k_batch_stride_rows, bt, bt_stride,
+                     page_stride, n_pages);
   return idx_host::launch_status();
+}
+}  // namespace
+
+extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* wk,
+                                       const float* gamma, const float* cos_sin, int P, int B,
+                                       int G, int Din, int D, int rd, float eps, int start_pos,
+                                       int ratio, uint8_t* k_cache, int64_t k_batch_stride_rows,
+                                       int Tcap, void* stream) {
+  return publish_impl(latent, wk, gamma, cos_sin, P, B, G, Din, D, rd, eps, start_pos, ratio,
+                      k_cache, k_batch_stride_rows, Tcap, nullptr, 0, 0, 0, stream);
+}
+
+extern "C" idx_status idx_publish_keys_paged(const uint16_t* latent, const uint16_t* wk,
+                                             const float* gamma, const float* cos_sin, int P,
+                                             int B, int G, int Din, int D, int rd, float eps,
+                                             int start_pos, int ratio, uint8_t* k_pages,
+                                             int64_t page_stride, int n_pages,
+                                             const int32_t* block_table, int64_t bt_stride,
+                                             int Tcap, void* stream) {
+  if ((int64_t)B * G > 0) {
+    if (!block_table || n_pages <= 0) return IDX_EINVAL;
+    if (page_stride < (int64_t)idx::kPubPageRows * idx::kRowBytes) return IDX_EINVAL;
+    if (bt_stride < ((int64_t)Tcap + idx::kPubPageRows - 1) / idx::kPubPageRows)
+      return IDX_EINVAL;
+  }
+  return publish_impl(latent, wk, gamma, cos_sin, P, B, G, Din, D, rd, eps, start_pos, ratio,
+                      k_pages, 0, Tcap, block_table, bt_stride, page_stride, n_pages, stream);
 }
 
 // Host-side YaRN RoPE table (the YaRN method of Peng et al.): base inverse

@@ -98,16 +98,39 @@ struct PosMap {
 // reading them).  No per-tile vector address arithmetic.
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
 
+// Paged key cache ([VLLM, DeepseekV4IndexerCache]: pages of 64 compressed
+// positions): row t of a sequence lives in slot t % 64 of physical page
+// bt_row[t / 64], page p at pages + p * page_stride bytes.  A 64-key tile of
+// plain mode starts at a multiple of 64, so it is exactly one page.
+constexpr int kPageRows = 64;  // compressed positions per page
+
+struct PageMap {
+  const int32_t* bt;    // [B][bt_stride] physical page ids, or null (contiguous rows)
+  int64_t bt_stride;
+  int64_t page_stride;  // bytes
+  int n_pages;          // valid ids are [0, n_pages)
+};
+
 template <bool CAND>
 __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
-                                             const PosMap<CAND>& pm, int v0, int lane) {
+                                             const PosMap<CAND>& pm, int v0, int lane,
+                                             const int32_t* __restrict__ bt_row = nullptr,
+                                             int64_t page_stride = 0, int n_pages = 0) {
   KeyTile kt;
   const int half = lane >> 5;
   if constexpr (!CAND) {
     const int left = pm.vlim - v0;
-    const int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytes : 0;
+    int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytes : 0;
+    const uint8_t* base = kseq + (int64_t)v0 * kRowBytes;
+    if (bt_row) {  // uniform: the tile's page, read only for a tile with keys
+      const int page = nrec > 0 ? bt_row[v0 >> 6] : -1;
+      // an id outside [0, n_pages) reads nothing (its keys read as zeros)
+      const bool ok = page >= 0 && page < n_pages;
+      base = kseq + (ok ? (int64_t)page * page_stride : 0);
+      nrec = ok ? nrec : 0;
+    }
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(kseq + (int64_t)v0 * kRowBytes), (short)0, nrec, kBufWord3);
+        const_cast<uint8_t*>(base), (short)0, nrec, kBufWord3);
     const int vs = (lane & 31) * kRowBytes, vc = vs + 16 * half;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -241,7 +264,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
-    FusedTopk tk) {
+    FusedTopk tk, PageMap pg) {
   constexpr int H = 32 * HT;
   __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
   __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
@@ -263,9 +286,11 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int vtotal = CAND ? n_cand * cbs : limit;
   const int vbeg = blockIdx.y * keys_per_wg;
   const int vend = min(vbeg + keys_per_wg, vtotal);
-  if (vbeg >= vend) {
-    if (TOPK)  // nothing to score: the row keeps its lowest positions, all masked
-      row_keep_prefix<256>(limit, tk.kout, tk.offset, tk.out + (int64_t)r * tk.ld_out);
+  // nothing to score, or (fused, scores not wanted) a row with at most kout
+  // reachable positions: it keeps [0, limit) and then the lowest masked
+  // positions, whatever the scores ([VLLM, _fill_short_context_topk_indices])
+  if (vbeg >= vend || (TOPK && !scores && limit <= tk.kout)) {
+    if (TOPK) row_keep_prefix<256>(limit, tk.kout, tk.offset, tk.out + (int64_t)r * tk.ld_out);
     return;
   }
   pm.vlim = vend;
@@ -280,12 +305,15 @@ __global__ __launch_bounds__(256) void score_kernel(
   // latency overlaps the query load and quantisation.  kTileSets register
   // sets: while one tile computes, the next kTileSets - 1 tiles of this wave
   // are in flight
-  const uint8_t* kseq = kc + (int64_t)b * kstride * kRowBytes;
+  // contiguous: the sequence's rows; paged: the page pool (plain mode only)
+  const uint8_t* kseq = pg.bt ? kc : kc + (int64_t)b * kstride * kRowBytes;
+  const int32_t* bt_row = pg.bt ? pg.bt + (int64_t)b * pg.bt_stride : nullptr;
   const int ntiles = (vend - vbeg + 63) >> 6;
   int j = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile bases stay scalar
   KeyTile buf[kTileSets];
 #pragma unroll
-  for (int i = 0; i < kTileSets - 1; ++i) buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane);
+  for (int i = 0; i < kTileSets - 1; ++i)
+    buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, bt_row, pg.page_stride, pg.n_pages);
 
   uint32_t* hist_s = (key_hist || TOPK) ? hist_lds : nullptr;
   if (hist_s)
@@ -343,7 +371,8 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int u = 0; u < kTileSets; ++u) {
       buf[(u + kTileSets - 1) % kTileSets] =
-          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane);
+          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane, bt_row,
+                    pg.page_stride, pg.n_pages);
       score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
       if (j >= ntiles) goto done;
@@ -471,17 +500,20 @@ extern "C" idx_status idx_clear_key_hist(uint32_t* key_hist, int R, void* stream
   return idx_host::launch_status();
 }
 
-extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
-                                int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
-                                const int32_t* compress_lens, const int32_t* cand_blocks,
-                                int n_cand, int cand_block_size, float* scores, int64_t ld,
-                                uint32_t* key_hist, void* stream) {
+namespace {
+// Shared by the contiguous and the paged entry points: the key source is
+// (k_cache, k_batch_stride_rows) when pg.bt is null, else the page pool.
+idx_status score_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                      int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                      const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
+                      int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
+                      idx::PageMap pg, void* stream) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
   if (!q || !w || !k_cache || !compress_lens || !scores) return IDX_EINVAL;
-  if (ld < T || k_batch_stride_rows < T) return IDX_EINVAL;
+  if (ld < T || (!pg.bt && k_batch_stride_rows < T)) return IDX_EINVAL;
   if (cand_blocks && (n_cand <= 0 || cand_block_size <= 0)) return IDX_EINVAL;
   if (cand_blocks && n_cand > idx::kMaxCand) return IDX_EUNSUPPORTED;
   const int64_t R = (int64_t)B * S;
@@ -507,14 +539,15 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                                      : idx::score_kernel<1, false, false>);
   return launch_score(kern, grid, (size_t)kpw * sizeof(float), st, q, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
-                      cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0});
+                      cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
+                      pg);
 }
 
-extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
-                                     int64_t k_batch_stride_rows, int B, int S, int H, int D,
-                                     int T, const int32_t* compress_lens, int index_topk,
-                                     int32_t offset, int32_t* out, int64_t ld_out, float* scores,
-                                     int64_t ld, void* stream) {
+idx_status score_topk_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                           int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                           const int32_t* compress_lens, int index_topk, int32_t offset,
+                           int32_t* out, int64_t ld_out, float* scores, int64_t ld,
+                           idx::PageMap pg, void* stream) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0 || index_topk <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -522,7 +555,8 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
   if (!q || !w || !k_cache || !compress_lens || !out) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
-  if (k_batch_stride_rows < T || ld_out < kout || (scores && ld < T)) return IDX_EINVAL;
+  if ((!pg.bt && k_batch_stride_rows < T) || ld_out < kout || (scores && ld < T))
+    return IDX_EINVAL;
   const int64_t R = (int64_t)B * S;
   if (R > 0x7fffffffLL) return IDX_EINVAL;
   hipStream_t st = (hipStream_t)stream;
@@ -534,7 +568,69 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
   return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
-                      (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out});
+                      (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg);
+}
+
+// Page map arguments shared by the paged entry points.
+idx_status page_map(const int32_t* block_table, int64_t bt_stride, int64_t page_stride,
+                    int n_pages, int T, idx::PageMap& pg) {
+  if (!block_table || n_pages <= 0) return IDX_EINVAL;
+  if (page_stride < (int64_t)idx::kPageRows * idx::kRowBytes) return IDX_EINVAL;
+  if (bt_stride < ((int64_t)T + idx::kPageRows - 1) / idx::kPageRows) return IDX_EINVAL;
+  pg = idx::PageMap{block_table, bt_stride, page_stride, n_pages};
+  return IDX_OK;
+}
+}  // namespace
+
+extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                                const int32_t* compress_lens, const int32_t* cand_blocks,
+                                int n_cand, int cand_block_size, float* scores, int64_t ld,
+                                uint32_t* key_hist, void* stream) {
+  return score_impl(q, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens, cand_blocks,
+                    n_cand, cand_block_size, scores, ld, key_hist,
+                    idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                     int64_t k_batch_stride_rows, int B, int S, int H, int D,
+                                     int T, const int32_t* compress_lens, int index_topk,
+                                     int32_t offset, int32_t* out, int64_t ld_out, float* scores,
+                                     int64_t ld, void* stream) {
+  return score_topk_impl(q, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                         index_topk, offset, out, ld_out, scores, ld,
+                         idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_score_paged(const uint16_t* q, const uint16_t* w, const uint8_t* k_pages,
+                                      int64_t page_stride, int n_pages,
+                                      const int32_t* block_table, int64_t bt_stride, int B, int S,
+                                      int H, int D, int T, const int32_t* compress_lens,
+                                      float* scores, int64_t ld, uint32_t* key_hist,
+                                      void* stream) {
+  idx::PageMap pg{nullptr, 0, 0, 0};
+  if (T > 0 && B > 0 && S > 0) {  // the page map matters only when there is work
+    const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, T, pg);
+    if (e != IDX_OK) return e;
+  }
+  return score_impl(q, w, k_pages, 0, B, S, H, D, T, compress_lens, nullptr, 0, 0, scores, ld,
+                    key_hist, pg, stream);
+}
+
+extern "C" idx_status idx_score_topk_paged(const uint16_t* q, const uint16_t* w,
+                                           const uint8_t* k_pages, int64_t page_stride,
+                                           int n_pages, const int32_t* block_table,
+                                           int64_t bt_stride, int B, int S, int H, int D, int T,
+                                           const int32_t* compress_lens, int index_topk,
+                                           int32_t offset, int32_t* out, int64_t ld_out,
+                                           float* scores, int64_t ld, void* stream) {
+  idx::PageMap pg{nullptr, 0, 0, 0};
+  if (T > 0 && B > 0 && S > 0) {  // the page map matters only when there is work
+    const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, T, pg);
+    if (e != IDX_OK) return e;
+  }
+  return score_topk_impl(q, w, k_pages, 0, B, S, H, D, T, compress_lens, index_topk, offset, out,
+                         ld_out, scores, ld, pg, stream);
 }
 
 extern "C" idx_status idx_timing_arm(int slot) {

@@ -144,9 +144,13 @@ class IndexerStep:
         self.cur = (self.cur + 1) % len(self.caches)
 
     def keys_scored(self):
-        """Algorithmic (query, key) pairs scored per step."""
+        """Algorithmic (query, key) pairs scored per step.  The fused launch
+        without scores kept does not score rows whose compress_lens is at
+        most k_out (their result is the closed form)."""
         wl = self.wl
         cl = np.minimum(wl.compress_lens().astype(np.int64), wl.T)
+        if self.fused and self.scores is None:
+            cl = np.where(cl > self.kout, cl, 0)
         n = int(cl.sum())
         if self.two_level:
             n += wl.R * min(wl.ctb * wl.cbs, wl.T)

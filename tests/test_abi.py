@@ -147,3 +147,31 @@ def test_candidate_topk_rejects_bad_arguments(lib):
                                    None) == IDX_EINVAL
     assert lib.idx_topk_candidates(None, 8, 0, 8, None, None, 2, 4, None, 4, 0, None, 4,
                                    None) == IDX_OK
+
+
+def test_paged_entry_points_reject_bad_page_maps(lib):
+    """Page pool, page stride and block table are checked before any launch."""
+    d = ctypes.c_void_p(0x1000)
+    T = 200  # 4 pages of 64 positions
+
+    def score(ps=64 * 68, npg=8, bt=d, bts=4, **kw):
+        return lib.idx_score_paged(d, d, d, ps, npg, bt, bts, 1, 1, 64, 128, T, d, d, T, None,
+                                   None)
+
+    def fused(ps=64 * 68, npg=8, bt=d, bts=4):
+        return lib.idx_score_topk_paged(d, d, d, ps, npg, bt, bts, 1, 1, 64, 128, T, d, 64, 0, d,
+                                        64, None, 0, None)
+
+    def publish(ps=64 * 68, npg=8, bt=d, bts=4, Tcap=T, sp=4 * 50 - 1):
+        return lib.idx_publish_keys_paged(d, d, d, d, 300, 1, 1, 512, 128, 64, 1e-6, sp, 4, d, ps,
+                                          npg, bt, bts, Tcap, None)
+
+    for call in (score, fused, publish):
+        assert call(bt=None) == IDX_EINVAL  # no block table
+        assert call(npg=0) == IDX_EINVAL  # empty page pool
+        assert call(ps=64 * 68 - 1) == IDX_EINVAL  # a page shorter than 64 rows
+        assert call(bts=3) == IDX_EINVAL  # the table row misses page 3
+    assert publish(Tcap=64, sp=4 * 64 + 3) == IDX_EINVAL  # row 64 beyond Tcap
+    # nothing to do: no rows
+    assert lib.idx_score_paged(d, d, d, 64 * 68, 8, None, 4, 0, 1, 64, 128, T, d, d, T, None,
+                               None) == IDX_OK
