@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU work for the oracle baseline sample")
+    ap.add_argument("--paged", action="store_true",
+                    help="key cache in pages of 64 positions behind a block table (the paged "
+                         "entry points; single-level workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -168,7 +171,7 @@ def main():
     cache_bytes = wl.B * wl.T * 68
     n_caches = max(1, min(8, math.ceil(3 * LLC_BYTES / cache_bytes))) if cache_bytes > 2 ** 20 else 1
     # the product path: indices only (a fused launch does not write scores)
-    st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False)
+    st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False, paged=args.paged)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -212,7 +215,8 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     qps = wl.R / step_s
     keys = st.keys_scored()
-    traffic = measured_traffic(wl.name)
+    # the committed counter summary covers the contiguous layout
+    traffic = None if args.paged else measured_traffic(wl.name)
     line = {
         "metric": METRIC,
         "value": qps,
@@ -230,7 +234,8 @@ def main():
                    "end_pos": wl.end_pos, "compress_ratio": wl.ratio, "compressed_keys": wl.T,
                    "index_n_heads": wl.H, "index_head_dim": 128, "index_topk": wl.topk,
                    "candidate_topk_blocks": wl.ctb, "candidate_block_size": wl.cbs,
-                   "publish": wl.publish, "key_cache_copies": n_caches},
+                   "publish": wl.publish, "key_cache_copies": n_caches,
+                   "key_cache_layout": "paged" if args.paged else "contiguous"},
         "keys_scored_per_s": keys / step_s,
         "score_kernel_ms": score_ms,
         "score_kernel_timed_steps": len(timed),

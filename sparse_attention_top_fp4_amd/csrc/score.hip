@@ -111,10 +111,11 @@ struct PageMap {
   int n_pages;          // valid ids are [0, n_pages)
 };
 
+// Paged tiles take their page id from `page` (uniform; see the caller).
 template <bool CAND>
 __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
                                              const PosMap<CAND>& pm, int v0, int lane,
-                                             const int32_t* __restrict__ bt_row = nullptr,
+                                             bool paged = false, int page = -1,
                                              int64_t page_stride = 0, int n_pages = 0) {
   KeyTile kt;
   const int half = lane >> 5;
@@ -122,8 +123,7 @@ __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
     const int left = pm.vlim - v0;
     int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytes : 0;
     const uint8_t* base = kseq + (int64_t)v0 * kRowBytes;
-    if (bt_row) {  // uniform: the tile's page, read only for a tile with keys
-      const int page = nrec > 0 ? bt_row[v0 >> 6] : -1;
+    if (paged) {
       // an id outside [0, n_pages) reads nothing (its keys read as zeros)
       const bool ok = page >= 0 && page < n_pages;
       base = kseq + (ok ? (int64_t)page * page_stride : 0);
@@ -306,14 +306,28 @@ __global__ __launch_bounds__(256) void score_kernel(
   // sets: while one tile computes, the next kTileSets - 1 tiles of this wave
   // are in flight
   // contiguous: the sequence's rows; paged: the page pool (plain mode only)
-  const uint8_t* kseq = pg.bt ? kc : kc + (int64_t)b * kstride * kRowBytes;
-  const int32_t* bt_row = pg.bt ? pg.bt + (int64_t)b * pg.bt_stride : nullptr;
+  const bool paged = !CAND && pg.bt;
+  const uint8_t* kseq = paged ? kc : kc + (int64_t)b * kstride * kRowBytes;
   const int ntiles = (vend - vbeg + 63) >> 6;
   int j = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile bases stay scalar
+  // paged: lane i holds the page of this wave's i-th tile (tile j + 4i; a
+  // chunk has at most 128 tiles, 32 per wave), read here once, so a tile
+  // takes its page with a readlane instead of a memory access; the table is
+  // read only for tiles with keys
+  int pid_lane = -1;
+  if (paged) {
+    const int v0l = vbeg + 64 * (j + 4 * lane);
+    if (v0l < vend) pid_lane = pg.bt[(int64_t)b * pg.bt_stride + (v0l >> 6)];
+  }
+  auto tile_page = [&](int i) {  // i: uniform tile count of this wave
+    return paged ? __builtin_amdgcn_readlane(pid_lane, i < 63 ? i : 63) : -1;
+  };
+  int it = 0;  // tiles of this wave started
   KeyTile buf[kTileSets];
 #pragma unroll
   for (int i = 0; i < kTileSets - 1; ++i)
-    buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, bt_row, pg.page_stride, pg.n_pages);
+    buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, paged, tile_page(i),
+                       pg.page_stride, pg.n_pages);
 
   uint32_t* hist_s = (key_hist || TOPK) ? hist_lds : nullptr;
   if (hist_s)
@@ -371,10 +385,11 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int u = 0; u < kTileSets; ++u) {
       buf[(u + kTileSets - 1) % kTileSets] =
-          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane, bt_row,
-                    pg.page_stride, pg.n_pages);
+          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane, paged,
+                    tile_page(it + kTileSets - 1), pg.page_stride, pg.n_pages);
       score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
+      ++it;
       if (j >= ntiles) goto done;
     }
   }

@@ -12,9 +12,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (idx_clear_key_hist, idx_fp4_quant, idx_publish_keys, idx_score, idx_score_topk,
-               idx_select_candidate_blocks, idx_select_workspace_size, idx_topk,
-               idx_topk_candidates,
+from . import (PAGE_ROWS, idx_clear_key_hist, idx_fp4_quant, idx_publish_keys,
+               idx_publish_keys_paged, idx_score, idx_score_paged, idx_score_topk,
+               idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
+               idx_topk, idx_topk_candidates,
                idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
 
@@ -50,7 +51,8 @@ class IndexerStep:
     # rows up to this width are scored and ranked in one launch
     FUSED_MAX_T = 8192
 
-    def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True):
+    def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True,
+                 paged: bool = False):
         torch = _torch()
         self.wl = wl
         R, T = wl.R, wl.T
@@ -63,6 +65,24 @@ class IndexerStep:
         for _ in range(1, n_caches):
             self.caches.append(self.caches[0].clone())
         self.cur = 0
+        # paged: each cache copy becomes a pool of pages of PAGE_ROWS rows,
+        # the sequences' logical pages in a seeded random order
+        self.paged = paged
+        if paged:
+            if wl.ctb:
+                raise ValueError("the paged path covers single-level scoring")
+            npg = (T + PAGE_ROWS - 1) // PAGE_ROWS
+            perm = np.random.default_rng(7).permutation(wl.B * npg).astype(np.int32)
+            self.block_table = to_device(perm.reshape(wl.B, npg))
+            dst = torch.from_numpy(perm.astype(np.int64)).cuda()
+            pools = []
+            for kc in self.caches:
+                padded = torch.zeros((wl.B, npg * PAGE_ROWS, 68), dtype=torch.uint8, device="cuda")
+                padded[:, :kc.shape[1]] = kc
+                pool = torch.empty((wl.B * npg, PAGE_ROWS * 68), dtype=torch.uint8, device="cuda")
+                pool[dst] = padded.reshape(wl.B * npg, PAGE_ROWS * 68)
+                pools.append(pool)
+            self.caches = pools
         # single-level rows up to FUSED_MAX_T take the fused score + top-k
         # launch; its scores are written only when kept
         self.fused = not wl.ctb and T <= self.FUSED_MAX_T
@@ -115,17 +135,31 @@ class IndexerStep:
         wl = self.wl
         kc = self.caches[self.cur]
         if self.publish:
-            idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
-                             wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+            if self.paged:
+                idx_publish_keys_paged(self.latent, self.wk, self.gamma, self.cos_sin,
+                                       wl.start_pos, wl.ratio, wl.eps, kc, self.block_table, wl.T,
+                                       rd=wl.rd, stream=stream)
+            else:
+                idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
+                                 wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
         if time_slot is not None:
             idx_timing_arm(time_slot)
         if self.fused:
-            idx_score_topk(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
-                           self.out, scores=self.scores, stream=stream)
+            if self.paged:
+                idx_score_topk_paged(self.q, self.w, kc, self.block_table, wl.B, wl.S, wl.T,
+                                     self.cl, wl.topk, wl.offset, self.out, scores=self.scores,
+                                     stream=stream)
+            else:
+                idx_score_topk(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
+                               self.out, scores=self.scores, stream=stream)
             self.cur = (self.cur + 1) % len(self.caches)
             return
-        idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
-                  key_hist=self.key_hist, stream=stream)
+        if self.paged:
+            idx_score_paged(self.q, self.w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
+                            self.scores, key_hist=self.key_hist, stream=stream)
+        else:
+            idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                      key_hist=self.key_hist, stream=stream)
         if self.two_level:
             idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
                                         workspace=self.sel_ws, stream=stream)
