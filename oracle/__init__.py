@@ -29,6 +29,12 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
                    themselves are parity unpinned (the pages name them only).
   publish          pinned: pre-quantisation key vs a float64 restatement within
                    bf16 rounding; RoPE identity at position 0; norm preservation.
+  q_rope_quant     pinned: RoPE identity at position 0 and with rd = 0 (the
+                   rows are then the quantiser's); rotation vs a float64
+                   restatement within bf16 rounding; pair norms; weights
+                   exact for power-of-two scales, within one bf16 ulp of the
+                   float64 product otherwise; the round trip re-quantises to
+                   the same rows.
 """
 from __future__ import annotations
 
@@ -75,6 +81,8 @@ def lib():
         L.orc_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
         L.orc_yarn_cos_sin.restype = None
         L.orc_publish.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, P, i64, P]
+        L.orc_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
+        L.orc_q_rope_quant.restype = None
         L.orc_publish.restype = None
         _lib = L
     return _lib
@@ -186,6 +194,29 @@ def publish(latent, wk, gamma, cos_sin, start_pos, ratio, eps, kc, rd=64):
     lib().orc_publish(_p(latent), _p(wk), _p(gamma), _p(cos_sin), cos_sin.shape[0], B, G, Din, rd,
                       eps, start_pos, ratio, _p(kc), kc.shape[1], _p(pre))
     return pre
+
+
+def q_rope_quant(q, w_raw, scale, cos_sin, start_pos, S, rd=64):
+    """[IDX, forward: RoPE on the query heads' last rd dims at positions
+    start_pos + s, fp4_act_quant, weights_proj(x) * scale];
+    [VLLM, fused_indexer_q_rope_quant].  q uint16 [B*S][H][128] (before
+    RoPE), w_raw uint16 [B*S][H], scale float32, cos_sin float32
+    [P][rd/2][2].  Returns (rows uint8 [B*S][H][68], round trip uint16
+    [B*S][H][128], pre-quantisation uint16 [B*S][H][128], weights uint16
+    [B*S][H])."""
+    q = _c(q, np.uint16)
+    w_raw = _c(w_raw, np.uint16)
+    cos_sin = _c(cos_sin, np.float32)
+    R, H, _ = q.shape
+    assert R % S == 0 and w_raw.shape == (R, H)
+    rows = np.empty((R, H, 68), np.uint8)
+    rt = np.empty((R, H, 128), np.uint16)
+    pre = np.empty((R, H, 128), np.uint16)
+    w_out = np.empty((R, H), np.uint16)
+    lib().orc_q_rope_quant(_p(q), _p(w_raw), float(np.float32(scale)), _p(cos_sin),
+                           cos_sin.shape[0], R // S, S, H, rd, start_pos, _p(rows), _p(rt),
+                           _p(pre), _p(w_out))
+    return rows, rt, pre, w_out
 
 
 # ------------------------------------------------- tiny numpy brute force

@@ -470,6 +470,22 @@ void orc_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len, 
  * dims as interleaved pairs (x0, x1) rotated by (c, s):
  * (x0*c - x1*s, x0*s + x1*c), each product and sum rounded in fp32,
  * then bf16.  z: [128] bf16. */
+/* [IDX, forward: apply_rotary_emb on the last rd dims]: interleaved pairs
+ * (x0, x1) = (z[D-rd+2i], z[D-rd+2i+1]) rotated by (c, s) = cs_row[i]:
+ * (x0*c - x1*s, x0*s + x1*c), each product and sum rounded in fp32 (no
+ * fused multiply-add), then bf16.  z: [128] bf16, in place. */
+static void rope_row(uint16_t *z, const float *cs_row, int rd)
+{
+    int base = HEAD_DIM - rd;
+    for (int i = 0; i < rd / 2; ++i) {
+        float x0 = bf16_to_f32(z[base + 2 * i]), x1 = bf16_to_f32(z[base + 2 * i + 1]);
+        float c = cs_row[2 * i], s = cs_row[2 * i + 1];
+        float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
+        z[base + 2 * i] = f32_to_bf16(a - bb);
+        z[base + 2 * i + 1] = f32_to_bf16(cc + dd);
+    }
+}
+
 static void publish_prequant(const uint16_t *latent, const uint16_t *wk, const float *gamma,
                              const float *cs_row, int Din, int rd, float eps, uint16_t *z)
 {
@@ -489,14 +505,7 @@ static void publish_prequant(const uint16_t *latent, const uint16_t *wk, const f
         v = v * gamma[o];
         z[o] = f32_to_bf16(v);
     }
-    int base = HEAD_DIM - rd;
-    for (int i = 0; i < rd / 2; ++i) {
-        float x0 = bf16_to_f32(z[base + 2 * i]), x1 = bf16_to_f32(z[base + 2 * i + 1]);
-        float c = cs_row[2 * i], s = cs_row[2 * i + 1];
-        float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
-        z[base + 2 * i] = f32_to_bf16(a - bb);
-        z[base + 2 * i + 1] = f32_to_bf16(cc + dd);
-    }
+    rope_row(z, cs_row, rd);
 }
 
 /* Position and cache row of group g ([IDX, forward]: in prefill group j sits
@@ -533,5 +542,37 @@ void orc_publish(const uint16_t *latent, const uint16_t *wk, const float *gamma,
         if (prequant)
             memcpy(prequant + bg * HEAD_DIM, z, sizeof(z));
         quant_row(z, kc + (b * kstride + row) * ROW_BYTES, NULL);
+    }
+}
+
+/* ------------------------------------------------------ query RoPE + quant */
+
+/* The query side of the step ([IDX, forward]: q split into heads,
+ * apply_rotary_emb(q[..., -rd:], freqs_cis[start_pos:end_pos]),
+ * fp4_act_quant(q), weights = weights_proj(x) * (softmax_scale *
+ * n_heads^-0.5); [VLLM, fused_indexer_q_rope_quant] does the three in one
+ * step).  Row r = b*S + s sits at position start_pos + s.
+ *   q: [R][H][128] bf16 before RoPE; w_raw: [R][H] bf16; scale: fp32
+ *   cos_sin: [P][rd/2][2] fp32
+ *   rows: [R][H][68] quantised heads; rt (optional): [R][H][128] their bf16
+ *   round trip; prequant (optional): [R][H][128] bf16 after RoPE, before
+ *   quantisation; w_out: [R][H] bf16, bf16(fp32(w_raw) * scale). */
+void orc_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float scale, const float *cos_sin,
+                      int P, int B, int S, int H, int rd, int start_pos, uint8_t *rows,
+                      uint16_t *rt, uint16_t *prequant, uint16_t *w_out)
+{
+    (void)P;
+    int64_t R = (int64_t)B * S;
+#pragma omp parallel for schedule(static)
+    for (int64_t rh = 0; rh < R * H; ++rh) {
+        int64_t r = rh / H;
+        int pos = start_pos + (int)(r % S);
+        uint16_t z[HEAD_DIM];
+        memcpy(z, q + rh * HEAD_DIM, sizeof(z));
+        rope_row(z, cos_sin + (int64_t)pos * rd, rd);
+        if (prequant)
+            memcpy(prequant + rh * HEAD_DIM, z, sizeof(z));
+        quant_row(z, rows + rh * ROW_BYTES, rt ? rt + rh * HEAD_DIM : NULL);
+        w_out[rh] = f32_to_bf16(bf16_to_f32(w_raw[rh]) * scale);
     }
 }
