@@ -87,6 +87,31 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
                          void *stream);
 
 /*
+ * idx_q_rope_quant -- the query side of the step ([IDX, forward: q split
+ * into heads, apply_rotary_emb(q[..., -rd:], freqs_cis[start_pos:end_pos]),
+ * fp4_act_quant(q), weights = weights_proj(x) * softmax_scale *
+ * n_heads^-0.5]; [VLLM, fused_indexer_q_rope_quant] does the three in one
+ * step).  Row r = b*S + s sits at position start_pos + s.  Per head: RoPE
+ * on the last rd dims as interleaved pairs (x0, x1) rotated by (c, s) =
+ * cos_sin[pos][i]: (x0*c - x1*s, x0*s + x1*c), each product and sum
+ * rounded in fp32, result bf16 (as idx_publish_keys); then the block-32
+ * quantiser of idx_fp4_quant.  Weights: bf16(fp32(w_raw) * w_scale).
+ *   q            device, [B*S][H][D] bf16 before RoPE, 16-byte aligned
+ *   w_raw        device, [B*S][H] bf16 (weights_proj output)
+ *   cos_sin      device, [P][rd/2][2] fp32; start_pos + S - 1 < P
+ *   q_rows       device, [B*S][H][68] quantised heads, 4-byte aligned
+ *   q_roundtrip  device, [B*S][H][D] bf16 dequantised heads, 16-byte
+ *                aligned, or NULL.  It is a valid q for idx_score: the
+ *                quantiser maps it to the same values (the same scores)
+ *   w_out        device, [B*S][H] bf16, the w of idx_score
+ * Requires D == 128 and rd even with 0 <= rd <= D.
+ */
+idx_status idx_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float w_scale,
+                            const float *cos_sin, int P, int B, int S, int H, int D, int rd,
+                            int start_pos, uint8_t *q_rows, uint16_t *q_roundtrip,
+                            uint16_t *w_out, void *stream);
+
+/*
  * idx_score -- rectified, weighted head sum of fp4 q against the fp4 keys
  * ([IDX, forward: the einsum of q and index_k, relu, times weights, sum over
  * heads, compress_lens mask, level-two candidate mask]).

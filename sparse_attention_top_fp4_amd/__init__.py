@@ -15,7 +15,8 @@ import ctypes
 import os
 
 __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_score_paged",
-           "idx_score_topk_paged", "idx_publish_keys_paged", "idx_clear_key_hist", "idx_topk",
+           "idx_score_topk_paged", "idx_publish_keys_paged", "idx_q_rope_quant",
+           "idx_clear_key_hist", "idx_topk",
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
@@ -72,6 +73,7 @@ def load_library():
                                        ctypes.c_int32, P, i64, P, i64, P]
     L.idx_publish_keys_paged.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                          P, i64, i32, P, i64, i32, P]
+    L.idx_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
     L.idx_timing_arm.argtypes = [i32]
     L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
@@ -79,7 +81,8 @@ def load_library():
                  "idx_topk_candidates",
                  "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read",
-                 "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged"):
+                 "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged",
+                 "idx_q_rope_quant"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -287,6 +290,33 @@ def idx_publish_keys_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_
                                                  rd, eps, start_pos, ratio, _ptr(k_pages), ps,
                                                  npg, _ptr(block_table), bts, Tcap,
                                                  _stream(stream)), "idx_publish_keys_paged")
+
+
+def idx_q_rope_quant(q, w_raw, w_scale, cos_sin, start_pos, S, q_rows, w_out,
+                     q_roundtrip=None, rd=64, stream=None):
+    """Query RoPE + fp4 quantise + weight scaling: q [B*S, H, 128] bf16
+    (before RoPE), w_raw [B*S, H] bf16, cos_sin [P, rd/2, 2] float32, rows
+    r = b*S + s at position start_pos + s; q_rows [B*S, H, 68] uint8,
+    w_out [B*S, H] bf16, q_roundtrip [B*S, H, 128] bf16 or None."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w_raw, "w_raw", _bf16_types(), 2)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    _dev(q_rows, "q_rows", (torch.uint8,), 3)
+    _dev(w_out, "w_out", _bf16_types(), 2)
+    R, H, D = q.shape
+    if R % S or tuple(w_raw.shape) != (R, H) or tuple(w_out.shape) != (R, H):
+        raise ValueError("q/w rows must be B*S")
+    if tuple(q_rows.shape) != (R, H, ROW_BYTES):
+        raise ValueError("q_rows must be [B*S, H, 68]")
+    if q_roundtrip is not None:
+        _dev(q_roundtrip, "q_roundtrip", _bf16_types(), 3)
+        if tuple(q_roundtrip.shape) != (R, H, D):
+            raise ValueError("q_roundtrip must be shaped like q")
+    _check(load_library().idx_q_rope_quant(_ptr(q), _ptr(w_raw), w_scale, _ptr(cos_sin),
+                                           cos_sin.shape[0], R // S, S, H, D, rd, start_pos,
+                                           _ptr(q_rows), _ptr(q_roundtrip), _ptr(w_out),
+                                           _stream(stream)), "idx_q_rope_quant")
 
 
 def idx_clear_key_hist(key_hist, stream=None):

@@ -49,7 +49,96 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t* __restri
   }
 }
 
+// The query step ([IDX, forward: the query heads' RoPE on the last rd dims
+// at positions start_pos + s, fp4_act_quant, weights_proj(x) * softmax_scale
+// * n_heads^-0.5]; [VLLM, fused_indexer_q_rope_quant] fuses the three).
+// One thread per block of 32 values of a head: word i of the block holds the
+// pair (32j + 2i, 32j + 2i + 1), a RoPE pair whenever 32j + 2i >= D - rd
+// (pairs never straddle a block: 32 and D - rd are even).  Rotation as the
+// key publish: (x0*c - x1*s, x0*s + x1*c), every product and sum rounded
+// in fp32 (the library is built with -ffp-contract=off), then bf16; then
+// the quantiser.  The block-0 thread of each head also writes
+// bf16(fp32(w_raw) * w_scale).
+__global__ __launch_bounds__(256) void q_rope_quant_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ w_raw, float w_scale,
+    const float* __restrict__ cos_sin, int rd, int S, int H, int start_pos, int64_t n_blocks,
+    uint8_t* __restrict__ rows, uint16_t* __restrict__ rt, uint16_t* __restrict__ w_out) {
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= n_blocks) return;
+  const int64_t rh = blk >> 2;  // head row r * H + h
+  const int j = (int)(blk & 3);
+  const int64_t r = rh / H;
+  const int pos = start_pos + (int)(r % S);
+  const uint4* src = reinterpret_cast<const uint4*>(q + blk * kBlock);
+  uint32_t xp[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    xp[4 * i + 0] = v.x;
+    xp[4 * i + 1] = v.y;
+    xp[4 * i + 2] = v.z;
+    xp[4 * i + 3] = v.w;
+  }
+  const int base = kHeadDim - rd;
+  if (32 * j + 32 > base) {  // some of the block's pairs are RoPE pairs
+    const float* cs = cos_sin + (int64_t)pos * rd;  // [rd/2][2]
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * j + 2 * i;
+      if (d >= base) {
+        const int pi = (d - base) >> 1;
+        const float x0 = bf16f(xp[i] & 0xffffu), x1 = bf16f(xp[i] >> 16);
+        const float c = cs[2 * pi], sn = cs[2 * pi + 1];
+        const float a = x0 * c, bb = x1 * sn, cc = x0 * sn, dd = x1 * c;
+        xp[i] = f32_to_bf16(a - bb) | (f32_to_bf16(cc + dd) << 16);
+      }
+    }
+  }
+  uint32_t codes[4];
+  const int e = quant_block32(xp, codes);
+  uint8_t* dst = rows + rh * kRowBytes;
+  uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
+  dst[64 + j] = (uint8_t)(e + 127);
+  if (rt) {
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c0 = (codes[i / 4] >> (8 * (i % 4))) & 0xfu;
+      const uint32_t c1 = (codes[i / 4] >> (8 * (i % 4) + 4)) & 0xfu;
+      out[i] = e2m1_dequant_bf16(c0, e) | (e2m1_dequant_bf16(c1, e) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(rt + blk * kBlock);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  }
+  if (j == 0) w_out[rh] = (uint16_t)f32_to_bf16(bf16f(w_raw[rh]) * w_scale);
+}
+
 }  // namespace idx
+
+extern "C" idx_status idx_q_rope_quant(const uint16_t* q, const uint16_t* w_raw, float w_scale,
+                                       const float* cos_sin, int P, int B, int S, int H, int D,
+                                       int rd, int start_pos, uint8_t* q_rows,
+                                       uint16_t* q_roundtrip, uint16_t* w_out, void* stream) {
+  if (B < 0 || S < 0 || H < 0 || D <= 0 || P < 0 || start_pos < 0) return IDX_EINVAL;
+  if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
+  if (rd < 0 || rd > D || (rd & 1)) return IDX_EINVAL;
+  if ((int64_t)B * S * H == 0) return IDX_OK;
+  if (!q || !w_raw || !q_rows || !w_out || (rd > 0 && !cos_sin)) return IDX_EINVAL;
+  if (rd > 0 && (int64_t)start_pos + S - 1 >= P) return IDX_EINVAL;  // position not in the table
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(q_roundtrip) & 15) ||
+      (reinterpret_cast<uintptr_t>(q_rows) & 3))
+    return IDX_EINVAL;
+  const int64_t n_blocks = (int64_t)B * S * H * 4;
+  const int64_t grid = (n_blocks + 255) / 256;
+  if (grid > 0x7fffffffLL) return IDX_EINVAL;
+  hipLaunchKernelGGL(idx::q_rope_quant_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)stream, q, w_raw, w_scale, cos_sin, rd, S, H, start_pos,
+                     n_blocks, q_rows, q_roundtrip, w_out);
+  return idx_host::launch_status();
+}
 
 extern "C" idx_status idx_fp4_quant(const uint16_t* x, int64_t n_rows, uint8_t* rows68,
                                     uint16_t* roundtrip, void* stream) {

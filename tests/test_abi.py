@@ -175,3 +175,20 @@ def test_paged_entry_points_reject_bad_page_maps(lib):
     # nothing to do: no rows
     assert lib.idx_score_paged(d, d, d, 64 * 68, 8, None, 4, 0, 1, 64, 128, T, d, d, T, None,
                                None) == IDX_OK
+
+
+def test_q_rope_quant_rejects_bad_arguments(lib):
+    d = ctypes.c_void_p(0x1000)  # 16-byte aligned, never dereferenced
+
+    def call(q=d, P=64, S=8, D=128, rd=64, sp=0, rt=None):
+        return lib.idx_q_rope_quant(q, d, 0.5, d, P, 2, S, 64, D, rd, sp, d, rt, d, None)
+
+    assert call(D=64) == IDX_EUNSUPPORTED
+    assert call(rd=63) == IDX_EINVAL
+    assert call(rd=130) == IDX_EINVAL
+    assert call(sp=57) == IDX_EINVAL  # position 64 not in the table
+    assert call(sp=-1) == IDX_EINVAL
+    assert call(q=None) == IDX_EINVAL
+    assert call(q=ctypes.c_void_p(0x1008)) == IDX_EINVAL  # q not 16-byte aligned
+    assert call(rt=ctypes.c_void_p(0x1004)) == IDX_EINVAL  # round trip not 16-byte aligned
+    assert call(S=0) == IDX_OK  # nothing to do

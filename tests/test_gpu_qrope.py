@@ -1,0 +1,77 @@
+"""GPU parity of the query step (RoPE on the query heads' last rd dims at
+positions start_pos + s, fp4 quantise, weight scaling) against the oracle:
+quantised rows, their round trip and the scaled weights bit-exact; and the
+round trip, given to the score as q, gives the scores of the rows."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_top_fp4_amd.inputs import YARN, normal_bf16
+
+from gpu_util import bits, dev, fp4_cache, host, say, sync, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def idx():
+    import sparse_attention_top_fp4_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.mark.parametrize("B,S,H,sp,rd", [(4, 1, 64, 131071, 64), (1, 40, 64, 0, 64),
+                                         (2, 7, 32, 1000, 40), (3, 2, 64, 5, 0)])
+def test_q_rope_quant_matches_oracle(idx, B, S, H, sp, rd):
+    t = torch()
+    say("q rope quant", B, S, H, sp, rd)
+    rng = np.random.default_rng(B * 100 + S)
+    R = B * S
+    q = normal_bf16(rng, (R, H, 128))
+    w = normal_bf16(rng, (R, H))
+    scale = np.float32(128 ** -0.5 * H ** -0.5)
+    P = sp + S
+    cs = (oracle.yarn_cos_sin(P, rd, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                              YARN["beta_fast"], YARN["beta_slow"]) if rd
+          else np.zeros((P, 0, 2), np.float32))
+    rows_ref, rt_ref, _, w_ref = oracle.q_rope_quant(q, w, scale, cs, sp, S, rd=rd)
+    rows = t.full((R, H, 68), 7, dtype=t.uint8, device="cuda")
+    rt = t.zeros((R, H, 128), dtype=t.int16, device="cuda")
+    w_out = t.zeros((R, H), dtype=t.int16, device="cuda")
+    csd = dev(cs) if rd else t.zeros((P, 1, 2), dtype=t.float32, device="cuda")
+    idx.idx_q_rope_quant(dev(q), dev(w), float(scale), csd, sp, S, rows, w_out, q_roundtrip=rt,
+                         rd=rd)
+    sync()
+    assert np.array_equal(host(rows), rows_ref)
+    assert np.array_equal(host(rt, np.uint16), rt_ref)
+    assert np.array_equal(host(w_out, np.uint16), w_ref)
+
+
+def test_round_trip_is_a_valid_score_query(idx):
+    """The step's outputs feed idx_score: its scores equal the oracle's score
+    of the rotated, quantised heads with the scaled weights."""
+    t = torch()
+    say("q rope quant -> score")
+    rng = np.random.default_rng(5)
+    B, S, H, T, sp = 2, 3, 64, 700, 2797
+    R = B * S
+    q = normal_bf16(rng, (R, H, 128))
+    w = normal_bf16(rng, (R, H))
+    k = normal_bf16(rng, (B, T, 128))
+    scale = np.float32(128 ** -0.5 * H ** -0.5)
+    cs = oracle.yarn_cos_sin(sp + S, 64, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                             YARN["beta_fast"], YARN["beta_slow"])
+    _, rt_ref, _, w_ref = oracle.q_rope_quant(q, w, scale, cs, sp, S)
+    cl = np.array([(sp + s + 1) // 4 for _ in range(B) for s in range(S)], np.int32)
+    kc_ref, _ = oracle.fp4_quant_rows(k)
+    ref, _ = oracle.score(rt_ref, w_ref, kc_ref, B, S, H, T, cl)
+    rows = t.empty((R, H, 68), dtype=t.uint8, device="cuda")
+    rt = t.empty((R, H, 128), dtype=t.int16, device="cuda")
+    w_out = t.empty((R, H), dtype=t.int16, device="cuda")
+    idx.idx_q_rope_quant(dev(q), dev(w), float(scale), dev(cs), sp, S, rows, w_out, q_roundtrip=rt)
+    sc = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+    idx.idx_score(rt, w_out, fp4_cache(k), B, S, T, dev(cl), sc)
+    sync()
+    g = host(sc)
+    for r in range(R):
+        assert np.array_equal(bits(g[r, :cl[r]]), bits(ref[r, :cl[r]])), r
