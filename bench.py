@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--paged", action="store_true",
                     help="key cache in pages of 64 positions behind a block table (the paged "
                          "entry points; single-level workloads)")
+    ap.add_argument("--q-step", action="store_true",
+                    help="start from the query heads before RoPE: the step first runs the "
+                         "query step (RoPE, fp4 quantise, weight scaling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -171,7 +174,8 @@ def main():
     cache_bytes = wl.B * wl.T * 68
     n_caches = max(1, min(8, math.ceil(3 * LLC_BYTES / cache_bytes))) if cache_bytes > 2 ** 20 else 1
     # the product path: indices only (a fused launch does not write scores)
-    st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False, paged=args.paged)
+    st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False, paged=args.paged,
+                     q_step=args.q_step)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -235,7 +239,8 @@ def main():
                    "index_n_heads": wl.H, "index_head_dim": 128, "index_topk": wl.topk,
                    "candidate_topk_blocks": wl.ctb, "candidate_block_size": wl.cbs,
                    "publish": wl.publish, "key_cache_copies": n_caches,
-                   "key_cache_layout": "paged" if args.paged else "contiguous"},
+                   "key_cache_layout": "paged" if args.paged else "contiguous",
+                   "query_step": bool(args.q_step)},
         "keys_scored_per_s": keys / step_s,
         "score_kernel_ms": score_ms,
         "score_kernel_timed_steps": len(timed),

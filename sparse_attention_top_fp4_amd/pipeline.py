@@ -13,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import (PAGE_ROWS, idx_clear_key_hist, idx_fp4_quant, idx_publish_keys,
-               idx_publish_keys_paged, idx_score, idx_score_paged, idx_score_topk,
+               idx_publish_keys_paged, idx_q_rope_quant, idx_score, idx_score_paged,
+               idx_score_topk,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
                idx_topk, idx_topk_candidates,
                idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
@@ -52,7 +53,7 @@ class IndexerStep:
     FUSED_MAX_T = 8192
 
     def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True,
-                 paged: bool = False):
+                 paged: bool = False, q_step: bool = False):
         torch = _torch()
         self.wl = wl
         R, T = wl.R, wl.T
@@ -106,6 +107,19 @@ class IndexerStep:
             self.sel_ws = self._ws(idx_select_workspace_size(R, T, wl.ctb, wl.cbs))
             self.scores2 = torch.empty((R, T), dtype=torch.float32, device="cuda")
             self.out_l1 = torch.empty((R, self.kout), dtype=torch.int32, device="cuda")
+        # q_step: the step starts from the query heads before RoPE (the
+        # workload's q taken as such) and runs the query step first; the
+        # workload's weights are already scaled, so the weight scale is 1
+        self.q_step = q_step
+        if q_step:
+            H = wl.H
+            self.q_rows = torch.empty((R, H, 68), dtype=torch.uint8, device="cuda")
+            self.q_rt = torch.empty((R, H, 128), dtype=torch.int16, device="cuda")
+            self.w_q = torch.empty((R, H), dtype=torch.int16, device="cuda")
+            P = wl.start_pos + wl.S
+            self.cos_sin_q = to_device(idx_yarn_cos_sin(P, wl.rd, YARN["theta"], YARN["factor"],
+                                                        YARN["orig_len"], YARN["beta_fast"],
+                                                        YARN["beta_slow"]))
         self.publish = bool(wl.publish)
         if self.publish:
             self.latent = to_device(inp["latent"])
@@ -142,23 +156,29 @@ class IndexerStep:
             else:
                 idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                                  wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+        q, w = self.q, self.w
+        if self.q_step:
+            idx_q_rope_quant(self.q, self.w, 1.0, self.cos_sin_q, wl.start_pos, wl.S,
+                             self.q_rows, self.w_q, q_roundtrip=self.q_rt, rd=wl.rd,
+                             stream=stream)
+            q, w = self.q_rt, self.w_q
         if time_slot is not None:
             idx_timing_arm(time_slot)
         if self.fused:
             if self.paged:
-                idx_score_topk_paged(self.q, self.w, kc, self.block_table, wl.B, wl.S, wl.T,
+                idx_score_topk_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T,
                                      self.cl, wl.topk, wl.offset, self.out, scores=self.scores,
                                      stream=stream)
             else:
-                idx_score_topk(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
+                idx_score_topk(q, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
                                self.out, scores=self.scores, stream=stream)
             self.cur = (self.cur + 1) % len(self.caches)
             return
         if self.paged:
-            idx_score_paged(self.q, self.w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
+            idx_score_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
                             self.scores, key_hist=self.key_hist, stream=stream)
         else:
-            idx_score(self.q, self.w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+            idx_score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                       key_hist=self.key_hist, stream=stream)
         if self.two_level:
             idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
@@ -167,7 +187,7 @@ class IndexerStep:
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
             # level two: only the candidate positions hold finite scores; the
             # histogram, reset by the level-one top-k, now counts them
-            idx_score(self.q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
+            idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
                       cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
                       stream=stream)
             idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs, wl.topk,
