@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--q-step", action="store_true",
                     help="start from the query heads before RoPE: the step first runs the "
                          "query step (RoPE, fp4 quantise, weight scaling)")
+    ap.add_argument("--prefill-publish", action="store_true",
+                    help="prefill workloads: the step first publishes the S / ratio keys of "
+                         "the prompt (key publish of many groups)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -174,8 +177,15 @@ def main():
     cache_bytes = wl.B * wl.T * 68
     n_caches = max(1, min(8, math.ceil(3 * LLC_BYTES / cache_bytes))) if cache_bytes > 2 ** 20 else 1
     # the product path: indices only (a fused launch does not write scores)
+    publish = None
+    if args.prefill_publish:
+        if wl.start_pos != 0 or wl.S < wl.ratio:
+            sys.exit("--prefill-publish needs a prefill workload")
+        from sparse_attention_top_fp4_amd.inputs import publish_inputs
+        inp.update(publish_inputs(wl, wl.S // wl.ratio, wl.seed() + 1000))
+        publish = True
     st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False, paged=args.paged,
-                     q_step=args.q_step)
+                     q_step=args.q_step, publish=publish)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -240,7 +250,8 @@ def main():
                    "candidate_topk_blocks": wl.ctb, "candidate_block_size": wl.cbs,
                    "publish": wl.publish, "key_cache_copies": n_caches,
                    "key_cache_layout": "paged" if args.paged else "contiguous",
-                   "query_step": bool(args.q_step)},
+                   "query_step": bool(args.q_step),
+                   "prefill_publish": bool(args.prefill_publish)},
         "keys_scored_per_s": keys / step_s,
         "score_kernel_ms": score_ms,
         "score_kernel_timed_steps": len(timed),

@@ -149,6 +149,16 @@ def generate(wl: Workload, seed=None, rows=None):
     return out
 
 
+def publish_inputs(wl: Workload, groups: int, seed: int):
+    """Key-publish inputs for `groups` groups per sequence, from their own
+    seeded stream: latent uint16 [B][groups][din] N(0,1) bf16, wk uint16
+    [128][din] N(0, 0.02^2) bf16, gamma float32 [128] ones."""
+    rng = np.random.default_rng(seed)
+    return {"latent": normal_bf16(rng, (wl.B, groups, wl.din)),
+            "wk": normal_bf16(rng, (HEAD_DIM, wl.din), std=0.02),
+            "gamma": np.ones(HEAD_DIM, np.float32)}
+
+
 def small_case(seed, B, S, H, T, start_pos=None, ratio=4, tcap=None):
     """A fuzz-sized decode/prefill case: q, k (bf16), w, and compress_lens
     for rows r = b*S + s.  start_pos None gives decode at end_pos = T*ratio

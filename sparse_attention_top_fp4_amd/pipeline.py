@@ -53,7 +53,7 @@ class IndexerStep:
     FUSED_MAX_T = 8192
 
     def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True,
-                 paged: bool = False, q_step: bool = False):
+                 paged: bool = False, q_step: bool = False, publish=None):
         torch = _torch()
         self.wl = wl
         R, T = wl.R, wl.T
@@ -120,7 +120,9 @@ class IndexerStep:
             self.cos_sin_q = to_device(idx_yarn_cos_sin(P, wl.rd, YARN["theta"], YARN["factor"],
                                                         YARN["orig_len"], YARN["beta_fast"],
                                                         YARN["beta_slow"]))
-        self.publish = bool(wl.publish)
+        # publish: None follows the workload; True on a prefill workload
+        # publishes its S / ratio groups (inp must hold their latent)
+        self.publish = bool(wl.publish) if publish is None else bool(publish)
         if self.publish:
             self.latent = to_device(inp["latent"])
             self.wk = to_device(inp["wk"])

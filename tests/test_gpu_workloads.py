@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from sparse_attention_top_fp4_amd.inputs import generate, workload
+from sparse_attention_top_fp4_amd.inputs import YARN, generate, workload
 
 from gpu_util import bits, host, say, sync, torch
 
@@ -181,3 +181,33 @@ def test_long_decode_publish_1m():
         assert inexact == 0
         assert np.array_equal(bits(scores[b]), bits(ref[0])), f"row {b}"
         assert np.array_equal(out[b], oracle.topk(ref, cl[b:b + 1], wl.topk, wl.offset)[0])
+
+
+def test_causal_prefill_with_prompt_publish():
+    """The prefill step publishing its 8192 prompt keys first (key publish of
+    many groups at positions 4j), then scoring them: every cache row against
+    the oracle's publish, and sampled rows' scores and indices."""
+    from sparse_attention_top_fp4_amd.inputs import publish_inputs
+    from sparse_attention_top_fp4_amd.pipeline import IndexerStep
+    wl = workload(2)
+    say("workload", 2, "prompt publish: generating")
+    inp = generate(wl)
+    G = wl.S // wl.ratio
+    inp.update(publish_inputs(wl, G, wl.seed() + 1000))
+    st = IndexerStep(wl, inp, publish=True)
+    say("workload", 2, "prompt publish: step")
+    st.step()
+    sync()
+    cs = oracle.yarn_cos_sin(G * wl.ratio, wl.rd, YARN["theta"], YARN["factor"],
+                             YARN["orig_len"], YARN["beta_fast"], YARN["beta_slow"])
+    kc = np.zeros((1, wl.T, 68), np.uint8)
+    oracle.publish(inp["latent"], inp["wk"], inp["gamma"], cs, 0, wl.ratio, wl.eps, kc)
+    assert np.array_equal(host(st.k_cache), kc)
+    cl = inp["cl"]
+    rows = np.array([8191, 8192, 20000, 32767])
+    ref, _ = oracle.score(inp["q"][rows], inp["w"][rows], kc, 1, len(rows), wl.H, wl.T, cl[rows])
+    sc = host(st.scores[torch().as_tensor(rows, device="cuda")])
+    for i, r in enumerate(rows):
+        n = int(cl[r])
+        assert np.array_equal(bits(sc[i, :n]), bits(ref[i, :n])), f"row {r}"
+    assert np.array_equal(host(st.out)[rows], oracle.topk(ref, cl[rows], wl.topk, wl.offset))
