@@ -19,16 +19,18 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace idx {
 
-// Steps after the linear layer, for the 128 threads o = 0..127 of a
-// workgroup (threads beyond them only take the barriers): k_norm, RoPE at
-// `pos`, quantise, store the row at dst.  y_s: the bf16 outputs as floats.
-__device__ __forceinline__ void publish_finish(const float* y_s, uint32_t* z_s, float* inv_s,
-                                               const float* __restrict__ gamma,
+// Steps after the linear layer, for the 128 threads o = 0..127 of a group
+// (every thread of the workgroup takes the barriers; threads with o >= 128
+// only take them): k_norm, RoPE at `pos`, quantise, store the row at dst
+// (null: not stored).  y_s: the group's bf16 outputs as floats.
+__device__ __forceinline__ void publish_finish(int o, const float* y_s, uint32_t* z_s,
+                                               float* inv_s, const float* __restrict__ gamma,
                                                const float* __restrict__ cos_sin, int rd,
                                                float eps, int pos, uint8_t* __restrict__ dst) {
-  const int o = threadIdx.x;
 
   if (o == 0) {
     float yv[kHeadDim];
@@ -140,12 +142,105 @@ __global__ __launch_bounds__(128) void publish_kernel(
     if (page >= 0 && page < n_pages)
       dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * kRowBytes;
   }
-  publish_finish(y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst);
+  publish_finish(threadIdx.x, y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst);
+}
+
+// Many groups (the prompt's keys): one workgroup of kPubGroups * 128 threads
+// publishes kPubGroups consecutive (sequence, group) slots, thread o of
+// group i computing output o of slot i.  wk is staged once per workgroup in
+// LDS as bf16 pairs with one pad word per row (lane o's reads of row o hit
+// distinct banks), the slots' latents as floats; every output is still the
+// sequential fma chain over the input features, i ascending.  Din <= 512 and
+// even (the LDS holds all of wk).
+constexpr int kPubGroups = 8;
+constexpr int kPubGroupsMaxDin = 512;
+
+__global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
+    const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
+    const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
+    int start_pos, int ratio, int B, int G, uint8_t* __restrict__ kc, int64_t kstride,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t pg_smem[];
+  const int wpr = Din / 2 + 1;                                        // words per wk row
+  uint32_t* wk_s = pg_smem;                                           // [128][wpr]
+  float* lat_s = reinterpret_cast<float*>(pg_smem + kHeadDim * wpr);  // [kPubGroups][Din]
+  __shared__ float y_s[kPubGroups][kHeadDim];
+  __shared__ uint32_t z_s[kPubGroups][kHeadDim];
+  __shared__ float inv_s[kPubGroups];
+  const int tid = threadIdx.x, gi = tid >> 7, o = tid & (kHeadDim - 1);
+  const int64_t nslots = (int64_t)B * G;
+  const int64_t bg0 = (int64_t)blockIdx.x * kPubGroups;
+
+  const uint32_t* wk32 = reinterpret_cast<const uint32_t*>(wk);
+  const int hw = Din / 2;
+  for (int i = tid; i < kHeadDim * hw; i += kPubGroups * kHeadDim) {
+    const int row = i / hw, col = i - row * hw;
+    wk_s[row * wpr + col] = wk32[i];
+  }
+  for (int i = tid; i < kPubGroups * Din; i += kPubGroups * kHeadDim) {
+    const int g = i / Din, k = i - g * Din;
+    const int64_t bg = bg0 + g;
+    lat_s[i] = bg < nslots ? bf16f(latent[bg * Din + k]) : 0.0f;
+  }
+  __syncthreads();
+
+  const uint32_t* wrow = wk_s + o * wpr;
+  const float2* lrow = reinterpret_cast<const float2*>(lat_s + gi * Din);  // Din even
+  float acc = 0.0f;  // y_o of slot gi: sum_i fma(wk[o][i], latent[i]), i ascending
+  // unrolled so the LDS reads of later pairs are in flight during the chain
+#pragma unroll 16
+  for (int k2 = 0; k2 < hw; ++k2) {
+    const uint32_t w2 = wrow[k2];
+    const float2 l2 = lrow[k2];
+    acc = __builtin_fmaf(bf16f(w2 & 0xffffu), l2.x, acc);
+    acc = __builtin_fmaf(bf16f(w2 >> 16), l2.y, acc);
+  }
+  y_s[gi][o] = bf16f(f32_to_bf16(acc));
+  __syncthreads();
+
+  const int64_t bg = bg0 + gi;
+  int pos = 0;
+  uint8_t* dst = nullptr;
+  if (bg < nslots) {
+    const int64_t b = bg / G;
+    const int g = (int)(bg - b * G);
+    pos = start_pos == 0 ? g * ratio : start_pos + 1 - ratio;
+    const int row = start_pos == 0 ? g : start_pos / ratio + g;
+    if (!bt) {
+      dst = kc + (b * kstride + row) * kRowBytes;
+    } else {
+      const int page = bt[b * bt_stride + row / kPubPageRows];
+      if (page >= 0 && page < n_pages)
+        dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * kRowBytes;
+    }
+  }
+  publish_finish(o, y_s[gi], z_s[gi], &inv_s[gi], gamma, cos_sin, rd, eps, pos, dst);
+}
+
+size_t publish_groups_lds(int Din) {
+  return ((size_t)kHeadDim * (Din / 2 + 1) + (size_t)kPubGroups * Din) * 4u;
 }
 
 }  // namespace idx
 
 namespace {
+// The many-groups kernel uses more than 64 KB of dynamic LDS; the limit is a
+// per-device function attribute, raised once on each device the library
+// runs on.
+bool set_groups_lds_limit() {
+  static std::atomic<uint64_t> done_mask{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done_mask.load(std::memory_order_acquire) & bit)) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&idx::publish_groups_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)idx::publish_groups_lds(idx::kPubGroupsMaxDin)) != hipSuccess)
+    return false;
+  if (bit) done_mask.fetch_or(bit, std::memory_order_acq_rel);
+  return true;
+}
+
 // Shared by the contiguous and the paged entry points (bt null: contiguous
 // rows of stride k_batch_stride_rows).
 idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float* gamma,
@@ -175,8 +270,20 @@ idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float*
   if (max_row >= Tcap) return IDX_EINVAL;
   if ((int64_t)B * G > 0x7fffffffLL) return IDX_EINVAL;
   if ((size_t)Din * 2 > 60 * 1024) return IDX_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  // many groups: workgroups of kPubGroups slots sharing wk in LDS
+  if ((int64_t)B * G >= idx::kPubGroups && Din <= idx::kPubGroupsMaxDin && (Din & 1) == 0 &&
+      (reinterpret_cast<uintptr_t>(wk) & 3) == 0) {
+    if (!set_groups_lds_limit()) return IDX_EHIP;
+    const int64_t nwg = ((int64_t)B * G + idx::kPubGroups - 1) / idx::kPubGroups;
+    hipLaunchKernelGGL(idx::publish_groups_kernel, dim3((unsigned)nwg),
+                       dim3(idx::kPubGroups * idx::kHeadDim), idx::publish_groups_lds(Din), st,
+                       latent, wk, gamma, cos_sin, Din, rd, eps, start_pos, ratio, B, G, k_cache,
+                       k_batch_stride_rows, bt, bt_stride, page_stride, n_pages);
+    return idx_host::launch_status();
+  }
   hipLaunchKernelGGL(idx::publish_kernel, dim3((unsigned)(B * G)), dim3(idx::kHeadDim),
-                     (size_t)Din * 2, (hipStream_t)stream, latent, wk, gamma, cos_sin, Din, rd, eps,
+                     (size_t)Din * 2, st, latent, wk, gamma, cos_sin, Din, rd, eps,
                      start_pos, ratio, G, k_cache, k_batch_stride_rows, bt, bt_stride,
                      page_stride, n_pages);
   return idx_host::launch_status();
