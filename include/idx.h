@@ -102,7 +102,8 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  *   q_rows       device, [B*S][H][68] quantised heads, 4-byte aligned
  *   q_roundtrip  device, [B*S][H][D] bf16 dequantised heads, 16-byte
  *                aligned, or NULL.  It is a valid q for idx_score: the
- *                quantiser maps it to the same values (the same scores)
+ *                quantiser maps it to the same values (the same scores);
+ *                idx_score_q4 takes q_rows directly
  *   w_out        device, [B*S][H] bf16, the w of idx_score
  * Requires D == 128 and rd even with 0 <= rd <= D.
  */
@@ -206,6 +207,25 @@ idx_status idx_score_topk_paged(const uint16_t *q, const uint16_t *w, const uint
                                 const int32_t *compress_lens, int index_topk, int32_t offset,
                                 int32_t *out, int64_t ld_out, float *scores, int64_t ld,
                                 void *stream);
+
+/*
+ * idx_score_q4, idx_score_topk_q4 -- idx_score and idx_score_topk with the
+ * query heads given already quantised ([VLLM, fused_indexer_q_rope_quant]
+ * hands its fp4 output to the indexer op): q_rows [B*S][H][68], the rows of
+ * idx_fp4_quant / idx_q_rope_quant, 4-byte aligned, in place of q.  Every
+ * other argument and every result as for the call without _q4; the scores
+ * equal those of idx_score given the rows' bf16 round trip.
+ */
+idx_status idx_score_q4(const uint8_t *q_rows, const uint16_t *w, const uint8_t *k_cache,
+                        int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                        const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
+                        int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
+                        void *stream);
+idx_status idx_score_topk_q4(const uint8_t *q_rows, const uint16_t *w, const uint8_t *k_cache,
+                             int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                             const int32_t *compress_lens, int index_topk, int32_t offset,
+                             int32_t *out, int64_t ld_out, float *scores, int64_t ld,
+                             void *stream);
 
 /*
  * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on

@@ -16,6 +16,7 @@ import os
 
 __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_score_paged",
            "idx_score_topk_paged", "idx_publish_keys_paged", "idx_q_rope_quant",
+           "idx_score_q4", "idx_score_topk_q4",
            "idx_clear_key_hist", "idx_topk",
            "idx_topk_candidates",
            "idx_topk_workspace_size",
@@ -74,6 +75,8 @@ def load_library():
     L.idx_publish_keys_paged.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                          P, i64, i32, P, i64, i32, P]
     L.idx_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
+    L.idx_score_q4.argtypes = L.idx_score.argtypes
+    L.idx_score_topk_q4.argtypes = L.idx_score_topk.argtypes
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
     L.idx_timing_arm.argtypes = [i32]
     L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
@@ -82,7 +85,7 @@ def load_library():
                  "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read",
                  "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged",
-                 "idx_q_rope_quant"):
+                 "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -176,6 +179,65 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
                                     _ptr(key_hist), _stream(stream)), "idx_score")
+
+
+def idx_score_q4(q_rows, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
+                 cand_block_size=0, key_hist=None, stream=None):
+    """idx_score with the query heads already quantised: q_rows [B*S, H, 68]
+    uint8 (from idx_q_rope_quant or idx_fp4_quant)."""
+    torch = _torch()
+    _dev(q_rows, "q_rows", (torch.uint8,), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    R, H, rb = q_rows.shape
+    if rb != ROW_BYTES or R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q_rows must be [B*S, H, 68] and w/compress_lens rows B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES or scores.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 68] and scores [B*S, ld]")
+    n_cand = 0
+    if cand_blocks is not None:
+        _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+        if cand_blocks.shape[0] != R:
+            raise ValueError("cand_blocks must have B*S rows")
+        n_cand = cand_blocks.shape[1]
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    _check(load_library().idx_score_q4(_ptr(q_rows), _ptr(w), _ptr(k_cache), k_cache.shape[1], B,
+                                       S, H, 128, T, _ptr(compress_lens), _ptr(cand_blocks),
+                                       n_cand, cand_block_size, _ptr(scores), scores.shape[1],
+                                       _ptr(key_hist), _stream(stream)), "idx_score_q4")
+
+
+def idx_score_topk_q4(q_rows, w, k_cache, B, S, T, compress_lens, index_topk, offset, out,
+                      scores=None, stream=None):
+    """idx_score_topk with the query heads already quantised: q_rows
+    [B*S, H, 68] uint8."""
+    torch = _torch()
+    _dev(q_rows, "q_rows", (torch.uint8,), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    R, H, rb = q_rows.shape
+    if rb != ROW_BYTES or R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q_rows must be [B*S, H, 68] and w/compress_lens rows B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES or out.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 68] and out [B*S, ld_out]")
+    ld = 0
+    if scores is not None:
+        _dev(scores, "scores", (torch.float32,), 2)
+        if scores.shape[0] != R:
+            raise ValueError("scores must be [B*S, ld]")
+        ld = scores.shape[1]
+    _check(load_library().idx_score_topk_q4(_ptr(q_rows), _ptr(w), _ptr(k_cache),
+                                            k_cache.shape[1], B, S, H, 128, T,
+                                            _ptr(compress_lens), index_topk, offset, _ptr(out),
+                                            out.shape[1], _ptr(scores), ld, _stream(stream)),
+           "idx_score_topk_q4")
 
 
 def idx_score_topk(q, w, k_cache, B, S, T, compress_lens, index_topk, offset, out, scores=None,

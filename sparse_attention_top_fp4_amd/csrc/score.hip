@@ -260,8 +260,8 @@ __device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint
 
 template <int HT, bool CAND, bool TOPK>
 __global__ __launch_bounds__(256) void score_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
-    const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ q4,
+    const uint16_t* __restrict__ w, const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
     FusedTopk tk, PageMap pg) {
@@ -333,8 +333,13 @@ __global__ __launch_bounds__(256) void score_kernel(
   if (hist_s)
     for (int i = tid; i < 2048; i += 256) hist_lds[i] = 0;
 
-  // --- quantise the query row: thread (h, g) handles block g of head h
-  if (tid < 4 * H) {
+  // --- the query row in LDS: given quantised (q4: H rows of 68 bytes, the
+  // LDS layout itself), or quantised here, thread (h, g) handling block g
+  // of head h
+  if (q4) {  // uniform
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q4 + (int64_t)r * H * kRowBytes);
+    for (int i = tid; i < H * 17; i += 256) qs[i] = src[i];
+  } else if (tid < 4 * H) {
     const int h = tid >> 2, g = tid & 3;
     const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kHeadDim + 32 * g);
     uint32_t xp[16];
@@ -518,7 +523,8 @@ extern "C" idx_status idx_clear_key_hist(uint32_t* key_hist, int R, void* stream
 namespace {
 // Shared by the contiguous and the paged entry points: the key source is
 // (k_cache, k_batch_stride_rows) when pg.bt is null, else the page pool.
-idx_status score_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
+                      const uint8_t* k_cache,
                       int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                       const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
                       int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
@@ -527,7 +533,8 @@ idx_status score_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cac
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
-  if (!q || !w || !k_cache || !compress_lens || !scores) return IDX_EINVAL;
+  if ((!q && !q4) || !w || !k_cache || !compress_lens || !scores) return IDX_EINVAL;
+  if (q4 && (reinterpret_cast<uintptr_t>(q4) & 3)) return IDX_EINVAL;
   if (ld < T || (!pg.bt && k_batch_stride_rows < T)) return IDX_EINVAL;
   if (cand_blocks && (n_cand <= 0 || cand_block_size <= 0)) return IDX_EINVAL;
   if (cand_blocks && n_cand > idx::kMaxCand) return IDX_EUNSUPPORTED;
@@ -552,13 +559,14 @@ idx_status score_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cac
                                      : idx::score_kernel<2, false, false>)
                       : (cand_blocks ? idx::score_kernel<1, true, false>
                                      : idx::score_kernel<1, false, false>);
-  return launch_score(kern, grid, (size_t)kpw * sizeof(float), st, q, w, k_cache,
+  return launch_score(kern, grid, (size_t)kpw * sizeof(float), st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
                       pg);
 }
 
-idx_status score_topk_impl(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
+                           const uint8_t* k_cache,
                            int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                            const int32_t* compress_lens, int index_topk, int32_t offset,
                            int32_t* out, int64_t ld_out, float* scores, int64_t ld,
@@ -568,7 +576,8 @@ idx_status score_topk_impl(const uint16_t* q, const uint16_t* w, const uint8_t* 
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
   if (T > idx::kFusedMaxT) return IDX_EUNSUPPORTED;
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
-  if (!q || !w || !k_cache || !compress_lens || !out) return IDX_EINVAL;
+  if ((!q && !q4) || !w || !k_cache || !compress_lens || !out) return IDX_EINVAL;
+  if (q4 && (reinterpret_cast<uintptr_t>(q4) & 3)) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
   if ((!pg.bt && k_batch_stride_rows < T) || ld_out < kout || (scores && ld < T))
     return IDX_EINVAL;
@@ -581,7 +590,7 @@ idx_status score_topk_impl(const uint16_t* q, const uint16_t* w, const uint8_t* 
   const int kpw = (T + 255) / 256 * 256;
   const size_t lds = (size_t)idx::kFusedMaxT * sizeof(float);
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
-  return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, w, k_cache, k_batch_stride_rows, S,
+  return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, q4, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
                       (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg);
 }
@@ -602,7 +611,8 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                                 const int32_t* compress_lens, const int32_t* cand_blocks,
                                 int n_cand, int cand_block_size, float* scores, int64_t ld,
                                 uint32_t* key_hist, void* stream) {
-  return score_impl(q, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens, cand_blocks,
+  return score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                    cand_blocks,
                     n_cand, cand_block_size, scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
 }
@@ -612,8 +622,8 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
                                      int T, const int32_t* compress_lens, int index_topk,
                                      int32_t offset, int32_t* out, int64_t ld_out, float* scores,
                                      int64_t ld, void* stream) {
-  return score_topk_impl(q, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
-                         index_topk, offset, out, ld_out, scores, ld,
+  return score_topk_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                         compress_lens, index_topk, offset, out, ld_out, scores, ld,
                          idx::PageMap{nullptr, 0, 0, 0}, stream);
 }
 
@@ -628,8 +638,8 @@ extern "C" idx_status idx_score_paged(const uint16_t* q, const uint16_t* w, cons
     const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, T, pg);
     if (e != IDX_OK) return e;
   }
-  return score_impl(q, w, k_pages, 0, B, S, H, D, T, compress_lens, nullptr, 0, 0, scores, ld,
-                    key_hist, pg, stream);
+  return score_impl(q, nullptr, w, k_pages, 0, B, S, H, D, T, compress_lens, nullptr, 0, 0,
+                    scores, ld, key_hist, pg, stream);
 }
 
 extern "C" idx_status idx_score_topk_paged(const uint16_t* q, const uint16_t* w,
@@ -644,8 +654,29 @@ extern "C" idx_status idx_score_topk_paged(const uint16_t* q, const uint16_t* w,
     const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, T, pg);
     if (e != IDX_OK) return e;
   }
-  return score_topk_impl(q, w, k_pages, 0, B, S, H, D, T, compress_lens, index_topk, offset, out,
-                         ld_out, scores, ld, pg, stream);
+  return score_topk_impl(q, nullptr, w, k_pages, 0, B, S, H, D, T, compress_lens, index_topk,
+                         offset, out, ld_out, scores, ld, pg, stream);
+}
+
+extern "C" idx_status idx_score_q4(const uint8_t* q_rows, const uint16_t* w,
+                                   const uint8_t* k_cache, int64_t k_batch_stride_rows, int B,
+                                   int S, int H, int D, int T, const int32_t* compress_lens,
+                                   const int32_t* cand_blocks, int n_cand, int cand_block_size,
+                                   float* scores, int64_t ld, uint32_t* key_hist, void* stream) {
+  return score_impl(nullptr, q_rows, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                    compress_lens, cand_blocks, n_cand, cand_block_size, scores, ld, key_hist,
+                    idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_score_topk_q4(const uint8_t* q_rows, const uint16_t* w,
+                                        const uint8_t* k_cache, int64_t k_batch_stride_rows,
+                                        int B, int S, int H, int D, int T,
+                                        const int32_t* compress_lens, int index_topk,
+                                        int32_t offset, int32_t* out, int64_t ld_out,
+                                        float* scores, int64_t ld, void* stream) {
+  return score_topk_impl(nullptr, q_rows, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                         compress_lens, index_topk, offset, out, ld_out, scores, ld,
+                         idx::PageMap{nullptr, 0, 0, 0}, stream);
 }
 
 extern "C" idx_status idx_timing_arm(int slot) {

@@ -14,7 +14,7 @@ import numpy as np
 
 from . import (PAGE_ROWS, idx_clear_key_hist, idx_fp4_quant, idx_publish_keys,
                idx_publish_keys_paged, idx_q_rope_quant, idx_score, idx_score_paged,
-               idx_score_topk,
+               idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
                idx_topk, idx_topk_candidates,
                idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
@@ -159,11 +159,19 @@ class IndexerStep:
                 idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
                                  wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
         q, w = self.q, self.w
+        q4 = None  # the quantised heads, when the score takes them directly
         if self.q_step:
+            # the score takes the rows directly; the paged and level-two
+            # scores take the bf16 round trip
+            direct = not self.paged and not self.two_level
             idx_q_rope_quant(self.q, self.w, 1.0, self.cos_sin_q, wl.start_pos, wl.S,
-                             self.q_rows, self.w_q, q_roundtrip=self.q_rt, rd=wl.rd,
-                             stream=stream)
-            q, w = self.q_rt, self.w_q
+                             self.q_rows, self.w_q, q_roundtrip=None if direct else self.q_rt,
+                             rd=wl.rd, stream=stream)
+            w = self.w_q
+            if direct:
+                q4 = self.q_rows
+            else:
+                q = self.q_rt
         if time_slot is not None:
             idx_timing_arm(time_slot)
         if self.fused:
@@ -171,6 +179,9 @@ class IndexerStep:
                 idx_score_topk_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T,
                                      self.cl, wl.topk, wl.offset, self.out, scores=self.scores,
                                      stream=stream)
+            elif q4 is not None:
+                idx_score_topk_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
+                                  self.out, scores=self.scores, stream=stream)
             else:
                 idx_score_topk(q, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
                                self.out, scores=self.scores, stream=stream)
@@ -179,6 +190,9 @@ class IndexerStep:
         if self.paged:
             idx_score_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
                             self.scores, key_hist=self.key_hist, stream=stream)
+        elif q4 is not None:
+            idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                         key_hist=self.key_hist, stream=stream)
         else:
             idx_score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                       key_hist=self.key_hist, stream=stream)

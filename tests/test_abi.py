@@ -192,3 +192,14 @@ def test_q_rope_quant_rejects_bad_arguments(lib):
     assert call(q=ctypes.c_void_p(0x1008)) == IDX_EINVAL  # q not 16-byte aligned
     assert call(rt=ctypes.c_void_p(0x1004)) == IDX_EINVAL  # round trip not 16-byte aligned
     assert call(S=0) == IDX_OK  # nothing to do
+
+
+def test_score_q4_rejects_unaligned_rows(lib):
+    d = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.idx_score_q4(odd, d, d, 8, 1, 1, 64, 128, 8, d, None, 0, 0, d, 8, None,
+                            None) == IDX_EINVAL
+    assert lib.idx_score_topk_q4(odd, d, d, 8, 1, 1, 64, 128, 8, d, 4, 0, d, 4, None, 0,
+                                 None) == IDX_EINVAL
+    assert lib.idx_score_q4(None, d, d, 8, 1, 1, 64, 128, 8, d, None, 0, 0, d, 8, None,
+                            None) == IDX_EINVAL

@@ -75,3 +75,57 @@ def test_round_trip_is_a_valid_score_query(idx):
     g = host(sc)
     for r in range(R):
         assert np.array_equal(bits(g[r, :cl[r]]), bits(ref[r, :cl[r]])), r
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_score_takes_the_quantised_rows(idx, fused):
+    """idx_score_q4 / idx_score_topk_q4 on the query step's rows give the
+    scores and indices of the oracle (and of idx_score on the round trip)."""
+    t = torch()
+    say("score from quantised rows", fused)
+    rng = np.random.default_rng(8)
+    B, S, H, T, sp = 2, 6, 64, 3000, 10000
+    R = B * S
+    q = normal_bf16(rng, (R, H, 128))
+    w = normal_bf16(rng, (R, H))
+    k = normal_bf16(rng, (B, T, 128))
+    cs = oracle.yarn_cos_sin(sp + S, 64, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                             YARN["beta_fast"], YARN["beta_slow"])
+    _, rt_ref, _, w_ref = oracle.q_rope_quant(q, w, 1.0, cs, sp, S)
+    cl = np.array([(sp + s + 1) // 4 for _ in range(B) for s in range(S)], np.int32)
+    cl = np.minimum(cl, T)
+    kc_ref, _ = oracle.fp4_quant_rows(k)
+    ref, _ = oracle.score(rt_ref, w_ref, kc_ref, B, S, H, T, cl)
+    rows = t.empty((R, H, 68), dtype=t.uint8, device="cuda")
+    rt = t.empty((R, H, 128), dtype=t.int16, device="cuda")
+    w_out = t.empty((R, H), dtype=t.int16, device="cuda")
+    idx.idx_q_rope_quant(dev(q), dev(w), 1.0, dev(cs), sp, S, rows, w_out, q_roundtrip=rt)
+    kc = fp4_cache(k)
+    sc = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+    sc2 = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+    if fused:
+        k_top = 700
+        out = t.full((R, k_top), -7, dtype=t.int32, device="cuda")
+        idx.idx_score_topk_q4(rows, w_out, kc, B, S, T, dev(cl), k_top, 2, out, scores=sc)
+        idx.idx_score_topk(rt, w_out, kc, B, S, T, dev(cl), k_top, 2,
+                           t.empty_like(out), scores=sc2)
+        sync()
+        assert np.array_equal(host(out), oracle.topk(ref, cl, k_top, 2))
+    else:
+        hist = t.zeros((R, 2048), dtype=t.int32, device="cuda")
+        hist2 = t.zeros((R, 2048), dtype=t.int32, device="cuda")
+        cand = np.array([[1, 5, 9, 30]] * R, np.int32)  # and the candidate mode
+        idx.idx_score_q4(rows, w_out, kc, B, S, T, dev(cl), sc, key_hist=hist)
+        idx.idx_score(rt, w_out, kc, B, S, T, dev(cl), sc2, key_hist=hist2)
+        sc3 = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+        idx.idx_score_q4(rows, w_out, kc, B, S, T, dev(cl), sc3, cand_blocks=dev(cand),
+                         cand_block_size=64)
+        sync()
+        assert np.array_equal(host(hist), host(hist2))
+        ref_c, _ = oracle.score(rt_ref, w_ref, kc_ref, B, S, H, T, cl, cand=cand, cbs=64)
+        assert np.array_equal(bits(host(sc3)), bits(ref_c))
+    g, g2 = host(sc), host(sc2)
+    for r in range(R):
+        n = int(cl[r])
+        assert np.array_equal(bits(g[r, :n]), bits(ref[r, :n])), r
+        assert np.array_equal(bits(g[r, :n]), bits(g2[r, :n])), r
