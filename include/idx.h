@@ -98,7 +98,8 @@ idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uin
  * quantiser of idx_fp4_quant.  Weights: bf16(fp32(w_raw) * w_scale).
  *   q            device, [B*S][H][D] bf16 before RoPE, 16-byte aligned
  *   w_raw        device, [B*S][H] bf16 (weights_proj output)
- *   cos_sin      device, [P][rd/2][2] fp32; start_pos + S - 1 < P
+ *   cos_sin      device, [P][rd/2][2] fp32, 8-byte aligned;
+ *                start_pos + S - 1 < P
  *   q_rows       device, [B*S][H][68] quantised heads, 4-byte aligned
  *   q_roundtrip  device, [B*S][H][D] bf16 dequantised heads, 16-byte
  *                aligned, or NULL.  It is a valid q for idx_score: the

@@ -58,18 +58,20 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t* __restri
 // key publish: (x0*c - x1*s, x0*s + x1*c), every product and sum rounded
 // in fp32 (the library is built with -ffp-contract=off), then bf16; then
 // the quantiser.  The block-0 thread of each head also writes
-// bf16(fp32(w_raw) * w_scale).
+// bf16(fp32(w_raw) * w_scale).  A workgroup's 64 rows leave through LDS in
+// one coalesced run of words.
 __global__ __launch_bounds__(256) void q_rope_quant_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ w_raw, float w_scale,
     const float* __restrict__ cos_sin, int rd, int S, int H, int start_pos, int64_t n_blocks,
     uint8_t* __restrict__ rows, uint16_t* __restrict__ rt, uint16_t* __restrict__ w_out) {
   const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blk >= n_blocks) return;
-  const int64_t rh = blk >> 2;  // head row r * H + h
+  const bool live = blk < n_blocks;  // every thread takes the barrier below
+  const int64_t rh = live ? blk >> 2 : 0;  // head row r * H + h
   const int j = (int)(blk & 3);
   const int64_t r = rh / H;
   const int pos = start_pos + (int)(r % S);
-  const uint4* src = reinterpret_cast<const uint4*>(q + blk * kBlock);
+  // a thread past the last block reads block 0 and stores nothing
+  const uint4* src = reinterpret_cast<const uint4*>(q + (live ? blk : 0) * kBlock);
   uint32_t xp[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -81,14 +83,15 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(
   }
   const int base = kHeadDim - rd;
   if (32 * j + 32 > base) {  // some of the block's pairs are RoPE pairs
-    const float* cs = cos_sin + (int64_t)pos * rd;  // [rd/2][2]
+    const float2* cs = reinterpret_cast<const float2*>(cos_sin + (int64_t)pos * rd);  // [rd/2]
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int d = 32 * j + 2 * i;
       if (d >= base) {
         const int pi = (d - base) >> 1;
         const float x0 = bf16f(xp[i] & 0xffffu), x1 = bf16f(xp[i] >> 16);
-        const float c = cs[2 * pi], sn = cs[2 * pi + 1];
+        const float2 csp = cs[pi];  // (cos, sin), one 8-byte load
+        const float c = csp.x, sn = csp.y;
         const float a = x0 * c, bb = x1 * sn, cc = x0 * sn, dd = x1 * c;
         xp[i] = f32_to_bf16(a - bb) | (f32_to_bf16(cc + dd) << 16);
       }
@@ -96,12 +99,14 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(
   }
   uint32_t codes[4];
   const int e = quant_block32(xp, codes);
-  uint8_t* dst = rows + rh * kRowBytes;
-  uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * j);
+  // the workgroup's 64 rows are contiguous: staged in LDS, then written as
+  // one coalesced run of words (no byte stores to device memory)
+  __shared__ uint32_t stage[64 * 17];
+  const int lrow = threadIdx.x >> 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
-  dst[64 + j] = (uint8_t)(e + 127);
-  if (rt) {
+  for (int i = 0; i < 4; ++i) stage[lrow * 17 + 4 * j + i] = codes[i];
+  reinterpret_cast<uint8_t*>(stage)[lrow * kRowBytes + 64 + j] = (uint8_t)(e + 127);
+  if (rt && live) {
     uint32_t out[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -113,7 +118,13 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) d[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
   }
-  if (j == 0) w_out[rh] = (uint16_t)f32_to_bf16(bf16f(w_raw[rh]) * w_scale);
+  if (j == 0 && live) w_out[rh] = (uint16_t)f32_to_bf16(bf16f(w_raw[rh]) * w_scale);
+  __syncthreads();
+  const int64_t rh0 = (int64_t)blockIdx.x * 64;  // first row of the workgroup
+  const int64_t nrows = n_blocks >> 2;
+  const int nw = (int)((nrows - rh0 < 64 ? nrows - rh0 : 64) * 17);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(rows + rh0 * kRowBytes);
+  for (int i = threadIdx.x; i < nw; i += 256) dst[i] = stage[i];
 }
 
 }  // namespace idx
@@ -129,7 +140,7 @@ extern "C" idx_status idx_q_rope_quant(const uint16_t* q, const uint16_t* w_raw,
   if (!q || !w_raw || !q_rows || !w_out || (rd > 0 && !cos_sin)) return IDX_EINVAL;
   if (rd > 0 && (int64_t)start_pos + S - 1 >= P) return IDX_EINVAL;  // position not in the table
   if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(q_roundtrip) & 15) ||
-      (reinterpret_cast<uintptr_t>(q_rows) & 3))
+      (reinterpret_cast<uintptr_t>(q_rows) & 3) || (reinterpret_cast<uintptr_t>(cos_sin) & 7))
     return IDX_EINVAL;
   const int64_t n_blocks = (int64_t)B * S * H * 4;
   const int64_t grid = (n_blocks + 255) / 256;

@@ -21,7 +21,8 @@ def idx():
 
 
 @pytest.mark.parametrize("B,S,H,sp,rd", [(4, 1, 64, 131071, 64), (1, 40, 64, 0, 64),
-                                         (2, 7, 32, 1000, 40), (3, 2, 64, 5, 0)])
+                                         (2, 7, 32, 1000, 40), (3, 2, 64, 5, 0),
+                                         (1, 3, 32, 7, 64)])  # 96 heads: a partial workgroup
 def test_q_rope_quant_matches_oracle(idx, B, S, H, sp, rd):
     t = torch()
     say("q rope quant", B, S, H, sp, rd)
