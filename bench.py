@@ -53,7 +53,7 @@ def parse():
                     help="minimum CPU work for the oracle baseline sample")
     ap.add_argument("--paged", action="store_true",
                     help="key cache in pages of 64 positions behind a block table (the paged "
-                         "entry points; single-level workloads)")
+                         "entry points)")
     ap.add_argument("--q-step", action="store_true",
                     help="start from the query heads before RoPE: the step first runs the "
                          "query step (RoPE, fp4 quantise, weight scaling)")

@@ -191,15 +191,19 @@ idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k
  *                (score) or the published rows (publish)
  *   bt_stride    >= ceil(T / 64) (score) or ceil(Tcap / 64) (publish)
  * Everything else, and every result, is as for the contiguous call of the
- * same name; the results are bit-identical to it on the same rows.
+ * same name; the results are bit-identical to it on the same rows.  In
+ * candidate mode an invalid id likewise scores as zero rows.
  */
 
-/* idx_score without candidate blocks, on a paged key cache. */
+/* idx_score on a paged key cache.  With cand_blocks (level two) the row's
+ * page ids are held on chip, which bounds T to 131072 (IDX_EUNSUPPORTED
+ * beyond). */
 idx_status idx_score_paged(const uint16_t *q, const uint16_t *w, const uint8_t *k_pages,
                            int64_t page_stride, int n_pages, const int32_t *block_table,
                            int64_t bt_stride, int B, int S, int H, int D, int T,
-                           const int32_t *compress_lens, float *scores, int64_t ld,
-                           uint32_t *key_hist, void *stream);
+                           const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
+                           int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
+                           void *stream);
 
 /* idx_score_topk on a paged key cache. */
 idx_status idx_score_topk_paged(const uint16_t *q, const uint16_t *w, const uint8_t *k_pages,

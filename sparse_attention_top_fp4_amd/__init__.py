@@ -68,8 +68,8 @@ def load_library():
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
     L.idx_publish_keys.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i64,
                                    i32, P]
-    L.idx_score_paged.argtypes = [P, P, P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, P, i64,
-                                  P, P]
+    L.idx_score_paged.argtypes = [P, P, P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, P, i32,
+                                  i32, P, i64, P, P]
     L.idx_score_topk_paged.argtypes = [P, P, P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, i32,
                                        ctypes.c_int32, P, i64, P, i64, P]
     L.idx_publish_keys_paged.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32,
@@ -282,10 +282,10 @@ def _pages(k_pages, block_table, B):
     return k_pages.stride(0), k_pages.shape[0], block_table.shape[1]
 
 
-def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, key_hist=None,
-                    stream=None):
-    """idx_score (no candidates) on a paged key cache: row t of sequence b in
-    slot t % 64 of page block_table[b, t // 64] of k_pages."""
+def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, cand_blocks=None,
+                    cand_block_size=0, key_hist=None, stream=None):
+    """idx_score on a paged key cache: row t of sequence b in slot t % 64 of
+    page block_table[b, t // 64] of k_pages."""
     torch = _torch()
     _dev(q, "q", _bf16_types(), 3)
     _dev(w, "w", _bf16_types(), 2)
@@ -300,10 +300,17 @@ def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, 
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if tuple(key_hist.shape) != (R, 2048):
             raise ValueError("key_hist must be [B*S, 2048]")
+    n_cand = 0
+    if cand_blocks is not None:
+        _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+        if cand_blocks.shape[0] != R:
+            raise ValueError("cand_blocks must have B*S rows")
+        n_cand = cand_blocks.shape[1]
     ps, npg, bts = _pages(k_pages, block_table, B)
     _check(load_library().idx_score_paged(_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
                                           _ptr(block_table), bts, B, S, H, D, T,
-                                          _ptr(compress_lens), _ptr(scores), scores.shape[1],
+                                          _ptr(compress_lens), _ptr(cand_blocks), n_cand,
+                                          cand_block_size, _ptr(scores), scores.shape[1],
                                           _ptr(key_hist), _stream(stream)), "idx_score_paged")
 
 

@@ -112,11 +112,13 @@ struct PageMap {
 };
 
 // Paged tiles take their page id from `page` (uniform; see the caller).
+// Candidate mode on pages: bt_lds holds the row's page ids (in LDS).
 template <bool CAND>
 __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
                                              const PosMap<CAND>& pm, int v0, int lane,
                                              bool paged = false, int page = -1,
-                                             int64_t page_stride = 0, int n_pages = 0) {
+                                             int64_t page_stride = 0, int n_pages = 0,
+                                             const int32_t* bt_lds = nullptr) {
   KeyTile kt;
   const int half = lane >> 5;
   if constexpr (!CAND) {
@@ -146,9 +148,20 @@ __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
   for (int t = 0; t < 2; ++t) {
     const int p = pm.pos(v0 + 32 * t + (lane & 31));
     const uint8_t* row = kseq + (int64_t)(p < 0 ? 0 : p) * kRowBytes;
+    bool zero = false;
+    if (bt_lds) {  // paged: slot p % 64 of page bt[p / 64]; an invalid id gives a zero row
+      const int pgid = p < 0 ? 0 : bt_lds[p >> 6];
+      zero = p >= 0 && (pgid < 0 || pgid >= n_pages);
+      row = kseq + (zero || p < 0 ? 0 : (int64_t)pgid * page_stride + (int64_t)(p & 63) * kRowBytes);
+    }
     kt.c[t][0] = ld16(row + 16 * half);
     kt.c[t][1] = ld16(row + 32 + 16 * half);
     kt.sc[t] = *reinterpret_cast<const uint32_t*>(row + 64);
+    if (zero) {
+      kt.c[t][0] = u32x4{0u, 0u, 0u, 0u};
+      kt.c[t][1] = u32x4{0u, 0u, 0u, 0u};
+      kt.sc[t] = 0u;
+    }
   }
   return kt;
 }
@@ -296,6 +309,14 @@ __global__ __launch_bounds__(256) void score_kernel(
   pm.vlim = vend;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // paged candidate mode: the row's page ids for positions < limit, in the
+  // dynamic LDS after the chunk's scores
+  int32_t* bt_lds = nullptr;
+  if (CAND && pg.bt) {
+    bt_lds = reinterpret_cast<int32_t*>(sbuf + keys_per_wg);
+    const int np = (limit + kPageRows - 1) / kPageRows;
+    for (int i = tid; i < np; i += 256) bt_lds[i] = pg.bt[(int64_t)b * pg.bt_stride + i];
+  }
   if (CAND) {
     for (int i = tid; i < n_cand; i += 256) cand_s[i] = cand[(int64_t)r * n_cand + i];
     __syncthreads();
@@ -306,7 +327,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   // sets: while one tile computes, the next kTileSets - 1 tiles of this wave
   // are in flight
   // contiguous: the sequence's rows; paged: the page pool (plain mode only)
-  const bool paged = !CAND && pg.bt;
+  const bool paged = !CAND && pg.bt;  // plain mode: pages by readlane (below)
   const uint8_t* kseq = paged ? kc : kc + (int64_t)b * kstride * kRowBytes;
   const int ntiles = (vend - vbeg + 63) >> 6;
   int j = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile bases stay scalar
@@ -327,7 +348,7 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
   for (int i = 0; i < kTileSets - 1; ++i)
     buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, paged, tile_page(i),
-                       pg.page_stride, pg.n_pages);
+                       pg.page_stride, pg.n_pages, bt_lds);
 
   uint32_t* hist_s = (key_hist || TOPK) ? hist_lds : nullptr;
   if (hist_s)
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int u = 0; u < kTileSets; ++u) {
       buf[(u + kTileSets - 1) % kTileSets] =
           load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane, paged,
-                    tile_page(it + kTileSets - 1), pg.page_stride, pg.n_pages);
+                    tile_page(it + kTileSets - 1), pg.page_stride, pg.n_pages, bt_lds);
       score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
       ++it;
@@ -484,6 +505,8 @@ idx_status launch_score(F kern, dim3 grid, size_t lds, hipStream_t st, Args... a
 }
 
 constexpr int kMaxKeysPerWg = 8192;  // bounds the LDS score buffer (32 KB)
+// paged candidate mode keeps the row's page ids in LDS too (2048 ids, 8 KB)
+constexpr int kMaxPagedCandT = 131072;
 int g_keys_per_wg_override = -1;
 
 int pick_keys_per_wg(int64_t R, int vtotal) {
@@ -549,6 +572,11 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   const int kpw = pick_keys_per_wg(R, (int)vtotal);
   const int64_t nchunks = (vtotal + kpw - 1) / kpw;
   if (nchunks > 65535) return IDX_EINVAL;
+  size_t lds = (size_t)kpw * sizeof(float);
+  if (cand_blocks && pg.bt) {  // the row's page ids follow the scores in LDS
+    if (T > kMaxPagedCandT) return IDX_EUNSUPPORTED;
+    lds += (size_t)((T + idx::kPageRows - 1) / idx::kPageRows) * sizeof(int32_t);
+  }
   if (cand_blocks) {
     if (R > 65535) return IDX_EUNSUPPORTED;
     hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048), (unsigned)R),
@@ -559,7 +587,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                                      : idx::score_kernel<2, false, false>)
                       : (cand_blocks ? idx::score_kernel<1, true, false>
                                      : idx::score_kernel<1, false, false>);
-  return launch_score(kern, grid, (size_t)kpw * sizeof(float), st, q, q4, w, k_cache,
+  return launch_score(kern, grid, lds, st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
                       pg);
@@ -631,15 +659,16 @@ extern "C" idx_status idx_score_paged(const uint16_t* q, const uint16_t* w, cons
                                       int64_t page_stride, int n_pages,
                                       const int32_t* block_table, int64_t bt_stride, int B, int S,
                                       int H, int D, int T, const int32_t* compress_lens,
-                                      float* scores, int64_t ld, uint32_t* key_hist,
-                                      void* stream) {
+                                      const int32_t* cand_blocks, int n_cand,
+                                      int cand_block_size, float* scores, int64_t ld,
+                                      uint32_t* key_hist, void* stream) {
   idx::PageMap pg{nullptr, 0, 0, 0};
   if (T > 0 && B > 0 && S > 0) {  // the page map matters only when there is work
     const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, T, pg);
     if (e != IDX_OK) return e;
   }
-  return score_impl(q, nullptr, w, k_pages, 0, B, S, H, D, T, compress_lens, nullptr, 0, 0,
-                    scores, ld, key_hist, pg, stream);
+  return score_impl(q, nullptr, w, k_pages, 0, B, S, H, D, T, compress_lens, cand_blocks, n_cand,
+                    cand_block_size, scores, ld, key_hist, pg, stream);
 }
 
 extern "C" idx_status idx_score_topk_paged(const uint16_t* q, const uint16_t* w,

@@ -70,8 +70,6 @@ class IndexerStep:
         # the sequences' logical pages in a seeded random order
         self.paged = paged
         if paged:
-            if wl.ctb:
-                raise ValueError("the paged path covers single-level scoring")
             npg = (T + PAGE_ROWS - 1) // PAGE_ROWS
             perm = np.random.default_rng(7).permutation(wl.B * npg).astype(np.int32)
             self.block_table = to_device(perm.reshape(wl.B, npg))
@@ -203,9 +201,14 @@ class IndexerStep:
                      workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
             # level two: only the candidate positions hold finite scores; the
             # histogram, reset by the level-one top-k, now counts them
-            idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                      cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
-                      stream=stream)
+            if self.paged:
+                idx_score_paged(q, self.w2, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
+                                self.scores2, cand_blocks=self.ids, cand_block_size=wl.cbs,
+                                key_hist=self.key_hist, stream=stream)
+            else:
+                idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
+                          cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
+                          stream=stream)
             idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs, wl.topk,
                                 wl.offset, self.out, key_hist=self.key_hist, stream=stream)
         else:

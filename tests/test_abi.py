@@ -155,8 +155,8 @@ def test_paged_entry_points_reject_bad_page_maps(lib):
     T = 200  # 4 pages of 64 positions
 
     def score(ps=64 * 68, npg=8, bt=d, bts=4, **kw):
-        return lib.idx_score_paged(d, d, d, ps, npg, bt, bts, 1, 1, 64, 128, T, d, d, T, None,
-                                   None)
+        return lib.idx_score_paged(d, d, d, ps, npg, bt, bts, 1, 1, 64, 128, T, d, None, 0, 0, d,
+                                   T, None, None)
 
     def fused(ps=64 * 68, npg=8, bt=d, bts=4):
         return lib.idx_score_topk_paged(d, d, d, ps, npg, bt, bts, 1, 1, 64, 128, T, d, 64, 0, d,
@@ -173,8 +173,11 @@ def test_paged_entry_points_reject_bad_page_maps(lib):
         assert call(bts=3) == IDX_EINVAL  # the table row misses page 3
     assert publish(Tcap=64, sp=4 * 64 + 3) == IDX_EINVAL  # row 64 beyond Tcap
     # nothing to do: no rows
-    assert lib.idx_score_paged(d, d, d, 64 * 68, 8, None, 4, 0, 1, 64, 128, T, d, d, T, None,
-                               None) == IDX_OK
+    assert lib.idx_score_paged(d, d, d, 64 * 68, 8, None, 4, 0, 1, 64, 128, T, d, None, 0, 0, d,
+                               T, None, None) == IDX_OK
+    # level two on pages keeps the row's page ids on chip: T <= 131072
+    assert lib.idx_score_paged(d, d, d, 64 * 68, 4096, d, 2049, 1, 1, 64, 128, 131073, d, d, 4,
+                               128, d, 131073, None, None) == IDX_EUNSUPPORTED
 
 
 def test_q_rope_quant_rejects_bad_arguments(lib):

@@ -148,3 +148,42 @@ def test_publish_paged_matches_oracle(idx, mode):
     for p in range(pg.shape[0]):
         if p not in mapped:
             assert np.array_equal(pg[p], before[p]), p
+
+
+def test_score_paged_candidates_match_oracle(idx):
+    """Level two on pages: candidate blocks of 128 positions (ids out of range
+    skipped), scores bit-identical to the oracle and to the contiguous path;
+    a candidate page whose id is outside the pool scores as zero rows."""
+    t = torch()
+    say("score paged candidates")
+    B, T, cbs = 2, 5000, 128
+    c = small_case(97, B, 1, 64, T)
+    c["cl"][:] = np.array([T, 3001], np.int32)
+    cand = np.array([[0, 7, 38, 39, -1, 500], [2, 3, 23, 30, 31, 1]], np.int32)
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref, _ = oracle.score(c["q"], c["w"], kc_ref, B, 1, 64, T, c["cl"], cand=cand, cbs=cbs)
+    kc = fp4_cache(c["k"])
+    pages, bt = _paginate(kc, [(int(x) + PAGE - 1) // PAGE for x in c["cl"]], 97)
+    sc = t.full((B, T), float("nan"), dtype=t.float32, device="cuda")
+    hist = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+    idx.idx_score_paged(dev(c["q"]), dev(c["w"]), pages, bt, B, 1, T, dev(c["cl"]), sc,
+                        cand_blocks=dev(cand), cand_block_size=cbs, key_hist=hist)
+    sc2 = t.full((B, T), float("nan"), dtype=t.float32, device="cuda")
+    hist2 = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+    idx.idx_score(dev(c["q"]), dev(c["w"]), kc, B, 1, T, dev(c["cl"]), sc2,
+                  cand_blocks=dev(cand), cand_block_size=cbs, key_hist=hist2)
+    sync()
+    assert np.array_equal(bits(host(sc)), bits(ref))
+    assert np.array_equal(bits(host(sc)), bits(host(sc2)))
+    assert np.array_equal(host(hist), host(hist2))
+    # sequence 1's page 46 (positions 2944..3007, inside candidate block 23)
+    # made invalid: its scored positions become relu(0) sums, +0
+    bt_bad = host(bt).copy()
+    bt_bad[1, 46] = pages.shape[0] + 3
+    idx.idx_score_paged(dev(c["q"]), dev(c["w"]), pages, dev(bt_bad), B, 1, T, dev(c["cl"]), sc,
+                        cand_blocks=dev(cand), cand_block_size=cbs)
+    sync()
+    g = host(sc)
+    assert np.all(g[1, 2944:3001] == 0.0) and not np.any(np.signbit(g[1, 2944:3001]))
+    assert np.array_equal(bits(g[1, 2940:2944]), bits(ref[1, 2940:2944]))
+    assert np.array_equal(bits(g[0]), bits(ref[0]))
