@@ -78,14 +78,14 @@ def test_round_trip_is_a_valid_score_query(idx):
         assert np.array_equal(bits(g[r, :cl[r]]), bits(ref[r, :cl[r]])), r
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_score_takes_the_quantised_rows(idx, fused):
+@pytest.mark.parametrize("fused,H", [(False, 64), (True, 64), (False, 32), (True, 32)])
+def test_score_takes_the_quantised_rows(idx, fused, H):
     """idx_score_q4 / idx_score_topk_q4 on the query step's rows give the
     scores and indices of the oracle (and of idx_score on the round trip)."""
     t = torch()
-    say("score from quantised rows", fused)
-    rng = np.random.default_rng(8)
-    B, S, H, T, sp = 2, 6, 64, 3000, 10000
+    say("score from quantised rows", fused, H)
+    rng = np.random.default_rng(8 + H)
+    B, S, T, sp = 2, 6, 3000, 10000
     R = B * S
     q = normal_bf16(rng, (R, H, 128))
     w = normal_bf16(rng, (R, H))
