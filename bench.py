@@ -100,7 +100,7 @@ def score_kernel_name(st) -> str:
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("score.hip", "idx_common.hpp"):
+    for name in ("score.hip", "idx_common.hpp", "row_topk.hpp"):
         with open(os.path.join(ROOT, "sparse_attention_top_fp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

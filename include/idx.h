@@ -12,7 +12,9 @@
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are device memory owned by the caller; the
- *     library never allocates device memory and keeps no state between calls.
+ *     library never allocates device memory and keeps no state between calls
+ *     other than the launch-timing hook (idx_timing_arm).  Calls may come
+ *     from several host threads; the timing hook itself is single-threaded.
  *   - bf16 tensors are passed as their 16-bit patterns (uint16_t).
  *   - stream is a hipStream_t (NULL = the default stream); every launch is
  *     asynchronous on it and calls on one stream run in call order.

@@ -28,6 +28,7 @@
 #include "row_topk.hpp"
 
 #include <hip/hip_ext.h>
+#include <atomic>
 
 namespace idx {
 
@@ -488,14 +489,15 @@ namespace {
 // ------------------------------------------------------- launch timing
 constexpr int kTimingSlots = 256;
 hipEvent_t g_timing_ev[kTimingSlots][2] = {};
-int g_timing_armed = -1;  // slot of the next score launch, or -1
+std::atomic<int> g_timing_armed{-1};  // slot of the next score launch, or -1
 
 // Launches the score kernel, through hipExtLaunchKernel with the armed
-// event pair when timing is armed.
+// event pair when timing is armed.  Launches from other threads only read
+// the flag, so they do not race with each other.
 template <typename... Args, typename F>
 idx_status launch_score(F kern, dim3 grid, size_t lds, hipStream_t st, Args... args) {
-  const int slot = g_timing_armed;
-  g_timing_armed = -1;
+  const int slot =
+      g_timing_armed.load(std::memory_order_relaxed) >= 0 ? g_timing_armed.exchange(-1) : -1;
   if (slot >= 0)
     hipExtLaunchKernelGGL(kern, grid, dim3(256), (uint32_t)lds, st, g_timing_ev[slot][0],
                           g_timing_ev[slot][1], 0u, args...);
@@ -507,15 +509,18 @@ idx_status launch_score(F kern, dim3 grid, size_t lds, hipStream_t st, Args... a
 constexpr int kMaxKeysPerWg = 8192;  // bounds the LDS score buffer (32 KB)
 // paged candidate mode keeps the row's page ids in LDS too (2048 ids, 8 KB)
 constexpr int kMaxPagedCandT = 131072;
-int g_keys_per_wg_override = -1;
+// IDX_SCORE_KEYS_PER_WG (tuning): keys per workgroup, read once per process
+int keys_per_wg_override() {
+  static const int v = [] {
+    const char* e = getenv("IDX_SCORE_KEYS_PER_WG");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
 
 int pick_keys_per_wg(int64_t R, int vtotal) {
-  if (g_keys_per_wg_override < 0) {
-    const char* e = getenv("IDX_SCORE_KEYS_PER_WG");
-    g_keys_per_wg_override = e ? atoi(e) : 0;
-  }
-  if (g_keys_per_wg_override > 0) {
-    const int o = (g_keys_per_wg_override + 255) / 256 * 256;
+  if (keys_per_wg_override() > 0) {
+    const int o = (keys_per_wg_override() + 255) / 256 * 256;
     return o < kMaxKeysPerWg ? o : kMaxKeysPerWg;
   }
   // about one workgroup per CU over the whole launch (256 CUs): measured on
@@ -713,7 +718,7 @@ extern "C" idx_status idx_timing_arm(int slot) {
   for (int i = 0; i < 2; ++i)
     if (!g_timing_ev[slot][i] && hipEventCreate(&g_timing_ev[slot][i]) != hipSuccess)
       return IDX_EHIP;
-  g_timing_armed = slot;
+  g_timing_armed.store(slot);
   return IDX_OK;
 }
 
