@@ -136,7 +136,9 @@ idx_status idx_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float w_sc
  *                  NULL.  When given, every t < T is first set to -inf and
  *                  only positions t < cl[r] inside the listed blocks of
  *                  cand_block_size positions are scored; ids < 0 or
- *                  >= ceil(T/cand_block_size) are skipped.
+ *                  >= ceil(T/cand_block_size) are skipped.  An id listed
+ *                  twice is scored twice (same values) and counted twice in
+ *                  key_hist, so with key_hist the ids must be distinct.
  *   scores         device, [B*S][ld] fp32, ld >= T.  Entries t >= cl[r] are
  *                  left unspecified without cand_blocks (callers mask by cl).
  *   key_hist       device, [B*S][2048] uint32, or NULL.  When given, the
@@ -279,7 +281,8 @@ idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t
  * candidate positions lie below compress_lens the row is ranked among them
  * only; otherwise every finite position is kept plus the lowest other
  * positions, as the full ranking does.
- *   cand_blocks  device, [R][n_cand] int32 block ids in ascending order
+ *   cand_blocks  device, [R][n_cand] int32 block ids in strictly
+ *                ascending order apart from skipped ids
  *                (idx_select_candidate_blocks' output); ids < 0 or
  *                >= ceil(T/cand_block_size) are skipped
  *   key_hist     device, [R][2048] from idx_score with these cand_blocks on
