@@ -93,7 +93,7 @@ class Workload:
 
 
 # YaRN constants for the key-publish RoPE table: the pages name the
-# parameters but print no values; these are this build's choice.
+# parameters but print no values; these values are chosen here.
 YARN = dict(theta=10000.0, factor=16.0, orig_len=65536, beta_fast=32.0, beta_slow=1.0)
 
 

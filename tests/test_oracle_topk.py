@@ -6,7 +6,7 @@ is not below compress_lens, offset added).  Short-context closed form: the
 vLLM attention.py page, _fill_short_context_topk_indices.  Block selection:
 "DeepSeek V4.1" page (select_candidate_blocks call) and the "Module compress"
 page (select_candidate_blocks), whose body is not given; the block-max
-reading is this build's.
+reading is chosen here (the pages leave the block score open).
 """
 import numpy as np
 import pytest
