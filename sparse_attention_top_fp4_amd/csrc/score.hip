@@ -256,6 +256,9 @@ __device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint
   float v[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) v[e] = sbuf[wbase + 64 * e];
+  // sh and wtot live at the end of the score buffer: every wave has its
+  // scores in registers before any scan writes there
+  __syncthreads();
   row_vals<EPT>(v, wbase, limit, span);  // whatever sbuf held past limit
   uint32_t mine = 0;
 #pragma unroll
@@ -272,19 +275,31 @@ __device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint
                      orow);
 }
 
+// The fused kernel (TOPK) is sized for four workgroups per CU: two key
+// tile sets per wave (at most 128 VGPRs) and 40 KB of LDS, the 8 KB
+// histogram plus the 32 KB score buffer, which also holds the query rows
+// until they are in registers and the ranking's scan words.
 template <int HT, bool CAND, bool TOPK>
-__global__ __launch_bounds__(256) void score_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TOPK ? 4 : 1))) void
+score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ q4,
     const uint16_t* __restrict__ w, const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
     FusedTopk tk, PageMap pg) {
   constexpr int H = 32 * HT;
-  __shared__ uint32_t qs[H * 17];  // H quantised query rows of 68 bytes
+  constexpr int kSets = TOPK ? 2 : kTileSets;  // key tile sets in registers
   __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
   __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
-  __shared__ uint32_t wtot[8], sh[4];
+  __shared__ uint32_t qs_own[TOPK ? 1 : H * 17];
   extern __shared__ __attribute__((aligned(16))) float sbuf[];  // this chunk's scores
+  // H quantised query rows of 68 bytes; the fused kernel keeps them at the
+  // start of its score buffer (kFusedMaxT words), free until the first tile
+  // is scored
+  uint32_t* qs = TOPK ? reinterpret_cast<uint32_t*>(sbuf) : qs_own;
+  // the fused ranking's scan words: the last 16 words of the score buffer
+  uint32_t* wtot = reinterpret_cast<uint32_t*>(sbuf) + kFusedMaxT - 16;
+  uint32_t* sh = wtot + 8;
   // rows in reverse dispatch order: causal rows grow with their index, so the
   // longest start first and the short ones fill the end of the launch
   const int r = gridDim.x - 1 - blockIdx.x;
@@ -324,8 +339,8 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
 
   // the first key tiles are requested before the query work, so their
-  // latency overlaps the query load and quantisation.  kTileSets register
-  // sets: while one tile computes, the next kTileSets - 1 tiles of this wave
+  // latency overlaps the query load and quantisation.  kSets register
+  // sets: while one tile computes, the next kSets - 1 tiles of this wave
   // are in flight
   // contiguous: the sequence's rows; paged: the page pool (plain mode only)
   const bool paged = !CAND && pg.bt;  // plain mode: pages by readlane (below)
@@ -345,9 +360,9 @@ __global__ __launch_bounds__(256) void score_kernel(
     return paged ? __builtin_amdgcn_readlane(pid_lane, i < 63 ? i : 63) : -1;
   };
   int it = 0;  // tiles of this wave started
-  KeyTile buf[kTileSets];
+  KeyTile buf[kSets];
 #pragma unroll
-  for (int i = 0; i < kTileSets - 1; ++i)
+  for (int i = 0; i < kSets - 1; ++i)
     buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, paged, tile_page(i),
                        pg.page_stride, pg.n_pages, bt_lds);
 
@@ -404,16 +419,17 @@ __global__ __launch_bounds__(256) void score_kernel(
       sA[ht][s] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
     }
   }
+  if (TOPK) __syncthreads();  // the query rows' words are score slots from here on
 
   float* srow = scores ? scores + (int64_t)r * ld : nullptr;
   // the loop body is unrolled over the sets so every set index is a
   // compile-time constant (the sets stay in distinct registers)
   while (true) {
 #pragma unroll
-    for (int u = 0; u < kTileSets; ++u) {
-      buf[(u + kTileSets - 1) % kTileSets] =
-          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kTileSets - 1)), lane, paged,
-                    tile_page(it + kTileSets - 1), pg.page_stride, pg.n_pages, bt_lds);
+    for (int u = 0; u < kSets; ++u) {
+      buf[(u + kSets - 1) % kSets] =
+          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kSets - 1)), lane, paged,
+                    tile_page(it + kSets - 1), pg.page_stride, pg.n_pages, bt_lds);
       score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
       ++it;
