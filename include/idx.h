@@ -196,7 +196,9 @@ idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k
  *   bt_stride    >= ceil(T / 64) (score) or ceil(Tcap / 64) (publish)
  * Everything else, and every result, is as for the contiguous call of the
  * same name; the results are bit-identical to it on the same rows.  In
- * candidate mode an invalid id likewise scores as zero rows.
+ * candidate mode an invalid id likewise scores as zero rows.  When there is
+ * work (B, S, T > 0), a null block_table, n_pages <= 0, page_stride < 64 *
+ * 68 or a bt_stride below the bound gives IDX_EINVAL before any launch.
  */
 
 /* idx_score on a paged key cache.  With cand_blocks (level two) the row's
@@ -209,7 +211,10 @@ idx_status idx_score_paged(const uint16_t *q, const uint16_t *w, const uint8_t *
                            int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
                            void *stream);
 
-/* idx_score_topk on a paged key cache. */
+/* idx_score_topk on a paged key cache ([IDX, forward: score, then the final
+ * topk]; pages as above).  T <= 8192 as for idx_score_topk
+ * (IDX_EUNSUPPORTED otherwise); without scores, rows with compress_lens <=
+ * index_topk are written in closed form and read no page. */
 idx_status idx_score_topk_paged(const uint16_t *q, const uint16_t *w, const uint8_t *k_pages,
                                 int64_t page_stride, int n_pages, const int32_t *block_table,
                                 int64_t bt_stride, int B, int S, int H, int D, int T,
@@ -351,7 +356,11 @@ idx_status idx_publish_keys(const uint16_t *latent, const uint16_t *wk, const fl
                             float eps, int start_pos, int ratio, uint8_t *k_cache,
                             int64_t k_batch_stride_rows, int Tcap, void *stream);
 
-/* idx_publish_keys into a paged key cache (rows < Tcap, as above). */
+/* idx_publish_keys into a paged key cache ([IDX, forward: the key-owning
+ * layer's store at start_pos // ratio]; pages as above): row t < Tcap goes
+ * to slot t % 64 of page block_table[b][t / 64]; a page id outside
+ * [0, n_pages) is not written.  Arguments and errors otherwise as
+ * idx_publish_keys. */
 idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, const float *gamma,
                                   const float *cos_sin, int P, int B, int G, int Din, int D,
                                   int rd, float eps, int start_pos, int ratio, uint8_t *k_pages,
