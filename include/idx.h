@@ -197,8 +197,9 @@ idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k
  * Everything else, and every result, is as for the contiguous call of the
  * same name; the results are bit-identical to it on the same rows.  In
  * candidate mode an invalid id likewise scores as zero rows.  When there is
- * work (B, S, T > 0), a null block_table, n_pages <= 0, page_stride < 64 *
- * 68 or a bt_stride below the bound gives IDX_EINVAL before any launch.
+ * work (score: B, S, T > 0; publish: B * G > 0), a null block_table,
+ * n_pages <= 0, page_stride < 64 * 68 or a bt_stride below the bound gives
+ * IDX_EINVAL before any launch.
  */
 
 /* idx_score on a paged key cache.  With cand_blocks (level two) the row's
