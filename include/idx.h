@@ -369,13 +369,19 @@ idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, co
                                   int64_t bt_stride, int Tcap, void *stream);
 
 /*
- * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys
- * ([CMP, yarn_freqs_cis]; the YaRN method of Peng et al.).  Base inverse
- * frequency theta^(-2i/rd); with orig_len > 0 and factor != 1 the
- * frequencies are blended towards base/factor by a linear ramp between the
- * correction dimensions of beta_fast and beta_slow rotations.  Angles,
+ * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys and
+ * idx_q_rope_quant ([CMP, yarn_freqs_cis]: precompute_freqs_cis with YaRN;
+ * the YaRN method of Peng et al.).  Pair i of the rd rotated dims has the
+ * plain frequency theta^(-2i/rd).  With orig_len > 0 and factor != 1 it is
+ * blended towards plain/factor by a linear ramp in i, 0 up to lo and 1 from
+ * hi, where lo = floor(d(beta_fast)), hi = ceil(d(beta_slow)) kept inside
+ * [0, rd - 1] (hi == lo widens the ramp to 0.001), and d(b) is the real
+ * dimension at which a pair turns b times over orig_len positions.  Angles,
  * cosines and sines in double, stored fp32.
  *   out  host, [P][rd/2][2] fp32 (cos, sin)
+ * IDX_EINVAL for P < 0, rd odd or <= 0, theta <= 1, factor <= 0, orig_len < 0,
+ * a non-positive beta when the ramp is used, or a null out with P > 0;
+ * IDX_EUNSUPPORTED for rd > 2048.
  */
 idx_status idx_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len,
                             double beta_fast, double beta_slow, float *out);

@@ -25,8 +25,17 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
   topk             pinned: numpy lexsort brute force; width/order/-1 invariants;
                    the short-context closed form [VLLM, _fill_short_context_topk_indices].
   select_blocks    pinned: numpy brute force; ctb >= nb keeps every reachable block.
-  yarn_cos_sin     pinned for factor 1 (plain RoPE); the YaRN constants
-                   themselves are parity unpinned (the pages name them only).
+  yarn_cos_sin     float64 numpy, written here (not in oracle.c).  Pinned:
+                   factor 1 is plain RoPE; the correction dimension of beta
+                   rotations satisfies its defining equation; the band
+                   (lo, hi) = (20, 33) hand-worked for the chosen constants;
+                   hand-worked frequency ratios inside the band.  The
+                   constants themselves are a reading (the pages name them
+                   only).
+  head sum order   the fp32 two-chain association is a contract shared with
+                   the GPU library (split chosen to match the matrix core's
+                   half-wave layout); the pages fix none.  A hand-worked
+                   golden tells it apart from the other plausible orders.
   publish          pinned: pre-quantisation key vs a float64 restatement within
                    bf16 rounding; RoPE identity at position 0; norm preservation.
   q_rope_quant     pinned: RoPE identity at position 0 and with rd = 0 (the
@@ -39,6 +48,7 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -78,8 +88,6 @@ def lib():
         L.orc_topk.restype = None
         L.orc_select_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64]
         L.orc_select_blocks.restype = None
-        L.orc_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
-        L.orc_yarn_cos_sin.restype = None
         L.orc_publish.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, P, i64, P]
         L.orc_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
         L.orc_q_rope_quant.restype = None
@@ -173,9 +181,52 @@ def select_blocks(scores, cl, ctb, cbs, T=None):
 
 
 # ---------------------------------------------------------------- publish
+def yarn_correction_dim(beta, rd, theta, orig_len):
+    """[CMP, yarn_freqs_cis] (YaRN, Peng et al., the "NTK-by-parts" band):
+    dimension pair i of a rd-wide RoPE turns orig_len * theta^(-2i/rd) /
+    (2 pi) times over the original context.  The correction dimension of
+    beta rotations is the real d at which that count equals beta, i.e. the
+    solution of theta^(2d/rd) = orig_len / (2 pi beta), found here as a
+    logarithm to base theta."""
+    return 0.5 * rd * math.log(orig_len / (2.0 * math.pi * beta), theta)
+
+
+def yarn_correction_range(rd, theta, orig_len, beta_fast, beta_slow):
+    """The integer band [lo, hi] of the ramp: lo = floor(d(beta_fast)) and
+    hi = ceil(d(beta_slow)), kept inside [0, rd - 1] (the clamp of
+    precompute_freqs_cis, which the page names as the table's builder)."""
+    lo = math.floor(yarn_correction_dim(beta_fast, rd, theta, orig_len))
+    hi = math.ceil(yarn_correction_dim(beta_slow, rd, theta, orig_len))
+    return max(lo, 0), min(hi, rd - 1)
+
+
+def yarn_frequencies(rd, theta, factor, orig_len, beta_fast, beta_slow):
+    """Rotation frequency of each of the rd/2 dimension pairs, float64.
+    Plain RoPE: theta^(-2i/rd).  With YaRN (orig_len > 0, factor != 1) pair
+    i moves from the plain frequency (below the band) to the plain frequency
+    divided by factor (above it) along a straight line in i across the band
+    (a band of width 0 is widened to 0.001)."""
+    i = np.arange(rd // 2, dtype=np.float64)
+    plain = np.power(float(theta), -2.0 * i / rd)
+    if orig_len <= 0 or factor == 1.0:
+        return plain
+    lo, hi = yarn_correction_range(rd, theta, orig_len, beta_fast, beta_slow)
+    width = float(hi - lo) if hi != lo else 0.001
+    ramp = np.clip((i - lo) / width, 0.0, 1.0)  # 0: plain, 1: plain / factor
+    return plain * (1.0 - ramp) + (plain / factor) * ramp
+
+
 def yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):
+    """[CMP, yarn_freqs_cis]: the [P][rd/2] table of (cos, sin) of position p
+    times each pair's frequency, in float64, stored float32 ([P, rd/2, 2]).
+    Built in row chunks to bound memory for long tables."""
+    f = yarn_frequencies(rd, theta, factor, orig_len, beta_fast, beta_slow)
     out = np.empty((P, rd // 2, 2), np.float32)
-    lib().orc_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow, _p(out))
+    for p0 in range(0, P, 1 << 16):
+        pos = np.arange(p0, min(P, p0 + (1 << 16)), dtype=np.float64)
+        ang = pos[:, None] * f[None, :]
+        out[p0:p0 + len(pos), :, 0] = np.cos(ang)
+        out[p0:p0 + len(pos), :, 1] = np.sin(ang)
     return out
 
 

@@ -19,6 +19,18 @@
  * arithmetic where the method is exact, one fixed fp32 operation order where
  * the contract fixes one.  No blocking, fusion or reordering.
  *
+ * Provenance of the one order that is not the pages': the pages sum the
+ * rectified, weighted head scores in bf16 torch ops and fix no association.
+ * The fp32 head sum here (heads [0, ceil(H/2)) and [ceil(H/2), H) each
+ * summed ascending, then one add) is a contract shared with the GPU
+ * library; its split into two chains was chosen to match how the matrix
+ * core leaves a key's heads in the two halves of a wavefront.  A hand-worked
+ * golden (tests/golden/head_order.txt) tells this association apart from a
+ * single chain, a pairwise tree and the other plausible splits.
+ *
+ * The RoPE table is not here: oracle/__init__.py builds it in float64 numpy
+ * (yarn_cos_sin), and every function below takes it as an input.
+ *
  * Parity status of each function is recorded in the file header of
  * oracle/__init__.py and in the design notes.
  */
@@ -414,53 +426,6 @@ void orc_select_blocks(const float *scores, int64_t ld, int R, int T, const int3
 }
 
 /* ------------------------------------------------------------ key publish */
-
-/* YaRN RoPE table ([CMP, yarn_freqs_cis]; the YaRN method of Peng et al.,
- * "YaRN: Efficient Context Window Extension of Large Language Models").
- * Base inverse frequency f_i = theta^(-2i/rd); with orig_len > 0 the
- * frequencies are blended towards f_i/factor by a linear ramp over the
- * dimension range [low, high] given by the correction dimensions of
- * beta_fast and beta_slow rotations.  Angles and cos/sin in double, stored
- * fp32.  out: [P][rd/2][2] = (cos, sin). */
-static double yarn_correction_dim(double rotations, int rd, double theta, int orig_len)
-{
-    return rd * log((double)orig_len / (rotations * 2.0 * M_PI)) / (2.0 * log(theta));
-}
-
-void orc_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len, double beta_fast,
-                      double beta_slow, float *out)
-{
-    int half = rd / 2;
-    double *freq = (double *)malloc(sizeof(double) * (size_t)half);
-    for (int i = 0; i < half; ++i)
-        freq[i] = pow(theta, -(2.0 * i) / rd);
-    if (orig_len > 0 && factor != 1.0) {
-        double lo = floor(yarn_correction_dim(beta_fast, rd, theta, orig_len));
-        double hi = ceil(yarn_correction_dim(beta_slow, rd, theta, orig_len));
-        if (lo < 0)
-            lo = 0;
-        if (hi > half - 1)
-            hi = half - 1;
-        if (hi == lo)
-            hi += 0.001;
-        for (int i = 0; i < half; ++i) {
-            double ramp = (i - lo) / (hi - lo);
-            if (ramp < 0)
-                ramp = 0;
-            if (ramp > 1)
-                ramp = 1;
-            freq[i] = freq[i] / factor * ramp + freq[i] * (1.0 - ramp);
-        }
-    }
-#pragma omp parallel for schedule(static)
-    for (int p = 0; p < P; ++p)
-        for (int i = 0; i < half; ++i) {
-            double a = (double)p * freq[i];
-            out[((int64_t)p * half + i) * 2 + 0] = (float)cos(a);
-            out[((int64_t)p * half + i) * 2 + 1] = (float)sin(a);
-        }
-    free(freq);
-}
 
 /* The key for one latent, before quantisation ([IDX, forward: the
  * index-key publish]): y = wk . latent (fp32, one fmaf per input feature in

@@ -316,11 +316,12 @@ extern "C" idx_status idx_publish_keys_paged(const uint16_t* latent, const uint1
                       k_pages, 0, Tcap, block_table, bt_stride, page_stride, n_pages, stream);
 }
 
-// Host-side YaRN RoPE table (the YaRN method of Peng et al.): base inverse
-// frequencies theta^(-2i/rd); with orig_len > 0 and factor != 1 the
-// frequency of dimension pair i is blended towards base/factor by a linear
-// ramp that is 0 below the correction dimension of beta_fast rotations and
-// 1 above that of beta_slow rotations over the original context length.
+// Host-side YaRN RoPE table (the YaRN method of Peng et al., in the form of
+// DeepSeek's precompute_freqs_cis that [CMP, yarn_freqs_cis] names).  Pair i
+// has the plain frequency theta^(-2i/rd).  With orig_len > 0 and factor != 1
+// it slides to plain/factor along a linear ramp in i: 0 up to the floor of
+// the correction dimension of beta_fast rotations over orig_len, 1 from the
+// ceiling of that of beta_slow rotations, both kept inside [0, rd - 1].
 extern "C" idx_status idx_yarn_cos_sin(int P, int rd, double theta, double factor, int orig_len,
                                        double beta_fast, double beta_slow, float* out) {
   if (P < 0 || rd <= 0 || (rd & 1) || !(theta > 1.0) || !(factor > 0.0) || orig_len < 0)
@@ -332,17 +333,19 @@ extern "C" idx_status idx_yarn_cos_sin(int P, int rd, double theta, double facto
   if (half > 1024) return IDX_EUNSUPPORTED;
   for (int i = 0; i < half; ++i) freq[i] = pow(theta, -(2.0 * i) / rd);
   if (orig_len > 0 && factor != 1.0) {
+    if (!(beta_fast > 0.0) || !(beta_slow > 0.0)) return IDX_EINVAL;
+    // dimension whose pair turns `rotations` times over orig_len positions
     auto corr_dim = [&](double rotations) {
       return rd * log((double)orig_len / (rotations * 2.0 * M_PI)) / (2.0 * log(theta));
     };
     double lo = floor(corr_dim(beta_fast)), hi = ceil(corr_dim(beta_slow));
     lo = lo < 0.0 ? 0.0 : lo;
-    hi = hi > half - 1 ? half - 1 : hi;
+    hi = hi > rd - 1 ? rd - 1 : hi;
     if (hi == lo) hi += 0.001;
     for (int i = 0; i < half; ++i) {
       double t = (i - lo) / (hi - lo);
       t = t < 0.0 ? 0.0 : (t > 1.0 ? 1.0 : t);
-      freq[i] = freq[i] / factor * t + freq[i] * (1.0 - t);
+      freq[i] = freq[i] * (1.0 - t) + freq[i] / factor * t;
     }
   }
   for (int64_t p = 0; p < P; ++p)

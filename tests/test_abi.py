@@ -109,13 +109,26 @@ def test_quant_rejects_bad_arguments(lib):
 
 
 def test_host_rope_table_matches_oracle(lib):
-    for factor, orig in ((YARN["factor"], YARN["orig_len"]), (1.0, 0)):
+    """The library's table (C, libm) against the oracle's own float64 numpy
+    table, which the tests pin to hand-worked values: within one fp32 rounding
+    of each other (the two float64 cosines may differ in their last bits)."""
+    for factor, orig in ((YARN["factor"], YARN["orig_len"]), (1.0, 0), (4.0, 4096)):
         a = idx.idx_yarn_cos_sin(5000, 64, YARN["theta"], factor, orig, YARN["beta_fast"],
                                  YARN["beta_slow"])
         b = oracle.yarn_cos_sin(5000, 64, YARN["theta"], factor, orig, YARN["beta_fast"],
                                 YARN["beta_slow"])
         diff = np.abs(a.astype(np.float64) - b.astype(np.float64))
         assert diff.max() <= 2.0 ** -24
+        assert np.mean(a == b) > 0.999
+
+
+def test_host_rope_table_rejects_bad_arguments(lib):
+    out = (ctypes.c_float * 64)()
+    assert lib.idx_yarn_cos_sin(1, 63, 1e4, 1.0, 0, 32.0, 1.0, out) == IDX_EINVAL
+    assert lib.idx_yarn_cos_sin(1, 64, 1.0, 1.0, 0, 32.0, 1.0, out) == IDX_EINVAL
+    assert lib.idx_yarn_cos_sin(1, 64, 1e4, 16.0, 65536, 0.0, 1.0, out) == IDX_EINVAL
+    assert lib.idx_yarn_cos_sin(1, 64, 1e4, 16.0, 65536, 32.0, 1.0, None) == IDX_EINVAL
+    assert lib.idx_yarn_cos_sin(0, 64, 1e4, 16.0, 65536, 32.0, 1.0, None) == IDX_OK
 
 
 def test_fused_score_topk_rejects_bad_arguments(lib):

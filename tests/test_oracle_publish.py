@@ -3,9 +3,13 @@
 Publish definition: "DeepSeek V4.1" page, class Indexer, forward (k =
 k_norm(wk(latent)), RoPE on the last rope_head_dim dims at the group's
 position, fp4 round trip, write into k_cache at start_pos // ratio).  RoPE
-table: "Module compress" page, yarn_freqs_cis (YaRN; constants not printed,
-so the YaRN constants are parity unpinned).
+table: "Module compress" page, yarn_freqs_cis (YaRN; its constants are not
+printed, so their values are a reading; the table's construction is pinned by
+the correction-dimension equation, a hand-worked band and hand-worked ramp
+values).
 """
+import math
+
 import numpy as np
 
 import oracle
@@ -44,16 +48,48 @@ def test_yarn_factor_one_is_plain_rope():
     assert np.all(t[0, :, 0] == 1.0) and np.all(t[0, :, 1] == 0.0)
 
 
-def test_yarn_ramp_properties():
+def test_yarn_correction_dim_meets_its_definition():
+    """The correction dimension d(beta) is where a pair turns beta times over
+    the original context: orig_len * theta^(-2d/rd) / (2 pi) == beta."""
+    for beta in (YARN["beta_fast"], YARN["beta_slow"], 4.0, 0.5):
+        for rd, theta, orig in ((64, YARN["theta"], YARN["orig_len"]), (128, 50000.0, 4096)):
+            d = oracle.yarn_correction_dim(beta, rd, theta, orig)
+            turns = orig * theta ** (-2.0 * d / rd) / (2.0 * math.pi)
+            assert abs(turns / beta - 1.0) < 1e-12
+
+
+def test_yarn_band_hand_worked():
+    """Band of the chosen constants (theta 1e4, rd 64, original length 65536,
+    beta 32 / 1), worked by hand:
+      d(32) = 32 * ln(65536 / (64 pi)) / ln(1e4) = 32 * 5.78673 / 9.21034 = 20.105
+      d(1)  = 32 * ln(65536 / (2 pi))  / ln(1e4) = 32 * 9.25250 / 9.21034 = 32.146
+    so lo = floor(20.105) = 20 and hi = ceil(32.146) = 33, inside [0, rd - 1]
+    (a clamp at rd/2 - 1 would have cut hi to 31)."""
+    assert oracle.yarn_correction_range(64, YARN["theta"], YARN["orig_len"], YARN["beta_fast"],
+                                        YARN["beta_slow"]) == (20, 33)
+    # clamps: a short original length puts d(beta_fast) below 0, a long one
+    # puts d(beta_slow) beyond rd - 1
+    assert oracle.yarn_correction_range(64, 1e4, 100, 32.0, 1.0)[0] == 0
+    assert oracle.yarn_correction_range(16, 1e4, 10 ** 9, 32.0, 1.0)[1] == 15
+
+
+def test_yarn_ramp_hand_worked():
+    """Frequency of pair i over its plain value, for the band [20, 33] and
+    factor 16: 1 for i <= 20; 1 - (15/16)(i - 20)/13 inside (i = 26: 118/208,
+    i = 31: 43/208).  Read back from the table's angle at position 1."""
     rd = 64
     t = oracle.yarn_cos_sin(2, rd, YARN["theta"], YARN["factor"], YARN["orig_len"],
                             YARN["beta_fast"], YARN["beta_slow"])
     f = np.arctan2(t[1, :, 1].astype(np.float64), t[1, :, 0].astype(np.float64))
-    base = YARN["theta"] ** (-(2.0 * np.arange(rd // 2)) / rd)
-    r = f / base
-    assert abs(r[0] - 1.0) < 1e-6 and abs(r[-1] - 1.0 / YARN["factor"]) < 1e-5
+    plain = YARN["theta"] ** (-(2.0 * np.arange(rd // 2)) / rd)
+    r = f / plain
+    assert np.all(np.abs(r[:21] - 1.0) < 1e-6)
+    assert abs(r[26] - 118.0 / 208.0) < 1e-6
+    assert abs(r[31] - 43.0 / 208.0) < 1e-5
     assert np.all(np.diff(r) <= 1e-6)
-    assert np.all((r >= 1.0 / YARN["factor"] - 1e-6) & (r <= 1.0 + 1e-6))
+    f64 = oracle.yarn_frequencies(rd, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                                  YARN["beta_fast"], YARN["beta_slow"])
+    assert f64[20] == plain[20] and abs(f64[26] / plain[26] - 118.0 / 208.0) < 1e-15
 
 
 def test_prequant_key_matches_float64_within_bf16_rounding():
