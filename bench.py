@@ -15,9 +15,13 @@ rather than from the 256 MB last-level cache.
 
 Prints one JSON line (rank 0, N = 1):
   value         queries/s over the K timed steps (host clock, synchronised)
-  roofline      the score kernel: algorithmic bytes per launch / its mean
-                duration from a HIP event pair attached to each launch on
-                the launch stream (hipExtLaunchKernel), against 8 TB/s
+  roofline      the score kernel: algorithmic bytes (decode: keys, fp4 query
+                heads, weights) or fp4 flops (prefill: every causal pair)
+                per launch / its mean duration from HIP event pairs attached
+                to about ten launches of the timed region on the launch
+                stream (hipExtLaunchKernel), against 8 TB/s or 10.1 PFLOP/s;
+                roofline.step: the whole step's algorithmic bytes or flops
+                over ms_per_step against the same peak
   cpu_baseline  the CPU oracle timed on the host on a bounded sample
 """
 from __future__ import annotations
@@ -45,9 +49,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = batched decode)")
-    ap.add_argument("--event-every", type=int, default=25,
+    ap.add_argument("--event-every", type=int, default=0,
                     help="time the score launch with HIP events on every n-th step of the "
-                         "timed region (a timed launch costs the host about 20 us)")
+                         "timed region; 0 (default): about ten steps spread over it (a timed "
+                         "launch costs the host about 20 us)")
+    ap.add_argument("--latency-steps", type=int, default=50,
+                    help="after the timed region, this many single steps each bracketed by "
+                         "an event pair, for the p10/p50/p90 step time")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="OpenMP threads of the oracle baseline (0: all host cores)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU work for the oracle baseline sample")
@@ -76,18 +86,79 @@ def scored_compress_lens(wl, st):
     return cl
 
 
-def score_kernel_bytes(wl, st) -> int:
-    """Algorithmic HBM bytes of one score launch: per scored (row, key) pair
-    the 68-byte key row and the 4-byte fp32 score; per row the bf16 query
-    (H x 128 x 2) and the bf16 weights (H x 2)."""
-    cl = scored_compress_lens(wl, st)
-    pairs = int(cl.sum())
-    rows = int((cl > 0).sum())
-    return pairs * (68 + 4) + rows * (wl.H * 128 * 2 + wl.H * 2)
+Q_ROW_BYTES = 68       # one fp4 query head: 64 code bytes + 4 scale bytes
+FLOP_PER_PAIR_HEAD = 2 * 128
 
 
-def score_kernel_flops(wl, st) -> int:
-    return int(scored_compress_lens(wl, st).sum()) * wl.H * 128 * 2
+def reachable_pairs(wl) -> int:
+    """(row, key) pairs below compress_lens: the causal pairs of a prefill,
+    B * T for a decode."""
+    import numpy as np
+    return int(np.minimum(wl.compress_lens().astype(np.int64), wl.T).sum())
+
+
+def score_kernel_bytes(wl, st=None) -> int:
+    """Algorithmic HBM bytes of one (level-one) score launch: the 68-byte key
+    row of every reachable (row, key) pair, each row's fp4 query heads (68
+    bytes a head) and its bf16 weights.  The fp32 score scratch the launch
+    also writes is an implementation cost, not algorithmic: it shows up in
+    the measured traffic instead."""
+    return reachable_pairs(wl) * 68 + wl.R * wl.H * (Q_ROW_BYTES + 2)
+
+
+def score_kernel_flops(wl, st=None) -> int:
+    """Algorithmic fp4 flops of one score launch: 2 * 128 per head for every
+    reachable pair.  A prefill's rows with compress_lens <= k_out are part of
+    it even where the fused launch writes them in closed form."""
+    return reachable_pairs(wl) * wl.H * FLOP_PER_PAIR_HEAD
+
+
+def scored_flops(wl, st) -> int:
+    """The flops the launch actually performs (closed-form rows excluded)."""
+    return int(scored_compress_lens(wl, st).sum()) * wl.H * FLOP_PER_PAIR_HEAD
+
+
+def step_bytes(wl, q_step=False, prefill_publish_groups=0) -> int:
+    """Algorithmic HBM bytes of one whole step: every score launch's keys,
+    the fp4 query and the weights (per level), the candidate block ids, the
+    key publish (wk, latent, the written rows) and the int32 indices of
+    every top-k the step keeps."""
+    kout = min(wl.topk, wl.T)
+    b = reachable_pairs(wl) * 68 + wl.R * wl.H * (Q_ROW_BYTES + 2) + wl.R * kout * 4
+    if wl.ctb:
+        nb = -(-wl.T // wl.cbs)
+        cand = wl.R * min(wl.ctb * wl.cbs, wl.T)
+        b += cand * 68 + wl.R * wl.H * 2            # level-two keys and weights
+        b += wl.R * min(wl.ctb, nb) * 4              # block ids
+        b += wl.R * kout * 4                         # level-one indices
+    if wl.publish:
+        b += 128 * wl.din * 2 + wl.B * wl.din * 2 + wl.B * 68
+    if q_step:
+        b += wl.R * wl.H * (128 * 2 + 2)             # bf16 heads before RoPE, raw weights
+    if prefill_publish_groups:
+        b += 128 * wl.din * 2 + wl.B * prefill_publish_groups * (wl.din * 2 + 68)
+    return b
+
+
+def step_flops(wl) -> int:
+    f = score_kernel_flops(wl)
+    if wl.ctb:
+        f += wl.R * min(wl.ctb * wl.cbs, wl.T) * wl.H * FLOP_PER_PAIR_HEAD
+    return f
+
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
+
+
+def timed_steps(steps: int, target: int = 10):
+    """Steps of the timed region whose score launch is timed: about `target`
+    of them, spread evenly and not starting at the first step."""
+    stride = max(1, -(-steps // target))
+    return list(range(stride // 2, steps, stride))[:256]
 
 
 def score_kernel_name(st) -> str:
@@ -121,11 +192,22 @@ def measured_traffic(wl_name):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, min_seconds):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, min_seconds, threads=None):
     """The oracle as it stands, on the host, on the same workload: quantise q,
     score every reachable key, top-k (the key cache is an input and is
     quantised outside the timed region).  Repeats the sample until at least
-    min_seconds of CPU work."""
+    min_seconds of CPU work.  threads: OpenMP thread count (default: all)."""
     import ctypes
 
     import numpy as np
@@ -134,7 +216,10 @@ def cpu_baseline(wl, inp, min_seconds):
     kc, _ = oracle.fp4_quant_rows(inp["k"])
     lib = oracle.lib()
     try:
-        threads = int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+        gomp = ctypes.CDLL("libgomp.so.1")
+        if threads:
+            gomp.omp_set_num_threads(int(threads))
+        threads = int(gomp.omp_get_max_threads())
     except OSError:
         threads = os.cpu_count()
     reps, t0 = 0, time.perf_counter()
@@ -152,6 +237,7 @@ def cpu_baseline(wl, inp, min_seconds):
             break
     del lib
     return {"value": reps * wl.R / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{reps} full step(s) of {wl.name} ({wl.R} queries x {wl.T} keys), "
                       f"{el:.1f} s"}
 
@@ -192,12 +278,12 @@ def main():
         st.step()
     torch.cuda.synchronize()
 
-    # the score launch of every n-th step of the timed region is timed by a
-    # HIP event pair that the library attaches to the launch itself
-    # (hipExtLaunchKernel on the launch stream: the kernel's own start and
-    # end, no marker packets between the kernels of a step)
-    every = max(1, args.event_every)
-    timed = list(range(0, args.steps, every))[:256]
+    # the score launch of about ten steps spread over the timed region is
+    # timed by a HIP event pair that the library attaches to the launch
+    # itself (hipExtLaunchKernel on the launch stream: the kernel's own start
+    # and end, no marker packets between the kernels of a step)
+    timed = (timed_steps(args.steps) if args.event_every <= 0
+             else list(range(0, args.steps, args.event_every))[:256])
     slot = {i: n for n, i in enumerate(timed)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -205,6 +291,20 @@ def main():
         st.step(time_slot=slot.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    score_ms_all = [idx.idx_timing_read(n) for n in slot.values()]
+
+    # after the timed region: the distribution of single-step times, each
+    # step bracketed by an event pair on the stream the steps run on
+    lat_us = []
+    if args.latency_steps > 0:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.latency_steps)]
+        for a, b in ev:
+            a.record()
+            st.step()
+            b.record()
+        torch.cuda.synchronize()
+        lat_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
 
     if args.copy_calibration:
         # known-size reference kernels for the counter calibration: a 256 MiB
@@ -216,17 +316,23 @@ def main():
         torch.cuda.synchronize()
 
     step_s = (t1 - t0) / args.steps
-    score_ms = float(np.mean([idx.idx_timing_read(n) for n in slot.values()]))
-    kb = score_kernel_bytes(wl, st)
-    kf = score_kernel_flops(wl, st)
+    score_ms = float(np.mean(score_ms_all))
+    kb = score_kernel_bytes(wl)
+    kf = score_kernel_flops(wl)
+    groups = wl.S // wl.ratio if args.prefill_publish else 0
+    sb = step_bytes(wl, q_step=args.q_step, prefill_publish_groups=groups)
+    sf = step_flops(wl)
     prefill = wl.S > 1
     if prefill:  # many queries share each key: the contraction bounds the kernel
         roof = {"bound": "mfma", "achieved": kf / (score_ms * 1e-3) / 1e12,
                 "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        step_roof = {"achieved": sf / step_s / 1e12, "flops": sf}
     else:
         roof = {"bound": "hbm", "achieved": kb / (score_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
+        step_roof = {"achieved": sb / step_s / 1e9, "bytes": sb}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    step_roof["frac"] = step_roof["achieved"] / roof["peak"]
     qps = wl.R / step_s
     keys = st.keys_scored()
     # the committed counter summary covers the contiguous layout
@@ -254,12 +360,19 @@ def main():
                    "prefill_publish": bool(args.prefill_publish)},
         "keys_scored_per_s": keys / step_s,
         "score_kernel_ms": score_ms,
+        "score_kernel_ms_dist": percentiles(score_ms_all),
         "score_kernel_timed_steps": len(timed),
+        "step_us_dist": percentiles(lat_us) if lat_us else None,
         "roofline": dict(roof, traffic=traffic, kernel=score_kernel_name(st),
-                         algorithmic_bytes_per_launch=kb, algorithmic_flops_per_launch=kf),
+                         algorithmic_bytes_per_launch=kb, algorithmic_flops_per_launch=kf,
+                         scored_flops_per_launch=scored_flops(wl, st),
+                         traffic_over_algorithmic=(traffic / kb if traffic and not prefill
+                                                   else None),
+                         step=step_roof),
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds,
+                                            threads=args.cpu_threads or None)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

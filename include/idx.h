@@ -80,10 +80,12 @@ idx_status idx_timing_read(int slot, float *ms);
  * scale 2^e with e the smallest integer such that 6*2^e >= amax, each value
  * rounded to the nearest e2m1 point of x/2^e with ties to the even code and
  * its sign kept.
- *   x          device, [n_rows][128] bf16
- *   rows68     device, [n_rows][68] output key rows (layout above)
- *   roundtrip  device, [n_rows][128] bf16 output (dequantised values), or NULL
- * n_rows >= 0 (0 launches nothing).
+ *   x          device, [n_rows][128] bf16, 16-byte aligned
+ *   rows68     device, [n_rows][68] output key rows (layout above), 4-byte
+ *              aligned
+ *   roundtrip  device, [n_rows][128] bf16 output (dequantised values), 16-byte
+ *              aligned, or NULL
+ * n_rows >= 0 (0 launches nothing).  A misaligned pointer gives IDX_EINVAL.
  */
 idx_status idx_fp4_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows68, uint16_t *roundtrip,
                          void *stream);
@@ -124,12 +126,20 @@ idx_status idx_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float w_sc
  * khat the dequantised key row t of sequence b.  The head sum is fp32 in
  * one fixed association: heads [0, H/2) and [H/2, H) are each summed
  * ascending, one fused multiply-add per head starting from +0, and the
- * score is the low sum plus the high sum (one rounded add); the dot
- * products are exact for the documented input range.
- *   q              device, [B*S][H][D] bf16, RoPE already applied
+ * score is the low sum plus the high sum (one rounded add).  Each per-head
+ * dot product is exact (it then matches an exact reference bit for bit)
+ * when, for that head and key, the four block exponent sums e_q,j + e_k,j
+ * of the blocks with a non-zero partial product differ by at most 9: every
+ * block partial is an integer below 4608 in units of 2^(e_q,j + e_k,j - 2),
+ * so the sum then fits fp32's 24 bits.  Block maxima of every row within a
+ * factor 2^4 of each other suffice; outside that the dots are rounded in an
+ * order the matrix core fixes.
+ *   q              device, [B*S][H][D] bf16, RoPE already applied, 16-byte
+ *                  aligned
  *   w              device, [B*S][H] bf16, weights_proj output already
  *                  multiplied by D^-0.5 * H^-0.5
- *   k_cache        device, key rows, sequence stride k_batch_stride_rows >= T
+ *   k_cache        device, key rows, 4-byte aligned, sequence stride
+ *                  k_batch_stride_rows >= T
  *   compress_lens  device, [B*S] int32: row r scores positions t < cl[r]
  *                  (values clamped to [0, T])
  *   cand_blocks    device, [B*S][n_cand] int32 block ids (level two), or
@@ -149,7 +159,12 @@ idx_status idx_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float w_sc
  *                  idx_clear_key_hist clears it once, and every idx_topk
  *                  that consumes it leaves it zeroed again.  idx_topk takes
  *                  it to skip its first pass; positions it does not count
- *                  are -inf there.
+ *                  are -inf there.  The top-k calls check its total: a row
+ *                  whose histogram does not count exactly its scored
+ *                  positions (one filled twice, or by another call) is
+ *                  ranked from its scores alone, more slowly.  A histogram
+ *                  with the right total but taken on other scores is not
+ *                  detected.
  * Requires D == 128 and H in {32, 64}.  T == 0 launches nothing.
  */
 idx_status idx_score(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
@@ -186,7 +201,8 @@ idx_status idx_score_topk(const uint16_t *q, const uint16_t *w, const uint8_t *k
  * physical page block_table[b][t / 64]; slot s of page p is the 68-byte row
  * at k_pages + p * page_stride + 68 * s.
  *   k_pages      device, the page pool
- *   page_stride  bytes between pages, >= 64 * 68
+ *   page_stride  bytes between pages, >= 64 * 68 and a multiple of 4 (the
+ *                pool itself 4-byte aligned)
  *   n_pages      pages in the pool; an id outside [0, n_pages) is never
  *                dereferenced: its keys score as zero rows (idx_score_paged)
  *                or its row is not written (idx_publish_keys_paged)
@@ -268,16 +284,21 @@ size_t idx_topk_workspace_size(int R, int T, int index_topk);
  *   key_hist       device, [R][2048] from idx_score on these scores and
  *                  compress_lens, or NULL (then the first digit is counted
  *                  here).  The call reads it and resets it to zero (in
- *                  stream order), ready for the next idx_score.
+ *                  stream order), ready for the next idx_score.  A row whose
+ *                  histogram total is not its count of positions below
+ *                  compress_lens (clamped to [0, T]) is ranked without it;
+ *                  rows wider than 262144 never use it.
  *   out            device, [R][ld_out] int32, ld_out >= k_out; only the first
  *                  k_out entries of each row are written
+ *   k_out          host, or NULL: receives the row width min(index_topk, T)
+ *                  once the arguments pass their checks
  *   ws, ws_bytes   device workspace of at least idx_topk_workspace_size bytes
  *                  (may be NULL when that size is 0)
  * NaN scores give unspecified results.
  */
 idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t *compress_lens,
                     uint32_t *key_hist, int index_topk, int32_t offset, int32_t *out,
-                    int64_t ld_out, void *ws, size_t ws_bytes, void *stream);
+                    int64_t ld_out, int32_t *k_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * idx_topk_candidates -- idx_topk for a level-two row, whose finite scores
@@ -295,7 +316,8 @@ idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t
  *                these scores and compress_lens, or NULL (then the first
  *                digit is counted here).  Read and reset to zero, as by
  *                idx_topk.
- *   scores, compress_lens, index_topk, offset, out, ld_out: as idx_topk
+ *   scores, compress_lens, index_topk, offset, out, ld_out, k_out: as
+ *                idx_topk
  * Requires T <= 65536, n_cand <= 2048 and n_cand * cand_block_size <= 8192
  * (IDX_EUNSUPPORTED otherwise).
  */
@@ -303,7 +325,7 @@ idx_status idx_topk_candidates(const float *scores, int64_t ld, int R, int T,
                                const int32_t *compress_lens, const int32_t *cand_blocks,
                                int n_cand, int cand_block_size, uint32_t *key_hist,
                                int index_topk, int32_t offset, int32_t *out, int64_t ld_out,
-                               void *stream);
+                               int32_t *k_out, void *stream);
 
 /*
  * Bytes of device workspace idx_select_candidate_blocks needs.
@@ -349,7 +371,7 @@ idx_status idx_select_candidate_blocks(const float *scores, int64_t ld, int R, i
  *   wk         device, [D][Din] bf16
  *   gamma      device, [D] fp32 (k_norm weight)
  *   cos_sin    device, [P][rd/2][2] fp32; every position used must be < P
- *   k_cache    device, written rows must be < Tcap
+ *   k_cache    device, 4-byte aligned; written rows must be < Tcap
  * Requires D == 128, rd even with 0 <= rd <= D, Din >= 1, ratio >= 1.
  */
 idx_status idx_publish_keys(const uint16_t *latent, const uint16_t *wk, const float *gamma,

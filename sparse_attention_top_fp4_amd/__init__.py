@@ -60,9 +60,9 @@ def load_library():
     L.idx_clear_key_hist.argtypes = [P, i32, P]
     L.idx_topk_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_workspace_size.restype = sz
-    L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, sz, P]
+    L.idx_topk.argtypes = [P, i64, i32, i32, P, P, i32, ctypes.c_int32, P, i64, P, P, sz, P]
     L.idx_topk_candidates.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, i32, ctypes.c_int32,
-                                      P, i64, P]
+                                      P, i64, P, P]
     L.idx_select_workspace_size.argtypes = [i32, i32, i32, i32]
     L.idx_select_workspace_size.restype = sz
     L.idx_select_candidate_blocks.argtypes = [P, i64, i32, i32, P, i32, i32, P, i64, P, sz, P]
@@ -408,7 +408,8 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
     (ld_out >= min(index_topk, T)).  workspace: uint8 device tensor of at
     least idx_topk_workspace_size bytes, allocated here when None.
     key_hist: the [R, 2048] histogram idx_score produced for these scores;
-    the call resets it to zero."""
+    the call resets it to zero.  Returns k_out = min(index_topk, T), the
+    width written per row."""
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)
@@ -422,9 +423,12 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if tuple(key_hist.shape) != (R, 2048):
             raise ValueError("key_hist must be [R, 2048]")
+    kout = ctypes.c_int32(-1)
     _check(load_library().idx_topk(_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
                                    _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
-                                   _ptr(workspace), wsb, _stream(stream)), "idx_topk")
+                                   ctypes.byref(kout), _ptr(workspace), wsb, _stream(stream)),
+           "idx_topk")
+    return kout.value
 
 
 def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, index_topk,
@@ -433,7 +437,7 @@ def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, 
     candidate blocks cand_blocks [R, n_cand] int32 (the output of
     idx_select_candidate_blocks); scores [R, ld] float32, out [R, ld_out].
     key_hist: the [R, 2048] histogram idx_score produced for these scores
-    with these candidate blocks; the call resets it to zero."""
+    with these candidate blocks; the call resets it to zero.  Returns k_out."""
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)
@@ -446,12 +450,14 @@ def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, 
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if key_hist.shape != (R, 2048):
             raise ValueError("key_hist must be [R, 2048]")
+    kout = ctypes.c_int32(-1)
     _check(load_library().idx_topk_candidates(_ptr(scores), scores.shape[1], R, T,
                                               _ptr(compress_lens), _ptr(cand_blocks),
                                               cand_blocks.shape[1], cand_block_size,
                                               _ptr(key_hist), index_topk, offset, _ptr(out),
-                                              out.shape[1], _stream(stream)),
+                                              out.shape[1], ctypes.byref(kout), _stream(stream)),
            "idx_topk_candidates")
+    return kout.value
 
 
 def idx_select_workspace_size(R, T, ctb, cbs) -> int:

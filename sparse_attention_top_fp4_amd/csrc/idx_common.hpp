@@ -144,4 +144,9 @@ namespace idx_host {
 inline idx_status launch_status() {
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }
+
+// p is a multiple of `bytes` (a power of two); null counts as aligned.
+inline bool aligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
 }  // namespace idx_host

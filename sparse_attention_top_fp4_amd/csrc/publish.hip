@@ -256,6 +256,8 @@ idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float*
   if ((int64_t)B * G == 0) return IDX_OK;
   if (!latent || !wk || !gamma || !k_cache || (rd > 0 && !cos_sin)) return IDX_EINVAL;
   if (!bt && k_batch_stride_rows < Tcap) return IDX_EINVAL;
+  // rows are written as 4-byte words
+  if (!idx_host::aligned(k_cache, 4) || (bt && (page_stride & 3))) return IDX_EINVAL;
   int64_t max_pos, max_row;
   if (start_pos == 0) {
     max_pos = (int64_t)(G - 1) * ratio;

@@ -156,6 +156,10 @@ extern "C" idx_status idx_fp4_quant(const uint16_t* x, int64_t n_rows, uint8_t* 
   if (n_rows < 0) return IDX_EINVAL;
   if (n_rows == 0) return IDX_OK;
   if (!x || !rows68) return IDX_EINVAL;
+  // x and roundtrip move as 16-byte words, the rows as 4-byte words
+  if (!idx_host::aligned(x, 16) || !idx_host::aligned(roundtrip, 16) ||
+      !idx_host::aligned(rows68, 4))
+    return IDX_EINVAL;
   const int64_t n_blocks = n_rows * 4;
   const int64_t grid = (n_blocks + 255) / 256;
   if (grid > 0x7fffffffLL) return IDX_EINVAL;

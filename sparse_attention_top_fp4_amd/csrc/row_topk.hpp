@@ -101,11 +101,13 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
 // Threshold bin of NB bin counts held in registers, thread i owning the
 // bins [NB - (i+1)*BPT, NB - i*BPT), the top bins first (cnt[j]: bin
 // NB - 1 - i*BPT - j): the bin b with count(bins > b) < krem <=
-// count(bins >= b).  Also returns the count of bin b.
+// count(bins >= b).  Also returns the count of bin b and, when total is
+// given, the sum of all the counts (the same in every thread).
 template <int NT, int NB>
 __device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], uint32_t krem,
                                                 uint32_t* sh, uint32_t* wtot, uint32_t& bin,
-                                                uint32_t& krem_out, uint32_t& bin_count) {
+                                                uint32_t& krem_out, uint32_t& bin_count,
+                                                uint32_t* total = nullptr) {
   constexpr int BPT = NB / NT;
   static_assert(BPT * NT == NB && BPT >= 1, "whole bins per thread");
   const int hi = NB - (int)threadIdx.x * BPT;  // my bins are [hi - BPT, hi)
@@ -113,6 +115,8 @@ __device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], 
 #pragma unroll
   for (int j = 0; j < BPT; ++j) mine += cnt[j];
   const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
+  // the wave totals stay in wtot until the next scan, past a barrier below
+  if (total) *total = waves_total<NT>(wtot);
   uint32_t cum = incl - mine;
   if (cum < krem && krem <= incl) {
 #pragma unroll

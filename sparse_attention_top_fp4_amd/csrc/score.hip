@@ -578,7 +578,10 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
   if ((!q && !q4) || !w || !k_cache || !compress_lens || !scores) return IDX_EINVAL;
-  if (q4 && (reinterpret_cast<uintptr_t>(q4) & 3)) return IDX_EINVAL;
+  // q moves as 16-byte words, quantised rows and key rows as 4-byte words
+  if (!idx_host::aligned(q, 16) || !idx_host::aligned(q4, 4) || !idx_host::aligned(k_cache, 4) ||
+      (pg.bt && (pg.page_stride & 3)))
+    return IDX_EINVAL;
   if (ld < T || (!pg.bt && k_batch_stride_rows < T)) return IDX_EINVAL;
   if (cand_blocks && (n_cand <= 0 || cand_block_size <= 0)) return IDX_EINVAL;
   if (cand_blocks && n_cand > idx::kMaxCand) return IDX_EUNSUPPORTED;
@@ -626,7 +629,9 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
   if (T > idx::kFusedMaxT) return IDX_EUNSUPPORTED;
   if ((int64_t)B * S == 0 || T == 0) return IDX_OK;
   if ((!q && !q4) || !w || !k_cache || !compress_lens || !out) return IDX_EINVAL;
-  if (q4 && (reinterpret_cast<uintptr_t>(q4) & 3)) return IDX_EINVAL;
+  if (!idx_host::aligned(q, 16) || !idx_host::aligned(q4, 4) || !idx_host::aligned(k_cache, 4) ||
+      (pg.bt && (pg.page_stride & 3)))
+    return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
   if ((!pg.bt && k_batch_stride_rows < T) || ld_out < kout || (scores && ld < T))
     return IDX_EINVAL;

@@ -289,21 +289,27 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
       return;
     }
     uint32_t b1 = 0, krem = 0, bcnt = 0;
+    bool hist_ok = false;
     if (hrow) {
       // first digit from the score histogram while the scores are in flight
 #pragma unroll
       for (int j = 0; j < HPT; ++j) hrow[hhi - 1 - j] = 0u;  // ready for the next score call
       for (int i = tid; i < 2048; i += NT) hist[i] = 0u;     // the next digit's histogram
-      // the -inf bin counts the T - (histogram total) unscored positions; T
-      // bounds that, which selects the same bin and remainder (only the
-      // returned count of the -inf bin grows)
+      // the -inf bin counts the T - c unscored positions; T bounds that,
+      // which selects the same bin and remainder (only the returned count of
+      // the -inf bin grows)
 #pragma unroll
       for (int j = 0; j < HPT; ++j)
         if (hhi - 1 - j == (int)kInfBin) hreg[j] += (uint32_t)T;
-      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bcnt);
+      uint32_t total;
+      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bcnt, &total);
+      // a histogram of these scores counts exactly the c positions below
+      // compress_lens; any other total (a stale or doubly filled histogram)
+      // is not used: the row is then ranked from its scores alone
+      hist_ok = total - (uint32_t)T == (uint32_t)c;
     }
     row_vals<EPT>(v, wbase, c, T);
-    if (hrow) {
+    if (hist_ok) {
       row_refine<NT, EPT>(v, hist, true, sh, wtot, b1, krem, bcnt, prefix, shift, need, bin_count);
     } else {
       row_select<NT, EPT>(v, hist, 0xffffffffu, T, kout, sh, wtot, prefix, shift, need,
@@ -405,14 +411,21 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   if (F >= (uint32_t)kout) {
     uint32_t prefix, need, bcnt;
     int shift;
+    bool hist_ok = false;
+    uint32_t b1, krem, bc1;
     if (hrow) {
       // the -inf slots number at most V (only the returned count of the
       // -inf bin grows, as in the rows kernel)
-      uint32_t b1, krem, bc1;
 #pragma unroll
       for (int j = 0; j < HPT; ++j)
         if (hhi - 1 - j == (int)kInfBin) hreg[j] += (uint32_t)V;
-      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bc1);
+      uint32_t total;
+      select_bin_regs<NT, 2048>(hreg, (uint32_t)kout, sh, wtot, b1, krem, bc1, &total);
+      // the level-two histogram counts exactly the F candidate positions
+      // below compress_lens; any other total is not used
+      hist_ok = total - (uint32_t)V == F;
+    }
+    if (hist_ok) {
       row_refine<NT, EPT>(v, hist, true, sh, wtot, b1, krem, bc1, prefix, shift, need, bcnt);
     } else {
       row_select<NT, EPT>(v, hist, 0xffffffffu, V, kout, sh, wtot, prefix, shift, need, bcnt);
@@ -500,6 +513,62 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     for (int i = tid; i < kout; i += NT) orow[i] = dst[i];
   }
   (void)lane;
+}
+
+// ------------------------------------------------ streaming one-row ranking
+// One workgroup ranks a whole row by streaming its scores from memory in
+// tiles of NT*EPT: three digit passes of LDS histograms over the row, then
+// the position-ordered emission tile by tile (block_emit), carrying the
+// counts of selected and tied keys from tile to tile.  Slow (the row is read
+// four times) but needs no histogram from the caller: the split path falls
+// back to it when the histogram it was given does not match the row.
+template <int NT>
+__device__ __noinline__ void stream_rank_row(const float* __restrict__ srow, int T, int c, int kout,
+                                             int32_t offset, int32_t* __restrict__ orow,
+                                             uint32_t* hist, uint32_t* sh, uint32_t* wtot,
+                                             uint32_t (*wcnt)[NT / 64]) {
+  constexpr int EPT = 4, NW = NT / 64, TILE = NT * EPT;
+  const int wb0 = (int)(threadIdx.x >> 6) * 64 * EPT;
+  uint32_t prefix = 0, krem = (uint32_t)kout;
+  for (int pass = 0; pass < 3; ++pass) {
+    uint32_t key[EPT];
+    {
+      const int nb = pass_bins(pass);
+      for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
+      if (threadIdx.x == 0) sh[2] = 0u;
+      __syncthreads();
+      for (int base = 0; base < T; base += TILE) {
+        load_keys<EPT>(srow, base + wb0, T, c, key);
+        hist_pass<EPT>(key, pass, prefix, hist, &sh[2]);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0 && sh[2])
+        hist[(kKeyNegInf >> pass_shift(pass)) & (uint32_t)(nb - 1)] += sh[2];
+      __syncthreads();
+      uint32_t bin, k2;
+      select_bin<NT>(hist, nb, krem, 0xffffffffu, 0u, sh, wtot, bin, k2);
+      prefix = extend_prefix(prefix, pass, bin);
+      krem = k2;
+    }
+  }
+  // keys above `prefix` are taken, and of those equal to it the `krem` at
+  // the lowest positions
+  uint32_t ob = 0, eqb = 0;
+  for (int base = 0; base < T; base += TILE) {
+    uint32_t key[EPT];
+    load_keys<EPT>(srow, base + wb0, T, c, key);
+    block_emit<NW, EPT>(key, base + wb0, prefix, krem, ob, eqb, c, offset, orow,
+                        (uint32_t)kout, wcnt);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      gt += wcnt[0][i];
+      eq += wcnt[1][i];
+    }
+    __syncthreads();  // every thread has read this tile's counts
+    ob += gt + (krem > eqb ? (eq < krem - eqb ? eq : krem - eqb) : 0u);
+    eqb += eq;
+  }
 }
 
 // ---------------------------------------- split path (score histogram given)
@@ -598,8 +667,9 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
 constexpr int kSplitBThreads = IDX_SPLIT_B_THREADS;
 
 __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
-    int T, const int32_t* __restrict__ cl_arr, uint32_t* __restrict__ key_hist, int kout,
-    int32_t offset, int32_t* __restrict__ out, int64_t ld_out, const uint32_t* __restrict__ ws) {
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
+    int64_t ld_out, const uint32_t* __restrict__ ws) {
   constexpr int NT = kSplitBThreads, NW = NT / 64;
   // sel[padded nwords] eq[padded nwords] ckey[cap] cpos[cap]; mask word w
   // lives at w + w/32, so threads owning consecutive runs of words hit
@@ -622,6 +692,23 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   uint32_t* ckey = dyn + 2 * nwp;
   uint32_t* cpos = ckey + kSplitCandCap;
   const int nreg = (int)L.nparts * kPartNW;
+
+  // The score histogram counts exactly the c positions below compress_lens
+  // when it comes from idx_score on these scores.  Any other total (a stale
+  // or doubly filled histogram) made kernel A's threshold meaningless: the
+  // row is then ranked from its scores alone.
+  {
+    __shared__ uint32_t wcnt[2][NW];
+    uint32_t hs = 0;
+    for (int i = tid; i < 2048; i += NT) hs += key_hist[(int64_t)r * 2048 + i];
+    const uint32_t htotal = block_sum<NT>(hs, wtot);
+    if (htotal != (uint32_t)c) {
+      stream_rank_row<NT>(scores + (int64_t)r * ld, T, c, kout, offset,
+                          out + (int64_t)r * ld_out, hist, sh, wtot, wcnt);
+      for (int i = tid; i < 2048; i += NT) key_hist[(int64_t)r * 2048 + i] = 0u;
+      return;
+    }
+  }
 
   // list counts (at most 256 regions) and the search state first
   static_assert(kSplitMaxT / kPart * kPartNW <= NT, "one region per thread");
@@ -1079,8 +1166,8 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
                        dim3(idx::kPartNW * 64), 0, st, scores, ld, T, cl, key_hist, kout,
                        (uint32_t*)ws);
     hipLaunchKernelGGL(idx::topk_split_b_kernel, dim3((unsigned)R), dim3(idx::kSplitBThreads),
-                       split_b_lds(T), st,
-                       T, cl, key_hist, kout, offset, out, ld_out, (const uint32_t*)ws);
+                       split_b_lds(T), st, scores, ld, T, cl, key_hist, kout, offset, out, ld_out,
+                       (const uint32_t*)ws);
     return idx_host::launch_status();
   }
   if (R > 65535) return IDX_EUNSUPPORTED;
@@ -1093,16 +1180,18 @@ idx_status topk_launch(const float* scores, int64_t ld, int R, int T, const int3
   hipLaunchKernelGGL(idx::zero_words_kernel, dim3((unsigned)zg), dim3(256), 0, st, w, zero_n);
   const dim3 grid((unsigned)n_chunks(T), (unsigned)R);
   const dim3 blk(idx::kChunkNW * 64);
-  if (!key_hist)
-    hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<0>, grid, blk, 0, st, scores, ld, T, cl,
-                       key_hist, kout, w, rw);
-  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<1>, grid, blk, 0, st, scores, ld, T, cl,
-                     key_hist, kout, w, rw);
-  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<2>, grid, blk, 0, st, scores, ld, T, cl,
-                     key_hist, kout, w, rw);
-  hipLaunchKernelGGL(idx::topk_chunk_count_kernel, grid, blk, 0, st, scores, ld, T, cl, key_hist,
+  // the chunked path counts its own first digit, so a score histogram (which
+  // it cannot check against the row without another pass) is only reset
+  const uint32_t* h1 = nullptr;
+  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<0>, grid, blk, 0, st, scores, ld, T, cl, h1,
                      kout, w, rw);
-  hipLaunchKernelGGL(idx::topk_chunk_emit_kernel, grid, blk, 0, st, scores, ld, T, cl, key_hist,
+  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<1>, grid, blk, 0, st, scores, ld, T, cl, h1,
+                     kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_hist_kernel<2>, grid, blk, 0, st, scores, ld, T, cl, h1,
+                     kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_count_kernel, grid, blk, 0, st, scores, ld, T, cl, h1,
+                     kout, w, rw);
+  hipLaunchKernelGGL(idx::topk_chunk_emit_kernel, grid, blk, 0, st, scores, ld, T, cl, h1,
                      kout, offset, out, ld_out, (const uint32_t*)w, rw);
   if (key_hist) zero_hist(key_hist, R, st);
   return idx_host::launch_status();
@@ -1126,12 +1215,16 @@ extern "C" size_t idx_topk_workspace_size(int R, int T, int index_topk) {
 extern "C" idx_status idx_topk(const float* scores, int64_t ld, int R, int T,
                                const int32_t* compress_lens, uint32_t* key_hist,
                                int index_topk, int32_t offset, int32_t* out, int64_t ld_out,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               int32_t* k_out, void* ws, size_t ws_bytes, void* stream) {
   if (R < 0 || T < 0 || index_topk <= 0) return IDX_EINVAL;
-  if (R == 0 || T == 0) return IDX_OK;
-  if (!scores || !compress_lens || !out) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
+  if (R == 0 || T == 0) {
+    if (k_out) *k_out = kout;
+    return IDX_OK;
+  }
+  if (!scores || !compress_lens || !out) return IDX_EINVAL;
   if (ld < T || ld_out < kout) return IDX_EINVAL;
+  if (k_out) *k_out = kout;
   return topk_launch(scores, ld, R, T, compress_lens, key_hist, index_topk, offset, out, ld_out,
                      ws, ws_bytes, (hipStream_t)stream);
 }
@@ -1174,14 +1267,18 @@ extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R
                                           const int32_t* compress_lens, const int32_t* cand_blocks,
                                           int n_cand, int cand_block_size, uint32_t* key_hist,
                                           int index_topk, int32_t offset, int32_t* out,
-                                          int64_t ld_out, void* stream) {
+                                          int64_t ld_out, int32_t* k_out, void* stream) {
   if (R < 0 || T < 0 || index_topk <= 0 || n_cand <= 0 || cand_block_size <= 0) return IDX_EINVAL;
-  if (R == 0 || T == 0) return IDX_OK;
-  if (!scores || !compress_lens || !cand_blocks || !out) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
+  if (R == 0 || T == 0) {
+    if (k_out) *k_out = kout;
+    return IDX_OK;
+  }
+  if (!scores || !compress_lens || !cand_blocks || !out) return IDX_EINVAL;
   if (ld < T || ld_out < kout) return IDX_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   if (index_topk >= T) {
+    if (k_out) *k_out = kout;
     hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T,
                        compress_lens, offset, out, ld_out);
     if (key_hist) zero_hist(key_hist, R, st);
@@ -1189,6 +1286,7 @@ extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R
   }
   const int64_t V = (int64_t)n_cand * cand_block_size;
   if (T > idx::kCandMaxT || n_cand > idx::kCandMaxIds || V > 8192) return IDX_EUNSUPPORTED;
+  if (k_out) *k_out = kout;
   // few rows, each a latency chain: many threads per row, few keys each
   if (V <= 2048)
     hipLaunchKernelGGL((idx::topk_cand_kernel<256, 8>), dim3((unsigned)R), dim3(256), 0, st,

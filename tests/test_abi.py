@@ -69,13 +69,13 @@ def test_score_rejects_bad_arguments_without_launching(lib):
 def test_topk_and_select_reject_bad_arguments(lib):
     P = ctypes.c_void_p
     d = P(0x1000)
-    assert lib.idx_topk(d, 8, 1, 8, d, None, 0, 0, d, 8, None, 0, None) == IDX_EINVAL  # topk 0
-    assert lib.idx_topk(d, 7, 1, 8, d, None, 4, 0, d, 8, None, 0, None) == IDX_EINVAL  # ld < T
-    assert lib.idx_topk(d, 8, 1, 8, d, None, 4, 0, d, 3, None, 0, None) == IDX_EINVAL  # ld_out < k
-    assert lib.idx_topk(None, 8, 0, 8, None, None, 4, 0, None, 8, None, 0, None) == IDX_OK  # R = 0
+    assert lib.idx_topk(d, 8, 1, 8, d, None, 0, 0, d, 8, None, None, 0, None) == IDX_EINVAL  # topk 0
+    assert lib.idx_topk(d, 7, 1, 8, d, None, 4, 0, d, 8, None, None, 0, None) == IDX_EINVAL  # ld < T
+    assert lib.idx_topk(d, 8, 1, 8, d, None, 4, 0, d, 3, None, None, 0, None) == IDX_EINVAL  # ld_out < k
+    assert lib.idx_topk(None, 8, 0, 8, None, None, 4, 0, None, 8, None, None, 0, None) == IDX_OK  # R = 0
     need = lib.idx_topk_workspace_size(4, 100000, 2048)
     assert need > 0
-    assert lib.idx_topk(d, 100000, 4, 100000, d, None, 2048, 0, d, 2048, None, 0, None) == IDX_EINVAL
+    assert lib.idx_topk(d, 100000, 4, 100000, d, None, 2048, 0, d, 2048, None, None, 0, None) == IDX_EINVAL
     assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 0, 4, d, 2, None, 0, None) == IDX_EINVAL
     assert lib.idx_select_candidate_blocks(d, 8, 1, 8, d, 2, 4, d, 1, d, 1 << 20,
                                            None, None) == IDX_EINVAL  # ld_ids < min(ctb, nb)
@@ -151,15 +151,56 @@ def test_fused_score_topk_rejects_bad_arguments(lib):
 def test_candidate_topk_rejects_bad_arguments(lib):
     d = ctypes.c_void_p(0x1000)
     assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, None, 2048, 0, d, 2048,
-                                   None) == IDX_EUNSUPPORTED  # row wider than the bit map
+                                   None, None) == IDX_EUNSUPPORTED  # row wider than the bit map
     assert lib.idx_topk_candidates(d, 65536, 1, 65536, d, d, 65, 128, None, 2048, 0, d, 2048,
-                                   None) == IDX_EUNSUPPORTED  # more than 8192 candidate slots
+                                   None, None) == IDX_EUNSUPPORTED  # more than 8192 candidate slots
     assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 0, 4, None, 4, 0, d, 4,
-                                   None) == IDX_EINVAL
+                                   None, None) == IDX_EINVAL
     assert lib.idx_topk_candidates(d, 8, 1, 8, d, d, 2, 4, None, 4, 0, d, 3,
-                                   None) == IDX_EINVAL
+                                   None, None) == IDX_EINVAL
     assert lib.idx_topk_candidates(None, 8, 0, 8, None, None, 2, 4, None, 4, 0, None, 4,
-                                   None) == IDX_OK
+                                   None, None) == IDX_OK
+
+
+def test_topk_reports_k_out(lib):
+    """idx_topk and idx_topk_candidates write the row width min(index_topk, T)
+    to the host k_out once their arguments pass (no device work here: R = 0)."""
+    k = ctypes.c_int32(-1)
+    assert lib.idx_topk(None, 8, 0, 8, None, None, 4, 0, None, 8, ctypes.byref(k), None, 0,
+                        None) == IDX_OK and k.value == 4
+    assert lib.idx_topk(None, 8, 0, 8, None, None, 20, 0, None, 8, ctypes.byref(k), None, 0,
+                        None) == IDX_OK and k.value == 8
+    k.value = -1
+    assert lib.idx_topk(ctypes.c_void_p(0x1000), 7, 1, 8, ctypes.c_void_p(0x1000), None, 4, 0,
+                        ctypes.c_void_p(0x1000), 8, ctypes.byref(k), None, 0,
+                        None) == IDX_EINVAL and k.value == -1  # rejected: untouched
+    assert lib.idx_topk_candidates(None, 8, 0, 8, None, None, 2, 4, None, 3, 0, None, 4,
+                                   ctypes.byref(k), None) == IDX_OK and k.value == 3
+
+
+def test_unaligned_pointers_are_rejected(lib):
+    """q is read as 16-byte words (idx_score, idx_score_topk), x and the round
+    trip of idx_fp4_quant likewise, key rows as 4-byte words: misaligned
+    pointers give IDX_EINVAL before any launch."""
+    a16, odd8, odd2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    # idx_fp4_quant(x, n_rows, rows68, roundtrip, stream)
+    assert lib.idx_fp4_quant(odd8, 1, a16, None, None) == IDX_EINVAL
+    assert lib.idx_fp4_quant(a16, 1, odd2, None, None) == IDX_EINVAL
+    assert lib.idx_fp4_quant(a16, 1, a16, odd8, None) == IDX_EINVAL
+
+    def score(q=a16, kc=a16):
+        return lib.idx_score(q, a16, kc, 8, 1, 1, 64, 128, 8, a16, None, 0, 0, a16, 8, None, None)
+
+    def fused(q=a16, kc=a16):
+        return lib.idx_score_topk(q, a16, kc, 8, 1, 1, 64, 128, 8, a16, 4, 0, a16, 4, None, 0,
+                                  None)
+
+    for call in (score, fused):
+        assert call(q=odd8) == IDX_EINVAL
+        assert call(kc=odd2) == IDX_EINVAL
+    # publish writes 4-byte words of the rows
+    assert lib.idx_publish_keys(a16, a16, a16, a16, 10, 1, 1, 512, 128, 64, 1e-6, 7, 4, odd2, 8,
+                                8, None) == IDX_EINVAL
 
 
 def test_paged_entry_points_reject_bad_page_maps(lib):
