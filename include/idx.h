@@ -301,6 +301,27 @@ idx_status idx_topk(const float *scores, int64_t ld, int R, int T, const int32_t
                     int64_t ld_out, int32_t *k_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * idx_topk_noalloc -- idx_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors as idx_topk, without the
+ * workspace: it comes from a static device array of the library, of
+ * idx_topk_noalloc_max_workspace() bytes (16 MiB), one per GPU the library
+ * runs on, held until the process ends.  A call whose idx_topk workspace
+ * would exceed it returns IDX_EUNSUPPORTED before any launch (e.g. more
+ * than 7 rows of 262144 positions).  The call allocates nothing.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and give undefined results;
+ * calls in one stream's order are safe.  The kernels initialise whatever
+ * part of the array they read, so a call does not depend on the previous
+ * contents.
+ */
+idx_status idx_topk_noalloc(const float *scores, int64_t ld, int R, int T,
+                            const int32_t *compress_lens, uint32_t *key_hist, int index_topk,
+                            int32_t offset, int32_t *out, int64_t ld_out, int32_t *k_out,
+                            void *stream);
+size_t idx_topk_noalloc_max_workspace(void);
+
+/*
  * idx_topk_candidates -- idx_topk for a level-two row, whose finite scores
  * all lie in its candidate blocks (as idx_score with the same cand_blocks
  * writes them; [IDX, forward: the level-two mask, then the final topk]).

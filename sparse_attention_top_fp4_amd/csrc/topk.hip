@@ -36,6 +36,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 namespace idx {
 
@@ -1297,4 +1298,55 @@ extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R
                        scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size,
                        key_hist, kout, offset, out, ld_out);
   return idx_host::launch_status();
+}
+
+// ------------------------------------------------- allocation-free top-k
+// For callers that cannot allocate device memory: the workspace of
+// idx_topk comes from this file-scope array instead of the caller.  Each
+// device the library runs on holds its own copy until the process ends; its
+// device address is looked up once per device (hipGetSymbolAddress) and
+// only that address is handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+idx_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return IDX_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return IDX_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return IDX_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return IDX_OK;
+}
+}  // namespace
+
+extern "C" size_t idx_topk_noalloc_max_workspace(void) { return kScratchBytes; }
+
+extern "C" idx_status idx_topk_noalloc(const float* scores, int64_t ld, int R, int T,
+                                       const int32_t* compress_lens, uint32_t* key_hist,
+                                       int index_topk, int32_t offset, int32_t* out,
+                                       int64_t ld_out, int32_t* k_out, void* stream) {
+  if (R < 0 || T < 0 || index_topk <= 0) return IDX_EINVAL;
+  const size_t need = topk_ws_bytes(R, T, index_topk);
+  if (need > kScratchBytes) return IDX_EUNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0 && R > 0 && T > 0 && scores && compress_lens && out) {
+    const idx_status e = scratch_address(&ws);
+    if (e != IDX_OK) return e;
+  }
+  return idx_topk(scores, ld, R, T, compress_lens, key_hist, index_topk, offset, out, ld_out,
+                  k_out, ws, ws ? kScratchBytes : 0, stream);
 }
