@@ -18,7 +18,7 @@ Prints one JSON line (rank 0, N = 1):
   roofline      the score kernel: algorithmic bytes (decode: keys, fp4 query
                 heads, weights) or fp4 flops (prefill: every causal pair)
                 per launch / its mean duration from HIP event pairs attached
-                to about ten launches of the timed region on the launch
+                to eight launches of the timed region on the launch
                 stream (hipExtLaunchKernel), against 8 TB/s or 10.1 PFLOP/s;
                 roofline.step: the whole step's algorithmic bytes or flops
                 over ms_per_step against the same peak
@@ -51,8 +51,8 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="workload id 0..4 (1 = batched decode)")
     ap.add_argument("--event-every", type=int, default=0,
                     help="time the score launch with HIP events on every n-th step of the "
-                         "timed region; 0 (default): about ten steps spread over it (a timed "
-                         "launch costs the host about 20 us)")
+                         "timed region; 0 (default): eight steps spread over it (a timed "
+                         "launch costs the host about 30 us)")
     ap.add_argument("--latency-steps", type=int, default=50,
                     help="after the timed region, this many single steps each bracketed by "
                          "an event pair, for the p10/p50/p90 step time")
@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--prefill-publish", action="store_true",
                     help="prefill workloads: the step first publishes the S / ratio keys of "
                          "the prompt (key publish of many groups)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the chip's ceilings (streaming read over grid sizes, "
+                         "fp4 matrix-core loop) and print them as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -154,11 +157,14 @@ def percentiles(xs):
             "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
 
-def timed_steps(steps: int, target: int = 10):
-    """Steps of the timed region whose score launch is timed: about `target`
-    of them, spread evenly and not starting at the first step."""
-    stride = max(1, -(-steps // target))
-    return list(range(stride // 2, steps, stride))[:256]
+def timed_steps(steps: int, target: int = 8):
+    """Steps of the timed region whose score launch is timed: `target` of
+    them (all steps when fewer), spread evenly over the region and not
+    starting at its first step.  A timed launch costs the host about 30 us,
+    so timing fewer launches disturbs the region less."""
+    if steps <= target:
+        return list(range(steps))
+    return sorted({int(round((i + 0.5) * steps / target)) for i in range(target)})
 
 
 def score_kernel_name(st) -> str:
@@ -242,6 +248,38 @@ def cpu_baseline(wl, inp, min_seconds, threads=None):
                       f"{el:.1f} s"}
 
 
+STREAM_GRIDS = (256, 512, 1024, 2048, 4096)
+
+
+def measure_ceilings(nbytes, reps=8):
+    """Streaming-read ceiling over `nbytes` (read from several copies in
+    turn, so the 256 MB last-level cache does not serve them) for each grid
+    size, and the fp4 matrix-core ceiling.  Best and median of `reps`."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_top_fp4_amd as idx
+    n = -(-nbytes // 16) * 4  # int32 words, a multiple of 16 bytes
+    copies = max(2, math.ceil(3 * LLC_BYTES / (n * 4)))
+    bufs = [torch.ones(n, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.empty(max(STREAM_GRIDS) * 256, dtype=torch.int32, device="cuda")
+    stream = {}
+    for g in STREAM_GRIDS:
+        ms = [idx.idx_probe_stream_read(bufs[i % copies], g, sink) for i in range(reps + 1)][1:]
+        gbs = [n * 4 / (m * 1e-3) / 1e9 for m in ms]
+        stream[str(g)] = {"best_GBs": max(gbs), "median_GBs": float(np.median(gbs))}
+    best = max(stream.values(), key=lambda v: v["best_GBs"])
+    del bufs
+    fsink = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
+    mf = []
+    for g in (256, 512):
+        runs = [idx.idx_probe_mfma_fp4(g, 4000, fsink) for _ in range(4)][1:]
+        mf.append({"grid": g, "best_TFLOPs": max(f / (m * 1e-3) / 1e12 for f, m in runs)})
+    return {"stream_read": {"bytes": n * 4, "copies": copies, "by_grid": stream,
+                            "best_GBs": best["best_GBs"], "median_GBs": best["median_GBs"]},
+            "mfma_fp4": {"by_grid": mf, "best_TFLOPs": max(m["best_TFLOPs"] for m in mf)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -257,6 +295,10 @@ def main():
 
     idx.load_library()
     wl = workload(args.config)
+    if args.ceilings:
+        print(json.dumps({"ceilings": measure_ceilings(wl.B * wl.T * 68),
+                          "workload_bytes_from": wl.name}), flush=True)
+        return
     t_gen = time.perf_counter()
     inp = generate(wl)
     t_gen = time.perf_counter() - t_gen
@@ -274,17 +316,20 @@ def main():
                      q_step=args.q_step, publish=publish)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        st.step()
-    torch.cuda.synchronize()
-
-    # the score launch of about ten steps spread over the timed region is
-    # timed by a HIP event pair that the library attaches to the launch
-    # itself (hipExtLaunchKernel on the launch stream: the kernel's own start
-    # and end, no marker packets between the kernels of a step)
     timed = (timed_steps(args.steps) if args.event_every <= 0
              else list(range(0, args.steps, args.event_every))[:256])
     slot = {i: n for n, i in enumerate(timed)}
+    # the warm-up also times one launch into every event pair, so the pairs
+    # exist before the timed region (creating one costs the host more than a
+    # step)
+    for i in range(max(args.warmup, len(timed))):
+        st.step(time_slot=i if i < len(timed) else None)
+    torch.cuda.synchronize()
+
+    # the score launch of eight steps spread over the timed region is timed
+    # by a HIP event pair that the library attaches to the launch itself
+    # (hipExtLaunchKernel on the launch stream: the kernel's own start and
+    # end, no marker packets between the kernels of a step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

@@ -78,6 +78,8 @@ def load_library():
     L.idx_score_q4.argtypes = L.idx_score.argtypes
     L.idx_score_topk_q4.argtypes = L.idx_score_topk.argtypes
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
+    L.idx_probe_stream_read.argtypes = [P, i64, i32, P, ctypes.POINTER(f32), P]
+    L.idx_probe_mfma_fp4.argtypes = [i32, i32, P, ctypes.POINTER(f64), ctypes.POINTER(f32), P]
     L.idx_timing_arm.argtypes = [i32]
     L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
     for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
@@ -85,7 +87,8 @@ def load_library():
                  "idx_select_candidate_blocks",
                  "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read",
                  "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged",
-                 "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4"):
+                 "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
+                 "idx_probe_stream_read", "idx_probe_mfma_fp4"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -95,6 +98,46 @@ def _check(status: int, what: str):
     if status != 0:
         msg = load_library().idx_status_string(status).decode()
         raise IdxError(f"{what}: {msg}")
+
+
+class BoundCall:
+    """One library call with every argument but the stream marshalled once:
+    calling it issues the call again on the given stream (a raw hipStream_t
+    handle, or None for torch's current stream) and raises on a non-zero
+    status.  For loops that repeat the same calls on the same buffers, where
+    re-checking and re-converting the tensors would cost more host time than
+    the kernels take."""
+
+    __slots__ = ("_fn", "_args", "_what", "_keep")
+
+    def __init__(self, fn, args, what, keep=()):
+        # keep: tensors the call's pointers refer to that the caller does not
+        # hold itself (a workspace allocated by the wrapper)
+        self._fn, self._args, self._what, self._keep = fn, args, what, keep
+
+    def __call__(self, stream=None):
+        if stream is None:
+            stream = _stream(None)
+        st = self._fn(*self._args, stream)
+        if st:
+            _check(st, self._what)
+
+
+def _issue(name, args, stream, what, bind, keep=()):
+    """Call library function `name` with `args` and the stream, or (bind)
+    return the call as a BoundCall without issuing it.  A bound call holds
+    raw device pointers: the caller keeps the tensors alive while it uses
+    the call."""
+    fn = getattr(load_library(), name)
+    if bind:
+        return BoundCall(fn, tuple(args), what, keep)
+    _check(fn(*args, _stream(stream)), what)
+    return None
+
+
+def current_stream_handle():
+    """The raw handle of torch's current stream, for BoundCall."""
+    return _stream(None)
 
 
 def _torch():
@@ -132,7 +175,7 @@ def _bf16_types():
     return (torch.bfloat16, torch.uint16, torch.int16)
 
 
-def idx_fp4_quant(x, rows68, roundtrip=None, stream=None):
+def idx_fp4_quant(x, rows68, roundtrip=None, stream=None, bind=False):
     """x [n, 128] bf16 -> rows68 [n, 68] uint8 (+ roundtrip [n, 128] bf16)."""
     torch = _torch()
     _dev(x, "x", _bf16_types())
@@ -144,12 +187,12 @@ def idx_fp4_quant(x, rows68, roundtrip=None, stream=None):
         _dev(roundtrip, "roundtrip", _bf16_types())
         if roundtrip.numel() != x.numel():
             raise ValueError("roundtrip must match x")
-    _check(load_library().idx_fp4_quant(_ptr(x), n, _ptr(rows68), _ptr(roundtrip),
-                                        _stream(stream)), "idx_fp4_quant")
+    return _issue("idx_fp4_quant", (_ptr(x), n, _ptr(rows68), _ptr(roundtrip)), stream,
+                  "idx_fp4_quant", bind)
 
 
 def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
-              cand_block_size=0, key_hist=None, stream=None):
+              cand_block_size=0, key_hist=None, stream=None, bind=False):
     """q [B*S, H, 128] bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8,
     compress_lens [B*S] int32, scores [B*S, ld] float32 (ld >= T),
     cand_blocks [B*S, n_cand] int32 or None, key_hist [B*S, 2048] int32
@@ -175,14 +218,14 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if tuple(key_hist.shape) != (R, 2048):
             raise ValueError("key_hist must be [B*S, 2048]")
-    _check(load_library().idx_score(_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D,
+    return _issue("idx_score", (_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
-                                    _ptr(key_hist), _stream(stream)), "idx_score")
+                                    _ptr(key_hist)), stream, "idx_score", bind)
 
 
 def idx_score_q4(q_rows, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
-                 cand_block_size=0, key_hist=None, stream=None):
+                 cand_block_size=0, key_hist=None, stream=None, bind=False):
     """idx_score with the query heads already quantised: q_rows [B*S, H, 68]
     uint8 (from idx_q_rope_quant or idx_fp4_quant)."""
     torch = _torch()
@@ -206,14 +249,14 @@ def idx_score_q4(q_rows, w, k_cache, B, S, T, compress_lens, scores, cand_blocks
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if tuple(key_hist.shape) != (R, 2048):
             raise ValueError("key_hist must be [B*S, 2048]")
-    _check(load_library().idx_score_q4(_ptr(q_rows), _ptr(w), _ptr(k_cache), k_cache.shape[1], B,
+    return _issue("idx_score_q4", (_ptr(q_rows), _ptr(w), _ptr(k_cache), k_cache.shape[1], B,
                                        S, H, 128, T, _ptr(compress_lens), _ptr(cand_blocks),
                                        n_cand, cand_block_size, _ptr(scores), scores.shape[1],
-                                       _ptr(key_hist), _stream(stream)), "idx_score_q4")
+                                       _ptr(key_hist)), stream, "idx_score_q4", bind)
 
 
 def idx_score_topk_q4(q_rows, w, k_cache, B, S, T, compress_lens, index_topk, offset, out,
-                      scores=None, stream=None):
+                      scores=None, stream=None, bind=False):
     """idx_score_topk with the query heads already quantised: q_rows
     [B*S, H, 68] uint8."""
     torch = _torch()
@@ -233,15 +276,15 @@ def idx_score_topk_q4(q_rows, w, k_cache, B, S, T, compress_lens, index_topk, of
         if scores.shape[0] != R:
             raise ValueError("scores must be [B*S, ld]")
         ld = scores.shape[1]
-    _check(load_library().idx_score_topk_q4(_ptr(q_rows), _ptr(w), _ptr(k_cache),
+    return _issue("idx_score_topk_q4", (_ptr(q_rows), _ptr(w), _ptr(k_cache),
                                             k_cache.shape[1], B, S, H, 128, T,
                                             _ptr(compress_lens), index_topk, offset, _ptr(out),
-                                            out.shape[1], _ptr(scores), ld, _stream(stream)),
-           "idx_score_topk_q4")
+                                            out.shape[1], _ptr(scores), ld), stream,
+                  "idx_score_topk_q4", bind)
 
 
 def idx_score_topk(q, w, k_cache, B, S, T, compress_lens, index_topk, offset, out, scores=None,
-                   stream=None):
+                   stream=None, bind=False):
     """idx_score then idx_topk in one launch, for T <= 8192: q [B*S, H, 128]
     bf16, w [B*S, H] bf16, k_cache [B, Tcap, 68] uint8, compress_lens [B*S]
     int32, out [B*S, ld_out] int32 (ld_out >= min(index_topk, T)); scores
@@ -263,10 +306,10 @@ def idx_score_topk(q, w, k_cache, B, S, T, compress_lens, index_topk, offset, ou
         if scores.shape[0] != R:
             raise ValueError("scores must be [B*S, ld]")
         ld = scores.shape[1]
-    _check(load_library().idx_score_topk(_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S,
+    return _issue("idx_score_topk", (_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S,
                                          H, D, T, _ptr(compress_lens), index_topk, offset,
-                                         _ptr(out), out.shape[1], _ptr(scores), ld,
-                                         _stream(stream)), "idx_score_topk")
+                                         _ptr(out), out.shape[1], _ptr(scores), ld), stream,
+                  "idx_score_topk", bind)
 
 
 def _pages(k_pages, block_table, B):
@@ -283,7 +326,7 @@ def _pages(k_pages, block_table, B):
 
 
 def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, cand_blocks=None,
-                    cand_block_size=0, key_hist=None, stream=None):
+                    cand_block_size=0, key_hist=None, stream=None, bind=False):
     """idx_score on a paged key cache: row t of sequence b in slot t % 64 of
     page block_table[b, t // 64] of k_pages."""
     torch = _torch()
@@ -307,15 +350,15 @@ def idx_score_paged(q, w, k_pages, block_table, B, S, T, compress_lens, scores, 
             raise ValueError("cand_blocks must have B*S rows")
         n_cand = cand_blocks.shape[1]
     ps, npg, bts = _pages(k_pages, block_table, B)
-    _check(load_library().idx_score_paged(_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
+    return _issue("idx_score_paged", (_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
                                           _ptr(block_table), bts, B, S, H, D, T,
                                           _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                           cand_block_size, _ptr(scores), scores.shape[1],
-                                          _ptr(key_hist), _stream(stream)), "idx_score_paged")
+                                          _ptr(key_hist)), stream, "idx_score_paged", bind)
 
 
 def idx_score_topk_paged(q, w, k_pages, block_table, B, S, T, compress_lens, index_topk, offset,
-                         out, scores=None, stream=None):
+                         out, scores=None, stream=None, bind=False):
     """idx_score_topk on a paged key cache (pages as for idx_score_paged)."""
     torch = _torch()
     _dev(q, "q", _bf16_types(), 3)
@@ -334,15 +377,15 @@ def idx_score_topk_paged(q, w, k_pages, block_table, B, S, T, compress_lens, ind
             raise ValueError("scores must be [B*S, ld]")
         ld = scores.shape[1]
     ps, npg, bts = _pages(k_pages, block_table, B)
-    _check(load_library().idx_score_topk_paged(_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
+    return _issue("idx_score_topk_paged", (_ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
                                                _ptr(block_table), bts, B, S, H, D, T,
                                                _ptr(compress_lens), index_topk, offset,
-                                               _ptr(out), out.shape[1], _ptr(scores), ld,
-                                               _stream(stream)), "idx_score_topk_paged")
+                                               _ptr(out), out.shape[1], _ptr(scores), ld), stream,
+                  "idx_score_topk_paged", bind)
 
 
 def idx_publish_keys_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_pages,
-                           block_table, Tcap, rd=64, stream=None):
+                           block_table, Tcap, rd=64, stream=None, bind=False):
     """idx_publish_keys into a paged key cache of Tcap rows per sequence."""
     torch = _torch()
     _dev(latent, "latent", _bf16_types(), 3)
@@ -354,15 +397,15 @@ def idx_publish_keys_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_
     if wk.shape[1] != Din or gamma.shape[0] != D:
         raise ValueError("shape mismatch in idx_publish_keys_paged")
     ps, npg, bts = _pages(k_pages, block_table, B)
-    _check(load_library().idx_publish_keys_paged(_ptr(latent), _ptr(wk), _ptr(gamma),
+    return _issue("idx_publish_keys_paged", (_ptr(latent), _ptr(wk), _ptr(gamma),
                                                  _ptr(cos_sin), cos_sin.shape[0], B, G, Din, D,
                                                  rd, eps, start_pos, ratio, _ptr(k_pages), ps,
-                                                 npg, _ptr(block_table), bts, Tcap,
-                                                 _stream(stream)), "idx_publish_keys_paged")
+                                                 npg, _ptr(block_table), bts, Tcap), stream,
+                  "idx_publish_keys_paged", bind)
 
 
 def idx_q_rope_quant(q, w_raw, w_scale, cos_sin, start_pos, S, q_rows, w_out,
-                     q_roundtrip=None, rd=64, stream=None):
+                     q_roundtrip=None, rd=64, stream=None, bind=False):
     """Query RoPE + fp4 quantise + weight scaling: q [B*S, H, 128] bf16
     (before RoPE), w_raw [B*S, H] bf16, cos_sin [P, rd/2, 2] float32, rows
     r = b*S + s at position start_pos + s; q_rows [B*S, H, 68] uint8,
@@ -382,20 +425,20 @@ def idx_q_rope_quant(q, w_raw, w_scale, cos_sin, start_pos, S, q_rows, w_out,
         _dev(q_roundtrip, "q_roundtrip", _bf16_types(), 3)
         if tuple(q_roundtrip.shape) != (R, H, D):
             raise ValueError("q_roundtrip must be shaped like q")
-    _check(load_library().idx_q_rope_quant(_ptr(q), _ptr(w_raw), w_scale, _ptr(cos_sin),
+    return _issue("idx_q_rope_quant", (_ptr(q), _ptr(w_raw), w_scale, _ptr(cos_sin),
                                            cos_sin.shape[0], R // S, S, H, D, rd, start_pos,
-                                           _ptr(q_rows), _ptr(q_roundtrip), _ptr(w_out),
-                                           _stream(stream)), "idx_q_rope_quant")
+                                           _ptr(q_rows), _ptr(q_roundtrip), _ptr(w_out)), stream,
+                  "idx_q_rope_quant", bind)
 
 
-def idx_clear_key_hist(key_hist, stream=None):
+def idx_clear_key_hist(key_hist, stream=None, bind=False):
     """Zero a [R, 2048] int32 score histogram before idx_score adds to it."""
     torch = _torch()
     _dev(key_hist, "key_hist", (torch.int32,), 2)
     if key_hist.shape[1] != 2048:
         raise ValueError("key_hist must be [R, 2048]")
-    _check(load_library().idx_clear_key_hist(_ptr(key_hist), key_hist.shape[0], _stream(stream)),
-           "idx_clear_key_hist")
+    return _issue("idx_clear_key_hist", (_ptr(key_hist), key_hist.shape[0]), stream,
+                  "idx_clear_key_hist", bind)
 
 
 def idx_topk_workspace_size(R, T, index_topk) -> int:
@@ -403,7 +446,7 @@ def idx_topk_workspace_size(R, T, index_topk) -> int:
 
 
 def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, key_hist=None,
-             stream=None):
+             stream=None, bind=False):
     """scores [R, ld] float32, compress_lens [R] int32, out [R, ld_out] int32
     (ld_out >= min(index_topk, T)).  workspace: uint8 device tensor of at
     least idx_topk_workspace_size bytes, allocated here when None.
@@ -424,15 +467,15 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
         if tuple(key_hist.shape) != (R, 2048):
             raise ValueError("key_hist must be [R, 2048]")
     kout = ctypes.c_int32(-1)
-    _check(load_library().idx_topk(_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
-                                   _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
-                                   ctypes.byref(kout), _ptr(workspace), wsb, _stream(stream)),
-           "idx_topk")
-    return kout.value
+    bound = _issue("idx_topk", (_ptr(scores), scores.shape[1], R, T, _ptr(compress_lens),
+                                _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
+                                ctypes.byref(kout), _ptr(workspace), wsb), stream, "idx_topk",
+                   bind, keep=(workspace,))
+    return bound if bind else kout.value
 
 
 def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, index_topk,
-                        offset, out, key_hist=None, stream=None):
+                        offset, out, key_hist=None, stream=None, bind=False):
     """Top-k of level-two rows whose finite scores lie in the ascending
     candidate blocks cand_blocks [R, n_cand] int32 (the output of
     idx_select_candidate_blocks); scores [R, ld] float32, out [R, ld_out].
@@ -451,13 +494,13 @@ def idx_topk_candidates(scores, T, compress_lens, cand_blocks, cand_block_size, 
         if key_hist.shape != (R, 2048):
             raise ValueError("key_hist must be [R, 2048]")
     kout = ctypes.c_int32(-1)
-    _check(load_library().idx_topk_candidates(_ptr(scores), scores.shape[1], R, T,
+    bound = _issue("idx_topk_candidates", (_ptr(scores), scores.shape[1], R, T,
                                               _ptr(compress_lens), _ptr(cand_blocks),
                                               cand_blocks.shape[1], cand_block_size,
                                               _ptr(key_hist), index_topk, offset, _ptr(out),
-                                              out.shape[1], ctypes.byref(kout), _stream(stream)),
-           "idx_topk_candidates")
-    return kout.value
+                                              out.shape[1], ctypes.byref(kout)), stream,
+                   "idx_topk_candidates", bind)
+    return bound if bind else kout.value
 
 
 def idx_select_workspace_size(R, T, ctb, cbs) -> int:
@@ -465,7 +508,8 @@ def idx_select_workspace_size(R, T, ctb, cbs) -> int:
 
 
 def idx_select_candidate_blocks(scores, T, compress_lens, candidate_topk_blocks,
-                                cand_block_size, block_ids, workspace=None, stream=None):
+                                cand_block_size, block_ids, workspace=None, stream=None,
+                                bind=False):
     torch = _torch()
     _dev(scores, "scores", (torch.float32,), 2)
     _dev(compress_lens, "compress_lens", (torch.int32,), 1)
@@ -475,14 +519,14 @@ def idx_select_candidate_blocks(scores, T, compress_lens, candidate_topk_blocks,
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().idx_select_candidate_blocks(
+    return _issue("idx_select_candidate_blocks", (
         _ptr(scores), scores.shape[1], R, T, _ptr(compress_lens), candidate_topk_blocks,
-        cand_block_size, _ptr(block_ids), block_ids.shape[1], _ptr(workspace), wsb,
-        _stream(stream)), "idx_select_candidate_blocks")
+        cand_block_size, _ptr(block_ids), block_ids.shape[1], _ptr(workspace), wsb), stream,
+        "idx_select_candidate_blocks", bind, keep=(workspace,))
 
 
 def idx_publish_keys(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache, rd=64,
-                     stream=None):
+                     stream=None, bind=False):
     """latent [B, G, Din] bf16, wk [128, Din] bf16, gamma [128] float32,
     cos_sin [P, rd/2, 2] float32, k_cache [B', Tcap, 68] uint8 (B' >= B)."""
     torch = _torch()
@@ -495,10 +539,10 @@ def idx_publish_keys(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache,
     D = wk.shape[0]
     if wk.shape[1] != Din or gamma.shape[0] != D or k_cache.shape[0] < B:
         raise ValueError("shape mismatch in idx_publish_keys")
-    _check(load_library().idx_publish_keys(_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin),
+    return _issue("idx_publish_keys", (_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin),
                                            cos_sin.shape[0], B, G, Din, D, rd, eps, start_pos,
                                            ratio, _ptr(k_cache), k_cache.shape[1],
-                                           k_cache.shape[1], _stream(stream)), "idx_publish_keys")
+                                           k_cache.shape[1]), stream, "idx_publish_keys", bind)
 
 
 def idx_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):
@@ -521,3 +565,29 @@ def idx_timing_read(slot: int) -> float:
     ms = ctypes.c_float()
     _check(load_library().idx_timing_read(int(slot), ctypes.byref(ms)), "idx_timing_read")
     return float(ms.value)
+
+
+def idx_probe_stream_read(buf, grid, sink, stream=None) -> float:
+    """Measured streaming read of the whole device tensor `buf` (its bytes a
+    multiple of 16) by `grid` workgroups; sink: int32 device tensor of at
+    least `grid` words.  Returns the kernel's duration in ms (waits)."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < grid:
+        raise ValueError("sink needs a word per workgroup")
+    ms = ctypes.c_float()
+    _check(load_library().idx_probe_stream_read(_ptr(buf), nbytes, grid, _ptr(sink),
+                                                ctypes.byref(ms), _stream(stream)),
+           "idx_probe_stream_read")
+    return float(ms.value)
+
+
+def idx_probe_mfma_fp4(grid, iters, sink, stream=None):
+    """Measured fp4 matrix-core loop: returns (flops, ms).  sink: float32
+    device tensor of at least grid * 256 elements."""
+    if sink.numel() < grid * 256:
+        raise ValueError("sink needs grid * 256 floats")
+    ms, fl = ctypes.c_float(), ctypes.c_double()
+    _check(load_library().idx_probe_mfma_fp4(grid, iters, _ptr(sink), ctypes.byref(fl),
+                                             ctypes.byref(ms), _stream(stream)),
+           "idx_probe_mfma_fp4")
+    return float(fl.value), float(ms.value)

@@ -10,10 +10,12 @@ own weights inside the selected blocks.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 
-from . import (PAGE_ROWS, idx_clear_key_hist, idx_fp4_quant, idx_publish_keys,
-               idx_publish_keys_paged, idx_q_rope_quant, idx_score, idx_score_paged,
+from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
+               idx_publish_keys, idx_publish_keys_paged, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
                idx_topk, idx_topk_candidates,
@@ -133,6 +135,9 @@ class IndexerStep:
                                                       YARN["orig_len"], YARN["beta_fast"],
                                                       YARN["beta_slow"]))
 
+        # every step's calls, marshalled once per key-cache copy
+        self._plans = [self._plan(kc) for kc in self.caches]
+
     @staticmethod
     def _ws(nbytes):
         torch = _torch()
@@ -143,78 +148,94 @@ class IndexerStep:
         return self.caches[self.cur]
 
     def step(self, stream=None, time_slot=None):
-        """Issue one step on the current stream (asynchronous).  time_slot:
-        when given, the (level-one) score launch records its kernel's start
-        and end into that library event pair (idx_timing_read reads it)."""
+        """Issue one step on `stream` (default: torch's current stream),
+        asynchronously.  time_slot: when given, the (level-one) score launch
+        records its kernel's start and end into that library event pair
+        (idx_timing_read reads it).  The step's calls were marshalled once
+        per key-cache copy (BoundCall), so a step costs the host little more
+        than the launches themselves."""
+        plan, score_at = self._plans[self.cur]
+        h = current_stream_handle() if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        for i, call in enumerate(plan):
+            if i == score_at and time_slot is not None:
+                idx_timing_arm(time_slot)
+            call(h)
+        self.cur = (self.cur + 1) % len(self.caches)
+
+    def _plan(self, kc):
+        """The calls of one step on key cache `kc`, bound (not issued), and
+        the position of the (level-one) score launch among them."""
         wl = self.wl
-        kc = self.caches[self.cur]
+        calls = []
+        b = dict(bind=True)
         if self.publish:
             if self.paged:
-                idx_publish_keys_paged(self.latent, self.wk, self.gamma, self.cos_sin,
-                                       wl.start_pos, wl.ratio, wl.eps, kc, self.block_table, wl.T,
-                                       rd=wl.rd, stream=stream)
+                calls.append(idx_publish_keys_paged(self.latent, self.wk, self.gamma, self.cos_sin,
+                                                    wl.start_pos, wl.ratio, wl.eps, kc,
+                                                    self.block_table, wl.T, rd=wl.rd, **b))
             else:
-                idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
-                                 wl.ratio, wl.eps, kc, rd=wl.rd, stream=stream)
+                calls.append(idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin,
+                                              wl.start_pos, wl.ratio, wl.eps, kc, rd=wl.rd, **b))
         q, w = self.q, self.w
         q4 = None  # the quantised heads, when the score takes them directly
         if self.q_step:
             # the score takes the rows directly; the paged and level-two
             # scores take the bf16 round trip
             direct = not self.paged and not self.two_level
-            idx_q_rope_quant(self.q, self.w, 1.0, self.cos_sin_q, wl.start_pos, wl.S,
-                             self.q_rows, self.w_q, q_roundtrip=None if direct else self.q_rt,
-                             rd=wl.rd, stream=stream)
+            calls.append(idx_q_rope_quant(self.q, self.w, 1.0, self.cos_sin_q, wl.start_pos,
+                                          wl.S, self.q_rows, self.w_q,
+                                          q_roundtrip=None if direct else self.q_rt, rd=wl.rd,
+                                          **b))
             w = self.w_q
             if direct:
                 q4 = self.q_rows
             else:
                 q = self.q_rt
-        if time_slot is not None:
-            idx_timing_arm(time_slot)
+        score_at = len(calls)
         if self.fused:
             if self.paged:
-                idx_score_topk_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T,
-                                     self.cl, wl.topk, wl.offset, self.out, scores=self.scores,
-                                     stream=stream)
+                calls.append(idx_score_topk_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T,
+                                                  self.cl, wl.topk, wl.offset, self.out,
+                                                  scores=self.scores, **b))
             elif q4 is not None:
-                idx_score_topk_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
-                                  self.out, scores=self.scores, stream=stream)
+                calls.append(idx_score_topk_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk,
+                                               wl.offset, self.out, scores=self.scores, **b))
             else:
-                idx_score_topk(q, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk, wl.offset,
-                               self.out, scores=self.scores, stream=stream)
-            self.cur = (self.cur + 1) % len(self.caches)
-            return
+                calls.append(idx_score_topk(q, w, kc, wl.B, wl.S, wl.T, self.cl, wl.topk,
+                                            wl.offset, self.out, scores=self.scores, **b))
+            return calls, score_at
         if self.paged:
-            idx_score_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
-                            self.scores, key_hist=self.key_hist, stream=stream)
+            calls.append(idx_score_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
+                                         self.scores, key_hist=self.key_hist, **b))
         elif q4 is not None:
-            idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
-                         key_hist=self.key_hist, stream=stream)
+            calls.append(idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                                      key_hist=self.key_hist, **b))
         else:
-            idx_score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
-                      key_hist=self.key_hist, stream=stream)
+            calls.append(idx_score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                                   key_hist=self.key_hist, **b))
         if self.two_level:
-            idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs, self.ids,
-                                        workspace=self.sel_ws, stream=stream)
-            idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
-                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
+            calls.append(idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs,
+                                                     self.ids, workspace=self.sel_ws, **b))
+            calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
+                                  workspace=self.topk_ws, key_hist=self.key_hist, **b))
             # level two: only the candidate positions hold finite scores; the
             # histogram, reset by the level-one top-k, now counts them
             if self.paged:
-                idx_score_paged(q, self.w2, kc, self.block_table, wl.B, wl.S, wl.T, self.cl,
-                                self.scores2, cand_blocks=self.ids, cand_block_size=wl.cbs,
-                                key_hist=self.key_hist, stream=stream)
+                calls.append(idx_score_paged(q, self.w2, kc, self.block_table, wl.B, wl.S, wl.T,
+                                             self.cl, self.scores2, cand_blocks=self.ids,
+                                             cand_block_size=wl.cbs, key_hist=self.key_hist,
+                                             **b))
             else:
-                idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                          cand_blocks=self.ids, cand_block_size=wl.cbs, key_hist=self.key_hist,
-                          stream=stream)
-            idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs, wl.topk,
-                                wl.offset, self.out, key_hist=self.key_hist, stream=stream)
+                calls.append(idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
+                                       cand_blocks=self.ids, cand_block_size=wl.cbs,
+                                       key_hist=self.key_hist, **b))
+            calls.append(idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs,
+                                             wl.topk, wl.offset, self.out,
+                                             key_hist=self.key_hist, **b))
         else:
-            idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
-                     workspace=self.topk_ws, key_hist=self.key_hist, stream=stream)
-        self.cur = (self.cur + 1) % len(self.caches)
+            calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
+                                  workspace=self.topk_ws, key_hist=self.key_hist, **b))
+        return calls, score_at
 
     def keys_scored(self):
         """Algorithmic (query, key) pairs scored per step.  The fused launch

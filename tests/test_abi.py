@@ -17,9 +17,14 @@ IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED = 0, 1, 2
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "idx.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text)))
+    """Every idx_* function declared in include/*.h."""
+    syms = set()
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", name)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            syms |= set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text))
+    return sorted(syms)
 
 
 @pytest.fixture(scope="module")
