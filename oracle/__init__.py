@@ -32,6 +32,14 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
                    hand-worked frequency ratios inside the band.  The
                    constants themselves are a reading (the pages name them
                    only).
+  fp8_quant_rows   pinned: the e4m3 value table against the format's
+                   definition, exhaustive ue8m0 exponent vs exact rationals,
+                   a hand-worked tie table (tests/golden/e4m3_rne_ties.txt),
+                   the nearest-point property over all bf16, idempotence.
+  head_dots_fp8    pinned: the float64 matmul of the dequantised rows,
+                   rounded once to fp32.
+  score_fp8        pinned: on fp4 round trips with equal block scales (exactly
+                   representable in e4m3) it equals score() bit for bit.
   head sum order   the fp32 two-chain association is a contract shared with
                    the GPU library (split chosen to match the matrix core's
                    half-wave layout); the pages fix none.  A hand-worked
@@ -92,6 +100,12 @@ def lib():
         L.orc_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
         L.orc_q_rope_quant.restype = None
         L.orc_publish.restype = None
+        L.orc_fp8_quant_rows.argtypes = [P, i64, P, P]
+        L.orc_fp8_quant_rows.restype = None
+        L.orc_head_dots_fp8.argtypes = [P, P, i64, i32, i32, i32, i32, P]
+        L.orc_head_dots_fp8.restype = i64
+        L.orc_score_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, i32, i32, P, i64]
+        L.orc_score_fp8.restype = i64
         _lib = L
     return _lib
 
@@ -151,6 +165,49 @@ def score(q, w, kc, B, S, H, T, cl, cand=None, cbs=0):
     inexact = lib().orc_score(_p(q), _p(w), _p(kc), kstride, B, S, H, T, _p(cl), _p(cand),
                               n_cand, cbs, _p(out), T)
     return out, inexact
+
+
+# ------------------------------------------------------------ FP8 cache
+def fp8_quant_rows(x_bf16: np.ndarray):
+    """[VLLM, _indexer_k_cache_head_dim] FP8 rows: e4m3 codes with one ue8m0
+    scale (stored fp32) per 128 values.  x_bf16: uint16 [..., 128].  Returns
+    (rows uint8 [..., 132], roundtrip uint16 [..., 128])."""
+    x = _c(x_bf16, np.uint16)
+    assert x.shape[-1] == 128
+    n = x.size // 128
+    rows = np.empty(x.shape[:-1] + (132,), np.uint8)
+    rt = np.empty_like(x)
+    lib().orc_fp8_quant_rows(_p(x), n, _p(rows), _p(rt))
+    return rows, rt
+
+
+def head_dots_fp8(q, kc, B, S, H, T):
+    """Per-head dots on FP8 rows, each the exact sum rounded once to fp32.
+    kc uint8 [B][Tcap][132].  Returns (d, count of dots rounded)."""
+    q = _c(q, np.uint16)
+    kc = _c(kc, np.uint8)
+    d = np.empty((B * S, H, T), np.float32)
+    n = lib().orc_head_dots_fp8(_p(q), _p(kc), kc.shape[1], B, S, H, T, _p(d))
+    return d, n
+
+
+def score_fp8(q, w, kc, B, S, H, T, cl, cand=None, cbs=0):
+    """score() on the FP8 cache (kc uint8 [B][Tcap][132]); q is quantised
+    per head by the FP8 quantiser.  Returns (scores, count of dots rounded)."""
+    q = _c(q, np.uint16)
+    w = _c(w, np.uint16)
+    kc = _c(kc, np.uint8)
+    cl = _c(cl, np.int32)
+    R = B * S
+    assert q.shape[:2] == (R, H) and w.shape == (R, H) and cl.shape == (R,) and H <= 1024
+    n_cand = 0
+    if cand is not None:
+        cand = _c(cand, np.int32)
+        n_cand = cand.shape[1]
+    out = np.empty((R, T), np.float32)
+    n = lib().orc_score_fp8(_p(q), _p(w), _p(kc), kc.shape[1], B, S, H, T, _p(cl), _p(cand),
+                            n_cand, cbs, _p(out), T)
+    return out, n
 
 
 # ------------------------------------------------------------------- top-k

@@ -259,6 +259,21 @@ int64_t orc_head_dots(const uint16_t *q, const uint8_t *kc, int64_t kstride, int
 
 /* ---------------------------------------------------------------- score */
 
+/* [IDX, forward: relu, times weights, sum over heads] in the fp32 order both
+ * sides share: heads [0, hs) and [hs, H), hs = ceil(H/2), each summed
+ * ascending by one fmaf per head from +0, then lo + hi (one rounded add,
+ * canonical +0). */
+static float head_sum(const float *dh, const uint16_t *wrow, int H)
+{
+    const int hsplit = (H + 1) / 2;
+    float lo = 0.0f, hi = 0.0f;
+    for (int h = 0; h < hsplit; ++h)
+        lo = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(wrow[h]), lo);
+    for (int h = hsplit; h < H; ++h)
+        hi = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(wrow[h]), hi);
+    return (lo + hi) + 0.0f;
+}
+
 static int in_candidates(const int32_t *cand, int n_cand, int cbs, int t)
 {
     int blk = t / cbs;
@@ -309,14 +324,7 @@ int64_t orc_score(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64
             float dh[1024];
             for (int h = 0; h < H; ++h)
                 dh[h] = exact_dot(&dq[h], &dk, &inexact);
-            /* two chains, each heads ascending from +0, then one add */
-            const int hsplit = (H + 1) / 2;
-            float lo = 0.0f, hi = 0.0f;
-            for (int h = 0; h < hsplit; ++h)
-                lo = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(w[r * H + h]), lo);
-            for (int h = hsplit; h < H; ++h)
-                hi = fmaf(fmaxf(dh[h], 0.0f), bf16_to_f32(w[r * H + h]), hi);
-            *out = (lo + hi) + 0.0f;
+            *out = head_sum(dh, w + r * H, H);
         }
         inexact_total += inexact;
     }
@@ -540,4 +548,191 @@ void orc_q_rope_quant(const uint16_t *q, const uint16_t *w_raw, float scale, con
         quant_row(z, rows + rh * ROW_BYTES, rt ? rt + rh * HEAD_DIM : NULL);
         w_out[rh] = f32_to_bf16(bf16_to_f32(w_raw[rh]) * scale);
     }
+}
+
+/* ------------------------------------------------------- FP8 key cache */
+
+/* The FP8 indexer cache ([VLLM, _indexer_k_cache_head_dim]: 128 fp8 bytes
+ * and one fp32 scale per 128 values, 132-byte rows; [VLLM,
+ * DeepseekV4Indexer.__init__]: quant_block_size 128, scale_fmt "ue8m0").
+ * Readings: the fp8 format is OCP e4m3 (finite maximum 448); the ue8m0 scale
+ * of a 128-value block is the power of two 2^e with e the smallest integer
+ * such that 448 * 2^e >= amax, amax first raised to at least 448 * 2^-126
+ * (the e2m1 rule of [CMP, fp4_quant_e8m0_inplace] with e4m3's maximum in
+ * place of e2m1's); values are rounded to the nearest e4m3 point of x/2^e,
+ * ties to the even code, sign kept; the query heads go through the same
+ * quantiser. */
+#define FP8_ROW_BYTES 132
+#define E4M3_MAX 448.0
+
+/* Value of a non-negative e4m3 code 0..126 (code 127 is NaN): exponent
+ * field E (bias 7), mantissa m: subnormal m * 2^-9 for E = 0, else
+ * (8 + m) * 2^(E - 10). */
+static double e4m3_value(int c)
+{
+    int E = c >> 3, m = c & 7;
+    return E == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), E - 10);
+}
+
+/* Nearest non-negative e4m3 code to y (0 <= y <= 448), ties to the even
+ * code: the codes order like their values, so the two neighbours of y are
+ * found by bisection and compared. */
+static int e4m3_code_of_magnitude(double y)
+{
+    int lo = 0, hi = 126; /* e4m3_value(lo) <= y <= e4m3_value(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (e4m3_value(mid) <= y)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double dl = y - e4m3_value(lo), dh = e4m3_value(hi) - y;
+    if (dl < dh)
+        return lo;
+    if (dh < dl)
+        return hi;
+    return (lo % 2 == 0) ? lo : hi;
+}
+
+/* Scale exponent of a 128-value block: the smallest e with 448 * 2^e >=
+ * amax, amax raised to at least 448 * 2^-126; exact double comparisons. */
+static int ue8m0_exponent_fp8(float amax)
+{
+    double a = (double)amax, floor_ = E4M3_MAX * ldexp(1.0, -126);
+    if (a < floor_)
+        a = floor_;
+    int E;
+    frexp(a, &E); /* a in [2^(E-1), 2^E) */
+    int e = E - 10;
+    while (ldexp(E4M3_MAX, e) < a)
+        ++e;
+    return e;
+}
+
+/* Row layout: bytes 0..127 the e4m3 codes of elements 0..127 (bit 7 =
+ * sign), bytes 128..131 the scale 2^e as a little-endian fp32. */
+static void quant_row_fp8(const uint16_t *x, uint8_t *row, uint16_t *rt)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        float v = fabsf(bf16_to_f32(x[i]));
+        if (v > amax)
+            amax = v;
+    }
+    int e = ue8m0_exponent_fp8(amax);
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        float v = bf16_to_f32(x[i]);
+        int c = e4m3_code_of_magnitude(ldexp(fabs((double)v), -e)); /* exact scaling */
+        int neg = signbit(v) ? 1 : 0;
+        row[i] = (uint8_t)(c | (neg << 7));
+        if (rt) {
+            double val = ldexp(e4m3_value(c), e);
+            rt[i] = f32_to_bf16((float)(neg ? -val : val)); /* exact: 4 significant bits */
+        }
+    }
+    float scale = ldexpf(1.0f, e);
+    memcpy(row + HEAD_DIM, &scale, 4);
+}
+
+/* x: [n_rows][128] bf16 -> rows: [n_rows][132]; rt (optional): [n_rows][128]. */
+void orc_fp8_quant_rows(const uint16_t *x, int64_t n_rows, uint8_t *rows, uint16_t *rt)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r)
+        quant_row_fp8(x + r * HEAD_DIM, rows + r * FP8_ROW_BYTES, rt ? rt + r * HEAD_DIM : NULL);
+}
+
+typedef struct {
+    double v[HEAD_DIM]; /* e4m3 values, scale not applied */
+    int e;
+} decoded_row_fp8;
+
+static void decode_row_fp8(const uint8_t *row, decoded_row_fp8 *d)
+{
+    for (int i = 0; i < HEAD_DIM; ++i) {
+        int c = row[i];
+        double v = e4m3_value(c & 0x7f);
+        d->v[i] = (c & 0x80) ? -v : v;
+    }
+    float scale;
+    memcpy(&scale, row + HEAD_DIM, 4);
+    int E;
+    frexpf(scale, &E);
+    d->e = E - 1; /* scale = 2^e */
+}
+
+/* [IDX, forward: the einsum of q against index_k] on fp8 rows: the sum of
+ * the 128 products of e4m3 values is exact in double (each product has at
+ * most 8 significant bits between 2^-18 and 2^17.6, so the sum needs at
+ * most 43 bits), then it is scaled by 2^(eq + ek) and rounded once to fp32. */
+static float exact_dot_fp8(const decoded_row_fp8 *q, const decoded_row_fp8 *k, int64_t *inexact)
+{
+    double s = 0.0;
+    for (int i = 0; i < HEAD_DIM; ++i)
+        s += q->v[i] * k->v[i];
+    double d = ldexp(s, q->e + k->e);
+    float f = (float)d;
+    if ((double)f != d)
+        (*inexact)++;
+    return f;
+}
+
+/* Per-head fp8 dots d[r][h][t] (test export).  q: [R][H][128] bf16,
+ * quantised here; kc: [B][Tcap][132].  Returns the count of dots whose fp32
+ * rounding was inexact (rounding is expected here, unlike fp4). */
+int64_t orc_head_dots_fp8(const uint16_t *q, const uint8_t *kc, int64_t kstride, int B, int S,
+                          int H, int T, float *d)
+{
+    int64_t R = (int64_t)B * S, inexact = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t b = r / S;
+        for (int h = 0; h < H; ++h) {
+            uint8_t qrow[FP8_ROW_BYTES];
+            decoded_row_fp8 dq, dk;
+            quant_row_fp8(q + (r * H + h) * HEAD_DIM, qrow, NULL);
+            decode_row_fp8(qrow, &dq);
+            for (int t = 0; t < T; ++t) {
+                decode_row_fp8(kc + (b * kstride + t) * FP8_ROW_BYTES, &dk);
+                d[(r * H + h) * (int64_t)T + t] = exact_dot_fp8(&dq, &dk, &inexact);
+            }
+        }
+    }
+    return inexact;
+}
+
+/* orc_score on the FP8 cache: q quantised per head by the fp8 quantiser,
+ * keys [B][Tcap][132]; masks and the head sum as orc_score. */
+int64_t orc_score_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *kc, int64_t kstride,
+                      int B, int S, int H, int T, const int32_t *cl, const int32_t *cand,
+                      int n_cand, int cbs, float *scores, int64_t ld)
+{
+    int64_t R = (int64_t)B * S, inexact_total = 0;
+    decoded_row_fp8 *dq = (decoded_row_fp8 *)malloc(sizeof(decoded_row_fp8) * (size_t)H);
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t b = r / S;
+        for (int h = 0; h < H; ++h) {
+            uint8_t qrow[FP8_ROW_BYTES];
+            quant_row_fp8(q + (r * H + h) * HEAD_DIM, qrow, NULL);
+            decode_row_fp8(qrow, &dq[h]);
+        }
+        int64_t inexact = 0;
+#pragma omp parallel for schedule(static) reduction(+ : inexact)
+        for (int t = 0; t < T; ++t) {
+            float *out = &scores[r * ld + t];
+            if (t >= cl[r] || (cand && !in_candidates(cand + r * (int64_t)n_cand, n_cand, cbs, t))) {
+                *out = -INFINITY;
+                continue;
+            }
+            decoded_row_fp8 dk;
+            decode_row_fp8(kc + (b * kstride + t) * FP8_ROW_BYTES, &dk);
+            float dh[1024];
+            for (int h = 0; h < H; ++h)
+                dh[h] = exact_dot_fp8(&dq[h], &dk, &inexact);
+            *out = head_sum(dh, w + r * H, H);
+        }
+        inexact_total += inexact;
+    }
+    free(dq);
+    return inexact_total;
 }
