@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("indexer queries/sec + keys scored/sec (decode, 128K ctx); % HBM / MFMA roofline")
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0
 LLC_BYTES = 256 * 2 ** 20
 
 
@@ -70,6 +71,9 @@ def parse():
     ap.add_argument("--prefill-publish", action="store_true",
                     help="prefill workloads: the step first publishes the S / ratio keys of "
                          "the prompt (key publish of many groups)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="key cache in FP8 rows (132 bytes: 128 e4m3 codes + fp32 scale per "
+                         "128 values), scored on the e4m3 matrix core")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the chip's ceilings (streaming read over grid sizes, "
                          "fp4 matrix-core loop) and print them as one JSON line")
@@ -100,13 +104,13 @@ def reachable_pairs(wl) -> int:
     return int(np.minimum(wl.compress_lens().astype(np.int64), wl.T).sum())
 
 
-def score_kernel_bytes(wl, st=None) -> int:
-    """Algorithmic HBM bytes of one (level-one) score launch: the 68-byte key
-    row of every reachable (row, key) pair, each row's fp4 query heads (68
-    bytes a head) and its bf16 weights.  The fp32 score scratch the launch
-    also writes is an implementation cost, not algorithmic: it shows up in
-    the measured traffic instead."""
-    return reachable_pairs(wl) * 68 + wl.R * wl.H * (Q_ROW_BYTES + 2)
+def score_kernel_bytes(wl, st=None, rb=68) -> int:
+    """Algorithmic HBM bytes of one (level-one) score launch: the key row
+    (rb bytes: 68 fp4, 132 FP8) of every reachable (row, key) pair, each
+    row's quantised query heads (rb bytes a head) and its bf16 weights.  The
+    fp32 score scratch the launch also writes is an implementation cost, not
+    algorithmic: it shows up in the measured traffic instead."""
+    return reachable_pairs(wl) * rb + wl.R * wl.H * (rb + 2)
 
 
 def score_kernel_flops(wl, st=None) -> int:
@@ -121,21 +125,21 @@ def scored_flops(wl, st) -> int:
     return int(scored_compress_lens(wl, st).sum()) * wl.H * FLOP_PER_PAIR_HEAD
 
 
-def step_bytes(wl, q_step=False, prefill_publish_groups=0) -> int:
+def step_bytes(wl, q_step=False, prefill_publish_groups=0, rb=68) -> int:
     """Algorithmic HBM bytes of one whole step: every score launch's keys,
-    the fp4 query and the weights (per level), the candidate block ids, the
-    key publish (wk, latent, the written rows) and the int32 indices of
-    every top-k the step keeps."""
+    the quantised query and the weights (per level), the candidate block
+    ids, the key publish (wk, latent, the written rows) and the int32
+    indices of every top-k the step keeps.  rb: bytes of a key row."""
     kout = min(wl.topk, wl.T)
-    b = reachable_pairs(wl) * 68 + wl.R * wl.H * (Q_ROW_BYTES + 2) + wl.R * kout * 4
+    b = reachable_pairs(wl) * rb + wl.R * wl.H * (rb + 2) + wl.R * kout * 4
     if wl.ctb:
         nb = -(-wl.T // wl.cbs)
         cand = wl.R * min(wl.ctb * wl.cbs, wl.T)
-        b += cand * 68 + wl.R * wl.H * 2            # level-two keys and weights
+        b += cand * rb + wl.R * wl.H * 2            # level-two keys and weights
         b += wl.R * min(wl.ctb, nb) * 4              # block ids
         b += wl.R * kout * 4                         # level-one indices
     if wl.publish:
-        b += 128 * wl.din * 2 + wl.B * wl.din * 2 + wl.B * 68
+        b += 128 * wl.din * 2 + wl.B * wl.din * 2 + wl.B * rb
     if q_step:
         b += wl.R * wl.H * (128 * 2 + 2)             # bf16 heads before RoPE, raw weights
     if prefill_publish_groups:
@@ -172,6 +176,8 @@ def score_kernel_name(st) -> str:
     single-level rows up to 8192 positions, else the score kernel."""
     if st.fused:
         return "idx::score_kernel<2, false, true> (score and top-k in one launch)"
+    if getattr(st, "fp8", False):
+        return "idx::score_kernel<2, false, false, true> (FP8 rows)"
     return "idx::score_kernel<2, false, false>"
 
 
@@ -302,7 +308,8 @@ def main():
     t_gen = time.perf_counter()
     inp = generate(wl)
     t_gen = time.perf_counter() - t_gen
-    cache_bytes = wl.B * wl.T * 68
+    rb = 132 if args.fp8 else 68
+    cache_bytes = wl.B * wl.T * rb
     n_caches = max(1, min(8, math.ceil(3 * LLC_BYTES / cache_bytes))) if cache_bytes > 2 ** 20 else 1
     # the product path: indices only (a fused launch does not write scores)
     publish = None
@@ -313,7 +320,7 @@ def main():
         inp.update(publish_inputs(wl, wl.S // wl.ratio, wl.seed() + 1000))
         publish = True
     st = IndexerStep(wl, inp, n_caches=n_caches, keep_scores=False, paged=args.paged,
-                     q_step=args.q_step, publish=publish)
+                     q_step=args.q_step, publish=publish, fp8=args.fp8)
     torch.cuda.synchronize()
 
     timed = (timed_steps(args.steps) if args.event_every <= 0
@@ -362,15 +369,15 @@ def main():
 
     step_s = (t1 - t0) / args.steps
     score_ms = float(np.mean(score_ms_all))
-    kb = score_kernel_bytes(wl)
+    kb = score_kernel_bytes(wl, rb=rb)
     kf = score_kernel_flops(wl)
     groups = wl.S // wl.ratio if args.prefill_publish else 0
-    sb = step_bytes(wl, q_step=args.q_step, prefill_publish_groups=groups)
+    sb = step_bytes(wl, q_step=args.q_step, prefill_publish_groups=groups, rb=rb)
     sf = step_flops(wl)
     prefill = wl.S > 1
     if prefill:  # many queries share each key: the contraction bounds the kernel
         roof = {"bound": "mfma", "achieved": kf / (score_ms * 1e-3) / 1e12,
-                "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+                "peak": FP8_PEAK_TFLOPS if args.fp8 else FP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
         step_roof = {"achieved": sf / step_s / 1e12, "flops": sf}
     else:
         roof = {"bound": "hbm", "achieved": kb / (score_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
@@ -381,7 +388,7 @@ def main():
     qps = wl.R / step_s
     keys = st.keys_scored()
     # the committed counter summary covers the contiguous layout
-    traffic = None if args.paged else measured_traffic(wl.name)
+    traffic = None if (args.paged or args.fp8) else measured_traffic(wl.name)
     line = {
         "metric": METRIC,
         "value": qps,
@@ -393,7 +400,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4xfp4->f32",
+        "dtype": "fp8xfp8->f32" if args.fp8 else "fp4xfp4->f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "queries_per_seq": wl.S,
                    "end_pos": wl.end_pos, "compress_ratio": wl.ratio, "compressed_keys": wl.T,
@@ -401,6 +408,7 @@ def main():
                    "candidate_topk_blocks": wl.ctb, "candidate_block_size": wl.cbs,
                    "publish": wl.publish, "key_cache_copies": n_caches,
                    "key_cache_layout": "paged" if args.paged else "contiguous",
+                   "key_row": "fp8 e4m3, 132 bytes" if args.fp8 else "fp4 e2m1, 68 bytes",
                    "query_step": bool(args.q_step),
                    "prefill_publish": bool(args.prefill_publish)},
         "keys_scored_per_s": keys / step_s,

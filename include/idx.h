@@ -259,6 +259,50 @@ idx_status idx_score_topk_q4(const uint8_t *q_rows, const uint16_t *w, const uin
                              void *stream);
 
 /*
+ * FP8 key cache ([VLLM, _indexer_k_cache_head_dim]: the FP8 indexer cache
+ * row is 128 fp8 bytes plus one fp32 scale per 128 values, 132 bytes;
+ * [VLLM, DeepseekV4Indexer.__init__]: quant_block_size 128, scale_fmt
+ * "ue8m0").  Row layout:
+ *   bytes 0..127    OCP e4m3 codes of elements 0..127 (bit 7 = sign)
+ *   bytes 128..131  the scale 2^e as a little-endian fp32
+ * e is the smallest integer with 448 * 2^e >= amax (amax of the 128 values,
+ * at least 448 * 2^-126), each value is the nearest e4m3 point of x / 2^e
+ * with ties to the even code, sign kept (the e2m1 rule of idx_fp4_quant
+ * with e4m3's maximum 448 and a block of 128).  The query heads go through
+ * the same quantiser.
+ */
+
+/* idx_fp8_quant -- 128-wide bf16 rows (16-byte aligned) -> 132-byte rows
+ * (4-byte aligned), and optionally their bf16 round trip (16-byte aligned,
+ * or NULL).  n_rows >= 0; misaligned pointers give IDX_EINVAL. */
+idx_status idx_fp8_quant(const uint16_t *x, int64_t n_rows, uint8_t *rows132, uint16_t *roundtrip,
+                         void *stream);
+
+/*
+ * idx_score_fp8 -- idx_score on the FP8 cache: k_cache holds 132-byte rows
+ * (sequence stride k_batch_stride_rows rows), q is quantised per head by the
+ * FP8 quantiser in the kernel, the dots run on the matrix core's e4m3 form.
+ * Every other argument and result as idx_score.  Unlike the fp4 rows, a
+ * 128-term e4m3 dot is not exact in fp32: each dot is rounded in the order
+ * the matrix core fixes, so the scores agree with an exactly rounded
+ * reference to within a few fp32 roundings per head, not bit for bit.
+ * Requires D == 128 and H in {32, 64}.
+ */
+idx_status idx_score_fp8(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
+                         int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                         const int32_t *compress_lens, const int32_t *cand_blocks, int n_cand,
+                         int cand_block_size, float *scores, int64_t ld, uint32_t *key_hist,
+                         void *stream);
+
+/* idx_publish_keys_fp8 -- idx_publish_keys into an FP8 cache (132-byte rows,
+ * 4-byte aligned): the same key (wk, k_norm, RoPE), quantised by the FP8
+ * quantiser.  Arguments and errors as idx_publish_keys. */
+idx_status idx_publish_keys_fp8(const uint16_t *latent, const uint16_t *wk, const float *gamma,
+                                const float *cos_sin, int P, int B, int G, int Din, int D, int rd,
+                                float eps, int start_pos, int ratio, uint8_t *k_cache,
+                                int64_t k_batch_stride_rows, int Tcap, void *stream);
+
+/*
  * idx_clear_key_hist -- zero a [R][2048] uint32 score histogram (device) on
  * the stream, before the first idx_score accumulates into it (idx_topk
  * resets it after each use).

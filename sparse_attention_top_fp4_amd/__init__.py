@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_score_paged",
+__all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_fp8",
+           "idx_score", "idx_score_topk", "idx_score_paged",
            "idx_score_topk_paged", "idx_publish_keys_paged", "idx_q_rope_quant",
            "idx_score_q4", "idx_score_topk_q4",
            "idx_clear_key_hist", "idx_topk",
@@ -25,6 +26,7 @@ __all__ = ["idx_fp4_quant", "idx_score", "idx_score_topk", "idx_score_paged",
            "load_library", "IdxError", "ROW_BYTES"]
 
 ROW_BYTES = 68
+FP8_ROW_BYTES = 132  # the FP8 cache row: 128 e4m3 bytes + fp32 scale
 PAGE_ROWS = 64  # compressed positions per page of a paged key cache
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libidx.so")
@@ -78,6 +80,9 @@ def load_library():
     L.idx_score_q4.argtypes = L.idx_score.argtypes
     L.idx_score_topk_q4.argtypes = L.idx_score_topk.argtypes
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
+    L.idx_fp8_quant.argtypes = [P, i64, P, P, P]
+    L.idx_score_fp8.argtypes = L.idx_score.argtypes
+    L.idx_publish_keys_fp8.argtypes = L.idx_publish_keys.argtypes
     L.idx_probe_stream_read.argtypes = [P, i64, i32, P, ctypes.POINTER(f32), P]
     L.idx_probe_mfma_fp4.argtypes = [i32, i32, P, ctypes.POINTER(f64), ctypes.POINTER(f32), P]
     L.idx_timing_arm.argtypes = [i32]
@@ -88,7 +93,8 @@ def load_library():
                  "idx_publish_keys", "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read",
                  "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged",
                  "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
-                 "idx_probe_stream_read", "idx_probe_mfma_fp4"):
+                 "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
+                 "idx_score_fp8", "idx_publish_keys_fp8"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -222,6 +228,73 @@ def idx_score(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
                                     T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
                                     cand_block_size, _ptr(scores), scores.shape[1],
                                     _ptr(key_hist)), stream, "idx_score", bind)
+
+
+def idx_fp8_quant(x, rows132, roundtrip=None, stream=None, bind=False):
+    """x [n, 128] bf16 -> rows132 [n, 132] uint8 FP8 rows (+ roundtrip)."""
+    torch = _torch()
+    _dev(x, "x", _bf16_types())
+    _dev(rows132, "rows132", (torch.uint8,))
+    n = x.numel() // 128
+    if x.shape[-1] != 128 or rows132.numel() != n * FP8_ROW_BYTES:
+        raise ValueError("x must be [..., 128] and rows132 [..., 132] with the same rows")
+    if roundtrip is not None:
+        _dev(roundtrip, "roundtrip", _bf16_types())
+        if roundtrip.numel() != x.numel():
+            raise ValueError("roundtrip must match x")
+    return _issue("idx_fp8_quant", (_ptr(x), n, _ptr(rows132), _ptr(roundtrip)), stream,
+                  "idx_fp8_quant", bind)
+
+
+def idx_score_fp8(q, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,
+                  cand_block_size=0, key_hist=None, stream=None, bind=False):
+    """idx_score on the FP8 cache: k_cache [B, Tcap, 132] uint8."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != FP8_ROW_BYTES or scores.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 132] and scores [B*S, ld]")
+    n_cand = 0
+    if cand_blocks is not None:
+        _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+        if cand_blocks.shape[0] != R:
+            raise ValueError("cand_blocks must have B*S rows")
+        n_cand = cand_blocks.shape[1]
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    return _issue("idx_score_fp8", (_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H,
+                                    D, T, _ptr(compress_lens), _ptr(cand_blocks), n_cand,
+                                    cand_block_size, _ptr(scores), scores.shape[1],
+                                    _ptr(key_hist)), stream, "idx_score_fp8", bind)
+
+
+def idx_publish_keys_fp8(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache, rd=64,
+                         stream=None, bind=False):
+    """idx_publish_keys into an FP8 cache k_cache [B', Tcap, 132] uint8."""
+    torch = _torch()
+    _dev(latent, "latent", _bf16_types(), 3)
+    _dev(wk, "wk", _bf16_types(), 2)
+    _dev(gamma, "gamma", (torch.float32,), 1)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    B, G, Din = latent.shape
+    D = wk.shape[0]
+    if (wk.shape[1] != Din or gamma.shape[0] != D or k_cache.shape[0] < B
+            or k_cache.shape[2] != FP8_ROW_BYTES):
+        raise ValueError("shape mismatch in idx_publish_keys_fp8")
+    return _issue("idx_publish_keys_fp8", (_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin),
+                                           cos_sin.shape[0], B, G, Din, D, rd, eps, start_pos,
+                                           ratio, _ptr(k_cache), k_cache.shape[1],
+                                           k_cache.shape[1]), stream, "idx_publish_keys_fp8",
+                  bind)
 
 
 def idx_score_q4(q_rows, w, k_cache, B, S, T, compress_lens, scores, cand_blocks=None,

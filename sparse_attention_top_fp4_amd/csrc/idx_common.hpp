@@ -86,6 +86,82 @@ __device__ __forceinline__ uint32_t e2m1_dequant_bf16(uint32_t code, int e) {
   return f32_to_bf16((code & 8u) ? -v : v);
 }
 
+// ------------------------------------------------------------ FP8 rows
+// The FP8 indexer cache ([VLLM, _indexer_k_cache_head_dim]: 128 fp8 bytes and
+// one fp32 scale per 128 values; [VLLM, DeepseekV4Indexer.__init__]:
+// quant_block_size 128, scale_fmt "ue8m0"): bytes 0..127 the OCP e4m3 codes
+// of elements 0..127 (bit 7 = sign), bytes 128..131 the scale 2^e as fp32.
+constexpr int kRowBytesF8 = 132;
+
+// e of the block scale: the smallest integer with 448 * 2^e >= amax, amax
+// raised to at least 448 * 2^-126.  With amax = m * 2^E, m in [1, 2):
+// 1.75 * 2^(8+e) >= m * 2^E  <=>  e = E - 8 when m <= 1.75, else E - 7.
+__device__ __forceinline__ int ue8m0_exponent_f8(float amax) {
+  const float a = fmaxf(amax, 0x1.cp-118f);  // 448 * 2^-126
+  const uint32_t u = __float_as_uint(a);
+  const int E = (int)(u >> 23) - 127;
+  return E - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+}
+
+// e4m3 code of the bf16 x at scale 2^e (|x| / 2^e <= 448): the nearest e4m3
+// point, ties to the even code, sign in bit 7.  y = |x| * 2^-e is exact (a
+// power-of-two scaling; a y that fp32 holds only as a subnormal rounds to
+// code 0 either way).  Below 2^-6 the e4m3 points are the multiples of 2^-9
+// (code = the multiple; 8 is the first normal, 2^-6); above, keeping the
+// fp32 exponent and top three mantissa bits with a round-half-even carry
+// gives the code after rebasing the exponent bias from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t xb16, int e) {
+  const float y = fabsf(bf16f(xb16)) * __uint_as_float((uint32_t)(127 - e) << 23);
+  uint32_t code;
+  if (y < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(y * 512.0f);
+  } else {
+    const uint32_t u = __float_as_uint(y);
+    uint32_t r = u >> 20;
+    const uint32_t low = u & 0xfffffu;
+    r += (low > 0x80000u || (low == 0x80000u && (r & 1u))) ? 1u : 0u;
+    code = r - (120u << 3);
+  }
+  return code | ((xb16 >> 8) & 0x80u);
+}
+
+// Dequantised bf16 of an e4m3 code at scale 2^e: (8 + m) * 2^(E - 10) for
+// exponent field E > 0, m * 2^-9 for E = 0, times 2^e (exact in fp32; the
+// bf16 rounding is the only one, and exact unless the value falls below
+// bf16's subnormals).
+__device__ __forceinline__ uint32_t e4m3_dequant_bf16(uint32_t code, int e) {
+  const uint32_t E = (code >> 3) & 15u, m = code & 7u;
+  const float v = E == 0u ? (float)m * 0x1p-9f
+                          : (float)(8u + m) * __uint_as_float((E + 117u) << 23);
+  const float sv = v * __uint_as_float((uint32_t)(127 + e) << 23);
+  return f32_to_bf16((code & 0x80u) ? -sv : sv);
+}
+
+// Quantise 128 bf16 values spread over four consecutive lanes (this lane:
+// 32 of them, packed two per word, element 2i in the low half of word i):
+// the four lanes agree on the block's e (returned); codes[j] gets elements
+// 4j..4j+3 of this lane's 32, element 4j+m in byte m.
+__device__ __forceinline__ int quant_block128_f8(const uint32_t (&xp)[16], uint32_t (&codes)[8]) {
+  u16x2_t m = __builtin_bit_cast(u16x2_t, xp[0] & 0x7fff7fffu);
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, xp[i] & 0x7fff7fffu));
+  uint32_t amax_bits = m[0] > m[1] ? m[0] : m[1];
+  // the four lanes of the block: exchange by xor 1 and 2 (all four active)
+  uint32_t o = (uint32_t)__shfl_xor((int)amax_bits, 1, 64);
+  amax_bits = o > amax_bits ? o : amax_bits;
+  o = (uint32_t)__shfl_xor((int)amax_bits, 2, 64);
+  amax_bits = o > amax_bits ? o : amax_bits;
+  const int e = ue8m0_exponent_f8(bf16f(amax_bits));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w0 = xp[2 * j], w1 = xp[2 * j + 1];
+    codes[j] = e4m3_code(w0 & 0xffffu, e) | (e4m3_code(w0 >> 16, e) << 8) |
+               (e4m3_code(w1 & 0xffffu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
+  }
+  return e;
+}
+
 // ---------------------------------------------------------- score keys
 // Order-preserving key of a score: larger score -> larger key; -0 maps to +0.
 // Integer form: negative floats have every bit flipped, the others only the

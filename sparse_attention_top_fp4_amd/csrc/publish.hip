@@ -30,7 +30,8 @@ namespace idx {
 __device__ __forceinline__ void publish_finish(int o, const float* y_s, uint32_t* z_s,
                                                float* inv_s, const float* __restrict__ gamma,
                                                const float* __restrict__ cos_sin, int rd,
-                                               float eps, int pos, uint8_t* __restrict__ dst) {
+                                               float eps, int pos, uint8_t* __restrict__ dst,
+                                               bool f8) {
 
   if (o == 0) {
     float yv[kHeadDim];
@@ -69,6 +70,22 @@ __device__ __forceinline__ void publish_finish(int o, const float* y_s, uint32_t
   }
   __syncthreads();
 
+  if (f8) {
+    // FP8 row: one e4m3 scale for the 128 values; every thread finds the
+    // amax itself (LDS broadcast reads, no further barrier) and writes its
+    // own code byte
+    if (o < kHeadDim && dst) {
+      uint32_t amax = 0;
+      for (int j = 0; j < kHeadDim; ++j) {
+        const uint32_t a = z_s[j] & 0x7fffu;
+        amax = a > amax ? a : amax;
+      }
+      const int e = ue8m0_exponent_f8(bf16f(amax));
+      dst[o] = (uint8_t)e4m3_code(z_s[o], e);
+      if (o == 0) *reinterpret_cast<uint32_t*>(dst + 128) = (uint32_t)(127 + e) << 23;
+    }
+    return;
+  }
   if (o < 4 && dst) {
     uint32_t xp[16];
 #pragma unroll
@@ -88,7 +105,9 @@ __global__ __launch_bounds__(128) void publish_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
     const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
     int start_pos, int ratio, int G, uint8_t* __restrict__ kc, int64_t kstride,
-    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages) {
+    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages,
+    bool f8) {
+  const int rb = f8 ? kRowBytesF8 : kRowBytes;
   extern __shared__ __attribute__((aligned(16))) uint16_t lat_s[];  // Din bf16
   __shared__ float y_s[kHeadDim];
   __shared__ uint32_t z_s[kHeadDim];
@@ -136,13 +155,13 @@ __global__ __launch_bounds__(128) void publish_kernel(
   // page id outside [0, n_pages) is not written)
   uint8_t* dst = nullptr;
   if (!bt) {
-    dst = kc + ((int64_t)b * kstride + row) * kRowBytes;
+    dst = kc + ((int64_t)b * kstride + row) * rb;
   } else {
     const int page = bt[(int64_t)b * bt_stride + row / kPubPageRows];
     if (page >= 0 && page < n_pages)
-      dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * kRowBytes;
+      dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * rb;
   }
-  publish_finish(threadIdx.x, y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst);
+  publish_finish(threadIdx.x, y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst, f8);
 }
 
 // Many groups (the prompt's keys): one workgroup of kPubGroups * 128 threads
@@ -159,8 +178,10 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
     const uint16_t* __restrict__ latent, const uint16_t* __restrict__ wk,
     const float* __restrict__ gamma, const float* __restrict__ cos_sin, int Din, int rd, float eps,
     int start_pos, int ratio, int B, int G, uint8_t* __restrict__ kc, int64_t kstride,
-    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages) {
+    const int32_t* __restrict__ bt, int64_t bt_stride, int64_t page_stride, int n_pages,
+    bool f8) {
   extern __shared__ __attribute__((aligned(16))) uint32_t pg_smem[];
+  const int rb = f8 ? kRowBytesF8 : kRowBytes;
   const int wpr = Din / 2 + 1;                                        // words per wk row
   uint32_t* wk_s = pg_smem;                                           // [128][wpr]
   float* lat_s = reinterpret_cast<float*>(pg_smem + kHeadDim * wpr);  // [kPubGroups][Din]
@@ -207,14 +228,14 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
     pos = start_pos == 0 ? g * ratio : start_pos + 1 - ratio;
     const int row = start_pos == 0 ? g : start_pos / ratio + g;
     if (!bt) {
-      dst = kc + (b * kstride + row) * kRowBytes;
+      dst = kc + (b * kstride + row) * rb;
     } else {
       const int page = bt[b * bt_stride + row / kPubPageRows];
       if (page >= 0 && page < n_pages)
-        dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * kRowBytes;
+        dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * rb;
     }
   }
-  publish_finish(o, y_s[gi], z_s[gi], &inv_s[gi], gamma, cos_sin, rd, eps, pos, dst);
+  publish_finish(o, y_s[gi], z_s[gi], &inv_s[gi], gamma, cos_sin, rd, eps, pos, dst, f8);
 }
 
 size_t publish_groups_lds(int Din) {
@@ -247,7 +268,8 @@ idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float*
                         const float* cos_sin, int P, int B, int G, int Din, int D, int rd,
                         float eps, int start_pos, int ratio, uint8_t* k_cache,
                         int64_t k_batch_stride_rows, int Tcap, const int32_t* bt,
-                        int64_t bt_stride, int64_t page_stride, int n_pages, void* stream) {
+                        int64_t bt_stride, int64_t page_stride, int n_pages, void* stream,
+                        bool f8 = false) {
   if (B < 0 || G < 0 || Din <= 0 || D <= 0 || ratio <= 0 || start_pos < 0 || P < 0 || Tcap < 0)
     return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
@@ -281,13 +303,13 @@ idx_status publish_impl(const uint16_t* latent, const uint16_t* wk, const float*
     hipLaunchKernelGGL(idx::publish_groups_kernel, dim3((unsigned)nwg),
                        dim3(idx::kPubGroups * idx::kHeadDim), idx::publish_groups_lds(Din), st,
                        latent, wk, gamma, cos_sin, Din, rd, eps, start_pos, ratio, B, G, k_cache,
-                       k_batch_stride_rows, bt, bt_stride, page_stride, n_pages);
+                       k_batch_stride_rows, bt, bt_stride, page_stride, n_pages, f8);
     return idx_host::launch_status();
   }
   hipLaunchKernelGGL(idx::publish_kernel, dim3((unsigned)(B * G)), dim3(idx::kHeadDim),
                      (size_t)Din * 2, st, latent, wk, gamma, cos_sin, Din, rd, eps,
                      start_pos, ratio, G, k_cache, k_batch_stride_rows, bt, bt_stride,
-                     page_stride, n_pages);
+                     page_stride, n_pages, f8);
   return idx_host::launch_status();
 }
 }  // namespace
@@ -299,6 +321,15 @@ extern "C" idx_status idx_publish_keys(const uint16_t* latent, const uint16_t* w
                                        int Tcap, void* stream) {
   return publish_impl(latent, wk, gamma, cos_sin, P, B, G, Din, D, rd, eps, start_pos, ratio,
                       k_cache, k_batch_stride_rows, Tcap, nullptr, 0, 0, 0, stream);
+}
+
+extern "C" idx_status idx_publish_keys_fp8(const uint16_t* latent, const uint16_t* wk,
+                                           const float* gamma, const float* cos_sin, int P, int B,
+                                           int G, int Din, int D, int rd, float eps, int start_pos,
+                                           int ratio, uint8_t* k_cache,
+                                           int64_t k_batch_stride_rows, int Tcap, void* stream) {
+  return publish_impl(latent, wk, gamma, cos_sin, P, B, G, Din, D, rd, eps, start_pos, ratio,
+                      k_cache, k_batch_stride_rows, Tcap, nullptr, 0, 0, 0, stream, true);
 }
 
 extern "C" idx_status idx_publish_keys_paged(const uint16_t* latent, const uint16_t* wk,

@@ -49,6 +49,46 @@ __global__ __launch_bounds__(256) void fp4_quant_kernel(const uint16_t* __restri
   }
 }
 
+// FP8 rows ([VLLM, _indexer_k_cache_head_dim]: 128 e4m3 bytes and one fp32
+// ue8m0 scale per 128 values): four threads per row, 32 values each, the
+// block's scale agreed between them (quant_block128_f8).
+__global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t n_quads,
+                                                        uint8_t* __restrict__ rows,
+                                                        uint16_t* __restrict__ rt) {
+  const int64_t qd = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (qd >= n_quads) return;  // whole rows: the four lanes of a row leave together
+  const int64_t row = qd >> 2;
+  const int j = (int)(qd & 3);
+  const uint4* src = reinterpret_cast<const uint4*>(x + qd * kBlock);
+  uint32_t xp[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    xp[4 * i + 0] = v.x;
+    xp[4 * i + 1] = v.y;
+    xp[4 * i + 2] = v.z;
+    xp[4 * i + 3] = v.w;
+  }
+  uint32_t codes[8];
+  const int e = quant_block128_f8(xp, codes);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(rows + row * kRowBytesF8);  // 4-byte aligned
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dst[8 * j + i] = codes[i];
+  if (j == 0) dst[32] = (uint32_t)(127 + e) << 23;  // the scale 2^e as fp32
+  if (rt) {
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = codes[i / 2] >> (16 * (i % 2));
+      out[i] = e4m3_dequant_bf16(w & 0xffu, e) | (e4m3_dequant_bf16((w >> 8) & 0xffu, e) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(rt + qd * kBlock);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  }
+}
+
 // The query step ([IDX, forward: the query heads' RoPE on the last rd dims
 // at positions start_pos + s, fp4_act_quant, weights_proj(x) * softmax_scale
 // * n_heads^-0.5]; [VLLM, fused_indexer_q_rope_quant] fuses the three).
@@ -165,5 +205,21 @@ extern "C" idx_status idx_fp4_quant(const uint16_t* x, int64_t n_rows, uint8_t* 
   if (grid > 0x7fffffffLL) return IDX_EINVAL;
   hipLaunchKernelGGL(idx::fp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0,
                      (hipStream_t)stream, x, n_blocks, rows68, roundtrip);
+  return idx_host::launch_status();
+}
+
+extern "C" idx_status idx_fp8_quant(const uint16_t* x, int64_t n_rows, uint8_t* rows132,
+                                    uint16_t* roundtrip, void* stream) {
+  if (n_rows < 0) return IDX_EINVAL;
+  if (n_rows == 0) return IDX_OK;
+  if (!x || !rows132) return IDX_EINVAL;
+  if (!idx_host::aligned(x, 16) || !idx_host::aligned(roundtrip, 16) ||
+      !idx_host::aligned(rows132, 4))
+    return IDX_EINVAL;
+  const int64_t n_quads = n_rows * 4;
+  const int64_t grid = (n_quads + 255) / 256;
+  if (grid > 0x7fffffffLL) return IDX_EINVAL;
+  hipLaunchKernelGGL(idx::fp8_quant_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)stream, x, n_quads, rows132, roundtrip);
   return idx_host::launch_status();
 }

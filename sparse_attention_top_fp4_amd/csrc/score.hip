@@ -61,10 +61,16 @@ constexpr int kMaxCand = 2048;  // candidate blocks per row held in LDS
 #endif
 constexpr int kTileSets = IDX_SCORE_TILE_SETS;  // key tiles per wave held in registers
 
-struct KeyTile {
-  u32x4 c[2][2];   // [key tile][K-step]: 16 code bytes of block 2*step + lane/32
-  uint32_t sc[2];  // [key tile]: the row's four scale bytes
+// fp4 rows: [key tile][K-step] 16 code bytes of block 2*step + lane/32, and
+// the row's four scale bytes.  fp8 rows (F8): [key tile][K-step] 32 code
+// bytes (two words of 16), K-half lane/32 of the step, and the row's fp32
+// scale.
+template <bool F8 = false>
+struct KeyTileT {
+  u32x4 c[2][2][F8 ? 2 : 1];
+  uint32_t sc[2];
 };
+typedef KeyTileT<false> KeyTile;
 
 // Virtual position v -> key position.  Plain mode scores positions
 // [0, limit) directly; candidate mode (level two) walks the listed blocks.
@@ -114,14 +120,52 @@ struct PageMap {
 
 // Paged tiles take their page id from `page` (uniform; see the caller).
 // Candidate mode on pages: bt_lds holds the row's page ids (in LDS).
-template <bool CAND>
-__device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
-                                             const PosMap<CAND>& pm, int v0, int lane,
-                                             bool paged = false, int page = -1,
-                                             int64_t page_stride = 0, int n_pages = 0,
-                                             const int32_t* bt_lds = nullptr) {
-  KeyTile kt;
+template <bool CAND, bool F8 = false>
+__device__ __forceinline__ KeyTileT<F8> load_tile(const uint8_t* __restrict__ kseq,
+                                                  const PosMap<CAND>& pm, int v0, int lane,
+                                                  bool paged = false, int page = -1,
+                                                  int64_t page_stride = 0, int n_pages = 0,
+                                                  const int32_t* bt_lds = nullptr) {
+  KeyTileT<F8> kt;
   const int half = lane >> 5;
+  if constexpr (F8) {
+    // 132-byte rows: K-step s, K-half `half` is bytes 64s + 32 half of the
+    // codes; the scale word sits at byte 128.  Plain mode streams through a
+    // buffer resource as the fp4 path does; candidate mode maps per lane.
+    if constexpr (!CAND) {
+      const int left = pm.vlim - v0;
+      const int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytesF8 : 0;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(kseq + (int64_t)v0 * kRowBytesF8), (short)0, nrec, kBufWord3);
+      const int vs = (lane & 31) * kRowBytesF8, vc = vs + 32 * half;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int o = vc + 32 * kRowBytesF8 * t;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const auto c = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 64 * st + 16 * q, 0, 0);
+            kt.c[t][st][q] = u32x4{c[0], c[1], c[2], c[3]};
+          }
+        }
+        kt.sc[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 32 * kRowBytesF8 * t + 128, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int p = pm.pos(v0 + 32 * t + (lane & 31));
+        const uint8_t* row = kseq + (int64_t)(p < 0 ? 0 : p) * kRowBytesF8;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          kt.c[t][st][0] = ld16(row + 64 * st + 32 * half);
+          kt.c[t][st][1] = ld16(row + 64 * st + 32 * half + 16);
+        }
+        kt.sc[t] = *reinterpret_cast<const uint32_t*>(row + 128);
+      }
+    }
+    return kt;
+  }
   if constexpr (!CAND) {
     const int left = pm.vlim - v0;
     int nrec = left > 0 ? (left < 64 ? left : 64) * kRowBytes : 0;
@@ -139,8 +183,8 @@ __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
     for (int t = 0; t < 2; ++t) {
       const auto c0 = __builtin_amdgcn_raw_buffer_load_b128(rs, vc + 32 * kRowBytes * t, 0, 0);
       const auto c1 = __builtin_amdgcn_raw_buffer_load_b128(rs, vc + 32 * kRowBytes * t + 32, 0, 0);
-      kt.c[t][0] = u32x4{c0[0], c0[1], c0[2], c0[3]};
-      kt.c[t][1] = u32x4{c1[0], c1[1], c1[2], c1[3]};
+      kt.c[t][0][0] = u32x4{c0[0], c0[1], c0[2], c0[3]};
+      kt.c[t][1][0] = u32x4{c1[0], c1[1], c1[2], c1[3]};
       kt.sc[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs + 32 * kRowBytes * t + 64, 0, 0);
     }
     return kt;
@@ -155,12 +199,12 @@ __device__ __forceinline__ KeyTile load_tile(const uint8_t* __restrict__ kseq,
       zero = p >= 0 && (pgid < 0 || pgid >= n_pages);
       row = kseq + (zero || p < 0 ? 0 : (int64_t)pgid * page_stride + (int64_t)(p & 63) * kRowBytes);
     }
-    kt.c[t][0] = ld16(row + 16 * half);
-    kt.c[t][1] = ld16(row + 32 + 16 * half);
+    kt.c[t][0][0] = ld16(row + 16 * half);
+    kt.c[t][1][0] = ld16(row + 32 + 16 * half);
     kt.sc[t] = *reinterpret_cast<const uint32_t*>(row + 64);
     if (zero) {
-      kt.c[t][0] = u32x4{0u, 0u, 0u, 0u};
-      kt.c[t][1] = u32x4{0u, 0u, 0u, 0u};
+      kt.c[t][0][0] = u32x4{0u, 0u, 0u, 0u};
+      kt.c[t][1][0] = u32x4{0u, 0u, 0u, 0u};
       kt.sc[t] = 0u;
     }
   }
@@ -181,8 +225,8 @@ __device__ __forceinline__ float relu_bits(float x) {
 // of the heads of key n of each key tile (two chains, heads ascending, from
 // +0); the swap hands the low half-wave the chains of key tile 0 and the
 // high half-wave those of key tile 1, and score = low chain + high chain.
-template <int HT>
-__device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)[HT][2],
+template <int HT, bool F8 = false>
+__device__ __forceinline__ float head_sum_tile(const KeyTileT<F8>& kt, const v8i (&A)[HT][2],
                                                const int (&sA)[HT][2],
                                                const float (&wv)[16 * HT], int lane) {
   float ch[2] = {0.0f, 0.0f};  // this half-wave's chain for key tile 0 and 1
@@ -191,16 +235,32 @@ __device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       v16f acc = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      // the high half-wave's blocks are the odd ones: shift its scale bytes
-      // down by one, then the MFMA's scale byte select (op_sel) picks byte 2s
-      const int scs = (int)(kt.sc[t] >> (8 * (lane >> 5)));
-      const u32x4 c0 = kt.c[t][0], c1 = kt.c[t][1];
-      const v8i B0 = v8i{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, 0, 0, 0, 0};
-      const v8i B1 = v8i{(int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w, 0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][0], B0, acc, 4, 4, 0, sA[ht][0],
-                                                            0, scs);
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][1], B1, acc, 4, 4, 0, sA[ht][1],
-                                                            2, scs);
+      if constexpr (F8) {
+        // e4m3 operands (format code 0), 32 bytes a lane; one scale for the
+        // whole row: the exponent byte of the fp32 scale is its e8m0 code
+        const int scs = (int)((kt.sc[t] >> 23) & 0xffu);
+        const u32x4 a0 = kt.c[t][0][0], a1 = kt.c[t][0][1], b0 = kt.c[t][1][0],
+                    b1 = kt.c[t][1][1];
+        const v8i B0 = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        const v8i B1 = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                           (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][0], B0, acc, 0, 0, 0,
+                                                              sA[ht][0], 0, scs);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][1], B1, acc, 0, 0, 0,
+                                                              sA[ht][1], 0, scs);
+      } else {
+        // the high half-wave's blocks are the odd ones: shift its scale bytes
+        // down by one, then the MFMA's scale byte select (op_sel) picks byte 2s
+        const int scs = (int)(kt.sc[t] >> (8 * (lane >> 5)));
+        const u32x4 c0 = kt.c[t][0][0], c1 = kt.c[t][1][0];
+        const v8i B0 = v8i{(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, 0, 0, 0, 0};
+        const v8i B1 = v8i{(int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w, 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][0], B0, acc, 4, 4, 0,
+                                                              sA[ht][0], 0, scs);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[ht][1], B1, acc, 4, 4, 0,
+                                                              sA[ht][1], 2, scs);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) ch[t] = __builtin_fmaf(relu_bits(acc[i]), wv[16 * ht + i], ch[t]);
     }
@@ -213,12 +273,12 @@ __device__ __forceinline__ float head_sum_tile(const KeyTile& kt, const v8i (&A)
 }
 
 // Score tile of the one-row kernel: staged in LDS, histogram in LDS.
-template <int HT, bool CAND>
-__device__ __forceinline__ void score_tile(const KeyTile& kt, const v8i (&A)[HT][2],
+template <int HT, bool CAND, bool F8 = false>
+__device__ __forceinline__ void score_tile(const KeyTileT<F8>& kt, const v8i (&A)[HT][2],
                                            const int (&sA)[HT][2], const float (&wv)[16 * HT],
                                            const PosMap<CAND>& pm, float* __restrict__ sbuf, int v0,
                                            int vbeg, int lane, uint32_t* hist_s) {
-  const float sc = head_sum_tile<HT>(kt, A, sA, wv, lane);
+  const float sc = head_sum_tile<HT, F8>(kt, A, sA, wv, lane);
   sbuf[v0 - vbeg + lane] = sc;  // staged in LDS, written out when the chunk is done
   if (hist_s) {
     // the head sum never yields -0 (two chains from +0, then their sum), so
@@ -279,7 +339,7 @@ __device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint
 // tile sets per wave (at most 128 VGPRs) and 40 KB of LDS, the 8 KB
 // histogram plus the 32 KB score buffer, which also holds the query rows
 // until they are in registers and the ranking's scan words.
-template <int HT, bool CAND, bool TOPK>
+template <int HT, bool CAND, bool TOPK, bool F8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TOPK ? 4 : 1))) void
 score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ q4,
@@ -287,11 +347,13 @@ score_kernel(
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
     FusedTopk tk, PageMap pg) {
+  static_assert(!(F8 && TOPK), "the fp8 rows have no fused ranking");
   constexpr int H = 32 * HT;
   constexpr int kSets = TOPK ? 2 : kTileSets;  // key tile sets in registers
+  constexpr int QW = F8 ? kRowBytesF8 / 4 : kRowBytes / 4;  // words of a quantised head
   __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
   __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
-  __shared__ uint32_t qs_own[TOPK ? 1 : H * 17];
+  __shared__ uint32_t qs_own[TOPK ? 1 : H * QW];
   extern __shared__ __attribute__((aligned(16))) float sbuf[];  // this chunk's scores
   // H quantised query rows of 68 bytes; the fused kernel keeps them at the
   // start of its score buffer (kFusedMaxT words), free until the first tile
@@ -344,7 +406,7 @@ score_kernel(
   // are in flight
   // contiguous: the sequence's rows; paged: the page pool (plain mode only)
   const bool paged = !CAND && pg.bt;  // plain mode: pages by readlane (below)
-  const uint8_t* kseq = paged ? kc : kc + (int64_t)b * kstride * kRowBytes;
+  const uint8_t* kseq = paged ? kc : kc + (int64_t)b * kstride * (F8 ? kRowBytesF8 : kRowBytes);
   const int ntiles = (vend - vbeg + 63) >> 6;
   int j = __builtin_amdgcn_readfirstlane(wave);  // uniform: tile bases stay scalar
   // paged: lane i holds the page of this wave's i-th tile (tile j + 4i; a
@@ -360,11 +422,11 @@ score_kernel(
     return paged ? __builtin_amdgcn_readlane(pid_lane, i < 63 ? i : 63) : -1;
   };
   int it = 0;  // tiles of this wave started
-  KeyTile buf[kSets];
+  KeyTileT<F8> buf[kSets];
 #pragma unroll
   for (int i = 0; i < kSets - 1; ++i)
-    buf[i] = load_tile(kseq, pm, vbeg + 64 * (j + 4 * i), lane, paged, tile_page(i),
-                       pg.page_stride, pg.n_pages, bt_lds);
+    buf[i] = load_tile<CAND, F8>(kseq, pm, vbeg + 64 * (j + 4 * i), lane, paged, tile_page(i),
+                                 pg.page_stride, pg.n_pages, bt_lds);
 
   uint32_t* hist_s = (key_hist || TOPK) ? hist_lds : nullptr;
   if (hist_s)
@@ -373,6 +435,29 @@ score_kernel(
   // --- the query row in LDS: given quantised (q4: H rows of 68 bytes, the
   // LDS layout itself), or quantised here, thread (h, g) handling block g
   // of head h
+  if constexpr (F8) {
+    // fp8 heads: four threads per head (32 values each), one e4m3 scale for
+    // the head's 128 values; qs holds H rows of 132 bytes
+    if (tid < 4 * H) {
+      const int h = tid >> 2, g = tid & 3;
+      const uint4* src =
+          reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kHeadDim + 32 * g);
+      uint32_t xp[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        xp[4 * i] = v.x;
+        xp[4 * i + 1] = v.y;
+        xp[4 * i + 2] = v.z;
+        xp[4 * i + 3] = v.w;
+      }
+      uint32_t codes[8];
+      const int e = quant_block128_f8(xp, codes);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[h * QW + 8 * g + i] = codes[i];
+      if (g == 0) qs[h * QW + 32] = (uint32_t)(127 + e) << 23;
+    }
+  } else {
   if (q4) {  // uniform
     const uint32_t* src = reinterpret_cast<const uint32_t*>(q4 + (int64_t)r * H * kRowBytes);
     for (int i = tid; i < H * 17; i += 256) qs[i] = src[i];
@@ -394,6 +479,7 @@ score_kernel(
     for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
     reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
   }
+  }
 
   // weights of the heads this lane's half-wave sums: wv[j] = w[r][H/2*half + j]
   float wv[16 * HT];
@@ -413,10 +499,18 @@ score_kernel(
     const int h = head_of_row<HT>(ht, lane & 31);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int g = 2 * s + (lane >> 5);
-      const uint32_t* p = qs + h * 17 + 4 * g;
-      A[ht][s] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
-      sA[ht][s] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+      if constexpr (F8) {
+        // K-step s, K-half lane/32: bytes 64s + 32 (lane/32) of the head
+        const uint32_t* p = qs + h * QW + 16 * s + 8 * (lane >> 5);
+        A[ht][s] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3],
+                       (int)p[4], (int)p[5], (int)p[6], (int)p[7]};
+        sA[ht][s] = (int)((qs[h * QW + 32] >> 23) & 0xffu);
+      } else {
+        const int g = 2 * s + (lane >> 5);
+        const uint32_t* p = qs + h * 17 + 4 * g;
+        A[ht][s] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
+        sA[ht][s] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+      }
     }
   }
   if (TOPK) __syncthreads();  // the query rows' words are score slots from here on
@@ -428,9 +522,9 @@ score_kernel(
 #pragma unroll
     for (int u = 0; u < kSets; ++u) {
       buf[(u + kSets - 1) % kSets] =
-          load_tile(kseq, pm, vbeg + 64 * (j + 4 * (kSets - 1)), lane, paged,
-                    tile_page(it + kSets - 1), pg.page_stride, pg.n_pages, bt_lds);
-      score_tile<HT, CAND>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
+          load_tile<CAND, F8>(kseq, pm, vbeg + 64 * (j + 4 * (kSets - 1)), lane, paged,
+                              tile_page(it + kSets - 1), pg.page_stride, pg.n_pages, bt_lds);
+      score_tile<HT, CAND, F8>(buf[u], A, sA, wv, pm, sbuf, vbeg + 64 * j, vbeg, lane, hist_s);
       j += 4;
       ++it;
       if (j >= ntiles) goto done;
@@ -572,7 +666,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                       int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                       const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
                       int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
-                      idx::PageMap pg, void* stream) {
+                      idx::PageMap pg, void* stream, bool f8 = false) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -611,6 +705,11 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                                      : idx::score_kernel<2, false, false>)
                       : (cand_blocks ? idx::score_kernel<1, true, false>
                                      : idx::score_kernel<1, false, false>);
+  if (f8)
+    kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true, false, true>
+                                  : idx::score_kernel<2, false, false, true>)
+                   : (cand_blocks ? idx::score_kernel<1, true, false, true>
+                                  : idx::score_kernel<1, false, false, true>);
   return launch_score(kern, grid, lds, st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
@@ -669,6 +768,17 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                     cand_blocks,
                     n_cand, cand_block_size, scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_score_fp8(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                    int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                                    const int32_t* compress_lens, const int32_t* cand_blocks,
+                                    int n_cand, int cand_block_size, float* scores, int64_t ld,
+                                    uint32_t* key_hist, void* stream) {
+  if (!q && (int64_t)B * S > 0 && T > 0) return IDX_EINVAL;
+  return score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                    cand_blocks, n_cand, cand_block_size, scores, ld, key_hist,
+                    idx::PageMap{nullptr, 0, 0, 0}, stream, true);
 }
 
 extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,

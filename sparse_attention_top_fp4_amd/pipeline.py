@@ -15,7 +15,8 @@ import ctypes
 import numpy as np
 
 from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
-               idx_publish_keys, idx_publish_keys_paged, idx_q_rope_quant, idx_score, idx_score_paged,
+               idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
+               idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
                idx_topk, idx_topk_candidates,
@@ -36,12 +37,14 @@ def to_device(a: np.ndarray):
     return torch.from_numpy(a).cuda()
 
 
-def quantize_cache(k_bf16_dev):
-    """bf16 keys [B, T, 128] on device -> 68-byte rows [B, T, 68]."""
+def quantize_cache(k_bf16_dev, fp8=False):
+    """bf16 keys [B, T, 128] on device -> 68-byte fp4 rows [B, T, 68], or
+    132-byte FP8 rows [B, T, 132]."""
     torch = _torch()
-    rows = torch.empty(tuple(k_bf16_dev.shape[:-1]) + (68,), dtype=torch.uint8,
+    rb = 132 if fp8 else 68
+    rows = torch.empty(tuple(k_bf16_dev.shape[:-1]) + (rb,), dtype=torch.uint8,
                        device=k_bf16_dev.device)
-    idx_fp4_quant(k_bf16_dev, rows)
+    (idx_fp8_quant if fp8 else idx_fp4_quant)(k_bf16_dev, rows)
     return rows
 
 
@@ -55,15 +58,20 @@ class IndexerStep:
     FUSED_MAX_T = 8192
 
     def __init__(self, wl, inp: dict, n_caches: int = 1, keep_scores: bool = True,
-                 paged: bool = False, q_step: bool = False, publish=None):
+                 paged: bool = False, q_step: bool = False, publish=None, fp8: bool = False):
         torch = _torch()
         self.wl = wl
         R, T = wl.R, wl.T
+        # fp8: the key cache holds FP8 rows (132 bytes) and every step scores
+        # them with idx_score_fp8 (no fused launch, no pages, no query step)
+        self.fp8 = fp8
+        if fp8 and (paged or q_step):
+            raise ValueError("the FP8 cache is contiguous and takes bf16 query heads")
         self.q = to_device(inp["q"])
         self.w = to_device(inp["w"])
         self.cl = to_device(inp["cl"])
         k = to_device(inp["k"])
-        self.caches = [quantize_cache(k)]
+        self.caches = [quantize_cache(k, fp8=fp8)]
         del k
         for _ in range(1, n_caches):
             self.caches.append(self.caches[0].clone())
@@ -86,7 +94,7 @@ class IndexerStep:
             self.caches = pools
         # single-level rows up to FUSED_MAX_T take the fused score + top-k
         # launch; its scores are written only when kept
-        self.fused = not wl.ctb and T <= self.FUSED_MAX_T
+        self.fused = not wl.ctb and T <= self.FUSED_MAX_T and not fp8
         self.scores = None
         if keep_scores or not self.fused:
             self.scores = torch.empty((R, T), dtype=torch.float32, device="cuda")
@@ -174,8 +182,9 @@ class IndexerStep:
                                                     wl.start_pos, wl.ratio, wl.eps, kc,
                                                     self.block_table, wl.T, rd=wl.rd, **b))
             else:
-                calls.append(idx_publish_keys(self.latent, self.wk, self.gamma, self.cos_sin,
-                                              wl.start_pos, wl.ratio, wl.eps, kc, rd=wl.rd, **b))
+                pub = idx_publish_keys_fp8 if self.fp8 else idx_publish_keys
+                calls.append(pub(self.latent, self.wk, self.gamma, self.cos_sin, wl.start_pos,
+                                 wl.ratio, wl.eps, kc, rd=wl.rd, **b))
         q, w = self.q, self.w
         q4 = None  # the quantised heads, when the score takes them directly
         if self.q_step:
@@ -211,8 +220,9 @@ class IndexerStep:
             calls.append(idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                                       key_hist=self.key_hist, **b))
         else:
-            calls.append(idx_score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
-                                   key_hist=self.key_hist, **b))
+            score = idx_score_fp8 if self.fp8 else idx_score
+            calls.append(score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                               key_hist=self.key_hist, **b))
         if self.two_level:
             calls.append(idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs,
                                                      self.ids, workspace=self.sel_ws, **b))
@@ -226,9 +236,10 @@ class IndexerStep:
                                              cand_block_size=wl.cbs, key_hist=self.key_hist,
                                              **b))
             else:
-                calls.append(idx_score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
-                                       cand_blocks=self.ids, cand_block_size=wl.cbs,
-                                       key_hist=self.key_hist, **b))
+                score = idx_score_fp8 if self.fp8 else idx_score
+                calls.append(score(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl, self.scores2,
+                                   cand_blocks=self.ids, cand_block_size=wl.cbs,
+                                   key_hist=self.key_hist, **b))
             calls.append(idx_topk_candidates(self.scores2, wl.T, self.cl, self.ids, wl.cbs,
                                              wl.topk, wl.offset, self.out,
                                              key_hist=self.key_hist, **b))
