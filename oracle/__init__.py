@@ -40,6 +40,11 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
                    rounded once to fp32.
   score_fp8        pinned: on fp4 round trips with equal block scales (exactly
                    representable in e4m3) it equals score() bit for bit.
+  score_bf16_literal  DIAGNOSTIC only (not compared with the GPU): the page's
+                   bf16 tensor pipeline, for the top-k overlap against the
+                   fp32 contract.  Pinned: one head with unit weight gives
+                   bf16(relu(dot)); the fp4 row decoding equals the
+                   quantiser's round trip.
   head sum order   the fp32 two-chain association is a contract shared with
                    the GPU library (split chosen to match the matrix core's
                    half-wave layout); the pages fix none.  A hand-worked
@@ -325,6 +330,69 @@ def q_rope_quant(q, w_raw, scale, cos_sin, start_pos, S, rd=64):
                            cos_sin.shape[0], R // S, S, H, rd, start_pos, _p(rows), _p(rt),
                            _p(pre), _p(w_out))
     return rows, rt, pre, w_out
+
+
+# ------------------------------------------- literal bf16 pipeline (C6)
+def _bf16_round(x):
+    """float64 -> nearest bf16 value (ties to even), as float64, through
+    float32 (exact for the values used here: every input is a float32)."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def score_bf16_literal(q, w, kc, S, H, T, cl):
+    """DIAGNOSTIC, not the contract: the Indexer's score as the page's torch
+    ops compute it in bf16 ([IDX, forward]: einsum of the fp4 round trips
+    into a bf16 tensor, relu_, times weights.unsqueeze(-1) into bf16,
+    .sum(dim=2) into bf16; [CMP] 'Module compress', precision: the scores
+    are bf16 tensors).  The einsum's dots are exact in fp32 (so bf16 of the
+    exact dot), the elementwise product is rounded to bf16, and the head sum
+    is accumulated in float64 and rounded once to bf16 (a bf16 reduction
+    accumulates wider than bf16; its order is the library's).  Positions
+    t >= cl are -inf.  Returns float64 [R][T]."""
+    _, qrt = fp4_quant_rows(q)
+    kd = np.stack([_dequant_rows(kc[b, :T]) for b in range(kc.shape[0])])
+    qd = (np.ascontiguousarray(qrt, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    wd = (np.ascontiguousarray(w, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    R = q.shape[0]
+    out = np.full((R, T), -np.inf)
+    for r in range(R):
+        d = qd[r].astype(np.float64) @ kd[r // S].T.astype(np.float64)   # [H][T], exact
+        e = _bf16_round(np.maximum(_bf16_round(d), 0.0))                  # einsum, relu_
+        m = _bf16_round(e * wd[r][:, None].astype(np.float64))            # * weights
+        sc = _bf16_round(m.sum(axis=0))                                   # sum over heads
+        c = int(min(max(cl[r], 0), T))
+        out[r, :c] = sc[:c]
+    return out
+
+
+def _dequant_rows(rows68):
+    """fp4 rows [n][68] -> their values [n][128] float32 (decoding the row
+    layout: element 2i in the low nibble of byte i, byte 64+j = e_j + 127)."""
+    rows68 = np.ascontiguousarray(rows68, np.uint8)
+    nib = np.empty(rows68.shape[:-1] + (128,), np.uint8)
+    nib[..., 0::2] = rows68[..., :64] & 0xF
+    nib[..., 1::2] = rows68[..., :64] >> 4
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    mag = grid[nib & 7]
+    sgn = np.where(nib & 8, -1.0, 1.0)
+    e = rows68[..., 64:68].astype(np.int64) - 127
+    scale = np.ldexp(1.0, np.repeat(e, 32, axis=-1))
+    return (sgn * mag * scale).astype(np.float32)
+
+
+def topk_overlap(s_a, s_b, cl, k):
+    """Mean over rows of |top-k(s_a) & top-k(s_b)| / k_row (ties to the lower
+    position on both sides)."""
+    a = topk(np.asarray(s_a, np.float32), cl, k)
+    b = topk(np.asarray(s_b, np.float32), cl, k)
+    fr = []
+    for r in range(a.shape[0]):
+        ra, rb = set(a[r][a[r] >= 0].tolist()), set(b[r][b[r] >= 0].tolist())
+        fr.append(len(ra & rb) / max(1, len(ra)))
+    return float(np.mean(fr))
 
 
 # ------------------------------------------------- tiny numpy brute force
