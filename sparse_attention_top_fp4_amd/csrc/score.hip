@@ -400,10 +400,33 @@ score_kernel(
     __syncthreads();
   }
 
-  // the first key tiles are requested before the query work, so their
-  // latency overlaps the query load and quantisation.  kSets register
-  // sets: while one tile computes, the next kSets - 1 tiles of this wave
-  // are in flight
+  // The query row and the weights are requested first, then the first key
+  // tiles: the query's latency overlaps the tiles' instead of queueing
+  // behind them (a workgroup cannot start its loop before its query is
+  // quantised).  Thread (h, g) = (tid / 4, tid % 4) loads block g of head h.
+  uint4 qv[4] = {};
+  uint32_t q4v[(H * 17 + 255) / 256] = {};
+  if (q4) {  // uniform: the quantised rows are the LDS layout itself
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q4 + (int64_t)r * H * kRowBytes);
+#pragma unroll
+    for (int k = 0; k < (H * 17 + 255) / 256; ++k)
+      if (tid + 256 * k < H * 17) q4v[k] = src[tid + 256 * k];
+  } else if (tid < 4 * H) {
+    const uint4* src =
+        reinterpret_cast<const uint4*>(q + ((int64_t)r * H + (tid >> 2)) * kHeadDim + 32 * (tid & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qv[i] = src[i];
+  }
+  // weights of the heads this lane's half-wave sums: wv[j] = w[r][H/2*half + j]
+  float wv[16 * HT];
+  {
+    const uint16_t* wrow = w + (int64_t)r * H + (lane >> 5) * (H / 2);
+#pragma unroll
+    for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(wrow[j]);
+  }
+
+  // kSets register sets of key tiles: while one tile computes, the next
+  // kSets - 1 tiles of this wave are in flight
   // contiguous: the sequence's rows; paged: the page pool (plain mode only)
   const bool paged = !CAND && pg.bt;  // plain mode: pages by readlane (below)
   const uint8_t* kseq = paged ? kc : kc + (int64_t)b * kstride * (F8 ? kRowBytesF8 : kRowBytes);
@@ -440,12 +463,10 @@ score_kernel(
     // the head's 128 values; qs holds H rows of 132 bytes
     if (tid < 4 * H) {
       const int h = tid >> 2, g = tid & 3;
-      const uint4* src =
-          reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kHeadDim + 32 * g);
       uint32_t xp[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v = src[i];
+        const uint4 v = qv[i];
         xp[4 * i] = v.x;
         xp[4 * i + 1] = v.y;
         xp[4 * i + 2] = v.z;
@@ -459,15 +480,15 @@ score_kernel(
     }
   } else {
   if (q4) {  // uniform
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(q4 + (int64_t)r * H * kRowBytes);
-    for (int i = tid; i < H * 17; i += 256) qs[i] = src[i];
+#pragma unroll
+    for (int k = 0; k < (H * 17 + 255) / 256; ++k)
+      if (tid + 256 * k < H * 17) qs[tid + 256 * k] = q4v[k];
   } else if (tid < 4 * H) {
     const int h = tid >> 2, g = tid & 3;
-    const uint4* src = reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * kHeadDim + 32 * g);
     uint32_t xp[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 v = src[i];
+      const uint4 v = qv[i];
       xp[4 * i] = v.x;
       xp[4 * i + 1] = v.y;
       xp[4 * i + 2] = v.z;
@@ -479,14 +500,6 @@ score_kernel(
     for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
     reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
   }
-  }
-
-  // weights of the heads this lane's half-wave sums: wv[j] = w[r][H/2*half + j]
-  float wv[16 * HT];
-  {
-    const uint16_t* wrow = w + (int64_t)r * H + (lane >> 5) * (H / 2);
-#pragma unroll
-    for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(wrow[j]);
   }
 
   __syncthreads();
