@@ -104,13 +104,20 @@ def reachable_pairs(wl) -> int:
     return int(np.minimum(wl.compress_lens().astype(np.int64), wl.T).sum())
 
 
-def score_kernel_bytes(wl, st=None, rb=68) -> int:
+def publish_bytes(wl, groups=1, rb=68) -> int:
+    """The key publish: wk once, each group's bf16 latent and its written row."""
+    return 128 * wl.din * 2 + wl.B * groups * (wl.din * 2 + rb)
+
+
+def score_kernel_bytes(wl, st=None, rb=68, publish=False) -> int:
     """Algorithmic HBM bytes of one (level-one) score launch: the key row
     (rb bytes: 68 fp4, 132 FP8) of every reachable (row, key) pair, each
-    row's quantised query heads (rb bytes a head) and its bf16 weights.  The
-    fp32 score scratch the launch also writes is an implementation cost, not
+    row's quantised query heads (rb bytes a head) and its bf16 weights, and
+    with `publish` the decode key publish the launch also runs.  The fp32
+    score scratch the launch also writes is an implementation cost, not
     algorithmic: it shows up in the measured traffic instead."""
-    return reachable_pairs(wl) * rb + wl.R * wl.H * (rb + 2)
+    b = reachable_pairs(wl) * rb + wl.R * wl.H * (rb + 2)
+    return b + (publish_bytes(wl, 1, rb) if publish else 0)
 
 
 def score_kernel_flops(wl, st=None) -> int:
@@ -139,11 +146,11 @@ def step_bytes(wl, q_step=False, prefill_publish_groups=0, rb=68) -> int:
         b += wl.R * min(wl.ctb, nb) * 4              # block ids
         b += wl.R * kout * 4                         # level-one indices
     if wl.publish:
-        b += 128 * wl.din * 2 + wl.B * wl.din * 2 + wl.B * rb
+        b += publish_bytes(wl, 1, rb)
     if q_step:
         b += wl.R * wl.H * (128 * 2 + 2)             # bf16 heads before RoPE, raw weights
     if prefill_publish_groups:
-        b += 128 * wl.din * 2 + wl.B * prefill_publish_groups * (wl.din * 2 + 68)
+        b += publish_bytes(wl, prefill_publish_groups, 68)
     return b
 
 
@@ -178,12 +185,14 @@ def score_kernel_name(st) -> str:
         return "idx::score_kernel<2, false, true> (score and top-k in one launch)"
     if getattr(st, "fp8", False):
         return "idx::score_kernel<2, false, false, true> (FP8 rows)"
+    if getattr(st, "publish_in_score", False):
+        return "idx::score_kernel<2, false, false> (with the key publish workgroups)"
     return "idx::score_kernel<2, false, false>"
 
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("score.hip", "idx_common.hpp", "row_topk.hpp"):
+    for name in ("score.hip", "idx_common.hpp", "row_topk.hpp", "publish_dev.hpp"):
         with open(os.path.join(ROOT, "sparse_attention_top_fp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -369,7 +378,7 @@ def main():
 
     step_s = (t1 - t0) / args.steps
     score_ms = float(np.mean(score_ms_all))
-    kb = score_kernel_bytes(wl, rb=rb)
+    kb = score_kernel_bytes(wl, rb=rb, publish=getattr(st, "publish_in_score", False))
     kf = score_kernel_flops(wl)
     groups = wl.S // wl.ratio if args.prefill_publish else 0
     sb = step_bytes(wl, q_step=args.q_step, prefill_publish_groups=groups, rb=rb)

@@ -456,6 +456,30 @@ idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, co
                                   int64_t bt_stride, int Tcap, void *stream);
 
 /*
+ * idx_publish_score -- idx_publish_keys then idx_score for a decode step
+ * that publishes its completed group ([IDX, forward]: the key-owning layer
+ * stores k = k_norm(wk(latent)) with RoPE and the fp4 round trip at
+ * start_pos // ratio before the score reads the cache; [VLLM]: "K write
+ * must land before indexer_op reads the cache").  One query row and one
+ * group per sequence (S = G = 1).  When the new key is the last scored
+ * position (start_pos // ratio == T - 1, the usual decode step), both run
+ * in one launch: one extra workgroup per sequence publishes the row and
+ * scores that key itself, and the other workgroups score positions
+ * [0, T - 1), so the publish overlaps the score.  Otherwise the two calls
+ * run one after the other on the stream.  Arguments, results and errors as
+ * the two calls (latent [B][1][Din], k_cache rows of 68 bytes with stride
+ * k_batch_stride_rows, which also bounds the published row); the cache row,
+ * the scores and key_hist equal those of the two calls bit for bit for the
+ * documented inputs.  Din <= 2048 for the single launch.
+ */
+idx_status idx_publish_score(const uint16_t *latent, const uint16_t *wk, const float *gamma,
+                             const float *cos_sin, int P, int Din, int rd, float eps,
+                             int start_pos, int ratio, const uint16_t *q, const uint16_t *w,
+                             uint8_t *k_cache, int64_t k_batch_stride_rows, int B, int H, int D,
+                             int T, const int32_t *compress_lens, float *scores, int64_t ld,
+                             uint32_t *key_hist, void *stream);
+
+/*
  * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys and
  * idx_q_rope_quant ([CMP, yarn_freqs_cis]: precompute_freqs_cis with YaRN;
  * the YaRN method of Peng et al.).  Pair i of the rd rotated dims has the

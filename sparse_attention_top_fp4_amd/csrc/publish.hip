@@ -16,88 +16,13 @@
 // before the score of the same step reads the cache, which the caller gets
 // by issuing both on one stream.
 #include "idx_common.hpp"
+#include "publish_dev.hpp"
 
 #include <math.h>
 
 #include <atomic>
 
 namespace idx {
-
-// Steps after the linear layer, for the 128 threads o = 0..127 of a group
-// (every thread of the workgroup takes the barriers; threads with o >= 128
-// only take them): k_norm, RoPE at `pos`, quantise, store the row at dst
-// (null: not stored).  y_s: the group's bf16 outputs as floats.
-__device__ __forceinline__ void publish_finish(int o, const float* y_s, uint32_t* z_s,
-                                               float* inv_s, const float* __restrict__ gamma,
-                                               const float* __restrict__ cos_sin, int rd,
-                                               float eps, int pos, uint8_t* __restrict__ dst,
-                                               bool f8) {
-
-  if (o == 0) {
-    float yv[kHeadDim];
-#pragma unroll
-    for (int j = 0; j < kHeadDim; ++j) yv[j] = y_s[j];
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kHeadDim; ++j) ss = __builtin_fmaf(yv[j], yv[j], ss);
-    const float mean = ss / (float)kHeadDim;
-    *inv_s = 1.0f / sqrtf(mean + eps);
-  }
-  __syncthreads();
-  if (o < kHeadDim) {
-    float v = y_s[o] * *inv_s;
-    v = v * gamma[o];
-    z_s[o] = f32_to_bf16(v);
-  }
-  __syncthreads();
-
-  const int base = kHeadDim - rd;
-  uint32_t r0 = 0, r1 = 0;
-  const bool lead = o < kHeadDim && o >= base && ((o - base) & 1) == 0;
-  if (lead) {
-    const int i = (o - base) >> 1;
-    const float x0 = bf16f(z_s[o]), x1 = bf16f(z_s[o + 1]);
-    const float c = cos_sin[((int64_t)pos * (rd / 2) + i) * 2];
-    const float s = cos_sin[((int64_t)pos * (rd / 2) + i) * 2 + 1];
-    const float a = x0 * c, bb = x1 * s, cc = x0 * s, dd = x1 * c;
-    r0 = f32_to_bf16(a - bb);
-    r1 = f32_to_bf16(cc + dd);
-  }
-  __syncthreads();
-  if (lead) {
-    z_s[o] = r0;
-    z_s[o + 1] = r1;
-  }
-  __syncthreads();
-
-  if (f8) {
-    // FP8 row: one e4m3 scale for the 128 values; every thread finds the
-    // amax itself (LDS broadcast reads, no further barrier) and writes its
-    // own code byte
-    if (o < kHeadDim && dst) {
-      uint32_t amax = 0;
-      for (int j = 0; j < kHeadDim; ++j) {
-        const uint32_t a = z_s[j] & 0x7fffu;
-        amax = a > amax ? a : amax;
-      }
-      const int e = ue8m0_exponent_f8(bf16f(amax));
-      dst[o] = (uint8_t)e4m3_code(z_s[o], e);
-      if (o == 0) *reinterpret_cast<uint32_t*>(dst + 128) = (uint32_t)(127 + e) << 23;
-    }
-    return;
-  }
-  if (o < 4 && dst) {
-    uint32_t xp[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xp[i] = z_s[32 * o + 2 * i] | (z_s[32 * o + 2 * i + 1] << 16);
-    uint32_t codes[4];
-    const int e = quant_block32(xp, codes);
-    uint32_t* dcodes = reinterpret_cast<uint32_t*>(dst + 16 * o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dcodes[i] = codes[i];
-    dst[64 + o] = (uint8_t)(e + 127);
-  }
-}
 
 constexpr int kPubPageRows = 64;  // compressed positions per page of a paged cache
 
@@ -122,33 +47,7 @@ __global__ __launch_bounds__(128) void publish_kernel(
   for (int i = o; i < Din; i += kHeadDim) lat_s[i] = latent[(int64_t)bg * Din + i];
   __syncthreads();
 
-  // y_o: the row of wk in chunks of 256 values; each chunk's wk loads and
-  // latent reads are issued together before its fixed-order fma chain
-  const uint16_t* wrow = wk + (int64_t)o * Din;
-  float acc = 0.0f;
-  int i = 0;
-  if ((Din & 7) == 0 && (reinterpret_cast<uintptr_t>(wk) & 15) == 0) {
-    const uint4* w4 = reinterpret_cast<const uint4*>(wrow);
-    const uint4* l4 = reinterpret_cast<const uint4*>(lat_s);
-    for (; i + 256 <= Din; i += 256) {
-      uint4 wv[32], lv[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) wv[j] = w4[i / 8 + j];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) lv[j] = l4[i / 8 + j];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t u[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-        const uint32_t l[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          acc = __builtin_fmaf(bf16f(u[m] & 0xffffu), bf16f(l[m] & 0xffffu), acc);
-          acc = __builtin_fmaf(bf16f(u[m] >> 16), bf16f(l[m] >> 16), acc);
-        }
-      }
-    }
-  }
-  for (; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), bf16f(lat_s[i]), acc);
+  const float acc = publish_linear(o, lat_s, wk, Din);
   y_s[o] = bf16f(f32_to_bf16(acc));
   __syncthreads();
   // contiguous rows, or slot row % 64 of the sequence's page row / 64 (a
@@ -161,7 +60,8 @@ __global__ __launch_bounds__(128) void publish_kernel(
     if (page >= 0 && page < n_pages)
       dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * rb;
   }
-  publish_finish(threadIdx.x, y_s, z_s, &inv_s, gamma, cos_sin, rd, eps, pos, dst, f8);
+  publish_finish(threadIdx.x, y_s, z_s, &inv_s, gamma, cos_sin + (int64_t)pos * rd, rd, eps,
+                 dst, f8);
 }
 
 // Many groups (the prompt's keys): one workgroup of kPubGroups * 128 threads
@@ -235,7 +135,8 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
         dst = kc + (int64_t)page * page_stride + (int64_t)(row % kPubPageRows) * rb;
     }
   }
-  publish_finish(o, y_s[gi], z_s[gi], &inv_s[gi], gamma, cos_sin, rd, eps, pos, dst, f8);
+  publish_finish(o, y_s[gi], z_s[gi], &inv_s[gi], gamma, cos_sin + (int64_t)pos * rd, rd, eps,
+                 dst, f8);
 }
 
 size_t publish_groups_lds(int Din) {

@@ -25,6 +25,7 @@
 // fit fp32 for the documented input range), so the only rounding is the
 // fixed-order head sum, which the oracle performs identically.
 #include "idx_common.hpp"
+#include "publish_dev.hpp"
 #include "row_topk.hpp"
 
 #include <hip/hip_ext.h>
@@ -335,23 +336,269 @@ __device__ __forceinline__ void fused_rank(float* sbuf, uint32_t* hist_lds, uint
                      orow);
 }
 
+// A decode step's key publish inside its score launch (idx_publish_score;
+// [IDX, forward]: the key-owning layer stores the completed group's key
+// before the score reads the cache).  The new key is row T - 1, the last
+// scored position, so one extra workgroup per sequence publishes it and
+// scores it for the row itself, while the other workgroups score [0, T - 1)
+// and never read that row: no workgroup waits for another.
+struct PubFuse {
+  const uint16_t* latent;  // [B][Din] bf16, one completed group per sequence
+  const uint16_t* wk;      // [128][Din] bf16
+  const float* gamma;      // [128] fp32
+  const float* cos_sin;    // [P][rd/2][2] fp32
+  uint8_t* kc;             // the key cache; row T - 1 of each sequence is written
+  int Din, rd, pos;        // pos: the group's position, start_pos + 1 - ratio
+  float eps;
+  int on;                  // 0: no publish in this launch
+};
+
+// The role of the extra workgroup of row r (sequence b, decode: one row per
+// sequence).  It runs beside workgroups that stream the cache at full HBM
+// rate, where every dependent memory round trip costs microseconds, so its
+// loads are all issued up front: the latent (as fp32), the query row,
+// gamma, the RoPE row and the head weights into LDS, then the whole wk
+// matrix into registers, row o's first 256 values in thread o and the next
+// 256 in thread o + 128 (more passes for Din > 512).  Row o's fma chain
+// runs through thread o's segment and continues, through LDS, in thread
+// o + 128's: the chain of the publish kernels, value for value.  Threads
+// 128..255 quantise the query heads while the first segment runs.  After
+// the key's publish steps, wave 0 scores the new key with the streaming
+// path's own tile code (matrix-core dots and head sum) on a tile that
+// holds only that key.  hist_lds: 2048 words; dyn: the score buffer, at
+// least kRoleDynWords words (the fp32 latent, then the bf16 query row);
+// qs: H quantised heads of 17 words.
+constexpr int kRoleSeg = 256;   // wk values per thread per pass
+constexpr int kRoleMaxDin = 2048;
+constexpr int kRoleDynWords = kRoleMaxDin + 64 * kHeadDim / 2;  // latent + query row
+
+template <int HT>
+__device__ __forceinline__ void publish_and_score_last(
+    const PubFuse& pf, const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
+    int64_t kstride, int T, int r, int b, int limit, float* srow, uint32_t* key_hist,
+    uint32_t* lds, float* dyn, uint32_t* qs) {
+  constexpr int H = 32 * HT;
+  constexpr int NW = kRoleSeg / 8;  // 16-byte words of a segment
+  const int tid = threadIdx.x;
+  const int o = tid & (kHeadDim - 1), half = tid >> 7;
+  const int Din = pf.Din;
+  float* y_s = reinterpret_cast<float*>(lds);                    // 128
+  uint32_t* z_s = lds + 128;                                     // 128
+  float* inv_s = reinterpret_cast<float*>(lds + 256);            // 1
+  uint32_t* row = lds + 260;                                     // 17 words: the new key
+  float* acc_s = reinterpret_cast<float*>(lds + 280);            // 128: chains in flight
+  float* gamma_s = reinterpret_cast<float*>(lds + 408);          // 128
+  float* cs_s = reinterpret_cast<float*>(lds + 536);             // rd <= 128
+  float* w_s = reinterpret_cast<float*>(lds + 664);              // H <= 64
+  float* lat_f = dyn;                                             // Din <= 2048
+  uint4* q_s = reinterpret_cast<uint4*>(dyn + kRoleMaxDin);       // H * 16 words of 16 bytes
+
+  // the small inputs first: their LDS stores wait for them, not for wk
+  const uint16_t* lat = pf.latent + (int64_t)b * Din;
+  const bool lat_vec = (Din & 7) == 0 && (reinterpret_cast<uintptr_t>(lat) & 15) == 0;
+  uint4 lv = uint4{0u, 0u, 0u, 0u};
+  if (lat_vec && tid < Din / 8) lv = reinterpret_cast<const uint4*>(lat)[tid];  // Din <= 2048
+  const float gm = tid < kHeadDim ? pf.gamma[tid] : 0.0f;
+  const float csv = tid < pf.rd ? pf.cos_sin[(int64_t)pf.pos * pf.rd + tid] : 0.0f;
+  const float wq = tid < H ? bf16f(w[(int64_t)r * H + tid]) : 0.0f;
+  // the query row: H * 16 = 512 HT words of 16 bytes, 2 HT a thread
+  constexpr int QV = H * kHeadDim / 8 / 256;
+  static_assert(QV * 256 * 8 == H * kHeadDim, "whole words per thread");
+  const uint4* qrow = reinterpret_cast<const uint4*>(q + (int64_t)r * H * kHeadDim);
+  uint4 qv[QV];
+#pragma unroll
+  for (int i = 0; i < QV; ++i) qv[i] = qrow[tid + 256 * i];
+  // keep wk's burst behind the small loads: their LDS stores below then
+  // wait for them alone
+  __builtin_amdgcn_sched_barrier(0);
+
+  const bool vec = (Din & 7) == 0 && (reinterpret_cast<uintptr_t>(pf.wk) & 15) == 0;
+  // segment g of the chain: values [256 g, min(256 (g + 1), Din)), read
+  // through one range-checked resource over the whole matrix (words past
+  // the segment's end are loaded, or read as zeros past the matrix, and
+  // not used), so the loads need no branches
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(pf.wk), (short)0, kHeadDim * Din * 2, kBufWord3);
+  auto load_seg = [&](int g, uint4 (&v)[NW]) {
+    const int off = (o * Din + kRoleSeg * g) * 2;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const auto c = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 16 * j, 0, 0);
+      v[j] = uint4{c[0], c[1], c[2], c[3]};
+    }
+  };
+  // acc continued over segment g; step j + 1's latent values are read into
+  // the other register set while step j computes.  The reads are issued
+  // whatever the segment's length (past Din they read other words of dyn,
+  // which holds kRoleDynWords >= 2048 + 8 floats, and go unused), so the
+  // waits before a step's fmas cover its own reads only.
+  auto run_seg = [&](int g, const uint4 (&v)[NW], float acc) {
+    const int n4 = (min(kRoleSeg * (g + 1), Din) - kRoleSeg * g) / 8;
+    const float4* l4 = reinterpret_cast<const float4*>(lat_f) + 2 * NW * g;
+    float4 L[2][2];
+    L[0][0] = l4[0];
+    L[0][1] = l4[1];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      if (j + 1 < NW) {
+        L[(j + 1) & 1][0] = l4[2 * j + 2];
+        L[(j + 1) & 1][1] = l4[2 * j + 3];
+      }
+      if (j < n4) {
+        const float4 la = L[j & 1][0], lb = L[j & 1][1];
+        const float x[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc = __builtin_fmaf(bf16f(u[m] & 0xffffu), x[2 * m], acc);
+          acc = __builtin_fmaf(bf16f(u[m] >> 16), x[2 * m + 1], acc);
+        }
+      }
+      // one step at a time: the chain is serial anyway, and reads hoisted
+      // further ahead would need the registers wk holds
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+
+  uint4 wv[NW];
+  if (vec) load_seg(half, wv);
+  if (lat_vec) {
+    if (tid < Din / 8) {
+      const uint32_t u[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        lat_f[8 * tid + 2 * m] = bf16f(u[m] & 0xffffu);
+        lat_f[8 * tid + 2 * m + 1] = bf16f(u[m] >> 16);
+      }
+    }
+  } else {
+    for (int i = tid; i < Din; i += 256) lat_f[i] = bf16f(lat[i]);
+  }
+  if (tid < kHeadDim) gamma_s[tid] = gm;
+  if (tid < pf.rd) cs_s[tid] = csv;
+  if (tid < H) w_s[tid] = wq;
+#pragma unroll
+  for (int i = 0; i < QV; ++i) q_s[tid + 256 * i] = qv[i];
+  __syncthreads();
+
+  // the query heads' quantisation from LDS, blocks (h, g) of 32 values, by
+  // threads 128..255 (t = 0..127) beside the chain's first segment
+  auto quant_q = [&](int t) {
+    for (int blk = t; blk < 4 * H; blk += kHeadDim) {
+      const int h = blk >> 2, g = blk & 3;
+      const uint4* src = q_s + h * 16 + 4 * g;
+      uint32_t xp[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        xp[4 * i] = v.x;
+        xp[4 * i + 1] = v.y;
+        xp[4 * i + 2] = v.z;
+        xp[4 * i + 3] = v.w;
+      }
+      uint32_t codes[4];
+      const int e = quant_block32(xp, codes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
+      reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
+    }
+  };
+
+  if (vec) {
+    const int nseg = (Din + kRoleSeg - 1) / kRoleSeg;
+    const int npass = (nseg + 1) / 2;
+    for (int p = 0; p < npass; ++p) {
+      const int g0 = 2 * p, g1 = 2 * p + 1;
+      if (half == 0) {
+        acc_s[o] = run_seg(g0, wv, p == 0 ? 0.0f : acc_s[o]);
+        if (p + 1 < npass) load_seg(g0 + 2, wv);
+      } else if (p == 0) {
+        quant_q(o);
+      }
+      __syncthreads();
+      if (half == 1 && g1 < nseg) {
+        acc_s[o] = run_seg(g1, wv, acc_s[o]);
+        if (p + 1 < npass) load_seg(g1 + 2, wv);
+      }
+      __syncthreads();
+    }
+    if (tid < kHeadDim) y_s[tid] = bf16f(f32_to_bf16(acc_s[tid]));
+  } else {  // element loads: one thread per chain, ascending from +0
+    if (tid < kHeadDim) {
+      const uint16_t* wrow = pf.wk + (int64_t)tid * Din;
+      float acc = 0.0f;
+      for (int i = 0; i < Din; ++i) acc = __builtin_fmaf(bf16f(wrow[i]), lat_f[i], acc);
+      y_s[tid] = bf16f(f32_to_bf16(acc));
+    } else {
+      quant_q(tid - kHeadDim);
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = pf.kc + ((int64_t)b * kstride + (T - 1)) * kRowBytes;
+  publish_finish(tid, y_s, z_s, inv_s, gamma_s, cs_s, pf.rd, pf.eps, dst, false, row);
+  __syncthreads();
+  if (tid < 64) {
+    // the tile: key 0 of key tile 0 is the new row (lane 0 holds blocks 0
+    // and 2, lane 32 blocks 1 and 3, both its scale word), every other key
+    // is zero; operands and weights as the streaming workgroups hold them
+    const int lane = tid;
+    v8i A[HT][2];
+    int sA[HT][2];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = head_of_row<HT>(ht, lane & 31);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int g = 2 * st + (lane >> 5);
+        const uint32_t* p = qs + h * 17 + 4 * g;
+        A[ht][st] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
+        sA[ht][st] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+      }
+    }
+    float wvh[16 * HT];
+#pragma unroll
+    for (int j = 0; j < 16 * HT; ++j) wvh[j] = w_s[(lane >> 5) * (H / 2) + j];
+    KeyTile kt;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      kt.c[t][0][0] = u32x4{0u, 0u, 0u, 0u};
+      kt.c[t][1][0] = u32x4{0u, 0u, 0u, 0u};
+      kt.sc[t] = 0u;
+    }
+    if ((lane & 31) == 0) {
+      const int hw = 4 * (lane >> 5);
+      kt.c[0][0][0] = u32x4{row[hw], row[hw + 1], row[hw + 2], row[hw + 3]};
+      kt.c[0][1][0] = u32x4{row[8 + hw], row[9 + hw], row[10 + hw], row[11 + hw]};
+      kt.sc[0] = row[16];
+    }
+    const float sc = head_sum_tile<HT>(kt, A, sA, wvh, lane);
+    if (lane == 0 && T - 1 < limit) {
+      if (srow) srow[T - 1] = sc;
+      if (key_hist) atomicAdd(&key_hist[(int64_t)r * 2048 + (score_key(sc) >> 21)], 1u);
+    }
+  }
+}
+
 // The fused kernel (TOPK) is sized for four workgroups per CU: two key
 // tile sets per wave (at most 128 VGPRs) and 40 KB of LDS, the 8 KB
 // histogram plus the 32 KB score buffer, which also holds the query rows
 // until they are in registers and the ranking's scan words.
 template <int HT, bool CAND, bool TOPK, bool F8 = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TOPK ? 4 : 1))) void
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TOPK ? 4 : (F8 ? 1 : 3)))) void
 score_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ q4,
     const uint16_t* __restrict__ w, const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
-    FusedTopk tk, PageMap pg) {
+    FusedTopk tk, PageMap pg, PubFuse pf) {
   static_assert(!(F8 && TOPK), "the fp8 rows have no fused ranking");
   constexpr int H = 32 * HT;
   constexpr int kSets = TOPK ? 2 : kTileSets;  // key tile sets in registers
   constexpr int QW = F8 ? kRowBytesF8 / 4 : kRowBytes / 4;  // words of a quantised head
-  __shared__ uint32_t hist_lds[2048];  // top-11-bit key digits of this workgroup's scores
+  // top-11-bit key digits of this workgroup's scores (the publish role's
+  // scratch, read as 16-byte words there)
+  __shared__ __attribute__((aligned(16))) uint32_t hist_lds[2048];
   __shared__ int32_t cand_s[CAND ? kMaxCand : 1];
   __shared__ uint32_t qs_own[TOPK ? 1 : H * QW];
   extern __shared__ __attribute__((aligned(16))) float sbuf[];  // this chunk's scores
@@ -374,8 +621,18 @@ score_kernel(
   pm.cbs = cbs;
   pm.nblk = CAND ? (T + cbs - 1) / cbs : 0;
   pm.limit = limit;
-  const int vtotal = CAND ? n_cand * cbs : limit;
-  const int vbeg = blockIdx.y * keys_per_wg;
+  if constexpr (!CAND && !TOPK && !F8) {
+    // uniform: the publishing workgroup, dispatched ahead of the chunks
+    if (pf.on && blockIdx.y == 0) {
+      publish_and_score_last<HT>(pf, q, w, kstride, T, r, b, limit,
+                                 scores ? scores + (int64_t)r * ld : nullptr, key_hist, hist_lds,
+                                 sbuf, qs_own);
+      return;
+    }
+  }
+  // with a publish in the launch, row T - 1 is the publishing workgroup's
+  const int vtotal = CAND ? n_cand * cbs : (pf.on && limit > T - 1 ? T - 1 : limit);
+  const int vbeg = ((int)blockIdx.y - (pf.on ? 1 : 0)) * keys_per_wg;
   const int vend = min(vbeg + keys_per_wg, vtotal);
   // nothing to score, or (fused, scores not wanted) a row with at most kout
   // reachable positions: it keeps [0, limit) and then the lowest masked
@@ -641,7 +898,7 @@ int keys_per_wg_override() {
   return v;
 }
 
-int pick_keys_per_wg(int64_t R, int vtotal) {
+int pick_keys_per_wg(int64_t R, int vtotal, int slots = 256) {
   if (keys_per_wg_override() > 0) {
     const int o = (keys_per_wg_override() + 255) / 256 * 256;
     return o < kMaxKeysPerWg ? o : kMaxKeysPerWg;
@@ -650,8 +907,10 @@ int pick_keys_per_wg(int64_t R, int vtotal) {
   // the decode shapes, one workgroup of four waves per CU streams as fast as
   // two or more, and each workgroup pays the query load and quantisation
   // once; at least 1024 keys per workgroup so that cost stays amortised
+  // slots: the CUs left for the chunks (fewer when other workgroups of the
+  // launch hold some of them)
   const int64_t total = R * (int64_t)vtotal;
-  int64_t kpw = (total + 255) / 256;
+  int64_t kpw = (total + slots - 1) / slots;
   if (kpw < 1024) kpw = 1024;
   if (kpw > vtotal) kpw = vtotal;
   if (kpw > kMaxKeysPerWg) kpw = kMaxKeysPerWg;
@@ -726,7 +985,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   return launch_score(kern, grid, lds, st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
-                      pg);
+                      pg, idx::PubFuse{});
 }
 
 idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
@@ -758,7 +1017,8 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
   auto kern = H == 64 ? idx::score_kernel<2, false, true> : idx::score_kernel<1, false, true>;
   return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, q4, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
-                      (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg);
+                      (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg,
+                      idx::PubFuse{});
 }
 
 // Page map arguments shared by the paged entry points.
@@ -781,6 +1041,59 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                     cand_blocks,
                     n_cand, cand_block_size, scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* wk,
+                                        const float* gamma, const float* cos_sin, int P, int Din,
+                                        int rd, float eps, int start_pos, int ratio,
+                                        const uint16_t* q, const uint16_t* w, uint8_t* k_cache,
+                                        int64_t k_batch_stride_rows, int B, int H, int D, int T,
+                                        const int32_t* compress_lens, float* scores, int64_t ld,
+                                        uint32_t* key_hist, void* stream) {
+  // every argument of both steps is checked before either launches
+  if (ratio <= 0 || start_pos < 0 || B < 0 || T < 0 || P < 0 || Din <= 0 || H <= 0 || D <= 0)
+    return IDX_EINVAL;
+  if (D != idx::kHeadDim || (H != 32 && H != 64)) return IDX_EUNSUPPORTED;
+  if (rd < 0 || rd > D || (rd & 1) || !(eps >= 0.0f)) return IDX_EINVAL;
+  if ((size_t)Din * 2 > 60 * 1024) return IDX_EUNSUPPORTED;
+  if (B == 0) return IDX_OK;
+  if (!latent || !wk || !gamma || !k_cache || (rd > 0 && !cos_sin) || !q || !w ||
+      !compress_lens || !scores)
+    return IDX_EINVAL;
+  if (!idx_host::aligned(q, 16) || !idx_host::aligned(k_cache, 4)) return IDX_EINVAL;
+  if (k_batch_stride_rows < T || ld < T) return IDX_EINVAL;
+  const int64_t row = start_pos / ratio;  // the completed group's cache row
+  const int pos = start_pos + 1 - ratio;  // its position
+  if (start_pos > 0 && pos < 0) return IDX_EINVAL;
+  if (rd > 0 && (start_pos > 0 ? pos : 0) >= P) return IDX_EINVAL;
+  if (row >= k_batch_stride_rows) return IDX_EINVAL;
+  const bool fuse = start_pos > 0 && row == (int64_t)T - 1 && Din <= idx::kRoleMaxDin;
+  if (!fuse) {  // two launches in stream order: the key, then the score
+    const int tcap = k_batch_stride_rows < 0x7fffffff ? (int)k_batch_stride_rows : 0x7fffffff;
+    const idx_status e = idx_publish_keys(latent, wk, gamma, cos_sin, P, B, 1, Din, D, rd, eps,
+                                          start_pos, ratio, k_cache, k_batch_stride_rows, tcap,
+                                          stream);
+    if (e != IDX_OK) return e;
+    return idx_score(q, w, k_cache, k_batch_stride_rows, B, 1, H, D, T, compress_lens, nullptr, 0,
+                     0, scores, ld, key_hist, stream);
+  }
+  // keys [0, T - 1) in chunks as idx_score would take them, and one more
+  // workgroup per sequence for the published key T - 1; while those are
+  // few, the chunks are sized to the CUs they leave (a CU streaming two
+  // chunks would set the launch's length)
+  const int kpw = pick_keys_per_wg(B, T - 1, B < 64 ? 256 - B : 256);
+  const int nch = (T - 1 + kpw - 1) / kpw;
+  if (nch + 1 > 65535) return IDX_EINVAL;
+  auto kern = H == 64 ? idx::score_kernel<2, false, false> : idx::score_kernel<1, false, false>;
+  // the publishing workgroup keeps the fp32 latent and the query row in
+  // the score buffer
+  const size_t lds = (size_t)(kpw > idx::kRoleDynWords ? kpw : idx::kRoleDynWords) * sizeof(float);
+  return launch_score(kern, dim3((unsigned)B, (unsigned)(nch + 1)), lds,
+                      (hipStream_t)stream, q, (const uint8_t*)nullptr, w,
+                      (const uint8_t*)k_cache, k_batch_stride_rows, 1, T, compress_lens,
+                      (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
+                      idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
+                      idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1});
 }
 
 extern "C" idx_status idx_score_fp8(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,

@@ -16,6 +16,7 @@ import numpy as np
 
 from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
                idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
+               idx_publish_score,
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
@@ -143,6 +144,13 @@ class IndexerStep:
                                                       YARN["orig_len"], YARN["beta_fast"],
                                                       YARN["beta_slow"]))
 
+        # the decode publish of the last scored key joins the score launch
+        # (idx_publish_score) on contiguous fp4 caches with bf16 queries
+        self.publish_in_score = (self.publish and wl.S == 1 and wl.start_pos > 0 and
+                                 wl.start_pos // wl.ratio == T - 1 and not paged and not fp8 and
+                                 not self.fused and not (q_step and not wl.ctb) and
+                                 wl.din <= 2048)
+
         # every step's calls, marshalled once per key-cache copy
         self._plans = [self._plan(kc) for kc in self.caches]
 
@@ -176,7 +184,10 @@ class IndexerStep:
         wl = self.wl
         calls = []
         b = dict(bind=True)
-        if self.publish:
+        # a decode step whose new key is the last scored position publishes
+        # it inside the score launch (one extra workgroup per sequence)
+        pub_in_score = self.publish_in_score
+        if self.publish and not pub_in_score:
             if self.paged:
                 calls.append(idx_publish_keys_paged(self.latent, self.wk, self.gamma, self.cos_sin,
                                                     wl.start_pos, wl.ratio, wl.eps, kc,
@@ -219,6 +230,11 @@ class IndexerStep:
         elif q4 is not None:
             calls.append(idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                                       key_hist=self.key_hist, **b))
+        elif pub_in_score:
+            calls.append(idx_publish_score(self.latent, self.wk, self.gamma, self.cos_sin,
+                                           wl.start_pos, wl.ratio, wl.eps, q, w, kc, wl.T,
+                                           self.cl, self.scores, key_hist=self.key_hist,
+                                           rd=wl.rd, **b))
         else:
             score = idx_score_fp8 if self.fp8 else idx_score
             calls.append(score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,

@@ -208,6 +208,35 @@ def test_unaligned_pointers_are_rejected(lib):
                                 8, None) == IDX_EINVAL
 
 
+def test_publish_score_checks_both_steps_before_launch(lib):
+    """idx_publish_score checks the publish's and the score's arguments
+    before either step launches, in its one-launch and two-launch forms."""
+    a16, odd8, odd2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    T = 100
+
+    def call(q=a16, kc=a16, sp=4 * (T - 1) + 3, ratio=4, P=400, Din=512, rd=64, eps=1e-6, B=2,
+             H=64, D=128, stride=T, ld=T, cl=a16, lat=a16):
+        return lib.idx_publish_score(lat, a16, a16, a16, P, Din, rd, eps, sp, ratio, q, a16, kc,
+                                     stride, B, H, D, T, cl, a16, ld, None, None)
+
+    for sp in (4 * (T - 1) + 3, 4 * 50 + 3, 0):  # one launch, two launches, prefill form
+        assert call(sp=sp, q=odd8) == IDX_EINVAL
+        assert call(sp=sp, kc=odd2) == IDX_EINVAL
+        assert call(sp=sp, ld=T - 1) == IDX_EINVAL
+        assert call(sp=sp, stride=T - 1) == IDX_EINVAL
+        assert call(sp=sp, cl=None) == IDX_EINVAL
+        assert call(sp=sp, lat=None) == IDX_EINVAL
+        assert call(sp=sp, H=48) == IDX_EUNSUPPORTED
+        assert call(sp=sp, D=64) == IDX_EUNSUPPORTED
+        assert call(sp=sp, rd=63) == IDX_EINVAL
+        assert call(sp=sp, eps=float("nan")) == IDX_EINVAL
+        assert call(sp=sp, B=0) == IDX_OK  # nothing to do
+    assert call(ratio=0) == IDX_EINVAL
+    assert call(P=4 * (T - 1)) == IDX_EINVAL  # the group's position has no RoPE entry
+    assert call(sp=4 * T + 3) == IDX_EINVAL  # its row is past the cache
+    assert call(Din=30721) == IDX_EUNSUPPORTED
+
+
 def test_paged_entry_points_reject_bad_page_maps(lib):
     """Page pool, page stride and block table are checked before any launch."""
     d = ctypes.c_void_p(0x1000)

@@ -166,6 +166,7 @@ def test_two_level_256k():
 def test_long_decode_publish_1m():
     from sparse_attention_top_fp4_amd.inputs import YARN
     wl, inp, st = _run(4)
+    assert st.publish_in_score  # the new key is published inside the score launch
     scores, out = host(st.scores), host(st.out)
     cl = inp["cl"]
     _invariants(out, cl, st.kout, wl.offset)
