@@ -456,6 +456,26 @@ idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, co
                                   int64_t bt_stride, int Tcap, void *stream);
 
 /*
+ * idx_score_select_blocks -- idx_score then idx_select_candidate_blocks on
+ * the scores just written: the level-one pass of the two-level indexer
+ * ([IDX, forward]: the candidate source layer scores every key, then
+ * select_candidate_blocks keeps its best blocks for the next layer).
+ * Arguments, outputs and errors are those of the two calls (ws sized by
+ * idx_select_workspace_size); the outputs equal theirs bit for bit.  When
+ * cand_block_size divides the score launch's chunk and the row has at most
+ * 1024 blocks, the score launch also writes the block maxima (from the
+ * chunk's scores in LDS) and one wave per row ranks them, so no pass reads
+ * the scores back (cand_block_size a power of two in [16, 1024]; other
+ * sizes run the two calls).
+ */
+idx_status idx_score_select_blocks(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
+                                   int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                                   const int32_t *compress_lens, float *scores, int64_t ld,
+                                   uint32_t *key_hist, int candidate_topk_blocks,
+                                   int cand_block_size, int32_t *block_ids, int64_t ld_ids,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/*
  * idx_publish_score -- idx_publish_keys then idx_score for a decode step
  * that publishes its completed group ([IDX, forward]: the key-owning layer
  * stores k = k_norm(wk(latent)) with RoPE and the fp4 round trip at

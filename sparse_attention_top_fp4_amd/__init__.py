@@ -22,7 +22,7 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
-           "idx_publish_score",
+           "idx_publish_score", "idx_score_select_blocks",
            "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
            "load_library", "IdxError", "ROW_BYTES"]
 
@@ -84,6 +84,8 @@ def load_library():
     L.idx_fp8_quant.argtypes = [P, i64, P, P, P]
     L.idx_score_fp8.argtypes = L.idx_score.argtypes
     L.idx_publish_keys_fp8.argtypes = L.idx_publish_keys.argtypes
+    L.idx_score_select_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i64, P,
+                                          i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
                                     i32, i32, i32, P, P, i64, P, P]
     L.idx_probe_stream_read.argtypes = [P, i64, i32, P, ctypes.POINTER(f32), P]
@@ -97,7 +99,8 @@ def load_library():
                  "idx_score_paged", "idx_score_topk_paged", "idx_publish_keys_paged",
                  "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
-                 "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score"):
+                 "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
+                 "idx_score_select_blocks"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -619,6 +622,38 @@ def idx_publish_keys(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache,
                                            cos_sin.shape[0], B, G, Din, D, rd, eps, start_pos,
                                            ratio, _ptr(k_cache), k_cache.shape[1],
                                            k_cache.shape[1]), stream, "idx_publish_keys", bind)
+
+
+def idx_score_select_blocks(q, w, k_cache, B, S, T, compress_lens, scores, candidate_topk_blocks,
+                            cand_block_size, block_ids, workspace, key_hist=None, stream=None,
+                            bind=False):
+    """idx_score then idx_select_candidate_blocks (the level-one pass):
+    arguments as those two wrappers take them; workspace as
+    idx_select_workspace_size sizes it."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(block_ids, "block_ids", (torch.int32,), 2)
+    _dev(workspace, "workspace", (torch.uint8,), 1)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES or scores.shape[0] != R:
+        raise ValueError("k_cache must be [>=B, Tcap, 68] and scores [B*S, ld]")
+    if block_ids.shape[0] != R:
+        raise ValueError("block_ids must have B*S rows")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    return _issue("idx_score_select_blocks",
+                  (_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D, T,
+                   _ptr(compress_lens), _ptr(scores), scores.shape[1], _ptr(key_hist),
+                   candidate_topk_blocks, cand_block_size, _ptr(block_ids), block_ids.shape[1],
+                   _ptr(workspace), workspace.numel()), stream, "idx_score_select_blocks", bind)
 
 
 def idx_publish_score(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_cache, T,

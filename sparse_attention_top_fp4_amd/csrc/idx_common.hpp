@@ -217,6 +217,14 @@ __device__ __forceinline__ uint32_t lanes_below_acc(uint64_t mask, uint32_t acc)
 
 // ------------------------------------------------------- host helpers
 namespace idx_host {
+
+// Block select from block maxima bmax[R][ld_b] (nb <= kSelectWaveMaxBlocks
+// blocks of cbs positions; the rule of idx_select_candidate_blocks), one
+// wave per row.  Defined in topk.hip.
+constexpr int kSelectWaveMaxBlocks = 1024;
+idx_status select_blocks_from_max(const float* bmax, int64_t ld_b, int R, int nb, int T,
+                                  const int32_t* compress_lens, int cbs, int ctb, int32_t* ids,
+                                  int64_t ld_ids, hipStream_t st);
 inline idx_status launch_status() {
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

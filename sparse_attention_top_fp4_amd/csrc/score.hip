@@ -353,6 +353,15 @@ struct PubFuse {
   int on;                  // 0: no publish in this launch
 };
 
+// Extra output of the plain launch: the maximum of each cbs-wide block of
+// the chunk's scores (the block score of the candidate select), written
+// when bmax is set; chunk starts are then multiples of bmax_cbs.
+struct Epi {
+  float* bmax;       // [R][bmax_ld], or null
+  int64_t bmax_ld;
+  int bmax_cbs;
+};
+
 // The role of the extra workgroup of row r (sequence b, decode: one row per
 // sequence).  It runs beside workgroups that stream the cache at full HBM
 // rate, where every dependent memory round trip costs microseconds, so its
@@ -591,7 +600,7 @@ score_kernel(
     const uint16_t* __restrict__ w, const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
-    FusedTopk tk, PageMap pg, PubFuse pf) {
+    FusedTopk tk, PageMap pg, PubFuse pf, Epi ep) {
   static_assert(!(F8 && TOPK), "the fp8 rows have no fused ranking");
   constexpr int H = 32 * HT;
   constexpr int kSets = TOPK ? 2 : kTileSets;  // key tile sets in registers
@@ -826,6 +835,35 @@ done:
       if (p >= 0) srow[p] = sbuf[i];
     }
   }
+  if (!CAND && !TOPK && ep.bmax) {
+    // block maxima from the scores in LDS (cbs a power of two in [16, 1024]
+    // dividing the chunk): run i of 16 positions per thread and pass, the
+    // maximum of its positions before the chunk end, then a butterfly over
+    // the cbs / 16 lanes of the block (all blocks at once); the block's
+    // first lane writes it.  A block reaching past the chunk end stops there
+    // (= at compress_lens, where the row's last chunk ends); blocks wholly
+    // past compress_lens are not written (the select ranks them as -inf).
+    const int rpb = ep.bmax_cbs >> 4;  // runs per block, 1..64
+    const int b0 = vbeg / ep.bmax_cbs;
+    // (cbs divides the chunk, so a block's runs sit in one wave and iterate
+    // together: the butterfly's lanes are all active)
+    for (int i = tid; 16 * i < keys_per_wg; i += 256) {
+      float m = -__builtin_inff();
+      const float4* src = reinterpret_cast<const float4*>(sbuf + 16 * i);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = src[q4];
+        const int t = 16 * i + 4 * q4;
+        m = t < n ? fmaxf(m, v.x) : m;
+        m = t + 1 < n ? fmaxf(m, v.y) : m;
+        m = t + 2 < n ? fmaxf(m, v.z) : m;
+        m = t + 3 < n ? fmaxf(m, v.w) : m;
+      }
+      for (int d = 1; d < rpb; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+      if ((i & (rpb - 1)) == 0 && 16 * i < n)
+        ep.bmax[(int64_t)r * ep.bmax_ld + b0 + i / rpb] = m;
+    }
+  }
   if (key_hist && !TOPK) {
     uint32_t* grow = key_hist + (int64_t)r * 2048;
     for (int i = tid; i < 2048; i += 256)
@@ -938,7 +976,8 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                       int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                       const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
                       int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
-                      idx::PageMap pg, void* stream, bool f8 = false) {
+                      idx::PageMap pg, void* stream, bool f8 = false,
+                      idx::Epi ep = idx::Epi{nullptr, 0, 0}) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -967,6 +1006,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
     if (T > kMaxPagedCandT) return IDX_EUNSUPPORTED;
     lds += (size_t)((T + idx::kPageRows - 1) / idx::kPageRows) * sizeof(int32_t);
   }
+  if (ep.bmax && (cand_blocks || ep.bmax_cbs <= 0 || kpw % ep.bmax_cbs)) return IDX_EINVAL;
   if (cand_blocks) {
     if (R > 65535) return IDX_EUNSUPPORTED;
     hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048), (unsigned)R),
@@ -985,7 +1025,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   return launch_score(kern, grid, lds, st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
-                      pg, idx::PubFuse{});
+                      pg, idx::PubFuse{}, ep);
 }
 
 idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
@@ -1018,7 +1058,7 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
   return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, q4, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
                       (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg,
-                      idx::PubFuse{});
+                      idx::PubFuse{}, idx::Epi{nullptr, 0, 0});
 }
 
 // Page map arguments shared by the paged entry points.
@@ -1041,6 +1081,49 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                     cand_blocks,
                     n_cand, cand_block_size, scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+extern "C" idx_status idx_score_select_blocks(const uint16_t* q, const uint16_t* w,
+                                              const uint8_t* k_cache, int64_t k_batch_stride_rows,
+                                              int B, int S, int H, int D, int T,
+                                              const int32_t* compress_lens, float* scores,
+                                              int64_t ld, uint32_t* key_hist,
+                                              int candidate_topk_blocks, int cand_block_size,
+                                              int32_t* block_ids, int64_t ld_ids, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  // the select's argument checks first: nothing launches on a bad call
+  if (B < 0 || S < 0 || T < 0 || candidate_topk_blocks <= 0 || cand_block_size <= 0)
+    return IDX_EINVAL;
+  const int64_t R = (int64_t)B * S;
+  if (R == 0 || T == 0) return IDX_OK;
+  if (!block_ids || !ws) return IDX_EINVAL;
+  const int nb = (int)(((int64_t)T + cand_block_size - 1) / cand_block_size);
+  const int kk = candidate_topk_blocks < nb ? candidate_topk_blocks : nb;
+  if (ld_ids < kk) return IDX_EINVAL;
+  if (ws_bytes < idx_select_workspace_size((int)R, T, candidate_topk_blocks, cand_block_size))
+    return IDX_EINVAL;
+  if (R > 65535) return IDX_EUNSUPPORTED;
+  const int kpw = pick_keys_per_wg(R, T);
+  const bool pow2 = (cand_block_size & (cand_block_size - 1)) == 0;
+  if (nb > idx_host::kSelectWaveMaxBlocks || !pow2 || cand_block_size < 16 ||
+      cand_block_size > 1024 || kpw % cand_block_size) {
+    // chunks that split blocks, or more blocks than one wave ranks: the
+    // two calls
+    const idx_status e = idx_score(q, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                                   compress_lens, nullptr, 0, 0, scores, ld, key_hist, stream);
+    if (e != IDX_OK) return e;
+    return idx_select_candidate_blocks(scores, ld, (int)R, T, compress_lens, candidate_topk_blocks,
+                                       cand_block_size, block_ids, ld_ids, ws, ws_bytes, stream);
+  }
+  float* bmax = (float*)ws;  // [R][nb], the select workspace's first region
+  const idx_status e = score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                                  compress_lens, nullptr, 0, 0, scores, ld, key_hist,
+                                  idx::PageMap{nullptr, 0, 0, 0}, stream, false,
+                                  idx::Epi{bmax, nb, cand_block_size});
+  if (e != IDX_OK) return e;
+  return idx_host::select_blocks_from_max(bmax, nb, (int)R, nb, T, compress_lens, cand_block_size,
+                                          candidate_topk_blocks, block_ids, ld_ids,
+                                          (hipStream_t)stream);
 }
 
 extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* wk,
@@ -1093,7 +1176,8 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
                       (const uint8_t*)k_cache, k_batch_stride_rows, 1, T, compress_lens,
                       (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
                       idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
-                      idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1});
+                      idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1},
+                      idx::Epi{nullptr, 0, 0});
 }
 
 extern "C" idx_status idx_score_fp8(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,

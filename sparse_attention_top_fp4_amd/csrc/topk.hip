@@ -1073,6 +1073,65 @@ __global__ __launch_bounds__(256) void block_max_kernel(const float* __restrict_
   if (lane == 0) bmax[(int64_t)r * nb + j] = m;
 }
 
+// Block select of up to 64 * EPL blocks by one wave, no LDS: block j (lane
+// j % 64, slot j / 64) ranks by its maximum's order key, blocks at or past
+// ceil(cl / cbs) as -inf, ties to the lower id.  The kout-th largest key u
+// is built bit by bit from the top (largest u with at least kout keys >= u),
+// each count a sum of ballot popcounts; then every block above u is taken,
+// and of those equal to u the kout - (#above) of lowest id, and the taken
+// ids leave in ascending order (-1 for a taken block past the reachable
+// ones), each slot a popcount of the lower taken ids.
+template <int EPL>
+__global__ __launch_bounds__(64) void select_wave_kernel(const float* __restrict__ bmax,
+                                                         int64_t ld_b, int nb, int T,
+                                                         const int32_t* __restrict__ cl_arr,
+                                                         int cbs, int kout,
+                                                         int32_t* __restrict__ ids,
+                                                         int64_t ld_ids) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  // the maxima are requested beside compress_lens (one round trip); blocks
+  // past the reachable ones are masked once both are in
+  float bm[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int j = e * 64 + lane;
+    bm[e] = bmax[(int64_t)r * ld_b + (j < nb ? j : 0)];
+  }
+  int c = cl_arr[r];
+  c = c < 0 ? 0 : (c > T ? T : c);
+  const int clb = (int)(((int64_t)c + cbs - 1) / cbs);
+  uint32_t key[EPL];  // 0: no such block (below every real key)
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int j = e * 64 + lane;
+    key[e] = j < nb ? (j < clb ? score_key(bm[e]) : kKeyNegInf) : 0u;
+  }
+  uint32_t u = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = u | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) cnt += (uint32_t)__popcll(__ballot(key[e] >= cand));
+    if (cnt >= (uint32_t)kout) u = cand;
+  }
+  uint32_t above = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) above += (uint32_t)__popcll(__ballot(key[e] > u));
+  const uint32_t need = (uint32_t)kout - above;
+  uint32_t eq_run = 0, sel_run = 0;
+  int32_t* orow = ids + (int64_t)r * ld_ids;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int j = e * 64 + lane;
+    const uint64_t em = __ballot(key[e] == u);
+    const bool take = key[e] > u || (key[e] == u && eq_run + lanes_below(em) < need);
+    eq_run += (uint32_t)__popcll(em);
+    const uint64_t tm = __ballot(take);
+    if (take) orow[sel_run + lanes_below(tm)] = j < clb ? j : -1;
+    sel_run += (uint32_t)__popcll(tm);
+  }
+}
+
 }  // namespace idx
 
 // ------------------------------------------------------------ host side
@@ -1260,8 +1319,26 @@ extern "C" idx_status idx_select_candidate_blocks(const float* scores, int64_t l
                      0, st, scores, ld, T, compress_lens, cand_block_size, nb, bmax, clb);
   const idx_status s = idx_host::launch_status();
   if (s != IDX_OK) return s;
+  if (nb <= idx_host::kSelectWaveMaxBlocks)
+    return idx_host::select_blocks_from_max(bmax, nb, R, nb, T, compress_lens, cand_block_size,
+                                            candidate_topk_blocks, block_ids, ld_ids, st);
   return topk_launch(bmax, nb, R, nb, clb, nullptr, candidate_topk_blocks, 0, block_ids, ld_ids,
                      tws, tws_bytes, st);
+}
+
+// One wave per row ranks the block maxima (nb <= kSelectWaveMaxBlocks).
+idx_status idx_host::select_blocks_from_max(const float* bmax, int64_t ld_b, int R, int nb, int T,
+                                            const int32_t* compress_lens, int cbs, int ctb,
+                                            int32_t* ids, int64_t ld_ids, hipStream_t st) {
+  if (nb <= 0 || nb > kSelectWaveMaxBlocks || R <= 0) return IDX_EINVAL;
+  const int kout = ctb < nb ? ctb : nb;
+  if (nb <= 512)
+    hipLaunchKernelGGL(idx::select_wave_kernel<8>, dim3((unsigned)R), dim3(64), 0, st, bmax, ld_b,
+                       nb, T, compress_lens, cbs, kout, ids, ld_ids);
+  else
+    hipLaunchKernelGGL(idx::select_wave_kernel<16>, dim3((unsigned)R), dim3(64), 0, st, bmax,
+                       ld_b, nb, T, compress_lens, cbs, kout, ids, ld_ids);
+  return idx_host::launch_status();
 }
 
 extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R, int T,

@@ -16,7 +16,7 @@ import numpy as np
 
 from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
                idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
-               idx_publish_score,
+               idx_publish_score, idx_score_select_blocks,
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
@@ -212,6 +212,7 @@ class IndexerStep:
             else:
                 q = self.q_rt
         score_at = len(calls)
+        selected = False  # the candidate blocks chosen with the level-one score
         if self.fused:
             if self.paged:
                 calls.append(idx_score_topk_paged(q, w, kc, self.block_table, wl.B, wl.S, wl.T,
@@ -235,13 +236,22 @@ class IndexerStep:
                                            wl.start_pos, wl.ratio, wl.eps, q, w, kc, wl.T,
                                            self.cl, self.scores, key_hist=self.key_hist,
                                            rd=wl.rd, **b))
+        elif self.two_level and not self.fp8:
+            # level one: the score launch also writes the block maxima and
+            # one wave per row selects the candidate blocks
+            selected = True
+            calls.append(idx_score_select_blocks(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
+                                                 wl.ctb, wl.cbs, self.ids, self.sel_ws,
+                                                 key_hist=self.key_hist, **b))
         else:
             score = idx_score_fp8 if self.fp8 else idx_score
             calls.append(score(q, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                                key_hist=self.key_hist, **b))
         if self.two_level:
-            calls.append(idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb, wl.cbs,
-                                                     self.ids, workspace=self.sel_ws, **b))
+            if not selected:
+                calls.append(idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb,
+                                                         wl.cbs, self.ids, workspace=self.sel_ws,
+                                                         **b))
             calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                                   workspace=self.topk_ws, key_hist=self.key_hist, **b))
             # level two: only the candidate positions hold finite scores; the

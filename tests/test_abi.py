@@ -237,6 +237,26 @@ def test_publish_score_checks_both_steps_before_launch(lib):
     assert call(Din=30721) == IDX_EUNSUPPORTED
 
 
+def test_score_select_blocks_checks_before_launch(lib):
+    """idx_score_select_blocks checks the select's arguments (block sizes,
+    id row width, workspace size) before the score launches."""
+    d = ctypes.c_void_p(0x1000)
+    T, R = 65536, 4
+    need = lib.idx_select_workspace_size(R, T, 64, 128)
+
+    def call(ctb=64, cbs=128, ld_ids=64, ws=d, ws_bytes=need, ids=d, B=R):
+        return lib.idx_score_select_blocks(d, d, d, T, B, 1, 64, 128, T, d, d, T, None, ctb, cbs,
+                                           ids, ld_ids, ws, ws_bytes, None)
+
+    assert call(ctb=0) == IDX_EINVAL
+    assert call(cbs=0) == IDX_EINVAL
+    assert call(ld_ids=63) == IDX_EINVAL  # a row of ids holds min(ctb, nb) = 64
+    assert call(ws_bytes=need - 1) == IDX_EINVAL
+    assert call(ws=None) == IDX_EINVAL
+    assert call(ids=None) == IDX_EINVAL
+    assert call(B=0) == IDX_OK  # nothing to do
+
+
 def test_paged_entry_points_reject_bad_page_maps(lib):
     """Page pool, page stride and block table are checked before any launch."""
     d = ctypes.c_void_p(0x1000)

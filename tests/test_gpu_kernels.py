@@ -122,16 +122,23 @@ def test_score_matches_oracle(idx, case):
         assert np.all(np.isnan(got[r, T:]))  # nothing written past T
 
 
-@pytest.mark.parametrize("cbs,cand_rows", [
-    (128, [[0, 3, 5, 7], [1, 2, -1, 6]]),
-    (48, [[0, 1, 20, 21], [4, 99, 5, 13]]),  # 99 is out of range: skipped
+@pytest.mark.parametrize("T,cbs,cand_rows", [
+    (1000, 128, [[0, 3, 5, 7], [1, 2, -1, 6]]),
+    (1000, 48, [[0, 1, 20, 21], [4, 99, 5, 13]]),  # 99 is out of range: skipped
+    # several workgroups per row, each writing -inf to its share of the
+    # unscored positions; duplicate and -1 ids
+    (65536, 128, [list(range(0, 512, 8)), [3, 3, 9, -1] + list(range(100, 160))]),
+    # more blocks than the in-launch bitmap holds: a fill runs first
+    (70000, 1, [list(range(0, 4096, 2)), list(range(69000, 70000)) + [5, 5, -3]]),
 ])
-def test_score_candidates_match_oracle(idx, cbs, cand_rows):
+def test_score_candidates_match_oracle(idx, T, cbs, cand_rows):
     t = torch()
-    B, H, T = 2, 64, 1000
-    say("score candidates", cbs, cand_rows)
+    B, H = 2, 64
+    say("score candidates", T, cbs, [len(x) for x in cand_rows])
     c = small_case(21, B, 1, H, T)
-    c["cl"][:] = [T, 700]
+    c["cl"][:] = [T, min(700, T) if T < 5000 else T - 777]
+    w = max(len(x) for x in cand_rows)
+    cand_rows = [x + [-1] * (w - len(x)) for x in cand_rows]
     cand = np.array(cand_rows, np.int32)
     kc_ref, _ = oracle.fp4_quant_rows(c["k"])
     ref_cand = np.where((cand >= 0) & (cand < (T + cbs - 1) // cbs), cand, -1)
@@ -209,15 +216,26 @@ def test_topk_real_score_distribution(idx):
 
 
 # ------------------------------------------------------ candidate blocks
-@pytest.mark.parametrize("T,cbs,ctb", [(65536, 128, 64), (1000, 100, 3), (700, 128, 64),
-                                       (5000, 7, 600)])
-def test_select_blocks_matches_oracle(idx, T, cbs, ctb):
+@pytest.mark.parametrize("T,cbs,ctb,fill", [
+    (65536, 128, 64, None), (1000, 100, 3, None), (700, 128, 64, None),
+    (5000, 7, 600, None),       # 715 blocks: the wave select's 16-per-lane form
+    (65536, 64, 64, None),      # 1024 blocks: its largest row
+    (10000, 7, 100, None),      # 1429 blocks: the row top-k instead
+    (4096, 32, 16, "equal"),    # every block maximum equal: the lowest ids
+    (4096, 32, 16, "zeros"),    # -0 and +0 maxima tie
+])
+def test_select_blocks_matches_oracle(idx, T, cbs, ctb, fill):
     t = torch()
-    say("select", T, cbs, ctb)
+    say("select", T, cbs, ctb, fill)
     rng = np.random.default_rng(T + cbs)
     R = 4
     s = rng.standard_normal((R, T)).astype(np.float32)
     s[:, ::3] = np.round(s[:, ::3])  # ties between block maxima
+    if fill == "equal":
+        s[:] = np.float32(0.5)
+    elif fill == "zeros":
+        s[:] = np.where(rng.random((R, T)) < 0.5, np.float32(-0.0), np.float32(0.0))
+        s[:, 5 * cbs] = 1.0  # one block above the rest
     cl = np.array([T, T // 2, 1, 0], np.int32)
     ref = oracle.select_blocks(s, cl, ctb, cbs)
     out = t.full((R, ref.shape[1]), -7, dtype=t.int32, device="cuda")
