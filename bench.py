@@ -182,12 +182,14 @@ def score_kernel_name(st) -> str:
     """The launch the score events bracket: the fused score + top-k kernel for
     single-level rows up to 8192 positions, else the score kernel."""
     if st.fused:
-        return "idx::score_kernel<2, false, true> (score and top-k in one launch)"
+        return "idx::score_kernel<2, false, true, false> (score and top-k in one launch)"
     if getattr(st, "fp8", False):
         return "idx::score_kernel<2, false, false, true> (FP8 rows)"
     if getattr(st, "publish_in_score", False):
-        return "idx::score_kernel<2, false, false> (with the key publish workgroups)"
-    return "idx::score_kernel<2, false, false>"
+        return "idx::score_kernel<2, false, false, false> (with the key publish workgroups)"
+    if getattr(st, "two_level", False):
+        return "idx::score_kernel<2, false, false, false> (level one, with its block maxima)"
+    return "idx::score_kernel<2, false, false, false>"
 
 
 def source_digest() -> str:
