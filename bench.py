@@ -399,7 +399,7 @@ def main():
     qps = wl.R / step_s
     keys = st.keys_scored()
     # the committed counter summary covers the contiguous layout
-    traffic = None if (args.paged or args.fp8) else measured_traffic(wl.name)
+    traffic = None if (args.paged or args.fp8 or args.q_step) else measured_traffic(wl.name)
     line = {
         "metric": METRIC,
         "value": qps,
