@@ -59,14 +59,29 @@ __device__ __forceinline__ uint32_t waves_total(const uint32_t* wtot) {
   return s;
 }
 
-template <int NT>
+// A workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// operations, not for its global loads in flight (which the fence of
+// __syncthreads drains as well).  For code in which no thread reads global
+// memory another thread of the workgroup wrote.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <bool LDS_ONLY>
+__device__ __forceinline__ void block_barrier() {
+  if constexpr (LDS_ONLY)
+    lds_barrier();
+  else
+    __syncthreads();
+}
+
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* wtot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_sum(v);
   if (lane == 63) wtot[w] = x;
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
   const uint32_t add = waves_below<NT>(wtot, w);
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
   return x + add;
 }
 
@@ -103,7 +118,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wtot) {
 // NB - 1 - i*BPT - j): the bin b with count(bins > b) < krem <=
 // count(bins >= b).  Also returns the count of bin b and, when total is
 // given, the sum of all the counts (the same in every thread).
-template <int NT, int NB>
+template <int NT, int NB, bool LDS_ONLY = false>
 __device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], uint32_t krem,
                                                 uint32_t* sh, uint32_t* wtot, uint32_t& bin,
                                                 uint32_t& krem_out, uint32_t& bin_count,
@@ -114,7 +129,7 @@ __device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], 
   uint32_t mine = 0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) mine += cnt[j];
-  const uint32_t incl = block_inclusive_sum<NT>(mine, wtot);
+  const uint32_t incl = block_inclusive_sum<NT, LDS_ONLY>(mine, wtot);
   // the wave totals stay in wtot until the next scan, past a barrier below
   if (total) *total = waves_total<NT>(wtot);
   uint32_t cum = incl - mine;
@@ -129,16 +144,16 @@ __device__ __forceinline__ void select_bin_regs(const uint32_t (&cnt)[NB / NT], 
       cum += cnt[j];
     }
   }
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
   bin = sh[0];
   krem_out = sh[1];
   bin_count = sh[2];
-  __syncthreads();
+  block_barrier<LDS_ONLY>();
 }
 
 // The same from an LDS histogram, where bin `xbin` counts `xcnt` more and
 // bin b is stored at hist[b ^ flip].
-template <int NT, int NB>
+template <int NT, int NB, bool LDS_ONLY = false>
 __device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem, uint32_t xbin,
                                              uint32_t xcnt, uint32_t* sh, uint32_t* wtot,
                                              uint32_t& bin, uint32_t& krem_out,
@@ -151,7 +166,7 @@ __device__ __forceinline__ void select_bin_r(const uint32_t* hist, uint32_t krem
     const int b = hi - 1 - j;
     cnt[j] = hist[(uint32_t)b ^ flip] + ((uint32_t)b == xbin ? xcnt : 0u);
   }
-  select_bin_regs<NT, NB>(cnt, krem, sh, wtot, bin, krem_out, bin_count);
+  select_bin_regs<NT, NB, LDS_ONLY>(cnt, krem, sh, wtot, bin, krem_out, bin_count);
 }
 
 // Row layout: element e of lane l of wave w is position w*64*EPT + 64e + l,

@@ -241,7 +241,6 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
     int64_t ld_out) {
-  constexpr int NV = EPT / 4;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t mbuf[NT * EPT / 16];
   __shared__ uint32_t wtot[2 * (NT / 64)];
@@ -338,7 +337,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     const int32_t* __restrict__ cand, int n_cand, int cbs, uint32_t* __restrict__ key_hist,
     int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out) {
-  constexpr int NV = EPT / 4, WPT = (kCandMaxT / 32) / NT;
+  constexpr int WPT = (kCandMaxT / 32) / NT;
   __shared__ uint32_t hist[2048];
   __shared__ int32_t ids[kCandMaxIds];
   __shared__ uint32_t mbuf[NT * EPT / 16];
@@ -596,8 +595,8 @@ struct SplitLayout {  // per-row workspace, in 32-bit words
     nparts = ((int64_t)T + kPart - 1) / kPart;
     cand_off = (nwords + 1) & ~(int64_t)1;               // [nparts][8 waves][1024] (key, pos)
     cnt_off = cand_off + nparts * kPartNW * 1024 * 2;    // [nparts][8 waves]
-    state_off = cnt_off + nparts * kPartNW;              // b1, krem
-    row_words = (state_off + 2 + 1) & ~(int64_t)1;       // rows and lists stay 8-byte aligned
+    state_off = cnt_off + nparts * kPartNW;              // b1, krem, histogram total
+    row_words = (state_off + 3 + 3) & ~(int64_t)3;       // rows 16-byte aligned, lists 8
   }
 };
 
@@ -616,7 +615,7 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
   const int base = part * kPart + w * SEG;
   float v[kPartEPT];
   load_vals<kPartEPT>(scores + (int64_t)r * ld, base, T, v);
-  uint32_t b1, krem;
+  uint32_t b1, krem, total;
   {
     constexpr int HPT = 2048 / NT;
     uint32_t hv[HPT], mine = 0;
@@ -627,7 +626,7 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
       hist[threadIdx.x + j * NT] = hv[j];
       mine += hv[j];
     }
-    const uint32_t total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
+    total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
     uint32_t bc;
     // positions the histogram does not count are -inf
     select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - total, sh, wtot, b1, krem,
@@ -636,6 +635,7 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
   if (part == 0 && threadIdx.x == 0) {
     wrow[L.state_off] = b1;
     wrow[L.state_off + 1] = krem;
+    wrow[L.state_off + 2] = total;  // kernel B checks it against compress_lens
   }
   const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
   const bool top = b1 >= 2044u;
@@ -694,55 +694,89 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   uint32_t* cpos = ckey + kSplitCandCap;
   const int nreg = (int)L.nparts * kPartNW;
 
-  // The score histogram counts exactly the c positions below compress_lens
-  // when it comes from idx_score on these scores.  Any other total (a stale
-  // or doubly filled histogram) made kernel A's threshold meaningless: the
-  // row is then ranked from its scores alone.
-  {
-    __shared__ uint32_t wcnt[2][NW];
-    uint32_t hs = 0;
-    for (int i = tid; i < 2048; i += NT) hs += key_hist[(int64_t)r * 2048 + i];
-    const uint32_t htotal = block_sum<NT>(hs, wtot);
-    if (htotal != (uint32_t)c) {
-      stream_rank_row<NT>(scores + (int64_t)r * ld, T, c, kout, offset,
-                          out + (int64_t)r * ld_out, hist, sh, wtot, wcnt);
-      for (int i = tid; i < 2048; i += NT) key_hist[(int64_t)r * 2048 + i] = 0u;
-      return;
-    }
-  }
-
-  // list counts (at most 256 regions) and the search state first
+  // Everything the ranking reads from kernel A's output is requested in one
+  // round: the search state (b1, krem and the histogram's total), the list
+  // counts (at most 256 regions), and the first 8 * tpr entries of every
+  // region (tpr threads per region, eight entries each; a region holds up to
+  // 1024, so these reads stay inside it whatever its count).
   static_assert(kSplitMaxT / kPart * kPartNW <= NT, "one region per thread");
   const uint32_t rc = tid < nreg ? wrow[L.cnt_off + tid] : 0u;
   const uint32_t b1 = wrow[L.state_off];
   uint32_t krem = wrow[L.state_off + 1];
-  // this thread's words of the above-threshold masks (kernel A's output) are
-  // requested once the list is in LDS: their latency then overlaps the
-  // threshold search, and no earlier wait on the list loads drains them
+  const uint32_t htotal = wrow[L.state_off + 2];
+  const uint32_t inf_count = key_hist[(int64_t)r * 2048 + kInfBin];
+  const int tpr = NT / nreg;  // at least 4
+  const int sj = tid / tpr, sli = tid - sj * tpr;
+  uint2 sv[8];
+  {
+    const uint2* src =
+        reinterpret_cast<const uint2*>(wrow + L.cand_off + (int64_t)(sj < nreg ? sj : 0) * 1024 * 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sv[u] = src[sli + u * tpr];
+  }
+  // this thread's words of the above-threshold masks (kernel A's output),
+  // requested in the same round as the state and the list: every barrier
+  // waits for the loads in flight, so any later request would be waited
+  // for on its own
   constexpr int kMaxWpt = (kSplitMaxT / 32 + NT - 1) / NT;
+  static_assert(kMaxWpt % 4 == 0, "whole 16-byte words per thread");
   const int wpt = (nw + NT - 1) / NT;
   uint32_t aw[kMaxWpt];
-  auto load_words = [&]() {
+  if ((wpt & 3) == 0 && (reinterpret_cast<uintptr_t>(wrow) & 15) == 0 && tid * wpt + wpt <= nw) {
+    // whole 16-byte words (rows are 16-byte aligned in a 16-byte aligned
+    // workspace): a quarter of the load instructions, each line read once;
+    // 8-byte words when the thread's count is even
+#pragma unroll
+    for (int j = 0; j < kMaxWpt; j += 4) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (j < wpt) v = *reinterpret_cast<const uint4*>(wrow + tid * wpt + j);
+      aw[j] = v.x;
+      aw[j + 1] = v.y;
+      aw[j + 2] = v.z;
+      aw[j + 3] = v.w;
+    }
+  } else if ((wpt & 1) == 0 && (reinterpret_cast<uintptr_t>(wrow) & 7) == 0 &&
+             tid * wpt + wpt <= nw) {
+#pragma unroll
+    for (int j = 0; j < kMaxWpt; j += 2) {
+      uint2 v = make_uint2(0u, 0u);
+      if (j < wpt) v = *reinterpret_cast<const uint2*>(wrow + tid * wpt + j);
+      aw[j] = v.x;
+      aw[j + 1] = v.y;
+    }
+  } else {
 #pragma unroll
     for (int j = 0; j < kMaxWpt; ++j) {
       const int word = tid * wpt + j;
       aw[j] = wrow[word < nw ? word : nw - 1];
     }
-  };
+  }
+
+  // The score histogram counts exactly the c positions below compress_lens
+  // when it comes from idx_score on these scores.  Any other total (a stale
+  // or doubly filled histogram; kernel A summed it) made kernel A's
+  // threshold meaningless: the row is then ranked from its scores alone.
+  if (htotal != (uint32_t)c) {
+    __shared__ uint32_t wcnt[2][NW];
+    stream_rank_row<NT>(scores + (int64_t)r * ld, T, c, kout, offset,
+                        out + (int64_t)r * ld_out, hist, sh, wtot, wcnt);
+    for (int i = tid; i < 2048; i += NT) key_hist[(int64_t)r * 2048 + i] = 0u;
+    return;
+  }
+
   for (int i = tid; i < nwp; i += NT) {
     sel[i] = 0u;
     eqm[i] = 0u;
   }
   // list counts -> region prefix, one block scan
-  const uint32_t rincl = block_inclusive_sum<NT>(rc, wtot);
+  const uint32_t rincl = block_inclusive_sum<NT, true>(rc, wtot);
   if (tid < nreg) regions[tid + 1] = rincl;
   if (tid == 0) regions[0] = 0;
-  __syncthreads();
+  lds_barrier();
   const uint32_t ncand = regions[nreg];
-  const bool only_inf = b1 == kInfBin && key_hist[(int64_t)r * 2048 + kInfBin] == 0u;
+  const bool only_inf = b1 == kInfBin && inf_count == 0u;
 
   uint32_t ustar = kKeyNegInf;
-  if (only_inf) load_words();
   if (!only_inf) {
     const bool in_lds = ncand <= (uint32_t)kSplitCandCap;
     // list element i lives in region j with regions[j] <= i < regions[j+1]
@@ -759,13 +793,21 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
     };
     if (in_lds) {
       // threads split evenly over the regions; each thread copies every
-      // tpr-th element of its region, eight loads in flight at a time
-      const int tpr = NT / nreg;  // at least 4
-      const int j = tid / tpr, li = tid - j * tpr;
+      // tpr-th element of its region: the first eight from the round above,
+      // the rest eight loads in flight at a time
+      const int j = sj, li = sli;
       if (j < nreg) {
         const uint32_t base = regions[j], cnt = regions[j + 1] - base;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t e = li + u * tpr;
+          if (e < cnt) {
+            ckey[base + e] = sv[u].x;
+            cpos[base + e] = sv[u].y;
+          }
+        }
         const uint2* src = reinterpret_cast<const uint2*>(wrow + L.cand_off + (int64_t)j * 1024 * 2);
-        for (uint32_t e0 = li; e0 < cnt; e0 += 8u * tpr) {
+        for (uint32_t e0 = li + 8u * tpr; e0 < cnt; e0 += 8u * tpr) {
           uint2 v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -782,11 +824,10 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
-    load_words();
-    // every pass over the list runs one of two loops, so the LDS loop never
-    // waits on the global loads in flight
+    // every pass over the list runs one of two loops (from LDS, or fetched
+    // from the workspace when the list does not fit)
     auto each = [&](auto&& body) {
       if (in_lds) {
         for (uint32_t i = tid; i < ncand; i += NT) body(ckey[i], cpos[i]);
@@ -798,20 +839,52 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
         }
       }
     };
-    uint32_t prefix = b1;
+    uint32_t prefix = b1, bc = 0;
     for (int pass = 1; pass < 3; ++pass) {
       const int nb = pass_bins(pass), shift = pass_shift(pass), ms = pass_match_shift(pass);
+      if (pass == 2 && bc <= 64u) {
+        // few keys share the 22-bit prefix (bc of them): collect them, and
+        // wave 0 finds the krem-th largest directly (lane i counts the keys
+        // above its own and those at least its own), two barriers instead
+        // of a histogram pass
+        __shared__ uint32_t small[64];
+        __shared__ uint32_t nsmall;
+        if (tid == 0) nsmall = 0u;
+        lds_barrier();
+        each([&](uint32_t k, uint32_t) {
+          if ((k >> ms) == prefix) small[atomicAdd(&nsmall, 1u)] = k;
+        });
+        lds_barrier();
+        if (tid < 64) {
+          const uint32_t mine = tid < (int)bc ? small[tid] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (uint32_t j = 0; j < bc; ++j) {
+            const uint32_t o = small[j];
+            gt += o > mine ? 1u : 0u;
+            ge += o >= mine ? 1u : 0u;
+          }
+          if (tid < (int)bc && gt < krem && krem <= ge) {  // one key value: equal writes
+            sh[0] = mine;
+            sh[1] = krem - gt;
+          }
+        }
+        lds_barrier();
+        prefix = sh[0];  // the whole key
+        krem = sh[1];
+        lds_barrier();
+        break;
+      }
       for (int i = tid; i < nb; i += NT) hist[i] = 0;
-      __syncthreads();
+      lds_barrier();
       each([&](uint32_t k, uint32_t) {
         if ((k >> ms) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
       });
-      __syncthreads();
-      uint32_t bin, k2, bc;
+      lds_barrier();
+      uint32_t bin, k2;
       if (pass == 1)
-        select_bin_r<NT, 2048>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
+        select_bin_r<NT, 2048, true>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
       else
-        select_bin_r<NT, 1024>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
+        select_bin_r<NT, 1024, true>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bc);
       prefix = extend_prefix(prefix, pass, bin);
       krem = k2;
     }
@@ -823,7 +896,7 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
     });
   }
   const uint32_t need = krem;
-  __syncthreads();
+  lds_barrier();
 
   // compaction: thread i owns words [i*wpt, (i+1)*wpt), wpt <= kMaxWpt; the
   // mask words are loaded together, the output row is assembled in LDS (the
