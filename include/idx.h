@@ -456,6 +456,30 @@ idx_status idx_publish_keys_paged(const uint16_t *latent, const uint16_t *wk, co
                                   int64_t bt_stride, int Tcap, void *stream);
 
 /*
+ * idx_score_topk_candidates -- the level-two pass of the two-level indexer
+ * ([IDX, forward]: scores of this layer's own weights, the non-candidate
+ * positions masked with -inf, then the top-k): idx_score in candidate mode,
+ * then idx_topk_candidates, with the scores kept per candidate slot instead
+ * of per position.  Slot v (0 <= v < n_cand * cand_block_size) is position
+ * cand_blocks[r][v / cbs] * cbs + v % cbs; slot_scores[r][v] receives its
+ * score (ld >= n_cand * cand_block_size; slots without a reachable position
+ * hold unspecified values), so no -inf fill of the row is needed.
+ * cand_blocks as idx_topk_candidates takes them (strictly ascending apart
+ * from skipped ids).  The other arguments, the indices, k_out and the
+ * histogram's handling are those of the two calls, and the indices equal
+ * theirs bit for bit.  The
+ * top-k's checks run before the score launches (IDX_EUNSUPPORTED where
+ * idx_topk_candidates would return it).
+ */
+idx_status idx_score_topk_candidates(const uint16_t *q, const uint16_t *w, const uint8_t *k_cache,
+                                     int64_t k_batch_stride_rows, int B, int S, int H, int D,
+                                     int T, const int32_t *compress_lens,
+                                     const int32_t *cand_blocks, int n_cand, int cand_block_size,
+                                     float *slot_scores, int64_t ld, uint32_t *key_hist,
+                                     int index_topk, int32_t offset, int32_t *out, int64_t ld_out,
+                                     int32_t *k_out, void *stream);
+
+/*
  * idx_score_select_blocks -- idx_score then idx_select_candidate_blocks on
  * the scores just written: the level-one pass of the two-level indexer
  * ([IDX, forward]: the candidate source layer scores every key, then

@@ -22,7 +22,7 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
-           "idx_publish_score", "idx_score_select_blocks",
+           "idx_publish_score", "idx_score_select_blocks", "idx_score_topk_candidates",
            "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
            "load_library", "IdxError", "ROW_BYTES"]
 
@@ -84,6 +84,8 @@ def load_library():
     L.idx_fp8_quant.argtypes = [P, i64, P, P, P]
     L.idx_score_fp8.argtypes = L.idx_score.argtypes
     L.idx_publish_keys_fp8.argtypes = L.idx_publish_keys.argtypes
+    L.idx_score_topk_candidates.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32,
+                                            P, i64, P, i32, ctypes.c_int32, P, i64, P, P]
     L.idx_score_select_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i64, P,
                                           i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
@@ -100,7 +102,7 @@ def load_library():
                  "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
-                 "idx_score_select_blocks"):
+                 "idx_score_select_blocks", "idx_score_topk_candidates"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -622,6 +624,42 @@ def idx_publish_keys(latent, wk, gamma, cos_sin, start_pos, ratio, eps, k_cache,
                                            cos_sin.shape[0], B, G, Din, D, rd, eps, start_pos,
                                            ratio, _ptr(k_cache), k_cache.shape[1],
                                            k_cache.shape[1]), stream, "idx_publish_keys", bind)
+
+
+def idx_score_topk_candidates(q, w, k_cache, B, S, T, compress_lens, cand_blocks,
+                              cand_block_size, slot_scores, index_topk, offset, out,
+                              key_hist=None, stream=None, bind=False):
+    """The level-two pass: idx_score in candidate mode with the scores kept
+    per candidate slot (slot_scores [B*S, ld] float32, ld >= n_cand *
+    cand_block_size), then idx_topk_candidates.  Returns k_out (None with
+    bind=True)."""
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+    _dev(slot_scores, "slot_scores", (torch.float32,), 2)
+    _dev(out, "out", (torch.int32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES:
+        raise ValueError("k_cache must be [>=B, Tcap, 68]")
+    if cand_blocks.shape[0] != R or slot_scores.shape[0] != R or out.shape[0] != R:
+        raise ValueError("cand_blocks, slot_scores and out must have B*S rows")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    k = ctypes.c_int32(-1)
+    r = _issue("idx_score_topk_candidates",
+               (_ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, S, H, D, T,
+                _ptr(compress_lens), _ptr(cand_blocks), cand_blocks.shape[1], cand_block_size,
+                _ptr(slot_scores), slot_scores.shape[1], _ptr(key_hist), index_topk, offset,
+                _ptr(out), out.shape[1], ctypes.byref(k)), stream, "idx_score_topk_candidates",
+               bind, keep=(k,))
+    return r if bind else k.value
 
 
 def idx_score_select_blocks(q, w, k_cache, B, S, T, compress_lens, scores, candidate_topk_blocks,

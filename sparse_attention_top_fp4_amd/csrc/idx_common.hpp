@@ -225,6 +225,13 @@ constexpr int kSelectWaveMaxBlocks = 1024;
 idx_status select_blocks_from_max(const float* bmax, int64_t ld_b, int R, int nb, int T,
                                   const int32_t* compress_lens, int cbs, int ctb, int32_t* ids,
                                   int64_t ld_ids, hipStream_t st);
+// idx_score in candidate mode with slot v's score at slot_scores[r][v]
+// (ld >= n_cand * cand_block_size) and no -inf fill.  Defined in score.hip.
+idx_status score_candidates_compact(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                    int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                                    const int32_t* compress_lens, const int32_t* cand_blocks,
+                                    int n_cand, int cand_block_size, float* slot_scores,
+                                    int64_t ld, uint32_t* key_hist, hipStream_t stream);
 inline idx_status launch_status() {
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

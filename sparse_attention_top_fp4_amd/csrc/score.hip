@@ -353,13 +353,18 @@ struct PubFuse {
   int on;                  // 0: no publish in this launch
 };
 
-// Extra output of the plain launch: the maximum of each cbs-wide block of
-// the chunk's scores (the block score of the candidate select), written
-// when bmax is set; chunk starts are then multiples of bmax_cbs.
+// Extra outputs of the plain and candidate launches.  Plain mode: the
+// maximum of each cbs-wide block of the chunk's scores (the block score of
+// the candidate select), written when bmax is set; chunk starts are then
+// multiples of bmax_cbs.  Candidate mode with compact: slot v's score goes
+// to scores[r][v] (the slots in list order, one contiguous run per chunk)
+// instead of to its position; slots without a reachable position hold
+// whatever their lanes computed.
 struct Epi {
   float* bmax;       // [R][bmax_ld], or null
   int64_t bmax_ld;
   int bmax_cbs;
+  int compact;
 };
 
 // The role of the extra workgroup of row r (sequence b, decode: one row per
@@ -824,11 +829,13 @@ done:
   }
   if (TOPK && !srow) {
     // scores not wanted: only the ranking below
-  } else if (!CAND && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
+  } else if ((!CAND || ep.compact) && (((uintptr_t)(srow + vbeg)) & 15) == 0) {
     float4* dst = reinterpret_cast<float4*>(srow + vbeg);
     const float4* src = reinterpret_cast<const float4*>(sbuf);
     for (int i = tid; i < (n >> 2); i += 256) dst[i] = src[i];
     for (int i = (n & ~3) + tid; i < n; i += 256) srow[vbeg + i] = sbuf[i];
+  } else if (CAND && ep.compact) {
+    for (int i = tid; i < n; i += 256) srow[vbeg + i] = sbuf[i];
   } else {
     for (int i = tid; i < n; i += 256) {
       const int p = pm.pos(vbeg + i);
@@ -977,7 +984,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                       const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
                       int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
                       idx::PageMap pg, void* stream, bool f8 = false,
-                      idx::Epi ep = idx::Epi{nullptr, 0, 0}) {
+                      idx::Epi ep = idx::Epi{nullptr, 0, 0, 0}) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -987,8 +994,11 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   if (!idx_host::aligned(q, 16) || !idx_host::aligned(q4, 4) || !idx_host::aligned(k_cache, 4) ||
       (pg.bt && (pg.page_stride & 3)))
     return IDX_EINVAL;
-  if (ld < T || (!pg.bt && k_batch_stride_rows < T)) return IDX_EINVAL;
   if (cand_blocks && (n_cand <= 0 || cand_block_size <= 0)) return IDX_EINVAL;
+  if (ep.compact && !cand_blocks) return IDX_EINVAL;
+  // a compact row holds the n_cand * cbs slots; a full row the T positions
+  const int64_t row_need = ep.compact ? (int64_t)n_cand * cand_block_size : T;
+  if (ld < row_need || (!pg.bt && k_batch_stride_rows < T)) return IDX_EINVAL;
   if (cand_blocks && n_cand > idx::kMaxCand) return IDX_EUNSUPPORTED;
   const int64_t R = (int64_t)B * S;
   if (R > 0x7fffffffLL) return IDX_EINVAL;
@@ -1009,8 +1019,11 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   if (ep.bmax && (cand_blocks || ep.bmax_cbs <= 0 || kpw % ep.bmax_cbs)) return IDX_EINVAL;
   if (cand_blocks) {
     if (R > 65535) return IDX_EUNSUPPORTED;
-    hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048), (unsigned)R),
-                       dim3(256), 0, st, scores, ld, T);
+    // full rows: every position outside the listed blocks is -inf
+    if (!ep.compact)
+      hipLaunchKernelGGL(idx::fill_neg_inf_kernel, dim3((unsigned)((T + 2047) / 2048),
+                                                        (unsigned)R),
+                         dim3(256), 0, st, scores, ld, T);
   }
   dim3 grid((unsigned)R, (unsigned)nchunks);
   auto kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true, false>
@@ -1058,7 +1071,7 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
   return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, q4, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
                       (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg,
-                      idx::PubFuse{}, idx::Epi{nullptr, 0, 0});
+                      idx::PubFuse{}, idx::Epi{nullptr, 0, 0, 0});
 }
 
 // Page map arguments shared by the paged entry points.
@@ -1081,6 +1094,20 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                     cand_blocks,
                     n_cand, cand_block_size, scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+// The candidate score with its slots written compactly (see Epi).
+idx_status idx_host::score_candidates_compact(const uint16_t* q, const uint16_t* w,
+                                              const uint8_t* k_cache, int64_t k_batch_stride_rows,
+                                              int B, int S, int H, int D, int T,
+                                              const int32_t* compress_lens,
+                                              const int32_t* cand_blocks, int n_cand,
+                                              int cand_block_size, float* slot_scores, int64_t ld,
+                                              uint32_t* key_hist, hipStream_t stream) {
+  if (!cand_blocks) return IDX_EINVAL;
+  return score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                    cand_blocks, n_cand, cand_block_size, slot_scores, ld, key_hist,
+                    idx::PageMap{nullptr, 0, 0, 0}, stream, false, idx::Epi{nullptr, 0, 0, 1});
 }
 
 extern "C" idx_status idx_score_select_blocks(const uint16_t* q, const uint16_t* w,
@@ -1119,7 +1146,7 @@ extern "C" idx_status idx_score_select_blocks(const uint16_t* q, const uint16_t*
   const idx_status e = score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
                                   compress_lens, nullptr, 0, 0, scores, ld, key_hist,
                                   idx::PageMap{nullptr, 0, 0, 0}, stream, false,
-                                  idx::Epi{bmax, nb, cand_block_size});
+                                  idx::Epi{bmax, nb, cand_block_size, 0});
   if (e != IDX_OK) return e;
   return idx_host::select_blocks_from_max(bmax, nb, (int)R, nb, T, compress_lens, cand_block_size,
                                           candidate_topk_blocks, block_ids, ld_ids,
@@ -1177,7 +1204,7 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
                       (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
                       idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
                       idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1},
-                      idx::Epi{nullptr, 0, 0});
+                      idx::Epi{nullptr, 0, 0, 0});
 }
 
 extern "C" idx_status idx_score_fp8(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,

@@ -336,7 +336,7 @@ template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_cand_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     const int32_t* __restrict__ cand, int n_cand, int cbs, uint32_t* __restrict__ key_hist,
-    int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out) {
+    int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out, int compact) {
   constexpr int WPT = (kCandMaxT / 32) / NT;
   __shared__ uint32_t hist[2048];
   __shared__ int32_t ids[kCandMaxIds];
@@ -356,14 +356,25 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   int c = cl_arr[r];
   c = c < 0 ? 0 : (c > T ? T : c);
   const int nb = (T + cbs - 1) / cbs;
+  const int V = n_cand * cbs;
+  const float* srow = scores + (int64_t)r * ld;
+  const int wbase = row_base<EPT>();
+  float v[EPT];
+  if (compact) {
+    // slot scores in slot order (idx_score_topk_candidates): requested
+    // beside the ids, not after them; slots past V read slot V - 1 (masked)
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int sv = wbase + 64 * e;
+      v[e] = srow[sv < V ? sv : V - 1];
+    }
+  }
   for (int i = tid; i < n_cand; i += NT) {
     const int id = cand[(int64_t)r * n_cand + i];
     ids[i] = (id < 0 || id >= nb) ? -1 : id;
   }
   for (int i = tid; i < 2048; i += NT) hist[i] = 0u;  // the next digit's histogram
   __syncthreads();
-  const int V = n_cand * cbs;
-  const float* srow = scores + (int64_t)r * ld;
   // slot v lies in candidate block v / cbs (a shift for the usual
   // power-of-two block size: the division is dozens of instructions)
   const bool pow2 = (cbs & (cbs - 1)) == 0;
@@ -377,8 +388,6 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
     const int p = id * cbs + (v - blk * cbs);
     return p < T ? p : -1;
   };
-  const int wbase = row_base<EPT>();
-  float v[EPT];
   uint32_t nfin = 0;
   {
     // validity as integer arithmetic on the sign bits, kept out of the
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
       asm volatile("" : "+v"(ok), "+v"(below_c));
       okp[e] = ok;
       fin[e] = below_c;
-      v[e] = srow[p & ~(p >> 31)];
+      if (!compact) v[e] = srow[p & ~(p >> 31)];
     }
     // no such slot: NaN (absent); at or past c: -inf
 #pragma unroll
@@ -1414,40 +1423,81 @@ idx_status idx_host::select_blocks_from_max(const float* bmax, int64_t ld_b, int
   return idx_host::launch_status();
 }
 
-extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R, int T,
-                                          const int32_t* compress_lens, const int32_t* cand_blocks,
-                                          int n_cand, int cand_block_size, uint32_t* key_hist,
-                                          int index_topk, int32_t offset, int32_t* out,
-                                          int64_t ld_out, int32_t* k_out, void* stream) {
+namespace {
+// idx_topk_candidates on full rows (compact = false) or on slot scores
+// (compact = true: scores[r][v] is slot v's score, ld >= n_cand * cbs).
+idx_status topk_candidates_impl(const float* scores, int64_t ld, int R, int T,
+                                const int32_t* compress_lens, const int32_t* cand_blocks,
+                                int n_cand, int cand_block_size, uint32_t* key_hist,
+                                int index_topk, int32_t offset, int32_t* out, int64_t ld_out,
+                                int32_t* k_out, hipStream_t st, bool compact, bool check_only) {
   if (R < 0 || T < 0 || index_topk <= 0 || n_cand <= 0 || cand_block_size <= 0) return IDX_EINVAL;
   const int kout = index_topk < T ? index_topk : T;
   if (R == 0 || T == 0) {
-    if (k_out) *k_out = kout;
+    if (k_out && !check_only) *k_out = kout;
     return IDX_OK;
   }
   if (!scores || !compress_lens || !cand_blocks || !out) return IDX_EINVAL;
-  if (ld < T || ld_out < kout) return IDX_EINVAL;
-  hipStream_t st = (hipStream_t)stream;
+  const int64_t V = (int64_t)n_cand * cand_block_size;
+  if (ld < (compact ? V : (int64_t)T) || ld_out < kout) return IDX_EINVAL;
+  if (index_topk < T && (T > idx::kCandMaxT || n_cand > idx::kCandMaxIds || V > 8192))
+    return IDX_EUNSUPPORTED;
+  if (check_only) return IDX_OK;
+  if (k_out) *k_out = kout;
   if (index_topk >= T) {
-    if (k_out) *k_out = kout;
     hipLaunchKernelGGL(idx::topk_all_kernel, dim3((unsigned)R), dim3(256), 0, st, T,
                        compress_lens, offset, out, ld_out);
     if (key_hist) zero_hist(key_hist, R, st);
     return idx_host::launch_status();
   }
-  const int64_t V = (int64_t)n_cand * cand_block_size;
-  if (T > idx::kCandMaxT || n_cand > idx::kCandMaxIds || V > 8192) return IDX_EUNSUPPORTED;
-  if (k_out) *k_out = kout;
   // few rows, each a latency chain: many threads per row, few keys each
   if (V <= 2048)
     hipLaunchKernelGGL((idx::topk_cand_kernel<256, 8>), dim3((unsigned)R), dim3(256), 0, st,
                        scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size,
-                       key_hist, kout, offset, out, ld_out);
+                       key_hist, kout, offset, out, ld_out, compact ? 1 : 0);
   else
     hipLaunchKernelGGL((idx::topk_cand_kernel<1024, 8>), dim3((unsigned)R), dim3(1024), 0, st,
                        scores, ld, T, compress_lens, cand_blocks, n_cand, cand_block_size,
-                       key_hist, kout, offset, out, ld_out);
+                       key_hist, kout, offset, out, ld_out, compact ? 1 : 0);
   return idx_host::launch_status();
+}
+}  // namespace
+
+extern "C" idx_status idx_topk_candidates(const float* scores, int64_t ld, int R, int T,
+                                          const int32_t* compress_lens, const int32_t* cand_blocks,
+                                          int n_cand, int cand_block_size, uint32_t* key_hist,
+                                          int index_topk, int32_t offset, int32_t* out,
+                                          int64_t ld_out, int32_t* k_out, void* stream) {
+  return topk_candidates_impl(scores, ld, R, T, compress_lens, cand_blocks, n_cand,
+                              cand_block_size, key_hist, index_topk, offset, out, ld_out, k_out,
+                              (hipStream_t)stream, false, false);
+}
+
+extern "C" idx_status idx_score_topk_candidates(
+    const uint16_t* q, const uint16_t* w, const uint8_t* k_cache, int64_t k_batch_stride_rows,
+    int B, int S, int H, int D, int T, const int32_t* compress_lens, const int32_t* cand_blocks,
+    int n_cand, int cand_block_size, float* slot_scores, int64_t ld, uint32_t* key_hist,
+    int index_topk, int32_t offset, int32_t* out, int64_t ld_out, int32_t* k_out, void* stream) {
+  if (B < 0 || S < 0) return IDX_EINVAL;
+  const int64_t R = (int64_t)B * S;
+  if (R > 0x7fffffffLL) return IDX_EINVAL;
+  // the top-k's checks first: nothing launches on a call it would refuse
+  const idx_status e = topk_candidates_impl(slot_scores, ld, (int)R, T, compress_lens,
+                                            cand_blocks, n_cand, cand_block_size, key_hist,
+                                            index_topk, offset, out, ld_out, k_out,
+                                            (hipStream_t)stream, true, true);
+  if (e != IDX_OK) return e;
+  if (R == 0 || T == 0) {
+    if (k_out) *k_out = index_topk < T ? index_topk : T;
+    return IDX_OK;
+  }
+  const idx_status s = idx_host::score_candidates_compact(
+      q, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens, cand_blocks, n_cand,
+      cand_block_size, slot_scores, ld, key_hist, (hipStream_t)stream);
+  if (s != IDX_OK) return s;
+  return topk_candidates_impl(slot_scores, ld, (int)R, T, compress_lens, cand_blocks, n_cand,
+                              cand_block_size, key_hist, index_topk, offset, out, ld_out, k_out,
+                              (hipStream_t)stream, true, false);
 }
 
 // ------------------------------------------------- allocation-free top-k

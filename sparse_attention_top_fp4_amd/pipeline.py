@@ -16,7 +16,7 @@ import numpy as np
 
 from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
                idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
-               idx_publish_score, idx_score_select_blocks,
+               idx_publish_score, idx_score_select_blocks, idx_score_topk_candidates,
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
@@ -151,6 +151,11 @@ class IndexerStep:
                                  not self.fused and not (q_step and not wl.ctb) and
                                  wl.din <= 2048)
 
+        # level two keeps its scores per candidate slot (scores2[r][v]) on
+        # contiguous fp4 caches with bf16 queries
+        self.l2_compact = (self.two_level and not paged and not fp8 and
+                           not (q_step and not wl.ctb))
+
         # every step's calls, marshalled once per key-cache copy
         self._plans = [self._plan(kc) for kc in self.caches]
 
@@ -256,6 +261,13 @@ class IndexerStep:
                                   workspace=self.topk_ws, key_hist=self.key_hist, **b))
             # level two: only the candidate positions hold finite scores; the
             # histogram, reset by the level-one top-k, now counts them
+            if self.l2_compact:
+                # level two in one call: slot scores, no -inf fill of the rows
+                calls.append(idx_score_topk_candidates(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl,
+                                                       self.ids, wl.cbs, self.scores2, wl.topk,
+                                                       wl.offset, self.out,
+                                                       key_hist=self.key_hist, **b))
+                return calls, score_at
             if self.paged:
                 calls.append(idx_score_paged(q, self.w2, kc, self.block_table, wl.B, wl.S, wl.T,
                                              self.cl, self.scores2, cand_blocks=self.ids,
@@ -273,6 +285,26 @@ class IndexerStep:
             calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
                                   workspace=self.topk_ws, key_hist=self.key_hist, **b))
         return calls, score_at
+
+    def level_two_rows(self):
+        """The level-two scores as full rows [R, T]: scores2 itself, or, when
+        level two keeps them per candidate slot, scattered to their
+        positions (-inf at every other position and at or past
+        compress_lens, as the full-row form leaves them)."""
+        if not self.l2_compact:
+            return self.scores2
+        torch = _torch()
+        wl = self.wl
+        R, T, cbs = wl.R, wl.T, wl.cbs
+        V = self.ids.shape[1] * cbs
+        v = torch.arange(V, device="cuda")
+        blk = self.ids.long()[:, v // cbs]
+        pos = blk * cbs + (v % cbs)[None, :]
+        ok = (blk >= 0) & (pos < T) & (pos < self.cl.long()[:, None].clamp(0, T))
+        full = torch.full((R, T + 1), float("-inf"), dtype=torch.float32, device="cuda")
+        idx = torch.where(ok, pos, torch.full_like(pos, T))  # invalid slots land in column T
+        full.scatter_(1, idx, torch.where(ok, self.scores2[:, :V], full[:, :1].expand(-1, V)))
+        return full[:, :T].contiguous()
 
     def keys_scored(self):
         """Algorithmic (query, key) pairs scored per step.  The fused launch

@@ -257,6 +257,27 @@ def test_score_select_blocks_checks_before_launch(lib):
     assert call(B=0) == IDX_OK  # nothing to do
 
 
+def test_score_topk_candidates_checks_before_launch(lib):
+    """idx_score_topk_candidates checks the top-k's arguments before the
+    score launches and leaves k_out untouched when it refuses."""
+    d = ctypes.c_void_p(0x1000)
+    T, B = 65536, 4
+
+    def call(n_cand=64, cbs=128, ld=8192, ld_out=2048, k=2048, kref=None, Bv=B, Tv=T):
+        return lib.idx_score_topk_candidates(d, d, d, Tv, Bv, 1, 64, 128, Tv, d, d, n_cand, cbs,
+                                             d, ld, None, k, 0, d, ld_out,
+                                             kref if kref is not None else None, None)
+
+    kk = ctypes.c_int32(-1)
+    assert call(ld=8191, kref=ctypes.byref(kk)) == IDX_EINVAL and kk.value == -1  # < n_cand * cbs
+    assert call(ld_out=2047) == IDX_EINVAL
+    assert call(n_cand=0) == IDX_EINVAL
+    assert call(k=0) == IDX_EINVAL
+    assert call(n_cand=65, ld=65 * 128) == IDX_EUNSUPPORTED  # more than 8192 slots ranked
+    assert call(Tv=70000) == IDX_EUNSUPPORTED  # rows past the candidate ranking's width
+    assert call(Bv=0, kref=ctypes.byref(kk)) == IDX_OK and kk.value == 2048
+
+
 def test_paged_entry_points_reject_bad_page_maps(lib):
     """Page pool, page stride and block table are checked before any launch."""
     d = ctypes.c_void_p(0x1000)

@@ -6,7 +6,12 @@ its own scores).  Cases take the single-launch form (block maxima from the
 score launch, one wave per row ranks them) and both two-call forms (blocks
 that straddle score chunks; more blocks than one wave ranks), with rows whose
 compress_lens is T, a part of T, 1 and 0, decode and prefill rows, and 32
-and 64 heads."""
+and 64 heads.  idx_score_topk_candidates, the level-two pass: slot scores
+bit-identical to the oracle's scores at the slots' positions, indices and
+the histogram's reset equal to idx_score + idx_topk_candidates, over
+ascending lists with skipped ids (negative, past the row's blocks) in
+between, rows with compress_lens below
+the blocks, short lists (fewer finite candidates than k) and k >= T."""
 import numpy as np
 import pytest
 
@@ -74,3 +79,73 @@ def test_score_select_blocks_matches_oracle(idx, case):
         assert np.array_equal(bits(got[r, :n]), bits(ref[r, :n])), r
     assert np.array_equal(host(hist).astype(np.int64), _counted_hist(ref, c["cl"], T))
     assert np.array_equal(host(ids), ids_ref)
+
+
+L2_CASES = [
+    # (seed, B, H, T, cbs, ids per row, k, cl override)
+    (141, 4, 64, 65536, 128, "select", 2048, None),            # the two-level workload's shape
+    (142, 2, 32, 20000, 128, "select", 500, [20000, 9000]),    # 32 heads, cl cuts blocks
+    (143, 3, 64, 5000, 64, "messy", 300, None),                # skipped ids in between
+    (144, 2, 64, 4096, 128, "few", 2048, None),                # fewer finite candidates than k
+    (145, 2, 64, 600, 128, "select", 2048, None),              # k >= T: the closed form
+]
+
+
+@pytest.mark.parametrize("case", L2_CASES)
+def test_score_topk_candidates_matches_two_calls(idx, case):
+    t = torch()
+    seed, B, H, T, cbs, mode, k, cl = case
+    say("level two", case)
+    c = small_case(seed, B, 1, H, T)
+    if cl is not None:
+        c["cl"] = np.array(cl, np.int32)
+    rng = np.random.default_rng(seed)
+    nb = (T + cbs - 1) // cbs
+    if mode == "select":
+        ids = np.stack([np.sort(rng.choice(nb, size=min(16, nb), replace=False))
+                        for _ in range(B)]).astype(np.int32)
+    elif mode == "messy":
+        # strictly ascending valid ids with skipped ones (negative, past the
+        # row's blocks) in between, as idx_topk_candidates takes them
+        ids = np.array([[-1, 0, 3, nb + 5, 7, 12, -4, 40],
+                        [1, 2, -4, 8, 9, 11, nb + 1, 70],
+                        [0, 1, 2, 3, 4, 5, 6, 78]], np.int32)[:B]
+    else:
+        ids = np.array([[1, 5], [0, 31]], np.int32)[:B]
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref_ids = np.where((ids >= 0) & (ids < nb), ids, -1)
+    ref, _ = oracle.score(c["q"], c["w"], kc_ref, B, 1, H, T, c["cl"], cand=ref_ids, cbs=cbs)
+    kc = fp4_cache(c["k"])
+    q, w, cld, idd = dev(c["q"]), dev(c["w"]), dev(c["cl"]), dev(ids)
+    kout = min(k, T)
+    V = ids.shape[1] * cbs
+    outs = []
+    for fused in (True, False):
+        hist = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        out = t.full((B, kout), -9, dtype=t.int32, device="cuda")
+        if fused:
+            sc = t.full((B, V + 5), float("nan"), dtype=t.float32, device="cuda")
+            ko = idx.idx_score_topk_candidates(q, w, kc, B, 1, T, cld, idd, cbs, sc, k, 7, out,
+                                               key_hist=hist)
+        else:
+            sc = t.full((B, T), float("nan"), dtype=t.float32, device="cuda")
+            idx.idx_score(q, w, kc, B, 1, T, cld, sc, cand_blocks=idd, cand_block_size=cbs,
+                          key_hist=hist)
+            ko = idx.idx_topk_candidates(sc, T, cld, idd, cbs, k, 7, out, key_hist=hist)
+        sync()
+        assert ko == kout
+        assert not host(hist).any()  # consumed and reset
+        outs.append((host(out), host(sc)))
+    (o_f, s_f), (o_2, s_2) = outs
+    assert np.array_equal(o_f, o_2)
+    assert np.array_equal(o_f, oracle.topk(ref, c["cl"], k, 7))
+    # slot scores at their reachable positions equal the oracle's
+    for r in range(B):
+        for v in range(V):
+            blk = ids[r, v // cbs]
+            if blk < 0 or blk >= nb:
+                continue
+            p = blk * cbs + v % cbs
+            if p < min(int(c["cl"][r]), T):
+                assert bits(s_f[r, v:v + 1])[0] == bits(ref[r, p:p + 1])[0], (r, v, p)
+    assert np.all(np.isnan(s_f[:, V:]))  # nothing past the slots

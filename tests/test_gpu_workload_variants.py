@@ -69,7 +69,7 @@ def test_paged_step_equals_contiguous(cid):
     if b.two_level:
         assert np.array_equal(host(b.ids), host(a.ids))
         assert np.array_equal(host(b.out_l1), host(a.out_l1))
-        assert _equal_below_cl(b.scores2, a.scores2, cl)
+        assert _equal_below_cl(b.level_two_rows(), a.level_two_rows(), cl)
     # a sampled row against the oracle directly, and (publish) the cache
     r = wl.R - 1
     sb = r // wl.S

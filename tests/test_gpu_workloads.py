@@ -132,7 +132,7 @@ def test_causal_prefill_32k():
 def test_two_level_256k():
     wl, inp, st = _run(3)
     s1, ids, o1 = host(st.scores), host(st.ids), host(st.out_l1)
-    s2, out = host(st.scores2), host(st.out)
+    s2, out = host(st.level_two_rows()), host(st.out)
     cl = inp["cl"]
     _invariants(out, cl, st.kout, wl.offset)
     _invariants(o1, cl, st.kout, wl.offset)
