@@ -943,7 +943,7 @@ int keys_per_wg_override() {
   return v;
 }
 
-int pick_keys_per_wg(int64_t R, int vtotal, int slots = 256) {
+int pick_keys_per_wg(int64_t R, int vtotal, int slots = 256, int min_kpw = 1024) {
   if (keys_per_wg_override() > 0) {
     const int o = (keys_per_wg_override() + 255) / 256 * 256;
     return o < kMaxKeysPerWg ? o : kMaxKeysPerWg;
@@ -951,12 +951,14 @@ int pick_keys_per_wg(int64_t R, int vtotal, int slots = 256) {
   // about one workgroup per CU over the whole launch (256 CUs): measured on
   // the decode shapes, one workgroup of four waves per CU streams as fast as
   // two or more, and each workgroup pays the query load and quantisation
-  // once; at least 1024 keys per workgroup so that cost stays amortised
+  // once; at least min_kpw keys per workgroup so that cost stays amortised
+  // (1024; 512 for candidate slots, whose launches are latency-bound: on the
+  // two-level workload 512 took the step from 56.9 to 55.3 us)
   // slots: the CUs left for the chunks (fewer when other workgroups of the
   // launch hold some of them)
   const int64_t total = R * (int64_t)vtotal;
   int64_t kpw = (total + slots - 1) / slots;
-  if (kpw < 1024) kpw = 1024;
+  if (kpw < min_kpw) kpw = min_kpw;
   if (kpw > vtotal) kpw = vtotal;
   if (kpw > kMaxKeysPerWg) kpw = kMaxKeysPerWg;
   if (kpw < 256) kpw = 256;
@@ -1008,7 +1010,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
     vtotal = (int64_t)n_cand * cand_block_size;
     if (vtotal > 0x7fffffffLL) return IDX_EINVAL;
   }
-  const int kpw = pick_keys_per_wg(R, (int)vtotal);
+  const int kpw = pick_keys_per_wg(R, (int)vtotal, 256, cand_blocks ? 512 : 1024);
   const int64_t nchunks = (vtotal + kpw - 1) / kpw;
   if (nchunks > 65535) return IDX_EINVAL;
   size_t lds = (size_t)kpw * sizeof(float);
