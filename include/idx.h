@@ -480,6 +480,37 @@ idx_status idx_score_topk_candidates(const uint16_t *q, const uint16_t *w, const
                                      int32_t *k_out, void *stream);
 
 /*
+ * idx_two_level_topk -- what follows the level-one select in a two-level
+ * step ([IDX, forward]: the top-k of the candidate source layer's scores,
+ * and the other layer's scores of the candidate blocks with their own
+ * top-k): idx_topk of the level-one scores into out1, then
+ * idx_score_topk_candidates into out2, with the same results bit for bit.
+ * The two rankings do not depend on each other, so when level one takes the
+ * split path (32768 < T <= 131072, key_hist given) and level two the
+ * 1024-thread candidate ranking (n_cand * cand_block_size > 2048,
+ * index_topk < T, key_hist2 given), they run side by side in one launch,
+ * after level one's first split kernel and the candidate score; otherwise
+ * the two calls run in order.
+ *   scores, ld, key_hist, out1, ld_out1, ws, ws_bytes: idx_topk's arguments
+ *           for level one (key_hist is reset for the next score call; ws as
+ *           idx_topk_workspace_size gives)
+ *   q .. ld_out2: idx_score_topk_candidates' arguments for level two (w2 its
+ *           head weights, out2 its indices, key_hist2 its histogram)
+ * The two histograms must be distinct buffers when both are given
+ * (IDX_EINVAL otherwise): the rankings read and reset them side by side.
+ * index_topk and offset serve both levels.  Every check of both calls runs
+ * before anything launches.
+ */
+idx_status idx_two_level_topk(const float *scores, int64_t ld, uint32_t *key_hist, int32_t *out1,
+                              int64_t ld_out1, void *ws, size_t ws_bytes, const uint16_t *q,
+                              const uint16_t *w2, const uint8_t *k_cache,
+                              int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
+                              const int32_t *compress_lens, const int32_t *cand_blocks,
+                              int n_cand, int cand_block_size, float *slot_scores, int64_t ld2,
+                              uint32_t *key_hist2, int index_topk, int32_t offset, int32_t *out2,
+                              int64_t ld_out2, void *stream);
+
+/*
  * idx_score_select_blocks -- idx_score then idx_select_candidate_blocks on
  * the scores just written: the level-one pass of the two-level indexer
  * ([IDX, forward]: the candidate source layer scores every key, then

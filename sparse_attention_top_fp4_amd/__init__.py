@@ -23,6 +23,7 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
            "idx_publish_score", "idx_score_select_blocks", "idx_score_topk_candidates",
+           "idx_two_level_topk",
            "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
            "load_library", "IdxError", "ROW_BYTES"]
 
@@ -86,6 +87,8 @@ def load_library():
     L.idx_publish_keys_fp8.argtypes = L.idx_publish_keys.argtypes
     L.idx_score_topk_candidates.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i32, i32,
                                             P, i64, P, i32, ctypes.c_int32, P, i64, P, P]
+    L.idx_two_level_topk.argtypes = [P, i64, P, P, i64, P, sz, P, P, P, i64, i32, i32, i32, i32, i32,
+                                     P, P, i32, i32, P, i64, P, i32, ctypes.c_int32, P, i64, P]
     L.idx_score_select_blocks.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, i64, P,
                                           i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
@@ -102,7 +105,7 @@ def load_library():
                  "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
-                 "idx_score_select_blocks", "idx_score_topk_candidates"):
+                 "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -660,6 +663,52 @@ def idx_score_topk_candidates(q, w, k_cache, B, S, T, compress_lens, cand_blocks
                 _ptr(out), out.shape[1], ctypes.byref(k)), stream, "idx_score_topk_candidates",
                bind, keep=(k,))
     return r if bind else k.value
+
+
+def idx_two_level_topk(scores, key_hist, out1, workspace, q, w2, k_cache, B, S, T,
+                       compress_lens, cand_blocks, cand_block_size, slot_scores, key_hist2,
+                       index_topk, offset, out2, stream=None, bind=False):
+    """The rest of a two-level step after the level-one select: idx_topk of
+    the level-one scores [B*S, ld] into out1 (key_hist: its histogram,
+    workspace: as for idx_topk, allocated here when None), then
+    idx_score_topk_candidates with head weights w2 into out2 (slot_scores,
+    key_hist2: level two's own buffers).  On the split path the two rankings
+    run side by side in one launch."""
+    torch = _torch()
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(out1, "out1", (torch.int32,), 2)
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w2, "w2", _bf16_types(), 2)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(cand_blocks, "cand_blocks", (torch.int32,), 2)
+    _dev(slot_scores, "slot_scores", (torch.float32,), 2)
+    _dev(out2, "out2", (torch.int32,), 2)
+    R, H, D = q.shape
+    if R != B * S or tuple(w2.shape) != (R, H) or compress_lens.shape[0] != R:
+        raise ValueError("q/w2/compress_lens rows must be B*S")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES:
+        raise ValueError("k_cache must be [>=B, Tcap, 68]")
+    for name, t in (("scores", scores), ("out1", out1), ("cand_blocks", cand_blocks),
+                    ("slot_scores", slot_scores), ("out2", out2)):
+        if t.shape[0] != R:
+            raise ValueError(f"{name} must have B*S rows")
+    for name, h in (("key_hist", key_hist), ("key_hist2", key_hist2)):
+        if h is not None:
+            _dev(h, name, (torch.int32,), 2)
+            if tuple(h.shape) != (R, 2048):
+                raise ValueError(f"{name} must be [B*S, 2048]")
+    need = idx_topk_workspace_size(R, T, index_topk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _issue("idx_two_level_topk",
+                  (_ptr(scores), scores.shape[1], _ptr(key_hist), _ptr(out1), out1.shape[1],
+                   _ptr(workspace), wsb, _ptr(q), _ptr(w2), _ptr(k_cache), k_cache.shape[1], B, S,
+                   H, D, T, _ptr(compress_lens), _ptr(cand_blocks), cand_blocks.shape[1],
+                   cand_block_size, _ptr(slot_scores), slot_scores.shape[1], _ptr(key_hist2),
+                   index_topk, offset, _ptr(out2), out2.shape[1]), stream, "idx_two_level_topk",
+                  bind, keep=(workspace,))
 
 
 def idx_score_select_blocks(q, w, k_cache, B, S, T, compress_lens, scores, candidate_topk_blocks,

@@ -333,8 +333,8 @@ constexpr int kCandMaxT = 65536;    // row width the fallback bit map covers
 constexpr int kCandMaxIds = 2048;   // candidate ids per row held in LDS
 
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) void topk_cand_kernel(
-    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+__device__ __forceinline__ void cand_rank_row(
+    int r, const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     const int32_t* __restrict__ cand, int n_cand, int cbs, uint32_t* __restrict__ key_hist,
     int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out, int compact) {
   constexpr int WPT = (kCandMaxT / 32) / NT;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   __shared__ uint32_t mbuf[NT * EPT / 16];
   __shared__ uint32_t wtot[2 * (NT / 64)];
   __shared__ uint32_t sh[4];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   uint32_t* hrow = key_hist ? key_hist + (int64_t)r * 2048 : nullptr;
   // the score histogram (level two: counts of the candidate positions below
   // compress_lens) is requested first, this thread's bins [hhi - HPT, hhi)
@@ -524,6 +524,15 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(
   (void)lane;
 }
 
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_cand_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    const int32_t* __restrict__ cand, int n_cand, int cbs, uint32_t* __restrict__ key_hist,
+    int kout, int32_t offset, int32_t* __restrict__ out, int64_t ld_out, int compact) {
+  cand_rank_row<NT, EPT>((int)blockIdx.x, scores, ld, T, cl_arr, cand, n_cand, cbs, key_hist, kout,
+                         offset, out, ld_out, compact);
+}
+
 // ------------------------------------------------ streaming one-row ranking
 // One workgroup ranks a whole row by streaming its scores from memory in
 // tiles of NT*EPT: three digit passes of LDS histograms over the row, then
@@ -676,8 +685,8 @@ __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
 #endif
 constexpr int kSplitBThreads = IDX_SPLIT_B_THREADS;
 
-__global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
-    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+__device__ __forceinline__ void split_b_row(
+    int r, const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
     int64_t ld_out, const uint32_t* __restrict__ ws) {
   constexpr int NT = kSplitBThreads, NW = NT / 64;
@@ -690,7 +699,7 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   __shared__ uint32_t wtot[NW];
   __shared__ uint32_t wtot2[2 * NW];
   __shared__ uint32_t sh[4];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const SplitLayout L(T);
   const uint32_t* wrow = ws + (int64_t)r * L.row_words;
   int c = cl_arr[r];
@@ -968,6 +977,33 @@ __global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
   // every thread read the histogram before the scans above: reset it for the
   // next score call
   for (int i = tid; i < 2048; i += NT) key_hist[(int64_t)r * 2048 + i] = 0u;
+}
+
+__global__ __launch_bounds__(kSplitBThreads) void topk_split_b_kernel(
+    const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out,
+    int64_t ld_out, const uint32_t* __restrict__ ws) {
+  split_b_row((int)blockIdx.x, scores, ld, T, cl_arr, key_hist, kout, offset, out, ld_out, ws);
+}
+
+// The two rankings of a two-level step in one launch (idx_two_level_topk):
+// workgroups [0, R) run kernel B on level one's rows, workgroups [R, 2R) the
+// candidate top-k on level two's slot scores.  Neither reads what the other
+// writes (each level has its own histogram), and each alone fills only R
+// CUs, so side by side they take about as long as the longer of the two.
+static_assert(kSplitBThreads == 1024, "the candidate rows run on 1024 threads");
+constexpr int kTwoLevelMaxT = 131072;  // kernel B's LDS beside the candidate kernel's
+__global__ __launch_bounds__(1024) void topk_split_b_cand_kernel(
+    int R, const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
+    uint32_t* __restrict__ key_hist, int kout, int32_t offset, int32_t* __restrict__ out1,
+    int64_t ld_out1, const uint32_t* __restrict__ ws, const float* __restrict__ slot_scores,
+    int64_t ld2, const int32_t* __restrict__ cand, int n_cand, int cbs,
+    uint32_t* __restrict__ key_hist2, int32_t* __restrict__ out2, int64_t ld_out2) {
+  if ((int)blockIdx.x < R)
+    split_b_row((int)blockIdx.x, scores, ld, T, cl_arr, key_hist, kout, offset, out1, ld_out1, ws);
+  else
+    cand_rank_row<1024, 8>((int)blockIdx.x - R, slot_scores, ld2, T, cl_arr, cand, n_cand, cbs,
+                           key_hist2, kout, offset, out2, ld_out2, 1);
 }
 
 // ------------------------------------------------- multi-workgroup path
@@ -1498,6 +1534,82 @@ extern "C" idx_status idx_score_topk_candidates(
   return topk_candidates_impl(slot_scores, ld, (int)R, T, compress_lens, cand_blocks, n_cand,
                               cand_block_size, key_hist, index_topk, offset, out, ld_out, k_out,
                               (hipStream_t)stream, true, false);
+}
+
+// The rest of a two-level step after the level-one select: the level-one
+// top-k of `scores` and level two's candidate score and top-k.  On the
+// split path (32768 < T <= kTwoLevelMaxT, histograms given, level two on
+// the 1024-thread candidate kernel) it is three launches: kernel A of level
+// one, the candidate score, then kernel B and the candidate top-k side by
+// side; otherwise idx_topk then idx_score_topk_candidates.
+namespace {
+bool set_two_level_lds_limit() {
+  static std::atomic<uint64_t> done_mask{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done_mask.load(std::memory_order_acquire) & bit)) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&idx::topk_split_b_cand_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)split_b_lds(idx::kTwoLevelMaxT)) != hipSuccess)
+    return false;
+  if (bit) done_mask.fetch_or(bit, std::memory_order_acq_rel);
+  return true;
+}
+}  // namespace
+
+extern "C" idx_status idx_two_level_topk(
+    const float* scores, int64_t ld, uint32_t* key_hist, int32_t* out1, int64_t ld_out1, void* ws,
+    size_t ws_bytes, const uint16_t* q, const uint16_t* w2, const uint8_t* k_cache,
+    int64_t k_batch_stride_rows, int B, int S, int H, int D, int T, const int32_t* compress_lens,
+    const int32_t* cand_blocks, int n_cand, int cand_block_size, float* slot_scores, int64_t ld2,
+    uint32_t* key_hist2, int index_topk, int32_t offset, int32_t* out2, int64_t ld_out2,
+    void* stream) {
+  if (B < 0 || S < 0 || T < 0 || index_topk <= 0) return IDX_EINVAL;
+  const int64_t R = (int64_t)B * S;
+  if (R > 0x7fffffffLL) return IDX_EINVAL;
+  if (R == 0 || T == 0) return IDX_OK;
+  // every check of both levels before anything launches
+  const int kout = index_topk < T ? index_topk : T;
+  if (!scores || !compress_lens || !out1 || ld < T || ld_out1 < kout) return IDX_EINVAL;
+  if (key_hist && key_hist == key_hist2) return IDX_EINVAL;  // one histogram per level
+  {
+    const idx_status e = topk_candidates_impl(slot_scores, ld2, (int)R, T, compress_lens,
+                                              cand_blocks, n_cand, cand_block_size, key_hist2,
+                                              index_topk, offset, out2, ld_out2, nullptr,
+                                              (hipStream_t)stream, true, true);
+    if (e != IDX_OK) return e;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t V = (int64_t)n_cand * cand_block_size;
+  const bool together = use_split(T, key_hist) && T <= idx::kTwoLevelMaxT && key_hist2 &&
+                        index_topk < T && V > 2048 && R <= 65535;
+  if (!together) {
+    const idx_status e = topk_launch(scores, ld, (int)R, T, compress_lens, key_hist, index_topk,
+                                     offset, out1, ld_out1, ws, ws_bytes, st);
+    if (e != IDX_OK) return e;
+    return idx_score_topk_candidates(q, w2, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                                     compress_lens, cand_blocks, n_cand, cand_block_size,
+                                     slot_scores, ld2, key_hist2, index_topk, offset, out2, ld_out2,
+                                     nullptr, stream);
+  }
+  if (!ws || ws_bytes < split_ws_bytes((int)R, T)) return IDX_EINVAL;
+  if (!set_two_level_lds_limit()) return IDX_EHIP;
+  const idx::SplitLayout L(T);
+  hipLaunchKernelGGL(idx::topk_split_a_kernel, dim3((unsigned)L.nparts, (unsigned)R),
+                     dim3(idx::kPartNW * 64), 0, st, scores, ld, T, compress_lens, key_hist, kout,
+                     (uint32_t*)ws);
+  idx_status e = idx_host::launch_status();
+  if (e != IDX_OK) return e;
+  e = idx_host::score_candidates_compact(q, w2, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                                         compress_lens, cand_blocks, n_cand, cand_block_size,
+                                         slot_scores, ld2, key_hist2, st);
+  if (e != IDX_OK) return e;
+  hipLaunchKernelGGL(idx::topk_split_b_cand_kernel, dim3((unsigned)(2 * R)), dim3(1024),
+                     split_b_lds(T), st, (int)R, scores, ld, T, compress_lens, key_hist, kout,
+                     offset, out1, ld_out1, (const uint32_t*)ws, slot_scores, ld2, cand_blocks,
+                     n_cand, cand_block_size, key_hist2, out2, ld_out2);
+  return idx_host::launch_status();
 }
 
 // ------------------------------------------------- allocation-free top-k

@@ -20,7 +20,7 @@ from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_qua
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
                idx_score_q4, idx_score_topk, idx_score_topk_q4,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
-               idx_topk, idx_topk_candidates,
+               idx_topk, idx_topk_candidates, idx_two_level_topk,
                idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
 from .inputs import YARN
 
@@ -155,6 +155,13 @@ class IndexerStep:
         # contiguous fp4 caches with bf16 queries
         self.l2_compact = (self.two_level and not paged and not fp8 and
                            not (q_step and not wl.ctb))
+        # ... and then runs after the level-one select as one call
+        # (idx_two_level_topk), whose two rankings may run side by side: level
+        # two counts into a histogram of its own
+        self.key_hist2 = None
+        if self.l2_compact:
+            self.key_hist2 = torch.empty((R, 2048), dtype=torch.int32, device="cuda")
+            idx_clear_key_hist(self.key_hist2)
 
         # every step's calls, marshalled once per key-cache copy
         self._plans = [self._plan(kc) for kc in self.caches]
@@ -257,17 +264,19 @@ class IndexerStep:
                 calls.append(idx_select_candidate_blocks(self.scores, wl.T, self.cl, wl.ctb,
                                                          wl.cbs, self.ids, workspace=self.sel_ws,
                                                          **b))
+            if self.l2_compact:
+                # the level-one top-k, and level two's slot scores (no -inf
+                # fill of the rows) and top-k, in one call
+                calls.append(idx_two_level_topk(self.scores, self.key_hist, self.out_l1,
+                                                self.topk_ws, q, self.w2, kc, wl.B, wl.S, wl.T,
+                                                self.cl, self.ids, wl.cbs, self.scores2,
+                                                self.key_hist2, wl.topk, wl.offset, self.out,
+                                                **b))
+                return calls, score_at
             calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out_l1,
                                   workspace=self.topk_ws, key_hist=self.key_hist, **b))
             # level two: only the candidate positions hold finite scores; the
             # histogram, reset by the level-one top-k, now counts them
-            if self.l2_compact:
-                # level two in one call: slot scores, no -inf fill of the rows
-                calls.append(idx_score_topk_candidates(q, self.w2, kc, wl.B, wl.S, wl.T, self.cl,
-                                                       self.ids, wl.cbs, self.scores2, wl.topk,
-                                                       wl.offset, self.out,
-                                                       key_hist=self.key_hist, **b))
-                return calls, score_at
             if self.paged:
                 calls.append(idx_score_paged(q, self.w2, kc, self.block_table, wl.B, wl.S, wl.T,
                                              self.cl, self.scores2, cand_blocks=self.ids,

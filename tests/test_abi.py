@@ -153,6 +153,28 @@ def test_fused_score_topk_rejects_bad_arguments(lib):
                               None, 0, None) == IDX_OK  # no rows
 
 
+def test_two_level_topk_checks_before_launch(lib):
+    """Both levels' checks, and one histogram passed for both levels, are
+    refused before anything launches."""
+    d = ctypes.c_void_p(0x1000)
+    h1, h2 = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+
+    def call(B=2, T=65536, ld=65536, ld_out1=2048, hist1=h1, hist2=h2, n_cand=64, cbs=128,
+             ld2=8192, k=2048, ld_out2=2048, H=64):
+        return lib.idx_two_level_topk(d, ld, hist1, d, ld_out1, d, 1 << 30, d, d, d, T, B, 1, H,
+                                      128, T, d, d, n_cand, cbs, d, ld2, hist2, k, 0, d, ld_out2,
+                                      None)
+    assert call(hist2=h1) == IDX_EINVAL        # one histogram for both levels
+    assert call(ld=65535) == IDX_EINVAL        # level one: ld < T
+    assert call(ld_out1=2047) == IDX_EINVAL    # level one: ld_out < k_out
+    assert call(ld2=8191) == IDX_EINVAL        # level two: slot row shorter than the slots
+    assert call(ld_out2=2047) == IDX_EINVAL    # level two: ld_out < k_out
+    assert call(T=70000, ld=70000) == IDX_EUNSUPPORTED  # level two's rows past 65536
+    assert call(n_cand=0) == IDX_EINVAL
+    assert call(k=0) == IDX_EINVAL
+    assert call(B=0) == IDX_OK                 # no rows
+
+
 def test_candidate_topk_rejects_bad_arguments(lib):
     d = ctypes.c_void_p(0x1000)
     assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, None, 2048, 0, d, 2048,

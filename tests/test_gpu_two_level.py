@@ -149,3 +149,76 @@ def test_score_topk_candidates_matches_two_calls(idx, case):
             if p < min(int(c["cl"][r]), T):
                 assert bits(s_f[r, v:v + 1])[0] == bits(ref[r, p:p + 1])[0], (r, v, p)
     assert np.all(np.isnan(s_f[:, V:]))  # nothing past the slots
+
+
+TL_CASES = [
+    # (seed, B, H, T, cbs, ids per row, k, cl override): level one split path
+    # and level two's 1024-thread ranking side by side, or the two in order
+    (151, 4, 64, 65536, 128, 64, 2048, None),                 # side by side: the workload's shape
+    (152, 3, 32, 50000, 128, 40, 2048, [50000, 40000, 1]),   # side by side, 32 heads, short rows
+    (153, 2, 64, 20000, 128, 24, 500, None),                  # level one on one workgroup: in order
+    (154, 2, 64, 65536, 64, 16, 2048, None),                  # level two on 256 threads: in order
+]
+
+
+@pytest.mark.parametrize("case", TL_CASES)
+def test_two_level_topk_equals_the_two_calls(idx, case):
+    """idx_two_level_topk against idx_topk then idx_score_topk_candidates on
+    the same level-one scores and histogram: both index sets bit for bit,
+    both histograms reset, and each equal to the oracle's top-k."""
+    t = torch()
+    seed, B, H, T, cbs, nid, k, cl = case
+    say("two-level top-k", case)
+    c = small_case(seed, B, 1, H, T)
+    if cl is not None:
+        c["cl"] = np.array(cl, np.int32)
+    rng = np.random.default_rng(seed)
+    w2 = rng.permutation(c["w"].reshape(-1)).reshape(c["w"].shape)  # level two's own weights
+    nb = (T + cbs - 1) // cbs
+    ids = np.stack([np.sort(rng.choice(nb, size=nid, replace=False)) for _ in range(B)]).astype(np.int32)
+    kc_ref, _ = oracle.fp4_quant_rows(c["k"])
+    ref1, _ = oracle.score(c["q"], c["w"], kc_ref, B, 1, H, T, c["cl"])
+    ref2, _ = oracle.score(c["q"], w2, kc_ref, B, 1, H, T, c["cl"], cand=ids, cbs=cbs)
+    kc = fp4_cache(c["k"])
+    q, w, wd2, cld, idd = dev(c["q"]), dev(c["w"]), dev(w2), dev(c["cl"]), dev(ids)
+    kout = min(k, T)
+    V = nid * cbs
+    res = []
+    for together in (True, False):
+        sc1 = t.empty((B, T), dtype=t.float32, device="cuda")
+        h1 = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        h2 = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        idx.idx_score(q, w, kc, B, 1, T, cld, sc1, key_hist=h1)
+        out1 = t.full((B, kout), -9, dtype=t.int32, device="cuda")
+        out2 = t.full((B, kout), -9, dtype=t.int32, device="cuda")
+        slot = t.full((B, V), float("nan"), dtype=t.float32, device="cuda")
+        if together:
+            idx.idx_two_level_topk(sc1, h1, out1, None, q, wd2, kc, B, 1, T, cld, idd, cbs, slot,
+                                   h2, k, 3, out2)
+        else:
+            idx.idx_topk(sc1, T, cld, k, 3, out1, key_hist=h1)
+            idx.idx_score_topk_candidates(q, wd2, kc, B, 1, T, cld, idd, cbs, slot, k, 3, out2,
+                                          key_hist=h2)
+        sync()
+        assert not host(h1).any() and not host(h2).any()  # both consumed and reset
+        res.append((host(out1), host(out2)))
+    (a1, a2), (b1, b2) = res
+    assert np.array_equal(a1, b1)
+    assert np.array_equal(a2, b2)
+    assert np.array_equal(a1, oracle.topk(ref1, c["cl"], k, 3))
+    assert np.array_equal(a2, oracle.topk(ref2, c["cl"], k, 3))
+
+
+def test_two_level_topk_rejects_one_shared_histogram(idx):
+    t = torch()
+    B, T = 2, 65536
+    c = small_case(160, B, 1, 64, T)
+    kc = fp4_cache(c["k"])
+    h = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+    sc1 = t.empty((B, T), dtype=t.float32, device="cuda")
+    out = t.empty((B, 2048), dtype=t.int32, device="cuda")
+    slot = t.empty((B, 8192), dtype=t.float32, device="cuda")
+    ids = dev(np.tile(np.arange(64, dtype=np.int32), (B, 1)))
+    with pytest.raises(idx.IdxError):
+        idx.idx_two_level_topk(sc1, h, out, None, dev(c["q"]), dev(c["w"]), kc, B, 1, T,
+                               dev(c["cl"]), ids, 128, slot, h, 2048, 0, out)
