@@ -194,7 +194,7 @@ def score_kernel_name(st) -> str:
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("score.hip", "idx_common.hpp", "row_topk.hpp", "publish_dev.hpp"):
+    for name in ("score.hip", "idx_common.hpp", "row_topk.hpp", "publish_dev.hpp", "split_topk.hpp"):
         with open(os.path.join(ROOT, "sparse_attention_top_fp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

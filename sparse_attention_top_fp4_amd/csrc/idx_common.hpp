@@ -226,12 +226,18 @@ idx_status select_blocks_from_max(const float* bmax, int64_t ld_b, int R, int nb
                                   const int32_t* compress_lens, int cbs, int ctb, int32_t* ids,
                                   int64_t ld_ids, hipStream_t st);
 // idx_score in candidate mode with slot v's score at slot_scores[r][v]
-// (ld >= n_cand * cand_block_size) and no -inf fill.  Defined in score.hip.
+// (ld >= n_cand * cand_block_size) and no -inf fill; with l1_scores, extra
+// workgroups of the launch also run kernel A of the split top-k of those
+// level-one scores [R][l1_ld] (histogram l1_hist, workspace l1_ws, k_out
+// l1_kout; T as the candidate rows').  Defined in score.hip.
 idx_status score_candidates_compact(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
                                     int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                                     const int32_t* compress_lens, const int32_t* cand_blocks,
                                     int n_cand, int cand_block_size, float* slot_scores,
-                                    int64_t ld, uint32_t* key_hist, hipStream_t stream);
+                                    int64_t ld, uint32_t* key_hist, hipStream_t stream,
+                                    const float* l1_scores = nullptr, int64_t l1_ld = 0,
+                                    const uint32_t* l1_hist = nullptr, uint32_t* l1_ws = nullptr,
+                                    int l1_kout = 0);
 inline idx_status launch_status() {
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_EHIP;
 }

@@ -27,6 +27,7 @@
 #include "idx_common.hpp"
 #include "publish_dev.hpp"
 #include "row_topk.hpp"
+#include "split_topk.hpp"
 
 #include <hip/hip_ext.h>
 #include <atomic>
@@ -365,6 +366,16 @@ struct Epi {
   int64_t bmax_ld;
   int bmax_cbs;
   int compact;
+  // candidate mode: the last l1_parts rows of the grid run kernel A of the
+  // level-one top-k instead (split_a_part on the level-one scores): the two
+  // are independent steps of a two-level step, and side by side they share
+  // one launch
+  int l1_parts;
+  const float* l1_scores;
+  int64_t l1_ld;
+  const uint32_t* l1_hist;
+  uint32_t* l1_ws;
+  int l1_kout;
 };
 
 // The role of the extra workgroup of row r (sequence b, decode: one row per
@@ -630,6 +641,15 @@ score_kernel(
   int limit = cl[r];
   limit = limit < 0 ? 0 : (limit > T ? T : limit);
 
+  if constexpr (CAND && !TOPK && !F8) {
+    // uniform: a workgroup of level one's kernel A (see Epi)
+    const int l1_first = (int)gridDim.y - ep.l1_parts;
+    if (ep.l1_parts && (int)blockIdx.y >= l1_first) {
+      split_a_part<256>(r, (int)blockIdx.y - l1_first, ep.l1_scores, ep.l1_ld, T, cl, ep.l1_hist,
+                        ep.l1_kout, ep.l1_ws, hist_lds, qs_own, qs_own + 8);
+      return;
+    }
+  }
   PosMap<CAND> pm;
   pm.cand = cand_s;
   pm.cbs = cbs;
@@ -1027,7 +1047,9 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                                                         (unsigned)R),
                          dim3(256), 0, st, scores, ld, T);
   }
-  dim3 grid((unsigned)R, (unsigned)nchunks);
+  if (ep.l1_parts && (!cand_blocks || !ep.compact || nchunks + ep.l1_parts > 65535))
+    return IDX_EINVAL;
+  dim3 grid((unsigned)R, (unsigned)(nchunks + ep.l1_parts));
   auto kern = H == 64 ? (cand_blocks ? idx::score_kernel<2, true, false>
                                      : idx::score_kernel<2, false, false>)
                       : (cand_blocks ? idx::score_kernel<1, true, false>
@@ -1098,15 +1120,26 @@ extern "C" idx_status idx_score(const uint16_t* q, const uint16_t* w, const uint
                     idx::PageMap{nullptr, 0, 0, 0}, stream);
 }
 
-// The candidate score with its slots written compactly (see Epi).
+// The candidate score with its slots written compactly (see Epi), and, when
+// l1_scores is given, level one's split kernel A in the same launch.
 idx_status idx_host::score_candidates_compact(const uint16_t* q, const uint16_t* w,
                                               const uint8_t* k_cache, int64_t k_batch_stride_rows,
                                               int B, int S, int H, int D, int T,
                                               const int32_t* compress_lens,
                                               const int32_t* cand_blocks, int n_cand,
                                               int cand_block_size, float* slot_scores, int64_t ld,
-                                              uint32_t* key_hist, hipStream_t stream) {
+                                              uint32_t* key_hist, hipStream_t stream,
+                                              const float* l1_scores, int64_t l1_ld,
+                                              const uint32_t* l1_hist, uint32_t* l1_ws,
+                                              int l1_kout) {
   if (!cand_blocks) return IDX_EINVAL;
+  if (l1_scores) {
+    const int parts = (int)idx::SplitLayout(T).nparts;
+    return score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                      cand_blocks, n_cand, cand_block_size, slot_scores, ld, key_hist,
+                      idx::PageMap{nullptr, 0, 0, 0}, stream, false,
+                      idx::Epi{nullptr, 0, 0, 1, parts, l1_scores, l1_ld, l1_hist, l1_ws, l1_kout});
+  }
   return score_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
                     cand_blocks, n_cand, cand_block_size, slot_scores, ld, key_hist,
                     idx::PageMap{nullptr, 0, 0, 0}, stream, false, idx::Epi{nullptr, 0, 0, 1});

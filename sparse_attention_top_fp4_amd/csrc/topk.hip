@@ -32,6 +32,7 @@
 // instead of an LDS atomic per element.
 #include "idx_common.hpp"
 #include "row_topk.hpp"
+#include "split_topk.hpp"
 
 #include <stdlib.h>
 
@@ -590,94 +591,16 @@ __device__ __noinline__ void stream_rank_row(const float* __restrict__ srow, int
 }
 
 // ---------------------------------------- split path (score histogram given)
-// Rows of 8193..262144 positions.  Kernel A: one workgroup of 512 threads per
-// 8192-position part of a row writes the part's "above the threshold bin"
-// bit mask and the (key, position) list of the elements inside the bin, one
-// list per wave.  Kernel B: one workgroup of 1024 threads per row resolves
-// the remaining digits on the collected list in LDS, marks the selected
-// list elements into the masks and compacts the row in position order.
-constexpr int kPartNW = 8, kPartEPT = 16, kPart = kPartNW * 64 * kPartEPT;  // 8192
-constexpr int kSplitMaxT = 262144;
-constexpr int kSplitCandCap = 8192;  // list elements resolved in LDS
-
-// LDS index of mask word w (one pad word per 32) and the padded length.
-__host__ __device__ __forceinline__ int split_pad(int w) { return w + (w >> 5); }
-__host__ __device__ __forceinline__ int split_padded_words(int nw) { return nw + (nw >> 5) + 1; }
-
-struct SplitLayout {  // per-row workspace, in 32-bit words
-  int64_t nwords;     // T/32 rounded up: above-mask words
-  int64_t nparts;
-  int64_t cand_off, cnt_off, state_off, row_words;
-  __host__ __device__ SplitLayout(int T) {
-    nwords = ((int64_t)T + 31) / 32;
-    nparts = ((int64_t)T + kPart - 1) / kPart;
-    cand_off = (nwords + 1) & ~(int64_t)1;               // [nparts][8 waves][1024] (key, pos)
-    cnt_off = cand_off + nparts * kPartNW * 1024 * 2;    // [nparts][8 waves]
-    state_off = cnt_off + nparts * kPartNW;              // b1, krem, histogram total
-    row_words = (state_off + 3 + 3) & ~(int64_t)3;       // rows 16-byte aligned, lists 8
-  }
-};
+// (kernel A's part and the workspace layout: split_topk.hpp)
 
 __global__ __launch_bounds__(kPartNW * 64) void topk_split_a_kernel(
     const float* __restrict__ scores, int64_t ld, int T, const int32_t* __restrict__ cl_arr,
     const uint32_t* __restrict__ key_hist, int kout, uint32_t* __restrict__ ws) {
-  constexpr int NT = kPartNW * 64, SEG = 64 * kPartEPT;
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t wtot[kPartNW];
   __shared__ uint32_t sh[4];
-  const int r = blockIdx.y, part = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const SplitLayout L(T);
-  uint32_t* wrow = ws + (int64_t)r * L.row_words;
-  int c = cl_arr[r];
-  c = c < 0 ? 0 : (c > T ? T : c);
-  const int base = part * kPart + w * SEG;
-  float v[kPartEPT];
-  load_vals<kPartEPT>(scores + (int64_t)r * ld, base, T, v);
-  uint32_t b1, krem, total;
-  {
-    constexpr int HPT = 2048 / NT;
-    uint32_t hv[HPT], mine = 0;
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) hv[j] = key_hist[(int64_t)r * 2048 + threadIdx.x + j * NT];
-#pragma unroll
-    for (int j = 0; j < HPT; ++j) {
-      hist[threadIdx.x + j * NT] = hv[j];
-      mine += hv[j];
-    }
-    total = block_sum<NT>(mine, wtot);  // its barriers also publish hist
-    uint32_t bc;
-    // positions the histogram does not count are -inf
-    select_bin_r<NT, 2048>(hist, (uint32_t)kout, kInfBin, (uint32_t)T - total, sh, wtot, b1, krem,
-                           bc);
-  }
-  if (part == 0 && threadIdx.x == 0) {
-    wrow[L.state_off] = b1;
-    wrow[L.state_off + 1] = krem;
-    wrow[L.state_off + 2] = total;  // kernel B checks it against compress_lens
-  }
-  const float lo = b1 <= kInfBin ? -__builtin_inff() : key_to_float(b1 << 21);
-  const bool top = b1 >= 2044u;
-  const float hi = top ? __builtin_inff() : key_to_float((b1 + 1u) << 21);
-  uint2* cand = reinterpret_cast<uint2*>(wrow + L.cand_off +
-                                         ((int64_t)part * kPartNW + w) * 1024 * 2);
-  uint32_t run = 0;
-  uint32_t myword = 0;  // lane 2e / 2e+1 collects the low / high half of step e's mask
-#pragma unroll
-  for (int e = 0; e < kPartEPT; ++e) {
-    const int t = base + e * 64 + lane;
-    const float x = t < T ? (t < c ? v[e] : -__builtin_inff()) : __builtin_nanf("");
-    const bool above = !top && x >= hi;
-    const bool isc = x >= lo && (top || x < hi);
-    const uint64_t am = __ballot(above);
-    const uint64_t cm = __ballot(isc);
-    myword = lane == 2 * e ? (uint32_t)am : (lane == 2 * e + 1 ? (uint32_t)(am >> 32) : myword);
-    if (isc) cand[run + lanes_below(cm)] = make_uint2(score_key(x), (uint32_t)t);
-    run += (uint32_t)__popcll(cm);
-  }
-  // the wave's 32 mask words in one store
-  const int64_t word = (base >> 5) + lane;
-  if (lane < 2 * kPartEPT && word < L.nwords) wrow[word] = myword;
-  if (lane == 0) wrow[L.cnt_off + (int64_t)part * kPartNW + w] = run;
+  split_a_part<kPartNW * 64>((int)blockIdx.y, (int)blockIdx.x, scores, ld, T, cl_arr, key_hist,
+                             kout, ws, hist, wtot, sh);
 }
 
 #ifndef IDX_SPLIT_B_THREADS
@@ -1539,9 +1462,9 @@ extern "C" idx_status idx_score_topk_candidates(
 // The rest of a two-level step after the level-one select: the level-one
 // top-k of `scores` and level two's candidate score and top-k.  On the
 // split path (32768 < T <= kTwoLevelMaxT, histograms given, level two on
-// the 1024-thread candidate kernel) it is three launches: kernel A of level
-// one, the candidate score, then kernel B and the candidate top-k side by
-// side; otherwise idx_topk then idx_score_topk_candidates.
+// the 1024-thread candidate kernel) it is two launches: the candidate score
+// with kernel A of level one beside it, then kernel B and the candidate
+// top-k side by side; otherwise idx_topk then idx_score_topk_candidates.
 namespace {
 bool set_two_level_lds_limit() {
   static std::atomic<uint64_t> done_mask{0};
@@ -1595,15 +1518,10 @@ extern "C" idx_status idx_two_level_topk(
   }
   if (!ws || ws_bytes < split_ws_bytes((int)R, T)) return IDX_EINVAL;
   if (!set_two_level_lds_limit()) return IDX_EHIP;
-  const idx::SplitLayout L(T);
-  hipLaunchKernelGGL(idx::topk_split_a_kernel, dim3((unsigned)L.nparts, (unsigned)R),
-                     dim3(idx::kPartNW * 64), 0, st, scores, ld, T, compress_lens, key_hist, kout,
-                     (uint32_t*)ws);
-  idx_status e = idx_host::launch_status();
-  if (e != IDX_OK) return e;
-  e = idx_host::score_candidates_compact(q, w2, k_cache, k_batch_stride_rows, B, S, H, D, T,
-                                         compress_lens, cand_blocks, n_cand, cand_block_size,
-                                         slot_scores, ld2, key_hist2, st);
+  // the candidate score, with level one's kernel A on extra workgroups
+  const idx_status e = idx_host::score_candidates_compact(
+      q, w2, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens, cand_blocks, n_cand,
+      cand_block_size, slot_scores, ld2, key_hist2, st, scores, ld, key_hist, (uint32_t*)ws, kout);
   if (e != IDX_OK) return e;
   hipLaunchKernelGGL(idx::topk_split_b_cand_kernel, dim3((unsigned)(2 * R)), dim3(1024),
                      split_b_lds(T), st, (int)R, scores, ld, T, compress_lens, key_hist, kout,
