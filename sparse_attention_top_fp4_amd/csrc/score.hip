@@ -905,7 +905,11 @@ done:
     }
     // the ranked layout only needs to cover [0, limit): 256 * EPT positions
     // with EPT sized to the row (the ranking's work is proportional to EPT)
-    if (limit <= 256 * 16)
+    if (limit <= 256 * 4)
+      fused_rank<4>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
+    else if (limit <= 256 * 8)
+      fused_rank<8>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
+    else if (limit <= 256 * 16)
       fused_rank<16>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);
     else if (limit <= 256 * 24)
       fused_rank<24>(sbuf, hist_lds, sh, wtot, limit, T, tk, orow);

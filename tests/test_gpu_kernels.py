@@ -352,10 +352,13 @@ FUSED_CASES = [
     (74, 2, 1, 32, 777, None, 100, True),       # ragged width, 32 heads
     (75, 1, 20, 64, 1500, 5800, 2048, True),    # index_topk >= T
     (76, 2, 9, 64, 5000, 15990, 7, False),      # tiny k
-    # rows ranked in layouts of 16, 24 and 32 positions per thread: cl
-    # straddles 4096 / 4097 and 6144 / 6145
+    # rows ranked in layouts of 4, 8, 16, 24 and 32 positions per thread: cl
+    # straddles 1024 / 1025, 2048 / 2049, 4096 / 4097 and 6144 / 6145
+    (81, 1, 12, 64, 3000, 4092, 500, True),     # cl 1023..1026
+    (82, 1, 12, 64, 3000, 8188, 300, False),    # cl 2047..2050
     (79, 1, 12, 64, 6144, 16380, 2048, True),   # cl 4095..4098
     (80, 1, 12, 64, 7000, 24572, 2048, False),  # cl 6143..6146
+    (83, 2, 1, 64, 512, None, 256, False),      # the tiny decode's shape
 ]
 
 
