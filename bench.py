@@ -148,7 +148,9 @@ def step_bytes(wl, q_step=False, prefill_publish_groups=0, rb=68) -> int:
     if wl.publish:
         b += publish_bytes(wl, 1, rb)
     if q_step:
-        b += wl.R * wl.H * (128 * 2 + 2)             # bf16 heads before RoPE, raw weights
+        # the step starts from the bf16 heads before RoPE and the raw weights;
+        # the quantised heads and scaled weights are intermediate
+        b += wl.R * wl.H * (128 * 2 + 2) - wl.R * wl.H * (rb + 2)
     if prefill_publish_groups:
         b += publish_bytes(wl, prefill_publish_groups, 68)
     return b

@@ -259,6 +259,32 @@ idx_status idx_score_topk_q4(const uint8_t *q_rows, const uint16_t *w, const uin
                              void *stream);
 
 /*
+ * idx_score_qrope, idx_score_topk_qrope -- the query step inside the score
+ * launch ([IDX, forward]: RoPE on the query heads' last rd dims at position
+ * start_pos + s, fp4_act_quant of the heads, weights_proj output times
+ * softmax_scale * n_heads^-0.5; [VLLM, fused_indexer_q_rope_quant]):
+ * idx_q_rope_quant followed by idx_score_q4 / idx_score_topk_q4 on its
+ * rows and weights, in one launch and with the same results bit for bit.
+ * q holds the heads before RoPE, w_raw the raw weights, w_scale the
+ * weights' factor, cos_sin, P, rd and start_pos as for idx_q_rope_quant
+ * (rd even, 0 <= rd <= 128; when rd > 0, cos_sin 8-byte aligned with every
+ * position start_pos + s, s < S, below P).  Every other argument and result
+ * as for idx_score (no candidate blocks) and idx_score_topk.  An invalid
+ * query-step argument gives IDX_EINVAL before any launch.
+ */
+idx_status idx_score_qrope(const uint16_t *q, const uint16_t *w_raw, float w_scale,
+                           const float *cos_sin, int P, int rd, int start_pos,
+                           const uint8_t *k_cache, int64_t k_batch_stride_rows, int B, int S,
+                           int H, int D, int T, const int32_t *compress_lens, float *scores,
+                           int64_t ld, uint32_t *key_hist, void *stream);
+idx_status idx_score_topk_qrope(const uint16_t *q, const uint16_t *w_raw, float w_scale,
+                                const float *cos_sin, int P, int rd, int start_pos,
+                                const uint8_t *k_cache, int64_t k_batch_stride_rows, int B, int S,
+                                int H, int D, int T, const int32_t *compress_lens, int index_topk,
+                                int32_t offset, int32_t *out, int64_t ld_out, float *scores,
+                                int64_t ld, void *stream);
+
+/*
  * FP8 key cache ([VLLM, _indexer_k_cache_head_dim]: the FP8 indexer cache
  * row is 128 fp8 bytes plus one fp32 scale per 128 values, 132 bytes;
  * [VLLM, DeepseekV4Indexer.__init__]: quant_block_size 128, scale_fmt

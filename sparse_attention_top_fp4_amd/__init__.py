@@ -17,7 +17,7 @@ import os
 __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_fp8",
            "idx_score", "idx_score_topk", "idx_score_paged",
            "idx_score_topk_paged", "idx_publish_keys_paged", "idx_q_rope_quant",
-           "idx_score_q4", "idx_score_topk_q4",
+           "idx_score_q4", "idx_score_topk_q4", "idx_score_qrope", "idx_score_topk_qrope",
            "idx_clear_key_hist", "idx_topk",
            "idx_topk_candidates",
            "idx_topk_workspace_size",
@@ -79,6 +79,10 @@ def load_library():
     L.idx_publish_keys_paged.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                          P, i64, i32, P, i64, i32, P]
     L.idx_q_rope_quant.argtypes = [P, P, f32, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P]
+    L.idx_score_qrope.argtypes = [P, P, f32, P, i32, i32, i32, P, i64, i32, i32, i32, i32, i32, P,
+                                  P, i64, P, P]
+    L.idx_score_topk_qrope.argtypes = [P, P, f32, P, i32, i32, i32, P, i64, i32, i32, i32, i32,
+                                       i32, P, i32, ctypes.c_int32, P, i64, P, i64, P]
     L.idx_score_q4.argtypes = L.idx_score.argtypes
     L.idx_score_topk_q4.argtypes = L.idx_score_topk.argtypes
     L.idx_yarn_cos_sin.argtypes = [i32, i32, f64, f64, i32, f64, f64, P]
@@ -105,7 +109,8 @@ def load_library():
                  "idx_q_rope_quant", "idx_score_q4", "idx_score_topk_q4",
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
-                 "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk"):
+                 "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk",
+                 "idx_score_qrope", "idx_score_topk_qrope"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -513,6 +518,70 @@ def idx_q_rope_quant(q, w_raw, w_scale, cos_sin, start_pos, S, q_rows, w_out,
                                            cos_sin.shape[0], R // S, S, H, D, rd, start_pos,
                                            _ptr(q_rows), _ptr(q_roundtrip), _ptr(w_out)), stream,
                   "idx_q_rope_quant", bind)
+
+
+def _qstep_args(q, w_raw, cos_sin, B, S):
+    torch = _torch()
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w_raw, "w_raw", _bf16_types(), 2)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    R, H, D = q.shape
+    if R != B * S or tuple(w_raw.shape) != (R, H):
+        raise ValueError("q/w_raw rows must be B*S")
+    return R, H, D
+
+
+def idx_score_qrope(q, w_raw, w_scale, cos_sin, start_pos, k_cache, B, S, T, compress_lens,
+                    scores, key_hist=None, rd=64, stream=None, bind=False):
+    """The query step (idx_q_rope_quant) inside the score launch: q [B*S, H,
+    128] bf16 before RoPE, w_raw [B*S, H] bf16, w_scale, cos_sin [P, rd/2, 2]
+    float32; rows r = b*S + s at position start_pos + s.  Other arguments
+    as idx_score (no candidate blocks)."""
+    torch = _torch()
+    R, H, D = _qstep_args(q, w_raw, cos_sin, B, S)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    if compress_lens.shape[0] != R or scores.shape[0] != R:
+        raise ValueError("compress_lens and scores must have B*S rows")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES:
+        raise ValueError("k_cache must be [>=B, Tcap, 68]")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [B*S, 2048]")
+    return _issue("idx_score_qrope", (_ptr(q), _ptr(w_raw), w_scale, _ptr(cos_sin),
+                                          cos_sin.shape[0], rd, start_pos, _ptr(k_cache),
+                                          k_cache.shape[1], B, S, H, D, T, _ptr(compress_lens),
+                                          _ptr(scores), scores.shape[1], _ptr(key_hist)), stream,
+                  "idx_score_qrope", bind)
+
+
+def idx_score_topk_qrope(q, w_raw, w_scale, cos_sin, start_pos, k_cache, B, S, T, compress_lens,
+                         index_topk, offset, out, scores=None, rd=64, stream=None, bind=False):
+    """idx_score_topk with the query step in its launch (arguments as
+    idx_score_qrope and idx_score_topk)."""
+    torch = _torch()
+    R, H, D = _qstep_args(q, w_raw, cos_sin, B, S)
+    _dev(k_cache, "k_cache", (torch.uint8,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    if compress_lens.shape[0] != R or out.shape[0] != R:
+        raise ValueError("compress_lens and out must have B*S rows")
+    if k_cache.shape[0] < B or k_cache.shape[2] != ROW_BYTES:
+        raise ValueError("k_cache must be [>=B, Tcap, 68]")
+    ld = 0
+    if scores is not None:
+        _dev(scores, "scores", (torch.float32,), 2)
+        if scores.shape[0] != R:
+            raise ValueError("scores must be [B*S, ld]")
+        ld = scores.shape[1]
+    return _issue("idx_score_topk_qrope", (_ptr(q), _ptr(w_raw), w_scale, _ptr(cos_sin),
+                                               cos_sin.shape[0], rd, start_pos, _ptr(k_cache),
+                                               k_cache.shape[1], B, S, H, D, T,
+                                               _ptr(compress_lens), index_topk, offset, _ptr(out),
+                                               out.shape[1], _ptr(scores), ld), stream,
+                  "idx_score_topk_qrope", bind)
 
 
 def idx_clear_key_hist(key_hist, stream=None, bind=False):

@@ -354,6 +354,21 @@ struct PubFuse {
   int on;                  // 0: no publish in this launch
 };
 
+// The query step inside the score launch ([IDX, forward]: RoPE on the query
+// heads' last rd dims at position start_pos + s, then fp4_act_quant; the
+// head weights times w_scale), value for value as idx_q_rope_quant computes
+// it: the thread that quantises block g of head h first rotates the block's
+// RoPE pairs (adjacent dims, so a pair never leaves the block), each
+// product and sum rounded in fp32 and the pair to bf16; each weight is
+// bf16(fp32(w) * w_scale).
+struct QStep {
+  const float* cos_sin;  // [P][rd/2] (cos, sin) pairs
+  int rd;
+  int start_pos;
+  float w_scale;
+  int on;  // 0: the query heads are used as given
+};
+
 // Extra outputs of the plain and candidate launches.  Plain mode: the
 // maximum of each cbs-wide block of the chunk's scores (the block score of
 // the candidate select), written when bmax is set; chunk starts are then
@@ -616,7 +631,7 @@ score_kernel(
     const uint16_t* __restrict__ w, const uint8_t* __restrict__ kc, int64_t kstride, int S, int T,
     const int32_t* __restrict__ cl, const int32_t* __restrict__ cand, int n_cand, int cbs,
     float* __restrict__ scores, int64_t ld, uint32_t* __restrict__ key_hist, int keys_per_wg,
-    FusedTopk tk, PageMap pg, PubFuse pf, Epi ep) {
+    FusedTopk tk, PageMap pg, PubFuse pf, Epi ep, QStep qst) {
   static_assert(!(F8 && TOPK), "the fp8 rows have no fused ranking");
   constexpr int H = 32 * HT;
   constexpr int kSets = TOPK ? 2 : kTileSets;  // key tile sets in registers
@@ -708,12 +723,29 @@ score_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) qv[i] = src[i];
   }
+  // the query step's (cos, sin) of this thread's RoPE pairs: pair i of the
+  // block is dims 32 g + 2 i and + 1, rotated when 32 g + 2 i >= D - rd
+  float2 csv[16];
+  const int rope_base = kHeadDim - qst.rd;
+  const bool rope_blk = !F8 && !q4 && qst.on && tid < 4 * H && 32 * (tid & 3) + 32 > rope_base;
+  if (rope_blk) {
+    const float2* cs = reinterpret_cast<const float2*>(
+        qst.cos_sin + (int64_t)(qst.start_pos + r % S) * qst.rd);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int d = 32 * (tid & 3) + 2 * i;
+      csv[i] = cs[d >= rope_base ? (d - rope_base) >> 1 : 0];
+    }
+  }
   // weights of the heads this lane's half-wave sums: wv[j] = w[r][H/2*half + j]
   float wv[16 * HT];
   {
     const uint16_t* wrow = w + (int64_t)r * H + (lane >> 5) * (H / 2);
 #pragma unroll
     for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(wrow[j]);
+    if (qst.on)  // uniform
+#pragma unroll
+      for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(f32_to_bf16(wv[j] * qst.w_scale));
   }
 
   // kSets register sets of key tiles: while one tile computes, the next
@@ -784,6 +816,17 @@ score_kernel(
       xp[4 * i + 1] = v.y;
       xp[4 * i + 2] = v.z;
       xp[4 * i + 3] = v.w;
+    }
+    if (rope_blk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (32 * g + 2 * i >= rope_base) {
+          const float x0 = bf16f(xp[i] & 0xffffu), x1 = bf16f(xp[i] >> 16);
+          const float c = csv[i].x, sn = csv[i].y;
+          const float a = x0 * c, bb = x1 * sn, cc = x0 * sn, dd = x1 * c;
+          xp[i] = f32_to_bf16(a - bb) | (f32_to_bf16(cc + dd) << 16);
+        }
+      }
     }
     uint32_t codes[4];
     const int e = quant_block32(xp, codes);
@@ -1010,7 +1053,8 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
                       const int32_t* compress_lens, const int32_t* cand_blocks, int n_cand,
                       int cand_block_size, float* scores, int64_t ld, uint32_t* key_hist,
                       idx::PageMap pg, void* stream, bool f8 = false,
-                      idx::Epi ep = idx::Epi{nullptr, 0, 0, 0}) {
+                      idx::Epi ep = idx::Epi{nullptr, 0, 0, 0},
+                      idx::QStep qst = idx::QStep{nullptr, 0, 0, 1.0f, 0}) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -1066,7 +1110,7 @@ idx_status score_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
   return launch_score(kern, grid, lds, st, q, q4, w, k_cache,
                       k_batch_stride_rows, S, T, compress_lens, cand_blocks, n_cand,
                       cand_block_size, scores, ld, key_hist, kpw, idx::FusedTopk{0, 0, nullptr, 0},
-                      pg, idx::PubFuse{}, ep);
+                      pg, idx::PubFuse{}, ep, qst);
 }
 
 idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t* w,
@@ -1074,7 +1118,8 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
                            int64_t k_batch_stride_rows, int B, int S, int H, int D, int T,
                            const int32_t* compress_lens, int index_topk, int32_t offset,
                            int32_t* out, int64_t ld_out, float* scores, int64_t ld,
-                           idx::PageMap pg, void* stream) {
+                           idx::PageMap pg, void* stream,
+                           idx::QStep qst = idx::QStep{nullptr, 0, 0, 1.0f, 0}) {
   if (B < 0 || S < 0 || T < 0 || H <= 0 || D <= 0 || index_topk <= 0) return IDX_EINVAL;
   if (D != idx::kHeadDim) return IDX_EUNSUPPORTED;
   if (H != 32 && H != 64) return IDX_EUNSUPPORTED;
@@ -1099,7 +1144,7 @@ idx_status score_topk_impl(const uint16_t* q, const uint8_t* q4, const uint16_t*
   return launch_score(kern, dim3((unsigned)R, 1u), lds, st, q, q4, w, k_cache, k_batch_stride_rows, S,
                       T, compress_lens, (const int32_t*)nullptr, 0, 0, scores, ld,
                       (uint32_t*)nullptr, kpw, idx::FusedTopk{kout, offset, out, ld_out}, pg,
-                      idx::PubFuse{}, idx::Epi{nullptr, 0, 0, 0});
+                      idx::PubFuse{}, idx::Epi{nullptr, 0, 0, 0}, qst);
 }
 
 // Page map arguments shared by the paged entry points.
@@ -1243,7 +1288,7 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
                       (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
                       idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
                       idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1},
-                      idx::Epi{nullptr, 0, 0, 0});
+                      idx::Epi{nullptr, 0, 0, 0}, idx::QStep{nullptr, 0, 0, 1.0f, 0});
 }
 
 extern "C" idx_status idx_score_fp8(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
@@ -1265,6 +1310,50 @@ extern "C" idx_status idx_score_topk(const uint16_t* q, const uint16_t* w, const
   return score_topk_impl(q, nullptr, w, k_cache, k_batch_stride_rows, B, S, H, D, T,
                          compress_lens, index_topk, offset, out, ld_out, scores, ld,
                          idx::PageMap{nullptr, 0, 0, 0}, stream);
+}
+
+namespace {
+// The query step's arguments (as idx_q_rope_quant checks them).
+idx_status qstep_args(const float* cos_sin, int P, int rd, int start_pos, int S, int D,
+                      float w_scale, idx::QStep& qs) {
+  if (P < 0 || start_pos < 0 || rd < 0 || rd > D || (rd & 1)) return IDX_EINVAL;
+  if (rd > 0 && (!cos_sin || !idx_host::aligned(cos_sin, 8) ||
+                 (int64_t)start_pos + S - 1 >= P))  // every position in the table
+    return IDX_EINVAL;
+  qs = idx::QStep{cos_sin, rd, start_pos, w_scale, 1};
+  return IDX_OK;
+}
+}  // namespace
+
+extern "C" idx_status idx_score_qrope(const uint16_t* q, const uint16_t* w_raw, float w_scale,
+                                      const float* cos_sin, int P, int rd, int start_pos,
+                                      const uint8_t* k_cache, int64_t k_batch_stride_rows, int B,
+                                      int S, int H, int D, int T, const int32_t* compress_lens,
+                                      float* scores, int64_t ld, uint32_t* key_hist,
+                                      void* stream) {
+  if (D != idx::kHeadDim && D > 0) return IDX_EUNSUPPORTED;
+  idx::QStep qs;
+  const idx_status e = qstep_args(cos_sin, P, rd, start_pos, S < 0 ? 0 : S, D, w_scale, qs);
+  if (e != IDX_OK) return e;
+  return score_impl(q, nullptr, w_raw, k_cache, k_batch_stride_rows, B, S, H, D, T, compress_lens,
+                    nullptr, 0, 0, scores, ld, key_hist, idx::PageMap{nullptr, 0, 0, 0}, stream,
+                    false, idx::Epi{nullptr, 0, 0, 0}, qs);
+}
+
+extern "C" idx_status idx_score_topk_qrope(const uint16_t* q, const uint16_t* w_raw,
+                                           float w_scale, const float* cos_sin, int P, int rd,
+                                           int start_pos, const uint8_t* k_cache,
+                                           int64_t k_batch_stride_rows, int B, int S, int H, int D,
+                                           int T, const int32_t* compress_lens, int index_topk,
+                                           int32_t offset, int32_t* out, int64_t ld_out,
+                                           float* scores, int64_t ld, void* stream) {
+  if (D != idx::kHeadDim && D > 0) return IDX_EUNSUPPORTED;
+  idx::QStep qs;
+  const idx_status e = qstep_args(cos_sin, P, rd, start_pos, S < 0 ? 0 : S, D, w_scale, qs);
+  if (e != IDX_OK) return e;
+  return score_topk_impl(q, nullptr, w_raw, k_cache, k_batch_stride_rows, B, S, H, D, T,
+                         compress_lens, index_topk, offset, out, ld_out, scores, ld,
+                         idx::PageMap{nullptr, 0, 0, 0}, stream, qs);
 }
 
 extern "C" idx_status idx_score_paged(const uint16_t* q, const uint16_t* w, const uint8_t* k_pages,

@@ -18,7 +18,8 @@ from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_qua
                idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
                idx_publish_score, idx_score_select_blocks, idx_score_topk_candidates,
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
-               idx_score_q4, idx_score_topk, idx_score_topk_q4,
+               idx_score_q4, idx_score_topk, idx_score_topk_q4, idx_score_qrope,
+               idx_score_topk_qrope,
                idx_score_topk_paged, idx_select_candidate_blocks, idx_select_workspace_size,
                idx_topk, idx_topk_candidates, idx_two_level_topk,
                idx_timing_arm, idx_topk_workspace_size, idx_yarn_cos_sin)
@@ -120,6 +121,10 @@ class IndexerStep:
         # workload's q taken as such) and runs the query step first; the
         # workload's weights are already scaled, so the weight scale is 1
         self.q_step = q_step
+        # the query step runs inside the score launch on one-level
+        # contiguous fp4 steps (idx_score_qrope, idx_score_topk_qrope); the
+        # others run it as its own launch into these buffers
+        self.qrope = q_step and not paged and not self.two_level and not fp8
         if q_step:
             H = wl.H
             self.q_rows = torch.empty((R, H, 68), dtype=torch.uint8, device="cuda")
@@ -210,6 +215,21 @@ class IndexerStep:
                                  wl.ratio, wl.eps, kc, rd=wl.rd, **b))
         q, w = self.q, self.w
         q4 = None  # the quantised heads, when the score takes them directly
+        if self.qrope:
+            qs = dict(w_scale=1.0, cos_sin=self.cos_sin_q, start_pos=wl.start_pos, rd=wl.rd)
+            score_at = len(calls)
+            if self.fused:
+                calls.append(idx_score_topk_qrope(q, w, qs["w_scale"], qs["cos_sin"],
+                                                  qs["start_pos"], kc, wl.B, wl.S, wl.T, self.cl,
+                                                  wl.topk, wl.offset, self.out,
+                                                  scores=self.scores, rd=qs["rd"], **b))
+                return calls, score_at
+            calls.append(idx_score_qrope(q, w, qs["w_scale"], qs["cos_sin"], qs["start_pos"], kc,
+                                         wl.B, wl.S, wl.T, self.cl, self.scores,
+                                         key_hist=self.key_hist, rd=qs["rd"], **b))
+            calls.append(idx_topk(self.scores, wl.T, self.cl, wl.topk, wl.offset, self.out,
+                                  workspace=self.topk_ws, key_hist=self.key_hist, **b))
+            return calls, score_at
         if self.q_step:
             # the score takes the rows directly; the paged and level-two
             # scores take the bf16 round trip

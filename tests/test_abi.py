@@ -175,6 +175,30 @@ def test_two_level_topk_checks_before_launch(lib):
     assert call(B=0) == IDX_OK                 # no rows
 
 
+def test_score_with_query_step_checks_its_arguments(lib):
+    """The query step's arguments of idx_score_qrope / idx_score_topk_qrope
+    are refused before any launch, as idx_q_rope_quant refuses them."""
+    d = ctypes.c_void_p(0x1000)
+    f = ctypes.c_float(1.0)
+
+    def score(rd=64, sp=10, P=20, S=4, cs=d):
+        return lib.idx_score_qrope(d, d, f, cs, P, rd, sp, d, 64, 1, S, 64, 128, 64, d, d, 64,
+                                   None, None)
+
+    def topk(rd=64, sp=10, P=20, S=4, cs=d):
+        return lib.idx_score_topk_qrope(d, d, f, cs, P, rd, sp, d, 64, 1, S, 64, 128, 64, d, 32, 0,
+                                        d, 32, None, 0, None)
+    for call in (score, topk):
+        assert call(rd=63) == IDX_EINVAL          # odd rd
+        assert call(rd=130) == IDX_EINVAL         # rd past the head
+        assert call(sp=17, P=20) == IDX_EINVAL    # position 20 not in the table
+        assert call(sp=-1) == IDX_EINVAL
+        assert call(cs=None) == IDX_EINVAL        # no table with rd > 0
+        assert call(cs=ctypes.c_void_p(0x1004)) == IDX_EINVAL  # table not 8-byte aligned
+    assert lib.idx_score_qrope(d, d, f, None, 0, 0, 0, d, 64, 0, 1, 64, 128, 64, d, d, 64, None,
+                               None) == IDX_OK   # rd 0, no rows
+
+
 def test_candidate_topk_rejects_bad_arguments(lib):
     d = ctypes.c_void_p(0x1000)
     assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, None, 2048, 0, d, 2048,

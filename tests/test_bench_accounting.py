@@ -87,3 +87,11 @@ def test_more_than_one_gpu_is_refused():
     assert p.returncode == 2 and "one GPU" in p.stderr
     p = _run_bench([], env={"WORLD_SIZE": "4"})
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_query_step_bytes_replace_the_quantised_heads():
+    """With the query step, the step starts from bf16 heads (256 B a head)
+    and raw weights (2 B) instead of quantised heads (68 B) and weights."""
+    from sparse_attention_top_fp4_amd.inputs import workload
+    wl = workload(1)
+    assert bench.step_bytes(wl, q_step=True) - bench.step_bytes(wl) == wl.R * wl.H * (256 + 2 - 70)

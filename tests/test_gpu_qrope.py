@@ -130,3 +130,71 @@ def test_score_takes_the_quantised_rows(idx, fused, H):
         n = int(cl[r])
         assert np.array_equal(bits(g[r, :n]), bits(ref[r, :n])), r
         assert np.array_equal(bits(g[r, :n]), bits(g2[r, :n])), r
+
+
+QS_CASES = [
+    # (fused, B, S, H, T, start_pos, rd, w_scale, k)
+    (False, 2, 6, 64, 3000, 10000, 64, 1.0, 0),          # decode-like rows, several chunks
+    (False, 64, 1, 64, 32768, 131071, 64, 1.0, 0),       # the batched decode's rows (sampled)
+    (True, 2, 6, 64, 3000, 10000, 64, 1.0, 700),         # fused top-k
+    (True, 1, 9, 32, 5000, 15990, 40, 0.0625, 300),      # 32 heads, rd 40, scaled weights
+    (False, 3, 2, 64, 700, 5, 0, 0.5, 0),                # rd 0: no rotation, weights scaled
+]
+
+
+@pytest.mark.parametrize("case", QS_CASES)
+def test_score_with_query_step_equals_the_two_calls(idx, case):
+    """idx_score_qrope / idx_score_topk_qrope: the query step inside the
+    score launch gives bit for bit the scores, histogram and indices of
+    idx_q_rope_quant then idx_score_q4 / idx_score_topk_q4, and the
+    oracle's (checked on up to eight rows)."""
+    t = torch()
+    fused, B, S, H, T, sp, rd, wsc, k = case
+    say("score with the query step", case)
+    rng = np.random.default_rng(300 + B * S + H)
+    R = B * S
+    q = normal_bf16(rng, (R, H, 128))
+    w = normal_bf16(rng, (R, H))
+    kk = normal_bf16(rng, (B, T, 128))
+    P = sp + S
+    cs = (oracle.yarn_cos_sin(P, rd, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                              YARN["beta_fast"], YARN["beta_slow"]) if rd
+          else np.zeros((P, 1, 2), np.float32))
+    cl = np.minimum(np.array([(sp + s + 1) // 4 for _ in range(B) for s in range(S)], np.int32), T)
+    kc = fp4_cache(kk)
+    qd, wd, csd, cld = dev(q), dev(w), dev(cs), dev(cl)
+    rows = t.empty((R, H, 68), dtype=t.uint8, device="cuda")
+    w_out = t.empty((R, H), dtype=t.int16, device="cuda")
+    idx.idx_q_rope_quant(qd, wd, wsc, csd, sp, S, rows, w_out, rd=rd)
+    sc1 = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+    sc2 = t.full((R, T), float("nan"), dtype=t.float32, device="cuda")
+    if fused:
+        o1 = t.full((R, k), -7, dtype=t.int32, device="cuda")
+        o2 = t.full((R, k), -7, dtype=t.int32, device="cuda")
+        idx.idx_score_topk_qrope(qd, wd, wsc, csd, sp, kc, B, S, T, cld, k, 2, o1, scores=sc1,
+                                 rd=rd)
+        idx.idx_score_topk_q4(rows, w_out, kc, B, S, T, cld, k, 2, o2, scores=sc2)
+        sync()
+        assert np.array_equal(host(o1), host(o2))
+    else:
+        h1 = t.zeros((R, 2048), dtype=t.int32, device="cuda")
+        h2 = t.zeros((R, 2048), dtype=t.int32, device="cuda")
+        idx.idx_score_qrope(qd, wd, wsc, csd, sp, kc, B, S, T, cld, sc1, key_hist=h1, rd=rd)
+        idx.idx_score_q4(rows, w_out, kc, B, S, T, cld, sc2, key_hist=h2)
+        sync()
+        assert np.array_equal(host(h1), host(h2))
+    g1, g2 = host(sc1), host(sc2)
+    assert np.array_equal(bits(np.nan_to_num(g1, nan=7.0)), bits(np.nan_to_num(g2, nan=7.0)))
+    # the oracle on a sample of rows
+    rs = np.unique(np.linspace(0, R - 1, min(R, 8)).astype(int))
+    bsel = sorted({int(r) // S for r in rs})
+    _, rt_ref, _, w_ref = oracle.q_rope_quant(q, w, np.float32(wsc), cs, sp, S, rd=rd)
+    kc_ref, _ = oracle.fp4_quant_rows(kk[bsel])
+    for r in rs:
+        b, s = divmod(int(r), S)
+        ref, _ = oracle.score(rt_ref[r:r + 1], w_ref[r:r + 1], kc_ref[bsel.index(b):bsel.index(b) + 1],
+                              1, 1, H, T, cl[r:r + 1])
+        n = int(cl[r])
+        assert np.array_equal(bits(g1[r, :n]), bits(ref[0, :n])), r
+        if fused:
+            assert np.array_equal(host(o1)[r], oracle.topk(ref, cl[r:r + 1], k, 2)[0]), r
