@@ -36,6 +36,19 @@ idx_status idx_probe_stream_read(const void *buf, int64_t bytes, int grid, uint3
 idx_status idx_probe_mfma_fp4(int grid, int iters, float *sink, double *flops, float *ms,
                               void *stream);
 
+/*
+ * idx_probe_bf16_convert -- the gfx950 conversion instruction that rounds
+ * two fp32 values to bf16 (used by the query step inside the score launch)
+ * against the software round-to-nearest-even of the other kernels, over
+ * every finite fp32 bit pattern; waits for the result.
+ *   count       device, one 8-byte aligned word (cleared, then counted into)
+ *   mismatches  host, the number of finite inputs on which they differ
+ * IDX_EINVAL for a null or misaligned pointer, IDX_EHIP when a HIP call
+ * fails.
+ */
+idx_status idx_probe_bf16_convert(unsigned long long *count, unsigned long long *mismatches,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

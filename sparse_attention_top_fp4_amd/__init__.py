@@ -99,6 +99,8 @@ def load_library():
                                     i32, i32, i32, P, P, i64, P, P]
     L.idx_probe_stream_read.argtypes = [P, i64, i32, P, ctypes.POINTER(f32), P]
     L.idx_probe_mfma_fp4.argtypes = [i32, i32, P, ctypes.POINTER(f64), ctypes.POINTER(f32), P]
+    L.idx_probe_bf16_convert.argtypes = [P, ctypes.POINTER(ctypes.c_ulonglong), P]
+    L.idx_probe_bf16_convert.restype = i32
     L.idx_timing_arm.argtypes = [i32]
     L.idx_timing_read.argtypes = [i32, ctypes.POINTER(f32)]
     for name in ("idx_fp4_quant", "idx_score", "idx_score_topk", "idx_clear_key_hist", "idx_topk",
@@ -894,3 +896,14 @@ def idx_probe_mfma_fp4(grid, iters, sink, stream=None):
                                              ctypes.byref(ms), _stream(stream)),
            "idx_probe_mfma_fp4")
     return float(fl.value), float(ms.value)
+
+
+def idx_probe_bf16_convert(stream=None) -> int:
+    """The number of finite fp32 inputs on which the bf16 conversion
+    instruction differs from the software round-to-nearest-even (0 expected)."""
+    torch = _torch()
+    count = torch.zeros(1, dtype=torch.int64, device="cuda")
+    n = ctypes.c_ulonglong(0)
+    _check(load_library().idx_probe_bf16_convert(_ptr(count), ctypes.byref(n), _stream(stream)),
+           "idx_probe_bf16_convert")
+    return int(n.value)

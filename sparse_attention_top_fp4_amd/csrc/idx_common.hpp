@@ -28,6 +28,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two finite fp32 values to a pair of bf16 (a in the low half), nearest-even,
+// in one conversion instruction of gfx950: equal to f32_to_bf16 on both for
+// every finite input (idx_probe_bf16_convert checks all of them).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
 // ------------------------------------------------------------- quantiser
 // [CMP, fp4_quant_e8m0_inplace]: the scale is the power-of-two ceiling of
 // amax/6 with amax raised to at least 6*2^-126.  Writing the (normal) amax as

@@ -120,3 +120,34 @@ extern "C" idx_status idx_probe_mfma_fp4(int grid, int iters, float* sink, doubl
                         (hipStream_t)stream, g_probe_ev[0], g_probe_ev[1], 0u, iters, sink);
   return probe_wait(ms);
 }
+
+// The bf16 conversion instruction against the software round-to-nearest-even
+// over every finite fp32 bit pattern (pairs 2i, 2i + 1 per conversion).
+__global__ __launch_bounds__(256) void bf16_convert_probe_kernel(unsigned long long* bad) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long mine = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 31); i += stride) {
+    const uint32_t u0 = (uint32_t)(2 * i), u1 = u0 + 1u;
+    const float a = __uint_as_float(u0), b = __uint_as_float(u1);
+    const uint32_t hw = idx::f32x2_to_bf16x2(a, b);
+    const bool fa = (u0 & 0x7f800000u) != 0x7f800000u, fb = (u1 & 0x7f800000u) != 0x7f800000u;
+    mine += (fa && (hw & 0xffffu) != idx::f32_to_bf16(a)) ? 1u : 0u;
+    mine += (fb && (hw >> 16) != idx::f32_to_bf16(b)) ? 1u : 0u;
+  }
+  if (mine) atomicAdd(bad, mine);
+}
+
+extern "C" idx_status idx_probe_bf16_convert(unsigned long long* count,
+                                              unsigned long long* mismatches, void* stream) {
+  if (!count || !mismatches || !idx_host::aligned(count, 8)) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemsetAsync(count, 0, sizeof(unsigned long long), st) != hipSuccess) return IDX_EHIP;
+  hipLaunchKernelGGL(bf16_convert_probe_kernel, dim3(16384), dim3(256), 0, st, count);
+  const idx_status s = idx_host::launch_status();
+  if (s != IDX_OK) return s;
+  if (hipMemcpyAsync(mismatches, count, sizeof(unsigned long long), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return IDX_EHIP;
+  return IDX_OK;
+}

@@ -745,7 +745,11 @@ score_kernel(
     for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(wrow[j]);
     if (qst.on)  // uniform
 #pragma unroll
-      for (int j = 0; j < 16 * HT; ++j) wv[j] = bf16f(f32_to_bf16(wv[j] * qst.w_scale));
+      for (int j = 0; j < 16 * HT; j += 2) {
+        const uint32_t p = f32x2_to_bf16x2(wv[j] * qst.w_scale, wv[j + 1] * qst.w_scale);
+        wv[j] = bf16f(p & 0xffffu);
+        wv[j + 1] = bf16f(p >> 16);
+      }
   }
 
   // kSets register sets of key tiles: while one tile computes, the next
@@ -824,7 +828,7 @@ score_kernel(
           const float x0 = bf16f(xp[i] & 0xffffu), x1 = bf16f(xp[i] >> 16);
           const float c = csv[i].x, sn = csv[i].y;
           const float a = x0 * c, bb = x1 * sn, cc = x0 * sn, dd = x1 * c;
-          xp[i] = f32_to_bf16(a - bb) | (f32_to_bf16(cc + dd) << 16);
+          xp[i] = f32x2_to_bf16x2(a - bb, cc + dd);
         }
       }
     }

@@ -199,6 +199,13 @@ def test_score_with_query_step_checks_its_arguments(lib):
                                None) == IDX_OK   # rd 0, no rows
 
 
+def test_bf16_probe_rejects_null_pointers(lib):
+    n = ctypes.c_ulonglong(0)
+    assert lib.idx_probe_bf16_convert(None, ctypes.byref(n), None) == IDX_EINVAL
+    assert lib.idx_probe_bf16_convert(ctypes.c_void_p(0x1000), None, None) == IDX_EINVAL
+    assert lib.idx_probe_bf16_convert(ctypes.c_void_p(0x1004), ctypes.byref(n), None) == IDX_EINVAL
+
+
 def test_candidate_topk_rejects_bad_arguments(lib):
     d = ctypes.c_void_p(0x1000)
     assert lib.idx_topk_candidates(d, 70000, 1, 70000, d, d, 64, 128, None, 2048, 0, d, 2048,

@@ -198,3 +198,12 @@ def test_score_with_query_step_equals_the_two_calls(idx, case):
         assert np.array_equal(bits(g1[r, :n]), bits(ref[0, :n])), r
         if fused:
             assert np.array_equal(host(o1)[r], oracle.topk(ref, cl[r:r + 1], k, 2)[0]), r
+
+
+def test_bf16_conversion_instruction_matches_rne(idx):
+    """The score launch's query step rounds with the gfx950 instruction that
+    converts two fp32 values to bf16; the other kernels (and the query
+    step's own launch) round in software.  They agree on every finite fp32
+    input."""
+    say("bf16 conversion instruction, exhaustive")
+    assert idx.idx_probe_bf16_convert() == 0
