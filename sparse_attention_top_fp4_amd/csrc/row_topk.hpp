@@ -1,19 +1,23 @@
-// row_topk.hpp -- one workgroup ranks one row whose order keys sit in
+// row_topk.hpp -- one workgroup ranks one row whose scores sit in
 // registers: the threshold search of the Indexer's top-k and the
 // position-ordered output ([IDX, forward]: keep min(index_topk, T) positions
 // by score, re-sort them by position, t + offset where t < compress_lens and
 // -1 otherwise; ties go to the lower position).
 //
-// Layout: wave w owns the positions [w*64*EPT, (w+1)*64*EPT); in step i its
-// lane l holds the four consecutive positions w*64*EPT + i*256 + 4l + [0, 4),
-// key[4i + j] for position +j.  Loads of that layout are contiguous per wave.
+// Layout: element e of lane l of wave w is position w*64*EPT + 64e + l
+// (row_base), so every load instruction reads 64 consecutive words and the
+// ballot of element e is the bit map of 64 consecutive positions.
 //
 // Search: radix select on the order keys in digits of 11, 11 and 10 bits.
-// Each pass histograms in LDS the next digit of the keys whose higher digits
-// equal the threshold prefix found so far (the first digit may come from the
-// score kernel instead), and the search stops as soon as every element of
-// the prefix bin is taken.  Output: per step, a wave scan of the selected
-// counts gives every selected position its slot in position order.
+// The first digit's histogram comes from the score kernel or is counted
+// here; each later pass histograms in LDS the next digit of the scores whose
+// higher digits equal the threshold prefix found so far, and the search stops
+// as soon as every element of the prefix bin is taken.
+//
+// Output: the waves' ballots of the taken scores (and of the tied ones, when
+// only some are taken) are written to LDS as position-ordered bit-map words;
+// one thread per 32-position word then takes its first slot from a block scan
+// of the word counts and writes its positions in order.
 #pragma once
 
 #include "idx_common.hpp"
@@ -236,24 +240,21 @@ __device__ __forceinline__ float key_above(uint32_t cut) {
 }
 
 // Scores of the positions: position >= T -> NaN (absent), position >= c ->
-// -inf.  A wave whose positions all lie below c (c <= T) keeps them as they
-// are.  Otherwise validity is integer arithmetic (sign bit of t - c) kept
-// out of the compiler's reach: compare masks hoisted above the loads would
-// hold two scalar registers per element.
+// -inf (c <= T).  A wave whose positions all lie below c keeps them as they
+// are.  Otherwise element e (position wbase + 64e) is tested as 64e < c - wbase
+// and 64e < T - wbase: two compares against constants and two selects.  The
+// bounds take an empty asm that reads the last element, so the compares
+// cannot be hoisted above the loads (a hoisted mask would hold two scalar
+// registers per element).
 template <int EPT>
 __device__ __forceinline__ void row_vals(float (&v)[EPT], int wbase, int c, int T) {
   const int wend = (__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) + 1) * 64 * EPT;
   if (wend <= c) return;
+  int rc = c - wbase, rt = T - wbase;
+  asm volatile("" : "+v"(rc), "+v"(rt) : "v"(v[EPT - 1]));
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int t = wbase + 64 * e;
-    uint32_t below_c = (uint32_t)(t - c) >> 31, below_t = (uint32_t)(t - T) >> 31;
-    asm volatile("" : "+v"(below_c), "+v"(below_t));
-    // masked: -inf below T, NaN (0x7fc00000) past it
-    const uint32_t m = 0xff800000u ^ (0x80400000u & (below_t - 1u));
-    const uint32_t u = __float_as_uint(v[e]);
-    v[e] = __uint_as_float(m ^ ((u ^ m) & (0u - below_c)));
-  }
+  for (int e = 0; e < EPT; ++e)
+    v[e] = 64 * e < rt ? (64 * e < rc ? v[e] : -__builtin_inff()) : __builtin_nanf("");
 }
 
 // The remaining digits of the threshold search, among the scores whose
@@ -289,9 +290,17 @@ __device__ __forceinline__ void row_refine(const float (&v)[EPT], uint32_t* hist
     // counted by the digit of the bits (the key digit of a negative score is
     // its complement, applied when the bins are read)
     const KeyRange in(prefix << shift, (prefix << shift) | ((1u << shift) - 1u));
+    // the count is a register the compiler cannot rebuild per element
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one));
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if (in.has(v[e])) atomicAdd(&hist[(__float_as_uint(v[e]) >> nshift) & nbm], 1u);
+    for (int e = 0; e < EPT; ++e) {
+      // the two compares' masks ANDed as scalars give the lanes that count
+      // (a wave-level test to skip empty elements cost more scalar issue
+      // than the two vector instructions it saves)
+      const bool ge = v[e] >= in.f_lo, le = v[e] <= in.f_hi;
+      if (ge & le) atomicAdd(&hist[(__float_as_uint(v[e]) >> nshift) & nbm], one);
+    }
     __syncthreads();
     uint32_t bin, k2;
     if (pass == 1)
@@ -387,7 +396,9 @@ __device__ __forceinline__ void row_emit(const float (&v)[EPT], uint32_t prefix,
       const KeyRange tied(lo, hi);
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
-        const uint64_t m = __ballot(tied.has(v[e]));
+        // the two compares' masks ANDed as scalars (a ballot of their
+        // conjunction costs a select and a third compare)
+        const uint64_t m = __ballot(v[e] >= tied.f_lo) & __ballot(v[e] <= tied.f_hi);
         qlo = (uint32_t)idx_writelane_i32((int)(uint32_t)m, e, (int)qlo);
         qhi = (uint32_t)idx_writelane_i32((int)(uint32_t)(m >> 32), e, (int)qhi);
       }

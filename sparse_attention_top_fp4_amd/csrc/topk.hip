@@ -14,18 +14,24 @@
 // histogram's total).  Given that histogram:
 //
 //  - single-workgroup path (rows up to 32768): the row is loaded once into
-//    registers; elements in the threshold bin are compacted into an LDS list
-//    and the two remaining digits are resolved on that short list; the
-//    selection is then written as two position-ordered bit masks in LDS (keys
-//    above the threshold; keys equal to it), and one thread per 32-position
-//    word turns them into output slots with two block scans, taking equal
-//    keys from the lowest positions.  Comparisons after the threshold search
-//    are done on the float scores (the threshold key maps back to a float;
-//    -0 equals +0 there as in the key order).
-//  - chunked path (longer rows): chunks of 4096 positions over many
-//    workgroups; the remaining digit histograms and per-chunk counts live in
-//    a device workspace, one launch per step, and each workgroup re-derives
-//    the earlier thresholds from the global histograms.
+//    registers and ranked there (row_topk.hpp): the remaining digits are LDS
+//    histograms of the scores in the threshold's range, and the selection is
+//    written as two position-ordered bit masks in LDS (keys above the
+//    threshold; keys equal to it), which one thread per 32-position word
+//    turns into output slots with one block scan, taking equal keys from the
+//    lowest positions.  Comparisons after the threshold search are done on
+//    the float scores (the threshold key maps back to a float; -0 equals +0
+//    there as in the key order).
+//  - split path (rows of 32769..262144 positions with a score histogram,
+//    split_topk.hpp): kernel A, one workgroup per 8192-position part, writes
+//    the part's above-the-bin mask and the list of its elements inside the
+//    threshold bin; kernel B, one workgroup per row, resolves the remaining
+//    digits on the gathered list and compacts the row.
+//  - chunked path (longer rows, and rows past 32768 without a histogram):
+//    chunks of 4096 positions over many workgroups; the remaining digit
+//    histograms and per-chunk counts live in a device workspace, one launch
+//    per step, and each workgroup re-derives the earlier thresholds from the
+//    global histograms.
 //
 // Without a score histogram the first digit is histogrammed here as well.
 // Elements equal to -inf (masked positions) are counted with a wave ballot
