@@ -419,6 +419,75 @@ idx_status idx_topk_candidates(const float *scores, int64_t ld, int R, int T,
                                int32_t *k_out, void *stream);
 
 /*
+ * The top-k of rows split along their positions (T-split): one owner per
+ * slice of consecutive positions (a GPU of a context-parallel group, say)
+ * ranks its slice, the slices' (position, score) lists are gathered, and
+ * idx_merge_topk ranks their union.  The result is idx_topk's on the whole
+ * rows ([IDX, forward: topk of min(index_topk, end_pos//ratio), sort by
+ * position, -1 where not below compress_lens, plus offset]): a position in a
+ * row's top k is beaten by fewer than k positions of the row, so it is in its
+ * slice's top k, and the union of the slices' lists is ranked by the same
+ * (score descending, position ascending) order.
+ *
+ * Bytes of device workspace idx_topk_pairs needs.
+ */
+size_t idx_topk_pairs_workspace_size(int R, int T_slice, int index_topk);
+
+/*
+ * idx_topk_pairs -- the top-k of one slice of each row, as pairs.  The slice
+ * holds row positions [slice_start, slice_start + T_slice); its scores are
+ * scores[r][0 .. T_slice) (a pointer to the slice's first column).
+ *   scores          device, [R][ld] fp32, ld >= T_slice
+ *   compress_lens   device, [R] int32: the rows' own lengths (positions
+ *                   t >= compress_lens[r] of the row count as -inf); the
+ *                   slice's are clamp(cl - slice_start, 0, T_slice)
+ *   key_hist        device, [R][2048] from idx_score of this slice with the
+ *                   slice's compress_lens, or NULL; read and reset as by
+ *                   idx_topk
+ *   pos_out         device, [R][ld_out] int32, ld_out >= k_out =
+ *                   min(index_topk, T_slice): the slice's top k_out row
+ *                   positions in ascending order, -1 where not below
+ *                   compress_lens (idx_topk of the slice with offset
+ *                   slice_start)
+ *   score_out       device, [R][ld_out] fp32: the score of each listed
+ *                   position, -inf for -1
+ *   k_out           host, or NULL: receives k_out
+ *   ws, ws_bytes    device workspace, at least idx_topk_pairs_workspace_size
+ * Requires slice_start >= 0 and slice_start + T_slice < 2^31 (IDX_EINVAL
+ * otherwise).  NaN scores give unspecified results.
+ */
+idx_status idx_topk_pairs(const float *scores, int64_t ld, int R, int T_slice, int slice_start,
+                          const int32_t *compress_lens, uint32_t *key_hist, int index_topk,
+                          int32_t *pos_out, float *score_out, int64_t ld_out, int32_t *k_out,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * idx_merge_topk -- the rows' top-k from their slices' pairs.  List g of row
+ * r holds n pairs at pos[g*list_stride + r*ld + j], score[...same], j < n:
+ * idx_topk_pairs of slice g, the slices in ascending position order and
+ * none overlapping (a shorter list padded with position -1).  Entries with
+ * position -1 are skipped.  Row r: with c = clamp(compress_lens[r], 0, T)
+ * <= k_out = min(index_topk, T), the closed form (t + offset for t < c,
+ * then -1); otherwise the k_out listed pairs first by (score descending, -0
+ * equal to +0; position ascending), written by ascending position as
+ * position + offset (-1 for a position >= c).  Lists that are the slices'
+ * top-k lists hold at least k_out valid pairs whenever c > k_out; with fewer,
+ * every valid pair is written and the rest of the row is -1.
+ *   pos, score      device, int32 / fp32 as above (may be NULL when n == 0)
+ *   G               lists per row, >= 1; G * n <= 32768 (IDX_EUNSUPPORTED)
+ *   list_stride     >= (R - 1) * ld + n when G > 1, ld >= n
+ *   compress_lens   device, [R] int32
+ *   T               the rows' width
+ *   out             device, [R][ld_out] int32, ld_out >= k_out
+ *   k_out           host, or NULL: receives k_out
+ * NaN scores give unspecified results.
+ */
+idx_status idx_merge_topk(const int32_t *pos, const float *score, int G, int n,
+                          int64_t list_stride, int64_t ld, int R, const int32_t *compress_lens,
+                          int T, int index_topk, int32_t offset, int32_t *out, int64_t ld_out,
+                          int32_t *k_out, void *stream);
+
+/*
  * Bytes of device workspace idx_select_candidate_blocks needs.
  */
 size_t idx_select_workspace_size(int R, int T, int candidate_topk_blocks, int cand_block_size);

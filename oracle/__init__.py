@@ -51,6 +51,12 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
                    golden tells it apart from the other plausible orders.
   publish          pinned: pre-quantisation key vs a float64 restatement within
                    bf16 rounding; RoPE identity at position 0; norm preservation.
+  topk_pairs,      the T-split top-k, numpy over topk().  Pinned: merging the
+  merge_topk       slices' lists equals topk() of the whole row for every
+                   slicing tried (ties across slice edges, -0 and +0,
+                   compress_lens in every slice, k beyond a slice's width);
+                   a hand-worked two-slice tie; the full-lexsort brute force
+                   on tiny rows.
   q_rope_quant     pinned: RoPE identity at position 0 and with rd = 0 (the
                    rows are then the quantiser's); rotation vs a float64
                    restatement within bf16 rounding; pair norms; weights
@@ -405,6 +411,55 @@ def topk_bruteforce(scores_row: np.ndarray, cl: int, k: int, offset: int = 0) ->
     order = np.lexsort((t, -s))[: min(k, T)]
     order = np.sort(order)
     return np.where(order < cl, order + offset, -1).astype(np.int32)
+
+
+def topk_pairs(scores, cl, k, start, T_slice):
+    """The top-k of the slice [start, start + T_slice) of each row as pairs
+    ([IDX, forward: topk of the masked scores, position re-sort, -1 where not
+    below compress_lens]; the T-split of a row over several owners): the
+    slice ranked by topk() with compress_lens clamp(cl - start, 0, T_slice)
+    and offset start, so the positions are the row's; and the score of each
+    listed position, -inf for -1.  Returns (pos [R][k_out] int32, score
+    [R][k_out] float32), k_out = min(k, T_slice)."""
+    scores = np.asarray(scores, np.float32)
+    sl = np.ascontiguousarray(scores[:, start:start + T_slice])
+    lens = np.clip(np.asarray(cl, np.int64) - start, 0, T_slice).astype(np.int32)
+    pos = topk(sl, lens, k, offset=start)
+    idx = np.clip(pos.astype(np.int64) - start, 0, max(T_slice - 1, 0))
+    got = np.take_along_axis(sl, idx, axis=1) if T_slice else np.zeros_like(pos, np.float32)
+    sc = np.where(pos >= 0, got, np.float32(-np.inf)).astype(np.float32)
+    return pos, sc
+
+
+def merge_topk(pos, score, cl, T, k, offset=0):
+    """The rows' top-k from their slices' pairs (pos, score [G][R][n], list g
+    of row r from slice g, -1 entries skipped).  A position in the row's top
+    k is beaten by fewer than k positions of the row, hence of its slice, so
+    the union of the slices' lists holds it; the union is ranked here by a
+    full sort on (score descending, -0 equal to +0; position ascending), the
+    first k_out = min(k, T) kept and written by position as position +
+    offset (-1 at or past compress_lens).  Rows with compress_lens <= k_out
+    take the closed form; with fewer valid pairs than k_out, every valid pair
+    is written and the rest is -1."""
+    pos = np.asarray(pos, np.int32)
+    score = np.asarray(score, np.float32)
+    G, R, n = pos.shape
+    kout = min(k, T)
+    out = np.full((R, kout), -1, np.int32)
+    ar = np.arange(kout)
+    for r in range(R):
+        c = min(max(int(cl[r]), 0), T)
+        if c <= kout:
+            out[r] = np.where(ar < c, ar + offset, -1)
+            continue
+        p = pos[:, r, :].reshape(-1).astype(np.int64)
+        s = score[:, r, :].reshape(-1).astype(np.float64)
+        keep = p >= 0
+        p, s = p[keep], s[keep]
+        s = np.where(s == 0.0, 0.0, s)
+        sel = np.sort(p[np.lexsort((p, -s))[:kout]])
+        out[r, :sel.size] = np.where(sel < c, sel + offset, -1)
+    return out
 
 
 def select_blocks_bruteforce(scores_row, cl, ctb, cbs):

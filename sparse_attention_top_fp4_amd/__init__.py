@@ -23,7 +23,8 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
            "idx_publish_score", "idx_score_select_blocks", "idx_score_topk_candidates",
-           "idx_two_level_topk",
+           "idx_two_level_topk", "idx_topk_pairs", "idx_topk_pairs_workspace_size",
+           "idx_merge_topk",
            "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
            "load_library", "IdxError", "ROW_BYTES"]
 
@@ -97,6 +98,11 @@ def load_library():
                                           i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
                                     i32, i32, i32, P, P, i64, P, P]
+    L.idx_topk_pairs_workspace_size.argtypes = [i32, i32, i32]
+    L.idx_topk_pairs_workspace_size.restype = sz
+    L.idx_topk_pairs.argtypes = [P, i64, i32, i32, i32, P, P, i32, P, P, i64, P, P, sz, P]
+    L.idx_merge_topk.argtypes = [P, P, i32, i32, i64, i64, i32, P, i32, i32, ctypes.c_int32, P,
+                                 i64, P, P]
     L.idx_probe_stream_read.argtypes = [P, i64, i32, P, ctypes.POINTER(f32), P]
     L.idx_probe_mfma_fp4.argtypes = [i32, i32, P, ctypes.POINTER(f64), ctypes.POINTER(f32), P]
     L.idx_probe_bf16_convert.argtypes = [P, ctypes.POINTER(ctypes.c_ulonglong), P]
@@ -112,7 +118,7 @@ def load_library():
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
                  "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk",
-                 "idx_score_qrope", "idx_score_topk_qrope"):
+                 "idx_score_qrope", "idx_score_topk_qrope", "idx_topk_pairs", "idx_merge_topk"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -626,6 +632,71 @@ def idx_topk(scores, T, compress_lens, index_topk, offset, out, workspace=None, 
                                 _ptr(key_hist), index_topk, offset, _ptr(out), out.shape[1],
                                 ctypes.byref(kout), _ptr(workspace), wsb), stream, "idx_topk",
                    bind, keep=(workspace,))
+    return bound if bind else kout.value
+
+
+def idx_topk_pairs_workspace_size(R: int, T_slice: int, index_topk: int) -> int:
+    return int(load_library().idx_topk_pairs_workspace_size(R, T_slice, index_topk))
+
+
+def idx_topk_pairs(scores, slice_start, T_slice, compress_lens, index_topk, pos_out, score_out,
+                   workspace=None, key_hist=None, stream=None, bind=False):
+    """The top-k of the slice [slice_start, slice_start + T_slice) of each row
+    of scores [R, ld] float32, as (position, score) pairs: pos_out [R, ld_out]
+    int32 gets the slice's top min(index_topk, T_slice) row positions in
+    ascending order (-1 where not below compress_lens [R], the rows' own
+    lengths), score_out [R, ld_out] float32 their scores (-inf for -1).
+    key_hist: a histogram idx_score made of this slice with the slice's
+    compress_lens, or None.  Returns the width written per row."""
+    torch = _torch()
+    _dev(scores, "scores", (torch.float32,), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(pos_out, "pos_out", (torch.int32,), 2)
+    _dev(score_out, "score_out", (torch.float32,), 2)
+    R, ld = scores.shape
+    if not 0 <= slice_start <= ld or T_slice < 0 or slice_start + T_slice > ld:
+        raise ValueError("the slice must lie inside the rows of scores")
+    if compress_lens.shape[0] != R or pos_out.shape[0] != R or score_out.shape != pos_out.shape:
+        raise ValueError("scores, compress_lens, pos_out and score_out need the same rows")
+    need = idx_topk_pairs_workspace_size(R, T_slice, index_topk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (R, 2048):
+            raise ValueError("key_hist must be [R, 2048]")
+    kout = ctypes.c_int32(-1)
+    first = ctypes.c_void_p(scores.data_ptr() + 4 * slice_start)
+    bound = _issue("idx_topk_pairs", (first, ld, R, T_slice, slice_start, _ptr(compress_lens),
+                                      _ptr(key_hist), index_topk, _ptr(pos_out), _ptr(score_out),
+                                      pos_out.shape[1], ctypes.byref(kout), _ptr(workspace), wsb),
+                   stream, "idx_topk_pairs", bind, keep=(workspace,))
+    return bound if bind else kout.value
+
+
+def idx_merge_topk(pos, score, compress_lens, T, index_topk, offset, out, stream=None,
+                   bind=False):
+    """The row top-k from the slices' pairs: pos [G, R, n] int32 and score
+    [G, R, n] float32 hold list g of row r (idx_topk_pairs of slice g, the
+    slices in position order; shorter lists padded with -1); out [R, ld_out]
+    int32 gets what idx_topk gives on the rows of width T with compress_lens
+    [R].  Returns k_out = min(index_topk, T)."""
+    torch = _torch()
+    _dev(pos, "pos", (torch.int32,), 3)
+    _dev(score, "score", (torch.float32,), 3)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(out, "out", (torch.int32,), 2)
+    G, R, n = pos.shape
+    if tuple(score.shape) != (G, R, n):
+        raise ValueError("pos and score must have the same shape")
+    if compress_lens.shape[0] != R or out.shape[0] != R:
+        raise ValueError("pos, compress_lens and out need the same rows")
+    kout = ctypes.c_int32(-1)
+    bound = _issue("idx_merge_topk", (_ptr(pos), _ptr(score), G, n, R * n, n, R,
+                                      _ptr(compress_lens), T, index_topk, offset, _ptr(out),
+                                      out.shape[1], ctypes.byref(kout)),
+                   stream, "idx_merge_topk", bind)
     return bound if bind else kout.value
 
 

@@ -388,3 +388,40 @@ def test_score_q4_rejects_unaligned_rows(lib):
                                  None) == IDX_EINVAL
     assert lib.idx_score_q4(None, d, d, 8, 1, 1, 64, 128, 8, d, None, 0, 0, d, 8, None,
                             None) == IDX_EINVAL
+
+
+def test_tsplit_pairs_and_merge_check_before_launch(lib):
+    """idx_topk_pairs and idx_merge_topk refuse their invalid arguments before
+    any launch (the pointers below are never dereferenced)."""
+    d = ctypes.c_void_p(0x1000)
+    kout = ctypes.c_int32(-1)
+    ws_need = lib.idx_topk_pairs_workspace_size(4, 32768, 2048)
+    assert ws_need >= lib.idx_topk_workspace_size(4, 32768, 2048) + 16
+
+    def pairs(ld=32768, R=4, Tg=32768, start=0, k=2048, ld_out=2048, ws=d, wsb=ws_need,
+              pos=d, sc=d):
+        return lib.idx_topk_pairs(d, ld, R, Tg, start, d, None, k, pos, sc, ld_out,
+                                  ctypes.byref(kout), ws, wsb, None)
+    assert pairs(ld=32767) == IDX_EINVAL          # ld < T_slice
+    assert pairs(ld_out=2047) == IDX_EINVAL       # ld_out < k_out
+    assert pairs(start=-1) == IDX_EINVAL
+    assert pairs(start=2 ** 31 - 100) == IDX_EINVAL  # positions past int32
+    assert pairs(k=0) == IDX_EINVAL
+    assert pairs(ws=None) == IDX_EINVAL
+    assert pairs(wsb=ws_need - 1) == IDX_EINVAL
+    assert pairs(sc=None) == IDX_EINVAL
+    assert pairs(R=0) == IDX_OK and kout.value == 2048  # no rows: k_out only
+    assert pairs(Tg=100, ld=100, R=0) == IDX_OK and kout.value == 100
+
+    def merge(G=8, n=2048, stride=4 * 2048, ld=2048, R=4, T=262144, k=2048, ld_out=2048,
+              pos=d, sc=d):
+        return lib.idx_merge_topk(pos, sc, G, n, stride, ld, R, d, T, k, 0, d, ld_out,
+                                  ctypes.byref(kout), None)
+    assert merge(G=17) == IDX_EUNSUPPORTED        # 17 x 2048 pairs per row
+    assert merge(G=0) == IDX_EINVAL
+    assert merge(stride=4 * 2048 - 1) == IDX_EINVAL  # lists of a row would overlap
+    assert merge(ld=2047) == IDX_EINVAL           # ld < n
+    assert merge(ld_out=2047) == IDX_EINVAL
+    assert merge(pos=None) == IDX_EINVAL
+    assert merge(k=0) == IDX_EINVAL
+    assert merge(R=0) == IDX_OK and kout.value == 2048
