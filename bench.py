@@ -77,6 +77,11 @@ def parse():
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the chip's ceilings (streaming read over grid sizes, "
                          "fp4 matrix-core loop) and print them as one JSON line")
+    ap.add_argument("--tsplit", type=int, default=0,
+                    help="only measure one owner's share of the ranking when the rows are "
+                         "split along their positions over this many owners (the top-k of "
+                         "one slice as (position, score) pairs and the merge of every "
+                         "slice's list) and print it as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -299,6 +304,70 @@ def measure_ceilings(nbytes, reps=8):
             "mfma_fp4": {"by_grid": mf, "best_TFLOPs": max(m["best_TFLOPs"] for m in mf)}}
 
 
+def measure_tsplit(wl, G, steps, warmup):
+    """One owner's share of the ranking of a T-split: the rows' positions in
+    G equal slices, each owner ranking its slice (idx_topk_pairs, here the
+    last slice, without a score histogram) and every owner merging the G
+    gathered lists (idx_merge_topk).  The scores are one step's of the
+    workload on one GPU; the merged rows are checked against idx_topk of the
+    whole rows before timing.  Times are event pairs around `steps` calls."""
+    import torch
+
+    import sparse_attention_top_fp4_amd as idx
+    from sparse_attention_top_fp4_amd.inputs import generate
+    from sparse_attention_top_fp4_amd.pipeline import IndexerStep
+
+    R, T, k = wl.R, wl.T, wl.topk
+    if G < 2 or T % G:
+        sys.exit(f"--tsplit {G}: needs at least 2 slices that divide T = {T}")
+    st = IndexerStep(wl, generate(wl))
+    st.step()
+    torch.cuda.synchronize()
+    Tg = T // G
+    n = min(k, Tg)
+    kout = min(k, T)
+    pos = torch.full((G, R, n), -1, dtype=torch.int32, device="cuda")
+    sco = torch.full((G, R, n), float("-inf"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, idx.idx_topk_pairs_workspace_size(R, Tg, k)), dtype=torch.uint8,
+                     device="cuda")
+    for g in range(G):
+        idx.idx_topk_pairs(st.scores, g * Tg, Tg, st.cl, k, pos[g], sco[g], workspace=ws)
+    out = torch.empty((R, kout), dtype=torch.int32, device="cuda")
+    idx.idx_merge_topk(pos, sco, st.cl, T, k, wl.offset, out)
+    whole = torch.empty((R, kout), dtype=torch.int32, device="cuda")
+    idx.idx_topk(st.scores, T, st.cl, k, wl.offset, whole)
+    torch.cuda.synchronize()
+    if not torch.equal(out, whole):
+        sys.exit("--tsplit: the merged rows differ from the whole rows' top-k")
+    g = G - 1
+    pairs = idx.idx_topk_pairs(st.scores, g * Tg, Tg, st.cl, k, pos[g], sco[g], workspace=ws,
+                               bind=True)
+    merge = idx.idx_merge_topk(pos, sco, st.cl, T, k, wl.offset, out, bind=True)
+
+    def timed(calls):
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            for c in calls:
+                c()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    pairs_us, merge_us, share_us = timed([pairs]), timed([merge]), timed([pairs, merge])
+    return {"metric": "T-split ranking share per owner (us)", "value": share_us, "unit": "us",
+            "higher_is_better": False, "steps": steps, "warmup": warmup,
+            "config": {"workload": wl.name, "rows": R, "positions": T, "slices": G,
+                       "slice_positions": Tg, "index_topk": k, "pairs_per_list": n},
+            "pairs_us": pairs_us, "merge_us": merge_us, "share_us": share_us,
+            "exchange_bytes": G * R * n * 8,
+            "checked": "merged rows equal idx_topk of the whole rows"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -317,6 +386,9 @@ def main():
     if args.ceilings:
         print(json.dumps({"ceilings": measure_ceilings(wl.B * wl.T * 68),
                           "workload_bytes_from": wl.name}), flush=True)
+        return
+    if args.tsplit:
+        print(json.dumps(measure_tsplit(wl, args.tsplit, args.steps, args.warmup)), flush=True)
         return
     t_gen = time.perf_counter()
     inp = generate(wl)

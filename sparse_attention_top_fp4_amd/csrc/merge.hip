@@ -55,6 +55,96 @@ struct ListPos {
   __device__ __forceinline__ int operator()(int s) const { return posl[s]; }
 };
 
+// Largest / smallest float over the wave by DPP scan steps (the pattern of
+// wave_inclusive_sum); lanes whose source lies outside the row read the
+// identity.  NaN lanes are skipped (fmaxf / fminf return the other operand).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const int o = __builtin_amdgcn_update_dpp((int)0xff800000u, __float_as_int(v), CTRL, ROWS, 0xf,
+                                            false);
+  return fmaxf(v, __int_as_float(o));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_min_step(float v) {
+  const int o = __builtin_amdgcn_update_dpp((int)0x7f800000u, __float_as_int(v), CTRL, ROWS, 0xf,
+                                            false);
+  return fminf(v, __int_as_float(o));
+}
+// row_shr:1, 2, 4, 8 inside each row of 16 lanes, then row_bcast:15 (rows 1
+// and 3) and row_bcast:31 (rows 2 and 3): lane 63 holds the wave's result
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = dpp_max_step<0x111, 0xf>(v);
+  v = dpp_max_step<0x112, 0xf>(v);
+  v = dpp_max_step<0x114, 0xf>(v);
+  v = dpp_max_step<0x118, 0xf>(v);
+  v = dpp_max_step<0x142, 0xa>(v);
+  v = dpp_max_step<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_min_f32(float v) {
+  v = dpp_min_step<0x111, 0xf>(v);
+  v = dpp_min_step<0x112, 0xf>(v);
+  v = dpp_min_step<0x114, 0xf>(v);
+  v = dpp_min_step<0x118, 0xf>(v);
+  v = dpp_min_step<0x142, 0xa>(v);
+  v = dpp_min_step<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Threshold search of the merge (the result as row_refine's).  The lists hold
+// only the slices' top scores, which the fixed top 11 key bits would put in a
+// handful of bins, so that the LDS atomics of a wave hit one address; the
+// first digit here is (key >> s) - (kmin >> s) instead, for the least s that
+// keeps the valid keys' span [kmin, kmax] within 2048 bins, so the bins
+// follow the scores' own spread.  Bins are aligned to 2^s in key space, so
+// each is a (prefix, shift) range of the key bits and the later digits are
+// the next bits below it (at most 11 per pass).
+template <int EPT>
+__device__ __forceinline__ void merge_select(const float (&v)[EPT], float hi, float lo,
+                                             uint32_t* hist, uint32_t* sh, uint32_t* wtot,
+                                             uint32_t kout, uint32_t& prefix, int& shift,
+                                             uint32_t& need, uint32_t& bin_count) {
+  const int tid = threadIdx.x;
+  const uint32_t kmax = score_key(hi), kmin = score_key(lo);
+  int s = 0;
+  while ((kmax >> s) - (kmin >> s) >= 2048u) ++s;  // s <= 21
+  const uint32_t kb = kmin >> s;
+  // (hist was cleared before the barrier that published the range)
+  uint32_t one = 1u;  // the count in one register, not rebuilt per element
+  asm volatile("" : "+v"(one));
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (v[e] == v[e]) atomicAdd(&hist[(score_key(v[e]) >> s) - kb], one);
+  __syncthreads();
+  uint32_t bin, krem, bcnt;
+  select_bin_r<kMergeNT, 2048>(hist, kout, 0xffffffffu, 0u, sh, wtot, bin, krem, bcnt);
+  prefix = kb + bin;
+  shift = s;
+  while (bcnt != krem && shift > 0) {  // uniform
+    const int nshift = shift > 11 ? shift - 11 : 0;
+    const uint32_t nbm = (1u << (shift - nshift)) - 1u;
+    const uint32_t lo_key = prefix << shift;
+    // the digits of a negative score are the complement of its bits
+    const uint32_t flip = (lo_key & 0x80000000u) ? 0u : nbm;
+    for (int i = tid; i < 2048; i += kMergeNT) hist[i] = 0u;
+    __syncthreads();
+    const KeyRange in(lo_key, lo_key | ((1u << shift) - 1u));
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const bool ge = v[e] >= in.f_lo, le = v[e] <= in.f_hi;
+      if (ge & le) atomicAdd(&hist[(__float_as_uint(v[e]) >> nshift) & nbm], one);
+    }
+    __syncthreads();
+    uint32_t k2;
+    select_bin_r<kMergeNT, 2048>(hist, krem, 0xffffffffu, 0u, sh, wtot, bin, k2, bcnt, flip);
+    prefix = (prefix << (shift - nshift)) | bin;
+    shift = nshift;
+    krem = k2;
+  }
+  need = krem;
+  bin_count = bcnt;
+}
+
 template <int EPT>
 __global__ __launch_bounds__(kMergeNT) void topk_merge_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ score, int G, int n,
@@ -63,8 +153,9 @@ __global__ __launch_bounds__(kMergeNT) void topk_merge_kernel(
   extern __shared__ uint32_t dyn_lds[];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t mbuf[kMergeNT * EPT / 16];
-  __shared__ uint32_t wtot[2 * (kMergeNT / 64)];
+  __shared__ uint32_t wtot[3 * (kMergeNT / 64)];
   __shared__ uint32_t sh[4];
+  constexpr int NW = kMergeNT / 64;
   lds_i32* posl = (lds_i32*)dyn_lds;
   const int r = blockIdx.x, tid = threadIdx.x;
   int32_t* orow = out + (int64_t)r * ld_out;
@@ -76,38 +167,83 @@ __global__ __launch_bounds__(kMergeNT) void topk_merge_kernel(
   }
   const int N = G * n;  // 0 when the lists are empty (n == 0)
   const int wbase = row_base<EPT>();
-  float v[EPT];
+  // Every pair is requested before any is used, with no branch between the
+  // loads (a branch per element would make each load wait for the one
+  // before): a slot past the list end re-reads the last pair, and is
+  // dropped below.
+  int pp[EPT];
+  float ss[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) v[e] = __builtin_nanf("");
-  uint32_t nvalid = 0;
-  if (wbase < N) {
-    // slot wbase + 64e as (list g, entry j): one division, then steps of 64
-    int g = wbase / n, j = wbase - g * n;
+  for (int e = 0; e < EPT; ++e) {
+    pp[e] = -1;
+    ss[e] = 0.0f;
+  }
+  if (N > 0) {
+    const int64_t rbase = (int64_t)r * ld;
+    const int64_t o_last = (int64_t)(G - 1) * list_stride + rbase + (n - 1);
+    if (n >= 64) {
+      // slot wbase + 64e as (list g, entry j): one division, then steps of
+      // 64 that wrap at most once
+      int g = wbase / n, j = wbase - g * n;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int s = wbase + 64 * e;
-      if (s < N) {
-        const int64_t o = (int64_t)g * list_stride + (int64_t)r * ld + j;
-        const int p = pos[o];
-        const float sc = score[o];
-        v[e] = p >= 0 ? sc : __builtin_nanf("");
-        nvalid += p >= 0 ? 1u : 0u;
-        posl[s] = p;
+      for (int e = 0; e < EPT; ++e) {
+        const int64_t o = wbase + 64 * e < N ? (int64_t)g * list_stride + rbase + j : o_last;
+        pp[e] = pos[o];
+        ss[e] = score[o];
+        j += 64;
+        const bool wrap = j >= n;
+        j = wrap ? j - n : j;
+        g += wrap ? 1 : 0;
       }
-      j += 64;
-      while (j >= n) {  // n may be below 64 (n >= 1 here)
-        j -= n;
-        ++g;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int sl = wbase + 64 * e < N ? wbase + 64 * e : N - 1;
+        const int g = sl / n, j = sl - g * n;
+        const int64_t o = (int64_t)g * list_stride + rbase + j;
+        pp[e] = pos[o];
+        ss[e] = score[o];
       }
     }
   }
-  // (block_sum's barriers also publish posl)
-  const uint32_t V = block_sum<kMergeNT>(nvalid, wtot);
+  float v[EPT];
+  uint32_t nvalid = 0;
+  float hi = -__builtin_inff(), lo = __builtin_inff();  // the valid scores' range
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int s = wbase + 64 * e;
+    const int p = s < N ? pp[e] : -1;
+    v[e] = p >= 0 ? ss[e] : __builtin_nanf("");
+    nvalid += p >= 0 ? 1u : 0u;
+    hi = fmaxf(hi, v[e]);
+    lo = fminf(lo, v[e]);
+    if (s < N) posl[s] = p;
+  }
+  // the valid count and the range over the block in one exchange; the same
+  // barrier publishes posl and the cleared histogram
+  {
+    const int lane = tid & 63, w = tid >> 6;
+    const uint32_t vw = wave_sum(nvalid);
+    const float hw = wave_max_f32(hi), lw = wave_min_f32(lo);
+    float* wf = reinterpret_cast<float*>(wtot);
+    if (lane == 0) {
+      wtot[w] = vw;
+      wf[NW + w] = hw;
+      wf[2 * NW + w] = lw;
+    }
+    for (int i = tid; i < 2048; i += kMergeNT) hist[i] = 0u;
+    __syncthreads();
+    nvalid = wave_sum(lane < NW ? wtot[lane] : 0u);
+    hi = wave_max_f32(lane < NW ? wf[NW + lane] : -__builtin_inff());
+    lo = wave_min_f32(lane < NW ? wf[2 * NW + lane] : __builtin_inff());
+    __syncthreads();  // wtot is the scans' again
+  }
+  const uint32_t V = nvalid;
   int32_t* stage = kout <= 2048 ? reinterpret_cast<int32_t*>(hist) : nullptr;
   uint32_t prefix, need, bcnt;
   int shift;
   if (V >= (uint32_t)kout) {
-    row_select<kMergeNT, EPT>(v, hist, 0xffffffffu, N, kout, sh, wtot, prefix, shift, need, bcnt);
+    merge_select<EPT>(v, hi, lo, hist, sh, wtot, (uint32_t)kout, prefix, shift, need, bcnt);
   } else {
     // fewer valid pairs than k_out (lists that are not the slices' top-k
     // lists): every valid pair is taken, the rest of the row is -1
