@@ -82,7 +82,10 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
     bool f8) {
   extern __shared__ __attribute__((aligned(16))) uint32_t pg_smem[];
   const int rb = f8 ? kRowBytesF8 : kRowBytes;
-  const int wpr = Din / 2 + 1;                                        // words per wk row
+  // words per wk row: two pad words keep rows 8-byte aligned for the
+  // 8-byte reads below, and the 64 lanes' rows start on distinct bank pairs
+  // in each half-wave
+  const int wpr = Din / 2 + 2;
   uint32_t* wk_s = pg_smem;                                           // [128][wpr]
   float* lat_s = reinterpret_cast<float*>(pg_smem + kHeadDim * wpr);  // [kPubGroups][Din]
   __shared__ float y_s[kPubGroups][kHeadDim];
@@ -92,29 +95,105 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
   const int64_t nslots = (int64_t)B * G;
   const int64_t bg0 = (int64_t)blockIdx.x * kPubGroups;
 
+  // wk and the slots' latents into LDS, thread t taking column t % width of
+  // every (NT / width)-th row: one division per thread, not per word (Din <=
+  // 512, so a pass covers at least 4 wk rows and 2 latent rows).  The
+  // latents are requested first, so that they arrive beside wk.
+  constexpr int NT = kPubGroups * kHeadDim;
   const uint32_t* wk32 = reinterpret_cast<const uint32_t*>(wk);
   const int hw = Din / 2;
-  for (int i = tid; i < kHeadDim * hw; i += kPubGroups * kHeadDim) {
-    const int row = i / hw, col = i - row * hw;
-    wk_s[row * wpr + col] = wk32[i];
+  {
+    // at most kPubGroups / 2 slots per thread, all requested before any store
+    constexpr int kLat = kPubGroups / 2;
+    const int gpp = NT / Din, g0 = tid / Din, k = tid - g0 * Din;
+    if (g0 < gpp) {
+      uint16_t t[kLat];
+#pragma unroll
+      for (int u = 0; u < kLat; ++u) {
+        const int64_t bg = bg0 + g0 + u * gpp;  // a slot past the end re-reads slot 0
+        t[u] = latent[(g0 + u * gpp < kPubGroups && bg < nslots ? bg : bg0) * Din + k];
+      }
+#pragma unroll
+      for (int u = 0; u < kLat; ++u) {
+        const int g = g0 + u * gpp;
+        if (g < kPubGroups) lat_s[g * Din + k] = bg0 + g < nslots ? bf16f(t[u]) : 0.0f;
+      }
+    }
   }
-  for (int i = tid; i < kPubGroups * Din; i += kPubGroups * kHeadDim) {
-    const int g = i / Din, k = i - g * Din;
-    const int64_t bg = bg0 + g;
-    lat_s[i] = bg < nslots ? bf16f(latent[bg * Din + k]) : 0.0f;
+  if ((hw & 3) == 0 && (reinterpret_cast<uintptr_t>(wk) & 15) == 0) {  // uniform
+    // 16-byte loads: thread t takes words [4q, 4q + 4) of rows r0, r0 + rpp,
+    // ... (q = t % (hw / 4)), all requested before any LDS store (a store
+    // right after each load would wait out every load's latency in turn); a
+    // row past the end re-reads the last row and is not stored.  The rows'
+    // LDS starts are 8-byte aligned: two 8-byte stores per load.
+    const int qpr = hw >> 2, rpp = NT / qpr, r0 = tid / qpr, c = 4 * (tid - r0 * qpr);
+    const uint4* wk128 = reinterpret_cast<const uint4*>(wk);
+    if (r0 < rpp)
+      for (int row0 = r0; row0 < kHeadDim; row0 += 8 * rpp) {
+        uint4 t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = row0 + u * rpp;
+          t[u] = wk128[((row < kHeadDim ? row : kHeadDim - 1) * hw + c) >> 2];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = row0 + u * rpp;
+          if (row < kHeadDim) {
+            uint2* d = reinterpret_cast<uint2*>(wk_s + row * wpr + c);
+            d[0] = make_uint2(t[u].x, t[u].y);
+            d[1] = make_uint2(t[u].z, t[u].w);
+          }
+        }
+      }
+  } else {
+    // sixteen rows' loads in flight before their LDS stores; a row past the
+    // end re-reads the last row and is not stored
+    const int rpp = NT / hw, r0 = tid / hw, c = tid - r0 * hw;
+    if (r0 < rpp)
+      for (int row0 = r0; row0 < kHeadDim; row0 += 16 * rpp) {
+        uint32_t t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int row = row0 + u * rpp;
+          t[u] = wk32[(row < kHeadDim ? row : kHeadDim - 1) * hw + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int row = row0 + u * rpp;
+          if (row < kHeadDim) wk_s[row * wpr + c] = t[u];
+        }
+      }
   }
   __syncthreads();
 
   const uint32_t* wrow = wk_s + o * wpr;
-  const float2* lrow = reinterpret_cast<const float2*>(lat_s + gi * Din);  // Din even
   float acc = 0.0f;  // y_o of slot gi: sum_i fma(wk[o][i], latent[i]), i ascending
-  // unrolled so the LDS reads of later pairs are in flight during the chain
+  if ((Din & 3) == 0) {  // uniform
+    // four inputs per step: one 8-byte wk read and one 16-byte latent read
+    // (the latent read is the same address in every lane), half the LDS
+    // instructions of the two-input step, which bound this loop
+    const uint2* w4 = reinterpret_cast<const uint2*>(wrow);
+    const float4* l4 = reinterpret_cast<const float4*>(lat_s + gi * Din);
+#pragma unroll 8
+    for (int k4 = 0; k4 < Din / 4; ++k4) {
+      const uint2 w = w4[k4];
+      const float4 l = l4[k4];
+      acc = __builtin_fmaf(bf16f(w.x & 0xffffu), l.x, acc);
+      acc = __builtin_fmaf(bf16f(w.x >> 16), l.y, acc);
+      acc = __builtin_fmaf(bf16f(w.y & 0xffffu), l.z, acc);
+      acc = __builtin_fmaf(bf16f(w.y >> 16), l.w, acc);
+    }
+  } else {
+    const float2* lrow = reinterpret_cast<const float2*>(lat_s + gi * Din);  // Din even
+    // unrolled so the LDS reads of later pairs are in flight during the chain
 #pragma unroll 16
-  for (int k2 = 0; k2 < hw; ++k2) {
-    const uint32_t w2 = wrow[k2];
-    const float2 l2 = lrow[k2];
-    acc = __builtin_fmaf(bf16f(w2 & 0xffffu), l2.x, acc);
-    acc = __builtin_fmaf(bf16f(w2 >> 16), l2.y, acc);
+    for (int k2 = 0; k2 < hw; ++k2) {
+      const uint32_t w2 = wrow[k2];
+      const float2 l2 = lrow[k2];
+      acc = __builtin_fmaf(bf16f(w2 & 0xffffu), l2.x, acc);
+      acc = __builtin_fmaf(bf16f(w2 >> 16), l2.y, acc);
+    }
   }
   y_s[gi][o] = bf16f(f32_to_bf16(acc));
   __syncthreads();
@@ -140,7 +219,7 @@ __global__ __launch_bounds__(kPubGroups * kHeadDim) void publish_groups_kernel(
 }
 
 size_t publish_groups_lds(int Din) {
-  return ((size_t)kHeadDim * (Din / 2 + 1) + (size_t)kPubGroups * Din) * 4u;
+  return ((size_t)kHeadDim * (Din / 2 + 2) + (size_t)kPubGroups * Din) * 4u;
 }
 
 }  // namespace idx
