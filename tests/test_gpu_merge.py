@@ -11,7 +11,7 @@ than 32768 without a histogram), the longest lists (16 x 2048 pairs), lists
 shorter than a wave (k 5), k beyond a slice's width, k >= T, uneven slices,
 compress_lens in every slice, at 0 and at T, scores with many ties (across
 slice edges), -0 and +0, -inf; and lists that are not top-k lists (fewer
-valid pairs than k_out)."""
+valid pairs than k_out); and 12 seeded random shapes."""
 import numpy as np
 import pytest
 
@@ -126,3 +126,37 @@ def test_merge_rows_at_or_below_k_out_take_the_closed_form(idx):
     sync()
     s = rng.standard_normal((R, T)).astype(np.float32)
     assert np.array_equal(host(out), oracle.topk(s, cl, k, 9))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_merge_fuzz(idx, seed):
+    """Seeded random shapes: rows, width, slices (uneven), k on both sides of
+    the slices' and the rows' widths, compress_lens in [-2, T + 3], offsets of
+    both signs, ties."""
+    t = torch()
+    rng = np.random.default_rng(300 + seed)
+    R = int(rng.integers(1, 7))
+    T = int(rng.integers(2, 20000))
+    G = int(rng.integers(1, min(9, T) + 1))
+    k = int(rng.integers(1, 3000))
+    slices = _slices(T, G, False, rng) if G > 1 else [(0, T)]
+    n = max(min(k, w) for _, w in slices)  # G * n <= 9 * 2999: within the merge's 32768
+    s = _scores(rng, R, T, int(rng.integers(0, 40)))
+    cl = rng.integers(-2, T + 4, size=R).astype(np.int32)
+    offset = int(rng.integers(-1000, 1000))
+    say("merge fuzz", seed, R, T, G, k, n)
+    sd, cld = dev(s), dev(cl)
+    pos = t.full((G, R, n), -1, dtype=t.int32, device="cuda")
+    sco = t.full((G, R, n), float("-inf"), dtype=t.float32, device="cuda")
+    for g, (start, w) in enumerate(slices):
+        kl = min(k, w)
+        po = t.empty((R, kl), dtype=t.int32, device="cuda")
+        so = t.empty((R, kl), dtype=t.float32, device="cuda")
+        idx.idx_topk_pairs(sd, start, w, cld, k, po, so)
+        pos[g, :, :kl] = po
+        sco[g, :, :kl] = so
+    kout = min(k, T)
+    out = t.empty((R, kout), dtype=t.int32, device="cuda")
+    idx.idx_merge_topk(pos, sco, cld, T, k, offset, out)
+    sync()
+    assert np.array_equal(host(out), oracle.topk(s, cl, k, offset))
