@@ -67,8 +67,9 @@ __global__ __launch_bounds__(128) void publish_kernel(
 // Many groups (the prompt's keys): one workgroup of kPubGroups * 128 threads
 // publishes kPubGroups consecutive (sequence, group) slots, thread o of
 // group i computing output o of slot i.  wk is staged once per workgroup in
-// LDS as bf16 pairs with one pad word per row (lane o's reads of row o hit
-// distinct banks), the slots' latents as floats; every output is still the
+// LDS as bf16 pairs with two pad words per row (rows 8-byte aligned for the
+// chain's 8-byte reads, lane o's row on its own bank pair in each
+// half-wave), the slots' latents as floats; every output is still the
 // sequential fma chain over the input features, i ascending.  Din <= 512 and
 // even (the LDS holds all of wk).
 constexpr int kPubGroups = 8;
