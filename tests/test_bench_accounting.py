@@ -95,3 +95,11 @@ def test_query_step_bytes_replace_the_quantised_heads():
     from sparse_attention_top_fp4_amd.inputs import workload
     wl = workload(1)
     assert bench.step_bytes(wl, q_step=True) - bench.step_bytes(wl) == wl.R * wl.H * (256 + 2 - 70)
+
+
+def test_tsplit_needs_slices_that_divide_the_rows():
+    """--tsplit checks its slicing before any GPU work (the long decode's
+    262144 positions do not split in 3, and one slice is no split)."""
+    for g in ("3", "1"):
+        p = _run_bench(["--config", "4", "--tsplit", g, "--no-cpu"])
+        assert p.returncode != 0 and "--tsplit" in p.stderr, (g, p.stderr[-300:])
