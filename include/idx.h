@@ -650,6 +650,28 @@ idx_status idx_publish_score(const uint16_t *latent, const uint16_t *wk, const f
                              uint32_t *key_hist, void *stream);
 
 /*
+ * idx_publish_score_paged -- idx_publish_score on a paged key cache
+ * ([IDX, forward]: the key-owning layer's store before the score reads the
+ * cache; pages as idx_score_paged: row t of sequence b in slot t % 64 of
+ * page block_table[b][t / 64]).  The same single launch when the new key
+ * is the last scored position; otherwise idx_publish_keys_paged then
+ * idx_score_paged on the stream.  The published row's page id outside
+ * [0, n_pages) is not written, and that key is scored as the zero row the
+ * paged score reads there.  The block table must cover rows [0, max(T,
+ * start_pos / ratio + 1)).  Arguments, results and errors as those two
+ * calls; the page, the scores and key_hist equal theirs bit for bit for the
+ * documented inputs.  Din <= 2048 for the single launch.
+ */
+idx_status idx_publish_score_paged(const uint16_t *latent, const uint16_t *wk,
+                                   const float *gamma, const float *cos_sin, int P, int Din,
+                                   int rd, float eps, int start_pos, int ratio,
+                                   const uint16_t *q, const uint16_t *w, uint8_t *k_pages,
+                                   int64_t page_stride, int n_pages, const int32_t *block_table,
+                                   int64_t bt_stride, int B, int H, int D, int T,
+                                   const int32_t *compress_lens, float *scores, int64_t ld,
+                                   uint32_t *key_hist, void *stream);
+
+/*
  * idx_yarn_cos_sin -- host-side RoPE table for idx_publish_keys and
  * idx_q_rope_quant ([CMP, yarn_freqs_cis]: precompute_freqs_cis with YaRN;
  * the YaRN method of Peng et al.).  Pair i of the rd rotated dims has the

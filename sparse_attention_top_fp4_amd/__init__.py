@@ -22,7 +22,8 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
-           "idx_publish_score", "idx_score_select_blocks", "idx_score_topk_candidates",
+           "idx_publish_score", "idx_publish_score_paged", "idx_score_select_blocks",
+           "idx_score_topk_candidates",
            "idx_two_level_topk", "idx_topk_pairs", "idx_topk_pairs_workspace_size",
            "idx_merge_topk",
            "idx_yarn_cos_sin", "idx_timing_arm", "idx_timing_read", "library_path",
@@ -98,6 +99,8 @@ def load_library():
                                           i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
                                     i32, i32, i32, P, P, i64, P, P]
+    L.idx_publish_score_paged.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64,
+                                          i32, P, i64, i32, i32, i32, i32, P, P, i64, P, P]
     L.idx_topk_pairs_workspace_size.argtypes = [i32, i32, i32]
     L.idx_topk_pairs_workspace_size.restype = sz
     L.idx_topk_pairs.argtypes = [P, i64, i32, i32, i32, P, P, i32, P, P, i64, P, P, sz, P]
@@ -118,7 +121,8 @@ def load_library():
                  "idx_probe_stream_read", "idx_probe_mfma_fp4", "idx_fp8_quant",
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
                  "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk",
-                 "idx_score_qrope", "idx_score_topk_qrope", "idx_topk_pairs", "idx_merge_topk"):
+                 "idx_score_qrope", "idx_score_topk_qrope", "idx_topk_pairs", "idx_merge_topk",
+                 "idx_publish_score_paged"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -919,6 +923,42 @@ def idx_publish_score(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k
                    eps, start_pos, ratio, _ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, H,
                    D, T, _ptr(compress_lens), _ptr(scores), scores.shape[1], _ptr(key_hist)),
                   stream, "idx_publish_score", bind)
+
+
+def idx_publish_score_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_pages,
+                            block_table, T, compress_lens, scores, key_hist=None, rd=64,
+                            stream=None, bind=False):
+    """idx_publish_score on a paged key cache (pages as idx_score_paged):
+    latent [B, 1, Din] bf16, q [B, H, 128] bf16, w [B, H] bf16, k_pages
+    [n_pages, >=64, 68] uint8, block_table [B, n_blk] int32, compress_lens [B]
+    int32, scores [B, ld] float32, key_hist [B, 2048] int32 or None.  One
+    launch when the published row is the last scored position (T - 1)."""
+    torch = _torch()
+    _dev(latent, "latent", _bf16_types(), 3)
+    _dev(wk, "wk", _bf16_types(), 2)
+    _dev(gamma, "gamma", (torch.float32,), 1)
+    _dev(cos_sin, "cos_sin", (torch.float32,), 3)
+    _dev(q, "q", _bf16_types(), 3)
+    _dev(w, "w", _bf16_types(), 2)
+    _dev(compress_lens, "compress_lens", (torch.int32,), 1)
+    _dev(scores, "scores", (torch.float32,), 2)
+    B, G, Din = latent.shape
+    R, H, D = q.shape
+    if G != 1 or R != B or tuple(w.shape) != (B, H) or compress_lens.shape[0] != B:
+        raise ValueError("idx_publish_score_paged takes one group and one query row per sequence")
+    if wk.shape != (D, Din) or gamma.shape[0] != D or scores.shape[0] != B:
+        raise ValueError("shape mismatch in idx_publish_score_paged")
+    if key_hist is not None:
+        _dev(key_hist, "key_hist", (torch.int32,), 2)
+        if tuple(key_hist.shape) != (B, 2048):
+            raise ValueError("key_hist must be [B, 2048]")
+    ps, npg, bts = _pages(k_pages, block_table, B)
+    return _issue("idx_publish_score_paged",
+                  (_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin), cos_sin.shape[0], Din, rd,
+                   eps, start_pos, ratio, _ptr(q), _ptr(w), _ptr(k_pages), ps, npg,
+                   _ptr(block_table), bts, B, H, D, T, _ptr(compress_lens), _ptr(scores),
+                   scores.shape[1], _ptr(key_hist)),
+                  stream, "idx_publish_score_paged", bind)
 
 
 def idx_yarn_cos_sin(P, rd, theta, factor, orig_len, beta_fast, beta_slow):

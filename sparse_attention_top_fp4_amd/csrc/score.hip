@@ -414,9 +414,9 @@ constexpr int kRoleDynWords = kRoleMaxDin + 64 * kHeadDim / 2;  // latent + quer
 
 template <int HT>
 __device__ __forceinline__ void publish_and_score_last(
-    const PubFuse& pf, const uint16_t* __restrict__ q, const uint16_t* __restrict__ w,
-    int64_t kstride, int T, int r, int b, int limit, float* srow, uint32_t* key_hist,
-    uint32_t* lds, float* dyn, uint32_t* qs) {
+    const PubFuse& pf, const PageMap& pg, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ w, int64_t kstride, int T, int r, int b, int limit, float* srow,
+    uint32_t* key_hist, uint32_t* lds, float* dyn, uint32_t* qs) {
   constexpr int H = 32 * HT;
   constexpr int NW = kRoleSeg / 8;  // 16-byte words of a segment
   const int tid = threadIdx.x;
@@ -574,8 +574,20 @@ __device__ __forceinline__ void publish_and_score_last(
       quant_q(tid - kHeadDim);
     }
   }
+  // row T - 1: contiguous, or slot (T - 1) % 64 of its page; a page id
+  // outside [0, n_pages) is not written, and the row is scored as the zero
+  // row the paged score reads there
+  uint8_t* dst;
+  if (!pg.bt) {
+    dst = pf.kc + ((int64_t)b * kstride + (T - 1)) * kRowBytes;
+  } else {
+    const int page = pg.bt[(int64_t)b * pg.bt_stride + (T - 1) / kPageRows];
+    dst = page >= 0 && page < pg.n_pages
+              ? pf.kc + (int64_t)page * pg.page_stride + (int64_t)((T - 1) % kPageRows) * kRowBytes
+              : nullptr;
+    if (!dst && tid < 17) row[tid] = 0u;
+  }
   __syncthreads();
-  uint8_t* dst = pf.kc + ((int64_t)b * kstride + (T - 1)) * kRowBytes;
   publish_finish(tid, y_s, z_s, inv_s, gamma_s, cs_s, pf.rd, pf.eps, dst, false, row);
   __syncthreads();
   if (tid < 64) {
@@ -673,7 +685,7 @@ score_kernel(
   if constexpr (!CAND && !TOPK && !F8) {
     // uniform: the publishing workgroup, dispatched ahead of the chunks
     if (pf.on && blockIdx.y == 0) {
-      publish_and_score_last<HT>(pf, q, w, kstride, T, r, b, limit,
+      publish_and_score_last<HT>(pf, pg, q, w, kstride, T, r, b, limit,
                                  scores ? scores + (int64_t)r * ld : nullptr, key_hist, hist_lds,
                                  sbuf, qs_own);
       return;
@@ -1292,6 +1304,62 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
                       (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
                       idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
                       idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1},
+                      idx::Epi{nullptr, 0, 0, 0}, idx::QStep{nullptr, 0, 0, 1.0f, 0});
+}
+
+extern "C" idx_status idx_publish_score_paged(
+    const uint16_t* latent, const uint16_t* wk, const float* gamma, const float* cos_sin, int P,
+    int Din, int rd, float eps, int start_pos, int ratio, const uint16_t* q, const uint16_t* w,
+    uint8_t* k_pages, int64_t page_stride, int n_pages, const int32_t* block_table,
+    int64_t bt_stride, int B, int H, int D, int T, const int32_t* compress_lens, float* scores,
+    int64_t ld, uint32_t* key_hist, void* stream) {
+  // every argument of both steps is checked before either launches
+  if (ratio <= 0 || start_pos < 0 || B < 0 || T < 0 || P < 0 || Din <= 0 || H <= 0 || D <= 0)
+    return IDX_EINVAL;
+  if (D != idx::kHeadDim || (H != 32 && H != 64)) return IDX_EUNSUPPORTED;
+  if (rd < 0 || rd > D || (rd & 1) || !(eps >= 0.0f)) return IDX_EINVAL;
+  if ((size_t)Din * 2 > 60 * 1024) return IDX_EUNSUPPORTED;
+  if (B == 0) return IDX_OK;
+  if (!latent || !wk || !gamma || !k_pages || (rd > 0 && !cos_sin) || !q || !w ||
+      !compress_lens || !scores)
+    return IDX_EINVAL;
+  if (!idx_host::aligned(q, 16) || !idx_host::aligned(k_pages, 4) || (page_stride & 3))
+    return IDX_EINVAL;
+  if (ld < T) return IDX_EINVAL;
+  const int64_t row = start_pos / ratio;  // the completed group's cache row
+  const int pos = start_pos + 1 - ratio;  // its position
+  if (start_pos > 0 && pos < 0) return IDX_EINVAL;
+  if (rd > 0 && (start_pos > 0 ? pos : 0) >= P) return IDX_EINVAL;
+  // the block table covers the scored rows and the published one
+  const int64_t rows = row + 1 > T ? row + 1 : T;
+  if (rows > 0x7fffffffLL) return IDX_EINVAL;
+  idx::PageMap pg{nullptr, 0, 0, 0};
+  {
+    const idx_status e = page_map(block_table, bt_stride, page_stride, n_pages, (int)rows, pg);
+    if (e != IDX_OK) return e;
+  }
+  const bool fuse = start_pos > 0 && row == (int64_t)T - 1 && Din <= idx::kRoleMaxDin;
+  if (!fuse) {  // two launches in stream order: the key, then the score
+    const idx_status e = idx_publish_keys_paged(latent, wk, gamma, cos_sin, P, B, 1, Din, D, rd,
+                                                eps, start_pos, ratio, k_pages, page_stride,
+                                                n_pages, block_table, bt_stride, (int)rows, stream);
+    if (e != IDX_OK) return e;
+    return idx_score_paged(q, w, k_pages, page_stride, n_pages, block_table, bt_stride, B, 1, H,
+                           D, T, compress_lens, nullptr, 0, 0, scores, ld, key_hist, stream);
+  }
+  // as idx_publish_score: keys [0, T - 1) in chunks, one more workgroup per
+  // sequence for the published key T - 1
+  const int kpw = pick_keys_per_wg(B, T - 1, B < 64 ? 256 - B : 256);
+  const int nch = (T - 1 + kpw - 1) / kpw;
+  if (nch + 1 > 65535) return IDX_EINVAL;
+  auto kern = H == 64 ? idx::score_kernel<2, false, false> : idx::score_kernel<1, false, false>;
+  const size_t lds = (size_t)(kpw > idx::kRoleDynWords ? kpw : idx::kRoleDynWords) * sizeof(float);
+  return launch_score(kern, dim3((unsigned)B, (unsigned)(nch + 1)), lds,
+                      (hipStream_t)stream, q, (const uint8_t*)nullptr, w,
+                      (const uint8_t*)k_pages, 0, 1, T, compress_lens,
+                      (const int32_t*)nullptr, 0, 0, scores, ld, key_hist, kpw,
+                      idx::FusedTopk{0, 0, nullptr, 0}, pg,
+                      idx::PubFuse{latent, wk, gamma, cos_sin, k_pages, Din, rd, pos, eps, 1},
                       idx::Epi{nullptr, 0, 0, 0}, idx::QStep{nullptr, 0, 0, 1.0f, 0});
 }
 

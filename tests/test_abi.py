@@ -425,3 +425,27 @@ def test_tsplit_pairs_and_merge_check_before_launch(lib):
     assert merge(pos=None) == IDX_EINVAL
     assert merge(k=0) == IDX_EINVAL
     assert merge(R=0) == IDX_OK and kout.value == 2048
+
+
+def test_publish_score_paged_checks_before_launch(lib):
+    """idx_publish_score_paged refuses invalid arguments of either step before
+    any launch (the pointers are never dereferenced)."""
+    d = ctypes.c_void_p(0x1000)
+
+    def call(H=64, D=128, rd=64, sp=4 * 100 + 3, ps=64 * 68, npg=8, bt=d, bts=2, T=101, ld=101,
+             q=d, pages=d, P=512, din=512):
+        return lib.idx_publish_score_paged(d, d, d, d, P, din, rd, 1e-6, sp, 4, q, d, pages, ps,
+                                           npg, bt, bts, 2, H, D, T, d, d, ld, None, None)
+    assert call(H=48) == IDX_EUNSUPPORTED
+    assert call(D=64) == IDX_EUNSUPPORTED
+    assert call(rd=63) == IDX_EINVAL
+    assert call(bt=None) == IDX_EINVAL                 # no block table
+    assert call(npg=0) == IDX_EINVAL                   # empty pool
+    assert call(ps=64 * 68 - 4) == IDX_EINVAL          # a page shorter than 64 rows
+    assert call(ps=64 * 68 + 2) == IDX_EINVAL          # page stride not a multiple of 4
+    assert call(bts=1) == IDX_EINVAL                   # the table misses the published row's page
+    assert call(ld=100) == IDX_EINVAL                  # scores ld < T
+    assert call(q=ctypes.c_void_p(0x1008)) == IDX_EINVAL  # q not 16-byte aligned
+    assert call(pages=ctypes.c_void_p(0x1002)) == IDX_EINVAL  # pages not 4-byte aligned
+    assert call(P=100) == IDX_EINVAL                   # the key's position not in the RoPE table
+    assert call(din=40000) == IDX_EUNSUPPORTED

@@ -129,3 +129,88 @@ def test_publish_score_equals_two_calls(idx):
         outs.append((host(kc), bits(host(sc)), host(hist)))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+PAGE = 64
+PAGE_STRIDE = PAGE * 68 + 128  # padded pages
+
+
+def _paginate(kc_dev, seed, drop_last=()):
+    """Scatter a contiguous device cache [B, T, 68] into a page pool with a
+    padded stride, pages out of order and spare pages: (pages, block_table).
+    Sequences in drop_last get an id past the pool for their last page."""
+    t = torch()
+    B, T, _ = kc_dev.shape
+    npg = (T + PAGE - 1) // PAGE
+    rng = np.random.default_rng(seed)
+    n_pages = B * npg + 3
+    perm = rng.permutation(n_pages)
+    pages = t.zeros((n_pages, PAGE_STRIDE), dtype=t.uint8, device="cuda")
+    bt = np.zeros((B, npg), np.int32)
+    k = 0
+    for b in range(B):
+        for j in range(npg):
+            p = int(perm[k])
+            k += 1
+            rows = kc_dev[b, j * PAGE:(j + 1) * PAGE].reshape(-1)
+            pages[p, :rows.numel()] = rows
+            bt[b, j] = p
+        if b in drop_last:
+            bt[b, npg - 1] = n_pages + 9
+    return pages, dev(bt)
+
+
+PAGED_CASES = [
+    # (seed, B, H, T, Din, row, drop_last) -- row: the published cache row
+    (131, 3, 64, 5000, 512, 4999, ()),        # one launch
+    (132, 2, 32, 777, 203, 776, ()),          # ragged width, 32 heads, element loads
+    (133, 4, 64, 16384, 512, 16383, (1,)),    # the new row's page missing in one sequence
+    (134, 2, 64, 3000, 512, 2990, ()),        # two launches: key not at T - 1
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[str(c[0]) for c in PAGED_CASES])
+def test_publish_score_paged_equals_contiguous_and_two_calls(idx, case):
+    """idx_publish_score_paged leaves every page row, score and histogram
+    count as idx_publish_keys_paged followed by idx_score_paged, and (with
+    every page present) as the contiguous idx_publish_score and the
+    oracle."""
+    t = torch()
+    seed, B, H, T, din, row, drop = case
+    say("paged publish+score", case)
+    rng = np.random.default_rng(seed)
+    tcap = max(T, row + 1)
+    c = small_case(seed, B, 1, H, T, tcap=tcap)
+    start_pos = RATIO * row + RATIO - 1
+    latent = dev(normal_bf16(rng, (B, 1, din)))
+    wk = dev(normal_bf16(rng, (128, din), std=0.02))
+    gamma = dev((1.0 + 0.1 * rng.standard_normal(128)).astype(np.float32))
+    cs = dev(oracle.yarn_cos_sin(start_pos + 1, 64, YARN["theta"], YARN["factor"],
+                                 YARN["orig_len"], YARN["beta_fast"], YARN["beta_slow"]))
+    kc0, _ = oracle.fp4_quant_rows(c["k"])
+    q, w, cl = dev(c["q"]), dev(c["w"]), dev(c["cl"])
+    outs = []
+    for fused in (True, False):
+        pages, bt = _paginate(dev(kc0), seed, drop)
+        sc = t.full((B, T), float(SENTINEL), dtype=t.float32, device="cuda")
+        hist = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        if fused:
+            idx.idx_publish_score_paged(latent, wk, gamma, cs, start_pos, RATIO, EPS, q, w, pages,
+                                        bt, T, cl, sc, key_hist=hist)
+        else:
+            idx.idx_publish_keys_paged(latent, wk, gamma, cs, start_pos, RATIO, EPS, pages, bt,
+                                       tcap)
+            idx.idx_score_paged(q, w, pages, bt, B, 1, T, cl, sc, key_hist=hist)
+        sync()
+        outs.append((host(pages), bits(host(sc)), host(hist)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    if not drop:
+        kc = dev(kc0)
+        sc = t.full((B, T), float(SENTINEL), dtype=t.float32, device="cuda")
+        hist = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        idx.idx_publish_score(latent, wk, gamma, cs, start_pos, RATIO, EPS, q, w, kc, T, cl, sc,
+                              key_hist=hist)
+        sync()
+        assert np.array_equal(outs[0][1], bits(host(sc)))
+        assert np.array_equal(outs[0][2], host(hist))
