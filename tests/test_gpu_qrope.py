@@ -22,7 +22,10 @@ def idx():
 
 @pytest.mark.parametrize("B,S,H,sp,rd", [(4, 1, 64, 131071, 64), (1, 40, 64, 0, 64),
                                          (2, 7, 32, 1000, 40), (3, 2, 64, 5, 0),
-                                         (1, 3, 32, 7, 64)])  # 96 heads: a partial workgroup
+                                         (1, 3, 32, 7, 64),    # 96 heads: a partial workgroup
+                                         (2, 5, 64, 300, 42),  # RoPE from dim 86, inside a piece
+                                         (1, 1, 1, 3, 2),      # one head, one RoPE pair
+                                         (1, 2, 16, 9, 128)])  # every dim rotated
 def test_q_rope_quant_matches_oracle(idx, B, S, H, sp, rd):
     t = torch()
     say("q rope quant", B, S, H, sp, rd)
@@ -139,6 +142,7 @@ QS_CASES = [
     (True, 2, 6, 64, 3000, 10000, 64, 1.0, 700),         # fused top-k
     (True, 1, 9, 32, 5000, 15990, 40, 0.0625, 300),      # 32 heads, rd 40, scaled weights
     (False, 3, 2, 64, 700, 5, 0, 0.5, 0),                # rd 0: no rotation, weights scaled
+    (False, 2, 3, 64, 900, 50, 42, 0.25, 0),             # RoPE from dim 86, inside a block
 ]
 
 
