@@ -650,6 +650,24 @@ idx_status idx_publish_score(const uint16_t *latent, const uint16_t *wk, const f
                              uint32_t *key_hist, void *stream);
 
 /*
+ * idx_publish_score_fp8 -- idx_publish_score on an FP8 key cache: the
+ * steps idx_publish_keys_fp8 then idx_score_fp8 ([IDX, forward]: the
+ * key-owning layer's store before the score reads the cache; the FP8 row of
+ * [VLLM, _indexer_k_cache_head_dim], 128 e4m3 bytes and an fp32 ue8m0
+ * scale).  The same single launch when the new key is the last scored
+ * position, the two calls on the stream otherwise.  k_cache rows are 132
+ * bytes with stride k_batch_stride_rows.  Arguments, results and errors as
+ * the two calls; the cache row, the scores and key_hist equal theirs bit for
+ * bit for the documented inputs.  Din <= 2048 for the single launch.
+ */
+idx_status idx_publish_score_fp8(const uint16_t *latent, const uint16_t *wk, const float *gamma,
+                                 const float *cos_sin, int P, int Din, int rd, float eps,
+                                 int start_pos, int ratio, const uint16_t *q, const uint16_t *w,
+                                 uint8_t *k_cache, int64_t k_batch_stride_rows, int B, int H,
+                                 int D, int T, const int32_t *compress_lens, float *scores,
+                                 int64_t ld, uint32_t *key_hist, void *stream);
+
+/*
  * idx_publish_score_paged -- idx_publish_score on a paged key cache
  * ([IDX, forward]: the key-owning layer's store before the score reads the
  * cache; pages as idx_score_paged: row t of sequence b in slot t % 64 of

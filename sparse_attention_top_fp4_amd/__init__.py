@@ -22,7 +22,8 @@ __all__ = ["idx_fp4_quant", "idx_fp8_quant", "idx_score_fp8", "idx_publish_keys_
            "idx_topk_candidates",
            "idx_topk_workspace_size",
            "idx_select_candidate_blocks", "idx_select_workspace_size", "idx_publish_keys",
-           "idx_publish_score", "idx_publish_score_paged", "idx_score_select_blocks",
+           "idx_publish_score", "idx_publish_score_paged", "idx_publish_score_fp8",
+           "idx_score_select_blocks",
            "idx_score_topk_candidates",
            "idx_two_level_topk", "idx_topk_pairs", "idx_topk_pairs_workspace_size",
            "idx_merge_topk",
@@ -99,6 +100,7 @@ def load_library():
                                           i32, i32, P, i64, P, sz, P]
     L.idx_publish_score.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64, i32,
                                     i32, i32, i32, P, P, i64, P, P]
+    L.idx_publish_score_fp8.argtypes = L.idx_publish_score.argtypes
     L.idx_publish_score_paged.argtypes = [P, P, P, P, i32, i32, i32, f32, i32, i32, P, P, P, i64,
                                           i32, P, i64, i32, i32, i32, i32, P, P, i64, P, P]
     L.idx_topk_pairs_workspace_size.argtypes = [i32, i32, i32]
@@ -122,7 +124,7 @@ def load_library():
                  "idx_score_fp8", "idx_publish_keys_fp8", "idx_publish_score",
                  "idx_score_select_blocks", "idx_score_topk_candidates", "idx_two_level_topk",
                  "idx_score_qrope", "idx_score_topk_qrope", "idx_topk_pairs", "idx_merge_topk",
-                 "idx_publish_score_paged"):
+                 "idx_publish_score_paged", "idx_publish_score_fp8"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -889,13 +891,8 @@ def idx_score_select_blocks(q, w, k_cache, B, S, T, compress_lens, scores, candi
                    _ptr(workspace), workspace.numel()), stream, "idx_score_select_blocks", bind)
 
 
-def idx_publish_score(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_cache, T,
-                      compress_lens, scores, key_hist=None, rd=64, stream=None, bind=False):
-    """idx_publish_keys then idx_score for one decode step (one query row and
-    one group per sequence): latent [B, 1, Din] bf16, q [B, H, 128] bf16,
-    w [B, H] bf16, k_cache [B', Tcap, 68] uint8, compress_lens [B] int32,
-    scores [B, ld] float32, key_hist [B, 2048] int32 or None.  One launch
-    when the published row is the last scored position (T - 1)."""
+def _publish_score(name, rb, latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_cache,
+                   T, compress_lens, scores, key_hist, rd, stream, bind):
     torch = _torch()
     _dev(latent, "latent", _bf16_types(), 3)
     _dev(wk, "wk", _bf16_types(), 2)
@@ -909,20 +906,41 @@ def idx_publish_score(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k
     B, G, Din = latent.shape
     R, H, D = q.shape
     if G != 1 or R != B or tuple(w.shape) != (B, H) or compress_lens.shape[0] != B:
-        raise ValueError("idx_publish_score takes one group and one query row per sequence")
+        raise ValueError(f"{name} takes one group and one query row per sequence")
     if wk.shape != (D, Din) or gamma.shape[0] != D or k_cache.shape[0] < B:
-        raise ValueError("shape mismatch in idx_publish_score")
-    if k_cache.shape[2] != ROW_BYTES or scores.shape[0] != B:
-        raise ValueError("k_cache must be [>=B, Tcap, 68] and scores [B, ld]")
+        raise ValueError(f"shape mismatch in {name}")
+    if k_cache.shape[2] != rb or scores.shape[0] != B:
+        raise ValueError(f"k_cache must be [>=B, Tcap, {rb}] and scores [B, ld]")
     if key_hist is not None:
         _dev(key_hist, "key_hist", (torch.int32,), 2)
         if tuple(key_hist.shape) != (B, 2048):
             raise ValueError("key_hist must be [B, 2048]")
-    return _issue("idx_publish_score",
+    return _issue(name,
                   (_ptr(latent), _ptr(wk), _ptr(gamma), _ptr(cos_sin), cos_sin.shape[0], Din, rd,
                    eps, start_pos, ratio, _ptr(q), _ptr(w), _ptr(k_cache), k_cache.shape[1], B, H,
                    D, T, _ptr(compress_lens), _ptr(scores), scores.shape[1], _ptr(key_hist)),
-                  stream, "idx_publish_score", bind)
+                  stream, name, bind)
+
+
+def idx_publish_score(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_cache, T,
+                      compress_lens, scores, key_hist=None, rd=64, stream=None, bind=False):
+    """idx_publish_keys then idx_score for one decode step (one query row and
+    one group per sequence): latent [B, 1, Din] bf16, q [B, H, 128] bf16,
+    w [B, H] bf16, k_cache [B', Tcap, 68] uint8, compress_lens [B] int32,
+    scores [B, ld] float32, key_hist [B, 2048] int32 or None.  One launch
+    when the published row is the last scored position (T - 1)."""
+    return _publish_score("idx_publish_score", ROW_BYTES, latent, wk, gamma, cos_sin, start_pos,
+                          ratio, eps, q, w, k_cache, T, compress_lens, scores, key_hist, rd,
+                          stream, bind)
+
+
+def idx_publish_score_fp8(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_cache, T,
+                          compress_lens, scores, key_hist=None, rd=64, stream=None, bind=False):
+    """idx_publish_keys_fp8 then idx_score_fp8 for one decode step: as
+    idx_publish_score, with k_cache [B', Tcap, 132] uint8 FP8 rows."""
+    return _publish_score("idx_publish_score_fp8", FP8_ROW_BYTES, latent, wk, gamma, cos_sin,
+                          start_pos, ratio, eps, q, w, k_cache, T, compress_lens, scores,
+                          key_hist, rd, stream, bind)
 
 
 def idx_publish_score_paged(latent, wk, gamma, cos_sin, start_pos, ratio, eps, q, w, k_pages,

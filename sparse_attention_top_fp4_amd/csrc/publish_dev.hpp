@@ -102,16 +102,25 @@ __device__ __forceinline__ void publish_finish(int o, const float* y_s, uint32_t
   if (f8) {
     // FP8 row: one e4m3 scale for the 128 values; every thread finds the
     // amax itself (LDS broadcast reads, no further barrier) and writes its
-    // own code byte
-    if (o < kHeadDim && dst) {
+    // own code byte (and, with row_copy, the same byte of the row's 33-word
+    // copy in LDS)
+    if (o < kHeadDim && (dst || row_copy)) {
       uint32_t amax = 0;
       for (int j = 0; j < kHeadDim; ++j) {
         const uint32_t a = z_s[j] & 0x7fffu;
         amax = a > amax ? a : amax;
       }
       const int e = ue8m0_exponent_f8(bf16f(amax));
-      dst[o] = (uint8_t)e4m3_code(z_s[o], e);
-      if (o == 0) *reinterpret_cast<uint32_t*>(dst + 128) = (uint32_t)(127 + e) << 23;
+      const uint8_t code = (uint8_t)e4m3_code(z_s[o], e);
+      const uint32_t scale = (uint32_t)(127 + e) << 23;
+      if (dst) {
+        dst[o] = code;
+        if (o == 0) *reinterpret_cast<uint32_t*>(dst + 128) = scale;
+      }
+      if (row_copy) {
+        reinterpret_cast<uint8_t*>(row_copy)[o] = code;
+        if (o == 0) row_copy[32] = scale;
+      }
     }
     return;
   }

@@ -407,12 +407,13 @@ struct Epi {
 // path's own tile code (matrix-core dots and head sum) on a tile that
 // holds only that key.  hist_lds: 2048 words; dyn: the score buffer, at
 // least kRoleDynWords words (the fp32 latent, then the bf16 query row);
-// qs: H quantised heads of 17 words.
+// qs: H quantised heads of 17 words (F8: 33).  F8: the key cache and the
+// heads hold FP8 rows, as the fp8 score and the fp8 publish write them.
 constexpr int kRoleSeg = 256;   // wk values per thread per pass
 constexpr int kRoleMaxDin = 2048;
 constexpr int kRoleDynWords = kRoleMaxDin + 64 * kHeadDim / 2;  // latent + query row
 
-template <int HT>
+template <int HT, bool F8 = false>
 __device__ __forceinline__ void publish_and_score_last(
     const PubFuse& pf, const PageMap& pg, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ w, int64_t kstride, int T, int r, int b, int limit, float* srow,
@@ -425,7 +426,7 @@ __device__ __forceinline__ void publish_and_score_last(
   float* y_s = reinterpret_cast<float*>(lds);                    // 128
   uint32_t* z_s = lds + 128;                                     // 128
   float* inv_s = reinterpret_cast<float*>(lds + 256);            // 1
-  uint32_t* row = lds + 260;                                     // 17 words: the new key
+  uint32_t* row = lds + (F8 ? 728 : 260);                        // 17 words (F8: 33): the new key
   float* acc_s = reinterpret_cast<float*>(lds + 280);            // 128: chains in flight
   float* gamma_s = reinterpret_cast<float*>(lds + 408);          // 128
   float* cs_s = reinterpret_cast<float*>(lds + 536);             // rd <= 128
@@ -537,11 +538,19 @@ __device__ __forceinline__ void publish_and_score_last(
         xp[4 * i + 2] = v.z;
         xp[4 * i + 3] = v.w;
       }
-      uint32_t codes[4];
-      const int e = quant_block32(xp, codes);
+      if constexpr (F8) {  // a head's four blocks sit in one quad of lanes
+        uint32_t codes[8];
+        const int e = quant_block128_f8(xp, codes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
-      reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
+        for (int i = 0; i < 8; ++i) qs[h * 33 + 8 * g + i] = codes[i];
+        if (g == 0) qs[h * 33 + 32] = (uint32_t)(127 + e) << 23;
+      } else {
+        uint32_t codes[4];
+        const int e = quant_block32(xp, codes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qs[h * 17 + 4 * g + i] = codes[i];
+        reinterpret_cast<uint8_t*>(qs)[h * kRowBytes + 64 + g] = (uint8_t)(e + 127);
+      }
     }
   };
 
@@ -578,8 +587,8 @@ __device__ __forceinline__ void publish_and_score_last(
   // outside [0, n_pages) is not written, and the row is scored as the zero
   // row the paged score reads there
   uint8_t* dst;
-  if (!pg.bt) {
-    dst = pf.kc + ((int64_t)b * kstride + (T - 1)) * kRowBytes;
+  if (F8 || !pg.bt) {
+    dst = pf.kc + ((int64_t)b * kstride + (T - 1)) * (F8 ? kRowBytesF8 : kRowBytes);
   } else {
     const int page = pg.bt[(int64_t)b * pg.bt_stride + (T - 1) / kPageRows];
     dst = page >= 0 && page < pg.n_pages
@@ -588,7 +597,7 @@ __device__ __forceinline__ void publish_and_score_last(
     if (!dst && tid < 17) row[tid] = 0u;
   }
   __syncthreads();
-  publish_finish(tid, y_s, z_s, inv_s, gamma_s, cs_s, pf.rd, pf.eps, dst, false, row);
+  publish_finish(tid, y_s, z_s, inv_s, gamma_s, cs_s, pf.rd, pf.eps, dst, F8, row);
   __syncthreads();
   if (tid < 64) {
     // the tile: key 0 of key tile 0 is the new row (lane 0 holds blocks 0
@@ -602,29 +611,50 @@ __device__ __forceinline__ void publish_and_score_last(
       const int h = head_of_row<HT>(ht, lane & 31);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int g = 2 * st + (lane >> 5);
-        const uint32_t* p = qs + h * 17 + 4 * g;
-        A[ht][st] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
-        sA[ht][st] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+        if constexpr (F8) {  // K-step st, K-half lane/32: bytes 64 st + 32 (lane/32)
+          const uint32_t* p = qs + h * 33 + 16 * st + 8 * (lane >> 5);
+          A[ht][st] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3],
+                          (int)p[4], (int)p[5], (int)p[6], (int)p[7]};
+          sA[ht][st] = (int)((qs[h * 33 + 32] >> 23) & 0xffu);
+        } else {
+          const int g = 2 * st + (lane >> 5);
+          const uint32_t* p = qs + h * 17 + 4 * g;
+          A[ht][st] = v8i{(int)p[0], (int)p[1], (int)p[2], (int)p[3], 0, 0, 0, 0};
+          sA[ht][st] = reinterpret_cast<const uint8_t*>(qs)[h * kRowBytes + 64 + g];
+        }
       }
     }
     float wvh[16 * HT];
 #pragma unroll
     for (int j = 0; j < 16 * HT; ++j) wvh[j] = w_s[(lane >> 5) * (H / 2) + j];
-    KeyTile kt;
+    KeyTileT<F8> kt;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      kt.c[t][0][0] = u32x4{0u, 0u, 0u, 0u};
-      kt.c[t][1][0] = u32x4{0u, 0u, 0u, 0u};
-      kt.sc[t] = 0u;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < (F8 ? 2 : 1); ++u) kt.c[t][st][u] = z4;
+      kt.sc[t] = 0u;  // scale 2^-127 on zero codes: zero dots
     }
     if ((lane & 31) == 0) {
-      const int hw = 4 * (lane >> 5);
-      kt.c[0][0][0] = u32x4{row[hw], row[hw + 1], row[hw + 2], row[hw + 3]};
-      kt.c[0][1][0] = u32x4{row[8 + hw], row[9 + hw], row[10 + hw], row[11 + hw]};
-      kt.sc[0] = row[16];
+      if constexpr (F8) {  // lane 0: bytes 64 st + 0..31, lane 32: 64 st + 32..63
+        const int hw = 8 * (lane >> 5);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const uint32_t* p = row + 16 * st + hw;
+          kt.c[0][st][0] = u32x4{p[0], p[1], p[2], p[3]};
+          kt.c[0][st][1] = u32x4{p[4], p[5], p[6], p[7]};
+        }
+        kt.sc[0] = row[32];
+      } else {
+        const int hw = 4 * (lane >> 5);
+        kt.c[0][0][0] = u32x4{row[hw], row[hw + 1], row[hw + 2], row[hw + 3]};
+        kt.c[0][1][0] = u32x4{row[8 + hw], row[9 + hw], row[10 + hw], row[11 + hw]};
+        kt.sc[0] = row[16];
+      }
     }
-    const float sc = head_sum_tile<HT>(kt, A, sA, wvh, lane);
+    const float sc = head_sum_tile<HT, F8>(kt, A, sA, wvh, lane);
     if (lane == 0 && T - 1 < limit) {
       if (srow) srow[T - 1] = sc;
       if (key_hist) atomicAdd(&key_hist[(int64_t)r * 2048 + (score_key(sc) >> 21)], 1u);
@@ -682,10 +712,10 @@ score_kernel(
   pm.cbs = cbs;
   pm.nblk = CAND ? (T + cbs - 1) / cbs : 0;
   pm.limit = limit;
-  if constexpr (!CAND && !TOPK && !F8) {
+  if constexpr (!CAND && !TOPK) {
     // uniform: the publishing workgroup, dispatched ahead of the chunks
     if (pf.on && blockIdx.y == 0) {
-      publish_and_score_last<HT>(pf, pg, q, w, kstride, T, r, b, limit,
+      publish_and_score_last<HT, F8>(pf, pg, q, w, kstride, T, r, b, limit,
                                  scores ? scores + (int64_t)r * ld : nullptr, key_hist, hist_lds,
                                  sbuf, qs_own);
       return;
@@ -1253,13 +1283,16 @@ extern "C" idx_status idx_score_select_blocks(const uint16_t* q, const uint16_t*
                                           (hipStream_t)stream);
 }
 
-extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* wk,
-                                        const float* gamma, const float* cos_sin, int P, int Din,
-                                        int rd, float eps, int start_pos, int ratio,
-                                        const uint16_t* q, const uint16_t* w, uint8_t* k_cache,
-                                        int64_t k_batch_stride_rows, int B, int H, int D, int T,
-                                        const int32_t* compress_lens, float* scores, int64_t ld,
-                                        uint32_t* key_hist, void* stream) {
+namespace {
+// idx_publish_score and idx_publish_score_fp8: the same two steps on fp4 or
+// FP8 rows (f8: the key row as idx_publish_keys_fp8 writes it, the heads
+// and the score as idx_score_fp8 computes them).
+idx_status publish_score_impl(const uint16_t* latent, const uint16_t* wk, const float* gamma,
+                              const float* cos_sin, int P, int Din, int rd, float eps,
+                              int start_pos, int ratio, const uint16_t* q, const uint16_t* w,
+                              uint8_t* k_cache, int64_t k_batch_stride_rows, int B, int H, int D,
+                              int T, const int32_t* compress_lens, float* scores, int64_t ld,
+                              uint32_t* key_hist, void* stream, bool f8) {
   // every argument of both steps is checked before either launches
   if (ratio <= 0 || start_pos < 0 || B < 0 || T < 0 || P < 0 || Din <= 0 || H <= 0 || D <= 0)
     return IDX_EINVAL;
@@ -1280,12 +1313,14 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
   const bool fuse = start_pos > 0 && row == (int64_t)T - 1 && Din <= idx::kRoleMaxDin;
   if (!fuse) {  // two launches in stream order: the key, then the score
     const int tcap = k_batch_stride_rows < 0x7fffffff ? (int)k_batch_stride_rows : 0x7fffffff;
-    const idx_status e = idx_publish_keys(latent, wk, gamma, cos_sin, P, B, 1, Din, D, rd, eps,
-                                          start_pos, ratio, k_cache, k_batch_stride_rows, tcap,
-                                          stream);
+    const idx_status e =
+        (f8 ? idx_publish_keys_fp8 : idx_publish_keys)(latent, wk, gamma, cos_sin, P, B, 1, Din,
+                                                       D, rd, eps, start_pos, ratio, k_cache,
+                                                       k_batch_stride_rows, tcap, stream);
     if (e != IDX_OK) return e;
-    return idx_score(q, w, k_cache, k_batch_stride_rows, B, 1, H, D, T, compress_lens, nullptr, 0,
-                     0, scores, ld, key_hist, stream);
+    return (f8 ? idx_score_fp8 : idx_score)(q, w, k_cache, k_batch_stride_rows, B, 1, H, D, T,
+                                            compress_lens, nullptr, 0, 0, scores, ld, key_hist,
+                                            stream);
   }
   // keys [0, T - 1) in chunks as idx_score would take them, and one more
   // workgroup per sequence for the published key T - 1; while those are
@@ -1295,6 +1330,9 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
   const int nch = (T - 1 + kpw - 1) / kpw;
   if (nch + 1 > 65535) return IDX_EINVAL;
   auto kern = H == 64 ? idx::score_kernel<2, false, false> : idx::score_kernel<1, false, false>;
+  if (f8)
+    kern = H == 64 ? idx::score_kernel<2, false, false, true>
+                   : idx::score_kernel<1, false, false, true>;
   // the publishing workgroup keeps the fp32 latent and the query row in
   // the score buffer
   const size_t lds = (size_t)(kpw > idx::kRoleDynWords ? kpw : idx::kRoleDynWords) * sizeof(float);
@@ -1305,6 +1343,32 @@ extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* 
                       idx::FusedTopk{0, 0, nullptr, 0}, idx::PageMap{nullptr, 0, 0, 0},
                       idx::PubFuse{latent, wk, gamma, cos_sin, k_cache, Din, rd, pos, eps, 1},
                       idx::Epi{nullptr, 0, 0, 0}, idx::QStep{nullptr, 0, 0, 1.0f, 0});
+}
+}  // namespace
+
+extern "C" idx_status idx_publish_score(const uint16_t* latent, const uint16_t* wk,
+                                        const float* gamma, const float* cos_sin, int P, int Din,
+                                        int rd, float eps, int start_pos, int ratio,
+                                        const uint16_t* q, const uint16_t* w, uint8_t* k_cache,
+                                        int64_t k_batch_stride_rows, int B, int H, int D, int T,
+                                        const int32_t* compress_lens, float* scores, int64_t ld,
+                                        uint32_t* key_hist, void* stream) {
+  return publish_score_impl(latent, wk, gamma, cos_sin, P, Din, rd, eps, start_pos, ratio, q, w,
+                            k_cache, k_batch_stride_rows, B, H, D, T, compress_lens, scores, ld,
+                            key_hist, stream, false);
+}
+
+extern "C" idx_status idx_publish_score_fp8(const uint16_t* latent, const uint16_t* wk,
+                                            const float* gamma, const float* cos_sin, int P,
+                                            int Din, int rd, float eps, int start_pos, int ratio,
+                                            const uint16_t* q, const uint16_t* w,
+                                            uint8_t* k_cache, int64_t k_batch_stride_rows, int B,
+                                            int H, int D, int T, const int32_t* compress_lens,
+                                            float* scores, int64_t ld, uint32_t* key_hist,
+                                            void* stream) {
+  return publish_score_impl(latent, wk, gamma, cos_sin, P, Din, rd, eps, start_pos, ratio, q, w,
+                            k_cache, k_batch_stride_rows, B, H, D, T, compress_lens, scores, ld,
+                            key_hist, stream, true);
 }
 
 extern "C" idx_status idx_publish_score_paged(

@@ -15,7 +15,7 @@ import ctypes
 import numpy as np
 
 from . import (PAGE_ROWS, current_stream_handle, idx_clear_key_hist, idx_fp4_quant,
-               idx_publish_score_paged,
+               idx_publish_score_paged, idx_publish_score_fp8,
                idx_fp8_quant, idx_publish_keys, idx_publish_keys_fp8, idx_publish_keys_paged,
                idx_publish_score, idx_score_select_blocks, idx_score_topk_candidates,
                idx_score_fp8, idx_q_rope_quant, idx_score, idx_score_paged,
@@ -151,9 +151,10 @@ class IndexerStep:
                                                       YARN["beta_slow"]))
 
         # the decode publish of the last scored key joins the score launch
-        # (idx_publish_score, idx_publish_score_paged) on fp4 caches with bf16 queries
+        # (idx_publish_score, idx_publish_score_paged, idx_publish_score_fp8)
+        # with bf16 queries
         self.publish_in_score = (self.publish and wl.S == 1 and wl.start_pos > 0 and
-                                 wl.start_pos // wl.ratio == T - 1 and not fp8 and
+                                 wl.start_pos // wl.ratio == T - 1 and
                                  not self.fused and not (q_step and not wl.ctb) and
                                  wl.din <= 2048)
 
@@ -270,10 +271,10 @@ class IndexerStep:
             calls.append(idx_score_q4(q4, w, kc, wl.B, wl.S, wl.T, self.cl, self.scores,
                                       key_hist=self.key_hist, **b))
         elif pub_in_score:
-            calls.append(idx_publish_score(self.latent, self.wk, self.gamma, self.cos_sin,
-                                           wl.start_pos, wl.ratio, wl.eps, q, w, kc, wl.T,
-                                           self.cl, self.scores, key_hist=self.key_hist,
-                                           rd=wl.rd, **b))
+            pub_score = idx_publish_score_fp8 if self.fp8 else idx_publish_score
+            calls.append(pub_score(self.latent, self.wk, self.gamma, self.cos_sin,
+                                   wl.start_pos, wl.ratio, wl.eps, q, w, kc, wl.T, self.cl,
+                                   self.scores, key_hist=self.key_hist, rd=wl.rd, **b))
         elif self.two_level and not self.fp8:
             # level one: the score launch also writes the block maxima and
             # one wave per row selects the candidate blocks

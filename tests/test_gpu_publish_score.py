@@ -8,7 +8,9 @@ exactly the scored positions.  Cases cover the single launch (new key at
 T - 1: one extra workgroup per sequence), the two-launch form (new key
 elsewhere, start_pos 0, Din past 2048), rows whose compress_lens stops
 before the new key, a lone key (T = 1), 32 and 64 heads, and Din values
-that take the 16-byte and the element loads."""
+that take the 16-byte and the element loads.  The FP8 form
+(idx_publish_score_fp8) equals its two calls bit for bit, and its published
+row is the oracle's FP8 row of the oracle's key."""
 import numpy as np
 import pytest
 
@@ -129,6 +131,67 @@ def test_publish_score_equals_two_calls(idx):
         outs.append((host(kc), bits(host(sc)), host(hist)))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+FP8_CASES = [
+    # (seed, B, H, T, tcap, Din, row, cl), as CASES
+    (131, 3, 64, 5000, 5000, 512, 4999, None),          # one launch, several chunks
+    (132, 2, 32, 777, 800, 512, 776, None),             # 32 heads, spare rows
+    (133, 2, 64, 1, 1, 512, 0, None),                   # the new key alone
+    (134, 3, 64, 3000, 3000, 512, 2999, [3000, 2999, 1500]),  # rows that stop before it
+    (135, 2, 64, 2100, 2100, 203, 2099, None),          # element loads of wk
+    (136, 3, 64, 4000, 4096, 512, 3995, None),          # two launches: key not at T - 1
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[str(c[0]) for c in FP8_CASES])
+def test_publish_score_fp8_equals_two_calls(idx, case):
+    """idx_publish_score_fp8 against idx_publish_keys_fp8 then idx_score_fp8:
+    the same FP8 cache, scores and histogram bit for bit; the published row
+    is the oracle's FP8 quantisation of the oracle's published key."""
+    t = torch()
+    seed, B, H, T, tcap, din, row, cl = case
+    say("publish+score fp8", case)
+    rng = np.random.default_rng(seed)
+    c = small_case(seed, B, 1, H, T, tcap=tcap)
+    if cl is not None:
+        c["cl"] = np.array(cl, np.int32)
+    start_pos = RATIO * row + RATIO - 1
+    latent = normal_bf16(rng, (B, 1, din))
+    wk = normal_bf16(rng, (128, din), std=0.02)
+    gamma = (1.0 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    cs = oracle.yarn_cos_sin(start_pos + 1, 64, YARN["theta"], YARN["factor"], YARN["orig_len"],
+                             YARN["beta_fast"], YARN["beta_slow"])
+    pre = oracle.publish(latent, wk, gamma, cs, start_pos, RATIO, EPS,
+                         np.zeros((B, tcap, 68), np.uint8))
+    want_row, _ = oracle.fp8_quant_rows(pre[:, 0])
+    kc0, _ = oracle.fp8_quant_rows(c["k"])
+    args = [dev(latent), dev(wk), dev(gamma), dev(cs)]
+    q, w, cld = dev(c["q"]), dev(c["w"]), dev(c["cl"])
+    outs = []
+    for fused in (True, False):
+        kc = dev(kc0)
+        sc = t.full((B, T + 3), float(SENTINEL), dtype=t.float32, device="cuda")
+        hist = t.zeros((B, 2048), dtype=t.int32, device="cuda")
+        if fused:
+            idx.idx_publish_score_fp8(*args, start_pos, RATIO, EPS, q, w, kc, T, cld, sc,
+                                      key_hist=hist)
+        else:
+            idx.idx_publish_keys_fp8(*args, start_pos, RATIO, EPS, kc)
+            idx.idx_score_fp8(q, w, kc, B, 1, T, cld, sc, key_hist=hist)
+        sync()
+        outs.append((host(kc), bits(host(sc)), host(hist)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    kc_got = outs[0][0]
+    assert np.array_equal(kc_got[:, row], want_row)
+    rest = np.ones(tcap, bool)
+    rest[row] = False
+    assert np.array_equal(kc_got[:, rest], kc0[:, rest])  # no other row written
+    live = np.arange(T)[None, :] < np.minimum(c["cl"], T)[:, None]
+    assert np.all(outs[0][1][:, :T][~live] == bits(SENTINEL))
+    assert np.all(outs[0][1][:, T:] == bits(SENTINEL))
+    assert outs[0][2].sum() == live.sum()
 
 
 PAGE = 64
