@@ -261,16 +261,18 @@ def test_unaligned_pointers_are_rejected(lib):
                                 8, None) == IDX_EINVAL
 
 
-def test_publish_score_checks_both_steps_before_launch(lib):
-    """idx_publish_score checks the publish's and the score's arguments
-    before either step launches, in its one-launch and two-launch forms."""
+@pytest.mark.parametrize("name", ["idx_publish_score", "idx_publish_score_fp8"])
+def test_publish_score_checks_both_steps_before_launch(lib, name):
+    """idx_publish_score (and its FP8 form) checks the publish's and the
+    score's arguments before either step launches, in its one-launch and
+    two-launch forms."""
     a16, odd8, odd2 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
     T = 100
 
     def call(q=a16, kc=a16, sp=4 * (T - 1) + 3, ratio=4, P=400, Din=512, rd=64, eps=1e-6, B=2,
              H=64, D=128, stride=T, ld=T, cl=a16, lat=a16):
-        return lib.idx_publish_score(lat, a16, a16, a16, P, Din, rd, eps, sp, ratio, q, a16, kc,
-                                     stride, B, H, D, T, cl, a16, ld, None, None)
+        return getattr(lib, name)(lat, a16, a16, a16, P, Din, rd, eps, sp, ratio, q, a16, kc,
+                                  stride, B, H, D, T, cl, a16, ld, None, None)
 
     for sp in (4 * (T - 1) + 3, 4 * 50 + 3, 0):  # one launch, two launches, prefill form
         assert call(sp=sp, q=odd8) == IDX_EINVAL
